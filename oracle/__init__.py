@@ -1,0 +1,88 @@
+"""fp64 CPU oracle for the LiteLA forward.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+CPU-baseline leg of the benchmark.  The HIP product path never imports it.
+
+* ``linattn_fwd``  -- the linear (state) form in C, fp64, OpenMP over (b, h);
+  see ``linattn_oracle.c`` for the definition and the pages it follows.
+* ``brute``        -- the quadratic form in numpy (its pin).
+* ``exact``        -- the quadratic form in exact rational arithmetic (tiny sizes).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liblinattn_oracle.so")
+_lib = None
+
+F32 = 0
+BF16 = 1
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.oracle_linattn_fwd.restype = ctypes.c_int
+        lib.oracle_linattn_fwd.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float32:
+        return F32
+    raise TypeError(f"oracle inputs are float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def num_blocks(N: int, block_len: int | None) -> int:
+    L = N if (not block_len or block_len <= 0 or block_len >= N) else block_len
+    return (N + L - 1) // L if N > 0 else 0
+
+
+def linattn_fwd(q, k, v, *, block_len: int | None = None, eps: float = 1e-15,
+                nthreads: int = 0, return_states: bool = False):
+    """fp64 LiteLA forward on host arrays of shape [B, N, H, D].
+
+    q, k, v: float32, or uint16 holding bfloat16 bits (all three the same).
+    block_len: None/0 for non-causal, else the frame-block length in tokens.
+    Returns out as float64 [B, N, H, D]; with return_states also the inclusive
+    per-block states, float64 [B, H, NB, D, D+1].
+    """
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    if not (q.shape == k.shape == v.shape) or q.ndim != 4:
+        raise ValueError("q, k, v must share one [B, N, H, D] shape")
+    code = _dtype_code(q)
+    if _dtype_code(k) != code or _dtype_code(v) != code:
+        raise TypeError("q, k, v must share one dtype")
+    B, N, H, D = q.shape
+    out = np.empty((B, N, H, D), dtype=np.float64)
+    states = None
+    if return_states:
+        states = np.empty((B, H, max(num_blocks(N, block_len), 1), D, D + 1), dtype=np.float64)
+    rc = _load().oracle_linattn_fwd(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, code, B, H, N, D,
+        int(block_len or 0), float(eps), out.ctypes.data,
+        states.ctypes.data if states is not None else None, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_linattn_fwd failed ({rc})")
+    return (out, states) if return_states else out

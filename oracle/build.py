@@ -1,0 +1,30 @@
+"""Build the fp64 CPU oracle (test infrastructure) as oracle/liblinattn_oracle.so.
+
+Plain gcc, OpenMP, no FMA contraction and no -march=native, so the library is
+portable to whatever x86-64 host runs the tests and the arithmetic stays the
+plain sequence of multiplies and adds written in the source.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "linattn_oracle.c")
+LIB = os.path.join(HERE, "liblinattn_oracle.so")
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           "-Wall", "-Wextra", "-Werror", SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,148 @@
+/*
+ * LiteLA forward oracle: plain fp64 CPU implementation.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the checker for the HIP library; only
+ * the tests, the smoke check and the CPU-baseline leg of the benchmark may load
+ * it.  It shares no code, header or constant with the HIP path.
+ *
+ * What it computes (ReLU-kernel linear self-attention, as described on
+ * "Sana: the autoencoder does more of the work than the linear attention",
+ * section "What LiteLA actually computes", and on "How Linear Attention
+ * Improves Efficiency in DiT for High-Resolution Images", sections
+ * "Mathematical Foundation" and "Implementation Details"):
+ *
+ *   for every batch b and head h, with phi(x) = max(x, 0) applied elementwise,
+ *     a_n = phi(k[b,n,h,:]),  f_i = phi(q[b,i,h,:])               (vectors in R^D)
+ *     S[j][c] = sum_n a_n[j] * v[b,n,h,c]     for c < D             (D x D)
+ *     S[j][D] = sum_n a_n[j]                                        (the row of ones
+ *               appended to V makes this extra column the normaliser)
+ *     num_c = sum_j f_i[j] * S[j][c],   den = sum_j f_i[j] * S[j][D]
+ *     out[b,i,h,c] = num_c / (den + eps)                            (eps added to the
+ *               denominator only, after the cast to full precision)
+ *
+ * Block-causal variant (the video form named on the evermx.com SANA page,
+ * section "Model Family", and on the "How Linear Attention ..." page, section
+ * "Video Generation and Constant-Memory KV Cache", which keeps cumulative
+ * statistics per temporal block): the tokens are cut into contiguous blocks of
+ * block_len tokens (the last one may be shorter).  Blocks are visited in order;
+ * block beta's tokens are first added into S, and then block beta's queries are
+ * applied against that S.  So a query in block beta sees every key in blocks
+ * 0..beta (bidirectional inside its own block, causal across blocks).
+ * block_len <= 0, or >= N, is the non-causal operator.
+ *
+ * Arithmetic: every input element is decoded exactly to double (bf16 bits are
+ * the upper half of an IEEE float32), and all sums run sequentially in token
+ * order in double precision.  No blocking or reordering beyond that.
+ *
+ * Layout: q, k, v and out are contiguous [B][N][H][D].
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+
+/* Decode element idx of an array of float32 or of bfloat16 bit patterns. */
+static double load_elem(const void* base, int dtype, size_t idx) {
+    if (dtype == ORACLE_BF16) {
+        uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    return (double)((const float*)base)[idx];
+}
+
+static double relu(double x) { return x > 0.0 ? x : 0.0; }
+
+int oracle_abi_version(void) { return 1; }
+
+/*
+ * out    : [B][N][H][D] doubles (written).
+ * states : optional, [B][H][NB][D][D+1] doubles: S after each block has been
+ *          added (inclusive prefix); NB = number of blocks (1 if non-causal).
+ * nthreads <= 0 leaves the OpenMP default.
+ * Returns 0 on success, -1 on bad arguments.
+ */
+int oracle_linattn_fwd(const void* q, const void* k, const void* v, int in_dtype,
+                       int B, int H, int N, int D, int block_len, double eps,
+                       double* out, double* states, int nthreads) {
+    if (B < 0 || H < 0 || N < 0 || D < 1) return -1;
+    if (in_dtype != ORACLE_F32 && in_dtype != ORACLE_BF16) return -1;
+    if (B == 0 || H == 0 || N == 0) return 0;
+    if (!q || !k || !v || !out) return -1;
+    const int L = (block_len <= 0 || block_len >= N) ? N : block_len;
+    const int NB = (N + L - 1) / L;
+    const int W = D + 1; /* width of a state row: D value columns + normaliser */
+
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* S = (double*)malloc(sizeof(double) * (size_t)D * W);
+        double* a = (double*)malloc(sizeof(double) * (size_t)D);
+        double* f = (double*)malloc(sizeof(double) * (size_t)D);
+        if (!S || !a || !f) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long bh = 0; bh < (long)B * H; ++bh) {
+                const int b = (int)(bh / H), h = (int)(bh % H);
+                memset(S, 0, sizeof(double) * (size_t)D * W);
+                for (int beta = 0; beta < NB; ++beta) {
+                    const int n0 = beta * L;
+                    const int n1 = (n0 + L < N) ? n0 + L : N;
+                    /* add this block's keys and values into the state */
+                    for (int n = n0; n < n1; ++n) {
+                        const size_t row = (((size_t)b * N + n) * H + h) * (size_t)D;
+                        for (int j = 0; j < D; ++j) a[j] = relu(load_elem(k, in_dtype, row + j));
+                        for (int j = 0; j < D; ++j) {
+                            for (int c = 0; c < D; ++c)
+                                S[j * W + c] += a[j] * load_elem(v, in_dtype, row + c);
+                            S[j * W + D] += a[j];
+                        }
+                    }
+                    if (states) {
+                        double* dst = states + (((size_t)b * H + h) * NB + beta) * (size_t)D * W;
+                        memcpy(dst, S, sizeof(double) * (size_t)D * W);
+                    }
+                    /* apply the state to this block's queries */
+                    for (int i = n0; i < n1; ++i) {
+                        const size_t row = (((size_t)b * N + i) * H + h) * (size_t)D;
+                        for (int j = 0; j < D; ++j) f[j] = relu(load_elem(q, in_dtype, row + j));
+                        double den = 0.0;
+                        for (int j = 0; j < D; ++j) den += f[j] * S[j * W + D];
+                        for (int c = 0; c < D; ++c) {
+                            double num = 0.0;
+                            for (int j = 0; j < D; ++j) num += f[j] * S[j * W + c];
+                            out[row + c] = num / (den + eps);
+                        }
+                    }
+                }
+            }
+        }
+        free(S);
+        free(a);
+        free(f);
+    }
+    return failed ? -1 : 0;
+}
+
+/* Number of threads an OpenMP parallel region would use right now. */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

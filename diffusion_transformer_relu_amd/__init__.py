@@ -1,0 +1,173 @@
+"""Python binding of the gfx950 LiteLA forward library (libsana_linattn.so).
+
+Argument marshalling only: every step of the forward runs in the HIP kernels of
+the shared library; PyTorch provides device memory and the stream.  The
+functions below carry the names of the C entry points declared in
+include/sana_linattn.h and raise SanaError on a non-zero status.  If the
+library has not been built, importing this package raises ImportError: there
+is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libsana_linattn.so")
+
+SANA_DT_F32 = 0
+SANA_DT_BF16 = 1
+SANA_OK = 0
+SANA_ERR_INVALID_ARG = 1
+SANA_ERR_UNSUPPORTED = 2
+SANA_ERR_ALIGNMENT = 3
+SANA_ERR_ALIAS = 4
+SANA_ERR_WORKSPACE = 5
+SANA_ERR_HIP = 6
+SANA_STAGE_STATE = 1
+SANA_STAGE_MERGE = 2
+SANA_STAGE_APPLY = 4
+SANA_STAGE_ALL = 7
+
+# name -> (restype, argtypes) of every exported C entry point
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SIGNATURES = {
+    "sana_linattn_abi_version": (_I, []),
+    "sana_linattn_status_string": (ctypes.c_char_p, [_I]),
+    "sana_linattn_workspace_bytes": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]),
+    "sana_linattn_plan_info": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I),
+                                    ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "sana_linattn_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P,
+                              ctypes.c_size_t, _P]),
+    "sana_linattn_blockcausal_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
+                                          _P, ctypes.c_size_t, _P]),
+    "sana_linattn_fwd_stages": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P,
+                                     ctypes.c_size_t, _P, _I]),
+}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                      f"g.build()'` (hipcc, gfx950)")
+
+lib = ctypes.CDLL(LIB_PATH)
+for _name, (_res, _args) in _SIGNATURES.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class SanaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {sana_linattn_status_string(status)} (status {status})")
+
+
+def _check(status: int, where: str):
+    if status != SANA_OK:
+        raise SanaError(status, where)
+
+
+def sana_linattn_abi_version() -> int:
+    return lib.sana_linattn_abi_version()
+
+
+def sana_linattn_status_string(status: int) -> str:
+    return lib.sana_linattn_status_string(status).decode()
+
+
+def sana_linattn_workspace_bytes(B: int, H: int, N: int, D: int, block_len: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.sana_linattn_workspace_bytes(B, H, N, D, block_len, ctypes.byref(out)),
+           "sana_linattn_workspace_bytes")
+    return out.value
+
+
+def sana_linattn_plan_info(in_dtype: int, B: int, H: int, N: int, D: int, block_len: int = 0) -> dict:
+    vals = [ctypes.c_int(0) for _ in range(4)]
+    _check(lib.sana_linattn_plan_info(in_dtype, B, H, N, D, block_len, *[ctypes.byref(x) for x in vals]),
+           "sana_linattn_plan_info")
+    return dict(zip(("chunk_tokens", "num_chunks", "apply_tokens", "mfma"), (x.value for x in vals)))
+
+
+# ------------------------------------------------------------------ torch marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SANA_DT_BF16
+    if t.dtype == torch.float32:
+        return SANA_DT_F32
+    raise TypeError(f"LiteLA tensors are bfloat16 or float32, got {t.dtype}")
+
+
+def _shape(q, k, v, out):
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.dim() != 4 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous 4-d [B, N, H, D] GPU tensor")
+    if not (q.shape == k.shape == v.shape == out.shape):
+        raise ValueError("q, k, v and out must share one [B, N, H, D] shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    B, N, H, D = q.shape
+    return B, N, H, D
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def sana_linattn_fwd(q, k, v, out, workspace, *, eps: float = 1e-15, stream=None):
+    """Non-causal forward into `out` (torch tensors on the GPU; `workspace` a
+    uint8 GPU tensor of at least sana_linattn_workspace_bytes bytes)."""
+    B, N, H, D = _shape(q, k, v, out)
+    _check(lib.sana_linattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dtype_code(q),
+                                dtype_code(out), B, H, N, D, eps, workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream_handle(stream)),
+           "sana_linattn_fwd")
+
+
+def sana_linattn_blockcausal_fwd(q, k, v, out, workspace, block_len: int, *, eps: float = 1e-15,
+                                 stream=None):
+    """Block-causal forward into `out`; block_len >= 1 tokens per block."""
+    B, N, H, D = _shape(q, k, v, out)
+    _check(lib.sana_linattn_blockcausal_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                            dtype_code(q), dtype_code(out), B, H, N, D, block_len, eps,
+                                            workspace.data_ptr(),
+                                            workspace.numel() * workspace.element_size(),
+                                            _stream_handle(stream)),
+           "sana_linattn_blockcausal_fwd")
+
+
+def sana_linattn_fwd_stages(q, k, v, out, workspace, stages: int, *, block_len: int = 0,
+                            eps: float = 1e-15, stream=None):
+    """Runs the selected kernels (SANA_STAGE_* bits) of the forward."""
+    B, N, H, D = _shape(q, k, v, out)
+    _check(lib.sana_linattn_fwd_stages(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                       dtype_code(q), dtype_code(out), B, H, N, D, block_len, eps,
+                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                       _stream_handle(stream), stages),
+           "sana_linattn_fwd_stages")
+
+
+def linattn_fwd(q, k, v, *, eps: float = 1e-15, out_dtype=None, block_len: int | None = None,
+                stream=None):
+    """Allocates `out` (float32 unless out_dtype is given) and the workspace with
+    torch, then runs the non-causal (block_len None) or block-causal forward."""
+    torch = _torch()
+    out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    B, N, H, D = q.shape
+    ws = torch.empty(max(sana_linattn_workspace_bytes(B, H, N, D, block_len or 0), 1),
+                     dtype=torch.uint8, device=q.device)
+    if block_len is None:
+        sana_linattn_fwd(q, k, v, out, ws, eps=eps, stream=stream)
+    else:
+        sana_linattn_blockcausal_fwd(q, k, v, out, ws, block_len, eps=eps, stream=stream)
+    return out

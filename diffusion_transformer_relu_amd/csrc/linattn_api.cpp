@@ -1,0 +1,221 @@
+// C ABI of the LiteLA forward library: argument checks, work decomposition,
+// workspace layout and the enqueueing of the three kernels.  The operator and
+// the conventions are documented in include/sana_linattn.h.
+#include "sana_linattn.h"
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "linattn_internal.h"
+
+using sana::Plan;
+
+namespace {
+
+constexpr int kMaxN = 1 << 30;        // keeps every token index, and N + block_len, in int range
+constexpr int kMaxBH = 1 << 24;       // batch and head counts
+constexpr int kTargetGroups = 1024;   // work-groups wanted per launch (256 CUs x 4)
+
+// Positive integer from the environment, or 0 when unset or not a positive integer.
+int env_positive(const char* name) {
+    const char* s = std::getenv(name);
+    if (!s || !*s) return 0;
+    char* end = nullptr;
+    const long v = std::strtol(s, &end, 10);
+    if (*end != '\0' || v <= 0 || v > kMaxN) return 0;
+    return (int)v;
+}
+
+bool env_is(const char* name, const char* value) {
+    const char* s = std::getenv(name);
+    return s && std::strcmp(s, value) == 0;
+}
+
+int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+long round_up(long a, long m) { return (a + m - 1) / m * m; }
+
+// Decomposition of one call.  Sizes were range-checked by the caller.
+int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block_len, Plan* pl) {
+    if (B < 0 || H < 0 || N < 0 || D < 1 || block_len < 0) return SANA_ERR_INVALID_ARG;
+    if ((in_dtype != SANA_DT_F32 && in_dtype != SANA_DT_BF16) ||
+        (out_dtype != SANA_DT_F32 && out_dtype != SANA_DT_BF16))
+        return SANA_ERR_INVALID_ARG;
+    if (D != sana::kD) return SANA_ERR_UNSUPPORTED;
+    if (N > kMaxN || B > kMaxBH || H > kMaxBH) return SANA_ERR_UNSUPPORTED;
+
+    std::memset(pl, 0, sizeof *pl);
+    pl->B = B;
+    pl->H = H;
+    pl->N = N;
+    pl->in_dtype = in_dtype;
+    pl->out_dtype = out_dtype;
+    if (B == 0 || H == 0 || N == 0) return SANA_OK;   // empty problem, no workspace
+
+    pl->L = (block_len == 0 || block_len >= N) ? N : block_len;
+    pl->NB = ceil_div(N, pl->L);
+    pl->mfma = (in_dtype == SANA_DT_BF16 && !env_is("SANA_LINATTN_PATH", "valu")) ? 1 : 0;
+    pl->HP = pl->mfma ? (H + 1) / 2 : H;
+    const long units = (long)B * pl->HP * pl->NB;   // independent (b, head unit, block) triples
+
+    // State chunk: the largest power-of-two multiple of the LDS tile that still
+    // gives about kTargetGroups work-groups; never longer than a block.
+    int chunk = env_positive("SANA_LINATTN_CHUNK");
+    if (chunk) {
+        chunk = (int)round_up(chunk, sana::kStateTile);
+    } else {
+        chunk = sana::kStateTile;
+        for (int c = 2048; c >= sana::kStateTile; c /= 2) {
+            if (units * ceil_div(pl->L, c) >= kTargetGroups) { chunk = c; break; }
+        }
+    }
+    chunk = (int)std::min<long>(chunk, round_up(pl->L, sana::kStateTile));
+    pl->chunk = chunk;
+    pl->cpb = ceil_div(pl->L, chunk);
+    pl->P = pl->NB * pl->cpb;
+
+    // Apply tile, in tokens per work-group.
+    if (pl->mfma) {
+        int tile = env_positive("SANA_LINATTN_APPLY_TILE");
+        if (tile) {
+            tile = (int)round_up(tile, 64);
+        } else {
+            tile = 64;
+            for (int t = 512; t >= 64; t /= 2) {
+                if (units * ceil_div(pl->L, t) >= kTargetGroups) { tile = t; break; }
+            }
+        }
+        pl->tile = (int)std::min<long>(tile, round_up(pl->L, 64));
+    } else {
+        pl->tile = sana::kValuApplyTokens;
+    }
+    pl->tpb = ceil_div(pl->L, pl->tile);
+
+    // Launch grids are one-dimensional.
+    if ((long)B * pl->HP * pl->P > INT_MAX || units * pl->tpb > INT_MAX || (long)B * H > INT_MAX)
+        return SANA_ERR_UNSUPPORTED;
+
+    const size_t bh = (size_t)B * H;
+    size_t off = 0;
+    pl->off_part = off;
+    off += round_up((long)(bh * pl->P * sana::kStateFloats * sizeof(float)), 256);
+    pl->off_state = off;
+    off += round_up((long)(bh * pl->NB * sana::kStateFloats * sizeof(float)), 256);
+    pl->off_pack = off;
+    off += round_up((long)(bh * pl->NB * sana::kPackBytes), 256);
+    pl->bytes = off;
+    return SANA_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return na && nb && x < y + nb && y < x + na;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int forward(const void* q, const void* k, const void* v, void* out, int in_dtype, int out_dtype,
+            int B, int H, int N, int D, int block_len, float eps, void* workspace,
+            size_t workspace_bytes, hipStream_t stream, int stages) {
+    Plan pl;
+    const int st = make_plan(in_dtype, out_dtype, B, H, N, D, block_len, &pl);
+    if (st != SANA_OK) return st;
+    if (!std::isfinite(eps) || eps < 0.f) return SANA_ERR_INVALID_ARG;
+    if (stages <= 0 || (stages & ~SANA_STAGE_ALL)) return SANA_ERR_INVALID_ARG;
+    if (B == 0 || H == 0 || N == 0) return SANA_OK;
+    if (!q || !k || !v || !out || !workspace) return SANA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(workspace, 256))
+        return SANA_ERR_ALIGNMENT;
+    const size_t elems = (size_t)B * N * H * D;
+    const size_t in_bytes = elems * (in_dtype == SANA_DT_BF16 ? 2 : 4);
+    const size_t out_bytes = elems * (out_dtype == SANA_DT_BF16 ? 2 : 4);
+    if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, k, in_bytes) ||
+        overlaps(out, out_bytes, v, in_bytes))
+        return SANA_ERR_ALIAS;
+    if (overlaps(workspace, pl.bytes, q, in_bytes) || overlaps(workspace, pl.bytes, k, in_bytes) ||
+        overlaps(workspace, pl.bytes, v, in_bytes) || overlaps(workspace, pl.bytes, out, out_bytes))
+        return SANA_ERR_ALIAS;
+    if (workspace_bytes < pl.bytes) return SANA_ERR_WORKSPACE;
+
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    float* part = reinterpret_cast<float*>(ws + pl.off_part);
+    float* state = reinterpret_cast<float*>(ws + pl.off_state);
+    uint8_t* pack = ws + pl.off_pack;
+    if ((stages & SANA_STAGE_STATE) && sana::launch_state(pl, k, v, part, stream) != hipSuccess)
+        return SANA_ERR_HIP;
+    if ((stages & SANA_STAGE_MERGE) && sana::launch_merge(pl, part, state, pack, stream) != hipSuccess)
+        return SANA_ERR_HIP;
+    if ((stages & SANA_STAGE_APPLY) && sana::launch_apply(pl, q, state, pack, out, eps, stream) != hipSuccess)
+        return SANA_ERR_HIP;
+    return SANA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sana_linattn_abi_version(void) { return SANA_LINATTN_ABI_VERSION; }
+
+const char* sana_linattn_status_string(int status) {
+    switch (status) {
+        case SANA_OK: return "success";
+        case SANA_ERR_INVALID_ARG: return "invalid argument";
+        case SANA_ERR_UNSUPPORTED: return "unsupported size or head dim (D must be 32)";
+        case SANA_ERR_ALIGNMENT: return "misaligned pointer (tensors need 16 bytes, workspace 256)";
+        case SANA_ERR_ALIAS: return "output or workspace overlaps another buffer";
+        case SANA_ERR_WORKSPACE: return "workspace too small";
+        case SANA_ERR_HIP: return "HIP runtime error while enqueueing";
+        default: return "unknown status";
+    }
+}
+
+int sana_linattn_workspace_bytes(int B, int H, int N, int D, int block_len, size_t* bytes) {
+    if (!bytes) return SANA_ERR_INVALID_ARG;
+    Plan pl;
+    const int st = make_plan(SANA_DT_BF16, SANA_DT_F32, B, H, N, D, block_len, &pl);
+    if (st != SANA_OK) return st;
+    // The vector path (fp32 inputs) needs at least as much; report the larger.
+    Plan pv;
+    make_plan(SANA_DT_F32, SANA_DT_F32, B, H, N, D, block_len, &pv);
+    *bytes = pl.bytes > pv.bytes ? pl.bytes : pv.bytes;
+    return SANA_OK;
+}
+
+int sana_linattn_plan_info(int in_dtype, int B, int H, int N, int D, int block_len, int* chunk_tokens,
+                           int* num_chunks, int* apply_tokens, int* mfma) {
+    Plan pl;
+    const int st = make_plan(in_dtype, SANA_DT_F32, B, H, N, D, block_len, &pl);
+    if (st != SANA_OK) return st;
+    if (chunk_tokens) *chunk_tokens = pl.chunk;
+    if (num_chunks) *num_chunks = pl.P;
+    if (apply_tokens) *apply_tokens = pl.tile;
+    if (mfma) *mfma = pl.mfma;
+    return SANA_OK;
+}
+
+int sana_linattn_fwd(const void* q, const void* k, const void* v, void* out, int in_dtype, int out_dtype,
+                     int B, int H, int N, int D, float eps, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+    return forward(q, k, v, out, in_dtype, out_dtype, B, H, N, D, 0, eps, workspace, workspace_bytes,
+                   stream, SANA_STAGE_ALL);
+}
+
+int sana_linattn_blockcausal_fwd(const void* q, const void* k, const void* v, void* out, int in_dtype,
+                                 int out_dtype, int B, int H, int N, int D, int block_len, float eps,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (block_len < 1) return SANA_ERR_INVALID_ARG;
+    return forward(q, k, v, out, in_dtype, out_dtype, B, H, N, D, block_len, eps, workspace,
+                   workspace_bytes, stream, SANA_STAGE_ALL);
+}
+
+int sana_linattn_fwd_stages(const void* q, const void* k, const void* v, void* out, int in_dtype,
+                            int out_dtype, int B, int H, int N, int D, int block_len, float eps,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream, int stages) {
+    return forward(q, k, v, out, in_dtype, out_dtype, B, H, N, D, block_len, eps, workspace,
+                   workspace_bytes, stream, stages);
+}
+
+}  // extern "C"

@@ -1,0 +1,432 @@
+// gfx950 kernels of the LiteLA forward (ReLU-kernel linear self-attention).
+//
+// The operator ("Sana: the autoencoder does more of the work than the linear
+// attention", section "What LiteLA actually computes"): per (batch, head) a
+// D x (D+1) state S = phi(K)^T [V | 1] with phi = ReLU, then
+// out_i = phi(q_i) S[:, :D] / (phi(q_i) S[:, D] + eps), all in fp32.
+// The pages compute it with two library matmuls on a ones-padded copy of V;
+// here it is three kernels on one stream and nothing is padded or copied:
+//
+//   1. state  (k_state_partial_*) - each work-group reduces one chunk of tokens
+//      of one head pair into a partial state; ReLU and the ones column are fused
+//      into the reduction.  bf16 inputs use v_mfma_f32_32x32x16_bf16 with the
+//      tokens as the reduction dimension (bf16 x bf16 products are exact in
+//      fp32); K/V tiles are staged through LDS to turn the token-major HBM rows
+//      into token-packed matrix operands.
+//   2. merge  (k_merge) - one work-group per (b, h) sums the partials in a fixed
+//      order (deterministic, no atomics).  For the block-causal operator it also
+//      forms the inclusive prefix over blocks ("cumulative statistics per
+//      temporal block", "How Linear Attention Improves Efficiency in DiT for
+//      High-Resolution Images", section "Video Generation and Constant-Memory KV
+//      Cache").  It writes the fp32 state and a bf16 hi/mid/lo operand pack for
+//      the apply kernel.
+//   3. apply  (k_apply_*) - q rows go straight from HBM into the A operand of
+//      the same MFMA (the feature axis is already contiguous); three bf16 split
+//      terms of S reproduce the fp32 state to ~2^-24, so numerator and
+//      normaliser keep fp32 accuracy, as the pages' fp32 attention policy asks.
+//
+// fp32 inputs take the vector kernels (k_*_valu), which also serve as a second
+// implementation for cross-checks.
+#include "linattn_internal.h"
+
+namespace sana {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// ReLU on two packed bf16: for the sign test a bf16 orders like an int16, so
+// max(x, 0) as int16 keeps positives and maps negatives (and -0) to +0.
+__device__ __forceinline__ uint32_t relu_bf16x2(uint32_t x) {
+    s16x2 s = __builtin_bit_cast(s16x2, x);
+    s = __builtin_elementwise_max(s, (s16x2){0, 0});
+    return __builtin_bit_cast(uint32_t, s);
+}
+
+__device__ __forceinline__ u32x4 relu_bf16x8(u32x4 x) {
+    return (u32x4){relu_bf16x2(x[0]), relu_bf16x2(x[1]), relu_bf16x2(x[2]), relu_bf16x2(x[3])};
+}
+
+__device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+// Round to nearest, ties to even (finite inputs; NaN is kept a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float load_in(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float load_in(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+
+__device__ __forceinline__ void store_out(float* p, size_t i, float x) { p[i] = x; }
+__device__ __forceinline__ void store_out(uint16_t* p, size_t i, float x) { p[i] = f32_to_bf16(x); }
+
+// Token range [c0, c1) of chunk p of a (b, head) unit.
+struct ChunkRange { int c0, c1; };
+__device__ __forceinline__ ChunkRange chunk_range(int p, int cpb, int chunk, int L, int N) {
+    const int beta = p / cpb, s = p - beta * cpb;
+    const int blk0 = beta * L;
+    const int blk1 = min(blk0 + L, N);
+    const int c0 = blk0 + s * chunk;
+    return {c0, min(c0 + chunk, blk1)};
+}
+
+// ------------------------------------------------------------------ state, bf16, MFMA
+// LDS tile: [tensor K|V][head 0|1][token 0..127][32 x bf16]; the second head's
+// rows are shifted by 64 bytes so that a 16-byte write from each head of one
+// token lands in different banks.
+constexpr int kHeadStride = kStateTile * 64 + 64;   // bytes
+constexpr int kTensorStride = 2 * kHeadStride;
+
+// grid.x = (b * HP + hp) * P + p; one work-group = one chunk of one head pair.
+// Wave w reduces head (w & 1) over token half (w >> 1) of each 128-token tile.
+__global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ part,
+    int N, int H, int HP, int L, int cpb, int P, int chunk) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kTensorStride];
+
+    const int p = blockIdx.x % P;
+    const int bhp = blockIdx.x / P;
+    const int hp = bhp % HP, b = bhp / HP;
+    const int h0 = 2 * hp;
+    const int nh = min(2, H - h0);
+    const ChunkRange cr = chunk_range(p, cpb, chunk, L, N);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hh = wave & 1, th = wave >> 1;
+
+    // Global -> register assignment: 16-byte piece id = tid + 256 i; piece
+    // (tok, head, part) covers features 8*part..8*part+7 of one head of one
+    // token, so a wave reads 8 whole 128-byte rows (both heads of 8 tokens).
+    u32x4 rk[4], rv[4];
+    auto load_tile = [&](int t0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int pc = tid + kThreads * i;
+            const int part_ = pc & 3, hd = (pc >> 2) & 1, tok = pc >> 3;
+            const int n = t0 + tok;
+            if (n < cr.c1 && hd < nh) {
+                const size_t off = (((size_t)b * N + n) * H + h0 + hd) * kD + part_ * 8;
+                rk[i] = *reinterpret_cast<const u32x4*>(k + off);
+                rv[i] = *reinterpret_cast<const u32x4*>(v + off);
+            } else {
+                rk[i] = (u32x4){0u, 0u, 0u, 0u};
+                rv[i] = (u32x4){0u, 0u, 0u, 0u};
+            }
+        }
+    };
+
+    f32x16 accV = {}, accO = {};
+    const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0 pairs
+    const int g = lane >> 5, j = lane & 31;
+
+    if (cr.c0 < cr.c1) load_tile(cr.c0);
+    for (int t0 = cr.c0; t0 < cr.c1; t0 += kStateTile) {
+        __syncthreads();   // the previous tile has been consumed
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int pc = tid + kThreads * i;
+            const int part_ = pc & 3, hd = (pc >> 2) & 1, tok = pc >> 3;
+            const int o = hd * kHeadStride + tok * 64 + part_ * 16;
+            *reinterpret_cast<u32x4*>(lds + o) = relu_bf16x8(rk[i]);
+            *reinterpret_cast<u32x4*>(lds + kTensorStride + o) = rv[i];
+        }
+        __syncthreads();
+        if (t0 + kStateTile < cr.c1) load_tile(t0 + kStateTile);   // in flight during the MFMAs
+
+        const uint16_t* Kt = reinterpret_cast<const uint16_t*>(lds + hh * kHeadStride);
+        const uint16_t* Vt = reinterpret_cast<const uint16_t*>(lds + kTensorStride + hh * kHeadStride);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            // 16 tokens per MFMA; element e of lane (g, j) is token tb + 2e + g,
+            // the same token for the K (row j) and the V (column j) operand.
+            const int tb = 64 * th + 16 * st;
+            u32x4 a, bv;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int r0 = (tb + 4 * t + g) * 32 + j;
+                const int r1 = r0 + 2 * 32;
+                a[t] = (uint32_t)Kt[r0] | ((uint32_t)Kt[r1] << 16);
+                bv[t] = (uint32_t)Vt[r0] | ((uint32_t)Vt[r1] << 16);
+            }
+            accV = mfma_bf16(a, bv, accV);
+            accO = mfma_bf16(a, ones, accO);
+        }
+    }
+
+    // Combine the two token halves of each head in a fixed order, then write.
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(lds);   // [head][V|O][16][64] floats = 16 KiB
+    if (th == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            red[((hh * 2 + 0) * 16 + r) * 64 + lane] = accV[r];
+            red[((hh * 2 + 1) * 16 + r) * 64 + lane] = accO[r];
+        }
+    }
+    __syncthreads();
+    if (th == 0 && hh < nh) {
+        float* dst = part + (((size_t)b * H + h0 + hh) * P + p) * kStateFloats;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            // accumulator r of lane (g, c) holds row 8*(r/4) + 4*g + r%4, column c
+            const int row = 8 * (r >> 2) + 4 * g + (r & 3);
+            dst[row * kW + j] = accV[r] + red[((hh * 2 + 0) * 16 + r) * 64 + lane];
+            if (j == 0) dst[row * kW + kD] = accO[r] + red[((hh * 2 + 1) * 16 + r) * 64 + lane];
+        }
+    }
+}
+
+// ------------------------------------------------------------------ state, vector path
+// grid.x = (b * H + h) * P + p.  Thread t owns state entries t, t+256, ... (5 at most).
+template <typename InT>
+__global__ __launch_bounds__(kThreads) void k_state_partial_valu(
+    const InT* __restrict__ k, const InT* __restrict__ v, float* __restrict__ part,
+    int N, int H, int L, int cpb, int P, int chunk) {
+    __shared__ float sa[kValuTile][kD + 1];   // ReLU(k) tile
+    __shared__ float sv[kValuTile][kW];       // [v | 1] tile
+
+    const int p = blockIdx.x % P;
+    const int bh = blockIdx.x / P;
+    const int h = bh % H, b = bh / H;
+    const ChunkRange cr = chunk_range(p, cpb, chunk, L, N);
+    const int tid = threadIdx.x;
+
+    float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int t0 = cr.c0; t0 < cr.c1; t0 += kValuTile) {
+        __syncthreads();
+        for (int e = tid; e < kValuTile * kD; e += kThreads) {
+            const int tok = e >> 5, jj = e & 31;
+            const int n = t0 + tok;
+            float kk = 0.f, vv = 0.f;
+            if (n < cr.c1) {
+                const size_t off = (((size_t)b * N + n) * H + h) * kD + jj;
+                kk = load_in(k, off);
+                vv = load_in(v, off);
+            }
+            sa[tok][jj] = kk > 0.f ? kk : 0.f;
+            sv[tok][jj] = vv;
+        }
+        if (tid < kValuTile) sv[tid][kD] = 1.f;
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < 5; ++m) {
+            const int o = tid + kThreads * m;
+            if (o < kStateFloats) {
+                const int jj = o / kW, c = o - jj * kW;
+                float s = acc[m];
+                for (int tok = 0; tok < kValuTile; ++tok) s += sa[tok][jj] * sv[tok][c];
+                acc[m] = s;
+            }
+        }
+    }
+    float* dst = part + ((size_t)bh * P + p) * kStateFloats;
+#pragma unroll
+    for (int m = 0; m < 5; ++m) {
+        const int o = tid + kThreads * m;
+        if (o < kStateFloats) dst[o] = acc[m];
+    }
+}
+
+// ------------------------------------------------------------------ merge / block scan
+// grid.x = b * H + h.  Sums the partials of each block in chunk order, carries
+// the running sum across blocks (inclusive prefix) and writes, per block, the
+// fp32 state and the bf16 split operand pack.
+__global__ __launch_bounds__(kThreads) void k_merge(
+    const float* __restrict__ part, float* __restrict__ state, uint8_t* __restrict__ pack,
+    int NB, int cpb, int P) {
+    const size_t bh = blockIdx.x;
+    const float* src = part + bh * P * kStateFloats;
+    for (int e = threadIdx.x; e < kStateFloats; e += kThreads) {
+        const int j = e / kW, c = e - j * kW;
+        const int ks = j >> 4, g = (j >> 3) & 1, el = j & 7;
+        float acc = 0.f;
+        for (int beta = 0; beta < NB; ++beta) {
+            for (int s = 0; s < cpb; ++s) acc += src[(size_t)(beta * cpb + s) * kStateFloats + e];
+            state[(bh * NB + beta) * kStateFloats + e] = acc;
+            // acc = hi + mid + lo; each remainder is exact in fp32
+            uint16_t sp[3];
+            float r = acc;
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                sp[i] = f32_to_bf16(r);
+                r -= bf16_to_f32(sp[i]);
+            }
+            uint8_t* pk = pack + (bh * NB + beta) * kPackBytes;
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                const int o = (c < kD) ? ((ks * 3 + i) * 64 + g * 32 + c) * 16 + el * 2
+                                       : kPackValueBytes + ((ks * 3 + i) * 2 + g) * 16 + el * 2;
+                *reinterpret_cast<uint16_t*>(pk + o) = sp[i];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ apply, bf16, MFMA
+// grid.x = (b * HP + hp) * (NB * tpb) + beta * tpb + tile.  Wave w handles head
+// 2*hp + (w & 1) and every other 32-token sub-tile (w >> 1) of the work-group's
+// token range, which never crosses a block boundary.
+template <typename OutT>
+__global__ __launch_bounds__(kThreads) void k_apply_mfma(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ pack, OutT* __restrict__ out,
+    int N, int H, int HP, int L, int NB, int tile, int tpb, float eps) {
+    const int per_unit = NB * tpb;
+    const int tau = blockIdx.x % per_unit;
+    const int bhp = blockIdx.x / per_unit;
+    const int hp = bhp % HP, b = bhp / HP;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int h = 2 * hp + (wave & 1);
+    const int sub = wave >> 1;
+    if (h >= H) return;
+    const int beta = tau / tpb, tib = tau - beta * tpb;
+    const int blk0 = beta * L;
+    const int blk1 = min(blk0 + L, N);
+    const int t0 = blk0 + tib * tile;
+    const int t1 = min(t0 + tile, blk1);
+    if (t0 >= t1) return;
+
+    const int g = lane >> 5, c = lane & 31;
+    const uint8_t* pk = pack + (((size_t)b * H + h) * NB + beta) * kPackBytes;
+    u32x4 nb[2][3], db[2][3];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            nb[ks][i] = *reinterpret_cast<const u32x4*>(pk + ((ks * 3 + i) * 64 + lane) * 16);
+            db[ks][i] = *reinterpret_cast<const u32x4*>(pk + kPackValueBytes + ((ks * 3 + i) * 2 + g) * 16);
+        }
+
+    for (int tt = t0 + 32 * sub; tt < t1; tt += 64) {
+        // A operand: row c of the sub-tile, features 8g..8g+7 (ks 0) and 16+8g.. (ks 1)
+        const int row = tt + c;
+        u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
+        if (row < t1) {
+            const uint16_t* src = q + (((size_t)b * N + row) * H + h) * kD + 8 * g;
+            a0 = relu_bf16x8(*reinterpret_cast<const u32x4*>(src));
+            a1 = relu_bf16x8(*reinterpret_cast<const u32x4*>(src + 16));
+        }
+        f32x16 an = {}, ad = {};
+#pragma unroll
+        for (int i = 2; i >= 0; --i) {   // small split terms first
+            an = mfma_bf16(a0, nb[0][i], an);
+            ad = mfma_bf16(a0, db[0][i], ad);
+            an = mfma_bf16(a1, nb[1][i], an);
+            ad = mfma_bf16(a1, db[1][i], ad);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int orow = tt + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (orow < t1) {
+                const float o = an[r] * __builtin_amdgcn_rcpf(ad[r] + eps);
+                store_out(out, (((size_t)b * N + orow) * H + h) * kD + c, o);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ apply, vector path
+// grid.x = ((b * H + h) * NB + beta) * tpb + tile; one thread per token.
+template <typename InT, typename OutT>
+__global__ __launch_bounds__(kThreads) void k_apply_valu(
+    const InT* __restrict__ q, const float* __restrict__ state, OutT* __restrict__ out,
+    int N, int H, int L, int NB, int tpb, float eps) {
+    __shared__ float s[kStateFloats];
+    const int tile = blockIdx.x % tpb;
+    const size_t bhb = blockIdx.x / tpb;            // (b * H + h) * NB + beta
+    const int beta = (int)(bhb % NB);
+    const size_t bh = bhb / NB;
+    const int h = (int)(bh % H), b = (int)(bh / H);
+    for (int e = threadIdx.x; e < kStateFloats; e += kThreads) s[e] = state[bhb * kStateFloats + e];
+    __syncthreads();
+    const int blk0 = beta * L;
+    const int blk1 = min(blk0 + L, N);
+    const int row = blk0 + tile * kValuApplyTokens + threadIdx.x;
+    if (row >= blk1) return;
+    const size_t base = (((size_t)b * N + row) * H + h) * kD;
+    float f[kD];
+#pragma unroll
+    for (int jj = 0; jj < kD; ++jj) {
+        const float x = load_in(q, base + jj);
+        f[jj] = x > 0.f ? x : 0.f;
+    }
+    float den = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < kD; ++jj) den += f[jj] * s[jj * kW + kD];
+    for (int cc = 0; cc < kD; ++cc) {
+        float num = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < kD; ++jj) num += f[jj] * s[jj * kW + cc];
+        store_out(out, base + cc, num / (den + eps));
+    }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_state(const Plan& pl, const void* k, const void* v, float* part, hipStream_t stream) {
+    if (pl.mfma) {
+        const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.P);
+        hipLaunchKernelGGL(k_state_partial_mfma, dim3(grid), dim3(kThreads), 0, stream,
+                           static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), part,
+                           pl.N, pl.H, pl.HP, pl.L, pl.cpb, pl.P, pl.chunk);
+    } else {
+        const unsigned grid = (unsigned)((size_t)pl.B * pl.H * pl.P);
+        if (pl.in_dtype == 1)
+            hipLaunchKernelGGL(k_state_partial_valu<uint16_t>, dim3(grid), dim3(kThreads), 0, stream,
+                               static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), part,
+                               pl.N, pl.H, pl.L, pl.cpb, pl.P, pl.chunk);
+        else
+            hipLaunchKernelGGL(k_state_partial_valu<float>, dim3(grid), dim3(kThreads), 0, stream,
+                               static_cast<const float*>(k), static_cast<const float*>(v), part,
+                               pl.N, pl.H, pl.L, pl.cpb, pl.P, pl.chunk);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const Plan& pl, const float* part, float* state, uint8_t* pack, hipStream_t stream) {
+    const unsigned grid = (unsigned)((size_t)pl.B * pl.H);
+    hipLaunchKernelGGL(k_merge, dim3(grid), dim3(kThreads), 0, stream, part, state, pack, pl.NB, pl.cpb, pl.P);
+    return hipGetLastError();
+}
+
+hipError_t launch_apply(const Plan& pl, const void* q, const float* state, const uint8_t* pack,
+                        void* out, float eps, hipStream_t stream) {
+    const bool out_bf16 = pl.out_dtype == 1;
+    if (pl.mfma) {
+        const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.NB * pl.tpb);
+        const uint16_t* qq = static_cast<const uint16_t*>(q);
+        if (out_bf16)
+            hipLaunchKernelGGL(k_apply_mfma<uint16_t>, dim3(grid), dim3(kThreads), 0, stream, qq, pack,
+                               static_cast<uint16_t*>(out), pl.N, pl.H, pl.HP, pl.L, pl.NB, pl.tile, pl.tpb, eps);
+        else
+            hipLaunchKernelGGL(k_apply_mfma<float>, dim3(grid), dim3(kThreads), 0, stream, qq, pack,
+                               static_cast<float*>(out), pl.N, pl.H, pl.HP, pl.L, pl.NB, pl.tile, pl.tpb, eps);
+    } else {
+        const unsigned grid = (unsigned)((size_t)pl.B * pl.H * pl.NB * pl.tpb);
+#define SANA_APPLY_VALU(IT, OT)                                                                        \
+    hipLaunchKernelGGL((k_apply_valu<IT, OT>), dim3(grid), dim3(kThreads), 0, stream,                   \
+                       static_cast<const IT*>(q), state, static_cast<OT*>(out), pl.N, pl.H, pl.L, pl.NB, \
+                       pl.tpb, eps)
+        if (pl.in_dtype == 1) {
+            if (out_bf16) SANA_APPLY_VALU(uint16_t, uint16_t); else SANA_APPLY_VALU(uint16_t, float);
+        } else {
+            if (out_bf16) SANA_APPLY_VALU(float, uint16_t); else SANA_APPLY_VALU(float, float);
+        }
+#undef SANA_APPLY_VALU
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sana

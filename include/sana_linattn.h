@@ -1,0 +1,171 @@
+/*
+ * sana_linattn.h -- C ABI of the MI355X (gfx950) LiteLA forward library.
+ *
+ * LiteLA is the ReLU-kernel linear self-attention of the Sana diffusion
+ * transformer.  The operation is defined on "Sana: the autoencoder does more of
+ * the work than the linear attention", section "What LiteLA actually computes"
+ * (ReLU feature map on q and k, V padded with a row of ones so that one state
+ * carries numerator and normaliser, cast to fp32, then divide by the normaliser
+ * plus eps), and on "How Linear Attention Improves Efficiency in DiT for
+ * High-Resolution Images", sections "Mathematical Foundation" and
+ * "Implementation Details".  For every batch b and head h, with phi = ReLU:
+ *
+ *     S[j][c] = sum_n phi(k[b,n,h,j]) * v[b,n,h,c]    (c < D)
+ *     S[j][D] = sum_n phi(k[b,n,h,j])
+ *     out[b,i,h,c] = (sum_j phi(q[b,i,h,j]) S[j][c]) / (sum_j phi(q[b,i,h,j]) S[j][D] + eps)
+ *
+ * The block-causal variant is the video form ("block causal linear attention",
+ * evermx.com SANA page, section "Model Family"; cumulative statistics per
+ * temporal block, "How Linear Attention ..." page, section "Video Generation
+ * and Constant-Memory KV Cache"): tokens are cut into contiguous blocks of
+ * block_len tokens (the last block may be shorter) and a query in block beta
+ * uses the state summed over the keys of blocks 0..beta.
+ *
+ * Conventions shared by every entry point below
+ * ---------------------------------------------
+ * Layout     q, k, v and out are contiguous row-major [B][N][H][D] arrays.
+ *            q and k are taken before the feature map: the library applies
+ *            ReLU itself (ReLU is idempotent, so already-activated inputs give
+ *            the same result).
+ * Dtypes     q, k and v share in_dtype; out has its own out_dtype.  All
+ *            accumulation is fp32.  A bf16 out is the fp32 result rounded to
+ *            nearest-even.  D must be 32 (the Sana head dim).
+ * Memory     Every pointer is device memory on the current HIP device, owned
+ *            by the caller.  The library allocates nothing, keeps nothing
+ *            after return, and never synchronises: work is enqueued on
+ *            `stream` (0 = the null stream) and the call returns at once.
+ *            Scratch space is the caller's `workspace`, sized by
+ *            sana_linattn_workspace_bytes(); its contents on entry do not
+ *            matter.  Two calls that run concurrently must not share a
+ *            workspace.  There is no global mutable state; calls are
+ *            re-entrant and thread-safe.
+ * Errors     Every argument is checked before anything is enqueued; on a
+ *            failed check nothing is enqueued and a sana_status_t code is
+ *            returned.  The library never aborts or prints.  A launch failure
+ *            reported by hipGetLastError() maps to SANA_ERR_HIP.
+ * Empty      B, H or N equal to 0 is a valid empty problem: SANA_OK, nothing
+ *            enqueued, no pointer dereferenced.
+ * Results    For fixed arguments and tuning the results are bitwise
+ *            repeatable (fixed-order reductions, no atomics).
+ */
+#ifndef SANA_LINATTN_H
+#define SANA_LINATTN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SANA_LINATTN_ABI_VERSION 1
+
+/* Symbols of this header are the only ones the shared library exports. */
+#if defined(__GNUC__) || defined(__clang__)
+#define SANA_API __attribute__((visibility("default")))
+#else
+#define SANA_API
+#endif
+
+typedef enum {
+    SANA_DT_F32 = 0,   /* IEEE float32 */
+    SANA_DT_BF16 = 1   /* bfloat16 (upper half of a float32) */
+} sana_dtype_t;
+
+typedef enum {
+    SANA_OK = 0,
+    SANA_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad dtype code,
+                                  eps non-finite or < 0, block_len < 1, unknown stage bit */
+    SANA_ERR_UNSUPPORTED = 2,  /* D != 32, or sizes beyond what the launch grid covers */
+    SANA_ERR_ALIGNMENT = 3,    /* q, k, v, out not 16-byte aligned, workspace not 256-byte aligned */
+    SANA_ERR_ALIAS = 4,        /* out or workspace overlaps an input, or each other */
+    SANA_ERR_WORKSPACE = 5,    /* workspace_bytes smaller than required */
+    SANA_ERR_HIP = 6           /* a HIP runtime error while enqueueing */
+} sana_status_t;
+
+/* Stage bits for sana_linattn_fwd_stages(). */
+#define SANA_STAGE_STATE 1  /* per-chunk partial states from k, v */
+#define SANA_STAGE_MERGE 2  /* fixed-order sum of the partials (and per-block prefix) */
+#define SANA_STAGE_APPLY 4  /* out from q and the merged state */
+#define SANA_STAGE_ALL   7
+
+/* Returns SANA_LINATTN_ABI_VERSION of the built library. */
+SANA_API int sana_linattn_abi_version(void);
+
+/* Static, NUL-terminated description of a status code ("unknown status" for
+ * values outside sana_status_t).  Never NULL. */
+SANA_API const char* sana_linattn_status_string(int status);
+
+/*
+ * Workspace needed by a call with these sizes.  block_len = 0 means the
+ * non-causal operator; otherwise it is the block length of the block-causal
+ * operator (a block_len >= N needs the same workspace as non-causal).
+ * Writes the byte count to *bytes (0 for an empty problem).  The answer
+ * depends on the tuning environment variables read by the library
+ * (SANA_LINATTN_CHUNK, SANA_LINATTN_APPLY_TILE, SANA_LINATTN_PATH), so query it
+ * in the same environment as the call.
+ * Errors: INVALID_ARG (bytes NULL, negative sizes, block_len < 0),
+ * UNSUPPORTED (D != 32, sizes too large).
+ */
+SANA_API int sana_linattn_workspace_bytes(int B, int H, int N, int D, int block_len, size_t* bytes);
+
+/*
+ * How a call with these sizes is decomposed (for tests and benchmarks).  Any
+ * output pointer may be NULL.
+ *   chunk_tokens  tokens per state-reduction chunk
+ *   num_chunks    chunks per (batch, head) across all blocks
+ *   apply_tokens  tokens per apply work-group
+ *   mfma          1 if the bf16 matrix-core path is used, 0 for the vector path
+ * Errors as for sana_linattn_workspace_bytes (in_dtype must be a valid code).
+ */
+SANA_API int sana_linattn_plan_info(int in_dtype, int B, int H, int N, int D, int block_len,
+                           int* chunk_tokens, int* num_chunks, int* apply_tokens, int* mfma);
+
+/*
+ * Non-causal LiteLA forward ("What LiteLA actually computes").
+ *   q, k, v    [B][N][H][D] in in_dtype, device, read only.
+ *   out        [B][N][H][D] in out_dtype, device, written; must not overlap
+ *              q, k, v or the workspace.
+ *   eps        added to the normaliser; finite and >= 0 (Sana uses a tiny
+ *              positive value; with eps = 0 a row whose normaliser is 0 gives
+ *              0/0 = NaN).
+ *   workspace  device scratch of at least
+ *              sana_linattn_workspace_bytes(B, H, N, D, 0) bytes.
+ */
+SANA_API int sana_linattn_fwd(const void* q, const void* k, const void* v, void* out,
+                     int in_dtype, int out_dtype, int B, int H, int N, int D, float eps,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Block-causal LiteLA forward: token i in block beta = i / block_len uses the
+ * state of the keys in blocks 0..beta (inclusive prefix; full attention inside
+ * the block).  block_len >= 1; block_len >= N equals sana_linattn_fwd.
+ * Arguments otherwise as for sana_linattn_fwd; the workspace is
+ * sana_linattn_workspace_bytes(B, H, N, D, block_len) bytes.
+ */
+SANA_API int sana_linattn_blockcausal_fwd(const void* q, const void* k, const void* v, void* out,
+                                 int in_dtype, int out_dtype, int B, int H, int N, int D,
+                                 int block_len, float eps,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The same forward split into its three kernels, for per-kernel timing: a call
+ * runs the stages whose bits are set in `stages`, in the order state, merge,
+ * apply.  Calling it three times with SANA_STAGE_STATE, SANA_STAGE_MERGE and
+ * SANA_STAGE_APPLY on one stream and one workspace produces the same bytes as
+ * one call with SANA_STAGE_ALL.  block_len = 0 selects the non-causal
+ * operator.  The merge stage reads what the state stage left in the
+ * workspace, and the apply stage what the merge stage left.  All arguments
+ * are checked on every call, whatever the stages.
+ */
+SANA_API int sana_linattn_fwd_stages(const void* q, const void* k, const void* v, void* out,
+                            int in_dtype, int out_dtype, int B, int H, int N, int D,
+                            int block_len, float eps,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream,
+                            int stages);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SANA_LINATTN_H */

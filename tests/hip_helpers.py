@@ -1,0 +1,62 @@
+"""Shared helpers of the GPU tests: upload seeded inputs, run the C ABI, compare
+with the fp64 oracle.  Not collected by pytest (no test_ prefix)."""
+import functools
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+
+# Parity bar: max-abs error <= 2e-3 * max|V| and relative L2 <= 1e-4, element by
+# element against the fp64 oracle on the same inputs.
+MAX_ABS_FRAC = 2e-3
+REL_L2 = 1e-4
+
+
+def to_device(a: np.ndarray) -> torch.Tensor:
+    t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 else torch.from_numpy(a)
+    return t.to("cuda:0")
+
+
+def decode(a: np.ndarray) -> np.ndarray:
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+@functools.lru_cache(maxsize=8)
+def inputs_and_oracle(w: workloads.Workload):
+    q, k, v = workloads.make_inputs(w)
+    want = oracle.linattn_fwd(q, k, v, block_len=w.block_len, eps=w.eps)
+    return (q, k, v), want
+
+
+def bf16_round(x64: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(x64).float().to(torch.bfloat16).double().numpy()
+
+
+def compare(got: np.ndarray, want: np.ndarray, v: np.ndarray, out_bf16: bool, label: str = ""):
+    """Returns (max_abs, rel_l2) and asserts the parity bar."""
+    vmax = np.max(np.abs(decode(v))) if v.size else 1.0
+    ref = bf16_round(want) if out_bf16 else want
+    diff = got - ref
+    max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    norm = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(diff) / norm) if norm > 0 else float(np.linalg.norm(diff))
+    assert np.all(np.isfinite(got)), label
+    assert max_abs <= MAX_ABS_FRAC * vmax, f"{label}: max abs {max_abs:.3e} > {MAX_ABS_FRAC}*{vmax:.3e}"
+    assert rel <= REL_L2, f"{label}: rel L2 {rel:.3e} > {REL_L2}"
+    if out_bf16:
+        # a bf16 result is within one bf16 ulp of the exact value
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(want), 1e-300))) - 7)
+        assert np.all(np.abs(got - want) <= ulp * 1.0001 + 1e-30), f"{label}: beyond one bf16 ulp"
+    return max_abs, rel
+
+
+def run_hip(q_np, k_np, v_np, *, block_len=0, eps=1e-15, out_dtype=torch.float32, stream=None):
+    import diffusion_transformer_relu_amd as sana
+    q, k, v = to_device(q_np), to_device(k_np), to_device(v_np)
+    out = sana.linattn_fwd(q, k, v, eps=eps, out_dtype=out_dtype, block_len=block_len or None, stream=stream)
+    torch.cuda.synchronize()
+    return out.float().cpu().double().numpy()

@@ -1,0 +1,132 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/sana_linattn.h declares, and rejects bad arguments before it touches
+the device (no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import diffusion_transformer_relu_amd as sana
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h")]
+
+
+def declared_functions():
+    names = []
+    for h in HEADERS:
+        src = open(h).read()
+        names += re.findall(r"SANA_API\s+[\w\s\*]+?\b(sana_\w+)\s*\(", src)
+    return names
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = declared_functions()
+    assert len(names) == 7, names
+    for n in names:
+        assert hasattr(sana.lib, n), n           # resolves in the shared library
+        assert n in sana._SIGNATURES, n          # and the binding declares its signature
+        assert hasattr(sana, n), n               # and exposes a function of the same name
+
+
+def test_version_and_status_strings():
+    assert sana.sana_linattn_abi_version() == 1
+    for s in range(7):
+        assert sana.sana_linattn_status_string(s) not in ("", "unknown status")
+    assert sana.sana_linattn_status_string(99) == "unknown status"
+    assert sana.sana_linattn_status_string(-1) == "unknown status"
+
+
+def test_workspace_and_plan_queries():
+    ws = sana.sana_linattn_workspace_bytes(1, 70, 16384, 32, 0)
+    assert ws > 0 and ws % 256 == 0
+    assert sana.sana_linattn_workspace_bytes(1, 70, 16384, 32, 1024) > ws   # one state per block
+    assert sana.sana_linattn_workspace_bytes(1, 70, 16384, 32, 16384) == ws  # block_len >= N
+    assert sana.sana_linattn_workspace_bytes(0, 70, 16384, 32, 0) == 0
+    assert sana.sana_linattn_workspace_bytes(1, 70, 0, 32, 0) == 0
+    info = sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 70, 16384, 32, 0)
+    assert info["mfma"] == 1 and info["chunk_tokens"] % 128 == 0 and info["apply_tokens"] % 64 == 0
+    assert info["num_chunks"] * info["chunk_tokens"] >= 16384
+    assert sana.sana_linattn_plan_info(sana.SANA_DT_F32, 1, 2, 256, 32, 0)["mfma"] == 0
+    bc = sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 70, 16384, 32, 1000)
+    assert bc["chunk_tokens"] <= 1024 and bc["num_chunks"] % 17 == 0        # chunks never cross blocks
+
+
+def test_tuning_environment(monkeypatch):
+    monkeypatch.setenv("SANA_LINATTN_CHUNK", "300")
+    monkeypatch.setenv("SANA_LINATTN_APPLY_TILE", "100")
+    info = sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 70, 16384, 32, 0)
+    assert info["chunk_tokens"] == 384 and info["apply_tokens"] == 128
+    monkeypatch.setenv("SANA_LINATTN_PATH", "valu")
+    assert sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 70, 16384, 32, 0)["mfma"] == 0
+    monkeypatch.setenv("SANA_LINATTN_CHUNK", "junk")
+    assert sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 70, 16384, 32, 0)["chunk_tokens"] % 128 == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((1, 70, 16384, 31, 0), sana.SANA_ERR_UNSUPPORTED),
+    ((1, 70, 16384, 64, 0), sana.SANA_ERR_UNSUPPORTED),
+    ((1, 70, 16384, 0, 0), sana.SANA_ERR_INVALID_ARG),
+    ((-1, 70, 16384, 32, 0), sana.SANA_ERR_INVALID_ARG),
+    ((1, -70, 16384, 32, 0), sana.SANA_ERR_INVALID_ARG),
+    ((1, 70, -5, 32, 0), sana.SANA_ERR_INVALID_ARG),
+    ((1, 70, 16384, 32, -1), sana.SANA_ERR_INVALID_ARG),
+    ((1, 70, (1 << 30) + 1, 32, 0), sana.SANA_ERR_UNSUPPORTED),
+])
+def test_workspace_query_errors(args, code):
+    out = ctypes.c_size_t(0)
+    assert sana.lib.sana_linattn_workspace_bytes(*args, ctypes.byref(out)) == code
+    assert sana.lib.sana_linattn_workspace_bytes(1, 1, 1, 32, 0, None) == sana.SANA_ERR_INVALID_ARG
+
+
+# Fake, never-dereferenced addresses: every call below fails a check before any launch.
+A = 1 << 32                 # 16- and 256-byte aligned
+MB = 1 << 20
+
+
+def fwd(q=A, k=A + 64 * MB, v=A + 128 * MB, out=A + 192 * MB, in_dt=1, out_dt=0, B=1, H=2, N=256,
+        D=32, eps=1e-15, ws=A + 512 * MB, ws_bytes=1 << 30, stream=None):
+    return sana.lib.sana_linattn_fwd(q, k, v, out, in_dt, out_dt, B, H, N, D, eps, ws, ws_bytes, stream)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), sana.SANA_ERR_INVALID_ARG),
+    (dict(k=None), sana.SANA_ERR_INVALID_ARG),
+    (dict(v=None), sana.SANA_ERR_INVALID_ARG),
+    (dict(out=None), sana.SANA_ERR_INVALID_ARG),
+    (dict(ws=None), sana.SANA_ERR_INVALID_ARG),
+    (dict(in_dt=2), sana.SANA_ERR_INVALID_ARG),
+    (dict(out_dt=-1), sana.SANA_ERR_INVALID_ARG),
+    (dict(D=16), sana.SANA_ERR_UNSUPPORTED),
+    (dict(B=-1), sana.SANA_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), sana.SANA_ERR_INVALID_ARG),
+    (dict(eps=float("inf")), sana.SANA_ERR_INVALID_ARG),
+    (dict(eps=-1e-6), sana.SANA_ERR_INVALID_ARG),
+    (dict(q=A + 2), sana.SANA_ERR_ALIGNMENT),
+    (dict(out=A + 192 * MB + 8), sana.SANA_ERR_ALIGNMENT),
+    (dict(ws=A + 512 * MB + 16), sana.SANA_ERR_ALIGNMENT),
+    (dict(out=A), sana.SANA_ERR_ALIAS),                         # out == q
+    (dict(out=A + 64 * MB + 16 * 1024), sana.SANA_ERR_ALIAS),   # out overlaps k's tail
+    (dict(ws=A + 128 * MB), sana.SANA_ERR_ALIAS),               # workspace == v
+    (dict(ws_bytes=1024), sana.SANA_ERR_WORKSPACE),
+])
+def test_forward_argument_errors(kw, code):
+    assert fwd(**kw) == code
+
+
+def test_empty_problems_succeed_without_touching_pointers():
+    for B, H, N in ((0, 2, 256), (1, 0, 256), (1, 2, 0)):
+        assert fwd(q=None, k=None, v=None, out=None, ws=None, ws_bytes=0, B=B, H=H, N=N) == sana.SANA_OK
+
+
+def test_blockcausal_and_stage_argument_errors():
+    args = (A, A + 64 * MB, A + 128 * MB, A + 192 * MB, 1, 0, 1, 2, 256, 32)
+    tail = (1e-15, A + 512 * MB, 1 << 30, None)
+    for L in (0, -3):
+        assert sana.lib.sana_linattn_blockcausal_fwd(*args, L, *tail) == sana.SANA_ERR_INVALID_ARG
+    assert sana.lib.sana_linattn_blockcausal_fwd(*args, 64, 1e-15, A + 512 * MB, 16, None) == \
+        sana.SANA_ERR_WORKSPACE
+    for stages in (0, 8, -1, 15):
+        assert sana.lib.sana_linattn_fwd_stages(*args, 0, *tail, stages) == sana.SANA_ERR_INVALID_ARG
+    assert sana.lib.sana_linattn_fwd_stages(*args, -1, *tail, 7) == sana.SANA_ERR_INVALID_ARG

@@ -1,0 +1,140 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, element
+by element, on the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from hip_helpers import compare, inputs_and_oracle, run_hip, to_device
+
+pytestmark = pytest.mark.gpu
+
+FULL = [workloads.S600M_1024, workloads.S1600M_1024, workloads.S1600M_2048,
+        workloads.HEADLINE, workloads.BLOCK_CAUSAL]
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu] {request.node.name}", flush=True)
+
+
+def test_tiny_config_f32():
+    w = workloads.TINY
+    (q, k, v), want = inputs_and_oracle(w)
+    got = run_hip(q, k, v, eps=w.eps)
+    compare(got, want, v, False, w.name)
+    assert np.all(got[:, :, 1, :] == 0.0)          # all-negative K head: the eps path gives exact zeros
+
+
+@pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["f32out", "bf16out"])
+def test_full_size_configs(w, out_dtype):
+    (q, k, v), want = inputs_and_oracle(w)
+    got = run_hip(q, k, v, block_len=w.block_len, eps=w.eps, out_dtype=out_dtype)
+    max_abs, rel = compare(got, want, v, out_dtype == torch.bfloat16, w.name)
+    print(f"[gpu] {w.name} {out_dtype}: max_abs={max_abs:.3e} rel_l2={rel:.3e}", flush=True)
+
+
+EDGE = [
+    # (B, N, H, block_len, in_dtype)
+    (1, 1, 1, 0, workloads.DT_BF16),
+    (1, 31, 3, 0, workloads.DT_BF16),
+    (2, 257, 5, 0, workloads.DT_BF16),
+    (3, 1000, 7, 0, workloads.DT_BF16),
+    (1, 4097, 2, 0, workloads.DT_BF16),
+    (2, 1000, 3, 100, workloads.DT_BF16),
+    (1, 999, 4, 1, workloads.DT_BF16),
+    (1, 1024, 2, 1024, workloads.DT_BF16),
+    (1, 700, 3, 5000, workloads.DT_BF16),
+    (1, 3000, 1, 257, workloads.DT_BF16),
+    (2, 300, 3, 0, workloads.DT_F32),
+    (1, 1000, 2, 64, workloads.DT_F32),
+]
+
+
+@pytest.mark.parametrize("path", ["mfma", "valu"])
+@pytest.mark.parametrize("B,N,H,L,dt", EDGE, ids=[f"B{b}N{n}H{h}L{l}{'bf16' if d else 'f32'}" for b, n, h, l, d in EDGE])
+def test_edge_shapes(monkeypatch, path, B, N, H, L, dt):
+    if path == "valu":
+        monkeypatch.setenv("SANA_LINATTN_PATH", "valu")
+    w = workloads.Workload(f"edge_{B}_{N}_{H}_{L}", B, N, H, 32, dt, seed=1000 + N + H, block_len=L)
+    (q, k, v), want = inputs_and_oracle(w)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        got = run_hip(q, k, v, block_len=L, eps=w.eps, out_dtype=out_dtype)
+        compare(got, want, v, out_dtype == torch.bfloat16, f"{w.name} {path} {out_dtype}")
+
+
+@pytest.mark.parametrize("chunk,tile", [("128", "64"), ("256", "128"), ("1024", "256"), ("2048", "512")])
+def test_decomposition_does_not_change_result(monkeypatch, chunk, tile):
+    monkeypatch.setenv("SANA_LINATTN_CHUNK", chunk)
+    monkeypatch.setenv("SANA_LINATTN_APPLY_TILE", tile)
+    w = workloads.with_shape(workloads.BLOCK_CAUSAL, N=5000, H=6, block_len=1024, name="decomp")
+    (q, k, v), want = inputs_and_oracle(w)
+    compare(run_hip(q, k, v, block_len=w.block_len, eps=w.eps), want, v, False, f"chunk {chunk} tile {tile}")
+    w2 = workloads.with_shape(workloads.HEADLINE, N=5000, H=6, name="decomp_nc")
+    (q, k, v), want = inputs_and_oracle(w2)
+    compare(run_hip(q, k, v, eps=w2.eps), want, v, False, f"nc chunk {chunk} tile {tile}")
+
+
+def test_bitwise_repeatable_and_stages_equal_full_call():
+    import diffusion_transformer_relu_amd as sana
+    w = workloads.with_shape(workloads.HEADLINE, N=4096, H=70, name="determinism")
+    q, k, v = [to_device(a) for a in workloads.make_inputs(w)]
+    B, N, H, D = q.shape
+    ws = torch.empty(sana.sana_linattn_workspace_bytes(B, H, N, D, 0), dtype=torch.uint8, device="cuda:0")
+    outs = []
+    for _ in range(3):
+        out = torch.empty(q.shape, dtype=torch.float32, device="cuda:0")
+        sana.sana_linattn_fwd(q, k, v, out, ws)
+        outs.append(out)
+    staged = torch.empty(q.shape, dtype=torch.float32, device="cuda:0")
+    for st in (sana.SANA_STAGE_STATE, sana.SANA_STAGE_MERGE, sana.SANA_STAGE_APPLY):
+        sana.sana_linattn_fwd_stages(q, k, v, staged, ws, st)
+    torch.cuda.synchronize()
+    for o in outs[1:] + [staged]:
+        assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
+
+
+def test_eps_path_rows_are_exact_zeros():
+    w = workloads.Workload("eps_rows", 1, 2000, 4, 32, workloads.DT_BF16, seed=77, negative_k_heads=(2,),
+                           negative_q_rows=((0, 5, 0), (0, 1999, 3), (0, 640, 1)))
+    (q, k, v), want = inputs_and_oracle(w)
+    for L in (0, 512):
+        got = run_hip(q, k, v, block_len=L, eps=w.eps)
+        assert np.all(got[0, :, 2] == 0.0)
+        for (_, n, h) in w.negative_q_rows:
+            assert np.all(got[0, n, h] == 0.0)
+    compare(run_hip(q, k, v, eps=w.eps), want, v, False, w.name)
+
+
+def test_non_default_stream_and_empty_problem():
+    import diffusion_transformer_relu_amd as sana
+    w = workloads.with_shape(workloads.S600M_1024, B=1, N=512, H=4, name="stream")
+    (q, k, v), want = inputs_and_oracle(w)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        got = run_hip(q, k, v, eps=w.eps, stream=s)
+    compare(got, want, v, False, w.name)
+    z = torch.empty((1, 0, 2, 32), dtype=torch.bfloat16, device="cuda:0")
+    out = torch.empty((1, 0, 2, 32), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(1, dtype=torch.uint8, device="cuda:0")
+    sana.sana_linattn_fwd(z, z, z, out, ws)
+    sana.sana_linattn_blockcausal_fwd(z, z, z, out, ws, 16)
+
+
+def test_device_argument_errors_leave_output_untouched():
+    import diffusion_transformer_relu_amd as sana
+    w = workloads.with_shape(workloads.S600M_1024, B=1, N=256, H=2, name="errs")
+    q, k, v = [to_device(a) for a in workloads.make_inputs(w)]
+    out = torch.full(q.shape, 7.0, dtype=torch.float32, device="cuda:0")
+    need = sana.sana_linattn_workspace_bytes(1, 2, 256, 32, 0)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda:0")
+    P, I = sana.lib.sana_linattn_fwd, q.data_ptr()
+    args = lambda qp, op, wp, wb: (qp, k.data_ptr(), v.data_ptr(), op, 1, 0, 1, 2, 256, 32, 1e-15, wp, wb, None)
+    assert P(*args(I + 2, out.data_ptr(), ws.data_ptr(), need)) == sana.SANA_ERR_ALIGNMENT
+    assert P(*args(I, I, ws.data_ptr(), need)) == sana.SANA_ERR_ALIAS
+    assert P(*args(I, out.data_ptr(), ws.data_ptr(), need - 1)) == sana.SANA_ERR_WORKSPACE
+    assert P(*args(I, out.data_ptr(), ws.data_ptr() + 128, need)) == sana.SANA_ERR_ALIGNMENT
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)

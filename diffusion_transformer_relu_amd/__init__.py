@@ -50,6 +50,13 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
                       f"g.build()'` (hipcc, gfx950)")
 
+# torch ships its own HIP runtime under the same soname as the system one
+# (libamdhip64.so.7).  Importing torch first makes this library bind to that
+# already-loaded runtime, so device pointers and streams are shared with
+# torch; loading the library first would pull in the system runtime and leave
+# torch running on a mix of the two.
+import torch  # noqa: E402,F401
+
 lib = ctypes.CDLL(LIB_PATH)
 for _name, (_res, _args) in _SIGNATURES.items():
     _fn = getattr(lib, _name)

@@ -18,7 +18,6 @@ namespace {
 
 constexpr int kMaxN = 1 << 30;        // keeps every token index, and N + block_len, in int range
 constexpr int kMaxBH = 1 << 24;       // batch and head counts
-constexpr int kTargetGroups = 1024;   // work-groups wanted per launch (256 CUs x 4)
 
 // Positive integer from the environment, or 0 when unset or not a positive integer.
 int env_positive(const char* name) {
@@ -61,32 +60,30 @@ int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block
     pl->HP = pl->mfma ? (H + 1) / 2 : H;
     const long units = (long)B * pl->HP * pl->NB;   // independent (b, head unit, block) triples
 
-    // State chunk: the largest power-of-two multiple of the LDS tile that still
-    // gives about kTargetGroups work-groups; never longer than a block.
+    // Work-groups per launch follow the tuned targets kStateGroups and
+    // kApplyGroups (each launch is a single round on the chip).  Chunks and
+    // apply tiles are whole multiples of 64 tokens and never cross a block.
     int chunk = env_positive("SANA_LINATTN_CHUNK");
     if (chunk) {
-        chunk = (int)round_up(chunk, sana::kStateTile);
+        chunk = (int)round_up(chunk, 64);
     } else {
-        chunk = sana::kStateTile;
-        for (int c = 2048; c >= sana::kStateTile; c /= 2) {
-            if (units * ceil_div(pl->L, c) >= kTargetGroups) { chunk = c; break; }
-        }
+        const long slots = sana::kStateGroups;
+        const long per_block = std::max<long>(1, slots / units);
+        chunk = (int)std::max<long>(round_up(ceil_div(pl->L, per_block), 64), sana::kMinChunk);
     }
-    chunk = (int)std::min<long>(chunk, round_up(pl->L, sana::kStateTile));
+    chunk = (int)std::min<long>(chunk, round_up(pl->L, 64));
     pl->chunk = chunk;
     pl->cpb = ceil_div(pl->L, chunk);
     pl->P = pl->NB * pl->cpb;
 
-    // Apply tile, in tokens per work-group.
     if (pl->mfma) {
         int tile = env_positive("SANA_LINATTN_APPLY_TILE");
         if (tile) {
             tile = (int)round_up(tile, 64);
         } else {
-            tile = 64;
-            for (int t = 512; t >= 64; t /= 2) {
-                if (units * ceil_div(pl->L, t) >= kTargetGroups) { tile = t; break; }
-            }
+            const long slots = sana::kApplyGroups;
+            const long per_block = std::max<long>(1, slots / units);
+            tile = (int)round_up(ceil_div(pl->L, per_block), 64);
         }
         pl->tile = (int)std::min<long>(tile, round_up(pl->L, 64));
     } else {
@@ -104,8 +101,6 @@ int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block
     off += round_up((long)(bh * pl->P * sana::kStateFloats * sizeof(float)), 256);
     pl->off_state = off;
     off += round_up((long)(bh * pl->NB * sana::kStateFloats * sizeof(float)), 256);
-    pl->off_pack = off;
-    off += round_up((long)(bh * pl->NB * sana::kPackBytes), 256);
     pl->bytes = off;
     return SANA_OK;
 }
@@ -143,12 +138,11 @@ int forward(const void* q, const void* k, const void* v, void* out, int in_dtype
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     float* part = reinterpret_cast<float*>(ws + pl.off_part);
     float* state = reinterpret_cast<float*>(ws + pl.off_state);
-    uint8_t* pack = ws + pl.off_pack;
     if ((stages & SANA_STAGE_STATE) && sana::launch_state(pl, k, v, part, stream) != hipSuccess)
         return SANA_ERR_HIP;
-    if ((stages & SANA_STAGE_MERGE) && sana::launch_merge(pl, part, state, pack, stream) != hipSuccess)
+    if ((stages & SANA_STAGE_MERGE) && sana::launch_merge(pl, part, state, stream) != hipSuccess)
         return SANA_ERR_HIP;
-    if ((stages & SANA_STAGE_APPLY) && sana::launch_apply(pl, q, state, pack, out, eps, stream) != hipSuccess)
+    if ((stages & SANA_STAGE_APPLY) && sana::launch_apply(pl, q, state, out, eps, stream) != hipSuccess)
         return SANA_ERR_HIP;
     return SANA_OK;
 }

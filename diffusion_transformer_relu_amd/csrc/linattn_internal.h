@@ -12,38 +12,40 @@ constexpr int kD = 32;                    // head dim (every Sana model: linear_
 constexpr int kW = kD + 1;                // state row: D value columns + the normaliser column
 constexpr int kStateFloats = kD * kW;     // 1056 floats per (b, h) state
 constexpr int kThreads = 256;             // 4 wave64 per work-group, every kernel
-constexpr int kStateTile = 128;           // tokens per LDS tile, matrix-core state kernel
+constexpr int kStateTile = 64;            // tokens per LDS tile, matrix-core state kernel
 constexpr int kValuTile = 64;             // tokens per LDS tile, vector state kernel
 constexpr int kValuApplyTokens = 256;     // tokens per work-group, vector apply kernel
+constexpr int kMergeThreads = 256;        // state entries per merge work-group
 
-// Apply-side operand pack for one (b, h, block): the fp32 state split into three
-// bf16 terms (hi + mid + lo), already in the per-lane order of the B operand of
-// v_mfma_f32_32x32x16_bf16.
-//   value part  [ks 2][split 3][lane 64][8 x bf16]   lane = 32*g + c, element e:
-//               S[16*ks + 8*g + e][c]
-//   norm part   [ks 2][split 3][g 2][8 x bf16]       element e: S[16*ks + 8*g + e][D]
-constexpr int kPackValueBytes = 2 * 3 * 64 * 16;               // 6144
-constexpr int kPackBytes = kPackValueBytes + 2 * 3 * 2 * 16;   // 6336
+// Work-group counts per launch, tuned on MI355X (256 CUs).  The state kernel
+// streams K/V fastest with about 2 work-groups per CU (measured: 560 groups of
+// 1024-token chunks beat 1120 groups of 512 tokens and 280 of 2048 at the
+// 4096px shape); the apply kernel wants one full round at 5 work-groups per CU
+// (its occupancy at 5 waves per SIMD).
+constexpr int kCUs = 256;
+constexpr int kStateGroups = 576;
+constexpr int kApplyGroups = kCUs * 5;
+constexpr int kMinChunk = 256;            // keeps the partial states a few % of the K/V bytes
 
 struct Plan {
     int B, H, N;
     int L;        // block length in tokens (N for the non-causal operator)
     int NB;       // number of blocks
     int HP;       // head units per batch: head pairs (matrix path) or heads (vector path)
-    int chunk;    // tokens per state chunk (multiple of kStateTile)
+    int chunk;    // tokens per state chunk (multiple of 64)
     int cpb;      // chunks per block
     int P;        // chunks per (b, h) = NB * cpb
     int tile;     // tokens per apply work-group
     int tpb;      // apply work-groups per block
     int mfma;     // 1: bf16 matrix-core kernels, 0: vector kernels
     int in_dtype, out_dtype;
-    size_t off_part, off_state, off_pack, bytes;
+    size_t off_part, off_state, bytes;
 };
 
 // Each launcher enqueues one kernel on `stream` and returns hipGetLastError().
 hipError_t launch_state(const Plan& pl, const void* k, const void* v, float* part, hipStream_t stream);
-hipError_t launch_merge(const Plan& pl, const float* part, float* state, uint8_t* pack, hipStream_t stream);
-hipError_t launch_apply(const Plan& pl, const void* q, const float* state, const uint8_t* pack,
-                        void* out, float eps, hipStream_t stream);
+hipError_t launch_merge(const Plan& pl, const float* part, float* state, hipStream_t stream);
+hipError_t launch_apply(const Plan& pl, const void* q, const float* state, void* out, float eps,
+                        hipStream_t stream);
 
 }  // namespace sana

@@ -13,17 +13,18 @@
 //      tokens as the reduction dimension (bf16 x bf16 products are exact in
 //      fp32); K/V tiles are staged through LDS to turn the token-major HBM rows
 //      into token-packed matrix operands.
-//   2. merge  (k_merge) - one work-group per (b, h) sums the partials in a fixed
-//      order (deterministic, no atomics).  For the block-causal operator it also
-//      forms the inclusive prefix over blocks ("cumulative statistics per
-//      temporal block", "How Linear Attention Improves Efficiency in DiT for
-//      High-Resolution Images", section "Video Generation and Constant-Memory KV
-//      Cache").  It writes the fp32 state and a bf16 hi/mid/lo operand pack for
-//      the apply kernel.
-//   3. apply  (k_apply_*) - q rows go straight from HBM into the A operand of
-//      the same MFMA (the feature axis is already contiguous); three bf16 split
-//      terms of S reproduce the fp32 state to ~2^-24, so numerator and
-//      normaliser keep fp32 accuracy, as the pages' fp32 attention policy asks.
+//   2. merge  (k_merge) - one thread per (b, h, state entry) sums the partials
+//      in a fixed order (deterministic, no atomics).  For the block-causal
+//      operator it also forms the inclusive prefix over blocks ("cumulative
+//      statistics per temporal block", "How Linear Attention Improves
+//      Efficiency in DiT for High-Resolution Images", section "Video
+//      Generation and Constant-Memory KV Cache").
+//   3. apply  (k_apply_*) - q rows go straight from HBM into a matrix operand
+//      (the feature axis is already contiguous) and the numerators come from
+//      the same MFMA against three bf16 split terms of S, which reproduce the
+//      fp32 state to ~2^-24; the normaliser is an fp32 dot product on the
+//      vector unit.  Both keep fp32 accuracy, as the pages' fp32 attention
+//      policy asks.
 //
 // fp32 inputs take the vector kernels (k_*_valu), which also serve as a second
 // implementation for cross-checks.
@@ -34,7 +35,9 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 // ReLU on two packed bf16: for the sign test a bf16 orders like an int16, so
@@ -57,6 +60,8 @@ __device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __builtin_bit_cast(float, (uint32_t)h << 16);
 }
+__device__ __forceinline__ float lo_bf16(uint32_t x) { return __builtin_bit_cast(float, x << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t x) { return __builtin_bit_cast(float, x & 0xffff0000u); }
 
 // Round to nearest, ties to even (finite inputs; NaN is kept a quiet NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
@@ -72,6 +77,17 @@ __device__ __forceinline__ float load_in(const uint16_t* p, size_t i) { return b
 __device__ __forceinline__ void store_out(float* p, size_t i, float x) { p[i] = x; }
 __device__ __forceinline__ void store_out(uint16_t* p, size_t i, float x) { p[i] = f32_to_bf16(x); }
 
+// Output stores are non-temporal: out is written once and never read here, and
+// streaming it past the caches raises the write bandwidth markedly on gfx950.
+__device__ __forceinline__ void store4(float* p, f32x4 x) {
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
+}
+__device__ __forceinline__ void store4(uint16_t* p, f32x4 x) {
+    const uint32_t lo = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+    __builtin_nontemporal_store((u32x2){lo, hi}, reinterpret_cast<u32x2*>(p));
+}
+
 // Token range [c0, c1) of chunk p of a (b, head) unit.
 struct ChunkRange { int c0, c1; };
 __device__ __forceinline__ ChunkRange chunk_range(int p, int cpb, int chunk, int L, int N) {
@@ -83,14 +99,16 @@ __device__ __forceinline__ ChunkRange chunk_range(int p, int cpb, int chunk, int
 }
 
 // ------------------------------------------------------------------ state, bf16, MFMA
-// LDS tile: [tensor K|V][head 0|1][token 0..127][32 x bf16]; the second head's
+// LDS tile: [tensor K|V][head 0|1][token 0..63][32 x bf16]; the second head's
 // rows are shifted by 64 bytes so that a 16-byte write from each head of one
 // token lands in different banks.
+constexpr int kPieces = kStateTile / 32;            // 16-byte pieces per thread per tensor
 constexpr int kHeadStride = kStateTile * 64 + 64;   // bytes
 constexpr int kTensorStride = 2 * kHeadStride;
 
 // grid.x = (b * HP + hp) * P + p; one work-group = one chunk of one head pair.
-// Wave w reduces head (w & 1) over token half (w >> 1) of each 128-token tile.
+// Wave w reduces head (w & 1) over token half (w >> 1) of each 64-token tile.
+// K and V are read once, so their loads are non-temporal.
 __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ part,
     int N, int H, int HP, int L, int cpb, int P, int chunk) {
@@ -109,17 +127,17 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
     // Global -> register assignment: 16-byte piece id = tid + 256 i; piece
     // (tok, head, part) covers features 8*part..8*part+7 of one head of one
     // token, so a wave reads 8 whole 128-byte rows (both heads of 8 tokens).
-    u32x4 rk[4], rv[4];
+    u32x4 rk[kPieces], rv[kPieces];
     auto load_tile = [&](int t0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kPieces; ++i) {
             const int pc = tid + kThreads * i;
             const int part_ = pc & 3, hd = (pc >> 2) & 1, tok = pc >> 3;
             const int n = t0 + tok;
             if (n < cr.c1 && hd < nh) {
                 const size_t off = (((size_t)b * N + n) * H + h0 + hd) * kD + part_ * 8;
-                rk[i] = *reinterpret_cast<const u32x4*>(k + off);
-                rv[i] = *reinterpret_cast<const u32x4*>(v + off);
+                rk[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + off));
+                rv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + off));
             } else {
                 rk[i] = (u32x4){0u, 0u, 0u, 0u};
                 rv[i] = (u32x4){0u, 0u, 0u, 0u};
@@ -135,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
     for (int t0 = cr.c0; t0 < cr.c1; t0 += kStateTile) {
         __syncthreads();   // the previous tile has been consumed
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kPieces; ++i) {
             const int pc = tid + kThreads * i;
             const int part_ = pc & 3, hd = (pc >> 2) & 1, tok = pc >> 3;
             const int o = hd * kHeadStride + tok * 64 + part_ * 16;
@@ -148,10 +166,10 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
         const uint16_t* Kt = reinterpret_cast<const uint16_t*>(lds + hh * kHeadStride);
         const uint16_t* Vt = reinterpret_cast<const uint16_t*>(lds + kTensorStride + hh * kHeadStride);
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
+        for (int st = 0; st < kStateTile / 32; ++st) {
             // 16 tokens per MFMA; element e of lane (g, j) is token tb + 2e + g,
             // the same token for the K (row j) and the V (column j) operand.
-            const int tb = 64 * th + 16 * st;
+            const int tb = (kStateTile / 2) * th + 16 * st;
             u32x4 a, bv;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -240,37 +258,33 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_valu(
 }
 
 // ------------------------------------------------------------------ merge / block scan
-// grid.x = b * H + h.  Sums the partials of each block in chunk order, carries
-// the running sum across blocks (inclusive prefix) and writes, per block, the
-// fp32 state and the bf16 split operand pack.
-__global__ __launch_bounds__(kThreads) void k_merge(
-    const float* __restrict__ part, float* __restrict__ state, uint8_t* __restrict__ pack,
-    int NB, int cpb, int P) {
-    const size_t bh = blockIdx.x;
-    const float* src = part + bh * P * kStateFloats;
-    for (int e = threadIdx.x; e < kStateFloats; e += kThreads) {
-        const int j = e / kW, c = e - j * kW;
-        const int ks = j >> 4, g = (j >> 3) & 1, el = j & 7;
-        float acc = 0.f;
-        for (int beta = 0; beta < NB; ++beta) {
-            for (int s = 0; s < cpb; ++s) acc += src[(size_t)(beta * cpb + s) * kStateFloats + e];
-            state[(bh * NB + beta) * kStateFloats + e] = acc;
-            // acc = hi + mid + lo; each remainder is exact in fp32
-            uint16_t sp[3];
-            float r = acc;
+// grid.x = (b * H + h) * kMergeGroups + m; thread t owns state entry
+// e = m * kMergeThreads + t.  For each block it sums that block's chunk
+// partials (groups of 8 loads in flight, added as a fixed pairwise tree), and
+// adds the block sum to the running state (inclusive prefix over blocks).
+constexpr int kMergeGroups = (kStateFloats + kMergeThreads - 1) / kMergeThreads;
+
+__global__ __launch_bounds__(kMergeThreads) void k_merge(
+    const float* __restrict__ part, float* __restrict__ state, int NB, int cpb, int P) {
+    const size_t bh = blockIdx.x / kMergeGroups;
+    const int e = (blockIdx.x % kMergeGroups) * kMergeThreads + threadIdx.x;
+    if (e >= kStateFloats) return;
+    const float* src = part + bh * P * kStateFloats + e;
+    float* dst = state + bh * NB * kStateFloats + e;
+    float acc = 0.f;
+#pragma unroll 4
+    for (int beta = 0; beta < NB; ++beta) {
+        const float* blk = src + (size_t)beta * cpb * kStateFloats;
+        float bs = 0.f;
+        for (int s0 = 0; s0 < cpb; s0 += 8) {
+            float x[8];
 #pragma unroll
-            for (int i = 0; i < 3; ++i) {
-                sp[i] = f32_to_bf16(r);
-                r -= bf16_to_f32(sp[i]);
-            }
-            uint8_t* pk = pack + (bh * NB + beta) * kPackBytes;
-#pragma unroll
-            for (int i = 0; i < 3; ++i) {
-                const int o = (c < kD) ? ((ks * 3 + i) * 64 + g * 32 + c) * 16 + el * 2
-                                       : kPackValueBytes + ((ks * 3 + i) * 2 + g) * 16 + el * 2;
-                *reinterpret_cast<uint16_t*>(pk + o) = sp[i];
-            }
+            for (int i = 0; i < 8; ++i)
+                x[i] = (s0 + i < cpb) ? blk[(size_t)(s0 + i) * kStateFloats] : 0.f;
+            bs += ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
         }
+        acc += bs;
+        dst[(size_t)beta * kStateFloats] = acc;
     }
 }
 
@@ -278,10 +292,24 @@ __global__ __launch_bounds__(kThreads) void k_merge(
 // grid.x = (b * HP + hp) * (NB * tpb) + beta * tpb + tile.  Wave w handles head
 // 2*hp + (w & 1) and every other 32-token sub-tile (w >> 1) of the work-group's
 // token range, which never crosses a block boundary.
+//
+// Per sub-tile the wave forms the transposed product out^T = S^T f^T with
+// f = ReLU(q): A = S^T as three bf16 split terms (built once per work-group
+// from the fp32 state), B = 32 q rows straight from HBM (lane (g, i) holds
+// features 8g..8g+7 and 16+8g..16+8g+7 of token i, the layout the operand
+// needs).  Lane (g, i) then owns 16 numerators of token i (columns
+// 8*(r/4) + 4g + r%4), so it computes token i's normaliser itself in fp32 from
+// the same registers (half the features here, half from lane i + 32) and takes
+// one reciprocal.  The normalised 32 x 32 tile goes through this wave's LDS so
+// that every store instruction writes whole 128-byte output rows.
+constexpr int kOutPitch = 36;   // floats per LDS output row: 32 + 4 keeps rows 16-byte aligned, no bank conflicts
+
 template <typename OutT>
-__global__ __launch_bounds__(kThreads) void k_apply_mfma(
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ pack, OutT* __restrict__ out,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))) void k_apply_mfma(
+    const uint16_t* __restrict__ q, const float* __restrict__ state, OutT* __restrict__ out,
     int N, int H, int HP, int L, int NB, int tile, int tpb, float eps) {
+    __shared__ __attribute__((aligned(16))) float otile[4][32 * kOutPitch];
+
     const int per_unit = NB * tpb;
     const int tau = blockIdx.x % per_unit;
     const int bhp = blockIdx.x / per_unit;
@@ -297,42 +325,90 @@ __global__ __launch_bounds__(kThreads) void k_apply_mfma(
     const int t1 = min(t0 + tile, blk1);
     if (t0 >= t1) return;
 
-    const int g = lane >> 5, c = lane & 31;
-    const uint8_t* pk = pack + (((size_t)b * H + h) * NB + beta) * kPackBytes;
-    u32x4 nb[2][3], db[2][3];
+    const int g = lane >> 5, i = lane & 31;
+    // A operand: lane (g, c = i), element e of (ks, split) = split term of
+    // S[16 ks + 8 g + e][c]; sden: this lane's 16 normaliser entries.
+    const float* S = state + (((size_t)b * H + h) * NB + beta) * kStateFloats;
+    u32x4 sa[2][3];
+    float sden[16];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            nb[ks][i] = *reinterpret_cast<const u32x4*>(pk + ((ks * 3 + i) * 64 + lane) * 16);
-            db[ks][i] = *reinterpret_cast<const u32x4*>(pk + kPackValueBytes + ((ks * 3 + i) * 2 + g) * 16);
-        }
-
-    for (int tt = t0 + 32 * sub; tt < t1; tt += 64) {
-        // A operand: row c of the sub-tile, features 8g..8g+7 (ks 0) and 16+8g.. (ks 1)
-        const int row = tt + c;
-        u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
-        if (row < t1) {
-            const uint16_t* src = q + (((size_t)b * N + row) * H + h) * kD + 8 * g;
-            a0 = relu_bf16x8(*reinterpret_cast<const u32x4*>(src));
-            a1 = relu_bf16x8(*reinterpret_cast<const u32x4*>(src + 16));
-        }
-        f32x16 an = {}, ad = {};
+        for (int d = 0; d < 4; ++d) {
+            uint32_t w[3] = {0u, 0u, 0u};
 #pragma unroll
-        for (int i = 2; i >= 0; --i) {   // small split terms first
-            an = mfma_bf16(a0, nb[0][i], an);
-            ad = mfma_bf16(a0, db[0][i], ad);
-            an = mfma_bf16(a1, nb[1][i], an);
-            ad = mfma_bf16(a1, db[1][i], ad);
-        }
+            for (int half = 0; half < 2; ++half) {
+                const int row = 16 * ks + 8 * g + 2 * d + half;
+                float r = S[row * kW + i];
+                sden[8 * ks + 2 * d + half] = S[row * kW + kD];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int orow = tt + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (orow < t1) {
-                const float o = an[r] * __builtin_amdgcn_rcpf(ad[r] + eps);
-                store_out(out, (((size_t)b * N + orow) * H + h) * kD + c, o);
+                for (int sp = 0; sp < 3; ++sp) {   // S = hi + mid + lo, each remainder exact
+                    const uint16_t t = f32_to_bf16(r);
+                    r -= bf16_to_f32(t);
+                    w[sp] |= (uint32_t)t << (16 * half);
+                }
             }
+#pragma unroll
+            for (int sp = 0; sp < 3; ++sp) sa[ks][sp][d] = w[sp];
         }
+    }
+
+    auto load_b = [&](int tt, u32x4& x0, u32x4& x1) {
+        const int row = tt + i;
+        if (row < t1) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(q + (((size_t)b * N + row) * H + h) * kD + 8 * g);
+            x0 = src[0];
+            x1 = src[2];
+        } else {
+            x0 = (u32x4){0u, 0u, 0u, 0u};
+            x1 = (u32x4){0u, 0u, 0u, 0u};
+        }
+    };
+    float* ot = otile[wave];
+    int tt = t0 + 32 * sub;
+    u32x4 a0, a1;
+    load_b(tt, a0, a1);
+    for (; tt < t1; tt += 64) {
+        u32x4 n0, n1;
+        load_b(tt + 64, n0, n1);       // next sub-tile of this wave, in flight during the MFMAs
+        a0 = relu_bf16x8(a0);
+        a1 = relu_bf16x8(a1);
+        f32x16 acc = {};
+#pragma unroll
+        for (int sp = 2; sp >= 0; --sp) {   // small split terms first
+            acc = mfma_bf16(sa[0][sp], a0, acc);
+            acc = mfma_bf16(sa[1][sp], a1, acc);
+        }
+        float dp = 0.f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            dp = fmaf(lo_bf16(a0[d]), sden[2 * d], dp);
+            dp = fmaf(hi_bf16(a0[d]), sden[2 * d + 1], dp);
+        }
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            dp = fmaf(lo_bf16(a1[d]), sden[8 + 2 * d], dp);
+            dp = fmaf(hi_bf16(a1[d]), sden[8 + 2 * d + 1], dp);
+        }
+        const float den = dp + __shfl_xor(dp, 32);   // same sum on lanes i and i + 32
+        const float rinv = 1.0f / (den + eps);
+
+        // tile row i = token tt + i; lane (g, i) holds columns 8 rr + 4 g .. +3
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            *reinterpret_cast<f32x4*>(ot + i * kOutPitch + 8 * rr + 4 * g) =
+                (f32x4){acc[4 * rr] * rinv, acc[4 * rr + 1] * rinv, acc[4 * rr + 2] * rinv, acc[4 * rr + 3] * rinv};
+        __builtin_amdgcn_wave_barrier();
+        // each store: 8 rows x 8 lanes x 4 columns = 8 whole output rows of this head
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            const int r = 8 * s4 + (lane >> 3), cc = (lane & 7) * 4;
+            const f32x4 x = *reinterpret_cast<const f32x4*>(ot + r * kOutPitch + cc);
+            if (tt + r < t1) store4(out + (((size_t)b * N + tt + r) * H + h) * kD + cc, x);
+        }
+        __builtin_amdgcn_wave_barrier();
+        a0 = n0;
+        a1 = n1;
     }
 }
 
@@ -395,23 +471,23 @@ hipError_t launch_state(const Plan& pl, const void* k, const void* v, float* par
     return hipGetLastError();
 }
 
-hipError_t launch_merge(const Plan& pl, const float* part, float* state, uint8_t* pack, hipStream_t stream) {
-    const unsigned grid = (unsigned)((size_t)pl.B * pl.H);
-    hipLaunchKernelGGL(k_merge, dim3(grid), dim3(kThreads), 0, stream, part, state, pack, pl.NB, pl.cpb, pl.P);
+hipError_t launch_merge(const Plan& pl, const float* part, float* state, hipStream_t stream) {
+    const unsigned grid = (unsigned)((size_t)pl.B * pl.H * kMergeGroups);
+    hipLaunchKernelGGL(k_merge, dim3(grid), dim3(kMergeThreads), 0, stream, part, state, pl.NB, pl.cpb, pl.P);
     return hipGetLastError();
 }
 
-hipError_t launch_apply(const Plan& pl, const void* q, const float* state, const uint8_t* pack,
-                        void* out, float eps, hipStream_t stream) {
+hipError_t launch_apply(const Plan& pl, const void* q, const float* state, void* out, float eps,
+                        hipStream_t stream) {
     const bool out_bf16 = pl.out_dtype == 1;
     if (pl.mfma) {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.NB * pl.tpb);
         const uint16_t* qq = static_cast<const uint16_t*>(q);
         if (out_bf16)
-            hipLaunchKernelGGL(k_apply_mfma<uint16_t>, dim3(grid), dim3(kThreads), 0, stream, qq, pack,
+            hipLaunchKernelGGL(k_apply_mfma<uint16_t>, dim3(grid), dim3(kThreads), 0, stream, qq, state,
                                static_cast<uint16_t*>(out), pl.N, pl.H, pl.HP, pl.L, pl.NB, pl.tile, pl.tpb, eps);
         else
-            hipLaunchKernelGGL(k_apply_mfma<float>, dim3(grid), dim3(kThreads), 0, stream, qq, pack,
+            hipLaunchKernelGGL(k_apply_mfma<float>, dim3(grid), dim3(kThreads), 0, stream, qq, state,
                                static_cast<float*>(out), pl.N, pl.H, pl.HP, pl.L, pl.NB, pl.tile, pl.tpb, eps);
     } else {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.H * pl.NB * pl.tpb);

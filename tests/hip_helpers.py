@@ -48,9 +48,13 @@ def compare(got: np.ndarray, want: np.ndarray, v: np.ndarray, out_bf16: bool, la
     assert max_abs <= MAX_ABS_FRAC * vmax, f"{label}: max abs {max_abs:.3e} > {MAX_ABS_FRAC}*{vmax:.3e}"
     assert rel <= REL_L2, f"{label}: rel L2 {rel:.3e} > {REL_L2}"
     if out_bf16:
-        # a bf16 result is within one bf16 ulp of the exact value
+        # A bf16 result is the fp32 result rounded once: within one bf16 ulp of
+        # the exact value, plus the fp32 pipeline's own absolute error, which
+        # dominates for outputs near zero (cancellation in the weighted sum).
         ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(want), 1e-300))) - 7)
-        assert np.all(np.abs(got - want) <= ulp * 1.0001 + 1e-30), f"{label}: beyond one bf16 ulp"
+        fp32_abs = 1e-6 * vmax
+        bad = np.abs(got - want) > ulp + fp32_abs
+        assert not np.any(bad), f"{label}: {int(bad.sum())} values beyond one bf16 ulp + {fp32_abs:.1e}"
     return max_abs, rel
 
 

@@ -46,7 +46,7 @@ def test_workspace_and_plan_queries():
     assert sana.sana_linattn_workspace_bytes(0, 70, 16384, 32, 0) == 0
     assert sana.sana_linattn_workspace_bytes(1, 70, 0, 32, 0) == 0
     info = sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 70, 16384, 32, 0)
-    assert info["mfma"] == 1 and info["chunk_tokens"] % 128 == 0 and info["apply_tokens"] % 64 == 0
+    assert info["mfma"] == 1 and info["chunk_tokens"] % 64 == 0 and info["apply_tokens"] % 64 == 0
     assert info["num_chunks"] * info["chunk_tokens"] >= 16384
     assert sana.sana_linattn_plan_info(sana.SANA_DT_F32, 1, 2, 256, 32, 0)["mfma"] == 0
     bc = sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 70, 16384, 32, 1000)
@@ -57,11 +57,11 @@ def test_tuning_environment(monkeypatch):
     monkeypatch.setenv("SANA_LINATTN_CHUNK", "300")
     monkeypatch.setenv("SANA_LINATTN_APPLY_TILE", "100")
     info = sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 70, 16384, 32, 0)
-    assert info["chunk_tokens"] == 384 and info["apply_tokens"] == 128
+    assert info["chunk_tokens"] == 320 and info["apply_tokens"] == 128
     monkeypatch.setenv("SANA_LINATTN_PATH", "valu")
     assert sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 70, 16384, 32, 0)["mfma"] == 0
     monkeypatch.setenv("SANA_LINATTN_CHUNK", "junk")
-    assert sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 70, 16384, 32, 0)["chunk_tokens"] % 128 == 0
+    assert sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 70, 16384, 32, 0)["chunk_tokens"] % 64 == 0
 
 
 @pytest.mark.parametrize("args,code", [
@@ -130,3 +130,20 @@ def test_blockcausal_and_stage_argument_errors():
     for stages in (0, 8, -1, 15):
         assert sana.lib.sana_linattn_fwd_stages(*args, 0, *tail, stages) == sana.SANA_ERR_INVALID_ARG
     assert sana.lib.sana_linattn_fwd_stages(*args, -1, *tail, 7) == sana.SANA_ERR_INVALID_ARG
+
+
+def test_one_hip_runtime_in_the_process():
+    # The library must bind to the HIP runtime torch brings in, whatever the
+    # import order: with two runtimes (or torch on the system one) torch's GPU
+    # calls fail.
+    import subprocess
+    import sys
+    code = ("import diffusion_transformer_relu_amd, torch, os\n"
+            "maps = open('/proc/self/maps').read().split('\\n')\n"
+            "paths = sorted({l.split()[-1] for l in maps if 'libamdhip64' in l})\n"
+            "bundled = os.path.join(os.path.dirname(torch.__file__), 'lib', 'libamdhip64.so')\n"
+            "print(len(paths), int(not os.path.exists(bundled) or paths == [bundled]), paths)\n")
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert res.returncode == 0, res.stderr
+    n, is_torch_runtime = res.stdout.split()[:2]
+    assert n == "1" and is_torch_runtime == "1", res.stdout

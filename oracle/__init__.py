@@ -34,7 +34,7 @@ def _load():
         lib.oracle_linattn_fwd.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-            ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+            ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -58,13 +58,15 @@ def num_blocks(N: int, block_len: int | None) -> int:
 
 
 def linattn_fwd(q, k, v, *, block_len: int | None = None, eps: float = 1e-15,
-                nthreads: int = 0, return_states: bool = False):
+                nthreads: int = 0, return_states: bool = False, state_in=None):
     """fp64 LiteLA forward on host arrays of shape [B, N, H, D].
 
     q, k, v: float32, or uint16 holding bfloat16 bits (all three the same).
     block_len: None/0 for non-causal, else the frame-block length in tokens.
+    state_in: optional float64 [B, H, D, D+1], the state before the first token
+    (a carried state from an earlier call over the preceding tokens).
     Returns out as float64 [B, N, H, D]; with return_states also the inclusive
-    per-block states, float64 [B, H, NB, D, D+1].
+    per-block states, float64 [B, H, NB, D, D+1] (the last one is the final state).
     """
     q = np.ascontiguousarray(q)
     k = np.ascontiguousarray(k)
@@ -79,10 +81,15 @@ def linattn_fwd(q, k, v, *, block_len: int | None = None, eps: float = 1e-15,
     states = None
     if return_states:
         states = np.empty((B, H, max(num_blocks(N, block_len), 1), D, D + 1), dtype=np.float64)
+    if state_in is not None:
+        state_in = np.ascontiguousarray(state_in, dtype=np.float64)
+        if state_in.shape != (B, H, D, D + 1):
+            raise ValueError(f"state_in must be [B, H, D, D+1] = {(B, H, D, D + 1)}")
     rc = _load().oracle_linattn_fwd(
         q.ctypes.data, k.ctypes.data, v.ctypes.data, code, B, H, N, D,
         int(block_len or 0), float(eps), out.ctypes.data,
-        states.ctypes.data if states is not None else None, int(nthreads))
+        states.ctypes.data if states is not None else None,
+        state_in.ctypes.data if state_in is not None else None, int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_linattn_fwd failed ({rc})")
     return (out, states) if return_states else out

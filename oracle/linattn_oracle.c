@@ -30,6 +30,13 @@
  * 0..beta (bidirectional inside its own block, causal across blocks).
  * block_len <= 0, or >= N, is the non-causal operator.
  *
+ * Carried state (the same page, same section: the running statistics act as a
+ * constant-memory cache that lets a long video be generated piece by piece):
+ * an optional state_in gives S before the first token of this call, so that a
+ * sequence cut at block boundaries and processed call by call, each call
+ * starting from the previous call's final state, gives the same outputs as one
+ * call over the whole sequence.
+ *
  * Arithmetic: every input element is decoded exactly to double (bf16 bits are
  * the upper half of an IEEE float32), and all sums run sequentially in token
  * order in double precision.  No blocking or reordering beyond that.
@@ -62,15 +69,17 @@ static double relu(double x) { return x > 0.0 ? x : 0.0; }
 int oracle_abi_version(void) { return 1; }
 
 /*
- * out    : [B][N][H][D] doubles (written).
- * states : optional, [B][H][NB][D][D+1] doubles: S after each block has been
- *          added (inclusive prefix); NB = number of blocks (1 if non-causal).
+ * out      : [B][N][H][D] doubles (written).
+ * states   : optional, [B][H][NB][D][D+1] doubles: S after each block has been
+ *            added (inclusive prefix); NB = number of blocks (1 if non-causal).
+ * state_in : optional, [B][H][D][D+1] doubles: S before the first token
+ *            (NULL = zero).
  * nthreads <= 0 leaves the OpenMP default.
  * Returns 0 on success, -1 on bad arguments.
  */
 int oracle_linattn_fwd(const void* q, const void* k, const void* v, int in_dtype,
                        int B, int H, int N, int D, int block_len, double eps,
-                       double* out, double* states, int nthreads) {
+                       double* out, double* states, const double* state_in, int nthreads) {
     if (B < 0 || H < 0 || N < 0 || D < 1) return -1;
     if (in_dtype != ORACLE_F32 && in_dtype != ORACLE_BF16) return -1;
     if (B == 0 || H == 0 || N == 0) return 0;
@@ -98,7 +107,10 @@ int oracle_linattn_fwd(const void* q, const void* k, const void* v, int in_dtype
 #pragma omp for schedule(dynamic, 1)
             for (long bh = 0; bh < (long)B * H; ++bh) {
                 const int b = (int)(bh / H), h = (int)(bh % H);
-                memset(S, 0, sizeof(double) * (size_t)D * W);
+                if (state_in)
+                    memcpy(S, state_in + (size_t)bh * D * W, sizeof(double) * (size_t)D * W);
+                else
+                    memset(S, 0, sizeof(double) * (size_t)D * W);
                 for (int beta = 0; beta < NB; ++beta) {
                     const int n0 = beta * L;
                     const int n1 = (n0 + L < N) ? n0 + L : N;

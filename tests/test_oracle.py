@@ -270,6 +270,31 @@ def test_block_len_one_is_token_causal_cumsum():
     np.testing.assert_allclose(got, r[:, :D] / (r[:, D:] + 1e-15), rtol=1e-12, atol=1e-14)
 
 
+@pytest.mark.parametrize("L,cuts", [(64, (0, 128, 192, 300)), (1, (0, 5, 6, 40)), (100, (0, 300))])
+def test_carried_state_chunks_equal_one_shot(L, cuts):
+    # A sequence cut at block boundaries and processed call by call, each call
+    # starting from the previous call's final state, equals one call over it all
+    # (the summation order is the same, so the fp64 results are identical).
+    N = 300
+    q, k, v = rand_inputs(19, 2, N, 3, 32, bf16=True)
+    full = oracle.linattn_fwd(q, k, v, block_len=L)
+    st = None
+    for a, b in zip(cuts, list(cuts[1:]) + [N]):
+        if a == b:
+            continue
+        part, states = oracle.linattn_fwd(q[:, a:b], k[:, a:b], v[:, a:b], block_len=L,
+                                          return_states=True, state_in=st)
+        assert np.array_equal(part, full[:, a:b])
+        st = states[:, :, -1]
+    # and the final carried state is relu(K)^T [V | 1] over the whole sequence
+    K = np.maximum(decode(k), 0.0)
+    V = decode(v)
+    for b in range(2):
+        for h in range(3):
+            np.testing.assert_allclose(st[b, h, :, :32], K[b, :, h].T @ V[b, :, h], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(st[b, h, :, 32], K[b, :, h].sum(0), rtol=1e-13, atol=0)
+
+
 def test_empty_inputs():
     z = np.zeros((1, 0, 2, 32), np.float32)
     assert oracle.linattn_fwd(z, z, z).shape == (1, 0, 2, 32)

@@ -42,6 +42,8 @@ _SIGNATURES = {
                               ctypes.c_size_t, _P]),
     "sana_linattn_blockcausal_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
                                           _P, ctypes.c_size_t, _P]),
+    "sana_linattn_blockcausal_stream_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
+                                                 _P, _P, _P, ctypes.c_size_t, _P]),
     "sana_linattn_fwd_stages": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P,
                                      ctypes.c_size_t, _P, _I]),
 }
@@ -151,6 +153,23 @@ def sana_linattn_blockcausal_fwd(q, k, v, out, workspace, block_len: int, *, eps
                                             workspace.numel() * workspace.element_size(),
                                             _stream_handle(stream)),
            "sana_linattn_blockcausal_fwd")
+
+
+def sana_linattn_blockcausal_stream_fwd(q, k, v, out, workspace, block_len: int, state_in=None,
+                                        state_out=None, *, eps: float = 1e-15, stream=None):
+    """Block-causal forward continuing a sequence: state_in / state_out are
+    float32 [B, H, D, D+1] GPU tensors (or None) holding the carried state."""
+    B, N, H, D = _shape(q, k, v, out)
+    for name, t in (("state_in", state_in), ("state_out", state_out)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous() or t.dtype != _torch().float32
+                              or tuple(t.shape) != (B, H, D, D + 1)):
+            raise ValueError(f"{name} must be a contiguous float32 [B, H, D, D+1] GPU tensor")
+    _check(lib.sana_linattn_blockcausal_stream_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dtype_code(q), dtype_code(out), B, H, N, D,
+        block_len, eps, state_in.data_ptr() if state_in is not None else None,
+        state_out.data_ptr() if state_out is not None else None, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(stream)),
+        "sana_linattn_blockcausal_stream_fwd")
 
 
 def sana_linattn_fwd_stages(q, k, v, out, workspace, stages: int, *, block_len: int = 0,

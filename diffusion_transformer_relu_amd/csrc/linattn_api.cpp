@@ -114,7 +114,8 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 
 int forward(const void* q, const void* k, const void* v, void* out, int in_dtype, int out_dtype,
             int B, int H, int N, int D, int block_len, float eps, void* workspace,
-            size_t workspace_bytes, hipStream_t stream, int stages) {
+            size_t workspace_bytes, hipStream_t stream, int stages,
+            const float* state_in = nullptr, float* state_out = nullptr) {
     Plan pl;
     const int st = make_plan(in_dtype, out_dtype, B, H, N, D, block_len, &pl);
     if (st != SANA_OK) return st;
@@ -133,6 +134,18 @@ int forward(const void* q, const void* k, const void* v, void* out, int in_dtype
     if (overlaps(workspace, pl.bytes, q, in_bytes) || overlaps(workspace, pl.bytes, k, in_bytes) ||
         overlaps(workspace, pl.bytes, v, in_bytes) || overlaps(workspace, pl.bytes, out, out_bytes))
         return SANA_ERR_ALIAS;
+    if (state_in || state_out) {
+        const size_t sb = (size_t)B * H * sana::kStateFloats * sizeof(float);
+        if ((state_in && !aligned(state_in, 4)) || (state_out && !aligned(state_out, 4)))
+            return SANA_ERR_ALIGNMENT;
+        if (state_in && (overlaps(state_in, sb, out, out_bytes) || overlaps(state_in, sb, workspace, pl.bytes)))
+            return SANA_ERR_ALIAS;
+        if (state_out && (overlaps(state_out, sb, q, in_bytes) || overlaps(state_out, sb, k, in_bytes) ||
+                          overlaps(state_out, sb, v, in_bytes) || overlaps(state_out, sb, out, out_bytes) ||
+                          overlaps(state_out, sb, workspace, pl.bytes) ||
+                          (state_in && state_in != state_out && overlaps(state_out, sb, state_in, sb))))
+            return SANA_ERR_ALIAS;
+    }
     if (workspace_bytes < pl.bytes) return SANA_ERR_WORKSPACE;
 
     uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -140,7 +153,7 @@ int forward(const void* q, const void* k, const void* v, void* out, int in_dtype
     float* state = reinterpret_cast<float*>(ws + pl.off_state);
     if ((stages & SANA_STAGE_STATE) && sana::launch_state(pl, k, v, part, stream) != hipSuccess)
         return SANA_ERR_HIP;
-    if ((stages & SANA_STAGE_MERGE) && sana::launch_merge(pl, part, state, stream) != hipSuccess)
+    if ((stages & SANA_STAGE_MERGE) && sana::launch_merge(pl, part, state, state_in, state_out, stream) != hipSuccess)
         return SANA_ERR_HIP;
     if ((stages & SANA_STAGE_APPLY) && sana::launch_apply(pl, q, state, out, eps, stream) != hipSuccess)
         return SANA_ERR_HIP;
@@ -203,6 +216,15 @@ int sana_linattn_blockcausal_fwd(const void* q, const void* k, const void* v, vo
     if (block_len < 1) return SANA_ERR_INVALID_ARG;
     return forward(q, k, v, out, in_dtype, out_dtype, B, H, N, D, block_len, eps, workspace,
                    workspace_bytes, stream, SANA_STAGE_ALL);
+}
+
+int sana_linattn_blockcausal_stream_fwd(const void* q, const void* k, const void* v, void* out, int in_dtype,
+                                        int out_dtype, int B, int H, int N, int D, int block_len, float eps,
+                                        const float* state_in, float* state_out, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+    if (block_len < 1) return SANA_ERR_INVALID_ARG;
+    return forward(q, k, v, out, in_dtype, out_dtype, B, H, N, D, block_len, eps, workspace,
+                   workspace_bytes, stream, SANA_STAGE_ALL, state_in, state_out);
 }
 
 int sana_linattn_fwd_stages(const void* q, const void* k, const void* v, void* out, int in_dtype,

@@ -44,7 +44,8 @@ struct Plan {
 
 // Each launcher enqueues one kernel on `stream` and returns hipGetLastError().
 hipError_t launch_state(const Plan& pl, const void* k, const void* v, float* part, hipStream_t stream);
-hipError_t launch_merge(const Plan& pl, const float* part, float* state, hipStream_t stream);
+hipError_t launch_merge(const Plan& pl, const float* part, float* state, const float* state_in,
+                        float* state_out, hipStream_t stream);
 hipError_t launch_apply(const Plan& pl, const void* q, const float* state, void* out, float eps,
                         hipStream_t stream);
 

@@ -259,19 +259,23 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_valu(
 
 // ------------------------------------------------------------------ merge / block scan
 // grid.x = (b * H + h) * kMergeGroups + m; thread t owns state entry
-// e = m * kMergeThreads + t.  For each block it sums that block's chunk
-// partials (groups of 8 loads in flight, added as a fixed pairwise tree), and
-// adds the block sum to the running state (inclusive prefix over blocks).
+// e = m * kMergeThreads + t.  Starting from the carried state (or zero), for
+// each block it sums that block's chunk partials (groups of 8 loads in flight,
+// added as a fixed pairwise tree), and adds the block sum to the running state
+// (inclusive prefix over blocks); the final running state is the carried state
+// out.  state_in and state_out may be the same array: each thread reads its own
+// entry before it writes it.
 constexpr int kMergeGroups = (kStateFloats + kMergeThreads - 1) / kMergeThreads;
 
 __global__ __launch_bounds__(kMergeThreads) void k_merge(
-    const float* __restrict__ part, float* __restrict__ state, int NB, int cpb, int P) {
+    const float* __restrict__ part, float* __restrict__ state, const float* state_in, float* state_out,
+    int NB, int cpb, int P) {
     const size_t bh = blockIdx.x / kMergeGroups;
     const int e = (blockIdx.x % kMergeGroups) * kMergeThreads + threadIdx.x;
     if (e >= kStateFloats) return;
     const float* src = part + bh * P * kStateFloats + e;
     float* dst = state + bh * NB * kStateFloats + e;
-    float acc = 0.f;
+    float acc = state_in ? state_in[bh * kStateFloats + e] : 0.f;
 #pragma unroll 4
     for (int beta = 0; beta < NB; ++beta) {
         const float* blk = src + (size_t)beta * cpb * kStateFloats;
@@ -286,6 +290,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(
         acc += bs;
         dst[(size_t)beta * kStateFloats] = acc;
     }
+    if (state_out) state_out[bh * kStateFloats + e] = acc;
 }
 
 // ------------------------------------------------------------------ apply, bf16, MFMA
@@ -471,9 +476,11 @@ hipError_t launch_state(const Plan& pl, const void* k, const void* v, float* par
     return hipGetLastError();
 }
 
-hipError_t launch_merge(const Plan& pl, const float* part, float* state, hipStream_t stream) {
+hipError_t launch_merge(const Plan& pl, const float* part, float* state, const float* state_in,
+                        float* state_out, hipStream_t stream) {
     const unsigned grid = (unsigned)((size_t)pl.B * pl.H * kMergeGroups);
-    hipLaunchKernelGGL(k_merge, dim3(grid), dim3(kMergeThreads), 0, stream, part, state, pl.NB, pl.cpb, pl.P);
+    hipLaunchKernelGGL(k_merge, dim3(grid), dim3(kMergeThreads), 0, stream, part, state, state_in, state_out,
+                       pl.NB, pl.cpb, pl.P);
     return hipGetLastError();
 }
 

@@ -149,6 +149,32 @@ SANA_API int sana_linattn_blockcausal_fwd(const void* q, const void* k, const vo
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Streaming block-causal forward with a carried state: the tokens of this call
+ * continue a longer sequence whose earlier tokens are summarised by state_in,
+ * the "constant-memory KV cache" of the video section ("How Linear Attention
+ * ...", section "Video Generation and Constant-Memory KV Cache").  Token i in
+ * block beta uses state_in plus the state of this call's blocks 0..beta; on
+ * return state_out holds state_in plus the state of all of this call's tokens,
+ * ready to be passed as state_in of the next call.  A sequence cut at block
+ * boundaries (every call but the last covers whole blocks) and processed call
+ * by call gives the outputs of one sana_linattn_blockcausal_fwd over it all.
+ *   state_in   [B][H][D][D+1] fp32, device, read only; NULL = zero state (the
+ *              first call).  Row j holds S[j][0..D-1] (sum of phi(k_j) * v)
+ *              and S[j][D] (sum of phi(k_j)).
+ *   state_out  [B][H][D][D+1] fp32, device, written; NULL = not wanted.  May be
+ *              the same pointer as state_in (updated in place), must not
+ *              otherwise overlap any other buffer.
+ * Other arguments as for sana_linattn_blockcausal_fwd (block_len >= N makes the
+ * call a single block).  With B, H or N = 0 nothing is enqueued and state_out
+ * is left as it is.  Both state pointers need 4-byte alignment.
+ */
+SANA_API int sana_linattn_blockcausal_stream_fwd(const void* q, const void* k, const void* v, void* out,
+                                                 int in_dtype, int out_dtype, int B, int H, int N, int D,
+                                                 int block_len, float eps, const float* state_in,
+                                                 float* state_out, void* workspace, size_t workspace_bytes,
+                                                 hipStream_t stream);
+
+/*
  * The same forward split into its three kernels, for per-kernel timing: a call
  * runs the stages whose bits are set in `stages`, in the order state, merge,
  * apply.  Calling it three times with SANA_STAGE_STATE, SANA_STAGE_MERGE and

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 8, names
     for n in names:
         assert hasattr(sana.lib, n), n           # resolves in the shared library
         assert n in sana._SIGNATURES, n          # and the binding declares its signature
@@ -147,3 +147,18 @@ def test_one_hip_runtime_in_the_process():
     assert res.returncode == 0, res.stderr
     n, is_torch_runtime = res.stdout.split()[:2]
     assert n == "1" and is_torch_runtime == "1", res.stdout
+
+
+def test_stream_argument_errors():
+    S0 = A + 700 * MB
+    args = (A, A + 64 * MB, A + 128 * MB, A + 192 * MB, 1, 0, 1, 2, 256, 32)
+    ws = (A + 512 * MB, 1 << 30, None)
+    f = sana.lib.sana_linattn_blockcausal_stream_fwd
+    assert f(*args, 0, 1e-15, S0, S0, *ws) == sana.SANA_ERR_INVALID_ARG          # block_len < 1
+    assert f(*args, 64, 1e-15, S0 + 2, None, *ws) == sana.SANA_ERR_ALIGNMENT
+    assert f(*args, 64, 1e-15, None, S0 + 1, *ws) == sana.SANA_ERR_ALIGNMENT
+    assert f(*args, 64, 1e-15, None, A, *ws) == sana.SANA_ERR_ALIAS               # state_out = q
+    assert f(*args, 64, 1e-15, A + 192 * MB, None, *ws) == sana.SANA_ERR_ALIAS    # state_in = out
+    assert f(*args, 64, 1e-15, S0, S0 + 64, *ws) == sana.SANA_ERR_ALIAS           # partly overlapping states
+    # in place (state_out == state_in) is allowed: the call gets as far as the workspace check
+    assert f(*args, 64, 1e-15, S0, S0, A + 512 * MB, 16, None) == sana.SANA_ERR_WORKSPACE

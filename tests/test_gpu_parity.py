@@ -138,3 +138,38 @@ def test_device_argument_errors_leave_output_untouched():
     assert P(*args(I, out.data_ptr(), ws.data_ptr() + 128, need)) == sana.SANA_ERR_ALIGNMENT
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
+
+
+@pytest.mark.parametrize("w,cuts", [
+    (workloads.Workload("stream_B2_N4096_H6_L512", 2, 4096, 6, 32, workloads.DT_BF16, seed=31, block_len=512),
+     (0, 1024, 2560)),
+    (workloads.Workload("stream_B1_N1000_H3_L64_f32", 1, 1000, 3, 32, workloads.DT_F32, seed=32, block_len=64),
+     (0, 64, 640)),
+    (workloads.BLOCK_CAUSAL, (0, 4096, 8192, 12288)),
+], ids=lambda x: x.name if hasattr(x, "name") else str(len(x)))
+def test_streaming_chunks_match_one_shot(w, cuts):
+    """Block-aligned chunks, each call continuing from the previous call's
+    carried state (updated in place), reproduce the one-shot block-causal
+    output; the final carried state is the whole sequence's state."""
+    import diffusion_transformer_relu_amd as sana
+    (q, k, v), want = inputs_and_oracle(w)
+    _, st_want = oracle.linattn_fwd(q, k, v, block_len=w.block_len, return_states=True)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    B, N, H, D = qd.shape
+    out = torch.empty((B, N, H, D), dtype=torch.float32, device="cuda:0")
+    state = torch.empty((B, H, D, D + 1), dtype=torch.float32, device="cuda:0")
+    bounds = list(cuts) + [N]
+    for c, (a, b) in enumerate(zip(bounds[:-1], bounds[1:])):
+        n = b - a
+        ws = torch.empty(sana.sana_linattn_workspace_bytes(B, H, n, D, w.block_len), dtype=torch.uint8,
+                         device="cuda:0")
+        o = torch.empty((B, n, H, D), dtype=torch.float32, device="cuda:0")
+        sana.sana_linattn_blockcausal_stream_fwd(qd[:, a:b].contiguous(), kd[:, a:b].contiguous(),
+                                                 vd[:, a:b].contiguous(), o, ws, w.block_len,
+                                                 state_in=state if c else None, state_out=state, eps=w.eps)
+        out[:, a:b] = o
+    torch.cuda.synchronize()
+    compare(out.cpu().double().numpy(), want, v, False, w.name)
+    got_state = state.cpu().double().numpy()
+    final = st_want[:, :, -1]
+    assert np.max(np.abs(got_state - final)) <= 1e-5 * np.max(np.abs(final))

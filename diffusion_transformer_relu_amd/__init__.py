@@ -44,6 +44,8 @@ _SIGNATURES = {
                                           _P, ctypes.c_size_t, _P]),
     "sana_linattn_blockcausal_stream_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
                                                  _P, _P, _P, ctypes.c_size_t, _P]),
+    "sana_linattn_fwd_strided": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
+                                      ctypes.POINTER(ctypes.c_int64), _P, ctypes.c_size_t, _P]),
     "sana_linattn_fwd_stages": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P,
                                      ctypes.c_size_t, _P, _I]),
 }
@@ -172,6 +174,30 @@ def sana_linattn_blockcausal_stream_fwd(q, k, v, out, workspace, block_len: int,
         "sana_linattn_blockcausal_stream_fwd")
 
 
+def _view_shape(q, k, v, out):
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.dim() != 4 or not t.is_cuda or t.stride(3) != 1 or t.stride(2) != t.shape[3]:
+            raise ValueError(f"{name} must be a 4-d [B, N, H, D] GPU view with contiguous heads")
+    if not (q.shape == k.shape == v.shape == out.shape):
+        raise ValueError("q, k, v and out must share one [B, N, H, D] shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    return tuple(q.shape)
+
+
+def sana_linattn_fwd_strided(q, k, v, out, workspace, *, block_len: int = 0, eps: float = 1e-15,
+                             stream=None):
+    """Forward on [B, N, H, D] views with free batch/token strides (e.g. the
+    q, k, v slices of one fused qkv projection), read in place."""
+    B, N, H, D = _view_shape(q, k, v, out)
+    st = (ctypes.c_int64 * 8)(q.stride(0), q.stride(1), k.stride(0), k.stride(1), v.stride(0), v.stride(1),
+                              out.stride(0), out.stride(1))
+    _check(lib.sana_linattn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dtype_code(q),
+                                        dtype_code(out), B, H, N, D, block_len, eps, st, workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), _stream_handle(stream)),
+           "sana_linattn_fwd_strided")
+
+
 def sana_linattn_fwd_stages(q, k, v, out, workspace, stages: int, *, block_len: int = 0,
                             eps: float = 1e-15, stream=None):
     """Runs the selected kernels (SANA_STAGE_* bits) of the forward."""
@@ -192,7 +218,9 @@ def linattn_fwd(q, k, v, *, eps: float = 1e-15, out_dtype=None, block_len: int |
     B, N, H, D = q.shape
     ws = torch.empty(max(sana_linattn_workspace_bytes(B, H, N, D, block_len or 0), 1),
                      dtype=torch.uint8, device=q.device)
-    if block_len is None:
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        sana_linattn_fwd_strided(q, k, v, out, ws, block_len=block_len or 0, eps=eps, stream=stream)
+    elif block_len is None:
         sana_linattn_fwd(q, k, v, out, ws, eps=eps, stream=stream)
     else:
         sana_linattn_blockcausal_fwd(q, k, v, out, ws, block_len, eps=eps, stream=stream)

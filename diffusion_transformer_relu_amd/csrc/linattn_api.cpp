@@ -112,27 +112,62 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// Bytes spanned by a [B][N][H][D] view with element strides st (B, N >= 1).
+size_t extent_bytes(sana::Strides st, int B, int N, int H, int D, size_t es) {
+    return (size_t)((B - 1) * st.b + (long long)(N - 1) * st.n + (long long)H * D) * es;
+}
+
+// Whether the (b, n) rows of H*D elements of a view with strides st are
+// pairwise disjoint (required of the output).
+bool rows_disjoint(sana::Strides st, int B, int N, int H, int D) {
+    const long long row = (long long)H * D;
+    long long s1 = st.n, c1 = N, s2 = st.b, c2 = B;   // inner and outer row strides and counts
+    if (c1 == 1) { s1 = s2; c1 = c2; s2 = 0; c2 = 1; }
+    if (c2 > 1 && s2 < s1) { std::swap(s1, s2); std::swap(c1, c2); }
+    if (c1 > 1 && s1 < row) return false;
+    if (c2 > 1 && s2 < (c1 - 1) * s1 + row) return false;
+    return true;
+}
+
 int forward(const void* q, const void* k, const void* v, void* out, int in_dtype, int out_dtype,
             int B, int H, int N, int D, int block_len, float eps, void* workspace,
             size_t workspace_bytes, hipStream_t stream, int stages,
-            const float* state_in = nullptr, float* state_out = nullptr) {
+            const float* state_in = nullptr, float* state_out = nullptr,
+            const int64_t* strides = nullptr) {
     Plan pl;
     const int st = make_plan(in_dtype, out_dtype, B, H, N, D, block_len, &pl);
     if (st != SANA_OK) return st;
     if (!std::isfinite(eps) || eps < 0.f) return SANA_ERR_INVALID_ARG;
     if (stages <= 0 || (stages & ~SANA_STAGE_ALL)) return SANA_ERR_INVALID_ARG;
+    const size_t es_in = in_dtype == SANA_DT_BF16 ? 2 : 4;
+    const size_t es_out = out_dtype == SANA_DT_BF16 ? 2 : 4;
+    const sana::Strides dense = {(long long)N * H * D, (long long)H * D};
+    pl.sq = pl.sk = pl.sv = pl.so = dense;
+    if (strides) {
+        for (int i = 0; i < 8; ++i)
+            if (strides[i] < 0 || strides[i] > (1LL << 46)) return SANA_ERR_INVALID_ARG;
+        pl.sq = {strides[0], strides[1]};
+        pl.sk = {strides[2], strides[3]};
+        pl.sv = {strides[4], strides[5]};
+        pl.so = {strides[6], strides[7]};
+        for (int i = 0; i < 8; ++i)   // every row starts 16-byte aligned
+            if ((strides[i] * (long long)(i < 6 ? es_in : es_out)) % 16) return SANA_ERR_ALIGNMENT;
+        if (B > 0 && H > 0 && N > 0 && !rows_disjoint(pl.so, B, N, H, D)) return SANA_ERR_ALIAS;
+    }
     if (B == 0 || H == 0 || N == 0) return SANA_OK;
     if (!q || !k || !v || !out || !workspace) return SANA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(workspace, 256))
         return SANA_ERR_ALIGNMENT;
-    const size_t elems = (size_t)B * N * H * D;
-    const size_t in_bytes = elems * (in_dtype == SANA_DT_BF16 ? 2 : 4);
-    const size_t out_bytes = elems * (out_dtype == SANA_DT_BF16 ? 2 : 4);
-    if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, k, in_bytes) ||
-        overlaps(out, out_bytes, v, in_bytes))
+    const size_t q_bytes = extent_bytes(pl.sq, B, N, H, D, es_in);
+    const size_t k_bytes = extent_bytes(pl.sk, B, N, H, D, es_in);
+    const size_t v_bytes = extent_bytes(pl.sv, B, N, H, D, es_in);
+    const size_t out_bytes = extent_bytes(pl.so, B, N, H, D, es_out);
+    const size_t in_bytes = std::max(q_bytes, std::max(k_bytes, v_bytes));
+    if (overlaps(out, out_bytes, q, q_bytes) || overlaps(out, out_bytes, k, k_bytes) ||
+        overlaps(out, out_bytes, v, v_bytes))
         return SANA_ERR_ALIAS;
-    if (overlaps(workspace, pl.bytes, q, in_bytes) || overlaps(workspace, pl.bytes, k, in_bytes) ||
-        overlaps(workspace, pl.bytes, v, in_bytes) || overlaps(workspace, pl.bytes, out, out_bytes))
+    if (overlaps(workspace, pl.bytes, q, q_bytes) || overlaps(workspace, pl.bytes, k, k_bytes) ||
+        overlaps(workspace, pl.bytes, v, v_bytes) || overlaps(workspace, pl.bytes, out, out_bytes))
         return SANA_ERR_ALIAS;
     if (state_in || state_out) {
         const size_t sb = (size_t)B * H * sana::kStateFloats * sizeof(float);
@@ -140,8 +175,9 @@ int forward(const void* q, const void* k, const void* v, void* out, int in_dtype
             return SANA_ERR_ALIGNMENT;
         if (state_in && (overlaps(state_in, sb, out, out_bytes) || overlaps(state_in, sb, workspace, pl.bytes)))
             return SANA_ERR_ALIAS;
-        if (state_out && (overlaps(state_out, sb, q, in_bytes) || overlaps(state_out, sb, k, in_bytes) ||
-                          overlaps(state_out, sb, v, in_bytes) || overlaps(state_out, sb, out, out_bytes) ||
+        (void)in_bytes;
+        if (state_out && (overlaps(state_out, sb, q, q_bytes) || overlaps(state_out, sb, k, k_bytes) ||
+                          overlaps(state_out, sb, v, v_bytes) || overlaps(state_out, sb, out, out_bytes) ||
                           overlaps(state_out, sb, workspace, pl.bytes) ||
                           (state_in && state_in != state_out && overlaps(state_out, sb, state_in, sb))))
             return SANA_ERR_ALIAS;
@@ -225,6 +261,15 @@ int sana_linattn_blockcausal_stream_fwd(const void* q, const void* k, const void
     if (block_len < 1) return SANA_ERR_INVALID_ARG;
     return forward(q, k, v, out, in_dtype, out_dtype, B, H, N, D, block_len, eps, workspace,
                    workspace_bytes, stream, SANA_STAGE_ALL, state_in, state_out);
+}
+
+int sana_linattn_fwd_strided(const void* q, const void* k, const void* v, void* out, int in_dtype,
+                             int out_dtype, int B, int H, int N, int D, int block_len, float eps,
+                             const int64_t* strides, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    if (!strides || block_len < 0) return SANA_ERR_INVALID_ARG;
+    return forward(q, k, v, out, in_dtype, out_dtype, B, H, N, D, block_len, eps, workspace,
+                   workspace_bytes, stream, SANA_STAGE_ALL, nullptr, nullptr, strides);
 }
 
 int sana_linattn_fwd_stages(const void* q, const void* k, const void* v, void* out, int in_dtype,

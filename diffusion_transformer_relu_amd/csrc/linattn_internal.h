@@ -27,6 +27,13 @@ constexpr int kStateGroups = 576;
 constexpr int kApplyGroups = kCUs * 5;
 constexpr int kMinChunk = 256;            // keeps the partial states a few % of the K/V bytes
 
+// Element strides of a [B][N][H][D] tensor view: consecutive heads are D
+// elements apart and features are contiguous; batch and token strides are free
+// (e.g. q, k, v as views of one fused qkv projection output).
+struct Strides {
+    long long b, n;
+};
+
 struct Plan {
     int B, H, N;
     int L;        // block length in tokens (N for the non-causal operator)
@@ -40,6 +47,7 @@ struct Plan {
     int mfma;     // 1: bf16 matrix-core kernels, 0: vector kernels
     int in_dtype, out_dtype;
     size_t off_part, off_state, bytes;
+    Strides sq, sk, sv, so;   // element strides of q, k, v, out
 };
 
 // Each launcher enqueues one kernel on `stream` and returns hipGetLastError().

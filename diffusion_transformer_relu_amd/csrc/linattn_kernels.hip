@@ -71,11 +71,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ float load_in(const float* p, size_t i) { return p[i]; }
-__device__ __forceinline__ float load_in(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+__device__ __forceinline__ float load_in(const float* p, long long i) { return p[i]; }
+__device__ __forceinline__ float load_in(const uint16_t* p, long long i) { return bf16_to_f32(p[i]); }
 
-__device__ __forceinline__ void store_out(float* p, size_t i, float x) { p[i] = x; }
-__device__ __forceinline__ void store_out(uint16_t* p, size_t i, float x) { p[i] = f32_to_bf16(x); }
+__device__ __forceinline__ void store_out(float* p, long long i, float x) { p[i] = x; }
+__device__ __forceinline__ void store_out(uint16_t* p, long long i, float x) { p[i] = f32_to_bf16(x); }
 
 // Output stores are non-temporal: out is written once and never read here, and
 // streaming it past the caches raises the write bandwidth markedly on gfx950.
@@ -111,7 +111,7 @@ constexpr int kTensorStride = 2 * kHeadStride;
 // K and V are read once, so their loads are non-temporal.
 __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ part,
-    int N, int H, int HP, int L, int cpb, int P, int chunk) {
+    int N, int H, int HP, int L, int cpb, int P, int chunk, Strides sk, Strides sv) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kTensorStride];
 
     const int p = blockIdx.x % P;
@@ -135,9 +135,9 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
             const int part_ = pc & 3, hd = (pc >> 2) & 1, tok = pc >> 3;
             const int n = t0 + tok;
             if (n < cr.c1 && hd < nh) {
-                const size_t off = (((size_t)b * N + n) * H + h0 + hd) * kD + part_ * 8;
-                rk[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + off));
-                rv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + off));
+                const long long col = (long long)(h0 + hd) * kD + part_ * 8;
+                rk[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + (b * sk.b + n * sk.n + col)));
+                rv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + (b * sv.b + n * sv.n + col)));
             } else {
                 rk[i] = (u32x4){0u, 0u, 0u, 0u};
                 rv[i] = (u32x4){0u, 0u, 0u, 0u};
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
 template <typename InT>
 __global__ __launch_bounds__(kThreads) void k_state_partial_valu(
     const InT* __restrict__ k, const InT* __restrict__ v, float* __restrict__ part,
-    int N, int H, int L, int cpb, int P, int chunk) {
+    int N, int H, int L, int cpb, int P, int chunk, Strides stk, Strides stv) {
     __shared__ float sa[kValuTile][kD + 1];   // ReLU(k) tile
     __shared__ float sv[kValuTile][kW];       // [v | 1] tile
 
@@ -229,9 +229,9 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_valu(
             const int n = t0 + tok;
             float kk = 0.f, vv = 0.f;
             if (n < cr.c1) {
-                const size_t off = (((size_t)b * N + n) * H + h) * kD + jj;
-                kk = load_in(k, off);
-                vv = load_in(v, off);
+                const long long col = (long long)h * kD + jj;
+                kk = load_in(k, b * stk.b + n * stk.n + col);
+                vv = load_in(v, b * stv.b + n * stv.n + col);
             }
             sa[tok][jj] = kk > 0.f ? kk : 0.f;
             sv[tok][jj] = vv;
@@ -312,7 +312,7 @@ constexpr int kOutPitch = 36;   // floats per LDS output row: 32 + 4 keeps rows 
 template <typename OutT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))) void k_apply_mfma(
     const uint16_t* __restrict__ q, const float* __restrict__ state, OutT* __restrict__ out,
-    int N, int H, int HP, int L, int NB, int tile, int tpb, float eps) {
+    int N, int H, int HP, int L, int NB, int tile, int tpb, float eps, Strides sq, Strides so) {
     __shared__ __attribute__((aligned(16))) float otile[4][32 * kOutPitch];
 
     const int per_unit = NB * tpb;
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
     auto load_b = [&](int tt, u32x4& x0, u32x4& x1) {
         const int row = tt + i;
         if (row < t1) {
-            const u32x4* src = reinterpret_cast<const u32x4*>(q + (((size_t)b * N + row) * H + h) * kD + 8 * g);
+            const u32x4* src = reinterpret_cast<const u32x4*>(q + (b * sq.b + row * sq.n + h * kD + 8 * g));
             x0 = src[0];
             x1 = src[2];
         } else {
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
         for (int s4 = 0; s4 < 4; ++s4) {
             const int r = 8 * s4 + (lane >> 3), cc = (lane & 7) * 4;
             const f32x4 x = *reinterpret_cast<const f32x4*>(ot + r * kOutPitch + cc);
-            if (tt + r < t1) store4(out + (((size_t)b * N + tt + r) * H + h) * kD + cc, x);
+            if (tt + r < t1) store4(out + (b * so.b + (tt + r) * so.n + h * kD + cc), x);
         }
         __builtin_amdgcn_wave_barrier();
         a0 = n0;
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
 template <typename InT, typename OutT>
 __global__ __launch_bounds__(kThreads) void k_apply_valu(
     const InT* __restrict__ q, const float* __restrict__ state, OutT* __restrict__ out,
-    int N, int H, int L, int NB, int tpb, float eps) {
+    int N, int H, int L, int NB, int tpb, float eps, Strides sq, Strides so) {
     __shared__ float s[kStateFloats];
     const int tile = blockIdx.x % tpb;
     const size_t bhb = blockIdx.x / tpb;            // (b * H + h) * NB + beta
@@ -435,11 +435,12 @@ __global__ __launch_bounds__(kThreads) void k_apply_valu(
     const int blk1 = min(blk0 + L, N);
     const int row = blk0 + tile * kValuApplyTokens + threadIdx.x;
     if (row >= blk1) return;
-    const size_t base = (((size_t)b * N + row) * H + h) * kD;
+    const long long qbase = b * sq.b + row * sq.n + (long long)h * kD;
+    const long long obase = b * so.b + row * so.n + (long long)h * kD;
     float f[kD];
 #pragma unroll
     for (int jj = 0; jj < kD; ++jj) {
-        const float x = load_in(q, base + jj);
+        const float x = load_in(q, qbase + jj);
         f[jj] = x > 0.f ? x : 0.f;
     }
     float den = 0.f;
@@ -449,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_valu(
         float num = 0.f;
 #pragma unroll
         for (int jj = 0; jj < kD; ++jj) num += f[jj] * s[jj * kW + cc];
-        store_out(out, base + cc, num / (den + eps));
+        store_out(out, obase + cc, num / (den + eps));
     }
 }
 
@@ -461,17 +462,17 @@ hipError_t launch_state(const Plan& pl, const void* k, const void* v, float* par
         const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.P);
         hipLaunchKernelGGL(k_state_partial_mfma, dim3(grid), dim3(kThreads), 0, stream,
                            static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), part,
-                           pl.N, pl.H, pl.HP, pl.L, pl.cpb, pl.P, pl.chunk);
+                           pl.N, pl.H, pl.HP, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
     } else {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.H * pl.P);
         if (pl.in_dtype == 1)
             hipLaunchKernelGGL(k_state_partial_valu<uint16_t>, dim3(grid), dim3(kThreads), 0, stream,
                                static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), part,
-                               pl.N, pl.H, pl.L, pl.cpb, pl.P, pl.chunk);
+                               pl.N, pl.H, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
         else
             hipLaunchKernelGGL(k_state_partial_valu<float>, dim3(grid), dim3(kThreads), 0, stream,
                                static_cast<const float*>(k), static_cast<const float*>(v), part,
-                               pl.N, pl.H, pl.L, pl.cpb, pl.P, pl.chunk);
+                               pl.N, pl.H, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
     }
     return hipGetLastError();
 }
@@ -492,16 +493,18 @@ hipError_t launch_apply(const Plan& pl, const void* q, const float* state, void*
         const uint16_t* qq = static_cast<const uint16_t*>(q);
         if (out_bf16)
             hipLaunchKernelGGL(k_apply_mfma<uint16_t>, dim3(grid), dim3(kThreads), 0, stream, qq, state,
-                               static_cast<uint16_t*>(out), pl.N, pl.H, pl.HP, pl.L, pl.NB, pl.tile, pl.tpb, eps);
+                               static_cast<uint16_t*>(out), pl.N, pl.H, pl.HP, pl.L, pl.NB, pl.tile, pl.tpb, eps,
+                               pl.sq, pl.so);
         else
             hipLaunchKernelGGL(k_apply_mfma<float>, dim3(grid), dim3(kThreads), 0, stream, qq, state,
-                               static_cast<float*>(out), pl.N, pl.H, pl.HP, pl.L, pl.NB, pl.tile, pl.tpb, eps);
+                               static_cast<float*>(out), pl.N, pl.H, pl.HP, pl.L, pl.NB, pl.tile, pl.tpb, eps,
+                               pl.sq, pl.so);
     } else {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.H * pl.NB * pl.tpb);
 #define SANA_APPLY_VALU(IT, OT)                                                                        \
     hipLaunchKernelGGL((k_apply_valu<IT, OT>), dim3(grid), dim3(kThreads), 0, stream,                   \
                        static_cast<const IT*>(q), state, static_cast<OT*>(out), pl.N, pl.H, pl.L, pl.NB, \
-                       pl.tpb, eps)
+                       pl.tpb, eps, pl.sq, pl.so)
         if (pl.in_dtype == 1) {
             if (out_bf16) SANA_APPLY_VALU(uint16_t, uint16_t); else SANA_APPLY_VALU(uint16_t, float);
         } else {

@@ -52,6 +52,7 @@
 #define SANA_LINATTN_H
 
 #include <stddef.h>
+#include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -173,6 +174,25 @@ SANA_API int sana_linattn_blockcausal_stream_fwd(const void* q, const void* k, c
                                                  int block_len, float eps, const float* state_in,
                                                  float* state_out, void* workspace, size_t workspace_bytes,
                                                  hipStream_t stream);
+
+/*
+ * Forward on strided views: q, k, v and out are [B][N][H][D] views whose heads
+ * are D elements apart and whose features are contiguous, but whose batch and
+ * token strides are free -- e.g. q, k and v as the three slices of one fused
+ * qkv projection output [B][N][3][H][D] (token stride 3*H*D), read in place
+ * without a copy.
+ *   block_len  0 = non-causal, >= 1 = block-causal.
+ *   strides    int64[8], in elements: batch and token stride of q, k, v, out,
+ *              in that order; all >= 0 and each a multiple of 16 bytes.  The
+ *              rows of out must not overlap each other (error ALIAS); inputs
+ *              may (a batch stride of 0 broadcasts).
+ * Other arguments as for sana_linattn_fwd; the workspace size does not depend
+ * on the strides.  Overlap checks use the byte range each view spans.
+ */
+SANA_API int sana_linattn_fwd_strided(const void* q, const void* k, const void* v, void* out,
+                                      int in_dtype, int out_dtype, int B, int H, int N, int D,
+                                      int block_len, float eps, const int64_t* strides,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * The same forward split into its three kernels, for per-kernel timing: a call

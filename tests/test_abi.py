@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     for n in names:
         assert hasattr(sana.lib, n), n           # resolves in the shared library
         assert n in sana._SIGNATURES, n          # and the binding declares its signature
@@ -162,3 +162,26 @@ def test_stream_argument_errors():
     assert f(*args, 64, 1e-15, S0, S0 + 64, *ws) == sana.SANA_ERR_ALIAS           # partly overlapping states
     # in place (state_out == state_in) is allowed: the call gets as far as the workspace check
     assert f(*args, 64, 1e-15, S0, S0, A + 512 * MB, 16, None) == sana.SANA_ERR_WORKSPACE
+
+
+def test_strided_argument_errors():
+    H, N, D = 2, 256, 32
+    dense = [N * H * D, H * D] * 4
+    f = sana.lib.sana_linattn_fwd_strided
+    args = (A, A + 64 * MB, A + 128 * MB, A + 192 * MB, 1, 0, 1, H, N, D, 0, 1e-15)
+    tail = (A + 512 * MB, 16, None)     # workspace too small: a passing call stops there, never launches
+    st = lambda xs: (ctypes.c_int64 * 8)(*xs)
+    assert f(*args, st(dense), *tail) == sana.SANA_ERR_WORKSPACE
+    assert f(*args, None, *tail) == sana.SANA_ERR_INVALID_ARG
+    assert f(*args[:10], -1, 1e-15, st(dense), *tail) == sana.SANA_ERR_INVALID_ARG
+    assert f(*args, st([-64] + dense[1:]), *tail) == sana.SANA_ERR_INVALID_ARG
+    assert f(*args, st(dense[:1] + [H * D + 4] + dense[2:]), *tail) == sana.SANA_ERR_ALIGNMENT   # 8-byte rows
+    # fused qkv slices: token stride 3*H*D for q, k, v is fine
+    fused = [N * 3 * H * D, 3 * H * D] * 3 + [N * H * D, H * D]
+    assert f(*args, st(fused), *tail) == sana.SANA_ERR_WORKSPACE
+    # output rows overlapping each other
+    assert f(*args, st(dense[:6] + [N * H * D, H * D // 2]), *tail) == sana.SANA_ERR_ALIAS
+    # [N, B, H, D] output layout (batch stride H*D, token stride B*H*D) is disjoint
+    args2 = args[:6] + (2,) + args[7:]
+    assert f(*args2, st(dense[:6] + [H * D, 2 * H * D]), *tail) == sana.SANA_ERR_WORKSPACE
+    assert f(*args2, st(dense[:6] + [H * D, H * D]), *tail) == sana.SANA_ERR_ALIAS

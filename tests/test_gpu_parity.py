@@ -173,3 +173,58 @@ def test_streaming_chunks_match_one_shot(w, cuts):
     got_state = state.cpu().double().numpy()
     final = st_want[:, :, -1]
     assert np.max(np.abs(got_state - final)) <= 1e-5 * np.max(np.abs(final))
+
+
+STRIDED = [
+    workloads.Workload("qkv_B2_N1000_H3_bf16", 2, 1000, 3, 32, workloads.DT_BF16, seed=41),
+    workloads.Workload("qkv_B2_N1000_H3_L128_f32", 2, 1000, 3, 32, workloads.DT_F32, seed=42, block_len=128),
+    workloads.S1600M_1024,
+]
+
+
+@pytest.mark.parametrize("w", STRIDED, ids=lambda w: w.name)
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["f32out", "bf16out"])
+def test_fused_qkv_views_read_in_place(w, out_dtype):
+    """q, k, v as the three slices of one [B, N, 3, H, D] projection output and
+    out as one slice of a [B, N, 2, H, D] buffer: the result equals the oracle's
+    on the contiguous tensors, and the other output slice stays untouched."""
+    import diffusion_transformer_relu_amd as sana
+    (q, k, v), want = inputs_and_oracle(w)
+    qkv = to_device(np.stack([q, k, v], axis=2))              # [B, N, 3, H, D]
+    qv, kv, vv = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    assert not qv.is_contiguous() and qv.stride(1) == 3 * w.H * 32
+    B, N, H, D = qv.shape
+    buf = torch.full((B, N, 2, H, D), 7.0, dtype=out_dtype, device="cuda:0")
+    out = buf[:, :, 1]
+    ws = torch.empty(sana.sana_linattn_workspace_bytes(B, H, N, D, w.block_len), dtype=torch.uint8, device="cuda:0")
+    sana.sana_linattn_fwd_strided(qv, kv, vv, out, ws, block_len=w.block_len, eps=w.eps)
+    torch.cuda.synchronize()
+    compare(out.float().cpu().double().numpy(), want, v, out_dtype == torch.bfloat16, w.name)
+    assert torch.all(buf[:, :, 0] == 7.0)
+
+
+@pytest.mark.parametrize("path", ["mfma", "valu"])
+def test_broadcast_and_transposed_views(monkeypatch, path):
+    """A batch stride of 0 (k, v shared by both batches) and an output laid out
+    [N, B, H, D] give the oracle's result on the materialised tensors; the
+    strided result is bitwise the contiguous call's."""
+    import diffusion_transformer_relu_amd as sana
+    if path == "valu":
+        monkeypatch.setenv("SANA_LINATTN_PATH", "valu")
+    w = workloads.Workload("bcast_B1_N777_H4_bf16", 1, 777, 4, 32, workloads.DT_BF16, seed=43)
+    q1, k1, v1 = workloads.make_inputs(w)
+    q2, _, _ = workloads.make_inputs(workloads.with_shape(w, seed=44))
+    q = np.concatenate([q1, q2], axis=0)
+    k, v = np.concatenate([k1, k1], axis=0), np.concatenate([v1, v1], axis=0)
+    want = oracle.linattn_fwd(q, k, v, eps=w.eps)
+    qd, kd, vd = to_device(q), to_device(k1).expand(2, -1, -1, -1), to_device(v1).expand(2, -1, -1, -1)
+    assert kd.stride(0) == 0
+    B, N, H, D = qd.shape
+    out = torch.empty((N, B, H, D), dtype=torch.float32, device="cuda:0").permute(1, 0, 2, 3)
+    ws = torch.empty(sana.sana_linattn_workspace_bytes(B, H, N, D, 0), dtype=torch.uint8, device="cuda:0")
+    sana.sana_linattn_fwd_strided(qd, kd, vd, out, ws, eps=w.eps)
+    dense = torch.empty((B, N, H, D), dtype=torch.float32, device="cuda:0")
+    sana.sana_linattn_fwd(qd, kd.contiguous(), vd.contiguous(), dense, ws, eps=w.eps)
+    torch.cuda.synchronize()
+    compare(out.cpu().double().numpy(), want, v, False, w.name)
+    assert torch.equal(out, dense)

@@ -106,6 +106,8 @@ constexpr int kPieces = kStateTile / 32;            // 16-byte pieces per thread
 constexpr int kHeadStride = kStateTile * 64 + 64;   // bytes
 constexpr int kTensorStride = 2 * kHeadStride;
 
+static_assert(2 * kTensorStride >= 2 * 2 * 16 * 64 * (int)sizeof(float), "reduction area exceeds the LDS tile");
+
 // grid.x = (b * HP + hp) * P + p; one work-group = one chunk of one head pair.
 // Wave w reduces head (w & 1) over token half (w >> 1) of each 64-token tile.
 // K and V are read once, so their loads are non-temporal.

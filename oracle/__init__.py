@@ -21,6 +21,7 @@ _lib = None
 
 F32 = 0
 BF16 = 1
+F16 = 2
 
 
 def _load():
@@ -36,6 +37,8 @@ def _load():
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_decode.restype = ctypes.c_int
+        lib.oracle_decode.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p]
         _lib = lib
     return _lib
 
@@ -45,7 +48,18 @@ def _dtype_code(a: np.ndarray) -> int:
         return BF16
     if a.dtype == np.float32:
         return F32
-    raise TypeError(f"oracle inputs are float32 or uint16 (bf16 bits), got {a.dtype}")
+    if a.dtype == np.float16:
+        return F16
+    raise TypeError(f"oracle inputs are float32, float16 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def decode(a: np.ndarray) -> np.ndarray:
+    """The oracle's own decoding of its inputs to float64 (for pinning it)."""
+    a = np.ascontiguousarray(a)
+    out = np.empty(a.shape, dtype=np.float64)
+    if _load().oracle_decode(a.ctypes.data, _dtype_code(a), a.size, out.ctypes.data) != 0:
+        raise RuntimeError("oracle_decode failed")
+    return out
 
 
 def max_threads() -> int:
@@ -61,7 +75,7 @@ def linattn_fwd(q, k, v, *, block_len: int | None = None, eps: float = 1e-15,
                 nthreads: int = 0, return_states: bool = False, state_in=None):
     """fp64 LiteLA forward on host arrays of shape [B, N, H, D].
 
-    q, k, v: float32, or uint16 holding bfloat16 bits (all three the same).
+    q, k, v: float32, float16, or uint16 holding bfloat16 bits (all three the same).
     block_len: None/0 for non-causal, else the frame-block length in tokens.
     state_in: optional float64 [B, H, D, D+1], the state before the first token
     (a carried state from an earlier call over the preceding tokens).

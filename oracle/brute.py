@@ -18,7 +18,8 @@ import numpy as np
 
 
 def decode(x: np.ndarray) -> np.ndarray:
-    """float32 array, or uint16 array of bfloat16 bits -> float64."""
+    """float32 or float16 array (numpy's own widening), or uint16 array of
+    bfloat16 bits -> float64."""
     if x.dtype == np.uint16:
         return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
     return x.astype(np.float64)

@@ -38,11 +38,13 @@
  * call over the whole sequence.
  *
  * Arithmetic: every input element is decoded exactly to double (bf16 bits are
- * the upper half of an IEEE float32), and all sums run sequentially in token
- * order in double precision.  No blocking or reordering beyond that.
+ * the upper half of an IEEE float32; fp16 is IEEE binary16), and all sums run
+ * sequentially in token order in double precision.  No blocking or reordering
+ * beyond that.
  *
  * Layout: q, k, v and out are contiguous [B][N][H][D].
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -51,9 +53,25 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F16 = 2 };
 
-/* Decode element idx of an array of float32 or of bfloat16 bit patterns. */
+/* IEEE 754 binary16 from its bits: 1 sign bit, 5 exponent bits (bias 15), 10
+ * fraction bits; exponent 0 holds the subnormals frac * 2^-24, exponent 31
+ * infinities and NaNs.  Every binary16 value is exact in double. */
+static double half_to_double(uint16_t h) {
+    const int sign = h >> 15, e = (h >> 10) & 0x1f, frac = h & 0x3ff;
+    double x;
+    if (e == 0)
+        x = ldexp((double)frac, -24);
+    else if (e == 31)
+        x = frac ? NAN : INFINITY;
+    else
+        x = ldexp((double)(frac | 0x400), e - 25);
+    return sign ? -x : x;
+}
+
+/* Decode element idx of an array of float32, of bfloat16 bit patterns or of
+ * binary16 bit patterns. */
 static double load_elem(const void* base, int dtype, size_t idx) {
     if (dtype == ORACLE_BF16) {
         uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
@@ -61,7 +79,15 @@ static double load_elem(const void* base, int dtype, size_t idx) {
         memcpy(&f, &bits, sizeof f);
         return (double)f;
     }
+    if (dtype == ORACLE_F16) return half_to_double(((const uint16_t*)base)[idx]);
     return (double)((const float*)base)[idx];
+}
+
+/* The decoding above, exposed so that tests can pin it: out[i] = element i. */
+int oracle_decode(const void* src, int dtype, size_t n, double* out) {
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F16) return -1;
+    for (size_t i = 0; i < n; ++i) out[i] = load_elem(src, dtype, i);
+    return 0;
 }
 
 static double relu(double x) { return x > 0.0 ? x : 0.0; }
@@ -81,7 +107,7 @@ int oracle_linattn_fwd(const void* q, const void* k, const void* v, int in_dtype
                        int B, int H, int N, int D, int block_len, double eps,
                        double* out, double* states, const double* state_in, int nthreads) {
     if (B < 0 || H < 0 || N < 0 || D < 1) return -1;
-    if (in_dtype != ORACLE_F32 && in_dtype != ORACLE_BF16) return -1;
+    if (in_dtype != ORACLE_F32 && in_dtype != ORACLE_BF16 && in_dtype != ORACLE_F16) return -1;
     if (B == 0 || H == 0 || N == 0) return 0;
     if (!q || !k || !v || !out) return -1;
     const int L = (block_len <= 0 || block_len >= N) ? N : block_len;

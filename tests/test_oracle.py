@@ -26,9 +26,12 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def rand_inputs(seed, B, N, H, D, bf16=True, scale=1.0):
+    """bf16=True: bfloat16 bits; False: float32; "f16": float16."""
     rng = np.random.default_rng(seed)
     xs = [(rng.standard_normal((B, N, H, D)).astype(np.float32) * np.float32(scale)) for _ in range(3)]
-    if bf16:
+    if bf16 == "f16":
+        xs = [x.astype(np.float16) for x in xs]
+    elif bf16:
         xs = [workloads.f32_to_bf16_bits(x) for x in xs]
     return xs
 
@@ -72,10 +75,39 @@ def test_bf16_and_f32_inputs_agree_with_torch_decode():
     assert np.array_equal(a, b)
 
 
+# ---------------------------------------------------------------- fp16 decode
+def test_f16_decode_known_patterns():
+    # IEEE 754 binary16: sign, 5 exponent bits (bias 15), 10 fraction bits.
+    cases = {0x3C00: 1.0, 0x3555: 0.333251953125, 0xC000: -2.0, 0x7BFF: 65504.0,
+             0x0400: 2.0 ** -14, 0x0001: 2.0 ** -24, 0x03FF: 1023 * 2.0 ** -24,
+             0x8000: -0.0, 0x7C00: np.inf, 0xFC00: -np.inf}
+    bits = np.array(list(cases), dtype=np.uint16).view(np.float16)
+    got = oracle.decode(bits)
+    for b, g in zip(cases, got):
+        assert g == cases[b] and np.signbit(g) == np.signbit(cases[b]), (hex(b), g)
+    assert np.isnan(oracle.decode(np.array([0x7E00, 0xFD01], dtype=np.uint16).view(np.float16))).all()
+
+
+def test_f16_decode_every_pattern_matches_numpy():
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    got, want = oracle.decode(allbits), allbits.astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def test_f16_inputs_agree_with_their_f32_widening():
+    q, k, v = rand_inputs(12, 2, 64, 3, 32, bf16="f16")
+    a = oracle.linattn_fwd(q, k, v)
+    b = oracle.linattn_fwd(*[x.astype(np.float32) for x in (q, k, v)])
+    assert np.array_equal(a, b)
+
+
 # ---------------------------------------------------------------- exact and quadratic forms
-@pytest.mark.parametrize("block_len", [0, 4, 1, 7])
-def test_matches_exact_rational(block_len):
-    q, k, v = rand_inputs(3, 1, 7, 2, 4, bf16=True)
+@pytest.mark.parametrize("block_len,dt", [(0, True), (4, True), (1, True), (7, True), (0, "f16"), (3, "f16")])
+def test_matches_exact_rational(block_len, dt):
+    q, k, v = rand_inputs(3, 1, 7, 2, 4, bf16=dt)
     ex = exact_fwd(q, k, v, block_len=block_len)
     want = np.array([[[[float(x) for x in c] for c in h] for h in n] for n in ex])
     got = oracle.linattn_fwd(q, k, v, block_len=block_len)
@@ -83,7 +115,8 @@ def test_matches_exact_rational(block_len):
 
 
 @pytest.mark.parametrize("shape,bf16", [((1, 256, 2, 32), False), ((2, 300, 3, 32), True),
-                                        ((1, 129, 1, 8), True), ((3, 33, 5, 16), False)])
+                                        ((1, 129, 1, 8), True), ((3, 33, 5, 16), False),
+                                        ((2, 200, 3, 32), "f16")])
 def test_linear_form_equals_quadratic_form(shape, bf16):
     q, k, v = rand_inputs(5, *shape, bf16=bf16)
     got = oracle.linattn_fwd(q, k, v)
@@ -306,3 +339,14 @@ def test_workload_generator_matches_torch_rounding():
     ours = workloads.f32_to_bf16_bits(x)
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(ours, ref)
+
+
+def test_f16_workload_generator_matches_torch_rounding():
+    w = workloads.Workload("f16_gen", 1, 64, 3, 32, workloads.DT_F16, seed=9, v_scale=0.5)
+    q, k, v = workloads.make_inputs(w)
+    assert q.dtype == np.float16
+    for t, x in enumerate((q, k, v)):
+        f = np.random.default_rng([9, t]).standard_normal(size=(1, 64, 3, 32), dtype=np.float32)
+        if t == 2:
+            f *= np.float32(0.5)
+        assert np.array_equal(x, torch.from_numpy(f).to(torch.float16).numpy())

@@ -19,7 +19,8 @@ the same shape and a unit-normal value distribution stand in for them.
 Recipe: ``numpy.random.default_rng([seed, t])`` with t = 0, 1, 2 for q, k, v
 draws ``standard_normal`` in float32, an optional scale is applied, and bf16
 inputs are then rounded to bfloat16 with round-to-nearest-even (the rounding of
-``torch.Tensor.to(torch.bfloat16)`` for finite values).  Layout is contiguous
+``torch.Tensor.to(torch.bfloat16)`` for finite values); fp16 inputs are rounded
+to IEEE binary16 the same way (numpy's cast).  Layout is contiguous
 [B, N, H, D].
 """
 from __future__ import annotations
@@ -30,6 +31,7 @@ import numpy as np
 
 DT_F32 = 0   # matches the C-ABI dtype code for float32
 DT_BF16 = 1  # matches the C-ABI dtype code for bfloat16
+DT_F16 = 2   # matches the C-ABI dtype code for IEEE binary16
 
 
 @dataclass(frozen=True)
@@ -39,7 +41,7 @@ class Workload:
     N: int
     H: int
     D: int
-    in_dtype: int          # DT_F32 or DT_BF16
+    in_dtype: int          # DT_F32, DT_BF16 or DT_F16
     seed: int
     block_len: int = 0     # 0 = non-causal; otherwise frame-block length in tokens
     v_scale: float = 1.0
@@ -54,7 +56,7 @@ class Workload:
 
     def algorithmic_bytes(self, out_bytes: int) -> int:
         """Bytes the method must move: read q, k, v once, write out once."""
-        s_in = 2 if self.in_dtype == DT_BF16 else 4
+        s_in = 4 if self.in_dtype == DT_F32 else 2
         return self.token_heads * self.D * (3 * s_in + out_bytes)
 
     def algorithmic_flops(self) -> int:
@@ -94,7 +96,8 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 def make_inputs(w: Workload):
     """Return (q, k, v) as numpy arrays of shape [B, N, H, D]: uint16 bf16 bits
-    when w.in_dtype is DT_BF16, float32 otherwise."""
+    when w.in_dtype is DT_BF16, float16 (numpy's round-to-nearest-even cast)
+    when it is DT_F16, float32 otherwise."""
     shape = (w.B, w.N, w.H, w.D)
     out = []
     for t in range(3):
@@ -108,7 +111,11 @@ def make_inputs(w: Workload):
         if t == 0:
             for (b, n, h) in w.negative_q_rows:
                 x[b, n, h, :] = -np.abs(x[b, n, h, :])
-        out.append(f32_to_bf16_bits(x) if w.in_dtype == DT_BF16 else x)
+        if w.in_dtype == DT_BF16:
+            x = f32_to_bf16_bits(x)
+        elif w.in_dtype == DT_F16:
+            x = x.astype(np.float16)
+        out.append(x)
     return tuple(out)
 
 

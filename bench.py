@@ -135,7 +135,8 @@ def main() -> int:
     ap.add_argument("--out-dtype", choices=("f32", "bf16"), default="f32")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time budget of the oracle CPU baseline (0 skips it)")
-    ap.add_argument("--no-extras", action="store_true", help="skip the bf16-out and block-causal timings")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other-out-dtype, block-causal and fp16-input timings")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="with --no-extras, still run the device-to-device copy (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -308,6 +309,19 @@ def main() -> int:
             "pct_hbm_peak": round(100 * alg_bytes / ms / 1e6 / HBM_PEAK_GBPS, 2),
             "note": "same-shape buffers as the non-causal run, block_len 1024"}
         del outs2, ws_bc
+
+        # fp16 inputs (the same values, converted on the device), fp32 out
+        sets16 = [[t.to(torch.float16) for t in st] for st in sets]
+
+        def f16(i):
+            q, k, v = sets16[i % NSETS]
+            sana.sana_linattn_fwd(q, k, v, outs[i % NSETS], ws, eps=w.eps, stream=stream)
+        ms = timed(f16, args.steps)
+        extra["f16_in_" + args.out_dtype + "out"] = {
+            "ms_per_step": round(ms, 5), "GBps": round(alg_bytes / ms / 1e6, 1),
+            "pct_hbm_peak": round(100 * alg_bytes / ms / 1e6 / HBM_PEAK_GBPS, 2),
+            "note": "the headline inputs converted to fp16 on the device"}
+        del sets16
 
     line = {
         "metric": METRIC,

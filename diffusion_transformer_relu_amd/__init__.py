@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "libsana_linattn.so")
 
 SANA_DT_F32 = 0
 SANA_DT_BF16 = 1
+SANA_DT_F16 = 2
 SANA_OK = 0
 SANA_ERR_INVALID_ARG = 1
 SANA_ERR_UNSUPPORTED = 2
@@ -113,7 +114,9 @@ def dtype_code(t) -> int:
         return SANA_DT_BF16
     if t.dtype == torch.float32:
         return SANA_DT_F32
-    raise TypeError(f"LiteLA tensors are bfloat16 or float32, got {t.dtype}")
+    if t.dtype == torch.float16:
+        return SANA_DT_F16
+    raise TypeError(f"LiteLA tensors are bfloat16, float16 or float32, got {t.dtype}")
 
 
 def _shape(q, k, v, out):

@@ -40,8 +40,8 @@ long round_up(long a, long m) { return (a + m - 1) / m * m; }
 // Decomposition of one call.  Sizes were range-checked by the caller.
 int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block_len, Plan* pl) {
     if (B < 0 || H < 0 || N < 0 || D < 1 || block_len < 0) return SANA_ERR_INVALID_ARG;
-    if ((in_dtype != SANA_DT_F32 && in_dtype != SANA_DT_BF16) ||
-        (out_dtype != SANA_DT_F32 && out_dtype != SANA_DT_BF16))
+    if ((in_dtype != SANA_DT_F32 && in_dtype != SANA_DT_BF16 && in_dtype != SANA_DT_F16) ||
+        (out_dtype != SANA_DT_F32 && out_dtype != SANA_DT_BF16 && out_dtype != SANA_DT_F16))
         return SANA_ERR_INVALID_ARG;
     if (D != sana::kD) return SANA_ERR_UNSUPPORTED;
     if (N > kMaxN || B > kMaxBH || H > kMaxBH) return SANA_ERR_UNSUPPORTED;
@@ -56,7 +56,7 @@ int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block
 
     pl->L = (block_len == 0 || block_len >= N) ? N : block_len;
     pl->NB = ceil_div(N, pl->L);
-    pl->mfma = (in_dtype == SANA_DT_BF16 && !env_is("SANA_LINATTN_PATH", "valu")) ? 1 : 0;
+    pl->mfma = (in_dtype != SANA_DT_F32 && !env_is("SANA_LINATTN_PATH", "valu")) ? 1 : 0;
     pl->HP = pl->mfma ? (H + 1) / 2 : H;
     const long units = (long)B * pl->HP * pl->NB;   // independent (b, head unit, block) triples
 
@@ -81,7 +81,8 @@ int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block
         if (tile) {
             tile = (int)round_up(tile, 64);
         } else {
-            const long slots = sana::kApplyGroups;
+            // fp16 q runs the apply kernel at 4 waves per SIMD instead of 5
+            const long slots = in_dtype == SANA_DT_F16 ? sana::kApplyGroups * 4 / 5 : sana::kApplyGroups;
             const long per_block = std::max<long>(1, slots / units);
             tile = (int)round_up(ceil_div(pl->L, per_block), 64);
         }
@@ -139,8 +140,8 @@ int forward(const void* q, const void* k, const void* v, void* out, int in_dtype
     if (st != SANA_OK) return st;
     if (!std::isfinite(eps) || eps < 0.f) return SANA_ERR_INVALID_ARG;
     if (stages <= 0 || (stages & ~SANA_STAGE_ALL)) return SANA_ERR_INVALID_ARG;
-    const size_t es_in = in_dtype == SANA_DT_BF16 ? 2 : 4;
-    const size_t es_out = out_dtype == SANA_DT_BF16 ? 2 : 4;
+    const size_t es_in = in_dtype == SANA_DT_F32 ? 4 : 2;
+    const size_t es_out = out_dtype == SANA_DT_F32 ? 4 : 2;
     const sana::Strides dense = {(long long)N * H * D, (long long)H * D};
     pl.sq = pl.sk = pl.sv = pl.so = dense;
     if (strides) {

@@ -26,7 +26,10 @@
 //      vector unit.  Both keep fp32 accuracy, as the pages' fp32 attention
 //      policy asks.
 //
-// fp32 inputs take the vector kernels (k_*_valu), which also serve as a second
+// fp16 inputs take the same matrix-core kernels (products of fp16 values are
+// exact in fp32 as well); in the apply kernel each ReLU(q) element is split
+// exactly into two bf16 terms, so the state side stays the bf16 split.  fp32
+// inputs take the vector kernels (k_*_valu), which also serve as a second
 // implementation for cross-checks.
 #include "linattn_internal.h"
 
@@ -34,6 +37,7 @@ namespace sana {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -57,6 +61,38 @@ __device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x16 mfma_f16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// The 16-bit input formats: bf16 (F16 = false) or IEEE binary16 (F16 = true).
+// ReLU on packed values works the same for both: the sign is the top bit.
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma16(u32x4 a, u32x4 b, f32x16 c) {
+    if constexpr (F16)
+        return mfma_f16(a, b, c);
+    else
+        return mfma_bf16(a, b, c);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// Splits two packed non-negative fp16 values exactly into bf16 terms,
+// x = hi + lo: hi keeps the top 8 significant bits of the fp32 widening, and
+// the remainder has at most the 3 low significant bits of the 11, so it is a
+// bf16 value too.  f0, f1 receive the fp32 values.
+__device__ __forceinline__ void split_f16x2(uint32_t w, uint32_t& hi, uint32_t& lo, float& f0, float& f1) {
+    f0 = f16_to_f32((uint16_t)(w & 0xffffu));
+    f1 = f16_to_f32((uint16_t)(w >> 16));
+    const uint32_t t0 = __builtin_bit_cast(uint32_t, f0) & 0xffff0000u;
+    const uint32_t t1 = __builtin_bit_cast(uint32_t, f1) & 0xffff0000u;
+    const float r0 = f0 - __builtin_bit_cast(float, t0);
+    const float r1 = f1 - __builtin_bit_cast(float, t1);
+    hi = (t0 >> 16) | t1;
+    lo = (__builtin_bit_cast(uint32_t, r0) >> 16) | (__builtin_bit_cast(uint32_t, r1) & 0xffff0000u);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __builtin_bit_cast(float, (uint32_t)h << 16);
 }
@@ -71,11 +107,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Element types by ABI code: float (0), bf16 bits in uint16_t (1), _Float16 (2).
 __device__ __forceinline__ float load_in(const float* p, long long i) { return p[i]; }
 __device__ __forceinline__ float load_in(const uint16_t* p, long long i) { return bf16_to_f32(p[i]); }
+__device__ __forceinline__ float load_in(const _Float16* p, long long i) { return (float)p[i]; }
 
+// fp32 -> fp16 conversion rounds to nearest even; outputs lie within the range
+// of V, so they never overflow.
 __device__ __forceinline__ void store_out(float* p, long long i, float x) { p[i] = x; }
 __device__ __forceinline__ void store_out(uint16_t* p, long long i, float x) { p[i] = f32_to_bf16(x); }
+__device__ __forceinline__ void store_out(_Float16* p, long long i, float x) { p[i] = (_Float16)x; }
 
 // Output stores are non-temporal: out is written once and never read here, and
 // streaming it past the caches raises the write bandwidth markedly on gfx950.
@@ -86,6 +127,11 @@ __device__ __forceinline__ void store4(uint16_t* p, f32x4 x) {
     const uint32_t lo = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
     const uint32_t hi = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
     __builtin_nontemporal_store((u32x2){lo, hi}, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void store4(_Float16* p, f32x4 x) {
+    const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)x[0]), h1 = __builtin_bit_cast(uint16_t, (_Float16)x[1]);
+    const uint32_t h2 = __builtin_bit_cast(uint16_t, (_Float16)x[2]), h3 = __builtin_bit_cast(uint16_t, (_Float16)x[3]);
+    __builtin_nontemporal_store((u32x2){h0 | (h1 << 16), h2 | (h3 << 16)}, reinterpret_cast<u32x2*>(p));
 }
 
 // Token range [c0, c1) of chunk p of a (b, head) unit.
@@ -111,6 +157,7 @@ static_assert(2 * kTensorStride >= 2 * 2 * 16 * 64 * (int)sizeof(float), "reduct
 // grid.x = (b * HP + hp) * P + p; one work-group = one chunk of one head pair.
 // Wave w reduces head (w & 1) over token half (w >> 1) of each 64-token tile.
 // K and V are read once, so their loads are non-temporal.
+template <bool F16>
 __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ part,
     int N, int H, int HP, int L, int cpb, int P, int chunk, Strides sk, Strides sv) {
@@ -148,7 +195,8 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
     };
 
     f32x16 accV = {}, accO = {};
-    const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0 pairs
+    constexpr uint32_t kOne2 = F16 ? 0x3c003c00u : 0x3f803f80u;   // 1.0 in both halves
+    const u32x4 ones = {kOne2, kOne2, kOne2, kOne2};
     const int g = lane >> 5, j = lane & 31;
 
     if (cr.c0 < cr.c1) load_tile(cr.c0);
@@ -180,8 +228,8 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
                 a[t] = (uint32_t)Kt[r0] | ((uint32_t)Kt[r1] << 16);
                 bv[t] = (uint32_t)Vt[r0] | ((uint32_t)Vt[r1] << 16);
             }
-            accV = mfma_bf16(a, bv, accV);
-            accO = mfma_bf16(a, ones, accO);
+            accV = mfma16<F16>(a, bv, accV);
+            accO = mfma16<F16>(a, ones, accO);
         }
     }
 
@@ -311,8 +359,10 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(
 // that every store instruction writes whole 128-byte output rows.
 constexpr int kOutPitch = 36;   // floats per LDS output row: 32 + 4 keeps rows 16-byte aligned, no bank conflicts
 
-template <typename OutT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))) void k_apply_mfma(
+// Occupancy target 5 waves per SIMD (4 for fp16 q, whose exact bf16 split
+// needs a few more registers).
+template <bool F16, typename OutT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(F16 ? 4 : 5, 8))) void k_apply_mfma(
     const uint16_t* __restrict__ q, const float* __restrict__ state, OutT* __restrict__ out,
     int N, int H, int HP, int L, int NB, int tile, int tpb, float eps, Strides sq, Strides so) {
     __shared__ __attribute__((aligned(16))) float otile[4][32 * kOutPitch];
@@ -378,24 +428,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
     for (; tt < t1; tt += 64) {
         u32x4 n0, n1;
         load_b(tt + 64, n0, n1);       // next sub-tile of this wave, in flight during the MFMAs
-        a0 = relu_bf16x8(a0);
+        a0 = relu_bf16x8(a0);   // the sign test is the same for fp16
         a1 = relu_bf16x8(a1);
         f32x16 acc = {};
-#pragma unroll
-        for (int sp = 2; sp >= 0; --sp) {   // small split terms first
-            acc = mfma_bf16(sa[0][sp], a0, acc);
-            acc = mfma_bf16(sa[1][sp], a1, acc);
-        }
         float dp = 0.f;
+        if constexpr (F16) {
+            // one 16-feature half at a time (fewer live registers); the
+            // normaliser takes the fp32 values as they are split
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            dp = fmaf(lo_bf16(a0[d]), sden[2 * d], dp);
-            dp = fmaf(hi_bf16(a0[d]), sden[2 * d + 1], dp);
-        }
+            for (int ks = 0; ks < 2; ++ks) {
+                const u32x4 x = ks ? a1 : a0;
+                u32x4 hi, lo;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            dp = fmaf(lo_bf16(a1[d]), sden[8 + 2 * d], dp);
-            dp = fmaf(hi_bf16(a1[d]), sden[8 + 2 * d + 1], dp);
+                for (int d = 0; d < 4; ++d) {
+                    uint32_t h, l;
+                    float f0, f1;
+                    split_f16x2(x[d], h, l, f0, f1);
+                    hi[d] = h;
+                    lo[d] = l;
+                    dp = fmaf(f0, sden[8 * ks + 2 * d], dp);
+                    dp = fmaf(f1, sden[8 * ks + 2 * d + 1], dp);
+                }
+#pragma unroll
+                for (int sp = 2; sp >= 0; --sp) acc = mfma_bf16(sa[ks][sp], lo, acc);   // small terms first
+#pragma unroll
+                for (int sp = 2; sp >= 0; --sp) acc = mfma_bf16(sa[ks][sp], hi, acc);
+            }
+        } else {
+#pragma unroll
+            for (int sp = 2; sp >= 0; --sp) {   // small split terms first
+                acc = mfma_bf16(sa[0][sp], a0, acc);
+                acc = mfma_bf16(sa[1][sp], a1, acc);
+            }
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                dp = fmaf(lo_bf16(a0[d]), sden[2 * d], dp);
+                dp = fmaf(hi_bf16(a0[d]), sden[2 * d + 1], dp);
+            }
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                dp = fmaf(lo_bf16(a1[d]), sden[8 + 2 * d], dp);
+                dp = fmaf(hi_bf16(a1[d]), sden[8 + 2 * d + 1], dp);
+            }
         }
         const float den = dp + __shfl_xor(dp, 32);   // same sum on lanes i and i + 32
         const float rinv = 1.0f / (den + eps);
@@ -459,22 +533,39 @@ __global__ __launch_bounds__(kThreads) void k_apply_valu(
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
+namespace {
+template <typename T> struct Tag { using type = T; };
+
+// Calls f(Tag<T>{}) with T the element type of ABI dtype code `code`.
+template <typename F> void by_dtype(int code, F&& f) {
+    if (code == 1)
+        f(Tag<uint16_t>{});
+    else if (code == 2)
+        f(Tag<_Float16>{});
+    else
+        f(Tag<float>{});
+}
+}  // namespace
+
 hipError_t launch_state(const Plan& pl, const void* k, const void* v, float* part, hipStream_t stream) {
+    const uint16_t* k16 = static_cast<const uint16_t*>(k);
+    const uint16_t* v16 = static_cast<const uint16_t*>(v);
     if (pl.mfma) {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.P);
-        hipLaunchKernelGGL(k_state_partial_mfma, dim3(grid), dim3(kThreads), 0, stream,
-                           static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), part,
-                           pl.N, pl.H, pl.HP, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
+        if (pl.in_dtype == 2)
+            hipLaunchKernelGGL(k_state_partial_mfma<true>, dim3(grid), dim3(kThreads), 0, stream, k16, v16, part,
+                               pl.N, pl.H, pl.HP, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
+        else
+            hipLaunchKernelGGL(k_state_partial_mfma<false>, dim3(grid), dim3(kThreads), 0, stream, k16, v16, part,
+                               pl.N, pl.H, pl.HP, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
     } else {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.H * pl.P);
-        if (pl.in_dtype == 1)
-            hipLaunchKernelGGL(k_state_partial_valu<uint16_t>, dim3(grid), dim3(kThreads), 0, stream,
-                               static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), part,
+        by_dtype(pl.in_dtype, [&](auto in) {
+            using IT = typename decltype(in)::type;
+            hipLaunchKernelGGL(k_state_partial_valu<IT>, dim3(grid), dim3(kThreads), 0, stream,
+                               static_cast<const IT*>(k), static_cast<const IT*>(v), part,
                                pl.N, pl.H, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
-        else
-            hipLaunchKernelGGL(k_state_partial_valu<float>, dim3(grid), dim3(kThreads), 0, stream,
-                               static_cast<const float*>(k), static_cast<const float*>(v), part,
-                               pl.N, pl.H, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
+        });
     }
     return hipGetLastError();
 }
@@ -489,30 +580,31 @@ hipError_t launch_merge(const Plan& pl, const float* part, float* state, const f
 
 hipError_t launch_apply(const Plan& pl, const void* q, const float* state, void* out, float eps,
                         hipStream_t stream) {
-    const bool out_bf16 = pl.out_dtype == 1;
     if (pl.mfma) {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.NB * pl.tpb);
-        const uint16_t* qq = static_cast<const uint16_t*>(q);
-        if (out_bf16)
-            hipLaunchKernelGGL(k_apply_mfma<uint16_t>, dim3(grid), dim3(kThreads), 0, stream, qq, state,
-                               static_cast<uint16_t*>(out), pl.N, pl.H, pl.HP, pl.L, pl.NB, pl.tile, pl.tpb, eps,
-                               pl.sq, pl.so);
-        else
-            hipLaunchKernelGGL(k_apply_mfma<float>, dim3(grid), dim3(kThreads), 0, stream, qq, state,
-                               static_cast<float*>(out), pl.N, pl.H, pl.HP, pl.L, pl.NB, pl.tile, pl.tpb, eps,
-                               pl.sq, pl.so);
+        const uint16_t* q16 = static_cast<const uint16_t*>(q);
+        by_dtype(pl.out_dtype, [&](auto o) {
+            using OT = typename decltype(o)::type;
+            if (pl.in_dtype == 2)
+                hipLaunchKernelGGL((k_apply_mfma<true, OT>), dim3(grid), dim3(kThreads), 0, stream, q16, state,
+                                   static_cast<OT*>(out), pl.N, pl.H, pl.HP, pl.L, pl.NB, pl.tile, pl.tpb, eps,
+                                   pl.sq, pl.so);
+            else
+                hipLaunchKernelGGL((k_apply_mfma<false, OT>), dim3(grid), dim3(kThreads), 0, stream, q16, state,
+                                   static_cast<OT*>(out), pl.N, pl.H, pl.HP, pl.L, pl.NB, pl.tile, pl.tpb, eps,
+                                   pl.sq, pl.so);
+        });
     } else {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.H * pl.NB * pl.tpb);
-#define SANA_APPLY_VALU(IT, OT)                                                                        \
-    hipLaunchKernelGGL((k_apply_valu<IT, OT>), dim3(grid), dim3(kThreads), 0, stream,                   \
-                       static_cast<const IT*>(q), state, static_cast<OT*>(out), pl.N, pl.H, pl.L, pl.NB, \
-                       pl.tpb, eps, pl.sq, pl.so)
-        if (pl.in_dtype == 1) {
-            if (out_bf16) SANA_APPLY_VALU(uint16_t, uint16_t); else SANA_APPLY_VALU(uint16_t, float);
-        } else {
-            if (out_bf16) SANA_APPLY_VALU(float, uint16_t); else SANA_APPLY_VALU(float, float);
-        }
-#undef SANA_APPLY_VALU
+        by_dtype(pl.in_dtype, [&](auto in) {
+            by_dtype(pl.out_dtype, [&](auto o) {
+                using IT = typename decltype(in)::type;
+                using OT = typename decltype(o)::type;
+                hipLaunchKernelGGL((k_apply_valu<IT, OT>), dim3(grid), dim3(kThreads), 0, stream,
+                                   static_cast<const IT*>(q), state, static_cast<OT*>(out), pl.N, pl.H, pl.L,
+                                   pl.NB, pl.tpb, eps, pl.sq, pl.so);
+            });
+        });
     }
     return hipGetLastError();
 }

@@ -23,13 +23,18 @@
  *
  * Conventions shared by every entry point below
  * ---------------------------------------------
- * Layout     q, k, v and out are contiguous row-major [B][N][H][D] arrays.
+ * Layout     q, k, v and out are contiguous row-major [B][N][H][D] arrays
+ *            (sana_linattn_fwd_strided takes views with free batch and token
+ *            strides).
  *            q and k are taken before the feature map: the library applies
  *            ReLU itself (ReLU is idempotent, so already-activated inputs give
  *            the same result).
- * Dtypes     q, k and v share in_dtype; out has its own out_dtype.  All
- *            accumulation is fp32.  A bf16 out is the fp32 result rounded to
- *            nearest-even.  D must be 32 (the Sana head dim).
+ * Dtypes     q, k and v share in_dtype; out has its own out_dtype; each is
+ *            fp32, bf16 or fp16.  All accumulation is fp32, as the Sana page
+ *            ("What LiteLA actually computes") requires because fp16
+ *            activations overflow.  A bf16 or fp16 out is the fp32 result
+ *            rounded to nearest-even (outputs lie within the range of V, so an
+ *            fp16 out cannot overflow).  D must be 32 (the Sana head dim).
  * Memory     Every pointer is device memory on the current HIP device, owned
  *            by the caller.  The library allocates nothing, keeps nothing
  *            after return, and never synchronises: work is enqueued on
@@ -70,7 +75,8 @@ extern "C" {
 
 typedef enum {
     SANA_DT_F32 = 0,   /* IEEE float32 */
-    SANA_DT_BF16 = 1   /* bfloat16 (upper half of a float32) */
+    SANA_DT_BF16 = 1,  /* bfloat16 (upper half of a float32) */
+    SANA_DT_F16 = 2    /* IEEE binary16 */
 } sana_dtype_t;
 
 typedef enum {

@@ -36,10 +36,17 @@ def bf16_round(x64: np.ndarray) -> np.ndarray:
     return torch.from_numpy(x64).float().to(torch.bfloat16).double().numpy()
 
 
-def compare(got: np.ndarray, want: np.ndarray, v: np.ndarray, out_bf16: bool, label: str = ""):
-    """Returns (max_abs, rel_l2) and asserts the parity bar."""
+def f16_round(x64: np.ndarray) -> np.ndarray:
+    return x64.astype(np.float32).astype(np.float16).astype(np.float64)
+
+
+def compare(got: np.ndarray, want: np.ndarray, v: np.ndarray, out_bf16, label: str = ""):
+    """Returns (max_abs, rel_l2) and asserts the parity bar.  out_bf16: False
+    (fp32 out), True (bf16 out) or "f16" (fp16 out)."""
+    out_f16 = isinstance(out_bf16, str) and out_bf16 == "f16"
+    out_bf16 = out_bf16 is True
     vmax = np.max(np.abs(decode(v))) if v.size else 1.0
-    ref = bf16_round(want) if out_bf16 else want
+    ref = bf16_round(want) if out_bf16 else f16_round(want) if out_f16 else want
     diff = got - ref
     max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
     norm = float(np.linalg.norm(ref))
@@ -47,14 +54,17 @@ def compare(got: np.ndarray, want: np.ndarray, v: np.ndarray, out_bf16: bool, la
     assert np.all(np.isfinite(got)), label
     assert max_abs <= MAX_ABS_FRAC * vmax, f"{label}: max abs {max_abs:.3e} > {MAX_ABS_FRAC}*{vmax:.3e}"
     assert rel <= REL_L2, f"{label}: rel L2 {rel:.3e} > {REL_L2}"
-    if out_bf16:
-        # A bf16 result is the fp32 result rounded once: within one bf16 ulp of
-        # the exact value, plus the fp32 pipeline's own absolute error, which
+    if out_bf16 or out_f16:
+        # A 16-bit result is the fp32 result rounded once: within one ulp of
+        # the exact value (bf16: 8 significant bits; fp16: 11, with subnormal
+        # spacing 2^-24), plus the fp32 pipeline's own absolute error, which
         # dominates for outputs near zero (cancellation in the weighted sum).
-        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(want), 1e-300))) - 7)
+        e = np.floor(np.log2(np.maximum(np.abs(want), 1e-300)))
+        ulp = np.exp2(e - 7) if out_bf16 else np.exp2(np.maximum(e, -14) - 10)
         fp32_abs = 1e-6 * vmax
         bad = np.abs(got - want) > ulp + fp32_abs
-        assert not np.any(bad), f"{label}: {int(bad.sum())} values beyond one bf16 ulp + {fp32_abs:.1e}"
+        name = "bf16" if out_bf16 else "fp16"
+        assert not np.any(bad), f"{label}: {int(bad.sum())} values beyond one {name} ulp + {fp32_abs:.1e}"
     return max_abs, rel
 
 

@@ -49,6 +49,8 @@ def test_workspace_and_plan_queries():
     assert info["mfma"] == 1 and info["chunk_tokens"] % 64 == 0 and info["apply_tokens"] % 64 == 0
     assert info["num_chunks"] * info["chunk_tokens"] >= 16384
     assert sana.sana_linattn_plan_info(sana.SANA_DT_F32, 1, 2, 256, 32, 0)["mfma"] == 0
+    f16 = sana.sana_linattn_plan_info(sana.SANA_DT_F16, 1, 70, 16384, 32, 0)
+    assert f16["mfma"] == 1 and f16["apply_tokens"] >= info["apply_tokens"]   # fp16 apply: 4 work-groups per CU
     bc = sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 70, 16384, 32, 1000)
     assert bc["chunk_tokens"] <= 1024 and bc["num_chunks"] % 17 == 0        # chunks never cross blocks
 
@@ -96,8 +98,9 @@ def fwd(q=A, k=A + 64 * MB, v=A + 128 * MB, out=A + 192 * MB, in_dt=1, out_dt=0,
     (dict(v=None), sana.SANA_ERR_INVALID_ARG),
     (dict(out=None), sana.SANA_ERR_INVALID_ARG),
     (dict(ws=None), sana.SANA_ERR_INVALID_ARG),
-    (dict(in_dt=2), sana.SANA_ERR_INVALID_ARG),
+    (dict(in_dt=3), sana.SANA_ERR_INVALID_ARG),
     (dict(out_dt=-1), sana.SANA_ERR_INVALID_ARG),
+    (dict(out_dt=3), sana.SANA_ERR_INVALID_ARG),
     (dict(D=16), sana.SANA_ERR_UNSUPPORTED),
     (dict(B=-1), sana.SANA_ERR_INVALID_ARG),
     (dict(eps=float("nan")), sana.SANA_ERR_INVALID_ARG),

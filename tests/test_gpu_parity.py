@@ -228,3 +228,57 @@ def test_broadcast_and_transposed_views(monkeypatch, path):
     torch.cuda.synchronize()
     compare(out.cpu().double().numpy(), want, v, False, w.name)
     assert torch.equal(out, dense)
+
+
+
+F16_CASES = [
+    workloads.Workload("f16_sana1600m_2048px_B2_N4096_H70", 2, 4096, 70, 32, workloads.DT_F16, seed=51),
+    workloads.Workload("f16_sana1600m_4096px_B1_N16384_H70", 1, 16384, 70, 32, workloads.DT_F16, seed=52,
+                       v_scale=0.5),
+    workloads.Workload("f16_blockcausal_B1_N8192_H70_L1024", 1, 8192, 70, 32, workloads.DT_F16, seed=53,
+                       block_len=1024),
+]
+
+
+@pytest.mark.parametrize("w", F16_CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.float16, torch.bfloat16], ids=["f32out", "f16out", "bf16out"])
+def test_f16_inputs(w, out_dtype):
+    """fp16 q, k, v (fp32 accumulation) at Sana shapes, every output dtype."""
+    (q, k, v), want = inputs_and_oracle(w)
+    got = run_hip(q, k, v, block_len=w.block_len, eps=w.eps, out_dtype=out_dtype)
+    kind = {torch.float32: False, torch.float16: "f16", torch.bfloat16: True}[out_dtype]
+    compare(got, want, v, kind, w.name)
+
+
+F16_EDGE = [(1, 1, 1, 0), (2, 33, 3, 0), (1, 1000, 5, 64), (3, 257, 7, 100), (1, 4097, 2, 0)]
+
+
+@pytest.mark.parametrize("path", ["mfma", "valu"])
+@pytest.mark.parametrize("B,N,H,L", F16_EDGE, ids=[f"B{b}N{n}H{h}L{l}" for b, n, h, l in F16_EDGE])
+def test_f16_edge_shapes(monkeypatch, path, B, N, H, L):
+    if path == "valu":
+        monkeypatch.setenv("SANA_LINATTN_PATH", "valu")
+    w = workloads.Workload(f"f16edge_B{B}N{N}H{H}L{L}", B, N, H, 32, workloads.DT_F16, seed=60 + N % 7,
+                           block_len=L)
+    (q, k, v), want = inputs_and_oracle(w)
+    for out_dtype, kind in ((torch.float32, False), (torch.float16, "f16")):
+        got = run_hip(q, k, v, block_len=L, eps=w.eps, out_dtype=out_dtype)
+        compare(got, want, v, kind, f"{w.name}/{path}/{kind}")
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [(1e-5, 1.0), (30.0, 1e4), (1.0, 1e-4)],
+                         ids=["subnormal_k", "large_kv", "tiny_v"])
+def test_f16_extreme_magnitudes(k_scale, v_scale):
+    """fp16 inputs far from unit scale: subnormal keys, values near the top of
+    the fp16 range (the state and the normaliser grow far beyond it, which fp32
+    accumulation absorbs), tiny values.  fp16 out cannot overflow since every
+    output lies within the range of V."""
+    rng = np.random.default_rng(71)
+    shape = (2, 2048, 6, 32)
+    q = rng.standard_normal(shape, dtype=np.float32).astype(np.float16)
+    k = (rng.standard_normal(shape, dtype=np.float32) * np.float32(k_scale)).astype(np.float16)
+    v = (rng.standard_normal(shape, dtype=np.float32) * np.float32(v_scale)).astype(np.float16)
+    want = oracle.linattn_fwd(q, k, v)
+    for out_dtype, kind in ((torch.float32, False), (torch.float16, "f16")):
+        got = run_hip(q, k, v, out_dtype=out_dtype)
+        compare(got, want, v, kind, f"k{k_scale}_v{v_scale}/{kind}")

@@ -94,10 +94,12 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out_dtype: str = "f32") ->
         return copy_bytes / statistics.median([x for x in copies if x >= 0.95 * top])
 
     sf, sw = calib(fetch), calib(write)
-    apply_tag = "<float>" if out_dtype == "f32" else "<unsigned short>"
-    kernels = {"k_state_partial_mfma": lambda n: "k_state_partial_mfma" in n,
+    # bf16 inputs: template argument F16 = false; the apply kernel's second
+    # template argument is the output element type
+    apply_tag = "k_apply_mfma<false, " + ("float>" if out_dtype == "f32" else "unsigned short>")
+    kernels = {"k_state_partial_mfma": lambda n: "k_state_partial_mfma<false>" in n,
                "k_merge": lambda n: "k_merge" in n,
-               "k_apply_mfma": lambda n: "k_apply_mfma" in n and apply_tag in n}
+               "k_apply_mfma": lambda n: apply_tag in n}
     algo = {"k_state_partial_mfma": w.token_heads * w.D * 4,
             "k_merge": None,
             "k_apply_mfma": w.token_heads * w.D * (2 + out_bytes)}
@@ -127,6 +129,25 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out_dtype: str = "f32") ->
     return 0
 
 
+def short_kernel_name(name: str) -> str:
+    """'void ns::(anonymous namespace)::k<a, b>(args)' -> 'k<a, b>'."""
+    head = name.split("(unsigned", 1)[0].split("(float", 1)[0]
+    head = head.replace("(anonymous namespace)::", "").replace("void ", "")
+    return head.split("::")[-1] if "<" not in head else head[head.rfind("::", 0, head.find("<")) + 2:]
+
+
+def summarize_trace(stats_csv: str) -> int:
+    """Markdown table of a rocprofv3 --kernel-trace --stats run_kernel_stats.csv."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    print("| kernel | calls | avg µs | min µs | max µs | share % |")
+    print("|---|---|---|---|---|---|")
+    for r in rows:
+        print(f"| `{short_kernel_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,7 +163,12 @@ def main() -> int:
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a profiled bench run into profiles/traffic.json")
+    ap.add_argument("--trace-from", metavar="STATS_CSV",
+                    help="no GPU run: print a rocprofv3 --kernel-trace --stats run_kernel_stats.csv as a "
+                         "markdown table")
     args = ap.parse_args()
+    if args.trace_from:
+        return summarize_trace(args.trace_from)
     if args.traffic_from:
         return summarize_traffic(*args.traffic_from, out_dtype=args.out_dtype)
 

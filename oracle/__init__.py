@@ -5,6 +5,7 @@ CPU-baseline leg of the benchmark.  The HIP product path never imports it.
 
 * ``linattn_fwd``  -- the linear (state) form in C, fp64, OpenMP over (b, h);
   see ``linattn_oracle.c`` for the definition and the pages it follows.
+* ``linattn_bwd``  -- its gradients (dq, dk, dv) in C, fp64, same structure.
 * ``brute``        -- the quadratic form in numpy (its pin).
 * ``exact``        -- the quadratic form in exact rational arithmetic (tiny sizes).
 """
@@ -37,6 +38,11 @@ def _load():
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_linattn_bwd.restype = ctypes.c_int
+        lib.oracle_linattn_bwd.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.oracle_decode.restype = ctypes.c_int
         lib.oracle_decode.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p]
         _lib = lib
@@ -107,3 +113,24 @@ def linattn_fwd(q, k, v, *, block_len: int | None = None, eps: float = 1e-15,
     if rc != 0:
         raise RuntimeError(f"oracle_linattn_fwd failed ({rc})")
     return (out, states) if return_states else out
+
+
+def linattn_bwd(q, k, v, dout, *, block_len: int | None = None, eps: float = 1e-15, nthreads: int = 0):
+    """fp64 gradients (dq, dk, dv) of the LiteLA forward for dL/dout = dout.
+
+    q, k, v as for linattn_fwd; dout float32, float16 or uint16 bf16 bits,
+    [B, N, H, D].  Returns three float64 [B, N, H, D] arrays."""
+    q, k, v, dout = (np.ascontiguousarray(x) for x in (q, k, v, dout))
+    if not (q.shape == k.shape == v.shape == dout.shape) or q.ndim != 4:
+        raise ValueError("q, k, v, dout must share one [B, N, H, D] shape")
+    code = _dtype_code(q)
+    if _dtype_code(k) != code or _dtype_code(v) != code:
+        raise TypeError("q, k, v must share one dtype")
+    B, N, H, D = q.shape
+    dq, dk, dv = (np.empty((B, N, H, D), dtype=np.float64) for _ in range(3))
+    rc = _load().oracle_linattn_bwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data, code,
+                                    _dtype_code(dout), B, H, N, D, int(block_len or 0), float(eps),
+                                    dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_linattn_bwd failed ({rc})")
+    return dq, dk, dv

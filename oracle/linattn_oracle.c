@@ -176,6 +176,132 @@ int oracle_linattn_fwd(const void* q, const void* k, const void* v, int in_dtype
     return failed ? -1 : 0;
 }
 
+/*
+ * Backward of the same operator (test infrastructure, like the forward).
+ *
+ * Given dout = dL/dout, with f_i = phi(q_i), a_n = phi(k_n) and P = the state a
+ * query's block uses (the whole-sequence state when non-causal):
+ *   r_i   = 1 / (den_i + eps),  out_i = num_i * r_i
+ *   u_i   = dL/dnum_i = dout_i * r_i                                  (D)
+ *   w_i   = dL/dden_i = -r_i * (dout_i . out_i)                       (scalar)
+ *   dq_ij = [q_ij > 0] * (sum_c P[j][c] u_ic + P[j][D] w_i)
+ *   G^(beta)[j][c] = sum over queries i of block beta of f_ij [u_i | w_i]_c
+ *                    (dL/dP of the state block beta uses, D x (D+1))
+ * A key of block beta enters the state of every block >= beta, so it sees the
+ * suffix sum Ghat^(beta) = sum_{beta' >= beta} G^(beta'):
+ *   dk_nj = [k_nj > 0] * (sum_c Ghat[j][c] v_nc + Ghat[j][D])
+ *   dv_nc = sum_j a_nj Ghat[j][c]
+ * The derivative of ReLU at 0 is taken as 0.  dout has its own dtype code.
+ * dq, dk, dv: [B][N][H][D] doubles (written).  Returns 0, or -1 on bad
+ * arguments.
+ */
+int oracle_linattn_bwd(const void* q, const void* k, const void* v, const void* dout, int in_dtype,
+                       int dout_dtype, int B, int H, int N, int D, int block_len, double eps,
+                       double* dq, double* dk, double* dv, int nthreads) {
+    if (B < 0 || H < 0 || N < 0 || D < 1) return -1;
+    if (in_dtype != ORACLE_F32 && in_dtype != ORACLE_BF16 && in_dtype != ORACLE_F16) return -1;
+    if (dout_dtype != ORACLE_F32 && dout_dtype != ORACLE_BF16 && dout_dtype != ORACLE_F16) return -1;
+    if (B == 0 || H == 0 || N == 0) return 0;
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return -1;
+    const int L = (block_len <= 0 || block_len >= N) ? N : block_len;
+    const int NB = (N + L - 1) / L;
+    const int W = D + 1;
+
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+
+    int failed = 0;
+#pragma omp parallel
+    {
+        /* per (b, h): prefix states P[NB][D][W], gradient states G[NB][D][W] */
+        double* P = (double*)malloc(sizeof(double) * (size_t)NB * D * W);
+        double* G = (double*)malloc(sizeof(double) * (size_t)NB * D * W);
+        double* f = (double*)malloc(sizeof(double) * (size_t)D);
+        double* uw = (double*)malloc(sizeof(double) * (size_t)W);
+        double* x = (double*)malloc(sizeof(double) * (size_t)D);
+        if (!P || !G || !f || !uw || !x) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long bh = 0; bh < (long)B * H; ++bh) {
+                const int b = (int)(bh / H), h = (int)(bh % H);
+                /* forward states, inclusive prefix over blocks */
+                memset(P, 0, sizeof(double) * (size_t)NB * D * W);
+                for (int beta = 0; beta < NB; ++beta) {
+                    double* Pb = P + (size_t)beta * D * W;
+                    if (beta > 0) memcpy(Pb, Pb - (size_t)D * W, sizeof(double) * (size_t)D * W);
+                    const int n1 = (beta * L + L < N) ? beta * L + L : N;
+                    for (int n = beta * L; n < n1; ++n) {
+                        const size_t row = (((size_t)b * N + n) * H + h) * (size_t)D;
+                        for (int j = 0; j < D; ++j) f[j] = relu(load_elem(k, in_dtype, row + j));
+                        for (int j = 0; j < D; ++j) {
+                            for (int c = 0; c < D; ++c) Pb[j * W + c] += f[j] * load_elem(v, in_dtype, row + c);
+                            Pb[j * W + D] += f[j];
+                        }
+                    }
+                }
+                /* queries: dq and the per-block gradient states */
+                memset(G, 0, sizeof(double) * (size_t)NB * D * W);
+                for (int i = 0; i < N; ++i) {
+                    const int beta = i / L;
+                    const double* Pb = P + (size_t)beta * D * W;
+                    double* Gb = G + (size_t)beta * D * W;
+                    const size_t row = (((size_t)b * N + i) * H + h) * (size_t)D;
+                    for (int j = 0; j < D; ++j) f[j] = relu(load_elem(q, in_dtype, row + j));
+                    double den = 0.0;
+                    for (int j = 0; j < D; ++j) den += f[j] * Pb[j * W + D];
+                    const double r = 1.0 / (den + eps);
+                    double g_dot_out = 0.0;
+                    for (int c = 0; c < D; ++c) {
+                        double num = 0.0;
+                        for (int j = 0; j < D; ++j) num += f[j] * Pb[j * W + c];
+                        const double g = load_elem(dout, dout_dtype, row + c);
+                        uw[c] = g * r;
+                        g_dot_out += g * (num * r);
+                    }
+                    uw[D] = -r * g_dot_out;
+                    for (int j = 0; j < D; ++j) {
+                        double s = 0.0;
+                        for (int c = 0; c < W; ++c) s += Pb[j * W + c] * uw[c];
+                        dq[row + j] = load_elem(q, in_dtype, row + j) > 0.0 ? s : 0.0;
+                        for (int c = 0; c < W; ++c) Gb[j * W + c] += f[j] * uw[c];
+                    }
+                }
+                /* suffix sums over blocks */
+                for (int beta = NB - 2; beta >= 0; --beta)
+                    for (int e = 0; e < D * W; ++e) G[(size_t)beta * D * W + e] += G[(size_t)(beta + 1) * D * W + e];
+                /* keys: dk, dv */
+                for (int n = 0; n < N; ++n) {
+                    const double* Gb = G + (size_t)(n / L) * D * W;
+                    const size_t row = (((size_t)b * N + n) * H + h) * (size_t)D;
+                    for (int c = 0; c < D; ++c) x[c] = load_elem(v, in_dtype, row + c);
+                    for (int j = 0; j < D; ++j) f[j] = relu(load_elem(k, in_dtype, row + j));
+                    for (int j = 0; j < D; ++j) {
+                        double s = Gb[j * W + D];
+                        for (int c = 0; c < D; ++c) s += Gb[j * W + c] * x[c];
+                        dk[row + j] = load_elem(k, in_dtype, row + j) > 0.0 ? s : 0.0;
+                    }
+                    for (int c = 0; c < D; ++c) {
+                        double s = 0.0;
+                        for (int j = 0; j < D; ++j) s += f[j] * Gb[j * W + c];
+                        dv[row + c] = s;
+                    }
+                }
+            }
+        }
+        free(P);
+        free(G);
+        free(f);
+        free(uw);
+        free(x);
+    }
+    return failed ? -1 : 0;
+}
+
 /* Number of threads an OpenMP parallel region would use right now. */
 int oracle_max_threads(void) {
 #ifdef _OPENMP

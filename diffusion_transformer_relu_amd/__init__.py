@@ -49,6 +49,9 @@ _SIGNATURES = {
                                       ctypes.POINTER(ctypes.c_int64), _P, ctypes.c_size_t, _P]),
     "sana_linattn_fwd_stages": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P,
                                      ctypes.c_size_t, _P, _I]),
+    "sana_linattn_bwd_workspace_bytes": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]),
+    "sana_linattn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P,
+                              ctypes.c_size_t, _P]),
 }
 
 if not os.path.exists(LIB_PATH):
@@ -228,3 +231,40 @@ def linattn_fwd(q, k, v, *, eps: float = 1e-15, out_dtype=None, block_len: int |
     else:
         sana_linattn_blockcausal_fwd(q, k, v, out, ws, block_len, eps=eps, stream=stream)
     return out
+
+
+def sana_linattn_bwd_workspace_bytes(B: int, H: int, N: int, D: int, block_len: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.sana_linattn_bwd_workspace_bytes(B, H, N, D, block_len, ctypes.byref(out)),
+           "sana_linattn_bwd_workspace_bytes")
+    return out.value
+
+
+def sana_linattn_bwd(q, k, v, dout, dq, dk, dv, workspace, *, block_len: int = 0, eps: float = 1e-15,
+                     stream=None):
+    """Gradients dq, dk, dv (written in place) of the forward for upstream gradient dout."""
+    B, N, H, D = _shape(q, k, v, dout)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if tuple(t.shape) != (B, N, H, D) or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous GPU tensor of shape {(B, N, H, D)}")
+    if not (dq.dtype == dk.dtype == dv.dtype):
+        raise TypeError("dq, dk and dv must share one dtype")
+    _check(lib.sana_linattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                                dk.data_ptr(), dv.data_ptr(), dtype_code(q), dtype_code(dout), dtype_code(dq),
+                                B, H, N, D, block_len, eps, workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream_handle(stream)),
+           "sana_linattn_bwd")
+
+
+def linattn_bwd(q, k, v, dout, *, eps: float = 1e-15, grad_dtype=None, block_len: int | None = None,
+                stream=None):
+    """Allocates dq, dk, dv (q's dtype unless grad_dtype is given) and the
+    workspace with torch, runs the backward and returns (dq, dk, dv)."""
+    torch = _torch()
+    gt = grad_dtype or q.dtype
+    dq, dk, dv = (torch.empty(q.shape, dtype=gt, device=q.device) for _ in range(3))
+    B, N, H, D = q.shape
+    ws = torch.empty(max(sana_linattn_bwd_workspace_bytes(B, H, N, D, block_len or 0), 1), dtype=torch.uint8,
+                     device=q.device)
+    sana_linattn_bwd(q, k, v, dout, dq, dk, dv, ws, block_len=block_len or 0, eps=eps, stream=stream)
+    return dq, dk, dv

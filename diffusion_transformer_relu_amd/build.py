@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libsana_linattn.so")
-SOURCES = [os.path.join(CSRC, "linattn_kernels.hip"), os.path.join(CSRC, "linattn_api.cpp")]
+SOURCES = [os.path.join(CSRC, "linattn_kernels.hip"), os.path.join(CSRC, "linattn_bwd_kernels.hip"),
+           os.path.join(CSRC, "linattn_api.cpp")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

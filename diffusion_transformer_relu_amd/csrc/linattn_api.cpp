@@ -197,6 +197,88 @@ int forward(const void* q, const void* k, const void* v, void* out, int in_dtype
     return SANA_OK;
 }
 
+// Backward decomposition: the forward's state plan plus query/key tiles and
+// the gradient-state workspace behind the forward's.
+constexpr int kBwdTile = 256;   // tokens per query/key work-group (one per thread)
+
+int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, int N, int D, int block_len,
+                  sana::BwdPlan* bp) {
+    std::memset(bp, 0, sizeof *bp);
+    const int st = make_plan(in_dtype, SANA_DT_F32, B, H, N, D, block_len, &bp->fw);
+    if (st != SANA_OK) return st;
+    for (int c : {dout_dtype, grad_dtype})
+        if (c != SANA_DT_F32 && c != SANA_DT_BF16 && c != SANA_DT_F16) return SANA_ERR_INVALID_ARG;
+    bp->dout_dtype = dout_dtype;
+    bp->grad_dtype = grad_dtype;
+    if (B == 0 || H == 0 || N == 0) return SANA_OK;
+    const Plan& pl = bp->fw;
+    bp->tq = bp->tk = kBwdTile;
+    bp->tpbq = ceil_div(pl.L, bp->tq);
+    bp->tpbk = ceil_div(pl.L, bp->tk);
+    bp->Pq = pl.NB * bp->tpbq;
+    if ((long)B * H * pl.NB * std::max(bp->tpbq, bp->tpbk) > INT_MAX) return SANA_ERR_UNSUPPORTED;
+    const size_t bh = (size_t)B * H;
+    size_t off = pl.bytes;
+    bp->off_gpart = off;
+    off += round_up((long)(bh * bp->Pq * sana::kStateFloats * sizeof(float)), 256);
+    bp->off_ghat = off;
+    off += round_up((long)(bh * pl.NB * sana::kStateFloats * sizeof(float)), 256);
+    bp->bytes = off;
+    return SANA_OK;
+}
+
+int backward(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
+             int in_dtype, int dout_dtype, int grad_dtype, int B, int H, int N, int D, int block_len, float eps,
+             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    sana::BwdPlan bp;
+    const int st = make_bwd_plan(in_dtype, dout_dtype, grad_dtype, B, H, N, D, block_len, &bp);
+    if (st != SANA_OK) return st;
+    if (!std::isfinite(eps) || eps < 0.f) return SANA_ERR_INVALID_ARG;
+    if (B == 0 || H == 0 || N == 0) return SANA_OK;
+    const void* ins[4] = {q, k, v, dout};
+    void* outs[3] = {dq, dk, dv};
+    for (const void* p : ins)
+        if (!p) return SANA_ERR_INVALID_ARG;
+    for (void* p : outs)
+        if (!p) return SANA_ERR_INVALID_ARG;
+    if (!workspace) return SANA_ERR_INVALID_ARG;
+    for (const void* p : ins)
+        if (!aligned(p, 16)) return SANA_ERR_ALIGNMENT;
+    for (void* p : outs)
+        if (!aligned(p, 16)) return SANA_ERR_ALIGNMENT;
+    if (!aligned(workspace, 256)) return SANA_ERR_ALIGNMENT;
+    const size_t elems = (size_t)B * N * H * D;
+    const size_t es_in = in_dtype == SANA_DT_F32 ? 4 : 2;
+    const size_t in_b[4] = {elems * es_in, elems * es_in, elems * es_in,
+                            elems * (dout_dtype == SANA_DT_F32 ? 4 : 2)};
+    const size_t gb = elems * (grad_dtype == SANA_DT_F32 ? 4 : 2);
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 4; ++j)
+            if (overlaps(outs[i], gb, ins[j], in_b[j])) return SANA_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], gb, outs[j], gb)) return SANA_ERR_ALIAS;
+        if (overlaps(outs[i], gb, workspace, bp.bytes)) return SANA_ERR_ALIAS;
+    }
+    for (int j = 0; j < 4; ++j)
+        if (overlaps(workspace, bp.bytes, ins[j], in_b[j])) return SANA_ERR_ALIAS;
+    if (workspace_bytes < bp.bytes) return SANA_ERR_WORKSPACE;
+
+    Plan& pl = bp.fw;
+    pl.sq = pl.sk = pl.sv = pl.so = {(long long)N * H * D, (long long)H * D};
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    float* part = reinterpret_cast<float*>(ws + pl.off_part);
+    float* state = reinterpret_cast<float*>(ws + pl.off_state);
+    float* gpart = reinterpret_cast<float*>(ws + bp.off_gpart);
+    float* ghat = reinterpret_cast<float*>(ws + bp.off_ghat);
+    if (sana::launch_state(pl, k, v, part, stream) != hipSuccess ||
+        sana::launch_merge(pl, part, state, nullptr, nullptr, stream) != hipSuccess ||
+        sana::launch_bwd_query(bp, q, dout, state, dq, gpart, eps, stream) != hipSuccess ||
+        sana::launch_bwd_merge(bp, gpart, ghat, stream) != hipSuccess ||
+        sana::launch_bwd_key(bp, k, v, ghat, dk, dv, stream) != hipSuccess)
+        return SANA_ERR_HIP;
+    return SANA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -226,6 +308,27 @@ int sana_linattn_workspace_bytes(int B, int H, int N, int D, int block_len, size
     make_plan(SANA_DT_F32, SANA_DT_F32, B, H, N, D, block_len, &pv);
     *bytes = pl.bytes > pv.bytes ? pl.bytes : pv.bytes;
     return SANA_OK;
+}
+
+int sana_linattn_bwd_workspace_bytes(int B, int H, int N, int D, int block_len, size_t* bytes) {
+    if (!bytes) return SANA_ERR_INVALID_ARG;
+    size_t most = 0;
+    for (int dt : {SANA_DT_BF16, SANA_DT_F32}) {
+        sana::BwdPlan bp;
+        const int st = make_bwd_plan(dt, SANA_DT_F32, SANA_DT_F32, B, H, N, D, block_len, &bp);
+        if (st != SANA_OK) return st;
+        most = std::max(most, bp.bytes);
+    }
+    *bytes = most;
+    return SANA_OK;
+}
+
+int sana_linattn_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
+                     void* dv, int in_dtype, int dout_dtype, int grad_dtype, int B, int H, int N, int D,
+                     int block_len, float eps, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (block_len < 0) return SANA_ERR_INVALID_ARG;
+    return backward(q, k, v, dout, dq, dk, dv, in_dtype, dout_dtype, grad_dtype, B, H, N, D, block_len, eps,
+                    workspace, workspace_bytes, stream);
 }
 
 int sana_linattn_plan_info(int in_dtype, int B, int H, int N, int D, int block_len, int* chunk_tokens,

@@ -57,4 +57,24 @@ hipError_t launch_merge(const Plan& pl, const float* part, float* state, const f
 hipError_t launch_apply(const Plan& pl, const void* q, const float* state, void* out, float eps,
                         hipStream_t stream);
 
+// Backward: the forward's state and merge kernels rebuild the prefix states
+// P (fw.off_part, fw.off_state), then
+//   query kernel - per query tile: dq, and one partial gradient state
+//                  G = sum_i f_i [dL/dnum_i | dL/dden_i] per tile;
+//   suffix merge - Ghat of block beta = sum of the tiles' G over blocks >= beta;
+//   key kernel   - per key: dk, dv from Ghat of its block.
+struct BwdPlan {
+    Plan fw;
+    int dout_dtype, grad_dtype;
+    int tq, tpbq, Pq;    // query tile, query tiles per block, query tiles per (b, h)
+    int tk, tpbk;        // key tile, key tiles per block
+    size_t off_gpart, off_ghat, bytes;
+};
+
+hipError_t launch_bwd_query(const BwdPlan& bp, const void* q, const void* dout, const float* state, void* dq,
+                            float* gpart, float eps, hipStream_t stream);
+hipError_t launch_bwd_merge(const BwdPlan& bp, const float* gpart, float* ghat, hipStream_t stream);
+hipError_t launch_bwd_key(const BwdPlan& bp, const void* k, const void* v, const float* ghat, void* dk, void* dv,
+                          hipStream_t stream);
+
 }  // namespace sana

@@ -216,6 +216,37 @@ SANA_API int sana_linattn_fwd_stages(const void* q, const void* k, const void* v
                             void* workspace, size_t workspace_bytes, hipStream_t stream,
                             int stages);
 
+/*
+ * Backward: gradients of a scalar loss L with respect to q, k and v, given
+ * dout = dL/dout of the forward with the same arguments.  The operator is the
+ * forward above (non-causal when block_len is 0, block-causal otherwise); its
+ * derivative, with f = ReLU(q), a = ReLU(k), P the state a query's block uses,
+ * r = 1/(f.P[:, D] + eps), u = dout r, w = -r (dout . out):
+ *   dq_i = [q_i > 0] (P [u_i | w_i])
+ *   G^(b) = sum over queries i of block b of f_i [u_i | w_i]^T, and for a key n
+ *   of block b, with Ghat = sum of G over blocks >= b (the key enters the state
+ *   of every later block):
+ *   dk_n = [k_n > 0] (Ghat [v_n | 1]),   dv_n = Ghat[:, :D]^T a_n.
+ * The derivative of ReLU at 0 is taken as 0.  The states are rebuilt from k
+ * and v (nothing needs to be kept from the forward call).
+ *   q, k, v     [B][N][H][D] in in_dtype (fp32, bf16 or fp16), device, read only.
+ *   dout        [B][N][H][D] in dout_dtype, device, read only (may alias nothing
+ *               written).
+ *   dq, dk, dv  [B][N][H][D] in grad_dtype, device, written; must not overlap
+ *               each other, an input or the workspace (error ALIAS).
+ *   block_len   0 = non-causal, >= 1 = block-causal.
+ *   workspace   >= sana_linattn_bwd_workspace_bytes(B, H, N, D, block_len)
+ *               bytes, 256-byte aligned.
+ * Other conventions as for sana_linattn_fwd (16-byte alignment of the tensors,
+ * empty problems, error codes, asynchronous on `stream`, bitwise repeatable).
+ */
+SANA_API int sana_linattn_bwd_workspace_bytes(int B, int H, int N, int D, int block_len, size_t* bytes);
+
+SANA_API int sana_linattn_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                              void* dk, void* dv, int in_dtype, int dout_dtype, int grad_dtype, int B, int H,
+                              int N, int D, int block_len, float eps, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(sana.lib, n), n           # resolves in the shared library
         assert n in sana._SIGNATURES, n          # and the binding declares its signature
@@ -188,3 +188,46 @@ def test_strided_argument_errors():
     args2 = args[:6] + (2,) + args[7:]
     assert f(*args2, st(dense[:6] + [H * D, 2 * H * D]), *tail) == sana.SANA_ERR_WORKSPACE
     assert f(*args2, st(dense[:6] + [H * D, H * D]), *tail) == sana.SANA_ERR_ALIAS
+
+
+def bwd(q=A, k=A + 64 * MB, v=A + 128 * MB, g=A + 192 * MB, dq=A + 256 * MB, dk=A + 320 * MB, dv=A + 384 * MB,
+        in_dt=1, g_dt=1, gr_dt=1, B=1, H=2, N=256, D=32, L=0, eps=1e-15, ws=A + 512 * MB, ws_bytes=16):
+    # ws_bytes 16 is too small: a call whose other checks pass stops with WORKSPACE, never launching
+    return sana.lib.sana_linattn_bwd(q, k, v, g, dq, dk, dv, in_dt, g_dt, gr_dt, B, H, N, D, L, eps, ws,
+                                     ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, sana.SANA_ERR_WORKSPACE),
+    (dict(L=64), sana.SANA_ERR_WORKSPACE),
+    (dict(in_dt=0, g_dt=0, gr_dt=0), sana.SANA_ERR_WORKSPACE),
+    (dict(in_dt=2, g_dt=2, gr_dt=2), sana.SANA_ERR_WORKSPACE),
+    (dict(L=-1), sana.SANA_ERR_INVALID_ARG),
+    (dict(g=None), sana.SANA_ERR_INVALID_ARG),
+    (dict(dv=None), sana.SANA_ERR_INVALID_ARG),
+    (dict(ws=None), sana.SANA_ERR_INVALID_ARG),
+    (dict(g_dt=3), sana.SANA_ERR_INVALID_ARG),
+    (dict(gr_dt=-1), sana.SANA_ERR_INVALID_ARG),
+    (dict(in_dt=5), sana.SANA_ERR_INVALID_ARG),
+    (dict(D=64), sana.SANA_ERR_UNSUPPORTED),
+    (dict(eps=float("nan")), sana.SANA_ERR_INVALID_ARG),
+    (dict(dk=A + 320 * MB + 8), sana.SANA_ERR_ALIGNMENT),
+    (dict(g=A + 192 * MB + 2), sana.SANA_ERR_ALIGNMENT),
+    (dict(dq=A), sana.SANA_ERR_ALIAS),                  # dq == q
+    (dict(dk=A + 192 * MB), sana.SANA_ERR_ALIAS),       # dk == dout
+    (dict(dv=A + 256 * MB), sana.SANA_ERR_ALIAS),       # dv == dq
+    (dict(ws=A + 384 * MB), sana.SANA_ERR_ALIAS),       # workspace == dv
+    (dict(B=0), sana.SANA_OK),
+    (dict(N=0, q=None, ws=None), sana.SANA_OK),
+])
+def test_backward_argument_errors(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_backward_workspace_query():
+    fw = sana.sana_linattn_workspace_bytes(1, 70, 16384, 32, 0)
+    bw = sana.sana_linattn_bwd_workspace_bytes(1, 70, 16384, 32, 0)
+    assert bw > fw and bw % 256 == 0
+    assert sana.sana_linattn_bwd_workspace_bytes(1, 70, 16384, 32, 1024) > bw
+    assert sana.sana_linattn_bwd_workspace_bytes(0, 70, 16384, 32, 0) == 0
+    assert sana.lib.sana_linattn_bwd_workspace_bytes(1, 1, 1, 32, 0, None) == sana.SANA_ERR_INVALID_ARG

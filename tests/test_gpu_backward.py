@@ -1,0 +1,116 @@
+"""GPU parity of the backward (dq, dk, dv) through the C ABI against the fp64
+oracle's backward, element by element, on the same seeded inputs."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from hip_helpers import bf16_round, f16_round, to_device
+
+pytestmark = pytest.mark.gpu
+
+# Bar: the forward's (rel-L2 <= 1e-4) with max-abs taken relative to each
+# gradient's own scale, max-abs <= 2e-3 * max|exact gradient|.  A 16-bit
+# gradient is compared with the rounded exact gradient instead, and each
+# element must lie within one ulp of the exact value plus 1e-6 of the scale
+# (the fp32 pipeline's own error), as for a 16-bit forward output.
+REL_L2 = 1e-4
+MAX_ABS_FRAC = 2e-3
+
+DT = {workloads.DT_F32: torch.float32, workloads.DT_BF16: torch.bfloat16, workloads.DT_F16: torch.float16}
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu] {request.node.name}", flush=True)
+
+
+@functools.lru_cache(maxsize=4)
+def case(w, gdt):
+    q, k, v = workloads.make_inputs(w)
+    g = workloads.make_dout(w, gdt)
+    return (q, k, v, g), oracle.linattn_bwd(q, k, v, g, block_len=w.block_len, eps=w.eps)
+
+
+def check(got, want, grad_t, label):
+    for name, a, b in zip(("dq", "dk", "dv"), got, want):
+        a = a.float().cpu().double().numpy()
+        ref = b if grad_t == torch.float32 else (bf16_round(b) if grad_t == torch.bfloat16 else f16_round(b))
+        diff = a - ref
+        scale = float(np.max(np.abs(b))) if b.size else 1.0
+        rel = float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-300))
+        assert np.all(np.isfinite(a)), f"{label}/{name}"
+        assert rel <= REL_L2, f"{label}/{name}: rel L2 {rel:.3e}"
+        if grad_t == torch.float32:
+            assert float(np.max(np.abs(diff))) <= MAX_ABS_FRAC * scale, f"{label}/{name}: max abs"
+        else:
+            e = np.floor(np.log2(np.maximum(np.abs(b), 1e-300)))
+            ulp = np.exp2(e - 7) if grad_t == torch.bfloat16 else np.exp2(np.maximum(e, -14) - 10)
+            bad = np.abs(a - b) > ulp + 1e-6 * scale
+            assert not np.any(bad), f"{label}/{name}: {int(bad.sum())} values beyond one ulp"
+
+
+def run(q, k, v, g, block_len, eps, grad_t):
+    import diffusion_transformer_relu_amd as sana
+    out = sana.linattn_bwd(to_device(q), to_device(k), to_device(v), to_device(g), eps=eps, grad_dtype=grad_t,
+                           block_len=block_len or None)
+    torch.cuda.synchronize()
+    return out
+
+
+FULL = [workloads.S600M_1024, workloads.S1600M_2048, workloads.HEADLINE, workloads.BLOCK_CAUSAL]
+
+
+@pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
+@pytest.mark.parametrize("grad_t", [torch.float32, torch.bfloat16], ids=["f32grad", "bf16grad"])
+def test_backward_full_size(w, grad_t):
+    (q, k, v, g), want = case(w, workloads.DT_BF16)
+    check(run(q, k, v, g, w.block_len, w.eps, grad_t), want, grad_t, w.name)
+
+
+EDGE = [(2, 33, 3, 0, 1), (1, 257, 2, 64, 1), (3, 1000, 5, 100, 2), (1, 300, 2, 1, 0),
+        (1, 4097, 1, 0, 2), (2, 256, 3, 0, 0)]
+
+
+@pytest.mark.parametrize("B,N,H,L,dt", EDGE, ids=[f"B{b}N{n}H{h}L{l}dt{d}" for b, n, h, l, d in EDGE])
+def test_backward_edge_shapes(B, N, H, L, dt):
+    w = workloads.Workload(f"bwd_B{B}N{N}H{H}L{L}dt{dt}", B, N, H, 32, dt, seed=80 + N % 11, block_len=L)
+    (q, k, v, g), want = case(w, dt)
+    check(run(q, k, v, g, L, w.eps, DT[dt]), want, DT[dt], w.name)
+    check(run(q, k, v, g, L, w.eps, torch.float32), want, torch.float32, w.name + "/f32grad")
+
+
+def test_backward_single_token_is_identity_in_v():
+    """N = 1: out = v * den / (den + eps) does not depend on q or k (their
+    exact gradients vanish; what is left is rounding of cancelling terms), and
+    dv = dout * den / (den + eps)."""
+    w = workloads.Workload("bwd_N1", 2, 1, 3, 32, workloads.DT_F32, seed=93)
+    (q, k, v, g), (dq0, dk0, dv0) = case(w, workloads.DT_F32)
+    dq, dk, dv = (t.cpu().double().numpy() for t in run(q, k, v, g, 0, w.eps, torch.float32))
+    assert np.max(np.abs(dq0)) < 1e-12 and np.max(np.abs(dk0)) < 1e-12
+    assert np.max(np.abs(dq)) < 1e-5 and np.max(np.abs(dk)) < 1e-5
+    np.testing.assert_allclose(dv, dv0, rtol=1e-6, atol=1e-7)
+
+
+def test_backward_eps_path_and_repeatability():
+    w = workloads.Workload("bwd_eps", 1, 512, 3, 32, workloads.DT_BF16, seed=91, negative_k_heads=(1,),
+                           negative_q_rows=((0, 7, 0), (0, 300, 2)))
+    (q, k, v, g), want = case(w, workloads.DT_BF16)
+    a = run(q, k, v, g, 0, w.eps, torch.float32)
+    b = run(q, k, v, g, 0, w.eps, torch.float32)
+    check(a, want, torch.float32, w.name)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    for t in a:
+        assert torch.all(t[:, :, 1] == 0)
+    assert torch.all(a[0][0, 7, 0] == 0) and torch.all(a[0][0, 300, 2] == 0)
+
+
+def test_backward_mixed_dtypes():
+    """fp16 inputs with an fp32 upstream gradient and bf16 gradients out."""
+    w = workloads.Workload("bwd_mixed", 2, 2048, 6, 32, workloads.DT_F16, seed=92, block_len=512)
+    (q, k, v, g), want = case(w, workloads.DT_F32)
+    check(run(q, k, v, g, w.block_len, w.eps, torch.bfloat16), want, torch.bfloat16, w.name)

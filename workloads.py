@@ -123,3 +123,16 @@ def with_shape(w: Workload, **kw) -> Workload:
     """A copy of workload w with some fields changed (e.g. a smaller N)."""
     name = kw.pop("name", None) or (w.name + "_" + "_".join(f"{k}{v}" for k, v in kw.items()))
     return replace(w, name=name, **kw)
+
+
+def make_dout(w: Workload, dtype: int | None = None):
+    """Seeded upstream gradient dL/dout for backward tests, [B, N, H, D]:
+    ``default_rng([seed, 3])`` standard normal, in dtype (default w.in_dtype)
+    with the same rounding as make_inputs."""
+    dtype = w.in_dtype if dtype is None else dtype
+    x = np.random.default_rng([w.seed, 3]).standard_normal(size=(w.B, w.N, w.H, w.D), dtype=np.float32)
+    if dtype == DT_BF16:
+        return f32_to_bf16_bits(x)
+    if dtype == DT_F16:
+        return x.astype(np.float16)
+    return x

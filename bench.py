@@ -29,7 +29,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "LiteLA fwd GB/s & tokens*heads/s at N=16384,H=70,D=32; % of HBM peak"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "diffusion_transformer_relu_amd", "csrc", "linattn_kernels.hip")
+# the forward kernels and the headers they include
+KERNEL_SRC = [os.path.join(ROOT, "diffusion_transformer_relu_amd", "csrc", f)
+              for f in ("linattn_kernels.hip", "linattn_device.h", "linattn_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -38,8 +40,11 @@ def log(*a):
 
 
 def kernel_source_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel: str, workload: str, out_dtype: str):

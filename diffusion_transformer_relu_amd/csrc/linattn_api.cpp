@@ -212,7 +212,15 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
     bp->grad_dtype = grad_dtype;
     if (B == 0 || H == 0 || N == 0) return SANA_OK;
     const Plan& pl = bp->fw;
-    bp->tq = bp->tk = kBwdTile;
+    bp->key_mfma = bp->query_mfma = pl.mfma;
+    if (pl.mfma) {
+        // about one round of work-groups (head pairs x tiles), tiles of 64 tokens
+        const long units = (long)B * pl.HP * pl.NB;
+        const long per_block = std::max<long>(1, sana::kApplyGroups * 4 / 5 / units);
+        bp->tk = bp->tq = (int)std::min<long>(round_up(ceil_div(pl.L, per_block), 64), round_up(pl.L, 64));
+    } else {
+        bp->tk = bp->tq = kBwdTile;
+    }
     bp->tpbq = ceil_div(pl.L, bp->tq);
     bp->tpbk = ceil_div(pl.L, bp->tk);
     bp->Pq = pl.NB * bp->tpbq;

@@ -14,27 +14,17 @@
 //   dk_n = [k_n > 0] (Ghat [v_n | 1]),   dv_n = Ghat[:, :D]^T a_n
 // The derivative of ReLU at 0 is taken as 0.  Everything accumulates in fp32;
 // reductions run in fixed orders, so results are bitwise repeatable.
-#include "linattn_internal.h"
+#include "linattn_device.h"
 
 namespace sana {
 namespace {
 
-__device__ __forceinline__ float ld(const float* p, long long i) { return p[i]; }
-__device__ __forceinline__ float ld(const uint16_t* p, long long i) {
-    return __builtin_bit_cast(float, (uint32_t)p[i] << 16);
-}
-__device__ __forceinline__ float ld(const _Float16* p, long long i) { return (float)p[i]; }
-
-// Round to nearest, ties to even (finite inputs; NaN is kept a quiet NaN).
-__device__ __forceinline__ uint16_t to_bf16(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-__device__ __forceinline__ void st(float* p, long long i, float x) { p[i] = x; }
-__device__ __forceinline__ void st(uint16_t* p, long long i, float x) { p[i] = to_bf16(x); }
-__device__ __forceinline__ void st(_Float16* p, long long i, float x) { p[i] = (_Float16)x; }
+__device__ __forceinline__ float ld(const float* p, long long i) { return load_in(p, i); }
+__device__ __forceinline__ float ld(const uint16_t* p, long long i) { return load_in(p, i); }
+__device__ __forceinline__ float ld(const _Float16* p, long long i) { return load_in(p, i); }
+__device__ __forceinline__ void st(float* p, long long i, float x) { store_out(p, i, x); }
+__device__ __forceinline__ void st(uint16_t* p, long long i, float x) { store_out(p, i, x); }
+__device__ __forceinline__ void st(_Float16* p, long long i, float x) { store_out(p, i, x); }
 
 constexpr int kTok = 256;   // tokens per work-group of the vector kernels (one per thread)
 
@@ -176,6 +166,505 @@ __global__ __launch_bounds__(kThreads) void k_bwd_key_valu(
     }
 }
 
+// ------------------------------------------------------------------ matrix-core helpers
+constexpr int kPitch = 36;   // floats per LDS tile row: 32 + 4 keeps rows 16-byte aligned, no bank conflicts
+
+// MFMA operands of a D x (D+1) fp32 state S (row-major, kW floats per row),
+// each as three bf16 split terms, for lane (g, i) of a wave:
+//   transposed: A[row i][k = 16 ks + 8 g + e] = S[16 ks + 8 g + e][i]
+//   natural:    A[row i][k = 16 ks + 8 g + e] = S[i][16 ks + 8 g + e]
+__device__ __forceinline__ void state_operands(const float* S, int lane, bool transposed, u32x4 out[2][3]) {
+    const int g = lane >> 5, i = lane & 31;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int kk = 16 * ks + 8 * g + e;
+            x[e] = transposed ? S[kk * kW + i] : S[i * kW + kk];
+        }
+        split3_f32x8(x, out[ks]);
+    }
+}
+
+// acc += sum over the 32 features of A (three split terms) times the B operand
+// b0 (features 8g..8g+7 of this lane's token) and b1 (features 16+8g..): bf16
+// bits, or fp16 bits split exactly into two bf16 terms.  Small terms first.
+template <bool F16>
+__device__ __forceinline__ f32x16 mma_split(const u32x4 A[2][3], u32x4 b0, u32x4 b1, f32x16 acc) {
+    if constexpr (F16) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const u32x4 x = ks ? b1 : b0;
+            u32x4 hi, lo;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                uint32_t h, l;
+                float f0, f1;
+                split_f16x2(x[d], h, l, f0, f1);
+                hi[d] = h;
+                lo[d] = l;
+            }
+#pragma unroll
+            for (int sp = 2; sp >= 0; --sp) acc = mfma_bf16(A[ks][sp], lo, acc);
+#pragma unroll
+            for (int sp = 2; sp >= 0; --sp) acc = mfma_bf16(A[ks][sp], hi, acc);
+        }
+    } else {
+#pragma unroll
+        for (int sp = 2; sp >= 0; --sp) {
+            acc = mfma_bf16(A[0][sp], b0, acc);
+            acc = mfma_bf16(A[1][sp], b1, acc);
+        }
+    }
+    return acc;
+}
+
+// Bit j set when feature j of this lane's token is non-zero in the packed
+// operand words x0 (features 8g + ..) and x1 (16 + 8g + ..); the partner lane
+// (i + 32) contributes the other 16 features.
+__device__ __forceinline__ uint32_t nonzero_mask(u32x4 x0, u32x4 x1, int g) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        m |= (uint32_t)((x0[d] & 0xffffu) != 0) << (8 * g + 2 * d);
+        m |= (uint32_t)((x0[d] >> 16) != 0) << (8 * g + 2 * d + 1);
+        m |= (uint32_t)((x1[d] & 0xffffu) != 0) << (16 + 8 * g + 2 * d);
+        m |= (uint32_t)((x1[d] >> 16) != 0) << (16 + 8 * g + 2 * d + 1);
+    }
+    return m | (uint32_t)__shfl_xor((int)m, 32);
+}
+
+// Writes a wave's 32 x 32 accumulator tile (row 8*(r/4) + 4g + r%4 of column
+// i in register r of lane (g, i)) token-major through the wave's LDS tile, then
+// stores whole rows: dst(t) is the output row of token tt + t.  Rows t >= n
+// were computed from the clamped input row n - 1, so they hold exactly row
+// n - 1's values: they are stored there again (the same values), which keeps
+// every store unconditional.
+template <typename OutT, typename RowPtr>
+__device__ __forceinline__ void store_tile(float* ot, const f32x16& acc, int lane, int n, RowPtr dst) {
+    const int g = lane >> 5, i = lane & 31;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+        *reinterpret_cast<f32x4*>(ot + i * kPitch + 8 * rr + 4 * g) =
+            (f32x4){acc[4 * rr], acc[4 * rr + 1], acc[4 * rr + 2], acc[4 * rr + 3]};
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+        const int r = 8 * s4 + (lane >> 3), cc = (lane & 7) * 4;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(ot + r * kPitch + cc);
+        store4(dst(min(r, n - 1)) + cc, x);
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Split-term operands of the two heads of a work-group, kept in LDS (too many
+// to keep in registers next to the streaming tiles): [head][layout][ks][sp]
+// of 64 lanes x 16 bytes, layout 0 = transposed, 1 = natural (state_operands).
+struct OperandLds {
+    u32x4 v[2][2][2][3][64];
+};
+
+__device__ __forceinline__ void mma_split_lds(const OperandLds& o, int hh, int lay, int lane, u32x4 b0, u32x4 b1,
+                                              f32x16& acc, bool f16) {
+    u32x4 A[2][3];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int sp = 0; sp < 3; ++sp) A[ks][sp] = o.v[hh][lay][ks][sp][lane];
+    acc = f16 ? mma_split<true>(A, b0, b1, acc) : mma_split<false>(A, b0, b1, acc);
+}
+
+// ------------------------------------------------------------------ key pass, matrix cores
+// grid.x = (b * HP + hp) * (NB * tpb) + beta * tpb + tile.  Wave w handles head
+// 2*hp + (w & 1) and every other 32-key sub-tile (w >> 1) of the work-group's
+// range, which never crosses a block.  Per sub-tile, with a = ReLU(k):
+//   dv^T = Ghat_v^T a^T          (A = Ghat transposed, B = a straight from HBM)
+//   da^T = Ghat_v v^T + Ghat_z   (A = Ghat natural,    B = v straight from HBM)
+//   dk   = da masked by k > 0
+template <bool F16, typename OutT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_bwd_key_mfma(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ ghat,
+    OutT* __restrict__ dk, OutT* __restrict__ dv, int N, int H, int HP, int L, int NB, int tile, int tpb) {
+    __shared__ __attribute__((aligned(16))) float otile[4][32 * kPitch];
+    __shared__ OperandLds opnd;
+    __shared__ __attribute__((aligned(16))) float gzs[2][32];   // Ghat[:, D] of each head
+
+    const int per_unit = NB * tpb;
+    const int tau = blockIdx.x % per_unit;
+    const int bhp = blockIdx.x / per_unit;
+    const int hp = bhp % HP, b = bhp / HP;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int hh = wave & 1, h = 2 * hp + hh;
+    const int beta = tau / tpb, tib = tau - beta * tpb;
+    const int blk0 = beta * L, blk1 = min(blk0 + L, N);
+    const int t0 = blk0 + tib * tile, t1 = min(t0 + tile, blk1);
+    const int g = lane >> 5, i = lane & 31;
+
+    // waves 0 and 1 build the operands of heads 0 and 1; every wave reaches the barrier
+    if (wave < 2 && h < H) {
+        const float* G = ghat + (((size_t)b * H + h) * NB + beta) * kStateFloats;
+        u32x4 t[2][3];
+        state_operands(G, lane, true, t);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int sp = 0; sp < 3; ++sp) opnd.v[hh][0][ks][sp][lane] = t[ks][sp];
+        state_operands(G, lane, false, t);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int sp = 0; sp < 3; ++sp) opnd.v[hh][1][ks][sp][lane] = t[ks][sp];
+        if (lane < 32) gzs[hh][lane] = G[lane * kW + kD];
+    }
+    __syncthreads();
+    if (h >= H || t0 >= t1) return;
+
+    const long long hstride = (long long)H * kD;
+    // Rows past the range are clamped to its last row rather than skipped:
+    // every load is unconditional, so the compiler can count the loads in
+    // flight exactly and the prefetch overlaps the work.  A clamped row only
+    // feeds its own output column, which is never stored.
+    auto load_b = [&](const uint16_t* base, int tt, u32x4& x0, u32x4& x1) {
+        const int row = min(tt + i, t1 - 1);
+        const u32x4* src = reinterpret_cast<const u32x4*>(base + ((long long)b * N + row) * hstride + h * kD + 8 * g);
+        x0 = __builtin_nontemporal_load(src);
+        x1 = __builtin_nontemporal_load(src + 2);
+    };
+    float* ot = otile[wave];
+    // One 32-key sub-tile: x = {k features 8g.., k 16+8g.., v 8g.., v 16+8g..}.
+    auto body = [&](int tt, const u32x4 (&x)[4]) {
+        // keep the LDS operands in LDS: without this the loads are hoisted out
+        // of the loop and the registers they take cut the occupancy
+        asm volatile("" ::: "memory");
+        const u32x4 a0 = relu_bf16x8(x[0]), a1 = relu_bf16x8(x[1]);
+        const uint32_t mask = nonzero_mask(a0, a1, g);
+        const int n = min(32, t1 - tt);
+
+        f32x16 acc = {};
+        mma_split_lds(opnd, hh, 0, lane, a0, a1, acc, F16);
+        store_tile<OutT>(ot, acc, lane, n, [&](int t) { return dv + ((long long)b * N + tt + t) * hstride + h * kD; });
+
+        acc = (f32x16){};
+        mma_split_lds(opnd, hh, 1, lane, x[2], x[3], acc, F16);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const f32x4 z = *reinterpret_cast<const f32x4*>(&gzs[hh][8 * rr + 4 * g]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * rr + e, j = 8 * rr + 4 * g + e;
+                acc[r] = ((mask >> j) & 1u) ? acc[r] + z[e] : 0.f;
+            }
+        }
+        store_tile<OutT>(ot, acc, lane, n, [&](int t) { return dk + ((long long)b * N + tt + t) * hstride + h * kD; });
+    };
+    auto load = [&](int tt, u32x4 (&x)[4]) {
+        load_b(k, tt, x[0], x[1]);
+        load_b(v, tt, x[2], x[3]);
+    };
+    // two register sets alternate (no copies between them), so the next
+    // sub-tile's loads are in flight during the current one's work
+    u32x4 xa[4], xb[4];
+    int tt = t0 + 32 * (wave >> 1);
+    load(tt, xa);
+    while (tt < t1) {
+        load(tt + 64, xb);
+        body(tt, xa);
+        tt += 64;
+        if (tt >= t1) break;
+        load(tt + 64, xa);
+        body(tt, xb);
+        tt += 64;
+    }
+}
+
+// ------------------------------------------------------------------ query pass, matrix cores
+// Upstream gradient of one token in the accumulator layout: lane (g, i) gets
+// features 8 rr + 4 g .. + 3 (rr = 0..3) of its token.
+template <typename GT> struct GradRow;
+template <> struct GradRow<float> {
+    f32x4 x[4];
+    __device__ __forceinline__ void load(const float* row, int g) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) x[rr] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 8 * rr + 4 * g));
+    }
+    __device__ __forceinline__ float at(int rr, int e) const { return x[rr][e]; }
+};
+template <> struct GradRow<uint16_t> {
+    u32x2 x[4];
+    __device__ __forceinline__ void load(const uint16_t* row, int g) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) x[rr] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(row + 8 * rr + 4 * g));
+    }
+    __device__ __forceinline__ float at(int rr, int e) const {
+        const uint32_t w = x[rr][e >> 1];
+        return (e & 1) ? hi_bf16(w) : lo_bf16(w);
+    }
+};
+template <> struct GradRow<_Float16> {
+    u32x2 x[4];
+    __device__ __forceinline__ void load(const _Float16* row, int g) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) x[rr] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(row + 8 * rr + 4 * g));
+    }
+    __device__ __forceinline__ float at(int rr, int e) const {
+        const uint32_t w = x[rr][e >> 1];
+        return f16_to_f32((uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
+    }
+};
+
+// grid.x = (b * HP + hp) * (NB * tpb) + beta * tpb + tile.  Wave w handles head
+// 2*hp + (w & 1) and every other 32-query sub-tile (w >> 1).  Per sub-tile,
+// with f = ReLU(q) and P the block's state:
+//   num^T = P_v^T f^T (A = P transposed, B = f from HBM); den = f . P[:, D] in
+//   fp32; r = 1 / (den + eps); u = dout r; w = -r (dout . num r)
+//   dq^T = P_v u^T + P[:, D] w, masked by q > 0 (A = P natural, B = u as three
+//   bf16 terms read back from the wave's LDS tile; terms below 2^-24 dropped)
+//   G += f^T [u | w]  (tokens are the reduction dimension: f and u gathered
+//   from the LDS tiles, u and w split into three bf16 terms)
+// The two waves of a head then add their G in a fixed order and write the
+// tile's partial gradient state.
+template <bool F16, typename GT, typename OutT>
+__global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
+    const uint16_t* __restrict__ q, const GT* __restrict__ dout, const float* __restrict__ state,
+    OutT* __restrict__ dq, float* __restrict__ gpart, int N, int H, int HP, int L, int NB, int tile, int tpb,
+    float eps) {
+    __shared__ OperandLds opnd;                                     // P, both layouts, both heads
+    __shared__ __attribute__((aligned(16))) float pzs[2][32];       // P[:, D] of each head
+    __shared__ __attribute__((aligned(16))) float ut[4][32 * kPitch];   // u tile, then the dq tile
+    __shared__ __attribute__((aligned(16))) uint16_t ft[4][32 * 32];    // f tile (16-bit bits)
+    __shared__ float wv[4][32];                                     // w of each token
+
+    const int per_unit = NB * tpb;
+    const int tau = blockIdx.x % per_unit;
+    const int bhp = blockIdx.x / per_unit;
+    const int hp = bhp % HP, b = bhp / HP;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int hh = wave & 1, h = 2 * hp + hh;
+    const int beta = tau / tpb, tib = tau - beta * tpb;
+    const int blk0 = beta * L, blk1 = min(blk0 + L, N);
+    const int t0 = blk0 + tib * tile, t1 = min(t0 + tile, blk1);
+    const int g = lane >> 5, i = lane & 31;
+
+    if (wave < 2 && h < H) {
+        const float* Pst = state + (((size_t)b * H + h) * NB + beta) * kStateFloats;
+        u32x4 t[2][3];
+        state_operands(Pst, lane, true, t);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int sp = 0; sp < 3; ++sp) opnd.v[hh][0][ks][sp][lane] = t[ks][sp];
+        state_operands(Pst, lane, false, t);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int sp = 0; sp < 3; ++sp) opnd.v[hh][1][ks][sp][lane] = t[ks][sp];
+        if (lane < 32) pzs[hh][lane] = Pst[lane * kW + kD];
+    }
+    __syncthreads();
+
+    const long long hstride = (long long)H * kD;
+    const bool active = h < H && t0 < t1;
+    float* ot = ut[wave];
+    uint16_t* fw = ft[wave];
+    float* wl = wv[wave];
+    f32x16 accG = {}, accGz = {};
+
+    struct Tile {
+        u32x4 q0, q1;
+        GradRow<GT> gr;
+    };
+    // rows past the range are clamped to its last row: their dq columns then
+    // equal that row's (store_tile relies on it), and the gathers for G skip
+    // them
+    auto load = [&](int tt, Tile& x) {
+        const int row = min(tt + i, t1 - 1);
+        const uint16_t* qr = q + ((long long)b * N + row) * hstride + h * kD;
+        const u32x4* src = reinterpret_cast<const u32x4*>(qr + 8 * g);
+        x.q0 = __builtin_nontemporal_load(src);
+        x.q1 = __builtin_nontemporal_load(src + 2);
+        x.gr.load(dout + ((long long)b * N + row) * hstride + h * kD, g);
+    };
+    auto body = [&](int tt, const Tile& x) {
+        asm volatile("" ::: "memory");   // keep the LDS operands in LDS (see the key kernel)
+        const int n = min(32, t1 - tt);
+        const u32x4 f0 = relu_bf16x8(x.q0), f1 = relu_bf16x8(x.q1);
+        const uint32_t mask = nonzero_mask(f0, f1, g);
+        *reinterpret_cast<u32x4*>(fw + i * 32 + 8 * g) = f0;
+        *reinterpret_cast<u32x4*>(fw + i * 32 + 16 + 8 * g) = f1;
+
+        // numerators and the normaliser
+        f32x16 acc = {};
+        mma_split_lds(opnd, hh, 0, lane, f0, f1, acc, F16);
+        float dp = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const u32x4 fx = ks ? f1 : f0;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int j = 16 * ks + 8 * g + 2 * d;
+                float lo, hi;
+                if constexpr (F16) {
+                    lo = f16_to_f32((uint16_t)(fx[d] & 0xffffu));
+                    hi = f16_to_f32((uint16_t)(fx[d] >> 16));
+                } else {
+                    lo = lo_bf16(fx[d]);
+                    hi = hi_bf16(fx[d]);
+                }
+                dp = fmaf(lo, pzs[hh][j], dp);
+                dp = fmaf(hi, pzs[hh][j + 1], dp);
+            }
+        }
+        const float den = dp + __shfl_xor(dp, 32);
+        const float r = 1.0f / (den + eps);
+        float go = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) go = fmaf(x.gr.at(rr, e), acc[4 * rr + e], go);
+        go += __shfl_xor(go, 32);
+        const float w = -(r * r) * go;
+        // u to the LDS tile (token-major), w to the token vector
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            f32x4 u4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u4[e] = x.gr.at(rr, e) * r;
+            *reinterpret_cast<f32x4*>(ot + i * kPitch + 8 * rr + 4 * g) = u4;
+        }
+        if (g == 0) wl[i] = w;
+        __builtin_amdgcn_wave_barrier();
+
+        // G += f^T [u | w]: lane (g, c) gathers tokens 16 ks + 8 g + e
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            float uu[8], ww[8];
+            u32x4 af;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int tok = 16 * ks + 8 * g + e;
+                uu[e] = tok < n ? ot[tok * kPitch + i] : 0.f;
+                ww[e] = tok < n ? wl[tok] : 0.f;
+            }
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int tok = 16 * ks + 8 * g + 2 * d;
+                const uint32_t lo = tok < n ? fw[tok * 32 + i] : 0u, hi = tok + 1 < n ? fw[(tok + 1) * 32 + i] : 0u;
+                af[d] = lo | (hi << 16);
+            }
+            u32x4 bu[3], bw[3];
+            split3_f32x8(uu, bu);
+            split3_f32x8(ww, bw);
+            if constexpr (F16) {
+                u32x4 fhi, flo;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    uint32_t hv, lv;
+                    float f0_, f1_;
+                    split_f16x2(af[d], hv, lv, f0_, f1_);
+                    fhi[d] = hv;
+                    flo[d] = lv;
+                }
+#pragma unroll
+                for (int sp = 2; sp >= 0; --sp) {
+                    accG = mfma_bf16(flo, bu[sp], accG);
+                    accGz = mfma_bf16(flo, bw[sp], accGz);
+                }
+#pragma unroll
+                for (int sp = 2; sp >= 0; --sp) {
+                    accG = mfma_bf16(fhi, bu[sp], accG);
+                    accGz = mfma_bf16(fhi, bw[sp], accGz);
+                }
+            } else {
+#pragma unroll
+                for (int sp = 2; sp >= 0; --sp) {
+                    accG = mfma_bf16(af, bu[sp], accG);
+                    accGz = mfma_bf16(af, bw[sp], accGz);
+                }
+            }
+        }
+
+        // dq^T = P_v u^T (+ P[:, D] w), B = u in the operand layout from the tile
+        u32x4 ub[2][3];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            float uu[8];
+            const f32x4 a4 = *reinterpret_cast<const f32x4*>(ot + i * kPitch + 16 * ks + 8 * g);
+            const f32x4 b4 = *reinterpret_cast<const f32x4*>(ot + i * kPitch + 16 * ks + 8 * g + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uu[e] = a4[e];
+                uu[4 + e] = b4[e];
+            }
+            split3_f32x8(uu, ub[ks]);
+        }
+        __builtin_amdgcn_wave_barrier();
+        acc = (f32x16){};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            u32x4 A[3];
+#pragma unroll
+            for (int sp = 0; sp < 3; ++sp) A[sp] = opnd.v[hh][1][ks][sp][lane];
+            // products of split terms in increasing size; those below 2^-24 are dropped
+            acc = mfma_bf16(A[0], ub[ks][2], acc);
+            acc = mfma_bf16(A[1], ub[ks][1], acc);
+            acc = mfma_bf16(A[2], ub[ks][0], acc);
+            acc = mfma_bf16(A[0], ub[ks][1], acc);
+            acc = mfma_bf16(A[1], ub[ks][0], acc);
+            acc = mfma_bf16(A[0], ub[ks][0], acc);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const f32x4 z = *reinterpret_cast<const f32x4*>(&pzs[hh][8 * rr + 4 * g]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rg = 4 * rr + e, j = 8 * rr + 4 * g + e;
+                acc[rg] = ((mask >> j) & 1u) ? fmaf(z[e], w, acc[rg]) : 0.f;
+            }
+        }
+        store_tile<OutT>(ot, acc, lane, n, [&](int t) { return dq + ((long long)b * N + tt + t) * hstride + h * kD; });
+    };
+
+    if (active) {
+        Tile xa, xb;
+        int tt = t0 + 32 * (wave >> 1);
+        if (tt < t1) load(tt, xa);
+        while (tt < t1) {
+            if (tt + 64 < t1) load(tt + 64, xb);
+            body(tt, xa);
+            tt += 64;
+            if (tt >= t1) break;
+            if (tt + 64 < t1) load(tt + 64, xa);
+            body(tt, xb);
+            tt += 64;
+        }
+    }
+
+    // the two waves of a head add their G in a fixed order; the LDS operands
+    // are no longer needed, so their space holds the second wave's G
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(&opnd);   // [head][G | Gz][16][64]
+    if (wave >= 2) {
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) {
+            red[((hh * 2 + 0) * 16 + rg) * 64 + lane] = accG[rg];
+            red[((hh * 2 + 1) * 16 + rg) * 64 + lane] = accGz[rg];
+        }
+    }
+    __syncthreads();
+    if (wave < 2 && h < H) {
+        float* dst = gpart + ((((size_t)b * H + h) * NB + beta) * tpb + tib) * kStateFloats;
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) {
+            const int j = 8 * (rg >> 2) + 4 * g + (rg & 3);
+            dst[j * kW + i] = accG[rg] + red[((hh * 2 + 0) * 16 + rg) * 64 + lane];
+            if (i == 0) dst[j * kW + kD] = accGz[rg] + red[((hh * 2 + 1) * 16 + rg) * 64 + lane];
+        }
+    }
+}
+
+static_assert(sizeof(OperandLds) >= 2 * 2 * 16 * 64 * sizeof(float), "G reduction area exceeds the operand space");
+
 template <typename T> struct Tag { using type = T; };
 template <typename F> void by_dtype(int code, F&& f) {
     if (code == 1)
@@ -191,6 +680,25 @@ template <typename F> void by_dtype(int code, F&& f) {
 hipError_t launch_bwd_query(const BwdPlan& bp, const void* q, const void* dout, const float* state, void* dq,
                             float* gpart, float eps, hipStream_t stream) {
     const Plan& pl = bp.fw;
+    if (bp.query_mfma) {
+        const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.NB * bp.tpbq);
+        const uint16_t* q16 = static_cast<const uint16_t*>(q);
+        by_dtype(bp.dout_dtype, [&](auto gt) {
+            by_dtype(bp.grad_dtype, [&](auto ot) {
+                using GT = typename decltype(gt)::type;
+                using OT = typename decltype(ot)::type;
+                if (pl.in_dtype == 2)
+                    hipLaunchKernelGGL((k_bwd_query_mfma<true, GT, OT>), dim3(grid), dim3(kThreads), 0, stream, q16,
+                                       static_cast<const GT*>(dout), state, static_cast<OT*>(dq), gpart, pl.N, pl.H,
+                                       pl.HP, pl.L, pl.NB, bp.tq, bp.tpbq, eps);
+                else
+                    hipLaunchKernelGGL((k_bwd_query_mfma<false, GT, OT>), dim3(grid), dim3(kThreads), 0, stream, q16,
+                                       static_cast<const GT*>(dout), state, static_cast<OT*>(dq), gpart, pl.N, pl.H,
+                                       pl.HP, pl.L, pl.NB, bp.tq, bp.tpbq, eps);
+            });
+        });
+        return hipGetLastError();
+    }
     const unsigned grid = (unsigned)((size_t)pl.B * pl.H * pl.NB * bp.tpbq);
     by_dtype(pl.in_dtype, [&](auto it) {
         by_dtype(bp.dout_dtype, [&](auto gt) {
@@ -217,6 +725,23 @@ hipError_t launch_bwd_merge(const BwdPlan& bp, const float* gpart, float* ghat, 
 hipError_t launch_bwd_key(const BwdPlan& bp, const void* k, const void* v, const float* ghat, void* dk, void* dv,
                           hipStream_t stream) {
     const Plan& pl = bp.fw;
+    if (bp.key_mfma) {
+        const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.NB * bp.tpbk);
+        const uint16_t* k16 = static_cast<const uint16_t*>(k);
+        const uint16_t* v16 = static_cast<const uint16_t*>(v);
+        by_dtype(bp.grad_dtype, [&](auto ot) {
+            using OT = typename decltype(ot)::type;
+            if (pl.in_dtype == 2)
+                hipLaunchKernelGGL((k_bwd_key_mfma<true, OT>), dim3(grid), dim3(kThreads), 0, stream, k16, v16, ghat,
+                                   static_cast<OT*>(dk), static_cast<OT*>(dv), pl.N, pl.H, pl.HP, pl.L, pl.NB,
+                                   bp.tk, bp.tpbk);
+            else
+                hipLaunchKernelGGL((k_bwd_key_mfma<false, OT>), dim3(grid), dim3(kThreads), 0, stream, k16, v16,
+                                   ghat, static_cast<OT*>(dk), static_cast<OT*>(dv), pl.N, pl.H, pl.HP, pl.L, pl.NB,
+                                   bp.tk, bp.tpbk);
+        });
+        return hipGetLastError();
+    }
     const unsigned grid = (unsigned)((size_t)pl.B * pl.H * pl.NB * bp.tpbk);
     by_dtype(pl.in_dtype, [&](auto it) {
         by_dtype(bp.grad_dtype, [&](auto ot) {

@@ -1,0 +1,131 @@
+// Device helpers shared by the forward and backward kernels (gfx950).
+// Included only by the .hip sources; not part of the public ABI.
+#pragma once
+
+#include "linattn_internal.h"
+
+namespace sana {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// ReLU on two packed bf16: for the sign test a bf16 orders like an int16, so
+// max(x, 0) as int16 keeps positives and maps negatives (and -0) to +0.
+__device__ __forceinline__ uint32_t relu_bf16x2(uint32_t x) {
+    s16x2 s = __builtin_bit_cast(s16x2, x);
+    s = __builtin_elementwise_max(s, (s16x2){0, 0});
+    return __builtin_bit_cast(uint32_t, s);
+}
+
+__device__ __forceinline__ u32x4 relu_bf16x8(u32x4 x) {
+    return (u32x4){relu_bf16x2(x[0]), relu_bf16x2(x[1]), relu_bf16x2(x[2]), relu_bf16x2(x[3])};
+}
+
+__device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_f16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// The 16-bit input formats: bf16 (F16 = false) or IEEE binary16 (F16 = true).
+// ReLU on packed values works the same for both: the sign is the top bit.
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma16(u32x4 a, u32x4 b, f32x16 c) {
+    if constexpr (F16)
+        return mfma_f16(a, b, c);
+    else
+        return mfma_bf16(a, b, c);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// Splits two packed finite fp16 values exactly into bf16 terms, x = hi + lo:
+// hi keeps the top 8 significant bits of the fp32 widening (truncation toward
+// zero), and the remainder, of the same sign, has at most the 3 low
+// significant bits of the 11, so it is a bf16 value too.  f0, f1 receive the
+// fp32 values.
+__device__ __forceinline__ void split_f16x2(uint32_t w, uint32_t& hi, uint32_t& lo, float& f0, float& f1) {
+    f0 = f16_to_f32((uint16_t)(w & 0xffffu));
+    f1 = f16_to_f32((uint16_t)(w >> 16));
+    const uint32_t t0 = __builtin_bit_cast(uint32_t, f0) & 0xffff0000u;
+    const uint32_t t1 = __builtin_bit_cast(uint32_t, f1) & 0xffff0000u;
+    const float r0 = f0 - __builtin_bit_cast(float, t0);
+    const float r1 = f1 - __builtin_bit_cast(float, t1);
+    hi = (t0 >> 16) | t1;
+    lo = (__builtin_bit_cast(uint32_t, r0) >> 16) | (__builtin_bit_cast(uint32_t, r1) & 0xffff0000u);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+__device__ __forceinline__ float lo_bf16(uint32_t x) { return __builtin_bit_cast(float, x << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t x) { return __builtin_bit_cast(float, x & 0xffff0000u); }
+
+// Round to nearest, ties to even (finite inputs; NaN is kept a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Element types by ABI code: float (0), bf16 bits in uint16_t (1), _Float16 (2).
+__device__ __forceinline__ float load_in(const float* p, long long i) { return p[i]; }
+__device__ __forceinline__ float load_in(const uint16_t* p, long long i) { return bf16_to_f32(p[i]); }
+__device__ __forceinline__ float load_in(const _Float16* p, long long i) { return (float)p[i]; }
+
+// fp32 -> fp16 conversion rounds to nearest even; outputs lie within the range
+// of V, so they never overflow.
+__device__ __forceinline__ void store_out(float* p, long long i, float x) { p[i] = x; }
+__device__ __forceinline__ void store_out(uint16_t* p, long long i, float x) { p[i] = f32_to_bf16(x); }
+__device__ __forceinline__ void store_out(_Float16* p, long long i, float x) { p[i] = (_Float16)x; }
+
+// Output stores are non-temporal: out is written once and never read here, and
+// streaming it past the caches raises the write bandwidth markedly on gfx950.
+__device__ __forceinline__ void store4(float* p, f32x4 x) {
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
+}
+__device__ __forceinline__ void store4(uint16_t* p, f32x4 x) {
+    const uint32_t lo = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+    __builtin_nontemporal_store((u32x2){lo, hi}, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void store4(_Float16* p, f32x4 x) {
+    const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)x[0]), h1 = __builtin_bit_cast(uint16_t, (_Float16)x[1]);
+    const uint32_t h2 = __builtin_bit_cast(uint16_t, (_Float16)x[2]), h3 = __builtin_bit_cast(uint16_t, (_Float16)x[3]);
+    __builtin_nontemporal_store((u32x2){h0 | (h1 << 16), h2 | (h3 << 16)}, reinterpret_cast<u32x2*>(p));
+}
+
+// Three bf16 terms of an fp32 value, x = t0 + t1 + t2 to about 2^-24 relative:
+// each term is the round-to-nearest bf16 of what the previous ones left, and
+// each remainder is exact in fp32.
+__device__ __forceinline__ void split3_f32(float x, uint16_t t[3]) {
+#pragma unroll
+    for (int sp = 0; sp < 3; ++sp) {
+        t[sp] = f32_to_bf16(x);
+        x -= bf16_to_f32(t[sp]);
+    }
+}
+
+// Packs split terms of 8 consecutive fp32 values into three bf16x8 operands.
+__device__ __forceinline__ void split3_f32x8(const float* x, u32x4 out[3]) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        uint16_t a[3], b[3];
+        split3_f32(x[2 * d], a);
+        split3_f32(x[2 * d + 1], b);
+#pragma unroll
+        for (int sp = 0; sp < 3; ++sp) out[sp][d] = (uint32_t)a[sp] | ((uint32_t)b[sp] << 16);
+    }
+}
+
+}  // namespace sana

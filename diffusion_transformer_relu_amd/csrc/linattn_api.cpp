@@ -214,9 +214,10 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
     const Plan& pl = bp->fw;
     bp->key_mfma = bp->query_mfma = pl.mfma;
     if (pl.mfma) {
-        // about one round of work-groups (head pairs x tiles), tiles of 64 tokens
+        // about one round of work-groups (head pairs x tiles; 3 per CU fit the
+        // key kernel's registers and LDS), tiles of 64 tokens
         const long units = (long)B * pl.HP * pl.NB;
-        const long per_block = std::max<long>(1, sana::kApplyGroups * 4 / 5 / units);
+        const long per_block = std::max<long>(1, sana::kCUs * 3 / units);
         bp->tk = bp->tq = (int)std::min<long>(round_up(ceil_div(pl.L, per_block), 64), round_up(pl.L, 64));
     } else {
         bp->tk = bp->tq = kBwdTile;

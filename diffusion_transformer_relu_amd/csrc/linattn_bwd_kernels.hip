@@ -275,106 +275,136 @@ __device__ __forceinline__ void mma_split_lds(const OperandLds& o, int hh, int l
     acc = f16 ? mma_split<true>(A, b0, b1, acc) : mma_split<false>(A, b0, b1, acc);
 }
 
+// ------------------------------------------------------------------ input tiles through LDS
+// Two [B][N][H][D] 16-bit tensors, 64 tokens x 2 heads per tile, staged
+// through LDS by the whole work-group (the state kernel's scheme): the next
+// tile's global loads are issued into registers before the current tile is
+// worked on, so their latency is covered by a whole tile of work.  LDS layout
+// [tensor][head][token][32 x 16 bit]; the second head's rows are shifted by 64
+// bytes so that both heads' 16-byte writes of one token use different banks.
+constexpr int kTileTok = 64;
+constexpr int kTileHead = kTileTok * 64 + 64;   // bytes per head
+constexpr int kTileTensor = 2 * kTileHead;      // bytes per tensor
+
+struct TileLoader {
+    const uint16_t* x[2];   // the two tensors (the second may be null: one tensor only)
+    long long hstride;      // elements per token row (H * D)
+    int b, N, h0, nh, t1;
+    u32x4 r[2][2];          // [tensor][piece]: this thread's 2 pieces of 16 bytes
+
+    // piece p (0..511) of a tile: part (p & 3), head ((p >> 2) & 1), token p >> 3.
+    // A missing head reads as zero.  Tokens past t1 read as the row t1 - 1:
+    // their per-token results equal that row's (store_tile relies on it), and
+    // code that sums over tokens must skip them.
+    __device__ __forceinline__ void load(int t0) {
+#pragma unroll
+        for (int pi = 0; pi < 2; ++pi) {
+            const int pc = threadIdx.x + kThreads * pi;
+            const int part = pc & 3, hd = (pc >> 2) & 1, tok = pc >> 3;
+            const int n = min(t0 + tok, t1 - 1);
+            const bool ok = hd < nh;
+            const long long off = ((long long)b * N + n) * hstride + (h0 + (ok ? hd : 0)) * kD + part * 8;
+#pragma unroll
+            for (int ts = 0; ts < 2; ++ts) {
+                if (ts == 1 && !x[1]) break;
+                const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x[ts] + off));
+                r[ts][pi] = ok ? v : (u32x4){0u, 0u, 0u, 0u};
+            }
+        }
+    }
+    __device__ __forceinline__ void store(uint8_t* lds) const {
+#pragma unroll
+        for (int pi = 0; pi < 2; ++pi) {
+            const int pc = threadIdx.x + kThreads * pi;
+            const int part = pc & 3, hd = (pc >> 2) & 1, tok = pc >> 3;
+            const int o = hd * kTileHead + tok * 64 + part * 16;
+#pragma unroll
+            for (int ts = 0; ts < 2; ++ts) {
+                if (ts == 1 && !x[1]) break;
+                *reinterpret_cast<u32x4*>(lds + ts * kTileTensor + o) = r[ts][pi];
+            }
+        }
+    }
+};
+
+// B operand of token `tok` of a staged tile: lane (g, i) gets features 8g..8g+7
+// and 16+8g..16+8g+7 of tensor ts, head hh.
+__device__ __forceinline__ void tile_operand(const uint8_t* lds, int ts, int hh, int tok, int g, u32x4& x0,
+                                             u32x4& x1) {
+    const uint8_t* row = lds + ts * kTileTensor + hh * kTileHead + tok * 64 + 16 * g;
+    x0 = *reinterpret_cast<const u32x4*>(row);
+    x1 = *reinterpret_cast<const u32x4*>(row + 32);
+}
+
 // ------------------------------------------------------------------ key pass, matrix cores
-// grid.x = (b * HP + hp) * (NB * tpb) + beta * tpb + tile.  Wave w handles head
-// 2*hp + (w & 1) and every other 32-key sub-tile (w >> 1) of the work-group's
-// range, which never crosses a block.  Per sub-tile, with a = ReLU(k):
-//   dv^T = Ghat_v^T a^T          (A = Ghat transposed, B = a straight from HBM)
-//   da^T = Ghat_v v^T + Ghat_z   (A = Ghat natural,    B = v straight from HBM)
+// grid.x = (b * HP + hp) * (NB * tpb) + beta * tpb + tile.  The work-group
+// stages 64-key tiles of k and v (both heads) through LDS; wave w then handles
+// head 2*hp + (w & 1) and keys 32 (w >> 1) .. + 31 of the tile.  With
+// a = ReLU(k):
+//   dv^T = Ghat_v^T a^T          (A = Ghat transposed, B = a)
+//   da^T = Ghat_v v^T + Ghat_z   (A = Ghat natural,    B = v)
 //   dk   = da masked by k > 0
 template <bool F16, typename OutT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_bwd_key_mfma(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_bwd_key_mfma(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ ghat,
     OutT* __restrict__ dk, OutT* __restrict__ dv, int N, int H, int HP, int L, int NB, int tile, int tpb) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kTileTensor];
     __shared__ __attribute__((aligned(16))) float otile[4][32 * kPitch];
-    __shared__ OperandLds opnd;
-    __shared__ __attribute__((aligned(16))) float gzs[2][32];   // Ghat[:, D] of each head
 
     const int per_unit = NB * tpb;
     const int tau = blockIdx.x % per_unit;
     const int bhp = blockIdx.x / per_unit;
     const int hp = bhp % HP, b = bhp / HP;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int hh = wave & 1, h = 2 * hp + hh;
+    const int hh = wave & 1, th = wave >> 1, h = 2 * hp + hh;
     const int beta = tau / tpb, tib = tau - beta * tpb;
     const int blk0 = beta * L, blk1 = min(blk0 + L, N);
     const int t0 = blk0 + tib * tile, t1 = min(t0 + tile, blk1);
     const int g = lane >> 5, i = lane & 31;
+    const int nh = min(2, H - 2 * hp);
+    if (t0 >= t1) return;   // uniform over the work-group
 
-    // waves 0 and 1 build the operands of heads 0 and 1; every wave reaches the barrier
-    if (wave < 2 && h < H) {
-        const float* G = ghat + (((size_t)b * H + h) * NB + beta) * kStateFloats;
-        u32x4 t[2][3];
-        state_operands(G, lane, true, t);
+    // this wave's head: Ghat as split-term operands in both layouts, Ghat[:, D]
+    const int hs = min(h, H - 1);   // a missing second head computes on the first (never stored)
+    const float* G = ghat + (((size_t)b * H + hs) * NB + beta) * kStateFloats;
+    u32x4 gt[2][3], gn[2][3];
+    state_operands(G, lane, true, gt);
+    state_operands(G, lane, false, gn);
+    float gz[16];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int sp = 0; sp < 3; ++sp) opnd.v[hh][0][ks][sp][lane] = t[ks][sp];
-        state_operands(G, lane, false, t);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int sp = 0; sp < 3; ++sp) opnd.v[hh][1][ks][sp][lane] = t[ks][sp];
-        if (lane < 32) gzs[hh][lane] = G[lane * kW + kD];
-    }
-    __syncthreads();
-    if (h >= H || t0 >= t1) return;
+    for (int r = 0; r < 16; ++r) gz[r] = G[(8 * (r >> 2) + 4 * g + (r & 3)) * kW + kD];
 
     const long long hstride = (long long)H * kD;
-    // Rows past the range are clamped to its last row rather than skipped:
-    // every load is unconditional, so the compiler can count the loads in
-    // flight exactly and the prefetch overlaps the work.  A clamped row only
-    // feeds its own output column, which is never stored.
-    auto load_b = [&](const uint16_t* base, int tt, u32x4& x0, u32x4& x1) {
-        const int row = min(tt + i, t1 - 1);
-        const u32x4* src = reinterpret_cast<const u32x4*>(base + ((long long)b * N + row) * hstride + h * kD + 8 * g);
-        x0 = __builtin_nontemporal_load(src);
-        x1 = __builtin_nontemporal_load(src + 2);
-    };
+    TileLoader ld = {{k, v}, hstride, b, N, 2 * hp, nh, t1, {}};
     float* ot = otile[wave];
-    // One 32-key sub-tile: x = {k features 8g.., k 16+8g.., v 8g.., v 16+8g..}.
-    auto body = [&](int tt, const u32x4 (&x)[4]) {
-        // keep the LDS operands in LDS: without this the loads are hoisted out
-        // of the loop and the registers they take cut the occupancy
-        asm volatile("" ::: "memory");
-        const u32x4 a0 = relu_bf16x8(x[0]), a1 = relu_bf16x8(x[1]);
-        const uint32_t mask = nonzero_mask(a0, a1, g);
+    ld.load(t0);
+    for (int tt0 = t0; tt0 < t1; tt0 += kTileTok) {
+        __syncthreads();   // the previous tile has been consumed
+        ld.store(lds);
+        __syncthreads();
+        if (tt0 + kTileTok < t1) ld.load(tt0 + kTileTok);   // in flight during this tile's work
+
+        const int tt = tt0 + 32 * th;   // first key of this wave's half
         const int n = min(32, t1 - tt);
+        if (n <= 0 || h >= H) continue;
+        u32x4 k0, k1, v0, v1;
+        tile_operand(lds, 0, hh, 32 * th + i, g, k0, k1);
+        tile_operand(lds, 1, hh, 32 * th + i, g, v0, v1);
+        const u32x4 a0 = relu_bf16x8(k0), a1 = relu_bf16x8(k1);
+        const uint32_t mask = nonzero_mask(a0, a1, g);
 
         f32x16 acc = {};
-        mma_split_lds(opnd, hh, 0, lane, a0, a1, acc, F16);
+        acc = mma_split<F16>(gt, a0, a1, acc);
         store_tile<OutT>(ot, acc, lane, n, [&](int t) { return dv + ((long long)b * N + tt + t) * hstride + h * kD; });
 
         acc = (f32x16){};
-        mma_split_lds(opnd, hh, 1, lane, x[2], x[3], acc, F16);
+        acc = mma_split<F16>(gn, v0, v1, acc);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const f32x4 z = *reinterpret_cast<const f32x4*>(&gzs[hh][8 * rr + 4 * g]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * rr + e, j = 8 * rr + 4 * g + e;
-                acc[r] = ((mask >> j) & 1u) ? acc[r] + z[e] : 0.f;
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int j = 8 * (r >> 2) + 4 * g + (r & 3);
+            acc[r] = ((mask >> j) & 1u) ? acc[r] + gz[r] : 0.f;
         }
         store_tile<OutT>(ot, acc, lane, n, [&](int t) { return dk + ((long long)b * N + tt + t) * hstride + h * kD; });
-    };
-    auto load = [&](int tt, u32x4 (&x)[4]) {
-        load_b(k, tt, x[0], x[1]);
-        load_b(v, tt, x[2], x[3]);
-    };
-    // two register sets alternate (no copies between them), so the next
-    // sub-tile's loads are in flight during the current one's work
-    u32x4 xa[4], xb[4];
-    int tt = t0 + 32 * (wave >> 1);
-    load(tt, xa);
-    while (tt < t1) {
-        load(tt + 64, xb);
-        body(tt, xa);
-        tt += 64;
-        if (tt >= t1) break;
-        load(tt + 64, xa);
-        body(tt, xb);
-        tt += 64;
     }
 }
 
@@ -384,6 +414,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
 template <typename GT> struct GradRow;
 template <> struct GradRow<float> {
     f32x4 x[4];
+    __device__ __forceinline__ void load_lds(const uint8_t*, int) {}   // fp32 rows are not staged
     __device__ __forceinline__ void load(const float* row, int g) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) x[rr] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 8 * rr + 4 * g));
@@ -392,6 +423,11 @@ template <> struct GradRow<float> {
 };
 template <> struct GradRow<uint16_t> {
     u32x2 x[4];
+    // from a staged LDS row of 32 x 16 bit
+    __device__ __forceinline__ void load_lds(const uint8_t* row, int g) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) x[rr] = *reinterpret_cast<const u32x2*>(row + 16 * rr + 8 * g);
+    }
     __device__ __forceinline__ void load(const uint16_t* row, int g) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) x[rr] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(row + 8 * rr + 4 * g));
@@ -403,6 +439,10 @@ template <> struct GradRow<uint16_t> {
 };
 template <> struct GradRow<_Float16> {
     u32x2 x[4];
+    __device__ __forceinline__ void load_lds(const uint8_t* row, int g) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) x[rr] = *reinterpret_cast<const u32x2*>(row + 16 * rr + 8 * g);
+    }
     __device__ __forceinline__ void load(const _Float16* row, int g) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) x[rr] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(row + 8 * rr + 4 * g));
@@ -420,8 +460,9 @@ template <> struct GradRow<_Float16> {
 //   fp32; r = 1 / (den + eps); u = dout r; w = -r (dout . num r)
 //   dq^T = P_v u^T + P[:, D] w, masked by q > 0 (A = P natural, B = u as three
 //   bf16 terms read back from the wave's LDS tile; terms below 2^-24 dropped)
-//   G += f^T [u | w]  (tokens are the reduction dimension: f and u gathered
-//   from the LDS tiles, u and w split into three bf16 terms)
+//   G_v += f^T u  (tokens are the reduction dimension: f and u gathered from
+//   the LDS tiles, u split exactly into three bf16 terms by truncation)
+//   G_z += f^T w  (an fp32 dot product per lane on the vector unit)
 // The two waves of a head then add their G in a fixed order and write the
 // tile's partial gradient state.
 template <bool F16, typename GT, typename OutT>
@@ -434,6 +475,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
     __shared__ __attribute__((aligned(16))) float ut[4][32 * kPitch];   // u tile, then the dq tile
     __shared__ __attribute__((aligned(16))) uint16_t ft[4][32 * 32];    // f tile (16-bit bits)
     __shared__ float wv[4][32];                                     // w of each token
+    __shared__ __attribute__((aligned(16))) uint8_t lds_in[2 * kTileTensor];   // staged q (and 16-bit dout)
 
     const int per_unit = NB * tpb;
     const int tau = blockIdx.x % per_unit;
@@ -468,23 +510,14 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
     float* ot = ut[wave];
     uint16_t* fw = ft[wave];
     float* wl = wv[wave];
-    f32x16 accG = {}, accGz = {};
+    f32x16 accG = {};
+    float gz_acc = 0.f;   // lane (g, j): sum over this lane's tokens of f_j w
 
     struct Tile {
         u32x4 q0, q1;
         GradRow<GT> gr;
     };
-    // rows past the range are clamped to its last row: their dq columns then
-    // equal that row's (store_tile relies on it), and the gathers for G skip
-    // them
-    auto load = [&](int tt, Tile& x) {
-        const int row = min(tt + i, t1 - 1);
-        const uint16_t* qr = q + ((long long)b * N + row) * hstride + h * kD;
-        const u32x4* src = reinterpret_cast<const u32x4*>(qr + 8 * g);
-        x.q0 = __builtin_nontemporal_load(src);
-        x.q1 = __builtin_nontemporal_load(src + 2);
-        x.gr.load(dout + ((long long)b * N + row) * hstride + h * kD, g);
-    };
+    constexpr bool kStageDout = sizeof(GT) == 2;   // 16-bit dout is staged with q; fp32 dout is read per wave
     auto body = [&](int tt, const Tile& x) {
         asm volatile("" ::: "memory");   // keep the LDS operands in LDS (see the key kernel)
         const int n = min(32, t1 - tt);
@@ -534,27 +567,32 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
         }
         if (g == 0) wl[i] = w;
         __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");   // phase boundary: keeps each phase's LDS reads in its phase
 
         // G += f^T [u | w]: lane (g, c) gathers tokens 16 ks + 8 g + e
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             float uu[8], ww[8];
             u32x4 af;
+            // unconditional reads from one base per lane (immediate offsets),
+            // then tokens past the range are zeroed
+            const float* ob = ot + (16 * ks + 8 * g) * kPitch + i;
+            const float* wb = wl + 16 * ks + 8 * g;
+            const uint16_t* fb = fw + (16 * ks + 8 * g) * 32 + i;
+            const int nv = n - (16 * ks + 8 * g);   // valid tokens among this lane's 8
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int tok = 16 * ks + 8 * g + e;
-                uu[e] = tok < n ? ot[tok * kPitch + i] : 0.f;
-                ww[e] = tok < n ? wl[tok] : 0.f;
+                const float uv = ob[e * kPitch], wvv = wb[e];
+                uu[e] = e < nv ? uv : 0.f;
+                ww[e] = e < nv ? wvv : 0.f;
             }
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                const int tok = 16 * ks + 8 * g + 2 * d;
-                const uint32_t lo = tok < n ? fw[tok * 32 + i] : 0u, hi = tok + 1 < n ? fw[(tok + 1) * 32 + i] : 0u;
-                af[d] = lo | (hi << 16);
+                const uint32_t lo = fb[(2 * d) * 32], hi = fb[(2 * d + 1) * 32];
+                af[d] = (2 * d < nv ? lo : 0u) | ((2 * d + 1 < nv ? hi : 0u) << 16);
             }
-            u32x4 bu[3], bw[3];
-            split3_f32x8(uu, bu);
-            split3_f32x8(ww, bw);
+            u32x4 bu[3];
+            split3_trunc_f32x8(uu, bu);
             if constexpr (F16) {
                 u32x4 fhi, flo;
 #pragma unroll
@@ -564,26 +602,25 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
                     split_f16x2(af[d], hv, lv, f0_, f1_);
                     fhi[d] = hv;
                     flo[d] = lv;
+                    gz_acc = fmaf(f0_, ww[2 * d], gz_acc);
+                    gz_acc = fmaf(f1_, ww[2 * d + 1], gz_acc);
                 }
 #pragma unroll
-                for (int sp = 2; sp >= 0; --sp) {
-                    accG = mfma_bf16(flo, bu[sp], accG);
-                    accGz = mfma_bf16(flo, bw[sp], accGz);
-                }
+                for (int sp = 2; sp >= 0; --sp) accG = mfma_bf16(flo, bu[sp], accG);
 #pragma unroll
-                for (int sp = 2; sp >= 0; --sp) {
-                    accG = mfma_bf16(fhi, bu[sp], accG);
-                    accGz = mfma_bf16(fhi, bw[sp], accGz);
-                }
+                for (int sp = 2; sp >= 0; --sp) accG = mfma_bf16(fhi, bu[sp], accG);
             } else {
 #pragma unroll
-                for (int sp = 2; sp >= 0; --sp) {
-                    accG = mfma_bf16(af, bu[sp], accG);
-                    accGz = mfma_bf16(af, bw[sp], accGz);
+                for (int d = 0; d < 4; ++d) {
+                    gz_acc = fmaf(lo_bf16(af[d]), ww[2 * d], gz_acc);
+                    gz_acc = fmaf(hi_bf16(af[d]), ww[2 * d + 1], gz_acc);
                 }
+#pragma unroll
+                for (int sp = 2; sp >= 0; --sp) accG = mfma_bf16(af, bu[sp], accG);
             }
         }
 
+        asm volatile("" ::: "memory");
         // dq^T = P_v u^T (+ P[:, D] w), B = u in the operand layout from the tile
         u32x4 ub[2][3];
 #pragma unroll
@@ -596,7 +633,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
                 uu[e] = a4[e];
                 uu[4 + e] = b4[e];
             }
-            split3_f32x8(uu, ub[ks]);
+            split3_trunc_f32x8(uu, ub[ks]);
         }
         __builtin_amdgcn_wave_barrier();
         acc = (f32x16){};
@@ -625,31 +662,40 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
         store_tile<OutT>(ot, acc, lane, n, [&](int t) { return dq + ((long long)b * N + tt + t) * hstride + h * kD; });
     };
 
-    if (active) {
-        Tile xa, xb;
-        int tt = t0 + 32 * (wave >> 1);
-        if (tt < t1) load(tt, xa);
-        while (tt < t1) {
-            if (tt + 64 < t1) load(tt + 64, xb);
-            body(tt, xa);
-            tt += 64;
-            if (tt >= t1) break;
-            if (tt + 64 < t1) load(tt + 64, xa);
-            body(tt, xb);
-            tt += 64;
+    if (t0 < t1) {   // uniform over the work-group
+        const uint16_t* dsrc = kStageDout ? reinterpret_cast<const uint16_t*>(dout) : nullptr;
+        TileLoader ld = {{q, dsrc}, hstride, b, N, 2 * hp, min(2, H - 2 * hp), t1, {}};
+        ld.load(t0);
+        for (int tt0 = t0; tt0 < t1; tt0 += kTileTok) {
+            __syncthreads();   // the previous tile has been consumed
+            ld.store(lds_in);
+            __syncthreads();
+            if (tt0 + kTileTok < t1) ld.load(tt0 + kTileTok);   // in flight during this tile's work
+            const int tt = tt0 + 32 * (wave >> 1);
+            if (!active || tt >= t1) continue;
+            Tile x;
+            tile_operand(lds_in, 0, hh, 32 * (wave >> 1) + i, g, x.q0, x.q1);
+            if constexpr (kStageDout) {
+                x.gr.load_lds(lds_in + kTileTensor + hh * kTileHead + (32 * (wave >> 1) + i) * 64, g);
+            } else {
+                const int row = min(tt + i, t1 - 1);
+                x.gr.load(dout + ((long long)b * N + row) * hstride + h * kD, g);
+            }
+            body(tt, x);
         }
     }
 
     // the two waves of a head add their G in a fixed order; the LDS operands
     // are no longer needed, so their space holds the second wave's G
     __syncthreads();
-    float* red = reinterpret_cast<float*>(&opnd);   // [head][G | Gz][16][64]
+    // G_z of lane j: the sum of its two token halves (the same in both lanes:
+    // fp32 addition commutes)
+    const float gz = gz_acc + __shfl_xor(gz_acc, 32);
+    float* red = reinterpret_cast<float*>(&opnd);   // [head][16][64] G, then [head][32] G_z
     if (wave >= 2) {
 #pragma unroll
-        for (int rg = 0; rg < 16; ++rg) {
-            red[((hh * 2 + 0) * 16 + rg) * 64 + lane] = accG[rg];
-            red[((hh * 2 + 1) * 16 + rg) * 64 + lane] = accGz[rg];
-        }
+        for (int rg = 0; rg < 16; ++rg) red[(hh * 16 + rg) * 64 + lane] = accG[rg];
+        if (lane < 32) red[2 * 16 * 64 + hh * 32 + lane] = gz;
     }
     __syncthreads();
     if (wave < 2 && h < H) {
@@ -657,13 +703,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
 #pragma unroll
         for (int rg = 0; rg < 16; ++rg) {
             const int j = 8 * (rg >> 2) + 4 * g + (rg & 3);
-            dst[j * kW + i] = accG[rg] + red[((hh * 2 + 0) * 16 + rg) * 64 + lane];
-            if (i == 0) dst[j * kW + kD] = accGz[rg] + red[((hh * 2 + 1) * 16 + rg) * 64 + lane];
+            dst[j * kW + i] = accG[rg] + red[(hh * 16 + rg) * 64 + lane];
         }
+        if (lane < 32) dst[lane * kW + kD] = gz + red[2 * 16 * 64 + hh * 32 + lane];
     }
 }
 
-static_assert(sizeof(OperandLds) >= 2 * 2 * 16 * 64 * sizeof(float), "G reduction area exceeds the operand space");
+static_assert(sizeof(OperandLds) >= (2 * 16 * 64 + 2 * 32) * sizeof(float), "G reduction area exceeds the operand space");
 
 template <typename T> struct Tag { using type = T; };
 template <typename F> void by_dtype(int code, F&& f) {

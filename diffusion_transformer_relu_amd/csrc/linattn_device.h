@@ -70,13 +70,8 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 __device__ __forceinline__ float lo_bf16(uint32_t x) { return __builtin_bit_cast(float, x << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t x) { return __builtin_bit_cast(float, x & 0xffff0000u); }
 
-// Round to nearest, ties to even (finite inputs; NaN is kept a quiet NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
+// Round to nearest, ties to even: gfx950's v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // Element types by ABI code: float (0), bf16 bits in uint16_t (1), _Float16 (2).
 __device__ __forceinline__ float load_in(const float* p, long long i) { return p[i]; }

@@ -282,3 +282,16 @@ def test_f16_extreme_magnitudes(k_scale, v_scale):
     for out_dtype, kind in ((torch.float32, False), (torch.float16, "f16")):
         got = run_hip(q, k, v, out_dtype=out_dtype)
         compare(got, want, v, kind, f"k{k_scale}_v{v_scale}/{kind}")
+
+
+@pytest.mark.parametrize("in_dt", [workloads.DT_BF16, workloads.DT_F16])
+def test_16bit_out_is_the_fp32_out_rounded_to_nearest_even(in_dt):
+    """The bf16 and fp16 outputs are the fp32 output rounded once to nearest
+    even (torch's conversion on the host), bit for bit."""
+    w = workloads.Workload("round_B2_N3000_H5", 2, 3000, 5, 32, in_dt, seed=47, v_scale=3.0)
+    q, k, v = (to_device(x) for x in workloads.make_inputs(w))
+    import diffusion_transformer_relu_amd as sana
+    f32 = sana.linattn_fwd(q, k, v, out_dtype=torch.float32).cpu()
+    for t in (torch.bfloat16, torch.float16):
+        got = sana.linattn_fwd(q, k, v, out_dtype=t).cpu()
+        assert torch.equal(got.view(torch.int16), f32.to(t).view(torch.int16)), t

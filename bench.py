@@ -142,14 +142,41 @@ def short_kernel_name(name: str) -> str:
 
 
 def summarize_trace(stats_csv: str) -> int:
-    """Markdown table of a rocprofv3 --kernel-trace --stats run_kernel_stats.csv."""
+    """Markdown table of a rocprofv3 --kernel-trace --stats run_kernel_stats.csv;
+    with the run_kernel_trace.csv beside it, also each kernel's longest run of
+    back-to-back launches (the per-kernel loop this script times with HIP
+    events) and the whole forwards (state, merge, apply in sequence)."""
     import csv
+    import statistics
     rows = list(csv.DictReader(open(stats_csv)))
     print("| kernel | calls | avg µs | min µs | max µs | share % |")
     print("|---|---|---|---|---|---|")
     for r in rows:
         print(f"| `{short_kernel_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
               f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    trace_csv = os.path.join(os.path.dirname(stats_csv), os.path.basename(stats_csv).replace("kernel_stats",
+                                                                                             "kernel_trace"))
+    if not os.path.exists(trace_csv):
+        return 0
+    ev = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), short_kernel_name(r["Kernel_Name"]))
+                for r in csv.DictReader(open(trace_csv)))
+    runs = {}
+    i = 0
+    while i < len(ev):
+        j = i
+        while j + 1 < len(ev) and ev[j + 1][2] == ev[i][2]:
+            j += 1
+        if j - i + 1 > len(runs.get(ev[i][2], [])):
+            runs[ev[i][2]] = [(e - s) / 1e3 for s, e, _ in ev[i:j + 1]]
+        i = j + 1
+    print()
+    print("Longest run of back-to-back launches of each kernel:")
+    print()
+    print("| kernel | launches | mean µs | median µs |")
+    print("|---|---|---|---|")
+    for name, d in sorted(runs.items(), key=lambda kv: -len(kv[1])):
+        if len(d) >= 10:
+            print(f"| `{name}` | {len(d)} | {statistics.mean(d):.2f} | {statistics.median(d):.2f} |")
     return 0
 
 
@@ -353,6 +380,24 @@ def main() -> int:
             "pct_hbm_peak": round(100 * alg_bytes / ms / 1e6 / HBM_PEAK_GBPS, 2),
             "note": "the headline inputs converted to fp16 on the device"}
         del sets16
+
+        # backward (dq, dk, dv) of the same forward: bf16 q, k, v, dout -> bf16 gradients
+        grads = [[torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+                 for _ in range(NSETS)]
+        ws_bw = torch.empty(sana.sana_linattn_bwd_workspace_bytes(B, H, N, D, 0), dtype=torch.uint8, device=dev)
+
+        def bwd(i):
+            q, k, v = sets[i % NSETS]
+            dq, dk, dv = grads[i % NSETS]
+            sana.sana_linattn_bwd(q, k, v, sets[(i + 1) % NSETS][0], dq, dk, dv, ws_bw, eps=w.eps, stream=stream)
+        ms = timed(bwd, args.steps)
+        bw_bytes = w.token_heads * D * 2 * 7    # read q, k, v, dout; write dq, dk, dv (bf16)
+        extra["backward_bf16"] = {
+            "ms_per_step": round(ms, 5), "GBps": round(bw_bytes / ms / 1e6, 1),
+            "pct_hbm_peak": round(100 * bw_bytes / ms / 1e6 / HBM_PEAK_GBPS, 2),
+            "note": "sana_linattn_bwd, bf16 q/k/v/dout/gradients; dout is another input set; "
+                    "algorithmic bytes = 7 tensors"}
+        del grads, ws_bw
 
     line = {
         "metric": METRIC,

@@ -6,6 +6,7 @@ CPU-baseline leg of the benchmark.  The HIP product path never imports it.
 * ``linattn_fwd``  -- the linear (state) form in C, fp64, OpenMP over (b, h);
   see ``linattn_oracle.c`` for the definition and the pages it follows.
 * ``linattn_bwd``  -- its gradients (dq, dk, dv) in C, fp64, same structure.
+* ``linattn_jvp``  -- its forward-mode derivative (out, d out) in C, fp64.
 * ``brute``        -- the quadratic form in numpy (its pin).
 * ``exact``        -- the quadratic form in exact rational arithmetic (tiny sizes).
 """
@@ -43,6 +44,11 @@ def _load():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_linattn_jvp.restype = ctypes.c_int
+        lib.oracle_linattn_jvp.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.oracle_decode.restype = ctypes.c_int
         lib.oracle_decode.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p]
         _lib = lib
@@ -134,3 +140,21 @@ def linattn_bwd(q, k, v, dout, *, block_len: int | None = None, eps: float = 1e-
     if rc != 0:
         raise RuntimeError(f"oracle_linattn_bwd failed ({rc})")
     return dq, dk, dv
+
+
+def linattn_jvp(q, k, v, qt, kt, vt, *, block_len: int | None = None, eps: float = 1e-15, nthreads: int = 0):
+    """fp64 (out, tangent of out) of the LiteLA forward at (q, k, v) along the
+    tangents (qt, kt, vt), which share the inputs' dtype and shape."""
+    arrs = [np.ascontiguousarray(x) for x in (q, k, v, qt, kt, vt)]
+    if any(a.shape != arrs[0].shape for a in arrs) or arrs[0].ndim != 4:
+        raise ValueError("q, k, v and the tangents must share one [B, N, H, D] shape")
+    code = _dtype_code(arrs[0])
+    if any(_dtype_code(a) != code for a in arrs):
+        raise TypeError("q, k, v and the tangents must share one dtype")
+    B, N, H, D = arrs[0].shape
+    out, outt = (np.empty((B, N, H, D), dtype=np.float64) for _ in range(2))
+    rc = _load().oracle_linattn_jvp(*[a.ctypes.data for a in arrs], code, B, H, N, D, int(block_len or 0),
+                                    float(eps), out.ctypes.data, outt.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_linattn_jvp failed ({rc})")
+    return out, outt

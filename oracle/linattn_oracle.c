@@ -302,6 +302,112 @@ int oracle_linattn_bwd(const void* q, const void* k, const void* v, const void* 
     return failed ? -1 : 0;
 }
 
+/*
+ * Forward-mode derivative (JVP) of the same operator (test infrastructure).
+ *
+ * Given tangents qt, kt, vt of q, k, v, with f = phi(q), a_n = phi(k_n) and
+ * the derivative of ReLU taken as [x > 0]:
+ *   ft   = [q > 0] * qt,   at_n = [k_n > 0] * kt_n
+ *   S    = sum_n a_n [v_n | 1]^T                 (prefix over blocks when causal)
+ *   St   = sum_n (at_n [v_n | 1]^T + a_n [vt_n | 0]^T)
+ *   num  = S[:, :D]^T f,   den  = S[:, D] . f
+ *   numt = St[:, :D]^T f + S[:, :D]^T ft,   dent = St[:, D] . f + S[:, D] . ft
+ *   out  = num / (den + eps),   outt = (numt - out * dent) / (den + eps)
+ * Tangents have the inputs' dtype code.  out and outt: [B][N][H][D] doubles.
+ * Returns 0, or -1 on bad arguments.
+ */
+int oracle_linattn_jvp(const void* q, const void* k, const void* v, const void* qt, const void* kt,
+                       const void* vt, int in_dtype, int B, int H, int N, int D, int block_len, double eps,
+                       double* out, double* outt, int nthreads) {
+    if (B < 0 || H < 0 || N < 0 || D < 1) return -1;
+    if (in_dtype != ORACLE_F32 && in_dtype != ORACLE_BF16 && in_dtype != ORACLE_F16) return -1;
+    if (B == 0 || H == 0 || N == 0) return 0;
+    if (!q || !k || !v || !qt || !kt || !vt || !out || !outt) return -1;
+    const int L = (block_len <= 0 || block_len >= N) ? N : block_len;
+    const int NB = (N + L - 1) / L;
+    const int W = D + 1;
+
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* S = (double*)malloc(sizeof(double) * (size_t)D * W);
+        double* St = (double*)malloc(sizeof(double) * (size_t)D * W);
+        double* a = (double*)malloc(sizeof(double) * (size_t)D);
+        double* at = (double*)malloc(sizeof(double) * (size_t)D);
+        double* x = (double*)malloc(sizeof(double) * (size_t)D);
+        double* xt = (double*)malloc(sizeof(double) * (size_t)D);
+        if (!S || !St || !a || !at || !x || !xt) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long bh = 0; bh < (long)B * H; ++bh) {
+                const int b = (int)(bh / H), h = (int)(bh % H);
+                memset(S, 0, sizeof(double) * (size_t)D * W);
+                memset(St, 0, sizeof(double) * (size_t)D * W);
+                for (int beta = 0; beta < NB; ++beta) {
+                    const int n0 = beta * L;
+                    const int n1 = (n0 + L < N) ? n0 + L : N;
+                    for (int n = n0; n < n1; ++n) {   /* this block's keys into S and St */
+                        const size_t row = (((size_t)b * N + n) * H + h) * (size_t)D;
+                        for (int j = 0; j < D; ++j) {
+                            const double kk = load_elem(k, in_dtype, row + j);
+                            a[j] = relu(kk);
+                            at[j] = kk > 0.0 ? load_elem(kt, in_dtype, row + j) : 0.0;
+                            x[j] = load_elem(v, in_dtype, row + j);
+                            xt[j] = load_elem(vt, in_dtype, row + j);
+                        }
+                        for (int j = 0; j < D; ++j) {
+                            for (int c = 0; c < D; ++c) {
+                                S[j * W + c] += a[j] * x[c];
+                                St[j * W + c] += at[j] * x[c] + a[j] * xt[c];
+                            }
+                            S[j * W + D] += a[j];
+                            St[j * W + D] += at[j];
+                        }
+                    }
+                    for (int i = n0; i < n1; ++i) {   /* this block's queries */
+                        const size_t row = (((size_t)b * N + i) * H + h) * (size_t)D;
+                        for (int j = 0; j < D; ++j) {
+                            const double qq = load_elem(q, in_dtype, row + j);
+                            a[j] = relu(qq);                                           /* f */
+                            at[j] = qq > 0.0 ? load_elem(qt, in_dtype, row + j) : 0.0;   /* ft */
+                        }
+                        double den = 0.0, dent = 0.0;
+                        for (int j = 0; j < D; ++j) {
+                            den += a[j] * S[j * W + D];
+                            dent += St[j * W + D] * a[j] + S[j * W + D] * at[j];
+                        }
+                        for (int c = 0; c < D; ++c) {
+                            double num = 0.0, numt = 0.0;
+                            for (int j = 0; j < D; ++j) {
+                                num += a[j] * S[j * W + c];
+                                numt += St[j * W + c] * a[j] + S[j * W + c] * at[j];
+                            }
+                            const double o = num / (den + eps);
+                            out[row + c] = o;
+                            outt[row + c] = (numt - o * dent) / (den + eps);
+                        }
+                    }
+                }
+            }
+        }
+        free(S);
+        free(St);
+        free(a);
+        free(at);
+        free(x);
+        free(xt);
+    }
+    return failed ? -1 : 0;
+}
+
 /* Number of threads an OpenMP parallel region would use right now. */
 int oracle_max_threads(void) {
 #ifdef _OPENMP

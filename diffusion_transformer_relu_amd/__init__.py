@@ -50,6 +50,9 @@ _SIGNATURES = {
     "sana_linattn_fwd_stages": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P,
                                      ctypes.c_size_t, _P, _I]),
     "sana_linattn_bwd_workspace_bytes": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]),
+    "sana_linattn_jvp_workspace_bytes": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]),
+    "sana_linattn_jvp": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P,
+                              ctypes.c_size_t, _P]),
     "sana_linattn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P,
                               ctypes.c_size_t, _P]),
 }
@@ -268,3 +271,41 @@ def linattn_bwd(q, k, v, dout, *, eps: float = 1e-15, grad_dtype=None, block_len
                      device=q.device)
     sana_linattn_bwd(q, k, v, dout, dq, dk, dv, ws, block_len=block_len or 0, eps=eps, stream=stream)
     return dq, dk, dv
+
+
+def sana_linattn_jvp_workspace_bytes(B: int, H: int, N: int, D: int, block_len: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.sana_linattn_jvp_workspace_bytes(B, H, N, D, block_len, ctypes.byref(out)),
+           "sana_linattn_jvp_workspace_bytes")
+    return out.value
+
+
+def sana_linattn_jvp(q, k, v, q_t, k_t, v_t, out, out_t, workspace, *, block_len: int = 0, eps: float = 1e-15,
+                     stream=None):
+    """Output and its tangent along (q_t, k_t, v_t), written into out and out_t."""
+    B, N, H, D = _shape(q, k, v, out)
+    for name, t in (("q_t", q_t), ("k_t", k_t), ("v_t", v_t), ("out_t", out_t)):
+        if tuple(t.shape) != (B, N, H, D) or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous GPU tensor of shape {(B, N, H, D)}")
+    if not (q.dtype == q_t.dtype == k_t.dtype == v_t.dtype) or out.dtype != out_t.dtype:
+        raise TypeError("tangents must share the inputs' dtype, out_t the output's")
+    _check(lib.sana_linattn_jvp(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_t.data_ptr(), k_t.data_ptr(),
+                                v_t.data_ptr(), out.data_ptr(), out_t.data_ptr(), dtype_code(q), dtype_code(out),
+                                B, H, N, D, block_len, eps, workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream_handle(stream)),
+           "sana_linattn_jvp")
+
+
+def linattn_jvp(q, k, v, q_t, k_t, v_t, *, eps: float = 1e-15, out_dtype=None, block_len: int | None = None,
+                stream=None):
+    """Allocates out, out_t (float32 unless out_dtype is given) and the
+    workspace with torch and returns (out, out_t)."""
+    torch = _torch()
+    ot = out_dtype or torch.float32
+    out = torch.empty(q.shape, dtype=ot, device=q.device)
+    out_t = torch.empty(q.shape, dtype=ot, device=q.device)
+    B, N, H, D = q.shape
+    ws = torch.empty(max(sana_linattn_jvp_workspace_bytes(B, H, N, D, block_len or 0), 1), dtype=torch.uint8,
+                     device=q.device)
+    sana_linattn_jvp(q, k, v, q_t, k_t, v_t, out, out_t, ws, block_len=block_len or 0, eps=eps, stream=stream)
+    return out, out_t

@@ -288,6 +288,59 @@ int backward(const void* q, const void* k, const void* v, const void* dout, void
     return SANA_OK;
 }
 
+// Forward-mode derivative: the forward's plan with the workspace doubled (a
+// state and a tangent state per head).
+int make_jvp_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block_len, Plan* pl) {
+    const int st = make_plan(in_dtype, out_dtype, B, H, N, D, block_len, pl);
+    if (st != SANA_OK || B == 0 || H == 0 || N == 0) return st;
+    const size_t bh2 = (size_t)B * H * 2;
+    if ((long long)bh2 > INT_MAX) return SANA_ERR_UNSUPPORTED;
+    pl->off_part = 0;
+    pl->off_state = round_up((long)(bh2 * pl->P * sana::kStateFloats * sizeof(float)), 256);
+    pl->bytes = pl->off_state + round_up((long)(bh2 * pl->NB * sana::kStateFloats * sizeof(float)), 256);
+    return SANA_OK;
+}
+
+int jvp(const void* q, const void* k, const void* v, const void* qt, const void* kt, const void* vt, void* out,
+        void* outt, int in_dtype, int out_dtype, int B, int H, int N, int D, int block_len, float eps, void* workspace,
+        size_t workspace_bytes, hipStream_t stream) {
+    Plan pl;
+    const int st = make_jvp_plan(in_dtype, out_dtype, B, H, N, D, block_len, &pl);
+    if (st != SANA_OK) return st;
+    if (!std::isfinite(eps) || eps < 0.f) return SANA_ERR_INVALID_ARG;
+    if (B == 0 || H == 0 || N == 0) return SANA_OK;
+    const void* ins[6] = {q, k, v, qt, kt, vt};
+    void* outs[2] = {out, outt};
+    for (const void* p : ins)
+        if (!p) return SANA_ERR_INVALID_ARG;
+    if (!out || !outt || !workspace) return SANA_ERR_INVALID_ARG;
+    for (const void* p : ins)
+        if (!aligned(p, 16)) return SANA_ERR_ALIGNMENT;
+    if (!aligned(out, 16) || !aligned(outt, 16) || !aligned(workspace, 256)) return SANA_ERR_ALIGNMENT;
+    const size_t elems = (size_t)B * N * H * D;
+    const size_t ib = elems * (in_dtype == SANA_DT_F32 ? 4 : 2), ob = elems * (out_dtype == SANA_DT_F32 ? 4 : 2);
+    for (int i = 0; i < 2; ++i) {
+        for (const void* p : ins)
+            if (overlaps(outs[i], ob, p, ib)) return SANA_ERR_ALIAS;
+        if (overlaps(outs[i], ob, workspace, pl.bytes)) return SANA_ERR_ALIAS;
+    }
+    if (overlaps(out, ob, outt, ob)) return SANA_ERR_ALIAS;
+    for (const void* p : ins)
+        if (overlaps(workspace, pl.bytes, p, ib)) return SANA_ERR_ALIAS;
+    if (workspace_bytes < pl.bytes) return SANA_ERR_WORKSPACE;
+
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    float* part = reinterpret_cast<float*>(ws + pl.off_part);
+    float* state = reinterpret_cast<float*>(ws + pl.off_state);
+    Plan pm = pl;   // the merge sees the state and the tangent state of a head as two heads
+    pm.H = 2 * H;
+    if (sana::launch_jvp_state(pl, k, v, kt, vt, part, stream) != hipSuccess ||
+        sana::launch_merge(pm, part, state, nullptr, nullptr, stream) != hipSuccess ||
+        sana::launch_jvp_apply(pl, q, qt, state, out, outt, eps, stream) != hipSuccess)
+        return SANA_ERR_HIP;
+    return SANA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -338,6 +391,27 @@ int sana_linattn_bwd(const void* q, const void* k, const void* v, const void* do
     if (block_len < 0) return SANA_ERR_INVALID_ARG;
     return backward(q, k, v, dout, dq, dk, dv, in_dtype, dout_dtype, grad_dtype, B, H, N, D, block_len, eps,
                     workspace, workspace_bytes, stream);
+}
+
+int sana_linattn_jvp_workspace_bytes(int B, int H, int N, int D, int block_len, size_t* bytes) {
+    if (!bytes) return SANA_ERR_INVALID_ARG;
+    size_t most = 0;
+    for (int dt : {SANA_DT_BF16, SANA_DT_F32}) {
+        Plan pl;
+        const int st = make_jvp_plan(dt, SANA_DT_F32, B, H, N, D, block_len, &pl);
+        if (st != SANA_OK) return st;
+        most = std::max(most, pl.bytes);
+    }
+    *bytes = most;
+    return SANA_OK;
+}
+
+int sana_linattn_jvp(const void* q, const void* k, const void* v, const void* q_t, const void* k_t, const void* v_t,
+                     void* out, void* out_t, int in_dtype, int out_dtype, int B, int H, int N, int D, int block_len,
+                     float eps, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (block_len < 0) return SANA_ERR_INVALID_ARG;
+    return jvp(q, k, v, q_t, k_t, v_t, out, out_t, in_dtype, out_dtype, B, H, N, D, block_len, eps, workspace,
+               workspace_bytes, stream);
 }
 
 int sana_linattn_plan_info(int in_dtype, int B, int H, int N, int D, int block_len, int* chunk_tokens,

@@ -166,98 +166,6 @@ __global__ __launch_bounds__(kThreads) void k_bwd_key_valu(
     }
 }
 
-// ------------------------------------------------------------------ matrix-core helpers
-constexpr int kPitch = 36;   // floats per LDS tile row: 32 + 4 keeps rows 16-byte aligned, no bank conflicts
-
-// MFMA operands of a D x (D+1) fp32 state S (row-major, kW floats per row),
-// each as three bf16 split terms, for lane (g, i) of a wave:
-//   transposed: A[row i][k = 16 ks + 8 g + e] = S[16 ks + 8 g + e][i]
-//   natural:    A[row i][k = 16 ks + 8 g + e] = S[i][16 ks + 8 g + e]
-__device__ __forceinline__ void state_operands(const float* S, int lane, bool transposed, u32x4 out[2][3]) {
-    const int g = lane >> 5, i = lane & 31;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int kk = 16 * ks + 8 * g + e;
-            x[e] = transposed ? S[kk * kW + i] : S[i * kW + kk];
-        }
-        split3_f32x8(x, out[ks]);
-    }
-}
-
-// acc += sum over the 32 features of A (three split terms) times the B operand
-// b0 (features 8g..8g+7 of this lane's token) and b1 (features 16+8g..): bf16
-// bits, or fp16 bits split exactly into two bf16 terms.  Small terms first.
-template <bool F16>
-__device__ __forceinline__ f32x16 mma_split(const u32x4 A[2][3], u32x4 b0, u32x4 b1, f32x16 acc) {
-    if constexpr (F16) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const u32x4 x = ks ? b1 : b0;
-            u32x4 hi, lo;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                uint32_t h, l;
-                float f0, f1;
-                split_f16x2(x[d], h, l, f0, f1);
-                hi[d] = h;
-                lo[d] = l;
-            }
-#pragma unroll
-            for (int sp = 2; sp >= 0; --sp) acc = mfma_bf16(A[ks][sp], lo, acc);
-#pragma unroll
-            for (int sp = 2; sp >= 0; --sp) acc = mfma_bf16(A[ks][sp], hi, acc);
-        }
-    } else {
-#pragma unroll
-        for (int sp = 2; sp >= 0; --sp) {
-            acc = mfma_bf16(A[0][sp], b0, acc);
-            acc = mfma_bf16(A[1][sp], b1, acc);
-        }
-    }
-    return acc;
-}
-
-// Bit j set when feature j of this lane's token is non-zero in the packed
-// operand words x0 (features 8g + ..) and x1 (16 + 8g + ..); the partner lane
-// (i + 32) contributes the other 16 features.
-__device__ __forceinline__ uint32_t nonzero_mask(u32x4 x0, u32x4 x1, int g) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        m |= (uint32_t)((x0[d] & 0xffffu) != 0) << (8 * g + 2 * d);
-        m |= (uint32_t)((x0[d] >> 16) != 0) << (8 * g + 2 * d + 1);
-        m |= (uint32_t)((x1[d] & 0xffffu) != 0) << (16 + 8 * g + 2 * d);
-        m |= (uint32_t)((x1[d] >> 16) != 0) << (16 + 8 * g + 2 * d + 1);
-    }
-    return m | (uint32_t)__shfl_xor((int)m, 32);
-}
-
-// Writes a wave's 32 x 32 accumulator tile (row 8*(r/4) + 4g + r%4 of column
-// i in register r of lane (g, i)) token-major through the wave's LDS tile, then
-// stores whole rows: dst(t) is the output row of token tt + t.  Rows t >= n
-// were computed from the clamped input row n - 1, so they hold exactly row
-// n - 1's values: they are stored there again (the same values), which keeps
-// every store unconditional.
-template <typename OutT, typename RowPtr>
-__device__ __forceinline__ void store_tile(float* ot, const f32x16& acc, int lane, int n, RowPtr dst) {
-    const int g = lane >> 5, i = lane & 31;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-        *reinterpret_cast<f32x4*>(ot + i * kPitch + 8 * rr + 4 * g) =
-            (f32x4){acc[4 * rr], acc[4 * rr + 1], acc[4 * rr + 2], acc[4 * rr + 3]};
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-        const int r = 8 * s4 + (lane >> 3), cc = (lane & 7) * 4;
-        const f32x4 x = *reinterpret_cast<const f32x4*>(ot + r * kPitch + cc);
-        store4(dst(min(r, n - 1)) + cc, x);
-    }
-    __builtin_amdgcn_wave_barrier();
-}
-
 // Split-term operands of the two heads of a work-group, kept in LDS (too many
 // to keep in registers next to the streaming tiles): [head][layout][ks][sp]
 // of 64 lanes x 16 bytes, layout 0 = transposed, 1 = natural (state_operands).

@@ -78,4 +78,12 @@ hipError_t launch_bwd_merge(const BwdPlan& bp, const float* gpart, float* ghat, 
 hipError_t launch_bwd_key(const BwdPlan& bp, const void* k, const void* v, const float* ghat, void* dk, void* dv,
                           hipStream_t stream);
 
+// Forward-mode derivative: partial and merged states hold the state and the
+// tangent state of each head, [B][H][2][P or NB][kStateFloats]; the forward's
+// merge kernel runs on them as 2 H heads.
+hipError_t launch_jvp_state(const Plan& pl, const void* k, const void* v, const void* kt, const void* vt, float* part,
+                            hipStream_t stream);
+hipError_t launch_jvp_apply(const Plan& pl, const void* q, const void* qt, const float* state, void* out, void* outt,
+                            float eps, hipStream_t stream);
+
 }  // namespace sana

@@ -36,16 +36,6 @@
 namespace sana {
 namespace {
 
-// Token range [c0, c1) of chunk p of a (b, head) unit.
-struct ChunkRange { int c0, c1; };
-__device__ __forceinline__ ChunkRange chunk_range(int p, int cpb, int chunk, int L, int N) {
-    const int beta = p / cpb, s = p - beta * cpb;
-    const int blk0 = beta * L;
-    const int blk1 = min(blk0 + L, N);
-    const int c0 = blk0 + s * chunk;
-    return {c0, min(c0 + chunk, blk1)};
-}
-
 // ------------------------------------------------------------------ state, bf16, MFMA
 // LDS tile: [tensor K|V][head 0|1][token 0..63][32 x bf16]; the second head's
 // rows are shifted by 64 bytes so that a 16-byte write from each head of one

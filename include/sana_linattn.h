@@ -247,6 +247,32 @@ SANA_API int sana_linattn_bwd(const void* q, const void* k, const void* v, const
                               int N, int D, int block_len, float eps, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
+/*
+ * Forward-mode derivative (Jacobian-vector product): the forward's output and
+ * its directional derivative along tangents (q_t, k_t, v_t) of the inputs, as
+ * forward-mode differentiation through attention needs (the consistency-model
+ * distillation on the Sana page, section "Sana-Sprint: two steps, on an arc",
+ * differentiates the model this way).  With f = ReLU(q), a = ReLU(k),
+ * f_t = [q > 0] q_t, a_t = [k > 0] k_t, S the state of the forward and
+ * S_t = sum (a_t [v | 1]^T + a [v_t | 0]^T) (prefix over blocks likewise):
+ *   out   = num / (den + eps)  as in the forward,
+ *   out_t = (num_t - out den_t) / (den + eps),
+ *   num_t = S_t[:, :D]^T f + S[:, :D]^T f_t,  den_t = S_t[:, D] . f + S[:, D] . f_t.
+ * The derivative of ReLU at 0 is taken as 0.
+ *   q, k, v, q_t, k_t, v_t  [B][N][H][D] in in_dtype, device, read only.
+ *   out, out_t   [B][N][H][D] in out_dtype, device, written; must not overlap
+ *                each other, an input or the workspace (error ALIAS).
+ *   block_len    0 = non-causal, >= 1 = block-causal.
+ *   workspace    >= sana_linattn_jvp_workspace_bytes(...) bytes, 256-byte aligned.
+ * Other conventions as for sana_linattn_fwd.
+ */
+SANA_API int sana_linattn_jvp_workspace_bytes(int B, int H, int N, int D, int block_len, size_t* bytes);
+
+SANA_API int sana_linattn_jvp(const void* q, const void* k, const void* v, const void* q_t, const void* k_t,
+                              const void* v_t, void* out, void* out_t, int in_dtype, int out_dtype, int B, int H,
+                              int N, int D, int block_len, float eps, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

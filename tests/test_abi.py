@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(sana.lib, n), n           # resolves in the shared library
         assert n in sana._SIGNATURES, n          # and the binding declares its signature
@@ -231,3 +231,36 @@ def test_backward_workspace_query():
     assert sana.sana_linattn_bwd_workspace_bytes(1, 70, 16384, 32, 1024) > bw
     assert sana.sana_linattn_bwd_workspace_bytes(0, 70, 16384, 32, 0) == 0
     assert sana.lib.sana_linattn_bwd_workspace_bytes(1, 1, 1, 32, 0, None) == sana.SANA_ERR_INVALID_ARG
+
+
+def jvp(q=A, k=A + 64 * MB, v=A + 128 * MB, qt=A + 192 * MB, kt=A + 256 * MB, vt=A + 320 * MB, out=A + 384 * MB,
+        outt=A + 448 * MB, in_dt=1, out_dt=0, B=1, H=2, N=256, D=32, L=0, eps=1e-15, ws=A + 512 * MB, ws_bytes=16):
+    return sana.lib.sana_linattn_jvp(q, k, v, qt, kt, vt, out, outt, in_dt, out_dt, B, H, N, D, L, eps, ws,
+                                     ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, sana.SANA_ERR_WORKSPACE),
+    (dict(L=64, in_dt=2, out_dt=2), sana.SANA_ERR_WORKSPACE),
+    (dict(in_dt=0), sana.SANA_ERR_WORKSPACE),
+    (dict(L=-1), sana.SANA_ERR_INVALID_ARG),
+    (dict(kt=None), sana.SANA_ERR_INVALID_ARG),
+    (dict(outt=None), sana.SANA_ERR_INVALID_ARG),
+    (dict(in_dt=3), sana.SANA_ERR_INVALID_ARG),
+    (dict(D=16), sana.SANA_ERR_UNSUPPORTED),
+    (dict(eps=-1.0), sana.SANA_ERR_INVALID_ARG),
+    (dict(vt=A + 320 * MB + 4), sana.SANA_ERR_ALIGNMENT),
+    (dict(outt=A + 384 * MB), sana.SANA_ERR_ALIAS),     # out_t == out
+    (dict(out=A + 256 * MB), sana.SANA_ERR_ALIAS),      # out == k_t
+    (dict(ws=A + 448 * MB), sana.SANA_ERR_ALIAS),       # workspace == out_t
+    (dict(H=0), sana.SANA_OK),
+])
+def test_jvp_argument_errors(kw, code):
+    assert jvp(**kw) == code
+
+
+def test_jvp_workspace_query():
+    fw = sana.sana_linattn_workspace_bytes(1, 70, 16384, 32, 0)
+    jw = sana.sana_linattn_jvp_workspace_bytes(1, 70, 16384, 32, 0)
+    assert jw >= 2 * fw - 1024 and jw % 256 == 0
+    assert sana.lib.sana_linattn_jvp_workspace_bytes(1, 1, 1, 32, 0, None) == sana.SANA_ERR_INVALID_ARG

@@ -136,3 +136,17 @@ def make_dout(w: Workload, dtype: int | None = None):
     if dtype == DT_F16:
         return x.astype(np.float16)
     return x
+
+
+def make_tangents(w: Workload):
+    """Seeded tangents (q_t, k_t, v_t) for forward-mode derivative tests, in the
+    inputs' dtype: ``default_rng([seed, t])`` standard normal, t = 4, 5, 6."""
+    out = []
+    for t in (4, 5, 6):
+        x = np.random.default_rng([w.seed, t]).standard_normal(size=(w.B, w.N, w.H, w.D), dtype=np.float32)
+        if w.in_dtype == DT_BF16:
+            x = f32_to_bf16_bits(x)
+        elif w.in_dtype == DT_F16:
+            x = x.astype(np.float16)
+        out.append(x)
+    return tuple(out)

@@ -189,7 +189,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time budget of the oracle CPU baseline (0 skips it)")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the other-out-dtype, block-causal and fp16-input timings")
+                    help="skip the other-out-dtype, block-causal, fp16-input, backward and JVP timings")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="with --no-extras, still run the device-to-device copy (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -398,6 +398,23 @@ def main() -> int:
             "note": "sana_linattn_bwd, bf16 q/k/v/dout/gradients; dout is another input set; "
                     "algorithmic bytes = 7 tensors"}
         del grads, ws_bw
+
+        # forward-mode derivative: bf16 q, k, v and tangents -> out and out_t in the bench's out dtype
+        tangents = [torch.empty((B, N, H, D), dtype=out_t, device=dev) for _ in range(NSETS)]
+        ws_jv = torch.empty(sana.sana_linattn_jvp_workspace_bytes(B, H, N, D, 0), dtype=torch.uint8, device=dev)
+
+        def jvp(i):
+            q, k, v = sets[i % NSETS]
+            qt, kt, vt = sets[(i + 1) % NSETS]
+            sana.sana_linattn_jvp(q, k, v, qt, kt, vt, outs[i % NSETS], tangents[i % NSETS], ws_jv, eps=w.eps,
+                                  stream=stream)
+        ms = timed(jvp, args.steps)
+        jv_bytes = w.token_heads * D * (6 * 2 + 2 * out_bytes)   # read 6 bf16 tensors, write out and out_t
+        extra["jvp_bf16_" + args.out_dtype + "out"] = {
+            "ms_per_step": round(ms, 5), "GBps": round(jv_bytes / ms / 1e6, 1),
+            "pct_hbm_peak": round(100 * jv_bytes / ms / 1e6 / HBM_PEAK_GBPS, 2),
+            "note": "sana_linattn_jvp; tangents are another input set; algorithmic bytes = 6 inputs + 2 outputs"}
+        del tangents, ws_jv
 
     line = {
         "metric": METRIC,

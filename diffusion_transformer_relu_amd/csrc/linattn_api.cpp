@@ -43,7 +43,7 @@ int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block
     if ((in_dtype != SANA_DT_F32 && in_dtype != SANA_DT_BF16 && in_dtype != SANA_DT_F16) ||
         (out_dtype != SANA_DT_F32 && out_dtype != SANA_DT_BF16 && out_dtype != SANA_DT_F16))
         return SANA_ERR_INVALID_ARG;
-    if (D != sana::kD) return SANA_ERR_UNSUPPORTED;
+    if (D != 16 && D != 32 && D != 64) return SANA_ERR_UNSUPPORTED;
     if (N > kMaxN || B > kMaxBH || H > kMaxBH) return SANA_ERR_UNSUPPORTED;
 
     std::memset(pl, 0, sizeof *pl);
@@ -52,11 +52,12 @@ int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block
     pl->N = N;
     pl->in_dtype = in_dtype;
     pl->out_dtype = out_dtype;
+    pl->D = D;
     if (B == 0 || H == 0 || N == 0) return SANA_OK;   // empty problem, no workspace
 
     pl->L = (block_len == 0 || block_len >= N) ? N : block_len;
     pl->NB = ceil_div(N, pl->L);
-    pl->mfma = (in_dtype != SANA_DT_F32 && !env_is("SANA_LINATTN_PATH", "valu")) ? 1 : 0;
+    pl->mfma = (in_dtype != SANA_DT_F32 && D == sana::kD && !env_is("SANA_LINATTN_PATH", "valu")) ? 1 : 0;
     pl->HP = pl->mfma ? (H + 1) / 2 : H;
     const long units = (long)B * pl->HP * pl->NB;   // independent (b, head unit, block) triples
 
@@ -97,11 +98,12 @@ int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block
         return SANA_ERR_UNSUPPORTED;
 
     const size_t bh = (size_t)B * H;
+    const size_t sf = (size_t)D * (D + 1);   // floats per state
     size_t off = 0;
     pl->off_part = off;
-    off += round_up((long)(bh * pl->P * sana::kStateFloats * sizeof(float)), 256);
+    off += round_up((long)(bh * pl->P * sf * sizeof(float)), 256);
     pl->off_state = off;
-    off += round_up((long)(bh * pl->NB * sana::kStateFloats * sizeof(float)), 256);
+    off += round_up((long)(bh * pl->NB * sf * sizeof(float)), 256);
     pl->bytes = off;
     return SANA_OK;
 }
@@ -171,7 +173,7 @@ int forward(const void* q, const void* k, const void* v, void* out, int in_dtype
         overlaps(workspace, pl.bytes, v, v_bytes) || overlaps(workspace, pl.bytes, out, out_bytes))
         return SANA_ERR_ALIAS;
     if (state_in || state_out) {
-        const size_t sb = (size_t)B * H * sana::kStateFloats * sizeof(float);
+        const size_t sb = (size_t)B * H * D * (D + 1) * sizeof(float);
         if ((state_in && !aligned(state_in, 4)) || (state_out && !aligned(state_out, 4)))
             return SANA_ERR_ALIGNMENT;
         if (state_in && (overlaps(state_in, sb, out, out_bytes) || overlaps(state_in, sb, workspace, pl.bytes)))
@@ -206,6 +208,7 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
     std::memset(bp, 0, sizeof *bp);
     const int st = make_plan(in_dtype, SANA_DT_F32, B, H, N, D, block_len, &bp->fw);
     if (st != SANA_OK) return st;
+    if (D != sana::kD) return SANA_ERR_UNSUPPORTED;   // the backward is built for D = 32
     for (int c : {dout_dtype, grad_dtype})
         if (c != SANA_DT_F32 && c != SANA_DT_BF16 && c != SANA_DT_F16) return SANA_ERR_INVALID_ARG;
     bp->dout_dtype = dout_dtype;
@@ -292,7 +295,9 @@ int backward(const void* q, const void* k, const void* v, const void* dout, void
 // state and a tangent state per head).
 int make_jvp_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block_len, Plan* pl) {
     const int st = make_plan(in_dtype, out_dtype, B, H, N, D, block_len, pl);
-    if (st != SANA_OK || B == 0 || H == 0 || N == 0) return st;
+    if (st != SANA_OK) return st;
+    if (D != sana::kD) return SANA_ERR_UNSUPPORTED;   // the forward-mode derivative is built for D = 32
+    if (B == 0 || H == 0 || N == 0) return SANA_OK;
     const size_t bh2 = (size_t)B * H * 2;
     if ((long long)bh2 > INT_MAX) return SANA_ERR_UNSUPPORTED;
     pl->off_part = 0;
@@ -351,7 +356,7 @@ const char* sana_linattn_status_string(int status) {
     switch (status) {
         case SANA_OK: return "success";
         case SANA_ERR_INVALID_ARG: return "invalid argument";
-        case SANA_ERR_UNSUPPORTED: return "unsupported size or head dim (D must be 32)";
+        case SANA_ERR_UNSUPPORTED: return "unsupported size or head dim (forward: D = 16, 32 or 64; backward and JVP: D = 32)";
         case SANA_ERR_ALIGNMENT: return "misaligned pointer (tensors need 16 bytes, workspace 256)";
         case SANA_ERR_ALIAS: return "output or workspace overlaps another buffer";
         case SANA_ERR_WORKSPACE: return "workspace too small";

@@ -8,7 +8,7 @@
 
 namespace sana {
 
-constexpr int kD = 32;                    // head dim (every Sana model: linear_head_dim 32)
+constexpr int kD = 32;                    // head dim of the matrix-core kernels (every Sana model: 32)
 constexpr int kW = kD + 1;                // state row: D value columns + the normaliser column
 constexpr int kStateFloats = kD * kW;     // 1056 floats per (b, h) state
 constexpr int kThreads = 256;             // 4 wave64 per work-group, every kernel
@@ -44,7 +44,8 @@ struct Plan {
     int P;        // chunks per (b, h) = NB * cpb
     int tile;     // tokens per apply work-group
     int tpb;      // apply work-groups per block
-    int mfma;     // 1: bf16 matrix-core kernels, 0: vector kernels
+    int mfma;     // 1: 16-bit-input matrix-core kernels (D = 32), 0: vector kernels
+    int D;        // head dim: 32, or 16 / 64 (vector kernels only)
     int in_dtype, out_dtype;
     size_t off_part, off_state, bytes;
     Strides sq, sk, sv, so;   // element strides of q, k, v, out

@@ -33,6 +33,8 @@
 // implementation for cross-checks.
 #include "linattn_device.h"
 
+#include <type_traits>
+
 namespace sana {
 namespace {
 
@@ -149,13 +151,15 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
 }
 
 // ------------------------------------------------------------------ state, vector path
-// grid.x = (b * H + h) * P + p.  Thread t owns state entries t, t+256, ... (5 at most).
-template <typename InT>
+// grid.x = (b * H + h) * P + p.  Thread t owns state entries t, t+256, ...
+// Head dim DD (16, 32 or 64): a state is DD x (DD + 1).
+template <typename InT, int DD>
 __global__ __launch_bounds__(kThreads) void k_state_partial_valu(
     const InT* __restrict__ k, const InT* __restrict__ v, float* __restrict__ part,
     int N, int H, int L, int cpb, int P, int chunk, Strides stk, Strides stv) {
-    __shared__ float sa[kValuTile][kD + 1];   // ReLU(k) tile
-    __shared__ float sv[kValuTile][kW];       // [v | 1] tile
+    constexpr int WW = DD + 1, SF = DD * WW, M = (SF + kThreads - 1) / kThreads;
+    __shared__ float sa[kValuTile][DD + 1];   // ReLU(k) tile
+    __shared__ float sv[kValuTile][WW];       // [v | 1] tile
 
     const int p = blockIdx.x % P;
     const int bh = blockIdx.x / P;
@@ -163,76 +167,76 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_valu(
     const ChunkRange cr = chunk_range(p, cpb, chunk, L, N);
     const int tid = threadIdx.x;
 
-    float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+    float acc[M] = {};
     for (int t0 = cr.c0; t0 < cr.c1; t0 += kValuTile) {
         __syncthreads();
-        for (int e = tid; e < kValuTile * kD; e += kThreads) {
-            const int tok = e >> 5, jj = e & 31;
+        for (int e = tid; e < kValuTile * DD; e += kThreads) {
+            const int tok = e / DD, jj = e % DD;
             const int n = t0 + tok;
             float kk = 0.f, vv = 0.f;
             if (n < cr.c1) {
-                const long long col = (long long)h * kD + jj;
+                const long long col = (long long)h * DD + jj;
                 kk = load_in(k, b * stk.b + n * stk.n + col);
                 vv = load_in(v, b * stv.b + n * stv.n + col);
             }
             sa[tok][jj] = kk > 0.f ? kk : 0.f;
             sv[tok][jj] = vv;
         }
-        if (tid < kValuTile) sv[tid][kD] = 1.f;
+        if (tid < kValuTile) sv[tid][DD] = 1.f;
         __syncthreads();
 #pragma unroll
-        for (int m = 0; m < 5; ++m) {
+        for (int m = 0; m < M; ++m) {
             const int o = tid + kThreads * m;
-            if (o < kStateFloats) {
-                const int jj = o / kW, c = o - jj * kW;
+            if (o < SF) {
+                const int jj = o / WW, c = o - jj * WW;
                 float s = acc[m];
                 for (int tok = 0; tok < kValuTile; ++tok) s += sa[tok][jj] * sv[tok][c];
                 acc[m] = s;
             }
         }
     }
-    float* dst = part + ((size_t)bh * P + p) * kStateFloats;
+    float* dst = part + ((size_t)bh * P + p) * SF;
 #pragma unroll
-    for (int m = 0; m < 5; ++m) {
+    for (int m = 0; m < M; ++m) {
         const int o = tid + kThreads * m;
-        if (o < kStateFloats) dst[o] = acc[m];
+        if (o < SF) dst[o] = acc[m];
     }
 }
 
 // ------------------------------------------------------------------ merge / block scan
-// grid.x = (b * H + h) * kMergeGroups + m; thread t owns state entry
-// e = m * kMergeThreads + t.  Starting from the carried state (or zero), for
-// each block it sums that block's chunk partials (groups of 8 loads in flight,
-// added as a fixed pairwise tree), and adds the block sum to the running state
-// (inclusive prefix over blocks); the final running state is the carried state
-// out.  state_in and state_out may be the same array: each thread reads its own
+// grid.x = (b * H + h) * groups + m, groups = ceil(SF / kMergeThreads); thread
+// t owns state entry e = m * kMergeThreads + t of the SF = D (D + 1) entries.
+// Starting from the carried state (or zero), for each block it sums that
+// block's chunk partials (groups of 8 loads in flight, added as a fixed
+// pairwise tree), and adds the block sum to the running state (inclusive
+// prefix over blocks); the final running state is the carried state out.
+// state_in and state_out may be the same array: each thread reads its own
 // entry before it writes it.
-constexpr int kMergeGroups = (kStateFloats + kMergeThreads - 1) / kMergeThreads;
-
 __global__ __launch_bounds__(kMergeThreads) void k_merge(
     const float* __restrict__ part, float* __restrict__ state, const float* state_in, float* state_out,
-    int NB, int cpb, int P) {
-    const size_t bh = blockIdx.x / kMergeGroups;
-    const int e = (blockIdx.x % kMergeGroups) * kMergeThreads + threadIdx.x;
-    if (e >= kStateFloats) return;
-    const float* src = part + bh * P * kStateFloats + e;
-    float* dst = state + bh * NB * kStateFloats + e;
-    float acc = state_in ? state_in[bh * kStateFloats + e] : 0.f;
+    int NB, int cpb, int P, int SF) {
+    const int groups = (SF + kMergeThreads - 1) / kMergeThreads;
+    const size_t bh = blockIdx.x / groups;
+    const int e = (blockIdx.x % groups) * kMergeThreads + threadIdx.x;
+    if (e >= SF) return;
+    const float* src = part + bh * P * SF + e;
+    float* dst = state + bh * NB * SF + e;
+    float acc = state_in ? state_in[bh * SF + e] : 0.f;
 #pragma unroll 4
     for (int beta = 0; beta < NB; ++beta) {
-        const float* blk = src + (size_t)beta * cpb * kStateFloats;
+        const float* blk = src + (size_t)beta * cpb * SF;
         float bs = 0.f;
         for (int s0 = 0; s0 < cpb; s0 += 8) {
             float x[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                x[i] = (s0 + i < cpb) ? blk[(size_t)(s0 + i) * kStateFloats] : 0.f;
+                x[i] = (s0 + i < cpb) ? blk[(size_t)(s0 + i) * SF] : 0.f;
             bs += ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
         }
         acc += bs;
-        dst[(size_t)beta * kStateFloats] = acc;
+        dst[(size_t)beta * SF] = acc;
     }
-    if (state_out) state_out[bh * kStateFloats + e] = acc;
+    if (state_out) state_out[bh * SF + e] = acc;
 }
 
 // ------------------------------------------------------------------ apply, bf16, MFMA
@@ -387,37 +391,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(F16 ? 
 
 // ------------------------------------------------------------------ apply, vector path
 // grid.x = ((b * H + h) * NB + beta) * tpb + tile; one thread per token.
-template <typename InT, typename OutT>
+template <typename InT, typename OutT, int DD>
 __global__ __launch_bounds__(kThreads) void k_apply_valu(
     const InT* __restrict__ q, const float* __restrict__ state, OutT* __restrict__ out,
     int N, int H, int L, int NB, int tpb, float eps, Strides sq, Strides so) {
-    __shared__ float s[kStateFloats];
+    constexpr int WW = DD + 1, SF = DD * WW;
+    __shared__ float s[SF];
     const int tile = blockIdx.x % tpb;
     const size_t bhb = blockIdx.x / tpb;            // (b * H + h) * NB + beta
     const int beta = (int)(bhb % NB);
     const size_t bh = bhb / NB;
     const int h = (int)(bh % H), b = (int)(bh / H);
-    for (int e = threadIdx.x; e < kStateFloats; e += kThreads) s[e] = state[bhb * kStateFloats + e];
+    for (int e = threadIdx.x; e < SF; e += kThreads) s[e] = state[bhb * SF + e];
     __syncthreads();
     const int blk0 = beta * L;
     const int blk1 = min(blk0 + L, N);
     const int row = blk0 + tile * kValuApplyTokens + threadIdx.x;
     if (row >= blk1) return;
-    const long long qbase = b * sq.b + row * sq.n + (long long)h * kD;
-    const long long obase = b * so.b + row * so.n + (long long)h * kD;
-    float f[kD];
+    const long long qbase = b * sq.b + row * sq.n + (long long)h * DD;
+    const long long obase = b * so.b + row * so.n + (long long)h * DD;
+    float f[DD];
 #pragma unroll
-    for (int jj = 0; jj < kD; ++jj) {
+    for (int jj = 0; jj < DD; ++jj) {
         const float x = load_in(q, qbase + jj);
         f[jj] = x > 0.f ? x : 0.f;
     }
     float den = 0.f;
 #pragma unroll
-    for (int jj = 0; jj < kD; ++jj) den += f[jj] * s[jj * kW + kD];
-    for (int cc = 0; cc < kD; ++cc) {
+    for (int jj = 0; jj < DD; ++jj) den += f[jj] * s[jj * WW + DD];
+    for (int cc = 0; cc < DD; ++cc) {
         float num = 0.f;
 #pragma unroll
-        for (int jj = 0; jj < kD; ++jj) num += f[jj] * s[jj * kW + cc];
+        for (int jj = 0; jj < DD; ++jj) num += f[jj] * s[jj * WW + cc];
         store_out(out, obase + cc, num / (den + eps));
     }
 }
@@ -437,6 +442,16 @@ template <typename F> void by_dtype(int code, F&& f) {
     else
         f(Tag<float>{});
 }
+
+// Calls f(std::integral_constant<int, D>) for the supported head dims.
+template <typename F> void by_head_dim(int D, F&& f) {
+    if (D == 16)
+        f(std::integral_constant<int, 16>{});
+    else if (D == 64)
+        f(std::integral_constant<int, 64>{});
+    else
+        f(std::integral_constant<int, 32>{});
+}
 }  // namespace
 
 hipError_t launch_state(const Plan& pl, const void* k, const void* v, float* part, hipStream_t stream) {
@@ -453,10 +468,13 @@ hipError_t launch_state(const Plan& pl, const void* k, const void* v, float* par
     } else {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.H * pl.P);
         by_dtype(pl.in_dtype, [&](auto in) {
-            using IT = typename decltype(in)::type;
-            hipLaunchKernelGGL(k_state_partial_valu<IT>, dim3(grid), dim3(kThreads), 0, stream,
-                               static_cast<const IT*>(k), static_cast<const IT*>(v), part,
-                               pl.N, pl.H, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
+            by_head_dim(pl.D, [&](auto dd) {
+                using IT = typename decltype(in)::type;
+                constexpr int DD = decltype(dd)::value;
+                hipLaunchKernelGGL((k_state_partial_valu<IT, DD>), dim3(grid), dim3(kThreads), 0, stream,
+                                   static_cast<const IT*>(k), static_cast<const IT*>(v), part,
+                                   pl.N, pl.H, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
+            });
         });
     }
     return hipGetLastError();
@@ -464,9 +482,10 @@ hipError_t launch_state(const Plan& pl, const void* k, const void* v, float* par
 
 hipError_t launch_merge(const Plan& pl, const float* part, float* state, const float* state_in,
                         float* state_out, hipStream_t stream) {
-    const unsigned grid = (unsigned)((size_t)pl.B * pl.H * kMergeGroups);
+    const int SF = pl.D * (pl.D + 1);
+    const unsigned grid = (unsigned)((size_t)pl.B * pl.H * ((SF + kMergeThreads - 1) / kMergeThreads));
     hipLaunchKernelGGL(k_merge, dim3(grid), dim3(kMergeThreads), 0, stream, part, state, state_in, state_out,
-                       pl.NB, pl.cpb, pl.P);
+                       pl.NB, pl.cpb, pl.P, SF);
     return hipGetLastError();
 }
 
@@ -490,11 +509,14 @@ hipError_t launch_apply(const Plan& pl, const void* q, const float* state, void*
         const unsigned grid = (unsigned)((size_t)pl.B * pl.H * pl.NB * pl.tpb);
         by_dtype(pl.in_dtype, [&](auto in) {
             by_dtype(pl.out_dtype, [&](auto o) {
+              by_head_dim(pl.D, [&](auto dd) {
                 using IT = typename decltype(in)::type;
                 using OT = typename decltype(o)::type;
-                hipLaunchKernelGGL((k_apply_valu<IT, OT>), dim3(grid), dim3(kThreads), 0, stream,
+                constexpr int DD = decltype(dd)::value;
+                hipLaunchKernelGGL((k_apply_valu<IT, OT, DD>), dim3(grid), dim3(kThreads), 0, stream,
                                    static_cast<const IT*>(q), state, static_cast<OT*>(out), pl.N, pl.H, pl.L,
                                    pl.NB, pl.tpb, eps, pl.sq, pl.so);
+              });
             });
         });
     }

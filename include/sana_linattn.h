@@ -34,7 +34,10 @@
  *            ("What LiteLA actually computes") requires because fp16
  *            activations overflow.  A bf16 or fp16 out is the fp32 result
  *            rounded to nearest-even (outputs lie within the range of V, so an
- *            fp16 out cannot overflow).  D must be 32 (the Sana head dim).
+ *            fp16 out cannot overflow).  D is 32 (the Sana head dim, on the matrix
+ *            cores for 16-bit inputs) or, for the forward entry points, 16 or 64
+ *            (vector-unit kernels); the backward and the forward-mode
+ *            derivative take D = 32.
  * Memory     Every pointer is device memory on the current HIP device, owned
  *            by the caller.  The library allocates nothing, keeps nothing
  *            after return, and never synchronises: work is enqueued on
@@ -83,7 +86,8 @@ typedef enum {
     SANA_OK = 0,
     SANA_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad dtype code,
                                   eps non-finite or < 0, block_len < 1, unknown stage bit */
-    SANA_ERR_UNSUPPORTED = 2,  /* D != 32, or sizes beyond what the launch grid covers */
+    SANA_ERR_UNSUPPORTED = 2,  /* D not 16, 32 or 64 (32 for the backward and the JVP), or sizes
+                                  beyond what the launch grid covers */
     SANA_ERR_ALIGNMENT = 3,    /* q, k, v, out not 16-byte aligned, workspace not 256-byte aligned */
     SANA_ERR_ALIAS = 4,        /* out or workspace overlaps an input, or each other */
     SANA_ERR_WORKSPACE = 5,    /* workspace_bytes smaller than required */

@@ -38,6 +38,18 @@ def test_version_and_status_strings():
     assert sana.sana_linattn_status_string(-1) == "unknown status"
 
 
+def test_other_head_dims():
+    assert sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 8, 256, 64, 0)["mfma"] == 0
+    assert sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 8, 256, 16, 0)["mfma"] == 0
+    w16, w32, w64 = (sana.sana_linattn_workspace_bytes(1, 8, 4096, d, 0) for d in (16, 32, 64))
+    assert w16 < w32 < w64
+    for d in (8, 48, 128):
+        assert sana.lib.sana_linattn_workspace_bytes(1, 8, 4096, d, 0, ctypes.byref(ctypes.c_size_t())) == \
+            sana.SANA_ERR_UNSUPPORTED
+    for f in (sana.lib.sana_linattn_bwd_workspace_bytes, sana.lib.sana_linattn_jvp_workspace_bytes):
+        assert f(1, 8, 4096, 64, 0, ctypes.byref(ctypes.c_size_t())) == sana.SANA_ERR_UNSUPPORTED
+
+
 def test_workspace_and_plan_queries():
     ws = sana.sana_linattn_workspace_bytes(1, 70, 16384, 32, 0)
     assert ws > 0 and ws % 256 == 0
@@ -68,7 +80,7 @@ def test_tuning_environment(monkeypatch):
 
 @pytest.mark.parametrize("args,code", [
     ((1, 70, 16384, 31, 0), sana.SANA_ERR_UNSUPPORTED),
-    ((1, 70, 16384, 64, 0), sana.SANA_ERR_UNSUPPORTED),
+    ((1, 70, 16384, 128, 0), sana.SANA_ERR_UNSUPPORTED),
     ((1, 70, 16384, 0, 0), sana.SANA_ERR_INVALID_ARG),
     ((-1, 70, 16384, 32, 0), sana.SANA_ERR_INVALID_ARG),
     ((1, -70, 16384, 32, 0), sana.SANA_ERR_INVALID_ARG),
@@ -101,7 +113,9 @@ def fwd(q=A, k=A + 64 * MB, v=A + 128 * MB, out=A + 192 * MB, in_dt=1, out_dt=0,
     (dict(in_dt=3), sana.SANA_ERR_INVALID_ARG),
     (dict(out_dt=-1), sana.SANA_ERR_INVALID_ARG),
     (dict(out_dt=3), sana.SANA_ERR_INVALID_ARG),
-    (dict(D=16), sana.SANA_ERR_UNSUPPORTED),
+    (dict(D=48), sana.SANA_ERR_UNSUPPORTED),
+    (dict(D=16, ws_bytes=1024), sana.SANA_ERR_WORKSPACE),   # head dims 16 and 64 run on the vector unit
+    (dict(D=64, ws_bytes=1024), sana.SANA_ERR_WORKSPACE),
     (dict(B=-1), sana.SANA_ERR_INVALID_ARG),
     (dict(eps=float("nan")), sana.SANA_ERR_INVALID_ARG),
     (dict(eps=float("inf")), sana.SANA_ERR_INVALID_ARG),

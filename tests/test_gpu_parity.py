@@ -295,3 +295,51 @@ def test_16bit_out_is_the_fp32_out_rounded_to_nearest_even(in_dt):
     for t in (torch.bfloat16, torch.float16):
         got = sana.linattn_fwd(q, k, v, out_dtype=t).cpu()
         assert torch.equal(got.view(torch.int16), f32.to(t).view(torch.int16)), t
+
+
+HEAD_DIMS = [
+    workloads.Workload("d16_B2_N1000_H8_bf16", 2, 1000, 8, 16, workloads.DT_BF16, seed=121),
+    workloads.Workload("d16_B1_N4096_H72_L1024_f16", 1, 4096, 72, 16, workloads.DT_F16, seed=122, block_len=1024),
+    workloads.Workload("d64_B2_N1000_H5_f32", 2, 1000, 5, 64, workloads.DT_F32, seed=123, block_len=300),
+    workloads.Workload("d64_B1_N4096_H18_bf16", 1, 4096, 18, 64, workloads.DT_BF16, seed=124),
+]
+
+
+@pytest.mark.parametrize("w", HEAD_DIMS, ids=lambda w: w.name)
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["f32out", "bf16out"])
+def test_other_head_dims(w, out_dtype):
+    """Head dims 16 and 64 (vector-unit kernels) against the oracle."""
+    (q, k, v), want = inputs_and_oracle(w)
+    got = run_hip(q, k, v, block_len=w.block_len, eps=w.eps, out_dtype=out_dtype)
+    compare(got, want, v, out_dtype == torch.bfloat16, w.name)
+
+
+def test_other_head_dims_streaming_and_strided():
+    """D = 64 streamed with a carried state; D = 16 from a fused qkv buffer."""
+    import diffusion_transformer_relu_amd as sana
+    w = workloads.Workload("d64_stream", 2, 2048, 3, 64, workloads.DT_BF16, seed=125, block_len=256)
+    (q, k, v), want = inputs_and_oracle(w)
+    _, st_want = oracle.linattn_fwd(q, k, v, block_len=256, return_states=True)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    out = torch.empty((2, 2048, 3, 64), dtype=torch.float32, device="cuda:0")
+    state = torch.empty((2, 3, 64, 65), dtype=torch.float32, device="cuda:0")
+    for c, (a, b) in enumerate(((0, 768), (768, 2048))):
+        ws = torch.empty(sana.sana_linattn_workspace_bytes(2, 3, b - a, 64, 256), dtype=torch.uint8, device="cuda:0")
+        o = torch.empty((2, b - a, 3, 64), dtype=torch.float32, device="cuda:0")
+        sana.sana_linattn_blockcausal_stream_fwd(qd[:, a:b].contiguous(), kd[:, a:b].contiguous(),
+                                                 vd[:, a:b].contiguous(), o, ws, 256,
+                                                 state_in=state if c else None, state_out=state)
+        out[:, a:b] = o
+    torch.cuda.synchronize()
+    compare(out.cpu().double().numpy(), want, v, False, w.name)
+    fin = st_want[:, :, -1]
+    assert np.max(np.abs(state.cpu().double().numpy() - fin)) <= 1e-5 * np.max(np.abs(fin))
+
+    w2 = workloads.Workload("d16_qkv", 2, 777, 6, 16, workloads.DT_BF16, seed=126)
+    (q, k, v), want = inputs_and_oracle(w2)
+    qkv = to_device(np.stack([q, k, v], axis=2))
+    out = torch.empty((2, 777, 6, 16), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(sana.sana_linattn_workspace_bytes(2, 6, 777, 16, 0), dtype=torch.uint8, device="cuda:0")
+    sana.sana_linattn_fwd_strided(qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2], out, ws)
+    torch.cuda.synchronize()
+    compare(out.cpu().double().numpy(), want, v, False, w2.name)

@@ -16,6 +16,8 @@
 // reductions run in fixed orders, so results are bitwise repeatable.
 #include "linattn_device.h"
 
+#include <type_traits>
+
 namespace sana {
 namespace {
 
@@ -423,6 +425,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
 
     struct Tile {
         u32x4 q0, q1;
+        u32x4 g0, g1;      // 16-bit dout in the operand layout (staged dout only)
         GradRow<GT> gr;
     };
     constexpr bool kStageDout = sizeof(GT) == 2;   // 16-bit dout is staged with q; fp32 dout is read per wave
@@ -529,34 +532,48 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
         }
 
         asm volatile("" ::: "memory");
-        // dq^T = P_v u^T (+ P[:, D] w), B = u in the operand layout from the tile
-        u32x4 ub[2][3];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            float uu[8];
-            const f32x4 a4 = *reinterpret_cast<const f32x4*>(ot + i * kPitch + 16 * ks + 8 * g);
-            const f32x4 b4 = *reinterpret_cast<const f32x4*>(ot + i * kPitch + 16 * ks + 8 * g + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uu[e] = a4[e];
-                uu[4 + e] = b4[e];
-            }
-            split3_trunc_f32x8(uu, ub[ks]);
-        }
-        __builtin_amdgcn_wave_barrier();
         acc = (f32x16){};
+        float rs = 1.f;   // per-token factor of the MFMA result
+        if constexpr (kStageDout) {
+            // dq^T = r (P_v dout^T) + P[:, D] w: the 16-bit dout is an exact
+            // operand, so only P needs split terms
+            u32x4 A[2][3];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            u32x4 A[3];
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int sp = 0; sp < 3; ++sp) A[sp] = opnd.v[hh][1][ks][sp][lane];
-            // products of split terms in increasing size; those below 2^-24 are dropped
-            acc = mfma_bf16(A[0], ub[ks][2], acc);
-            acc = mfma_bf16(A[1], ub[ks][1], acc);
-            acc = mfma_bf16(A[2], ub[ks][0], acc);
-            acc = mfma_bf16(A[0], ub[ks][1], acc);
-            acc = mfma_bf16(A[1], ub[ks][0], acc);
-            acc = mfma_bf16(A[0], ub[ks][0], acc);
+                for (int sp = 0; sp < 3; ++sp) A[ks][sp] = opnd.v[hh][1][ks][sp][lane];
+            acc = mma_split<std::is_same<GT, _Float16>::value>(A, x.g0, x.g1, acc);
+            rs = r;
+        } else {
+            // fp32 dout: dq^T = P_v u^T + P[:, D] w, u read back in the operand
+            // layout and split into three bf16 terms
+            u32x4 ub[2][3];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                float uu[8];
+                const f32x4 a4 = *reinterpret_cast<const f32x4*>(ot + i * kPitch + 16 * ks + 8 * g);
+                const f32x4 b4 = *reinterpret_cast<const f32x4*>(ot + i * kPitch + 16 * ks + 8 * g + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    uu[e] = a4[e];
+                    uu[4 + e] = b4[e];
+                }
+                split3_trunc_f32x8(uu, ub[ks]);
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                u32x4 A[3];
+#pragma unroll
+                for (int sp = 0; sp < 3; ++sp) A[sp] = opnd.v[hh][1][ks][sp][lane];
+                // products of split terms in increasing size; those below 2^-24 are dropped
+                acc = mfma_bf16(A[0], ub[ks][2], acc);
+                acc = mfma_bf16(A[1], ub[ks][1], acc);
+                acc = mfma_bf16(A[2], ub[ks][0], acc);
+                acc = mfma_bf16(A[0], ub[ks][1], acc);
+                acc = mfma_bf16(A[1], ub[ks][0], acc);
+                acc = mfma_bf16(A[0], ub[ks][0], acc);
+            }
         }
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -564,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int rg = 4 * rr + e, j = 8 * rr + 4 * g + e;
-                acc[rg] = ((mask >> j) & 1u) ? fmaf(z[e], w, acc[rg]) : 0.f;
+                acc[rg] = ((mask >> j) & 1u) ? fmaf(z[e], w, acc[rg] * rs) : 0.f;
             }
         }
         store_tile<OutT>(ot, acc, lane, n, [&](int t) { return dq + ((long long)b * N + tt + t) * hstride + h * kD; });
@@ -584,6 +601,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
             Tile x;
             tile_operand(lds_in, 0, hh, 32 * (wave >> 1) + i, g, x.q0, x.q1);
             if constexpr (kStageDout) {
+                tile_operand(lds_in, 1, hh, 32 * (wave >> 1) + i, g, x.g0, x.g1);
                 x.gr.load_lds(lds_in + kTileTensor + hh * kTileHead + (32 * (wave >> 1) + i) * 64, g);
             } else {
                 const int row = min(tt + i, t1 - 1);

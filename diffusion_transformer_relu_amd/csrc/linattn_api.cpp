@@ -165,7 +165,6 @@ int forward(const void* q, const void* k, const void* v, void* out, int in_dtype
     const size_t k_bytes = extent_bytes(pl.sk, B, N, H, D, es_in);
     const size_t v_bytes = extent_bytes(pl.sv, B, N, H, D, es_in);
     const size_t out_bytes = extent_bytes(pl.so, B, N, H, D, es_out);
-    const size_t in_bytes = std::max(q_bytes, std::max(k_bytes, v_bytes));
     if (overlaps(out, out_bytes, q, q_bytes) || overlaps(out, out_bytes, k, k_bytes) ||
         overlaps(out, out_bytes, v, v_bytes))
         return SANA_ERR_ALIAS;
@@ -178,7 +177,6 @@ int forward(const void* q, const void* k, const void* v, void* out, int in_dtype
             return SANA_ERR_ALIGNMENT;
         if (state_in && (overlaps(state_in, sb, out, out_bytes) || overlaps(state_in, sb, workspace, pl.bytes)))
             return SANA_ERR_ALIAS;
-        (void)in_bytes;
         if (state_out && (overlaps(state_out, sb, q, q_bytes) || overlaps(state_out, sb, k, k_bytes) ||
                           overlaps(state_out, sb, v, v_bytes) || overlaps(state_out, sb, out, out_bytes) ||
                           overlaps(state_out, sb, workspace, pl.bytes) ||

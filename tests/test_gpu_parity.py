@@ -343,3 +343,56 @@ def test_other_head_dims_streaming_and_strided():
     sana.sana_linattn_fwd_strided(qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2], out, ws)
     torch.cuda.synchronize()
     compare(out.cpu().double().numpy(), want, v, False, w2.name)
+
+
+def test_offsets_beyond_2_31_elements():
+    """q, k, v and out of 2^31 + elements each (B=1, N=4M+, H=16, D=32; 20 GB on
+    the device): every offset past 2^31 is computed in 64 bits.  The inputs are
+    drawn on the device from a seeded generator; one head's slice is copied back
+    and checked against the oracle at the last tokens (the largest offsets)."""
+    import diffusion_transformer_relu_amd as sana
+    B, N, H, D = 1, (1 << 22) + 1000, 16, 32
+    gen = torch.Generator(device="cuda:0").manual_seed(2024)
+    q, k, v = (torch.randn((B, N, H, D), device="cuda:0", generator=gen).to(torch.bfloat16) for _ in range(3))
+    assert q.numel() > (1 << 31)
+    out = sana.linattn_fwd(q, k, v)
+    h = H - 1
+    sl = [x[:, :, h:h + 1].contiguous().cpu().view(torch.int16).numpy().view(np.uint16) for x in (q, k, v)]
+    tail = out[:, -64:, h:h + 1].cpu().double().numpy()
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    want = oracle.linattn_fwd(*sl)[:, -64:]
+    compare(tail, want, sl[2], False, "offsets>2^31")
+
+
+def test_concurrent_calls_from_two_threads_on_two_streams():
+    """Calls are re-entrant: two host threads, each with its own stream and
+    workspace, interleave many calls; every result equals the single-threaded one."""
+    import threading
+
+    import diffusion_transformer_relu_amd as sana
+    ws_ = [workloads.Workload(f"thr{t}", 2, 3000, 7, 32, workloads.DT_BF16, seed=130 + t, block_len=512 * t)
+           for t in range(2)]
+    ins = [[to_device(x) for x in workloads.make_inputs(w)] for w in ws_]
+    ref = [sana.linattn_fwd(*ins[t], block_len=ws_[t].block_len or None) for t in range(2)]
+    torch.cuda.synchronize()
+    results, errors = [[], []], []
+
+    def worker(t):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for _ in range(20):
+                    results[t].append(sana.linattn_fwd(*ins[t], block_len=ws_[t].block_len or None, stream=st))
+            st.synchronize()
+        except Exception as e:   # noqa: BLE001 - reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    for t in range(2):
+        assert len(results[t]) == 20 and all(torch.equal(r, ref[t]) for r in results[t])

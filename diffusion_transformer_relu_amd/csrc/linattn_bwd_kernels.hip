@@ -193,8 +193,10 @@ __device__ __forceinline__ void mma_split_lds(const OperandLds& o, int hh, int l
 // [tensor][head][token][32 x 16 bit]; the second head's rows are shifted by 64
 // bytes so that both heads' 16-byte writes of one token use different banks.
 constexpr int kTileTok = 64;
-constexpr int kTileHead = kTileTok * 64 + 64;   // bytes per head
-constexpr int kTileTensor = 2 * kTileHead;      // bytes per tensor
+constexpr int kTileRow = 80;                       // bytes per token row: 64 + 16 keeps 16-byte reads of
+                                                   // 8 consecutive rows in distinct banks
+constexpr int kTileHead = kTileTok * kTileRow + 64;   // bytes per head
+constexpr int kTileTensor = 2 * kTileHead;            // bytes per tensor
 
 struct TileLoader {
     const uint16_t* x[2];   // the two tensors (the second may be null: one tensor only)
@@ -227,7 +229,7 @@ struct TileLoader {
         for (int pi = 0; pi < 2; ++pi) {
             const int pc = threadIdx.x + kThreads * pi;
             const int part = pc & 3, hd = (pc >> 2) & 1, tok = pc >> 3;
-            const int o = hd * kTileHead + tok * 64 + part * 16;
+            const int o = hd * kTileHead + tok * kTileRow + part * 16;
 #pragma unroll
             for (int ts = 0; ts < 2; ++ts) {
                 if (ts == 1 && !x[1]) break;
@@ -237,11 +239,27 @@ struct TileLoader {
     }
 };
 
+// Bit r (r = 0..15) set when feature 8 (r / 4) + 4 g + r % 4 of a staged
+// 16-bit row is > 0: the accumulator rows of lane (g, i) for token i.
+__device__ __forceinline__ uint32_t positive_rows(const uint8_t* row, int g) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(row + 16 * rr + 8 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const short hv = (short)((e & 1) ? (x[e >> 1] >> 16) : (x[e >> 1] & 0xffffu));
+            m |= (uint32_t)(hv > 0) << (4 * rr + e);
+        }
+    }
+    return m;
+}
+
 // B operand of token `tok` of a staged tile: lane (g, i) gets features 8g..8g+7
 // and 16+8g..16+8g+7 of tensor ts, head hh.
 __device__ __forceinline__ void tile_operand(const uint8_t* lds, int ts, int hh, int tok, int g, u32x4& x0,
                                              u32x4& x1) {
-    const uint8_t* row = lds + ts * kTileTensor + hh * kTileHead + tok * 64 + 16 * g;
+    const uint8_t* row = lds + ts * kTileTensor + hh * kTileHead + tok * kTileRow + 16 * g;
     x0 = *reinterpret_cast<const u32x4*>(row);
     x1 = *reinterpret_cast<const u32x4*>(row + 32);
 }
@@ -301,7 +319,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
         tile_operand(lds, 0, hh, 32 * th + i, g, k0, k1);
         tile_operand(lds, 1, hh, 32 * th + i, g, v0, v1);
         const u32x4 a0 = relu_bf16x8(k0), a1 = relu_bf16x8(k1);
-        const uint32_t mask = nonzero_mask(a0, a1, g);
+        const uint32_t mask = positive_rows(lds + hh * kTileHead + (32 * th + i) * kTileRow, g);
 
         f32x16 acc = {};
         acc = mma_split<F16>(gt, a0, a1, acc);
@@ -310,15 +328,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
         acc = (f32x16){};
         acc = mma_split<F16>(gn, v0, v1, acc);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int j = 8 * (r >> 2) + 4 * g + (r & 3);
-            acc[r] = ((mask >> j) & 1u) ? acc[r] + gz[r] : 0.f;
-        }
+        for (int r = 0; r < 16; ++r) acc[r] = ((mask >> r) & 1u) ? acc[r] + gz[r] : 0.f;
         store_tile<OutT>(ot, acc, lane, n, [&](int t) { return dk + ((long long)b * N + tt + t) * hstride + h * kD; });
     }
 }
 
 // ------------------------------------------------------------------ query pass, matrix cores
+constexpr int kFRow = 40;   // 16-bit elements per f tile row: 32 + 8 (80 bytes, as kTileRow)
 // Upstream gradient of one token in the accumulator layout: lane (g, i) gets
 // features 8 rr + 4 g .. + 3 (rr = 0..3) of its token.
 template <typename GT> struct GradRow;
@@ -383,7 +399,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
     __shared__ OperandLds opnd;                                     // P, both layouts, both heads
     __shared__ __attribute__((aligned(16))) float pzs[2][32];       // P[:, D] of each head
     __shared__ __attribute__((aligned(16))) float ut[4][32 * kPitch];   // u tile, then the dq tile
-    __shared__ __attribute__((aligned(16))) uint16_t ft[4][32 * 32];    // f tile (16-bit bits)
+    __shared__ __attribute__((aligned(16))) uint16_t ft[4][32 * kFRow];  // f tile (16-bit bits), padded rows
     __shared__ float wv[4][32];                                     // w of each token
     __shared__ __attribute__((aligned(16))) uint8_t lds_in[2 * kTileTensor];   // staged q (and 16-bit dout)
 
@@ -426,6 +442,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
     struct Tile {
         u32x4 q0, q1;
         u32x4 g0, g1;      // 16-bit dout in the operand layout (staged dout only)
+        uint32_t mask;     // q > 0 at this lane's accumulator rows
         GradRow<GT> gr;
     };
     constexpr bool kStageDout = sizeof(GT) == 2;   // 16-bit dout is staged with q; fp32 dout is read per wave
@@ -433,9 +450,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
         asm volatile("" ::: "memory");   // keep the LDS operands in LDS (see the key kernel)
         const int n = min(32, t1 - tt);
         const u32x4 f0 = relu_bf16x8(x.q0), f1 = relu_bf16x8(x.q1);
-        const uint32_t mask = nonzero_mask(f0, f1, g);
-        *reinterpret_cast<u32x4*>(fw + i * 32 + 8 * g) = f0;
-        *reinterpret_cast<u32x4*>(fw + i * 32 + 16 + 8 * g) = f1;
+        const uint32_t mask = x.mask;
+        *reinterpret_cast<u32x4*>(fw + i * kFRow + 8 * g) = f0;
+        *reinterpret_cast<u32x4*>(fw + i * kFRow + 16 + 8 * g) = f1;
 
         // numerators and the normaliser
         f32x16 acc = {};
@@ -480,58 +497,22 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
         __builtin_amdgcn_wave_barrier();
         asm volatile("" ::: "memory");   // phase boundary: keeps each phase's LDS reads in its phase
 
-        // G += f^T [u | w]: lane (g, c) gathers tokens 16 ks + 8 g + e
+        // G_v += f^T u on fp32 MFMA (32 x 32 x 2: token pair m, lane (g, x)
+        // supplies f and u of token 2 m + g at feature x), G_z += f^T w on
+        // the vector unit; tokens past the range are skipped
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            float uu[8], ww[8];
-            u32x4 af;
-            // unconditional reads from one base per lane (immediate offsets),
-            // then tokens past the range are zeroed
-            const float* ob = ot + (16 * ks + 8 * g) * kPitch + i;
-            const float* wb = wl + 16 * ks + 8 * g;
-            const uint16_t* fb = fw + (16 * ks + 8 * g) * 32 + i;
-            const int nv = n - (16 * ks + 8 * g);   // valid tokens among this lane's 8
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float uv = ob[e * kPitch], wvv = wb[e];
-                uu[e] = e < nv ? uv : 0.f;
-                ww[e] = e < nv ? wvv : 0.f;
-            }
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const uint32_t lo = fb[(2 * d) * 32], hi = fb[(2 * d + 1) * 32];
-                af[d] = (2 * d < nv ? lo : 0u) | ((2 * d + 1 < nv ? hi : 0u) << 16);
-            }
-            u32x4 bu[3];
-            split3_trunc_f32x8(uu, bu);
-            if constexpr (F16) {
-                u32x4 fhi, flo;
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    uint32_t hv, lv;
-                    float f0_, f1_;
-                    split_f16x2(af[d], hv, lv, f0_, f1_);
-                    fhi[d] = hv;
-                    flo[d] = lv;
-                    gz_acc = fmaf(f0_, ww[2 * d], gz_acc);
-                    gz_acc = fmaf(f1_, ww[2 * d + 1], gz_acc);
-                }
-#pragma unroll
-                for (int sp = 2; sp >= 0; --sp) accG = mfma_bf16(flo, bu[sp], accG);
-#pragma unroll
-                for (int sp = 2; sp >= 0; --sp) accG = mfma_bf16(fhi, bu[sp], accG);
-            } else {
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    gz_acc = fmaf(lo_bf16(af[d]), ww[2 * d], gz_acc);
-                    gz_acc = fmaf(hi_bf16(af[d]), ww[2 * d + 1], gz_acc);
-                }
-#pragma unroll
-                for (int sp = 2; sp >= 0; --sp) accG = mfma_bf16(af, bu[sp], accG);
-            }
+        for (int m = 0; m < 16; ++m) {
+            const int tok = 2 * m + g;
+            const bool ok = tok < n;
+            const uint16_t fb = fw[tok * kFRow + i];
+            const float fv = F16 ? f16_to_f32(fb) : bf16_to_f32(fb);
+            const float uv = ot[tok * kPitch + i];
+            const float wv_ = wl[tok];
+            const float fa = ok ? fv : 0.f;
+            accG = __builtin_amdgcn_mfma_f32_32x32x2f32(fa, ok ? uv : 0.f, accG, 0, 0, 0);
+            gz_acc = fmaf(fa, ok ? wv_ : 0.f, gz_acc);
         }
 
-        asm volatile("" ::: "memory");
         acc = (f32x16){};
         float rs = 1.f;   // per-token factor of the MFMA result
         if constexpr (kStageDout) {
@@ -580,8 +561,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
             const f32x4 z = *reinterpret_cast<const f32x4*>(&pzs[hh][8 * rr + 4 * g]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int rg = 4 * rr + e, j = 8 * rr + 4 * g + e;
-                acc[rg] = ((mask >> j) & 1u) ? fmaf(z[e], w, acc[rg] * rs) : 0.f;
+                const int rg = 4 * rr + e;
+                acc[rg] = ((mask >> rg) & 1u) ? fmaf(z[e], w, acc[rg] * rs) : 0.f;
             }
         }
         store_tile<OutT>(ot, acc, lane, n, [&](int t) { return dq + ((long long)b * N + tt + t) * hstride + h * kD; });
@@ -600,9 +581,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
             if (!active || tt >= t1) continue;
             Tile x;
             tile_operand(lds_in, 0, hh, 32 * (wave >> 1) + i, g, x.q0, x.q1);
+            x.mask = positive_rows(lds_in + hh * kTileHead + (32 * (wave >> 1) + i) * kTileRow, g);
             if constexpr (kStageDout) {
                 tile_operand(lds_in, 1, hh, 32 * (wave >> 1) + i, g, x.g0, x.g1);
-                x.gr.load_lds(lds_in + kTileTensor + hh * kTileHead + (32 * (wave >> 1) + i) * 64, g);
+                x.gr.load_lds(lds_in + kTileTensor + hh * kTileHead + (32 * (wave >> 1) + i) * kTileRow, g);
             } else {
                 const int row = min(tt + i, t1 - 1);
                 x.gr.load(dout + ((long long)b * N + row) * hstride + h * kD, g);

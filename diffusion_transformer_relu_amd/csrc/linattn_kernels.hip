@@ -261,16 +261,16 @@ template <bool F16, typename OutT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(F16 ? 4 : 5, 8))) void k_apply_mfma(
     const uint16_t* __restrict__ q, const float* __restrict__ state, OutT* __restrict__ out,
     int N, int H, int HP, int L, int NB, int tile, int tpb, float eps, Strides sq, Strides so) {
-    __shared__ __attribute__((aligned(16))) float otile[4][32 * kOutPitch];
+    __shared__ __attribute__((aligned(16))) float otile[4][32 * kOutPitch];   // fp32 out only
 
     const int per_unit = NB * tpb;
     const int tau = blockIdx.x % per_unit;
     const int bhp = blockIdx.x / per_unit;
     const int hp = bhp % HP, b = bhp / HP;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int h = 2 * hp + (wave & 1);
+    const int hh = wave & 1, h = 2 * hp + hh;
     const int sub = wave >> 1;
-    if (h >= H) return;
+    const int hs = min(h, H - 1);   // a missing second head works on the first (never stored)
     const int beta = tau / tpb, tib = tau - beta * tpb;
     const int blk0 = beta * L;
     const int blk1 = min(blk0 + L, N);
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(F16 ? 
     const int g = lane >> 5, i = lane & 31;
     // A operand: lane (g, c = i), element e of (ks, split) = split term of
     // S[16 ks + 8 g + e][c]; sden: this lane's 16 normaliser entries.
-    const float* S = state + (((size_t)b * H + h) * NB + beta) * kStateFloats;
+    const float* S = state + (((size_t)b * H + hs) * NB + beta) * kStateFloats;
     u32x4 sa[2][3];
     float sden[16];
 #pragma unroll
@@ -306,24 +306,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(F16 ? 
         }
     }
 
+    // fp32 out: rows past the range read as zero and are not stored.  16-bit
+    // out: they are clamped to the range's last row, so every load is
+    // unconditional, and a clamped row's output equals the last row's (it is
+    // stored there again, with the same bits).
     auto load_b = [&](int tt, u32x4& x0, u32x4& x1) {
-        const int row = tt + i;
-        if (row < t1) {
-            const u32x4* src = reinterpret_cast<const u32x4*>(q + (b * sq.b + row * sq.n + h * kD + 8 * g));
+        if constexpr (sizeof(OutT) == 4) {
+            const int row = tt + i;
+            if (row < t1) {
+                const u32x4* src = reinterpret_cast<const u32x4*>(q + (b * sq.b + row * sq.n + h * kD + 8 * g));
+                x0 = src[0];
+                x1 = src[2];
+            } else {
+                x0 = (u32x4){0u, 0u, 0u, 0u};
+                x1 = (u32x4){0u, 0u, 0u, 0u};
+            }
+        } else {
+            const int row = min(tt + i, t1 - 1);
+            const u32x4* src = reinterpret_cast<const u32x4*>(q + (b * sq.b + row * sq.n + hs * kD + 8 * g));
             x0 = src[0];
             x1 = src[2];
-        } else {
-            x0 = (u32x4){0u, 0u, 0u, 0u};
-            x1 = (u32x4){0u, 0u, 0u, 0u};
         }
     };
-    float* ot = otile[wave];
-    int tt = t0 + 32 * sub;
-    u32x4 a0, a1;
-    load_b(tt, a0, a1);
-    for (; tt < t1; tt += 64) {
-        u32x4 n0, n1;
-        load_b(tt + 64, n0, n1);       // next sub-tile of this wave, in flight during the MFMAs
+    // normalised 32 x 32 output tile of one sub-tile: acc row 8 (r / 4) + 4 g + r % 4, column i
+    auto compute = [&](u32x4 a0, u32x4 a1) -> f32x16 {
         a0 = relu_bf16x8(a0);   // the sign test is the same for fp16
         a1 = relu_bf16x8(a1);
         f32x16 acc = {};
@@ -369,23 +375,94 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(F16 ? 
         }
         const float den = dp + __shfl_xor(dp, 32);   // same sum on lanes i and i + 32
         const float rinv = 1.0f / (den + eps);
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) acc[rg] *= rinv;
+        return acc;
+    };
 
-        // tile row i = token tt + i; lane (g, i) holds columns 8 rr + 4 g .. +3
+    if constexpr (sizeof(OutT) == 4) {
+        // fp32: one head's output row is a whole 128-byte line; each wave
+        // stores its own tile through its LDS tile
+        if (h >= H) return;
+        float* ot = otile[wave];
+        int tt = t0 + 32 * sub;
+        u32x4 a0, a1;
+        load_b(tt, a0, a1);
+        for (; tt < t1; tt += 64) {
+            u32x4 n0, n1;
+            load_b(tt + 64, n0, n1);       // next sub-tile of this wave, in flight during the MFMAs
+            const f32x16 acc = compute(a0, a1);
+            // tile row i = token tt + i; lane (g, i) holds columns 8 rr + 4 g .. +3
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-            *reinterpret_cast<f32x4*>(ot + i * kOutPitch + 8 * rr + 4 * g) =
-                (f32x4){acc[4 * rr] * rinv, acc[4 * rr + 1] * rinv, acc[4 * rr + 2] * rinv, acc[4 * rr + 3] * rinv};
-        __builtin_amdgcn_wave_barrier();
-        // each store: 8 rows x 8 lanes x 4 columns = 8 whole output rows of this head
+            for (int rr = 0; rr < 4; ++rr)
+                *reinterpret_cast<f32x4*>(ot + i * kOutPitch + 8 * rr + 4 * g) =
+                    (f32x4){acc[4 * rr], acc[4 * rr + 1], acc[4 * rr + 2], acc[4 * rr + 3]};
+            __builtin_amdgcn_wave_barrier();
+            // each store: 8 rows x 8 lanes x 4 columns = 8 whole output rows of this head
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-            const int r = 8 * s4 + (lane >> 3), cc = (lane & 7) * 4;
-            const f32x4 x = *reinterpret_cast<const f32x4*>(ot + r * kOutPitch + cc);
-            if (tt + r < t1) store4(out + (b * so.b + (tt + r) * so.n + h * kD + cc), x);
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const int r = 8 * s4 + (lane >> 3), cc = (lane & 7) * 4;
+                const f32x4 x = *reinterpret_cast<const f32x4*>(ot + r * kOutPitch + cc);
+                if (tt + r < t1) store4(out + (b * so.b + (tt + r) * so.n + h * kD + cc), x);
+            }
+            __builtin_amdgcn_wave_barrier();
+            a0 = n0;
+            a1 = n1;
         }
-        __builtin_amdgcn_wave_barrier();
-        a0 = n0;
-        a1 = n1;
+    } else {
+        // 16-bit: both heads of a token share one 128-byte output line.  The
+        // two waves of a sub-tile write their rows into a shared LDS tile and
+        // then store whole lines; all waves take the same number of steps
+        // (a step past the range works on the clamped last row).
+        constexpr int kCt = 68;   // 16-bit elements per row: 64 + 4 (136 bytes) spreads the banks
+        __shared__ __attribute__((aligned(16))) uint16_t ct[2][32 * kCt];
+        const int nh = min(2, H - 2 * hp);
+        const int steps = (t1 - t0 + 63) / 64;
+        int tt = t0 + 32 * sub;
+        u32x4 a0, a1;
+        load_b(tt, a0, a1);
+        for (int st = 0; st < steps; ++st, tt += 64) {
+            u32x4 n0, n1;
+            load_b(tt + 64, n0, n1);
+            const f32x16 acc = compute(a0, a1);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                f32x4 x4 = {acc[4 * rr], acc[4 * rr + 1], acc[4 * rr + 2], acc[4 * rr + 3]};
+                uint16_t* dst = &ct[sub][i * kCt + hh * 32 + 8 * rr + 4 * g];
+                if constexpr (std::is_same<OutT, _Float16>::value) {
+                    // pin the fp32 quotient: otherwise the multiply and the
+                    // narrowing fuse into one mixed-precision FMA that rounds
+                    // once, and the fp16 output would no longer be the fp32
+                    // output rounded
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(x4[e]));
+                    const uint32_t p0 = __builtin_bit_cast(uint16_t, (_Float16)x4[0]) |
+                                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x4[1]) << 16);
+                    const uint32_t p1 = __builtin_bit_cast(uint16_t, (_Float16)x4[2]) |
+                                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x4[3]) << 16);
+                    *reinterpret_cast<u32x2*>(dst) = (u32x2){p0, p1};
+                } else {
+                    const uint32_t p0 = (uint32_t)f32_to_bf16(x4[0]) | ((uint32_t)f32_to_bf16(x4[1]) << 16);
+                    const uint32_t p1 = (uint32_t)f32_to_bf16(x4[2]) | ((uint32_t)f32_to_bf16(x4[3]) << 16);
+                    *reinterpret_cast<u32x2*>(dst) = (u32x2){p0, p1};
+                }
+            }
+            __syncthreads();
+            // wave (sub, hh) stores rows 16 hh .. 16 hh + 15 of its sub-tile:
+            // 8 lanes x 16 bytes per 128-byte line (both heads)
+            // (rows past the range repeat the last row, with its bits)
+#pragma unroll
+            for (int k8 = 0; k8 < 2; ++k8) {
+                const int r = 16 * hh + 8 * k8 + (lane >> 3), chunk = lane & 7;
+                const u32x4 x = *reinterpret_cast<const u32x4*>(&ct[sub][r * kCt + chunk * 8]);
+                const int grow = min(tt + r, t1 - 1);
+                if (chunk < 4 * nh)
+                    __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(out + (b * so.b + grow * so.n + 2 * hp * kD + chunk * 8)));
+            }
+            __syncthreads();
+            a0 = n0;
+            a1 = n1;
+        }
     }
 }
 

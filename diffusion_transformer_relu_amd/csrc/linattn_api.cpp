@@ -215,11 +215,16 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
     const Plan& pl = bp->fw;
     bp->key_mfma = bp->query_mfma = pl.mfma;
     if (pl.mfma) {
-        // about one round of work-groups (head pairs x tiles; 3 per CU fit the
-        // key kernel's registers and LDS), tiles of 64 tokens
+        // one round of work-groups each (head pairs x tiles, tiles multiples
+        // of 64 tokens): the key kernel's registers and LDS fit 3 work-groups
+        // per CU, the query kernel's 2
         const long units = (long)B * pl.HP * pl.NB;
-        const long per_block = std::max<long>(1, sana::kCUs * 3 / units);
-        bp->tk = bp->tq = (int)std::min<long>(round_up(ceil_div(pl.L, per_block), 64), round_up(pl.L, 64));
+        auto tile_for = [&](long per_cu) {
+            const long per_block = std::max<long>(1, sana::kCUs * per_cu / units);
+            return (int)std::min<long>(round_up(ceil_div(pl.L, per_block), 64), round_up(pl.L, 64));
+        };
+        bp->tk = tile_for(3);
+        bp->tq = tile_for(2);
     } else {
         bp->tk = bp->tq = kBwdTile;
     }

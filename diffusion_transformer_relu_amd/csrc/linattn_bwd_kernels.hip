@@ -101,10 +101,16 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_valu(
 
 // ------------------------------------------------------------------ suffix merge
 // grid.x = (b * H + h) * kGroups + m; thread t owns entry e = m * 256 + t.
-// For beta = NB-1 down to 0: the block's tile partials are summed (groups of 8
-// loads in flight, a fixed pairwise tree) and added to the running suffix sum,
-// which is written as Ghat of block beta.
+// For beta = NB-1 down to 0: the block's tile partials are summed (in groups
+// of 8 added as a fixed pairwise tree, the groups in order) and added to the
+// running suffix sum, which is written as Ghat of block beta.  The loads of up
+// to 16 partials are issued together (the kernel is a few load round trips
+// long).
 constexpr int kGroups = (kStateFloats + kThreads - 1) / kThreads;
+
+__device__ __forceinline__ float tree8(const float* x) {
+    return ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+}
 
 __global__ __launch_bounds__(kThreads) void k_bwd_merge_suffix(const float* __restrict__ gpart,
                                                                 float* __restrict__ ghat, int NB, int tpb) {
@@ -114,17 +120,45 @@ __global__ __launch_bounds__(kThreads) void k_bwd_merge_suffix(const float* __re
     const float* src = gpart + bh * NB * tpb * kStateFloats + e;
     float* dst = ghat + bh * NB * kStateFloats + e;
     float acc = 0.f;
-    for (int beta = NB - 1; beta >= 0; --beta) {
-        const float* blk = src + (size_t)beta * tpb * kStateFloats;
-        float bs = 0.f;
-        for (int s0 = 0; s0 < tpb; s0 += 8) {
-            float x[8];
+    if (tpb == 1) {
+        // one partial per block: 16 blocks' loads at once, last block first
+        for (int b1 = NB; b1 > 0; b1 -= 16) {
+            float x[16];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = (s0 + i < tpb) ? blk[(size_t)(s0 + i) * kStateFloats] : 0.f;
-            bs += ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+            for (int i = 0; i < 16; ++i) x[i] = (b1 - 1 - i >= 0) ? src[(size_t)(b1 - 1 - i) * kStateFloats] : 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (b1 - 1 - i >= 0) {
+                    acc += 0.f + x[i];   // the block sum of one partial, as the general path forms it
+                    dst[(size_t)(b1 - 1 - i) * kStateFloats] = acc;
+                }
+            }
         }
-        acc += bs;
-        dst[(size_t)beta * kStateFloats] = acc;
+    } else if (tpb <= 16) {
+        for (int beta = NB - 1; beta >= 0; --beta) {
+            const float* blk = src + (size_t)beta * tpb * kStateFloats;
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[i] = (i < tpb) ? blk[(size_t)i * kStateFloats] : 0.f;
+            float bs = 0.f;
+            bs += tree8(x);
+            if (tpb > 8) bs += tree8(x + 8);
+            acc += bs;
+            dst[(size_t)beta * kStateFloats] = acc;
+        }
+    } else {
+        for (int beta = NB - 1; beta >= 0; --beta) {
+            const float* blk = src + (size_t)beta * tpb * kStateFloats;
+            float bs = 0.f;
+            for (int s0 = 0; s0 < tpb; s0 += 8) {
+                float x[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[i] = (s0 + i < tpb) ? blk[(size_t)(s0 + i) * kStateFloats] : 0.f;
+                bs += tree8(x);
+            }
+            acc += bs;
+            dst[(size_t)beta * kStateFloats] = acc;
+        }
     }
 }
 
@@ -277,7 +311,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ ghat,
     OutT* __restrict__ dk, OutT* __restrict__ dv, int N, int H, int HP, int L, int NB, int tile, int tpb) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kTileTensor];
-    __shared__ __attribute__((aligned(16))) float otile[4][32 * kPitch];
+    __shared__ __attribute__((aligned(16))) float otile[4][32 * kPitch];                // fp32 out
+    __shared__ __attribute__((aligned(16))) uint16_t ctile[2][2][32 * kPairRow];        // 16-bit out: [half][dv, dk]
 
     const int per_unit = NB * tpb;
     const int tau = blockIdx.x % per_unit;
@@ -314,22 +349,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
 
         const int tt = tt0 + 32 * th;   // first key of this wave's half
         const int n = min(32, t1 - tt);
-        if (n <= 0 || h >= H) continue;
+        if constexpr (sizeof(OutT) == 4) {
+            if (n <= 0 || h >= H) continue;
+        }
+        // (16-bit out: every wave computes, so that the work-group barrier
+        // below is reached by all; rows past the range hold the clamped last
+        // row and a missing head computes on zeros, never stored)
         u32x4 k0, k1, v0, v1;
         tile_operand(lds, 0, hh, 32 * th + i, g, k0, k1);
         tile_operand(lds, 1, hh, 32 * th + i, g, v0, v1);
         const u32x4 a0 = relu_bf16x8(k0), a1 = relu_bf16x8(k1);
         const uint32_t mask = positive_rows(lds + hh * kTileHead + (32 * th + i) * kTileRow, g);
 
-        f32x16 acc = {};
-        acc = mma_split<F16>(gt, a0, a1, acc);
-        store_tile<OutT>(ot, acc, lane, n, [&](int t) { return dv + ((long long)b * N + tt + t) * hstride + h * kD; });
-
-        acc = (f32x16){};
-        acc = mma_split<F16>(gn, v0, v1, acc);
+        f32x16 accv = {};
+        accv = mma_split<F16>(gt, a0, a1, accv);
+        f32x16 acck = {};
+        acck = mma_split<F16>(gn, v0, v1, acck);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = ((mask >> r) & 1u) ? acc[r] + gz[r] : 0.f;
-        store_tile<OutT>(ot, acc, lane, n, [&](int t) { return dk + ((long long)b * N + tt + t) * hstride + h * kD; });
+        for (int r = 0; r < 16; ++r) acck[r] = ((mask >> r) & 1u) ? acck[r] + gz[r] : 0.f;
+        if constexpr (sizeof(OutT) == 4) {
+            store_tile<OutT>(ot, accv, lane, n, [&](int t) { return dv + ((long long)b * N + tt + t) * hstride + h * kD; });
+            store_tile<OutT>(ot, acck, lane, n, [&](int t) { return dk + ((long long)b * N + tt + t) * hstride + h * kD; });
+        } else {
+            // both heads of a key share a 128-byte line of dk and of dv
+            put_pair_tile<OutT>(ctile[th][0], accv, lane, hh);
+            put_pair_tile<OutT>(ctile[th][1], acck, lane, hh);
+            __syncthreads();
+            // wave (th, hh) stores rows 16 hh .. 16 hh + 15 of its half; rows
+            // past the range repeat the last row (same bits)
+            auto row = [&](OutT* base) {
+                return [=](int r) {
+                    return reinterpret_cast<uint16_t*>(base + ((long long)b * N + min(tt + r, t1 - 1)) * hstride + 2 * hp * kD);
+                };
+            };
+            store_pair_rows<OutT>(ctile[th][0], lane, 16 * hh, nh, row(dv));
+            store_pair_rows<OutT>(ctile[th][1], lane, 16 * hh, nh, row(dk));
+            // the next tile's first barrier keeps the pair tiles until these reads are done
+        }
     }
 }
 

@@ -4,6 +4,8 @@
 
 #include "linattn_internal.h"
 
+#include <type_traits>
+
 namespace sana {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -242,6 +244,51 @@ __device__ __forceinline__ void store_tile(float* ot, const f32x16& acc, int lan
         store4(dst(min(r, n - 1)) + cc, x);
     }
     __builtin_amdgcn_wave_barrier();
+}
+
+// ------------------------------------------------------------------ 16-bit head-pair output lines
+// With 16-bit outputs one head's row is half a 128-byte line.  The two waves
+// of a head pair therefore write their tiles into one shared LDS tile
+// [32 tokens][kPairRow] (head hh in elements 32 hh .. 32 hh + 31 of each row),
+// and after a work-group barrier the rows are stored as whole lines.
+constexpr int kPairRow = 68;   // 16-bit elements per row: 64 + 4 (136 bytes) spreads the banks
+
+// acc of lane (g, i): token i, features 8 (r / 4) + 4 g + r % 4, rounded to
+// OutT (nearest-even) into head hh's half of the pair tile.
+template <typename OutT>
+__device__ __forceinline__ void put_pair_tile(uint16_t* ct, const f32x16& acc, int lane, int hh) {
+    const int g = lane >> 5, i = lane & 31;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        f32x4 x = {acc[4 * rr], acc[4 * rr + 1], acc[4 * rr + 2], acc[4 * rr + 3]};
+        uint32_t p0, p1;
+        if constexpr (std::is_same<OutT, _Float16>::value) {
+            // pin the fp32 values: otherwise a multiply that produced them and
+            // the narrowing can fuse into one mixed-precision FMA that rounds
+            // once, and the result would no longer be the fp32 value rounded
+#pragma unroll
+            for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(x[e]));
+            p0 = __builtin_bit_cast(uint16_t, (_Float16)x[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x[1]) << 16);
+            p1 = __builtin_bit_cast(uint16_t, (_Float16)x[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x[3]) << 16);
+        } else {
+            p0 = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+            p1 = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+        }
+        *reinterpret_cast<u32x2*>(ct + i * kPairRow + hh * 32 + 8 * rr + 4 * g) = (u32x2){p0, p1};
+    }
+}
+
+// Rows r0 .. r0 + 15 of a pair tile as whole lines: 8 lanes x 16 bytes per
+// row; dst(r) points at the head pair's first element of row r's token; only
+// the first nh heads are written.
+template <typename OutT, typename RowPtr>
+__device__ __forceinline__ void store_pair_rows(const uint16_t* ct, int lane, int r0, int nh, RowPtr dst) {
+#pragma unroll
+    for (int k8 = 0; k8 < 2; ++k8) {
+        const int r = r0 + 8 * k8 + (lane >> 3), chunk = lane & 7;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(ct + r * kPairRow + chunk * 8);
+        if (chunk < 4 * nh) __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(dst(r) + chunk * 8));
+    }
 }
 
 }  // namespace sana

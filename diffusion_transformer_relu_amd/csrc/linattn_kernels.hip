@@ -207,11 +207,16 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_valu(
 // grid.x = (b * H + h) * groups + m, groups = ceil(SF / kMergeThreads); thread
 // t owns state entry e = m * kMergeThreads + t of the SF = D (D + 1) entries.
 // Starting from the carried state (or zero), for each block it sums that
-// block's chunk partials (groups of 8 loads in flight, added as a fixed
-// pairwise tree), and adds the block sum to the running state (inclusive
+// block's chunk partials (in groups of 8 added as a fixed pairwise tree, the
+// groups in order), and adds the block sum to the running state (inclusive
 // prefix over blocks); the final running state is the carried state out.
-// state_in and state_out may be the same array: each thread reads its own
-// entry before it writes it.
+// The kernel is a few load round trips long, so the loads of up to 16
+// partials are issued together.  state_in and state_out may be the same
+// array: each thread reads its own entry before it writes it.
+__device__ __forceinline__ float tree8(const float* x) {
+    return ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+}
+
 __global__ __launch_bounds__(kMergeThreads) void k_merge(
     const float* __restrict__ part, float* __restrict__ state, const float* state_in, float* state_out,
     int NB, int cpb, int P, int SF) {
@@ -222,19 +227,45 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(
     const float* src = part + bh * P * SF + e;
     float* dst = state + bh * NB * SF + e;
     float acc = state_in ? state_in[bh * SF + e] : 0.f;
-#pragma unroll 4
-    for (int beta = 0; beta < NB; ++beta) {
-        const float* blk = src + (size_t)beta * cpb * SF;
-        float bs = 0.f;
-        for (int s0 = 0; s0 < cpb; s0 += 8) {
-            float x[8];
+    if (cpb == 1) {
+        // one partial per block (the block-causal case): 16 blocks' loads at once
+        for (int b0 = 0; b0 < NB; b0 += 16) {
+            float x[16];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                x[i] = (s0 + i < cpb) ? blk[(size_t)(s0 + i) * SF] : 0.f;
-            bs += ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+            for (int i = 0; i < 16; ++i) x[i] = (b0 + i < NB) ? src[(size_t)(b0 + i) * SF] : 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (b0 + i < NB) {
+                    acc += 0.f + x[i];   // the block sum of one partial, as the general path forms it
+                    dst[(size_t)(b0 + i) * SF] = acc;
+                }
+            }
         }
-        acc += bs;
-        dst[(size_t)beta * SF] = acc;
+    } else if (cpb <= 16) {
+        for (int beta = 0; beta < NB; ++beta) {
+            const float* blk = src + (size_t)beta * cpb * SF;
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[i] = (i < cpb) ? blk[(size_t)i * SF] : 0.f;
+            float bs = 0.f;
+            bs += tree8(x);
+            if (cpb > 8) bs += tree8(x + 8);
+            acc += bs;
+            dst[(size_t)beta * SF] = acc;
+        }
+    } else {
+        for (int beta = 0; beta < NB; ++beta) {
+            const float* blk = src + (size_t)beta * cpb * SF;
+            float bs = 0.f;
+            for (int s0 = 0; s0 < cpb; s0 += 8) {
+                float x[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[i] = (s0 + i < cpb) ? blk[(size_t)(s0 + i) * SF] : 0.f;
+                bs += tree8(x);
+            }
+            acc += bs;
+            dst[(size_t)beta * SF] = acc;
+        }
     }
     if (state_out) state_out[bh * SF + e] = acc;
 }

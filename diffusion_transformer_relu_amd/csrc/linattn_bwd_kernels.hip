@@ -556,17 +556,31 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
         // G_v += f^T u on fp32 MFMA (32 x 32 x 2: token pair m, lane (g, x)
         // supplies f and u of token 2 m + g at feature x), G_z += f^T w on
         // the vector unit; tokens past the range are skipped
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            const int tok = 2 * m + g;
-            const bool ok = tok < n;
+        auto gather = [&](int tok, float& fv, float& uv, float& wv_) {
             const uint16_t fb = fw[tok * kFRow + i];
-            const float fv = F16 ? f16_to_f32(fb) : bf16_to_f32(fb);
-            const float uv = ot[tok * kPitch + i];
-            const float wv_ = wl[tok];
-            const float fa = ok ? fv : 0.f;
-            accG = __builtin_amdgcn_mfma_f32_32x32x2f32(fa, ok ? uv : 0.f, accG, 0, 0, 0);
-            gz_acc = fmaf(fa, ok ? wv_ : 0.f, gz_acc);
+            fv = F16 ? f16_to_f32(fb) : bf16_to_f32(fb);
+            uv = ot[tok * kPitch + i];
+            wv_ = wl[tok];
+        };
+        if (n == 32) {   // a whole sub-tile (every one but a range's last)
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                float fv, uv, wv_;
+                gather(2 * m + g, fv, uv, wv_);
+                accG = __builtin_amdgcn_mfma_f32_32x32x2f32(fv, uv, accG, 0, 0, 0);
+                gz_acc = fmaf(fv, wv_, gz_acc);
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const int tok = 2 * m + g;
+                const bool ok = tok < n;
+                float fv, uv, wv_;
+                gather(tok, fv, uv, wv_);
+                const float fa = ok ? fv : 0.f;
+                accG = __builtin_amdgcn_mfma_f32_32x32x2f32(fa, ok ? uv : 0.f, accG, 0, 0, 0);
+                gz_acc = fmaf(fa, ok ? wv_ : 0.f, gz_acc);
+            }
         }
 
         acc = (f32x16){};

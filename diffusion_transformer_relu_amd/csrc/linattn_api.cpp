@@ -215,13 +215,28 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
     const Plan& pl = bp->fw;
     bp->key_mfma = bp->query_mfma = pl.mfma;
     if (pl.mfma) {
-        // one round of work-groups each (head pairs x tiles, tiles multiples
-        // of 64 tokens): the key kernel's registers and LDS fit 3 work-groups
-        // per CU, the query kernel's 2
+        // Tiles (multiples of 64 tokens inside one block) for the (batch, head
+        // pair, block) units: the key kernel's registers and LDS fit 3
+        // work-groups per CU, the query kernel's 2.  The tile count per block
+        // minimises rounds of work-groups x (tile + 64), the 64 tokens
+        // standing for a work-group's prologue and epilogue: one round when
+        // the units allow it, else short tiles that fill the last round.
         const long units = (long)B * pl.HP * pl.NB;
         auto tile_for = [&](long per_cu) {
-            const long per_block = std::max<long>(1, sana::kCUs * per_cu / units);
-            return (int)std::min<long>(round_up(ceil_div(pl.L, per_block), 64), round_up(pl.L, 64));
+            const long slots = sana::kCUs * per_cu;
+            const long max_tile = round_up(pl.L, 64);
+            const long pb_max = std::min<long>(ceil_div(pl.L, 64), 4 * slots / units + 1);
+            long best = max_tile, best_cost = LONG_MAX;
+            for (long pb = 1; pb <= pb_max; ++pb) {
+                const long tile = std::min<long>(round_up(ceil_div(pl.L, pb), 64), max_tile);
+                const long rounds = (units * ceil_div(pl.L, tile) + slots - 1) / slots;
+                const long cost = rounds * (tile + 64);
+                if (cost < best_cost) {
+                    best_cost = cost;
+                    best = tile;
+                }
+            }
+            return (int)best;
         };
         bp->tk = tile_for(3);
         bp->tq = tile_for(2);

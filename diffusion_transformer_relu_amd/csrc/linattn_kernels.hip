@@ -441,12 +441,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(F16 ? 
             a1 = n1;
         }
     } else {
-        // 16-bit: both heads of a token share one 128-byte output line.  The
-        // two waves of a sub-tile write their rows into a shared LDS tile and
-        // then store whole lines; all waves take the same number of steps
-        // (a step past the range works on the clamped last row).
-        constexpr int kCt = 68;   // 16-bit elements per row: 64 + 4 (136 bytes) spreads the banks
-        __shared__ __attribute__((aligned(16))) uint16_t ct[2][32 * kCt];
+        // 16-bit: both heads of a token share one 128-byte output line; the
+        // two waves of a sub-tile fill a pair tile and then store whole lines.
+        // All waves take the same number of steps (a step past the range
+        // works on the clamped last row).
+        __shared__ __attribute__((aligned(16))) uint16_t ct[2][32 * kPairRow];
         const int nh = min(2, H - 2 * hp);
         const int steps = (t1 - t0 + 63) / 64;
         int tt = t0 + 32 * sub;
@@ -456,40 +455,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(F16 ? 
             u32x4 n0, n1;
             load_b(tt + 64, n0, n1);
             const f32x16 acc = compute(a0, a1);
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                f32x4 x4 = {acc[4 * rr], acc[4 * rr + 1], acc[4 * rr + 2], acc[4 * rr + 3]};
-                uint16_t* dst = &ct[sub][i * kCt + hh * 32 + 8 * rr + 4 * g];
-                if constexpr (std::is_same<OutT, _Float16>::value) {
-                    // pin the fp32 quotient: otherwise the multiply and the
-                    // narrowing fuse into one mixed-precision FMA that rounds
-                    // once, and the fp16 output would no longer be the fp32
-                    // output rounded
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(x4[e]));
-                    const uint32_t p0 = __builtin_bit_cast(uint16_t, (_Float16)x4[0]) |
-                                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x4[1]) << 16);
-                    const uint32_t p1 = __builtin_bit_cast(uint16_t, (_Float16)x4[2]) |
-                                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x4[3]) << 16);
-                    *reinterpret_cast<u32x2*>(dst) = (u32x2){p0, p1};
-                } else {
-                    const uint32_t p0 = (uint32_t)f32_to_bf16(x4[0]) | ((uint32_t)f32_to_bf16(x4[1]) << 16);
-                    const uint32_t p1 = (uint32_t)f32_to_bf16(x4[2]) | ((uint32_t)f32_to_bf16(x4[3]) << 16);
-                    *reinterpret_cast<u32x2*>(dst) = (u32x2){p0, p1};
-                }
-            }
+            put_pair_tile<OutT>(ct[sub], acc, lane, hh);
             __syncthreads();
-            // wave (sub, hh) stores rows 16 hh .. 16 hh + 15 of its sub-tile:
-            // 8 lanes x 16 bytes per 128-byte line (both heads)
+            // wave (sub, hh) stores rows 16 hh .. 16 hh + 15 of its sub-tile
             // (rows past the range repeat the last row, with its bits)
-#pragma unroll
-            for (int k8 = 0; k8 < 2; ++k8) {
-                const int r = 16 * hh + 8 * k8 + (lane >> 3), chunk = lane & 7;
-                const u32x4 x = *reinterpret_cast<const u32x4*>(&ct[sub][r * kCt + chunk * 8]);
-                const int grow = min(tt + r, t1 - 1);
-                if (chunk < 4 * nh)
-                    __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(out + (b * so.b + grow * so.n + 2 * hp * kD + chunk * 8)));
-            }
+            store_pair_rows<OutT>(ct[sub], lane, 16 * hh, nh, [&](int r) {
+                return reinterpret_cast<uint16_t*>(out + (b * so.b + min(tt + r, t1 - 1) * so.n + 2 * hp * kD));
+            });
             __syncthreads();
             a0 = n0;
             a1 = n1;

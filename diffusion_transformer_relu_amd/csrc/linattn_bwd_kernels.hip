@@ -438,12 +438,15 @@ template <> struct GradRow<_Float16> {
 // grid.x = (b * HP + hp) * (NB * tpb) + beta * tpb + tile.  Wave w handles head
 // 2*hp + (w & 1) and every other 32-query sub-tile (w >> 1).  Per sub-tile,
 // with f = ReLU(q) and P the block's state:
-//   num^T = P_v^T f^T (A = P transposed, B = f from HBM); den = f . P[:, D] in
-//   fp32; r = 1 / (den + eps); u = dout r; w = -r (dout . num r)
-//   dq^T = P_v u^T + P[:, D] w, masked by q > 0 (A = P natural, B = u as three
-//   bf16 terms read back from the wave's LDS tile; terms below 2^-24 dropped)
-//   G_v += f^T u  (tokens are the reduction dimension: f and u gathered from
-//   the LDS tiles, u split exactly into three bf16 terms by truncation)
+//   num^T = P_v^T f^T (A = P transposed, B = f from the staged q tile);
+//   den = f . P[:, D] in fp32; r = 1 / (den + eps); u = dout r;
+//   w = -r (dout . num r)
+//   dq^T = P_v u^T + P[:, D] w, masked by q > 0 (A = P natural; B = the
+//   16-bit dout, exact, with r applied per token, or for fp32 dout u read
+//   back from the wave's LDS tile as three bf16 terms, products below 2^-24
+//   dropped)
+//   G_v += f^T u  (fp32 MFMA 32x32x2, tokens as the reduction dimension, two
+//   per instruction: f and u gathered from the LDS tiles)
 //   G_z += f^T w  (an fp32 dot product per lane on the vector unit)
 // The two waves of a head then add their G in a fixed order and write the
 // tile's partial gradient state.

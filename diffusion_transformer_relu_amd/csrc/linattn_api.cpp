@@ -216,8 +216,8 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
     bp->key_mfma = bp->query_mfma = pl.mfma;
     if (pl.mfma) {
         // Tiles (multiples of 64 tokens inside one block) for the (batch, head
-        // pair, block) units: the key kernel's registers and LDS fit 3
-        // work-groups per CU, the query kernel's 2.  The tile count per block
+        // pair, block) units: the key and query kernels' registers and LDS
+        // fit 3 work-groups per CU.  The tile count per block
         // minimises rounds of work-groups x (tile + 64), the 64 tokens
         // standing for a work-group's prologue and epilogue: one round when
         // the units allow it, else short tiles that fill the last round.
@@ -239,7 +239,7 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
             return (int)best;
         };
         bp->tk = tile_for(3);
-        bp->tq = tile_for(2);
+        bp->tq = tile_for(3);
     } else {
         bp->tk = bp->tq = kBwdTile;
     }

@@ -202,22 +202,12 @@ __global__ __launch_bounds__(kThreads) void k_bwd_key_valu(
     }
 }
 
-// Split-term operands of the two heads of a work-group, kept in LDS (too many
-// to keep in registers next to the streaming tiles): [head][layout][ks][sp]
-// of 64 lanes x 16 bytes, layout 0 = transposed, 1 = natural (state_operands).
+// Split-term operands of P (natural layout, state_operands) of the two heads
+// of a work-group, kept in LDS (too many to keep in registers next to the
+// streaming tiles): [head][ks][sp] of 64 lanes x 16 bytes.
 struct OperandLds {
-    u32x4 v[2][2][2][3][64];
+    u32x4 v[2][2][3][64];
 };
-
-__device__ __forceinline__ void mma_split_lds(const OperandLds& o, int hh, int lay, int lane, u32x4 b0, u32x4 b1,
-                                              f32x16& acc, bool f16) {
-    u32x4 A[2][3];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int sp = 0; sp < 3; ++sp) A[ks][sp] = o.v[hh][lay][ks][sp][lane];
-    acc = f16 ? mma_split<true>(A, b0, b1, acc) : mma_split<false>(A, b0, b1, acc);
-}
 
 // ------------------------------------------------------------------ input tiles through LDS
 // Two [B][N][H][D] 16-bit tensors, 64 tokens x 2 heads per tile, staged
@@ -286,6 +276,20 @@ __device__ __forceinline__ uint32_t positive_rows(const uint8_t* row, int g) {
             m |= (uint32_t)(hv > 0) << (4 * rr + e);
         }
     }
+    return m;
+}
+
+// The same mask from a row already loaded in the accumulator layout
+// (x[rr] = features 8 rr + 4 g .. + 3).
+__device__ __forceinline__ uint32_t positive_rows(const u32x2 x[4]) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const short hv = (short)((e & 1) ? (x[rr][e >> 1] >> 16) : (x[rr][e >> 1] & 0xffffu));
+            m |= (uint32_t)(hv > 0) << (4 * rr + e);
+        }
     return m;
 }
 
@@ -390,7 +394,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
 }
 
 // ------------------------------------------------------------------ query pass, matrix cores
-constexpr int kFRow = 40;   // 16-bit elements per f tile row: 32 + 8 (80 bytes, as kTileRow)
 // Upstream gradient of one token in the accumulator layout: lane (g, i) gets
 // features 8 rr + 4 g .. + 3 (rr = 0..3) of its token.
 template <typename GT> struct GradRow;
@@ -437,29 +440,30 @@ template <> struct GradRow<_Float16> {
 
 // grid.x = (b * HP + hp) * (NB * tpb) + beta * tpb + tile.  Wave w handles head
 // 2*hp + (w & 1) and every other 32-query sub-tile (w >> 1).  Per sub-tile,
-// with f = ReLU(q) and P the block's state:
-//   num^T = P_v^T f^T (A = P transposed, B = f from the staged q tile);
-//   den = f . P[:, D] in fp32; r = 1 / (den + eps); u = dout r;
-//   w = -r (dout . num r)
-//   dq^T = P_v u^T + P[:, D] w, masked by q > 0 (A = P natural; B = the
-//   16-bit dout, exact, with r applied per token, or for fp32 dout u read
-//   back from the wave's LDS tile as three bf16 terms, products below 2^-24
-//   dropped)
+// with f = ReLU(q), P the block's state, P_v = P[:, :D] and z = P[:, D]:
+//   den = f . z in fp32; r = 1 / (den + eps); u = dout r
+//   m^T = P_v dout^T on MFMA (A = P natural; B = the 16-bit dout, exact, or
+//   for fp32 dout u as three bf16 terms, products below 2^-24 dropped, which
+//   gives m = P_v u = r P_v dout directly)
+//   dout . num = f . (P_v dout) (no numerator product is needed), so
+//   w = -r^2 (f . P_v dout); dq = [q > 0] (r P_v dout + w z)
 //   G_v += f^T u  (fp32 MFMA 32x32x2, tokens as the reduction dimension, two
-//   per instruction: f and u gathered from the LDS tiles)
+//   per instruction: u and w from the wave's LDS tiles, f from the staged q)
 //   G_z += f^T w  (an fp32 dot product per lane on the vector unit)
+// f, the mask and dout are read in the accumulator layout (lane (g, i): token
+// i, features 8 rr + 4 g + e), the layout of the MFMA result.
 // The two waves of a head then add their G in a fixed order and write the
 // tile's partial gradient state.
 template <bool F16, typename GT, typename OutT>
-__global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_bwd_query_mfma(
     const uint16_t* __restrict__ q, const GT* __restrict__ dout, const float* __restrict__ state,
     OutT* __restrict__ dq, float* __restrict__ gpart, int N, int H, int HP, int L, int NB, int tile, int tpb,
     float eps) {
-    __shared__ OperandLds opnd;                                     // P, both layouts, both heads
+    using QT = typename std::conditional<F16, _Float16, uint16_t>::type;
+    __shared__ OperandLds opnd;                                     // P natural split terms, both heads
     __shared__ __attribute__((aligned(16))) float pzs[2][32];       // P[:, D] of each head
     __shared__ __attribute__((aligned(16))) float ut[4][32 * kPitch];   // u tile, then the dq tile
-    __shared__ __attribute__((aligned(16))) uint16_t ft[4][32 * kFRow];  // f tile (16-bit bits), padded rows
-    __shared__ float wv[4][32];                                     // w of each token
+    __shared__ __attribute__((aligned(16))) float wv[4][32];        // w of each token
     __shared__ __attribute__((aligned(16))) uint8_t lds_in[2 * kTileTensor];   // staged q (and 16-bit dout)
 
     const int per_unit = NB * tpb;
@@ -476,16 +480,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
     if (wave < 2 && h < H) {
         const float* Pst = state + (((size_t)b * H + h) * NB + beta) * kStateFloats;
         u32x4 t[2][3];
-        state_operands(Pst, lane, true, t);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int sp = 0; sp < 3; ++sp) opnd.v[hh][0][ks][sp][lane] = t[ks][sp];
         state_operands(Pst, lane, false, t);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int sp = 0; sp < 3; ++sp) opnd.v[hh][1][ks][sp][lane] = t[ks][sp];
+            for (int sp = 0; sp < 3; ++sp) opnd.v[hh][ks][sp][lane] = t[ks][sp];
         if (lane < 32) pzs[hh][lane] = Pst[lane * kW + kD];
     }
     __syncthreads();
@@ -493,58 +492,35 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
     const long long hstride = (long long)H * kD;
     const bool active = h < H && t0 < t1;
     float* ot = ut[wave];
-    uint16_t* fw = ft[wave];
     float* wl = wv[wave];
     f32x16 accG = {};
     float gz_acc = 0.f;   // lane (g, j): sum over this lane's tokens of f_j w
 
     struct Tile {
-        u32x4 q0, q1;
+        GradRow<QT> qa;    // q of this lane's token in the accumulator layout
         u32x4 g0, g1;      // 16-bit dout in the operand layout (staged dout only)
-        uint32_t mask;     // q > 0 at this lane's accumulator rows
-        GradRow<GT> gr;
+        GradRow<GT> gr;    // dout in the accumulator layout
     };
     constexpr bool kStageDout = sizeof(GT) == 2;   // 16-bit dout is staged with q; fp32 dout is read per wave
     auto body = [&](int tt, const Tile& x) {
         asm volatile("" ::: "memory");   // keep the LDS operands in LDS (see the key kernel)
         const int n = min(32, t1 - tt);
-        const u32x4 f0 = relu_bf16x8(x.q0), f1 = relu_bf16x8(x.q1);
-        const uint32_t mask = x.mask;
-        *reinterpret_cast<u32x4*>(fw + i * kFRow + 8 * g) = f0;
-        *reinterpret_cast<u32x4*>(fw + i * kFRow + 16 + 8 * g) = f1;
-
-        // numerators and the normaliser
-        f32x16 acc = {};
-        mma_split_lds(opnd, hh, 0, lane, f0, f1, acc, F16);
+        const uint32_t mask = positive_rows(x.qa.x);
+        // f at this lane's accumulator rows (decoded where used, to keep few
+        // registers live); z = P[:, D] at the same rows
+        auto fa = [&](int rr, int e) { return fmaxf(x.qa.at(rr, e), 0.f); };
+        auto zrow = [&](int rr) { return *reinterpret_cast<const f32x4*>(&pzs[hh][8 * rr + 4 * g]); };
         float dp = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const u32x4 fx = ks ? f1 : f0;
+        for (int rr = 0; rr < 4; ++rr) {
+            const f32x4 z = zrow(rr);
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const int j = 16 * ks + 8 * g + 2 * d;
-                float lo, hi;
-                if constexpr (F16) {
-                    lo = f16_to_f32((uint16_t)(fx[d] & 0xffffu));
-                    hi = f16_to_f32((uint16_t)(fx[d] >> 16));
-                } else {
-                    lo = lo_bf16(fx[d]);
-                    hi = hi_bf16(fx[d]);
-                }
-                dp = fmaf(lo, pzs[hh][j], dp);
-                dp = fmaf(hi, pzs[hh][j + 1], dp);
-            }
+            for (int e = 0; e < 4; ++e) dp = fmaf(fa(rr, e), z[e], dp);
         }
         const float den = dp + __shfl_xor(dp, 32);
         const float r = 1.0f / (den + eps);
-        float go = 0.f;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) go = fmaf(x.gr.at(rr, e), acc[4 * rr + e], go);
-        go += __shfl_xor(go, 32);
-        const float w = -(r * r) * go;
-        // u to the LDS tile (token-major), w to the token vector
+
+        // u to the LDS tile (token-major)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             f32x4 u4;
@@ -552,16 +528,68 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
             for (int e = 0; e < 4; ++e) u4[e] = x.gr.at(rr, e) * r;
             *reinterpret_cast<f32x4*>(ot + i * kPitch + 8 * rr + 4 * g) = u4;
         }
-        if (g == 0) wl[i] = w;
+
+        f32x16 acc = {};
+        float rs;   // per-token factor of the MFMA result: acc * rs = r P_v dout
+        {
+            u32x4 A[2][3];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int sp = 0; sp < 3; ++sp) A[ks][sp] = opnd.v[hh][ks][sp][lane];
+            if constexpr (kStageDout) {
+                acc = mma_split<std::is_same<GT, _Float16>::value>(A, x.g0, x.g1, acc);
+                rs = r;
+            } else {
+                // u read back in the operand layout (channels 16 ks + 8 g ..)
+                // and split into three bf16 terms
+                __builtin_amdgcn_wave_barrier();
+                asm volatile("" ::: "memory");
+                u32x4 ub[2][3];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    float uu[8];
+                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(ot + i * kPitch + 16 * ks + 8 * g);
+                    const f32x4 b4 = *reinterpret_cast<const f32x4*>(ot + i * kPitch + 16 * ks + 8 * g + 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        uu[e] = a4[e];
+                        uu[4 + e] = b4[e];
+                    }
+                    split3_trunc_f32x8(uu, ub[ks]);
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    // products of split terms in increasing size; those below 2^-24 are dropped
+                    acc = mfma_bf16(A[ks][0], ub[ks][2], acc);
+                    acc = mfma_bf16(A[ks][1], ub[ks][1], acc);
+                    acc = mfma_bf16(A[ks][2], ub[ks][0], acc);
+                    acc = mfma_bf16(A[ks][0], ub[ks][1], acc);
+                    acc = mfma_bf16(A[ks][1], ub[ks][0], acc);
+                    acc = mfma_bf16(A[ks][0], ub[ks][0], acc);
+                }
+                rs = 1.f;
+            }
+        }
+        // w = -r (dout . out) = -r (f . acc rs)
+        float go = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) go = fmaf(fa(rr, e), acc[4 * rr + e], go);
+        go += __shfl_xor(go, 32);
+        const float w = -r * (go * rs);
+        if (g == 0) wl[i] = i < n ? w : 0.f;   // 0 past the range: the G_z sum skips those tokens
         __builtin_amdgcn_wave_barrier();
         asm volatile("" ::: "memory");   // phase boundary: keeps each phase's LDS reads in its phase
 
         // G_v += f^T u on fp32 MFMA (32 x 32 x 2: token pair m, lane (g, x)
         // supplies f and u of token 2 m + g at feature x), G_z += f^T w on
         // the vector unit; tokens past the range are skipped
+        const uint8_t* qrows = lds_in + hh * kTileHead + 32 * (wave >> 1) * kTileRow;   // this sub-tile's q rows
         auto gather = [&](int tok, float& fv, float& uv, float& wv_) {
-            const uint16_t fb = fw[tok * kFRow + i];
-            fv = F16 ? f16_to_f32(fb) : bf16_to_f32(fb);
+            const uint16_t fb = *reinterpret_cast<const uint16_t*>(qrows + tok * kTileRow + 2 * i);
+            fv = fmaxf(F16 ? f16_to_f32(fb) : bf16_to_f32(fb), 0.f);
             uv = ot[tok * kPitch + i];
             wv_ = wl[tok];
         };
@@ -580,64 +608,23 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
                 const bool ok = tok < n;
                 float fv, uv, wv_;
                 gather(tok, fv, uv, wv_);
-                const float fa = ok ? fv : 0.f;
-                accG = __builtin_amdgcn_mfma_f32_32x32x2f32(fa, ok ? uv : 0.f, accG, 0, 0, 0);
-                gz_acc = fmaf(fa, ok ? wv_ : 0.f, gz_acc);
+                const float fa_ = ok ? fv : 0.f;
+                accG = __builtin_amdgcn_mfma_f32_32x32x2f32(fa_, ok ? uv : 0.f, accG, 0, 0, 0);
+                gz_acc = fmaf(fa_, ok ? wv_ : 0.f, gz_acc);
             }
         }
 
-        acc = (f32x16){};
-        float rs = 1.f;   // per-token factor of the MFMA result
-        if constexpr (kStageDout) {
-            // dq^T = r (P_v dout^T) + P[:, D] w: the 16-bit dout is an exact
-            // operand, so only P needs split terms
-            u32x4 A[2][3];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int sp = 0; sp < 3; ++sp) A[ks][sp] = opnd.v[hh][1][ks][sp][lane];
-            acc = mma_split<std::is_same<GT, _Float16>::value>(A, x.g0, x.g1, acc);
-            rs = r;
-        } else {
-            // fp32 dout: dq^T = P_v u^T + P[:, D] w, u read back in the operand
-            // layout and split into three bf16 terms
-            u32x4 ub[2][3];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                float uu[8];
-                const f32x4 a4 = *reinterpret_cast<const f32x4*>(ot + i * kPitch + 16 * ks + 8 * g);
-                const f32x4 b4 = *reinterpret_cast<const f32x4*>(ot + i * kPitch + 16 * ks + 8 * g + 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    uu[e] = a4[e];
-                    uu[4 + e] = b4[e];
-                }
-                split3_trunc_f32x8(uu, ub[ks]);
-            }
-            __builtin_amdgcn_wave_barrier();
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                u32x4 A[3];
-#pragma unroll
-                for (int sp = 0; sp < 3; ++sp) A[sp] = opnd.v[hh][1][ks][sp][lane];
-                // products of split terms in increasing size; those below 2^-24 are dropped
-                acc = mfma_bf16(A[0], ub[ks][2], acc);
-                acc = mfma_bf16(A[1], ub[ks][1], acc);
-                acc = mfma_bf16(A[2], ub[ks][0], acc);
-                acc = mfma_bf16(A[0], ub[ks][1], acc);
-                acc = mfma_bf16(A[1], ub[ks][0], acc);
-                acc = mfma_bf16(A[0], ub[ks][0], acc);
-            }
-        }
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-            const f32x4 z = *reinterpret_cast<const f32x4*>(&pzs[hh][8 * rr + 4 * g]);
+            const f32x4 z = zrow(rr);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int rg = 4 * rr + e;
                 acc[rg] = ((mask >> rg) & 1u) ? fmaf(z[e], w, acc[rg] * rs) : 0.f;
             }
         }
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");   // every read of the u tile precedes the dq tile's writes
         store_tile<OutT>(ot, acc, lane, n, [&](int t) { return dq + ((long long)b * N + tt + t) * hstride + h * kD; });
     };
 
@@ -653,8 +640,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_query_mfma(
             const int tt = tt0 + 32 * (wave >> 1);
             if (!active || tt >= t1) continue;
             Tile x;
-            tile_operand(lds_in, 0, hh, 32 * (wave >> 1) + i, g, x.q0, x.q1);
-            x.mask = positive_rows(lds_in + hh * kTileHead + (32 * (wave >> 1) + i) * kTileRow, g);
+            const uint8_t* qrow = lds_in + hh * kTileHead + (32 * (wave >> 1) + i) * kTileRow;
+            x.qa.load_lds(qrow, g);
             if constexpr (kStageDout) {
                 tile_operand(lds_in, 1, hh, 32 * (wave >> 1) + i, g, x.g0, x.g1);
                 x.gr.load_lds(lds_in + kTileTensor + hh * kTileHead + (32 * (wave >> 1) + i) * kTileRow, g);

@@ -46,7 +46,10 @@
  *            sana_linattn_workspace_bytes(); its contents on entry do not
  *            matter.  Two calls that run concurrently must not share a
  *            workspace.  There is no global mutable state; calls are
- *            re-entrant and thread-safe.
+ *            re-entrant and thread-safe.  A call enqueues kernel launches
+ *            only (no memset, copy or event), so it can be recorded into a
+ *            HIP graph by stream capture; replays read the recorded
+ *            buffers' current contents.
  * Errors     Every argument is checked before anything is enqueued; on a
  *            failed check nothing is enqueued and a sana_status_t code is
  *            returned.  The library never aborts or prints.  A launch failure

@@ -99,9 +99,9 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out_dtype: str = "f32") ->
         return copy_bytes / statistics.median([x for x in copies if x >= 0.95 * top])
 
     sf, sw = calib(fetch), calib(write)
-    # bf16 inputs: template argument F16 = false; the apply kernel's second
-    # template argument is the output element type
-    apply_tag = "k_apply_mfma<false, " + ("float>" if out_dtype == "f32" else "unsigned short>")
+    # bf16 inputs: the state kernel's template argument F16 = false; the apply
+    # kernel's template arguments are the input and output element types
+    apply_tag = "k_apply_mfma<unsigned short, " + ("float>" if out_dtype == "f32" else "unsigned short>")
     kernels = {"k_state_partial_mfma": lambda n: "k_state_partial_mfma<false>" in n,
                "k_merge": lambda n: "k_merge" in n,
                "k_apply_mfma": lambda n: apply_tag in n}

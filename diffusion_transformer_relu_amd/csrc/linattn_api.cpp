@@ -38,7 +38,10 @@ int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 long round_up(long a, long m) { return (a + m - 1) / m * m; }
 
 // Decomposition of one call.  Sizes were range-checked by the caller.
-int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block_len, Plan* pl) {
+// f32_mfma: fp32 inputs may use the matrix-core forward kernels (the forward-
+// mode derivative has vector kernels only for them).
+int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block_len, Plan* pl,
+              bool f32_mfma = true) {
     if (B < 0 || H < 0 || N < 0 || D < 1 || block_len < 0) return SANA_ERR_INVALID_ARG;
     if ((in_dtype != SANA_DT_F32 && in_dtype != SANA_DT_BF16 && in_dtype != SANA_DT_F16) ||
         (out_dtype != SANA_DT_F32 && out_dtype != SANA_DT_BF16 && out_dtype != SANA_DT_F16))
@@ -57,7 +60,8 @@ int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block
 
     pl->L = (block_len == 0 || block_len >= N) ? N : block_len;
     pl->NB = ceil_div(N, pl->L);
-    pl->mfma = (in_dtype != SANA_DT_F32 && D == sana::kD && !env_is("SANA_LINATTN_PATH", "valu")) ? 1 : 0;
+    pl->mfma = (D == sana::kD && !env_is("SANA_LINATTN_PATH", "valu") && (in_dtype != SANA_DT_F32 || f32_mfma)) ? 1 : 0;
+    pl->mfma16 = pl->mfma && in_dtype != SANA_DT_F32;
     pl->HP = pl->mfma ? (H + 1) / 2 : H;
     const long units = (long)B * pl->HP * pl->NB;   // independent (b, head unit, block) triples
 
@@ -82,8 +86,8 @@ int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block
         if (tile) {
             tile = (int)round_up(tile, 64);
         } else {
-            // fp16 q runs the apply kernel at 4 waves per SIMD instead of 5
-            const long slots = in_dtype == SANA_DT_F16 ? sana::kApplyGroups * 4 / 5 : sana::kApplyGroups;
+            // fp16 and fp32 q run the apply kernel at 4 waves per SIMD instead of 5
+            const long slots = in_dtype != SANA_DT_BF16 ? sana::kApplyGroups * 4 / 5 : sana::kApplyGroups;
             const long per_block = std::max<long>(1, slots / units);
             tile = (int)round_up(ceil_div(pl->L, per_block), 64);
         }
@@ -213,8 +217,8 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
     bp->grad_dtype = grad_dtype;
     if (B == 0 || H == 0 || N == 0) return SANA_OK;
     const Plan& pl = bp->fw;
-    bp->key_mfma = bp->query_mfma = pl.mfma;
-    if (pl.mfma) {
+    bp->key_mfma = bp->query_mfma = pl.mfma16;
+    if (pl.mfma16) {
         // Tiles (multiples of 64 tokens inside one block) for the (batch, head
         // pair, block) units: the key and query kernels' registers and LDS
         // fit 3 work-groups per CU.  The tile count per block
@@ -312,7 +316,7 @@ int backward(const void* q, const void* k, const void* v, const void* dout, void
 // Forward-mode derivative: the forward's plan with the workspace doubled (a
 // state and a tangent state per head).
 int make_jvp_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block_len, Plan* pl) {
-    const int st = make_plan(in_dtype, out_dtype, B, H, N, D, block_len, pl);
+    const int st = make_plan(in_dtype, out_dtype, B, H, N, D, block_len, pl, false);
     if (st != SANA_OK) return st;
     if (D != sana::kD) return SANA_ERR_UNSUPPORTED;   // the forward-mode derivative is built for D = 32
     if (B == 0 || H == 0 || N == 0) return SANA_OK;
@@ -388,9 +392,9 @@ int sana_linattn_workspace_bytes(int B, int H, int N, int D, int block_len, size
     Plan pl;
     const int st = make_plan(SANA_DT_BF16, SANA_DT_F32, B, H, N, D, block_len, &pl);
     if (st != SANA_OK) return st;
-    // The vector path (fp32 inputs) needs at least as much; report the larger.
+    // The vector path (chosen by SANA_LINATTN_PATH=valu) may need more; report the larger.
     Plan pv;
-    make_plan(SANA_DT_F32, SANA_DT_F32, B, H, N, D, block_len, &pv);
+    make_plan(SANA_DT_F32, SANA_DT_F32, B, H, N, D, block_len, &pv, false);
     *bytes = pl.bytes > pv.bytes ? pl.bytes : pv.bytes;
     return SANA_OK;
 }

@@ -246,6 +246,27 @@ __device__ __forceinline__ void store_tile(float* ot, const f32x16& acc, int lan
     __builtin_amdgcn_wave_barrier();
 }
 
+// ------------------------------------------------------------------ transposing LDS gathers
+// Operand of v_mfma_f32_32x32x16 with tokens as the reduction dimension, from
+// a token-major LDS tile of 16-bit elements (`pitch` per row): lane (g, m)
+// gets tile[row0 + 8 g + e][col0 + m], e = 0..7, packed in pairs.
+// ds_read_b64_tr_b16 works on groups of 16 lanes: lane r of a group supplies
+// the address of 4 consecutive elements (its "row" r), and lane j receives
+// element j % 4 of rows j / 4 + 4 q, q = 0..3.  Row r here is tile row
+// row0 + 8 g + r / 4 (+ 4 for the second read), columns col0 + 16 h + 4 (r % 4)
+// .. + 3, with g and h the group's halves of the wave and of the 32 columns.
+// Addresses must be 8-byte aligned (pitch and col0 multiples of 4).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ u32x4 gather_tokens_t16(const uint16_t* tile, int pitch, int row0, int col0, int lane) {
+    const int grp = lane >> 4, r = lane & 15;
+    const uint16_t* p = tile + (row0 + 8 * (grp >> 1) + (r >> 2)) * pitch + col0 + 16 * (grp & 1) + 4 * (r & 3);
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * pitch));
+    const u32x2 a2 = __builtin_bit_cast(u32x2, a), b2 = __builtin_bit_cast(u32x2, b);
+    return (u32x4){a2[0], a2[1], b2[0], b2[1]};
+}
+
 // ------------------------------------------------------------------ 16-bit head-pair output lines
 // With 16-bit outputs one head's row is half a 128-byte line.  The two waves
 // of a head pair therefore write their tiles into one shared LDS tile

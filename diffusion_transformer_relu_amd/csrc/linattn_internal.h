@@ -44,7 +44,8 @@ struct Plan {
     int P;        // chunks per (b, h) = NB * cpb
     int tile;     // tokens per apply work-group
     int tpb;      // apply work-groups per block
-    int mfma;     // 1: 16-bit-input matrix-core kernels (D = 32), 0: vector kernels
+    int mfma;     // 1: matrix-core forward kernels (D = 32; bf16, fp16 or fp32 inputs), 0: vector kernels
+    int mfma16;   // 1: mfma with 16-bit inputs (the backward and JVP matrix-core kernels need them)
     int D;        // head dim: 32, or 16 / 64 (vector kernels only)
     int in_dtype, out_dtype;
     size_t off_part, off_state, bytes;

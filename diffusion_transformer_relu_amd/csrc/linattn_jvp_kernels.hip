@@ -364,7 +364,7 @@ template <typename F> void by_dtype(int code, F&& f) {
 
 hipError_t launch_jvp_state(const Plan& pl, const void* k, const void* v, const void* kt, const void* vt, float* part,
                             hipStream_t stream) {
-    if (pl.mfma) {
+    if (pl.mfma16) {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.P);
         const uint16_t *k16 = static_cast<const uint16_t*>(k), *v16 = static_cast<const uint16_t*>(v),
                        *kt16 = static_cast<const uint16_t*>(kt), *vt16 = static_cast<const uint16_t*>(vt);
@@ -388,7 +388,7 @@ hipError_t launch_jvp_state(const Plan& pl, const void* k, const void* v, const 
 
 hipError_t launch_jvp_apply(const Plan& pl, const void* q, const void* qt, const float* state, void* out, void* outt,
                             float eps, hipStream_t stream) {
-    if (pl.mfma) {
+    if (pl.mfma16) {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.NB * pl.tpb);
         const uint16_t *q16 = static_cast<const uint16_t*>(q), *qt16 = static_cast<const uint16_t*>(qt);
         by_dtype(pl.out_dtype, [&](auto o) {

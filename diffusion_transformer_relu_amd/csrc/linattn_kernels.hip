@@ -150,6 +150,135 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
     }
 }
 
+// ------------------------------------------------------------------ state, matrix cores, fp32 inputs
+// grid.x = (b * HP + hp) * P + p, as above.  fp32 K and V: each 64-token tile
+// of both heads is loaded as 32-byte pieces (8 features of one head of one
+// token; 8 threads read a token's whole 256-byte head-pair row), K through
+// ReLU, and each value is split by truncation into three bf16 terms
+// (t1 + t2 + t3 = x exactly) staged in LDS as 16-bit term tiles.  Per 16
+// tokens each wave gathers, with transposing LDS reads, 8 tokens of one
+// feature per lane and accumulates
+//   S_v += a_i^T v_j over the term pairs i + j <= 4 (1-based; the dropped
+//          products are below 2^-24 of the exact one)
+//   S_1 += (a_1 + a_2 + a_3)^T 1 (exact)
+// Wave w: head w & 1, token half w >> 1 of each tile.
+constexpr int kF32Tile = 64 * kD;   // 16-bit elements of one term tile [token][feature] of one head
+
+__global__ __launch_bounds__(kThreads) void k_state_partial_mfma_f32(
+    const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ part,
+    int N, int H, int HP, int L, int cpb, int P, int chunk, Strides sk, Strides sv) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][3][2][kF32Tile];   // [tensor][term][head] = 48 KB
+
+    const int p = blockIdx.x % P;
+    const int bhp = blockIdx.x / P;
+    const int hp = bhp % HP, b = bhp / HP;
+    const int h0 = 2 * hp;
+    const int nh = min(2, H - h0);
+    const ChunkRange cr = chunk_range(p, cpb, chunk, L, N);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hh = wave & 1, th = wave >> 1;
+    const int g = lane >> 5, j = lane & 31;
+
+    // piece pc = tid + 256 i: part (pc & 3) = features 8 part .. + 7, head
+    // (pc >> 2) & 1, token pc >> 3
+    f32x4 rk[2][2], rv[2][2];
+    auto load_tile = [&](int t0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int pc = tid + kThreads * i;
+            const int part_ = pc & 3, hd = (pc >> 2) & 1, tok = pc >> 3;
+            const int n = t0 + tok;
+            if (n < cr.c1 && hd < nh) {
+                const long long col = (long long)(h0 + hd) * kD + part_ * 8;
+                const f32x4* ks = reinterpret_cast<const f32x4*>(k + (b * sk.b + n * sk.n + col));
+                const f32x4* vs = reinterpret_cast<const f32x4*>(v + (b * sv.b + n * sv.n + col));
+                rk[i][0] = __builtin_nontemporal_load(ks);
+                rk[i][1] = __builtin_nontemporal_load(ks + 1);
+                rv[i][0] = __builtin_nontemporal_load(vs);
+                rv[i][1] = __builtin_nontemporal_load(vs + 1);
+            } else {
+                rk[i][0] = rk[i][1] = rv[i][0] = rv[i][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    };
+
+    f32x16 accV = {}, accO = {};
+    const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0 pairs
+
+    if (cr.c0 < cr.c1) load_tile(cr.c0);
+    for (int t0 = cr.c0; t0 < cr.c1; t0 += 64) {
+        __syncthreads();   // the previous tile has been consumed
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int pc = tid + kThreads * i;
+            const int part_ = pc & 3, hd = (pc >> 2) & 1, tok = pc >> 3;
+            float a[8], w[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a[e] = fmaxf(rk[i][0][e], 0.f);
+                a[4 + e] = fmaxf(rk[i][1][e], 0.f);
+                w[e] = rv[i][0][e];
+                w[4 + e] = rv[i][1][e];
+            }
+            u32x4 ta[3], tv[3];
+            split3_trunc_f32x8(a, ta);
+            split3_trunc_f32x8(w, tv);
+            const int o = tok * kD + part_ * 8;
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                *reinterpret_cast<u32x4*>(&lds[0][t][hd][o]) = ta[t];
+                *reinterpret_cast<u32x4*>(&lds[1][t][hd][o]) = tv[t];
+            }
+        }
+        __syncthreads();
+        if (t0 + 64 < cr.c1) load_tile(t0 + 64);   // in flight during the MFMAs
+
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const int tb = 32 * th + 16 * st;   // first token of this K-step in the tile
+            u32x4 ta[3], tv[3];
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                ta[t] = gather_tokens_t16(lds[0][t][hh], kD, tb, 0, lane);   // lane (g, j): tokens tb + 8g + e, feature j
+                tv[t] = gather_tokens_t16(lds[1][t][hh], kD, tb, 0, lane);   // lane (g, c): tokens tb + 8g + e, channel c
+            }
+            // smallest products first
+            accV = mfma_bf16(ta[2], tv[0], accV);
+            accV = mfma_bf16(ta[1], tv[1], accV);
+            accV = mfma_bf16(ta[0], tv[2], accV);
+            accV = mfma_bf16(ta[1], tv[0], accV);
+            accV = mfma_bf16(ta[0], tv[1], accV);
+            accV = mfma_bf16(ta[0], tv[0], accV);
+            accO = mfma_bf16(ta[2], ones, accO);
+            accO = mfma_bf16(ta[1], ones, accO);
+            accO = mfma_bf16(ta[0], ones, accO);
+        }
+    }
+
+    // Combine the two token halves of each head in a fixed order, then write.
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(&lds[0][0][0][0]);   // [head][V|O][16][64] floats = 16 KiB
+    if (th == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            red[((hh * 2 + 0) * 16 + r) * 64 + lane] = accV[r];
+            red[((hh * 2 + 1) * 16 + r) * 64 + lane] = accO[r];
+        }
+    }
+    __syncthreads();
+    if (th == 0 && hh < nh) {
+        float* dst = part + (((size_t)b * H + h0 + hh) * P + p) * kStateFloats;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            // accumulator r of lane (g, c) holds row 8*(r/4) + 4*g + r%4, column c
+            const int row = 8 * (r >> 2) + 4 * g + (r & 3);
+            dst[row * kW + j] = accV[r] + red[((hh * 2 + 0) * 16 + r) * 64 + lane];
+            if (j == 0) dst[row * kW + kD] = accO[r] + red[((hh * 2 + 1) * 16 + r) * 64 + lane];
+        }
+    }
+}
+
 // ------------------------------------------------------------------ state, vector path
 // grid.x = (b * H + h) * P + p.  Thread t owns state entries t, t+256, ...
 // Head dim DD (16, 32 or 64): a state is DD x (DD + 1).
@@ -286,12 +415,19 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(
 // that every store instruction writes whole 128-byte output rows.
 constexpr int kOutPitch = 36;   // floats per LDS output row: 32 + 4 keeps rows 16-byte aligned, no bank conflicts
 
-// Occupancy target 5 waves per SIMD (4 for fp16 q, whose exact bf16 split
-// needs a few more registers).
-template <bool F16, typename OutT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(F16 ? 4 : 5, 8))) void k_apply_mfma(
-    const uint16_t* __restrict__ q, const float* __restrict__ state, OutT* __restrict__ out,
+// q is bf16 (InT uint16_t), fp16 or fp32.  A 16-bit q row half is one exact
+// B operand (fp16: split exactly into two bf16 terms); an fp32 q is split by
+// truncation into three bf16 terms and the products of S's and q's terms with
+// i + j <= 4 (1-based) are summed (the dropped ones are below 2^-24 of the
+// exact product).  Occupancy target 5 waves per SIMD (4 for fp16 and fp32 q,
+// whose splits need more registers).
+template <typename InT, typename OutT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(std::is_same<InT, uint16_t>::value ? 5 : 4, 8))) void k_apply_mfma(
+    const InT* __restrict__ q, const float* __restrict__ state, OutT* __restrict__ out,
     int N, int H, int HP, int L, int NB, int tile, int tpb, float eps, Strides sq, Strides so) {
+    constexpr bool F16 = std::is_same<InT, _Float16>::value;
+    constexpr bool F32 = std::is_same<InT, float>::value;
+    constexpr int QW = F32 ? 4 : 2;   // 16-byte pieces of a lane's q features (8 g .. + 7 and 16 + 8 g .. + 7)
     __shared__ __attribute__((aligned(16))) float otile[4][32 * kOutPitch];   // fp32 out only
 
     const int per_unit = NB * tpb;
@@ -341,31 +477,66 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(F16 ? 
     // out: they are clamped to the range's last row, so every load is
     // unconditional, and a clamped row's output equals the last row's (it is
     // stored there again, with the same bits).
-    auto load_b = [&](int tt, u32x4& x0, u32x4& x1) {
+    struct QRow {
+        u32x4 x[QW];
+    };
+    auto load_row = [&](const u32x4* src, QRow& r) {
+        if constexpr (F32) {   // features 8g..8g+7 = src[0..1], 16+8g..16+8g+7 = src[4..5]
+            r.x[0] = src[0];
+            r.x[1] = src[1];
+            r.x[2] = src[4];
+            r.x[3] = src[5];
+        } else {               // features 8g..8g+7 = src[0], 16+8g.. = src[2]
+            r.x[0] = src[0];
+            r.x[1] = src[2];
+        }
+    };
+    auto load_b = [&](int tt, QRow& r) {
         if constexpr (sizeof(OutT) == 4) {
             const int row = tt + i;
             if (row < t1) {
-                const u32x4* src = reinterpret_cast<const u32x4*>(q + (b * sq.b + row * sq.n + h * kD + 8 * g));
-                x0 = src[0];
-                x1 = src[2];
+                load_row(reinterpret_cast<const u32x4*>(q + (b * sq.b + row * sq.n + h * kD + 8 * g)), r);
             } else {
-                x0 = (u32x4){0u, 0u, 0u, 0u};
-                x1 = (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int c = 0; c < QW; ++c) r.x[c] = (u32x4){0u, 0u, 0u, 0u};
             }
         } else {
             const int row = min(tt + i, t1 - 1);
-            const u32x4* src = reinterpret_cast<const u32x4*>(q + (b * sq.b + row * sq.n + hs * kD + 8 * g));
-            x0 = src[0];
-            x1 = src[2];
+            load_row(reinterpret_cast<const u32x4*>(q + (b * sq.b + row * sq.n + hs * kD + 8 * g)), r);
         }
     };
     // normalised 32 x 32 output tile of one sub-tile: acc row 8 (r / 4) + 4 g + r % 4, column i
-    auto compute = [&](u32x4 a0, u32x4 a1) -> f32x16 {
-        a0 = relu_bf16x8(a0);   // the sign test is the same for fp16
-        a1 = relu_bf16x8(a1);
+    auto compute = [&](const QRow& qr) -> f32x16 {
         f32x16 acc = {};
         float dp = 0.f;
-        if constexpr (F16) {
+        if constexpr (F32) {
+            // f = ReLU(q) in fp32 (features 16 ks + 8 g + e at f[8 ks + e])
+            float f[16];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // through a scalar: bit_cast of a vector element expression
+                    // reads the vector's first element with this compiler
+                    const uint32_t bits = qr.x[c][e];
+                    f[4 * c + e] = fmaxf(__builtin_bit_cast(float, bits), 0.f);
+                }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) dp = fmaf(f[e], sden[e], dp);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                u32x4 fb[3];
+                split3_trunc_f32x8(f + 8 * ks, fb);
+                // term pairs (S, q) with i + j <= 4, smallest first
+                acc = mfma_bf16(sa[ks][2], fb[0], acc);
+                acc = mfma_bf16(sa[ks][1], fb[1], acc);
+                acc = mfma_bf16(sa[ks][0], fb[2], acc);
+                acc = mfma_bf16(sa[ks][1], fb[0], acc);
+                acc = mfma_bf16(sa[ks][0], fb[1], acc);
+                acc = mfma_bf16(sa[ks][0], fb[0], acc);
+            }
+        } else if constexpr (F16) {
+            const u32x4 a0 = relu_bf16x8(qr.x[0]), a1 = relu_bf16x8(qr.x[1]);   // the sign test is the same for fp16
             // one 16-feature half at a time (fewer live registers); the
             // normaliser takes the fp32 values as they are split
 #pragma unroll
@@ -388,6 +559,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(F16 ? 
                 for (int sp = 2; sp >= 0; --sp) acc = mfma_bf16(sa[ks][sp], hi, acc);
             }
         } else {
+            const u32x4 a0 = relu_bf16x8(qr.x[0]), a1 = relu_bf16x8(qr.x[1]);
 #pragma unroll
             for (int sp = 2; sp >= 0; --sp) {   // small split terms first
                 acc = mfma_bf16(sa[0][sp], a0, acc);
@@ -417,12 +589,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(F16 ? 
         if (h >= H) return;
         float* ot = otile[wave];
         int tt = t0 + 32 * sub;
-        u32x4 a0, a1;
-        load_b(tt, a0, a1);
+        QRow cur;
+        load_b(tt, cur);
         for (; tt < t1; tt += 64) {
-            u32x4 n0, n1;
-            load_b(tt + 64, n0, n1);       // next sub-tile of this wave, in flight during the MFMAs
-            const f32x16 acc = compute(a0, a1);
+            QRow nxt;
+            load_b(tt + 64, nxt);       // next sub-tile of this wave, in flight during the MFMAs
+            const f32x16 acc = compute(cur);
             // tile row i = token tt + i; lane (g, i) holds columns 8 rr + 4 g .. +3
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
@@ -437,8 +609,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(F16 ? 
                 if (tt + r < t1) store4(out + (b * so.b + (tt + r) * so.n + h * kD + cc), x);
             }
             __builtin_amdgcn_wave_barrier();
-            a0 = n0;
-            a1 = n1;
+            cur = nxt;
         }
     } else {
         // 16-bit: both heads of a token share one 128-byte output line; the
@@ -449,12 +620,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(F16 ? 
         const int nh = min(2, H - 2 * hp);
         const int steps = (t1 - t0 + 63) / 64;
         int tt = t0 + 32 * sub;
-        u32x4 a0, a1;
-        load_b(tt, a0, a1);
+        QRow cur;
+        load_b(tt, cur);
         for (int st = 0; st < steps; ++st, tt += 64) {
-            u32x4 n0, n1;
-            load_b(tt + 64, n0, n1);
-            const f32x16 acc = compute(a0, a1);
+            QRow nxt;
+            load_b(tt + 64, nxt);
+            const f32x16 acc = compute(cur);
             put_pair_tile<OutT>(ct[sub], acc, lane, hh);
             __syncthreads();
             // wave (sub, hh) stores rows 16 hh .. 16 hh + 15 of its sub-tile
@@ -463,8 +634,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(F16 ? 
                 return reinterpret_cast<uint16_t*>(out + (b * so.b + min(tt + r, t1 - 1) * so.n + 2 * hp * kD));
             });
             __syncthreads();
-            a0 = n0;
-            a1 = n1;
+            cur = nxt;
         }
     }
 }
@@ -539,7 +709,11 @@ hipError_t launch_state(const Plan& pl, const void* k, const void* v, float* par
     const uint16_t* v16 = static_cast<const uint16_t*>(v);
     if (pl.mfma) {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.P);
-        if (pl.in_dtype == 2)
+        if (pl.in_dtype == 0)
+            hipLaunchKernelGGL(k_state_partial_mfma_f32, dim3(grid), dim3(kThreads), 0, stream,
+                               static_cast<const float*>(k), static_cast<const float*>(v), part, pl.N, pl.H, pl.HP,
+                               pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
+        else if (pl.in_dtype == 2)
             hipLaunchKernelGGL(k_state_partial_mfma<true>, dim3(grid), dim3(kThreads), 0, stream, k16, v16, part,
                                pl.N, pl.H, pl.HP, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
         else
@@ -573,17 +747,14 @@ hipError_t launch_apply(const Plan& pl, const void* q, const float* state, void*
                         hipStream_t stream) {
     if (pl.mfma) {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.NB * pl.tpb);
-        const uint16_t* q16 = static_cast<const uint16_t*>(q);
-        by_dtype(pl.out_dtype, [&](auto o) {
-            using OT = typename decltype(o)::type;
-            if (pl.in_dtype == 2)
-                hipLaunchKernelGGL((k_apply_mfma<true, OT>), dim3(grid), dim3(kThreads), 0, stream, q16, state,
-                                   static_cast<OT*>(out), pl.N, pl.H, pl.HP, pl.L, pl.NB, pl.tile, pl.tpb, eps,
-                                   pl.sq, pl.so);
-            else
-                hipLaunchKernelGGL((k_apply_mfma<false, OT>), dim3(grid), dim3(kThreads), 0, stream, q16, state,
-                                   static_cast<OT*>(out), pl.N, pl.H, pl.HP, pl.L, pl.NB, pl.tile, pl.tpb, eps,
-                                   pl.sq, pl.so);
+        by_dtype(pl.in_dtype, [&](auto in) {
+            by_dtype(pl.out_dtype, [&](auto o) {
+                using IT = typename decltype(in)::type;
+                using OT = typename decltype(o)::type;
+                hipLaunchKernelGGL((k_apply_mfma<IT, OT>), dim3(grid), dim3(kThreads), 0, stream,
+                                   static_cast<const IT*>(q), state, static_cast<OT*>(out), pl.N, pl.H, pl.HP, pl.L,
+                                   pl.NB, pl.tile, pl.tpb, eps, pl.sq, pl.so);
+            });
         });
     } else {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.H * pl.NB * pl.tpb);

@@ -60,7 +60,8 @@ def test_workspace_and_plan_queries():
     info = sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 70, 16384, 32, 0)
     assert info["mfma"] == 1 and info["chunk_tokens"] % 64 == 0 and info["apply_tokens"] % 64 == 0
     assert info["num_chunks"] * info["chunk_tokens"] >= 16384
-    assert sana.sana_linattn_plan_info(sana.SANA_DT_F32, 1, 2, 256, 32, 0)["mfma"] == 0
+    assert sana.sana_linattn_plan_info(sana.SANA_DT_F32, 1, 2, 256, 32, 0)["mfma"] == 1   # fp32 in: split terms
+    assert sana.sana_linattn_plan_info(sana.SANA_DT_F32, 1, 2, 256, 64, 0)["mfma"] == 0
     f16 = sana.sana_linattn_plan_info(sana.SANA_DT_F16, 1, 70, 16384, 32, 0)
     assert f16["mfma"] == 1 and f16["apply_tokens"] >= info["apply_tokens"]   # fp16 apply: 4 work-groups per CU
     bc = sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 70, 16384, 32, 1000)

@@ -36,6 +36,21 @@ def test_full_size_configs(w, out_dtype):
     print(f"[gpu] {w.name} {out_dtype}: max_abs={max_abs:.3e} rel_l2={rel:.3e}", flush=True)
 
 
+F32_IN = [workloads.with_shape(workloads.HEADLINE, in_dtype=workloads.DT_F32, name="sana1600m_4096px_f32in"),
+          workloads.with_shape(workloads.BLOCK_CAUSAL, in_dtype=workloads.DT_F32, name="blockcausal_16x1024_f32in")]
+
+
+@pytest.mark.parametrize("w", F32_IN, ids=lambda w: w.name)
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["f32out", "bf16out"])
+def test_full_size_fp32_inputs(w, out_dtype):
+    """fp32 q, k, v at the bench shapes: the matrix-core kernels on three-term
+    bf16 splits of the inputs."""
+    (q, k, v), want = inputs_and_oracle(w)
+    got = run_hip(q, k, v, block_len=w.block_len, eps=w.eps, out_dtype=out_dtype)
+    max_abs, rel = compare(got, want, v, out_dtype == torch.bfloat16, w.name)
+    print(f"[gpu] {w.name} {out_dtype}: max_abs={max_abs:.3e} rel_l2={rel:.3e}", flush=True)
+
+
 EDGE = [
     # (B, N, H, block_len, in_dtype)
     (1, 1, 1, 0, workloads.DT_BF16),

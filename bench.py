@@ -381,6 +381,21 @@ def main() -> int:
             "note": "the headline inputs converted to fp16 on the device"}
         del sets16
 
+        # fp32 inputs (the same values widened on the device), same out dtype:
+        # 12 bytes more per token-head of input
+        sets32 = [[t.float() for t in st] for st in sets]
+
+        def f32(i):
+            q, k, v = sets32[i % NSETS]
+            sana.sana_linattn_fwd(q, k, v, outs[i % NSETS], ws, eps=w.eps, stream=stream)
+        ms = timed(f32, args.steps)
+        bytes32 = w.token_heads * D * (3 * 4 + out_bytes)
+        extra["f32_in_" + args.out_dtype + "out"] = {
+            "ms_per_step": round(ms, 5), "GBps": round(bytes32 / ms / 1e6, 1),
+            "pct_hbm_peak": round(100 * bytes32 / ms / 1e6 / HBM_PEAK_GBPS, 2),
+            "note": "the headline inputs widened to fp32 on the device; algorithmic bytes with 4-byte inputs"}
+        del sets32
+
         # backward (dq, dk, dv) of the same forward: bf16 q, k, v, dout -> bf16 gradients
         grads = [[torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev) for _ in range(3)]
                  for _ in range(NSETS)]

@@ -35,7 +35,8 @@
  *            activations overflow.  A bf16 or fp16 out is the fp32 result
  *            rounded to nearest-even (outputs lie within the range of V, so an
  *            fp16 out cannot overflow).  D is 32 (the Sana head dim, on the matrix
- *            cores for 16-bit inputs) or, for the forward entry points, 16 or 64
+ *            cores; fp32 inputs as three-term bf16 splits with the products
+ *            below 2^-24 dropped) or, for the forward entry points, 16 or 64
  *            (vector-unit kernels); the backward and the forward-mode
  *            derivative take D = 32.
  * Memory     Every pointer is device memory on the current HIP device, owned

@@ -72,7 +72,9 @@ int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block
     if (chunk) {
         chunk = (int)round_up(chunk, 64);
     } else {
-        const long slots = sana::kStateGroups;
+        // fp32 inputs on the matrix cores: their state kernel holds 3 work-
+        // groups per CU and streams best with one full round of them
+        const long slots = (pl->mfma && in_dtype == SANA_DT_F32) ? sana::kCUs * 3 : sana::kStateGroups;
         const long per_block = std::max<long>(1, slots / units);
         chunk = (int)std::max<long>(round_up(ceil_div(pl->L, per_block), 64), sana::kMinChunk);
     }
@@ -392,10 +394,12 @@ int sana_linattn_workspace_bytes(int B, int H, int N, int D, int block_len, size
     Plan pl;
     const int st = make_plan(SANA_DT_BF16, SANA_DT_F32, B, H, N, D, block_len, &pl);
     if (st != SANA_OK) return st;
-    // The vector path (chosen by SANA_LINATTN_PATH=valu) may need more; report the larger.
-    Plan pv;
+    // fp32 inputs (their own chunking) and the vector path (SANA_LINATTN_PATH=valu)
+    // may need more; report the largest.
+    Plan pf, pv;
+    make_plan(SANA_DT_F32, SANA_DT_F32, B, H, N, D, block_len, &pf);
     make_plan(SANA_DT_F32, SANA_DT_F32, B, H, N, D, block_len, &pv, false);
-    *bytes = pl.bytes > pv.bytes ? pl.bytes : pv.bytes;
+    *bytes = std::max(pl.bytes, std::max(pf.bytes, pv.bytes));
     return SANA_OK;
 }
 

@@ -219,11 +219,11 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
     bp->grad_dtype = grad_dtype;
     if (B == 0 || H == 0 || N == 0) return SANA_OK;
     const Plan& pl = bp->fw;
-    bp->key_mfma = bp->query_mfma = pl.mfma16;
-    if (pl.mfma16) {
+    bp->key_mfma = bp->query_mfma = pl.mfma;
+    if (pl.mfma) {
         // Tiles (multiples of 64 tokens inside one block) for the (batch, head
         // pair, block) units: the key and query kernels' registers and LDS
-        // fit 3 work-groups per CU.  The tile count per block
+        // fit 3 work-groups per CU (2 for fp32 inputs).  The tile count per block
         // minimises rounds of work-groups x (tile + 64), the 64 tokens
         // standing for a work-group's prologue and epilogue: one round when
         // the units allow it, else short tiles that fill the last round.
@@ -244,8 +244,9 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
             }
             return (int)best;
         };
-        bp->tk = tile_for(3);
-        bp->tq = tile_for(3);
+        const int per_cu = pl.mfma16 ? 3 : 2;
+        bp->tk = tile_for(per_cu);
+        bp->tq = tile_for(per_cu);
     } else {
         bp->tk = bp->tq = kBwdTile;
     }

@@ -293,6 +293,16 @@ __device__ __forceinline__ uint32_t positive_rows(const u32x2 x[4]) {
     return m;
 }
 
+// The same mask from an fp32 row in the accumulator layout.
+__device__ __forceinline__ uint32_t positive_rows(const f32x4 x[4]) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m |= (uint32_t)(x[rr][e] > 0.f) << (4 * rr + e);
+    return m;
+}
+
 // B operand of token `tok` of a staged tile: lane (g, i) gets features 8g..8g+7
 // and 16+8g..16+8g+7 of tensor ts, head hh.
 __device__ __forceinline__ void tile_operand(const uint8_t* lds, int ts, int hh, int tok, int g, u32x4& x0,
@@ -393,6 +403,140 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
     }
 }
 
+// fp32 inputs: features 8g..8g+7 and 16+8g..16+8g+7 of an fp32 row (the B
+// operand layout), 4 x 16 bytes.
+struct F32Operand {
+    f32x4 x[4];
+    __device__ __forceinline__ void load(const float* row, int g) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            x[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 16 * (p >> 1) + 8 * g + 4 * (p & 1)));
+    }
+    // the 8 values of half ks (features 16 ks + 8 g ..), optionally ReLU'd
+    __device__ __forceinline__ void half(int ks, bool relu, float out[8]) const {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float t = x[2 * ks + (e >> 2)][e & 3];
+            out[e] = relu ? fmaxf(t, 0.f) : t;
+        }
+    }
+    // bit j set when feature j of the token is > 0 (the partner lane, i + 32,
+    // holds the other 16 features)
+    __device__ __forceinline__ uint32_t positive(int g) const {
+        uint32_t m = 0;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m |= (uint32_t)(x[p][e] > 0.f) << (16 * (p >> 1) + 8 * g + 4 * (p & 1) + e);
+        return m | (uint32_t)__shfl_xor((int)m, 32);
+    }
+};
+
+// acc += A B over 32 features with A given as three split terms (index 0 the
+// largest) and B as an fp32 operand split here into three truncation terms:
+// the products of terms i + j <= 2, smallest first; the others lie below
+// 2^-24 of the product and are dropped.
+__device__ __forceinline__ f32x16 mma_split3(const u32x4 A[2][3], const F32Operand& b, bool relu, f32x16 acc) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        float x[8];
+        b.half(ks, relu, x);
+        u32x4 t[3];
+        split3_trunc_f32x8(x, t);
+        acc = mfma_bf16(A[ks][0], t[2], acc);
+        acc = mfma_bf16(A[ks][1], t[1], acc);
+        acc = mfma_bf16(A[ks][2], t[0], acc);
+        acc = mfma_bf16(A[ks][0], t[1], acc);
+        acc = mfma_bf16(A[ks][1], t[0], acc);
+        acc = mfma_bf16(A[ks][0], t[0], acc);
+    }
+    return acc;
+}
+
+// The key pass for fp32 k and v: the work-group, waves and sub-tiles of the
+// 16-bit kernel, but each wave reads its own 32 keys straight from global
+// memory in the operand layout (the next sub-tile's loads issued before this
+// one's work), and k, a = ReLU(k) and v enter the MFMAs as three bf16 terms.
+template <typename OutT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_bwd_key_mfma_f32(
+    const float* __restrict__ k, const float* __restrict__ v, const float* __restrict__ ghat,
+    OutT* __restrict__ dk, OutT* __restrict__ dv, int N, int H, int HP, int L, int NB, int tile, int tpb) {
+    __shared__ __attribute__((aligned(16))) float otile[4][32 * kPitch];                // fp32 out
+    __shared__ __attribute__((aligned(16))) uint16_t ctile[2][2][32 * kPairRow];        // 16-bit out: [half][dv, dk]
+
+    const int per_unit = NB * tpb;
+    const int tau = blockIdx.x % per_unit;
+    const int bhp = blockIdx.x / per_unit;
+    const int hp = bhp % HP, b = bhp / HP;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int hh = wave & 1, th = wave >> 1, h = 2 * hp + hh;
+    const int beta = tau / tpb, tib = tau - beta * tpb;
+    const int blk0 = beta * L, blk1 = min(blk0 + L, N);
+    const int t0 = blk0 + tib * tile, t1 = min(t0 + tile, blk1);
+    const int g = lane >> 5, i = lane & 31;
+    const int nh = min(2, H - 2 * hp);
+    if (t0 >= t1) return;   // uniform over the work-group
+
+    const int hs = min(h, H - 1);   // a missing second head computes on the first (never stored)
+    const float* G = ghat + (((size_t)b * H + hs) * NB + beta) * kStateFloats;
+    u32x4 gt[2][3], gn[2][3];
+    state_operands(G, lane, true, gt);
+    state_operands(G, lane, false, gn);
+    float gz[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) gz[r] = G[(8 * (r >> 2) + 4 * g + (r & 3)) * kW + kD];
+
+    const long long hstride = (long long)H * kD;
+    auto row_of = [&](const float* x, int tt) { return x + ((long long)b * N + min(tt + i, t1 - 1)) * hstride + hs * kD; };
+    float* ot = otile[wave];
+    F32Operand kc, vc;
+    kc.load(row_of(k, t0 + 32 * th), g);
+    vc.load(row_of(v, t0 + 32 * th), g);
+    for (int tt0 = t0; tt0 < t1; tt0 += kTileTok) {
+        const int tt = tt0 + 32 * th;   // first key of this wave's half
+        const int n = min(32, t1 - tt);
+        F32Operand kn, vn;
+        const bool more = tt0 + kTileTok < t1;
+        if (more) {   // in flight during this sub-tile's work
+            kn.load(row_of(k, tt + kTileTok), g);
+            vn.load(row_of(v, tt + kTileTok), g);
+        }
+        // (rows past the range hold the clamped last row: with 16-bit outputs
+        // every wave computes, so that the work-group barrier below is reached
+        // by all)
+        if (sizeof(OutT) == 2 || (n > 0 && h < H)) {
+            const uint32_t mask = kc.positive(g);
+            f32x16 accv = {};
+            accv = mma_split3(gt, kc, true, accv);
+            f32x16 acck = {};
+            acck = mma_split3(gn, vc, false, acck);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acck[r] = ((mask >> (8 * (r >> 2) + 4 * g + (r & 3))) & 1u) ? acck[r] + gz[r] : 0.f;
+            if constexpr (sizeof(OutT) == 4) {
+                store_tile<OutT>(ot, accv, lane, n, [&](int t) { return dv + ((long long)b * N + tt + t) * hstride + h * kD; });
+                store_tile<OutT>(ot, acck, lane, n, [&](int t) { return dk + ((long long)b * N + tt + t) * hstride + h * kD; });
+            } else {
+                __syncthreads();   // the previous sub-tile's pair tiles have been stored
+                put_pair_tile<OutT>(ctile[th][0], accv, lane, hh);
+                put_pair_tile<OutT>(ctile[th][1], acck, lane, hh);
+                __syncthreads();
+                auto row = [&](OutT* base) {
+                    return [=](int r) {
+                        return reinterpret_cast<uint16_t*>(base + ((long long)b * N + min(tt + r, t1 - 1)) * hstride + 2 * hp * kD);
+                    };
+                };
+                store_pair_rows<OutT>(ctile[th][0], lane, 16 * hh, nh, row(dv));
+                store_pair_rows<OutT>(ctile[th][1], lane, 16 * hh, nh, row(dk));
+            }
+        }
+        if (more) {
+            kc = kn;
+            vc = vn;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ query pass, matrix cores
 // Upstream gradient of one token in the accumulator layout: lane (g, i) gets
 // features 8 rr + 4 g .. + 3 (rr = 0..3) of its token.
@@ -454,17 +598,21 @@ template <> struct GradRow<_Float16> {
 // i, features 8 rr + 4 g + e), the layout of the MFMA result.
 // The two waves of a head then add their G in a fixed order and write the
 // tile's partial gradient state.
-template <bool F16, typename GT, typename OutT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_bwd_query_mfma(
-    const uint16_t* __restrict__ q, const GT* __restrict__ dout, const float* __restrict__ state,
+template <typename QT, typename GT, typename OutT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(QT) == 2 ? 3 : 2, 8))) void k_bwd_query_mfma(
+    const QT* __restrict__ q, const GT* __restrict__ dout, const float* __restrict__ state,
     OutT* __restrict__ dq, float* __restrict__ gpart, int N, int H, int HP, int L, int NB, int tile, int tpb,
     float eps) {
-    using QT = typename std::conditional<F16, _Float16, uint16_t>::type;
+    // 16-bit q (and 16-bit dout) are staged through LDS by the work-group;
+    // fp32 q is read by each wave straight from global memory, its f = ReLU(q)
+    // kept in an fp32 LDS tile per wave (in the staging area) for the G sums
+    constexpr bool kStage = sizeof(QT) == 2;
     __shared__ OperandLds opnd;                                     // P natural split terms, both heads
     __shared__ __attribute__((aligned(16))) float pzs[2][32];       // P[:, D] of each head
     __shared__ __attribute__((aligned(16))) float ut[4][32 * kPitch];   // u tile, then the dq tile
     __shared__ __attribute__((aligned(16))) float wv[4][32];        // w of each token
     __shared__ __attribute__((aligned(16))) uint8_t lds_in[2 * kTileTensor];   // staged q (and 16-bit dout)
+    static_assert(sizeof(lds_in) >= 4 * 32 * kPitch * sizeof(float), "f tiles exceed the staging area");
 
     const int per_unit = NB * tpb;
     const int tau = blockIdx.x % per_unit;
@@ -498,10 +646,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
 
     struct Tile {
         GradRow<QT> qa;    // q of this lane's token in the accumulator layout
-        u32x4 g0, g1;      // 16-bit dout in the operand layout (staged dout only)
+        u32x4 g0, g1;      // 16-bit dout in the operand layout
         GradRow<GT> gr;    // dout in the accumulator layout
     };
-    constexpr bool kStageDout = sizeof(GT) == 2;   // 16-bit dout is staged with q; fp32 dout is read per wave
+    constexpr bool kDoutOperand = sizeof(GT) == 2;   // 16-bit dout is the B operand as it is
+    float* ft = reinterpret_cast<float*>(lds_in) + wave * 32 * kPitch;   // fp32 q: f tile of this wave
     auto body = [&](int tt, const Tile& x) {
         asm volatile("" ::: "memory");   // keep the LDS operands in LDS (see the key kernel)
         const int n = min(32, t1 - tt);
@@ -520,13 +669,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
         const float den = dp + __shfl_xor(dp, 32);
         const float r = 1.0f / (den + eps);
 
-        // u to the LDS tile (token-major)
+        // u to the LDS tile (token-major); for fp32 q also f
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             f32x4 u4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) u4[e] = x.gr.at(rr, e) * r;
             *reinterpret_cast<f32x4*>(ot + i * kPitch + 8 * rr + 4 * g) = u4;
+            if constexpr (!kStage) {
+                f32x4 f4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) f4[e] = fa(rr, e);
+                *reinterpret_cast<f32x4*>(ft + i * kPitch + 8 * rr + 4 * g) = f4;
+            }
         }
 
         f32x16 acc = {};
@@ -537,7 +692,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int sp = 0; sp < 3; ++sp) A[ks][sp] = opnd.v[hh][ks][sp][lane];
-            if constexpr (kStageDout) {
+            if constexpr (kDoutOperand) {
                 acc = mma_split<std::is_same<GT, _Float16>::value>(A, x.g0, x.g1, acc);
                 rs = r;
             } else {
@@ -588,8 +743,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
         // the vector unit; tokens past the range are skipped
         const uint8_t* qrows = lds_in + hh * kTileHead + 32 * (wave >> 1) * kTileRow;   // this sub-tile's q rows
         auto gather = [&](int tok, float& fv, float& uv, float& wv_) {
-            const uint16_t fb = *reinterpret_cast<const uint16_t*>(qrows + tok * kTileRow + 2 * i);
-            fv = fmaxf(F16 ? f16_to_f32(fb) : bf16_to_f32(fb), 0.f);
+            if constexpr (kStage) {
+                const uint16_t fb = *reinterpret_cast<const uint16_t*>(qrows + tok * kTileRow + 2 * i);
+                fv = fmaxf(std::is_same<QT, _Float16>::value ? f16_to_f32(fb) : bf16_to_f32(fb), 0.f);
+            } else {
+                fv = ft[tok * kPitch + i];
+            }
             uv = ot[tok * kPitch + i];
             wv_ = wl[tok];
         };
@@ -628,9 +787,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
         store_tile<OutT>(ot, acc, lane, n, [&](int t) { return dq + ((long long)b * N + tt + t) * hstride + h * kD; });
     };
 
-    if (t0 < t1) {   // uniform over the work-group
-        const uint16_t* dsrc = kStageDout ? reinterpret_cast<const uint16_t*>(dout) : nullptr;
-        TileLoader ld = {{q, dsrc}, hstride, b, N, 2 * hp, min(2, H - 2 * hp), t1, {}};
+    if constexpr (!kStage) {
+        // fp32 q: each wave reads its sub-tiles' rows itself, the next
+        // sub-tile's loads in flight during this one's work
+        auto load = [&](int tt, Tile& x) {
+            const long long row = ((long long)b * N + min(tt + i, t1 - 1)) * hstride + h * kD;
+            x.qa.load(reinterpret_cast<const float*>(q) + row, g);
+            if constexpr (kDoutOperand) {
+                x.g0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dout + row + 8 * g));
+                x.g1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dout + row + 16 + 8 * g));
+            }
+            x.gr.load(dout + row, g);
+        };
+        if (active && t0 + 32 * (wave >> 1) < t1) {
+            Tile cur;
+            load(t0 + 32 * (wave >> 1), cur);
+            for (int tt = t0 + 32 * (wave >> 1); tt < t1; tt += kTileTok) {
+                Tile nxt;
+                const bool more = tt + kTileTok < t1;
+                if (more) load(tt + kTileTok, nxt);
+                body(tt, cur);
+                if (more) cur = nxt;
+            }
+        }
+    } else if (t0 < t1) {   // uniform over the work-group
+        const uint16_t* dsrc = kDoutOperand ? reinterpret_cast<const uint16_t*>(dout) : nullptr;
+        TileLoader ld = {{reinterpret_cast<const uint16_t*>(q), dsrc}, hstride, b, N, 2 * hp, min(2, H - 2 * hp), t1, {}};
         ld.load(t0);
         for (int tt0 = t0; tt0 < t1; tt0 += kTileTok) {
             __syncthreads();   // the previous tile has been consumed
@@ -642,7 +824,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
             Tile x;
             const uint8_t* qrow = lds_in + hh * kTileHead + (32 * (wave >> 1) + i) * kTileRow;
             x.qa.load_lds(qrow, g);
-            if constexpr (kStageDout) {
+            if constexpr (kDoutOperand) {
                 tile_operand(lds_in, 1, hh, 32 * (wave >> 1) + i, g, x.g0, x.g1);
                 x.gr.load_lds(lds_in + kTileTensor + hh * kTileHead + (32 * (wave >> 1) + i) * kTileRow, g);
             } else {
@@ -696,19 +878,17 @@ hipError_t launch_bwd_query(const BwdPlan& bp, const void* q, const void* dout, 
     const Plan& pl = bp.fw;
     if (bp.query_mfma) {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.NB * bp.tpbq);
-        const uint16_t* q16 = static_cast<const uint16_t*>(q);
         by_dtype(bp.dout_dtype, [&](auto gt) {
             by_dtype(bp.grad_dtype, [&](auto ot) {
                 using GT = typename decltype(gt)::type;
                 using OT = typename decltype(ot)::type;
-                if (pl.in_dtype == 2)
-                    hipLaunchKernelGGL((k_bwd_query_mfma<true, GT, OT>), dim3(grid), dim3(kThreads), 0, stream, q16,
-                                       static_cast<const GT*>(dout), state, static_cast<OT*>(dq), gpart, pl.N, pl.H,
-                                       pl.HP, pl.L, pl.NB, bp.tq, bp.tpbq, eps);
-                else
-                    hipLaunchKernelGGL((k_bwd_query_mfma<false, GT, OT>), dim3(grid), dim3(kThreads), 0, stream, q16,
-                                       static_cast<const GT*>(dout), state, static_cast<OT*>(dq), gpart, pl.N, pl.H,
-                                       pl.HP, pl.L, pl.NB, bp.tq, bp.tpbq, eps);
+                by_dtype(pl.in_dtype, [&](auto it) {
+                    using QT = typename decltype(it)::type;
+                    hipLaunchKernelGGL((k_bwd_query_mfma<QT, GT, OT>), dim3(grid), dim3(kThreads), 0, stream,
+                                       static_cast<const QT*>(q), static_cast<const GT*>(dout), state,
+                                       static_cast<OT*>(dq), gpart, pl.N, pl.H, pl.HP, pl.L, pl.NB, bp.tq, bp.tpbq,
+                                       eps);
+                });
             });
         });
         return hipGetLastError();
@@ -745,7 +925,12 @@ hipError_t launch_bwd_key(const BwdPlan& bp, const void* k, const void* v, const
         const uint16_t* v16 = static_cast<const uint16_t*>(v);
         by_dtype(bp.grad_dtype, [&](auto ot) {
             using OT = typename decltype(ot)::type;
-            if (pl.in_dtype == 2)
+            if (pl.in_dtype == 0)
+                hipLaunchKernelGGL((k_bwd_key_mfma_f32<OT>), dim3(grid), dim3(kThreads), 0, stream,
+                                   static_cast<const float*>(k), static_cast<const float*>(v), ghat,
+                                   static_cast<OT*>(dk), static_cast<OT*>(dv), pl.N, pl.H, pl.HP, pl.L, pl.NB, bp.tk,
+                                   bp.tpbk);
+            else if (pl.in_dtype == 2)
                 hipLaunchKernelGGL((k_bwd_key_mfma<true, OT>), dim3(grid), dim3(kThreads), 0, stream, k16, v16, ghat,
                                    static_cast<OT*>(dk), static_cast<OT*>(dv), pl.N, pl.H, pl.HP, pl.L, pl.NB,
                                    bp.tk, bp.tpbk);

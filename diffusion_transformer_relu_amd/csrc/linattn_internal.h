@@ -70,7 +70,7 @@ struct BwdPlan {
     int dout_dtype, grad_dtype;
     int tq, tpbq, Pq;    // query tile, query tiles per block, query tiles per (b, h)
     int tk, tpbk;        // key tile, key tiles per block
-    int query_mfma, key_mfma;   // 1: matrix-core query / key kernels (16-bit inputs)
+    int query_mfma, key_mfma;   // 1: matrix-core query / key kernels
     size_t off_gpart, off_ghat, bytes;
 };
 

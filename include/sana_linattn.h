@@ -130,7 +130,7 @@ SANA_API int sana_linattn_workspace_bytes(int B, int H, int N, int D, int block_
  *   chunk_tokens  tokens per state-reduction chunk
  *   num_chunks    chunks per (batch, head) across all blocks
  *   apply_tokens  tokens per apply work-group
- *   mfma          1 if the bf16 matrix-core path is used, 0 for the vector path
+ *   mfma          1 if the matrix-core path is used, 0 for the vector path
  * Errors as for sana_linattn_workspace_bytes (in_dtype must be a valid code).
  */
 SANA_API int sana_linattn_plan_info(int in_dtype, int B, int H, int N, int D, int block_len,

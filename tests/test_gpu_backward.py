@@ -71,6 +71,20 @@ def test_backward_full_size(w, grad_t):
     check(run(q, k, v, g, w.block_len, w.eps, grad_t), want, grad_t, w.name)
 
 
+F32_IN = [workloads.with_shape(workloads.HEADLINE, in_dtype=workloads.DT_F32, name="sana1600m_4096px_f32in"),
+          workloads.with_shape(workloads.BLOCK_CAUSAL, in_dtype=workloads.DT_F32, name="blockcausal_16x1024_f32in")]
+
+
+@pytest.mark.parametrize("w", F32_IN, ids=lambda w: w.name)
+@pytest.mark.parametrize("gdt,grad_t", [(workloads.DT_F32, torch.float32), (workloads.DT_BF16, torch.bfloat16)],
+                         ids=["f32dout_f32grad", "bf16dout_bf16grad"])
+def test_backward_full_size_fp32_inputs(w, gdt, grad_t):
+    """fp32 q, k, v: the matrix-core query and key kernels on three-term bf16
+    splits of the inputs, with an fp32 or a 16-bit upstream gradient."""
+    (q, k, v, g), want = case(w, gdt)
+    check(run(q, k, v, g, w.block_len, w.eps, grad_t), want, grad_t, w.name)
+
+
 EDGE = [(2, 33, 3, 0, 1), (1, 257, 2, 64, 1), (3, 1000, 5, 100, 2), (1, 300, 2, 1, 0),
         (1, 4097, 1, 0, 2), (2, 256, 3, 0, 0)]
 

@@ -51,7 +51,14 @@ static_assert(2 * kTensorStride >= 2 * 2 * 16 * 64 * (int)sizeof(float), "reduct
 // grid.x = (b * HP + hp) * P + p; one work-group = one chunk of one head pair.
 // Wave w reduces head (w & 1) over token half (w >> 1) of each 64-token tile.
 // K and V are read once, so their loads are non-temporal.
-template <bool F16>
+//
+// Head dim 64 (D64): a head's row is the 128 bytes a head pair of dim 32
+// takes, so the same tiles hold one head, its two 32-feature halves in place
+// of the two heads (H counts those halves, HP the heads).  The 64 x 65 state
+// is four 32 x 32 blocks: wave w accumulates block (K half w & 1, V half
+// w >> 1) over all tokens of each tile, the waves of V half 0 also the ones
+// column of their K half.
+template <bool F16, bool D64>
 __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ part,
     int N, int H, int HP, int L, int cpb, int P, int chunk, Strides sk, Strides sv) {
@@ -107,6 +114,20 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
         __syncthreads();
         if (t0 + kStateTile < cr.c1) load_tile(t0 + kStateTile);   // in flight during the MFMAs
 
+        if constexpr (D64) {
+            const uint16_t* Kt = reinterpret_cast<const uint16_t*>(lds + hh * kHeadStride);
+            const uint16_t* Vt = reinterpret_cast<const uint16_t*>(lds + kTensorStride + th * kHeadStride);
+            // a token row of one half is 32 contiguous 16-bit values (pitch 32)
+            static_assert(kHeadStride % 8 == 0, "transposing reads need 8-byte aligned rows");
+#pragma unroll
+            for (int st = 0; st < kStateTile / 16; ++st) {
+                const u32x4 a = gather_tokens_t16(Kt, kD, 16 * st, 0, lane);   // lane (g, j): tokens 16 st + 8 g + e, feature j
+                const u32x4 bv = gather_tokens_t16(Vt, kD, 16 * st, 0, lane);
+                accV = mfma16<F16>(a, bv, accV);
+                if (th == 0) accO = mfma16<F16>(a, ones, accO);
+            }
+            continue;
+        }
         const uint16_t* Kt = reinterpret_cast<const uint16_t*>(lds + hh * kHeadStride);
         const uint16_t* Vt = reinterpret_cast<const uint16_t*>(lds + kTensorStride + hh * kHeadStride);
 #pragma unroll
@@ -127,6 +148,18 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
         }
     }
 
+    if constexpr (D64) {
+        // each wave owns its block over the whole chunk
+        constexpr int W64 = 2 * kD + 1;
+        float* dst = part + (((size_t)b * HP + hp) * P + p) * (2 * kD * W64);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = kD * hh + 8 * (r >> 2) + 4 * g + (r & 3);
+            dst[row * W64 + kD * th + j] = accV[r];
+            if (th == 0 && j == 0) dst[row * W64 + 2 * kD] = accO[r];
+        }
+        return;
+    }
     // Combine the two token halves of each head in a fixed order, then write.
     __syncthreads();
     float* red = reinterpret_cast<float*>(lds);   // [head][V|O][16][64] floats = 16 KiB
@@ -420,14 +453,22 @@ constexpr int kOutPitch = 36;   // floats per LDS output row: 32 + 4 keeps rows 
 // truncation into three bf16 terms and the products of S's and q's terms with
 // i + j <= 4 (1-based) are summed (the dropped ones are below 2^-24 of the
 // exact product).  Occupancy target 5 waves per SIMD (4 for fp16 and fp32 q,
-// whose splits need more registers).
-template <typename InT, typename OutT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(std::is_same<InT, uint16_t>::value ? 5 : 4, 8))) void k_apply_mfma(
+// whose splits need more registers; 3 for head dim 64).
+//
+// Head dim 64 (D64, 16-bit q): H counts 32-feature halves of heads and HP the
+// heads; wave w computes output half w & 1 of head hp (columns 32 (w & 1) ..
+// + 31, stored as "head" 2 hp + (w & 1)), reducing over all 64 features of q
+// in four K-steps against the state's column half.
+template <typename InT, typename OutT, bool D64>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D64 ? 3 : std::is_same<InT, uint16_t>::value ? 5 : 4, 8))) void k_apply_mfma(
     const InT* __restrict__ q, const float* __restrict__ state, OutT* __restrict__ out,
     int N, int H, int HP, int L, int NB, int tile, int tpb, float eps, Strides sq, Strides so) {
     constexpr bool F16 = std::is_same<InT, _Float16>::value;
     constexpr bool F32 = std::is_same<InT, float>::value;
-    constexpr int QW = F32 ? 4 : 2;   // 16-byte pieces of a lane's q features (8 g .. + 7 and 16 + 8 g .. + 7)
+    static_assert(!(D64 && F32), "head dim 64 takes 16-bit q");
+    constexpr int KS = D64 ? 4 : 2;   // K-steps of 16 features
+    constexpr int SW = D64 ? 2 * kD + 1 : kW;   // state row
+    constexpr int QW = F32 ? 4 : KS;  // 16-byte pieces of a lane's q features (16 ks + 8 g .. + 7)
     __shared__ __attribute__((aligned(16))) float otile[4][32 * kOutPitch];   // fp32 out only
 
     const int per_unit = NB * tpb;
@@ -448,19 +489,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(std::i
     const int g = lane >> 5, i = lane & 31;
     // A operand: lane (g, c = i), element e of (ks, split) = split term of
     // S[16 ks + 8 g + e][c]; sden: this lane's 16 normaliser entries.
-    const float* S = state + (((size_t)b * H + hs) * NB + beta) * kStateFloats;
-    u32x4 sa[2][3];
-    float sden[16];
+    const float* S = D64 ? state + (((size_t)b * HP + hp) * NB + beta) * (2 * kD * SW) + kD * hh
+                         : state + (((size_t)b * H + hs) * NB + beta) * kStateFloats;
+    const float* Sz = D64 ? S - kD * hh + 2 * kD : S + kD;   // the normaliser column
+    u32x4 sa[KS][3];
+    float sden[8 * KS];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             uint32_t w[3] = {0u, 0u, 0u};
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int row = 16 * ks + 8 * g + 2 * d + half;
-                float r = S[row * kW + i];
-                sden[8 * ks + 2 * d + half] = S[row * kW + kD];
+                float r = S[row * SW + i];
+                sden[8 * ks + 2 * d + half] = Sz[row * SW];
 #pragma unroll
                 for (int sp = 0; sp < 3; ++sp) {   // S = hi + mid + lo, each remainder exact
                     const uint16_t t = f32_to_bf16(r);
@@ -486,23 +529,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(std::i
             r.x[1] = src[1];
             r.x[2] = src[4];
             r.x[3] = src[5];
-        } else {               // features 8g..8g+7 = src[0], 16+8g.. = src[2]
-            r.x[0] = src[0];
-            r.x[1] = src[2];
+        } else {               // features 16 ks + 8g..8g+7 = src[2 ks]
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) r.x[ks] = src[2 * ks];
         }
     };
     auto load_b = [&](int tt, QRow& r) {
         if constexpr (sizeof(OutT) == 4) {
             const int row = tt + i;
             if (row < t1) {
-                load_row(reinterpret_cast<const u32x4*>(q + (b * sq.b + row * sq.n + h * kD + 8 * g)), r);
+                load_row(reinterpret_cast<const u32x4*>(q + (b * sq.b + row * sq.n + (D64 ? 2 * hp : h) * kD + 8 * g)), r);
             } else {
 #pragma unroll
                 for (int c = 0; c < QW; ++c) r.x[c] = (u32x4){0u, 0u, 0u, 0u};
             }
         } else {
             const int row = min(tt + i, t1 - 1);
-            load_row(reinterpret_cast<const u32x4*>(q + (b * sq.b + row * sq.n + hs * kD + 8 * g)), r);
+            load_row(reinterpret_cast<const u32x4*>(q + (b * sq.b + row * sq.n + (D64 ? 2 * hp : hs) * kD + 8 * g)), r);
         }
     };
     // normalised 32 x 32 output tile of one sub-tile: acc row 8 (r / 4) + 4 g + r % 4, column i
@@ -536,12 +579,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(std::i
                 acc = mfma_bf16(sa[ks][0], fb[0], acc);
             }
         } else if constexpr (F16) {
-            const u32x4 a0 = relu_bf16x8(qr.x[0]), a1 = relu_bf16x8(qr.x[1]);   // the sign test is the same for fp16
-            // one 16-feature half at a time (fewer live registers); the
+            // one 16-feature step at a time (fewer live registers); the
             // normaliser takes the fp32 values as they are split
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const u32x4 x = ks ? a1 : a0;
+            for (int ks = 0; ks < KS; ++ks) {
+                const u32x4 x = relu_bf16x8(qr.x[ks]);   // the sign test is the same for fp16
                 u32x4 hi, lo;
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
@@ -559,22 +601,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(std::i
                 for (int sp = 2; sp >= 0; --sp) acc = mfma_bf16(sa[ks][sp], hi, acc);
             }
         } else {
-            const u32x4 a0 = relu_bf16x8(qr.x[0]), a1 = relu_bf16x8(qr.x[1]);
+            u32x4 a[KS];
 #pragma unroll
-            for (int sp = 2; sp >= 0; --sp) {   // small split terms first
-                acc = mfma_bf16(sa[0][sp], a0, acc);
-                acc = mfma_bf16(sa[1][sp], a1, acc);
-            }
+            for (int ks = 0; ks < KS; ++ks) a[ks] = relu_bf16x8(qr.x[ks]);
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                dp = fmaf(lo_bf16(a0[d]), sden[2 * d], dp);
-                dp = fmaf(hi_bf16(a0[d]), sden[2 * d + 1], dp);
-            }
+            for (int sp = 2; sp >= 0; --sp)   // small split terms first
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                dp = fmaf(lo_bf16(a1[d]), sden[8 + 2 * d], dp);
-                dp = fmaf(hi_bf16(a1[d]), sden[8 + 2 * d + 1], dp);
-            }
+                for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16(sa[ks][sp], a[ks], acc);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    dp = fmaf(lo_bf16(a[ks][d]), sden[8 * ks + 2 * d], dp);
+                    dp = fmaf(hi_bf16(a[ks][d]), sden[8 * ks + 2 * d + 1], dp);
+                }
         }
         const float den = dp + __shfl_xor(dp, 32);   // same sum on lanes i and i + 32
         const float rinv = 1.0f / (den + eps);
@@ -713,12 +753,16 @@ hipError_t launch_state(const Plan& pl, const void* k, const void* v, float* par
             hipLaunchKernelGGL(k_state_partial_mfma_f32, dim3(grid), dim3(kThreads), 0, stream,
                                static_cast<const float*>(k), static_cast<const float*>(v), part, pl.N, pl.H, pl.HP,
                                pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
+        else if (pl.D == 2 * kD)   // heads of dim 64 as pairs of 32-feature halves
+            hipLaunchKernelGGL((pl.in_dtype == 2 ? k_state_partial_mfma<true, true> : k_state_partial_mfma<false, true>),
+                               dim3(grid), dim3(kThreads), 0, stream, k16, v16, part, pl.N, 2 * pl.H, pl.HP, pl.L,
+                               pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
         else if (pl.in_dtype == 2)
-            hipLaunchKernelGGL(k_state_partial_mfma<true>, dim3(grid), dim3(kThreads), 0, stream, k16, v16, part,
-                               pl.N, pl.H, pl.HP, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
+            hipLaunchKernelGGL((k_state_partial_mfma<true, false>), dim3(grid), dim3(kThreads), 0, stream, k16, v16,
+                               part, pl.N, pl.H, pl.HP, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
         else
-            hipLaunchKernelGGL(k_state_partial_mfma<false>, dim3(grid), dim3(kThreads), 0, stream, k16, v16, part,
-                               pl.N, pl.H, pl.HP, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
+            hipLaunchKernelGGL((k_state_partial_mfma<false, false>), dim3(grid), dim3(kThreads), 0, stream, k16, v16,
+                               part, pl.N, pl.H, pl.HP, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
     } else {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.H * pl.P);
         by_dtype(pl.in_dtype, [&](auto in) {
@@ -751,7 +795,15 @@ hipError_t launch_apply(const Plan& pl, const void* q, const float* state, void*
             by_dtype(pl.out_dtype, [&](auto o) {
                 using IT = typename decltype(in)::type;
                 using OT = typename decltype(o)::type;
-                hipLaunchKernelGGL((k_apply_mfma<IT, OT>), dim3(grid), dim3(kThreads), 0, stream,
+                if constexpr (sizeof(IT) == 2) {
+                    if (pl.D == 2 * kD) {   // heads of dim 64 as pairs of 32-feature halves
+                        hipLaunchKernelGGL((k_apply_mfma<IT, OT, true>), dim3(grid), dim3(kThreads), 0, stream,
+                                           static_cast<const IT*>(q), state, static_cast<OT*>(out), pl.N, 2 * pl.H,
+                                           pl.HP, pl.L, pl.NB, pl.tile, pl.tpb, eps, pl.sq, pl.so);
+                        return;
+                    }
+                }
+                hipLaunchKernelGGL((k_apply_mfma<IT, OT, false>), dim3(grid), dim3(kThreads), 0, stream,
                                    static_cast<const IT*>(q), state, static_cast<OT*>(out), pl.N, pl.H, pl.HP, pl.L,
                                    pl.NB, pl.tile, pl.tpb, eps, pl.sq, pl.so);
             });

@@ -317,13 +317,19 @@ HEAD_DIMS = [
     workloads.Workload("d16_B1_N4096_H72_L1024_f16", 1, 4096, 72, 16, workloads.DT_F16, seed=122, block_len=1024),
     workloads.Workload("d64_B2_N1000_H5_f32", 2, 1000, 5, 64, workloads.DT_F32, seed=123, block_len=300),
     workloads.Workload("d64_B1_N4096_H18_bf16", 1, 4096, 18, 64, workloads.DT_BF16, seed=124),
+    workloads.Workload("d64_B3_N1000_H7_L100_f16", 3, 1000, 7, 64, workloads.DT_F16, seed=127, block_len=100),
+    workloads.Workload("d64_B2_N33_H1_bf16", 2, 33, 1, 64, workloads.DT_BF16, seed=128),
+    workloads.Workload("d64_B1_N4097_H3_L1_bf16", 1, 4097, 3, 64, workloads.DT_BF16, seed=129, block_len=1),
+    workloads.Workload("d64_B1_N16384_H35_bf16", 1, 16384, 35, 64, workloads.DT_BF16, seed=130),
 ]
 
 
 @pytest.mark.parametrize("w", HEAD_DIMS, ids=lambda w: w.name)
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["f32out", "bf16out"])
 def test_other_head_dims(w, out_dtype):
-    """Head dims 16 and 64 (vector-unit kernels) against the oracle."""
+    """Head dims 16 and 64 against the oracle (D = 64 with 16-bit inputs on the
+    matrix cores, with the 16384 x 35 heads case the headline's byte count;
+    the others on the vector unit)."""
     (q, k, v), want = inputs_and_oracle(w)
     got = run_hip(q, k, v, block_len=w.block_len, eps=w.eps, out_dtype=out_dtype)
     compare(got, want, v, out_dtype == torch.bfloat16, w.name)

@@ -99,11 +99,11 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out_dtype: str = "f32") ->
         return copy_bytes / statistics.median([x for x in copies if x >= 0.95 * top])
 
     sf, sw = calib(fetch), calib(write)
-    # bf16 inputs, head dim 32: the state kernel's template arguments F16 and
-    # D64 are false; the apply kernel's are the input and output element types
-    # and D64 = false
-    apply_tag = "k_apply_mfma<unsigned short, " + ("float" if out_dtype == "f32" else "unsigned short") + ", false>"
-    kernels = {"k_state_partial_mfma": lambda n: "k_state_partial_mfma<false, false>" in n,
+    # bf16 inputs, head dim 32: the state kernel's template arguments are
+    # F16 = false and the head dim; the apply kernel's the input and output
+    # element types and the head dim
+    apply_tag = "k_apply_mfma<unsigned short, " + ("float" if out_dtype == "f32" else "unsigned short") + ", 32>"
+    kernels = {"k_state_partial_mfma": lambda n: "k_state_partial_mfma<false, 32>" in n,
                "k_merge": lambda n: "k_merge" in n,
                "k_apply_mfma": lambda n: apply_tag in n}
     algo = {"k_state_partial_mfma": w.token_heads * w.D * 4,
@@ -412,21 +412,22 @@ def main() -> int:
                     "algorithmic bytes = 7 tensors"}
         del sets32, grads32, ws_b32
 
-        # head dim 64 at the same byte count: the headline buffers as 35 heads of 64
-        H64, D64 = H // 2, 2 * D
-        ws64 = torch.empty(sana.sana_linattn_workspace_bytes(B, H64, N, D64, 0), dtype=torch.uint8, device=dev)
-        sets64 = [[t.view(B, N, H64, D64) for t in st] for st in sets]
-        outs64 = [o.view(B, N, H64, D64) for o in outs]
+        # other head dims at the same byte count: the headline buffers viewed as
+        # 35 heads of 64 and as 140 heads of 16
+        for Hx, Dx in ((H // 2, 2 * D), (2 * H, D // 2)):
+            wsx = torch.empty(sana.sana_linattn_workspace_bytes(B, Hx, N, Dx, 0), dtype=torch.uint8, device=dev)
+            setsx = [[t.view(B, N, Hx, Dx) for t in st] for st in sets]
+            outsx = [o.view(B, N, Hx, Dx) for o in outs]
 
-        def d64(i):
-            q, k, v = sets64[i % NSETS]
-            sana.sana_linattn_fwd(q, k, v, outs64[i % NSETS], ws64, eps=w.eps, stream=stream)
-        ms = timed(d64, args.steps)
-        extra[f"d64_h{H64}_" + args.out_dtype + "out"] = {
-            "ms_per_step": round(ms, 5), "GBps": round(alg_bytes / ms / 1e6, 1),
-            "pct_hbm_peak": round(100 * alg_bytes / ms / 1e6 / HBM_PEAK_GBPS, 2),
-            "note": "head dim 64: the headline buffers viewed as B=1, N=16384, H=35, D=64, bf16 in"}
-        del sets64, outs64, ws64
+            def hdx(i):
+                q, k, v = setsx[i % NSETS]
+                sana.sana_linattn_fwd(q, k, v, outsx[i % NSETS], wsx, eps=w.eps, stream=stream)
+            ms = timed(hdx, args.steps)
+            extra[f"d{Dx}_h{Hx}_" + args.out_dtype + "out"] = {
+                "ms_per_step": round(ms, 5), "GBps": round(alg_bytes / ms / 1e6, 1),
+                "pct_hbm_peak": round(100 * alg_bytes / ms / 1e6 / HBM_PEAK_GBPS, 2),
+                "note": f"head dim {Dx}: the headline buffers viewed as B=1, N=16384, H={Hx}, D={Dx}, bf16 in"}
+            del setsx, outsx, wsx
 
         # backward (dq, dk, dv) of the same forward: bf16 q, k, v, dout -> bf16 gradients
         grads = [[torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev) for _ in range(3)]

@@ -396,8 +396,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
                     return reinterpret_cast<uint16_t*>(base + ((long long)b * N + min(tt + r, t1 - 1)) * hstride + 2 * hp * kD);
                 };
             };
-            store_pair_rows<OutT>(ctile[th][0], lane, 16 * hh, nh, row(dv));
-            store_pair_rows<OutT>(ctile[th][1], lane, 16 * hh, nh, row(dk));
+            store_pair_rows<OutT>(ctile[th][0], lane, 16 * hh, 4 * nh, row(dv));
+            store_pair_rows<OutT>(ctile[th][1], lane, 16 * hh, 4 * nh, row(dk));
             // the next tile's first barrier keeps the pair tiles until these reads are done
         }
     }
@@ -526,8 +526,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
                         return reinterpret_cast<uint16_t*>(base + ((long long)b * N + min(tt + r, t1 - 1)) * hstride + 2 * hp * kD);
                     };
                 };
-                store_pair_rows<OutT>(ctile[th][0], lane, 16 * hh, nh, row(dv));
-                store_pair_rows<OutT>(ctile[th][1], lane, 16 * hh, nh, row(dk));
+                store_pair_rows<OutT>(ctile[th][0], lane, 16 * hh, 4 * nh, row(dv));
+                store_pair_rows<OutT>(ctile[th][1], lane, 16 * hh, 4 * nh, row(dk));
             }
         }
         if (more) {

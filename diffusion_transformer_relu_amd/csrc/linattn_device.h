@@ -301,14 +301,15 @@ __device__ __forceinline__ void put_pair_tile(uint16_t* ct, const f32x16& acc, i
 
 // Rows r0 .. r0 + 15 of a pair tile as whole lines: 8 lanes x 16 bytes per
 // row; dst(r) points at the head pair's first element of row r's token; only
-// the first nh heads are written.
+// the first nchunk 16-byte chunks of each row are written (4 per head that
+// exists).
 template <typename OutT, typename RowPtr>
-__device__ __forceinline__ void store_pair_rows(const uint16_t* ct, int lane, int r0, int nh, RowPtr dst) {
+__device__ __forceinline__ void store_pair_rows(const uint16_t* ct, int lane, int r0, int nchunk, RowPtr dst) {
 #pragma unroll
     for (int k8 = 0; k8 < 2; ++k8) {
         const int r = r0 + 8 * k8 + (lane >> 3), chunk = lane & 7;
         const u32x4 x = *reinterpret_cast<const u32x4*>(ct + r * kPairRow + chunk * 8);
-        if (chunk < 4 * nh) __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(dst(r) + chunk * 8));
+        if (chunk < nchunk) __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(dst(r) + chunk * 8));
     }
 }
 

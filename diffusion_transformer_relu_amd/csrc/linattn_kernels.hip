@@ -52,16 +52,21 @@ static_assert(2 * kTensorStride >= 2 * 2 * 16 * 64 * (int)sizeof(float), "reduct
 // Wave w reduces head (w & 1) over token half (w >> 1) of each 64-token tile.
 // K and V are read once, so their loads are non-temporal.
 //
-// Head dim 64 (D64): a head's row is the 128 bytes a head pair of dim 32
-// takes, so the same tiles hold one head, its two 32-feature halves in place
-// of the two heads (H counts those halves, HP the heads).  The 64 x 65 state
-// is four 32 x 32 blocks: wave w accumulates block (K half w & 1, V half
-// w >> 1) over all tokens of each tile, the waves of V half 0 also the ones
-// column of their K half.
-template <bool F16, bool D64>
+// Other head dims HD reuse the tiles, which only see a token row as 32-feature
+// groups ("heads" here: H of them, HP pairs; HR real heads, rows of HR * HD
+// elements, pieces past the row read as zero):
+//  - HD = 64: a head is a pair of groups.  Its 64 x 65 state is four 32 x 32
+//    blocks: wave w accumulates block (K group w & 1, V group w >> 1) over all
+//    tokens of each tile, the waves of V group 0 also the ones column of their
+//    K group.
+//  - HD = 16: a group holds two heads.  The group's 32 x 32 product is formed
+//    as for HD = 32 and only its two diagonal 16 x 16 blocks (each head's keys
+//    against its own values) are kept.
+template <bool F16, int HD>
 __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ part,
-    int N, int H, int HP, int L, int cpb, int P, int chunk, Strides sk, Strides sv) {
+    int N, int H, int HP, int HR, int L, int cpb, int P, int chunk, Strides sk, Strides sv) {
+    constexpr bool D64 = HD == 2 * kD;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kTensorStride];
 
     const int p = blockIdx.x % P;
@@ -84,8 +89,8 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
             const int pc = tid + kThreads * i;
             const int part_ = pc & 3, hd = (pc >> 2) & 1, tok = pc >> 3;
             const int n = t0 + tok;
-            if (n < cr.c1 && hd < nh) {
-                const long long col = (long long)(h0 + hd) * kD + part_ * 8;
+            const int col = (h0 + hd) * kD + part_ * 8;
+            if (n < cr.c1 && col < HR * HD) {
                 rk[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + (b * sk.b + n * sk.n + col)));
                 rv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + (b * sv.b + n * sv.n + col)));
             } else {
@@ -171,6 +176,23 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
         }
     }
     __syncthreads();
+    if constexpr (HD == kD / 2) {
+        if (th == 0 && hh < nh) {
+            // rows 0..15 (r < 8) are the group's first head, 16..31 its second;
+            // the lanes of columns of the same half hold that head's state
+            constexpr int W16 = kD / 2 + 1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int half = r >> 3, head = 2 * (h0 + hh) + half;
+                if ((j >> 4) != half || head >= HR) continue;
+                const int row = 8 * ((r >> 2) & 1) + 4 * g + (r & 3);
+                float* dst = part + (((size_t)b * HR + head) * P + p) * (kD / 2 * W16);
+                dst[row * W16 + (j & 15)] = accV[r] + red[((hh * 2 + 0) * 16 + r) * 64 + lane];
+                if ((j & 15) == 0) dst[row * W16 + kD / 2] = accO[r] + red[((hh * 2 + 1) * 16 + r) * 64 + lane];
+            }
+        }
+        return;
+    }
     if (th == 0 && hh < nh) {
         float* dst = part + (((size_t)b * H + h0 + hh) * P + p) * kStateFloats;
 #pragma unroll
@@ -455,19 +477,25 @@ constexpr int kOutPitch = 36;   // floats per LDS output row: 32 + 4 keeps rows 
 // exact product).  Occupancy target 5 waves per SIMD (4 for fp16 and fp32 q,
 // whose splits need more registers; 3 for head dim 64).
 //
-// Head dim 64 (D64, 16-bit q): H counts 32-feature halves of heads and HP the
-// heads; wave w computes output half w & 1 of head hp (columns 32 (w & 1) ..
-// + 31, stored as "head" 2 hp + (w & 1)), reducing over all 64 features of q
-// in four K-steps against the state's column half.
-template <typename InT, typename OutT, bool D64>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D64 ? 3 : std::is_same<InT, uint16_t>::value ? 5 : 4, 8))) void k_apply_mfma(
+// Other head dims HD (16-bit q) use the 32-feature groups of a token row as
+// "heads" (H of them, HP pairs; HR real heads of rows HR * HD elements long):
+//  - HD = 64: wave w computes output half w & 1 of head hp (columns 32 (w & 1)
+//    .. + 31, stored as group 2 hp + (w & 1)), reducing over all 64 features
+//    of q in four K-steps against the state's column half.
+//  - HD = 16: group h holds heads 2h and 2h + 1; A is the block-diagonal
+//    32 x 32 matrix of their two states (zero off the diagonal blocks), so the
+//    product gives both heads' numerators, and each head takes its own
+//    normaliser (K-step 0 is the first head's features, 1 the second's).
+template <typename InT, typename OutT, int HD>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 2 * kD ? 3 : std::is_same<InT, uint16_t>::value ? 5 : 4, 8))) void k_apply_mfma(
     const InT* __restrict__ q, const float* __restrict__ state, OutT* __restrict__ out,
-    int N, int H, int HP, int L, int NB, int tile, int tpb, float eps, Strides sq, Strides so) {
+    int N, int H, int HP, int HR, int L, int NB, int tile, int tpb, float eps, Strides sq, Strides so) {
     constexpr bool F16 = std::is_same<InT, _Float16>::value;
     constexpr bool F32 = std::is_same<InT, float>::value;
-    static_assert(!(D64 && F32), "head dim 64 takes 16-bit q");
+    constexpr bool D64 = HD == 2 * kD, D16 = HD == kD / 2;
+    static_assert(HD == kD || !F32, "head dims 16 and 64 take 16-bit q");
     constexpr int KS = D64 ? 4 : 2;   // K-steps of 16 features
-    constexpr int SW = D64 ? 2 * kD + 1 : kW;   // state row
+    constexpr int SW = HD + 1;        // state row
     constexpr int QW = F32 ? 4 : KS;  // 16-byte pieces of a lane's q features (16 ks + 8 g .. + 7)
     __shared__ __attribute__((aligned(16))) float otile[4][32 * kOutPitch];   // fp32 out only
 
@@ -496,14 +524,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D64 ? 
     float sden[8 * KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+        // head dim 16: K-step ks is head 2 hs + ks (zero if there is none),
+        // present in the columns of the same half only
+        const int hr = 2 * hs + ks;
+        const bool on = !D16 || (hr < HR && (i >> 4) == ks);
+        const bool zon = !D16 || hr < HR;
+        const float* S16 = state + (((size_t)b * HR + min(hr, HR - 1)) * NB + beta) * (16 * 17);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             uint32_t w[3] = {0u, 0u, 0u};
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int row = 16 * ks + 8 * g + 2 * d + half;
-                float r = S[row * SW + i];
-                sden[8 * ks + 2 * d + half] = Sz[row * SW];
+                float r;
+                if constexpr (D16) {
+                    r = on ? S16[(row - 16 * ks) * 17 + (i & 15)] : 0.f;
+                    sden[8 * ks + 2 * d + half] = zon ? S16[(row - 16 * ks) * 17 + 16] : 0.f;
+                } else {
+                    r = S[row * SW + i];
+                    sden[8 * ks + 2 * d + half] = Sz[row * SW];
+                }
 #pragma unroll
                 for (int sp = 0; sp < 3; ++sp) {   // S = hi + mid + lo, each remainder exact
                     const uint16_t t = f32_to_bf16(r);
@@ -523,12 +563,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D64 ? 
     struct QRow {
         u32x4 x[QW];
     };
+    const bool second = !D16 || 2 * hs + 1 < HR;   // head dim 16: group hs has a second head
     auto load_row = [&](const u32x4* src, QRow& r) {
         if constexpr (F32) {   // features 8g..8g+7 = src[0..1], 16+8g..16+8g+7 = src[4..5]
             r.x[0] = src[0];
             r.x[1] = src[1];
             r.x[2] = src[4];
             r.x[3] = src[5];
+        } else if constexpr (D16) {   // the second head's features only if it exists
+            r.x[0] = src[0];
+            r.x[1] = second ? src[2] : (u32x4){0u, 0u, 0u, 0u};
         } else {               // features 16 ks + 8g..8g+7 = src[2 ks]
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) r.x[ks] = src[2 * ks];
@@ -551,7 +595,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D64 ? 
     // normalised 32 x 32 output tile of one sub-tile: acc row 8 (r / 4) + 4 g + r % 4, column i
     auto compute = [&](const QRow& qr) -> f32x16 {
         f32x16 acc = {};
-        float dp = 0.f;
+        float dp = 0.f, dp1 = 0.f;   // dp1: head dim 16, the group's second head
         if constexpr (F32) {
             // f = ReLU(q) in fp32 (features 16 ks + 8 g + e at f[8 ks + e])
             float f[16];
@@ -592,8 +636,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D64 ? 
                     split_f16x2(x[d], h, l, f0, f1);
                     hi[d] = h;
                     lo[d] = l;
-                    dp = fmaf(f0, sden[8 * ks + 2 * d], dp);
-                    dp = fmaf(f1, sden[8 * ks + 2 * d + 1], dp);
+                    float& t = (D16 && ks == 1) ? dp1 : dp;
+                    t = fmaf(f0, sden[8 * ks + 2 * d], t);
+                    t = fmaf(f1, sden[8 * ks + 2 * d + 1], t);
                 }
 #pragma unroll
                 for (int sp = 2; sp >= 0; --sp) acc = mfma_bf16(sa[ks][sp], lo, acc);   // small terms first
@@ -612,14 +657,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D64 ? 
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
-                    dp = fmaf(lo_bf16(a[ks][d]), sden[8 * ks + 2 * d], dp);
-                    dp = fmaf(hi_bf16(a[ks][d]), sden[8 * ks + 2 * d + 1], dp);
+                    float& t = (D16 && ks == 1) ? dp1 : dp;
+                    t = fmaf(lo_bf16(a[ks][d]), sden[8 * ks + 2 * d], t);
+                    t = fmaf(hi_bf16(a[ks][d]), sden[8 * ks + 2 * d + 1], t);
                 }
         }
         const float den = dp + __shfl_xor(dp, 32);   // same sum on lanes i and i + 32
         const float rinv = 1.0f / (den + eps);
+        if constexpr (D16) {
+            // rows 0..15 (r < 8) are the first head's outputs, 16..31 the second's
+            const float den1 = dp1 + __shfl_xor(dp1, 32);
+            const float rinv1 = 1.0f / (den1 + eps);
 #pragma unroll
-        for (int rg = 0; rg < 16; ++rg) acc[rg] *= rinv;
+            for (int rg = 0; rg < 16; ++rg) acc[rg] *= rg < 8 ? rinv : rinv1;
+        } else {
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) acc[rg] *= rinv;
+        }
         return acc;
     };
 
@@ -627,6 +681,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D64 ? 
         // fp32: one head's output row is a whole 128-byte line; each wave
         // stores its own tile through its LDS tile
         if (h >= H) return;
+        const int lim = HR * HD - h * kD;   // elements of the row from this group on (16 for a lone head of dim 16)
         float* ot = otile[wave];
         int tt = t0 + 32 * sub;
         QRow cur;
@@ -646,7 +701,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D64 ? 
             for (int s4 = 0; s4 < 4; ++s4) {
                 const int r = 8 * s4 + (lane >> 3), cc = (lane & 7) * 4;
                 const f32x4 x = *reinterpret_cast<const f32x4*>(ot + r * kOutPitch + cc);
-                if (tt + r < t1) store4(out + (b * so.b + (tt + r) * so.n + h * kD + cc), x);
+                if (tt + r < t1 && cc < lim) store4(out + (b * so.b + (tt + r) * so.n + h * kD + cc), x);
             }
             __builtin_amdgcn_wave_barrier();
             cur = nxt;
@@ -657,7 +712,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D64 ? 
         // All waves take the same number of steps (a step past the range
         // works on the clamped last row).
         __shared__ __attribute__((aligned(16))) uint16_t ct[2][32 * kPairRow];
-        const int nh = min(2, H - 2 * hp);
+        const int nchunk = min(8, (HR * HD - 2 * hp * kD) / 8);   // 16-byte chunks of the line that exist
         const int steps = (t1 - t0 + 63) / 64;
         int tt = t0 + 32 * sub;
         QRow cur;
@@ -670,7 +725,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D64 ? 
             __syncthreads();
             // wave (sub, hh) stores rows 16 hh .. 16 hh + 15 of its sub-tile
             // (rows past the range repeat the last row, with its bits)
-            store_pair_rows<OutT>(ct[sub], lane, 16 * hh, nh, [&](int r) {
+            store_pair_rows<OutT>(ct[sub], lane, 16 * hh, nchunk, [&](int r) {
                 return reinterpret_cast<uint16_t*>(out + (b * so.b + min(tt + r, t1 - 1) * so.n + 2 * hp * kD));
             });
             __syncthreads();
@@ -734,6 +789,9 @@ template <typename F> void by_dtype(int code, F&& f) {
 }
 
 // Calls f(std::integral_constant<int, D>) for the supported head dims.
+// 32-feature groups of a token row (the "heads" of the matrix-core kernels)
+int groups32(const Plan& pl) { return (pl.H * pl.D + kD - 1) / kD; }
+
 template <typename F> void by_head_dim(int D, F&& f) {
     if (D == 16)
         f(std::integral_constant<int, 16>{});
@@ -753,16 +811,13 @@ hipError_t launch_state(const Plan& pl, const void* k, const void* v, float* par
             hipLaunchKernelGGL(k_state_partial_mfma_f32, dim3(grid), dim3(kThreads), 0, stream,
                                static_cast<const float*>(k), static_cast<const float*>(v), part, pl.N, pl.H, pl.HP,
                                pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
-        else if (pl.D == 2 * kD)   // heads of dim 64 as pairs of 32-feature halves
-            hipLaunchKernelGGL((pl.in_dtype == 2 ? k_state_partial_mfma<true, true> : k_state_partial_mfma<false, true>),
-                               dim3(grid), dim3(kThreads), 0, stream, k16, v16, part, pl.N, 2 * pl.H, pl.HP, pl.L,
-                               pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
-        else if (pl.in_dtype == 2)
-            hipLaunchKernelGGL((k_state_partial_mfma<true, false>), dim3(grid), dim3(kThreads), 0, stream, k16, v16,
-                               part, pl.N, pl.H, pl.HP, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
         else
-            hipLaunchKernelGGL((k_state_partial_mfma<false, false>), dim3(grid), dim3(kThreads), 0, stream, k16, v16,
-                               part, pl.N, pl.H, pl.HP, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
+            by_head_dim(pl.D, [&](auto dd) {
+                constexpr int DD = decltype(dd)::value;
+                auto kern = pl.in_dtype == 2 ? k_state_partial_mfma<true, DD> : k_state_partial_mfma<false, DD>;
+                hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, k16, v16, part, pl.N,
+                                   groups32(pl), pl.HP, pl.H, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
+            });
     } else {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.H * pl.P);
         by_dtype(pl.in_dtype, [&](auto in) {
@@ -796,16 +851,18 @@ hipError_t launch_apply(const Plan& pl, const void* q, const float* state, void*
                 using IT = typename decltype(in)::type;
                 using OT = typename decltype(o)::type;
                 if constexpr (sizeof(IT) == 2) {
-                    if (pl.D == 2 * kD) {   // heads of dim 64 as pairs of 32-feature halves
-                        hipLaunchKernelGGL((k_apply_mfma<IT, OT, true>), dim3(grid), dim3(kThreads), 0, stream,
-                                           static_cast<const IT*>(q), state, static_cast<OT*>(out), pl.N, 2 * pl.H,
-                                           pl.HP, pl.L, pl.NB, pl.tile, pl.tpb, eps, pl.sq, pl.so);
-                        return;
-                    }
+                    by_head_dim(pl.D, [&](auto dd) {
+                        constexpr int DD = decltype(dd)::value;
+                        hipLaunchKernelGGL((k_apply_mfma<IT, OT, DD>), dim3(grid), dim3(kThreads), 0, stream,
+                                           static_cast<const IT*>(q), state, static_cast<OT*>(out), pl.N,
+                                           groups32(pl), pl.HP, pl.H, pl.L, pl.NB, pl.tile, pl.tpb, eps, pl.sq,
+                                           pl.so);
+                    });
+                } else {
+                    hipLaunchKernelGGL((k_apply_mfma<IT, OT, kD>), dim3(grid), dim3(kThreads), 0, stream,
+                                       static_cast<const IT*>(q), state, static_cast<OT*>(out), pl.N, pl.H, pl.HP,
+                                       pl.H, pl.L, pl.NB, pl.tile, pl.tpb, eps, pl.sq, pl.so);
                 }
-                hipLaunchKernelGGL((k_apply_mfma<IT, OT, false>), dim3(grid), dim3(kThreads), 0, stream,
-                                   static_cast<const IT*>(q), state, static_cast<OT*>(out), pl.N, pl.H, pl.HP, pl.L,
-                                   pl.NB, pl.tile, pl.tpb, eps, pl.sq, pl.so);
             });
         });
     } else {

@@ -41,7 +41,8 @@ def test_version_and_status_strings():
 def test_other_head_dims():
     assert sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 8, 256, 64, 0)["mfma"] == 1   # pairs of 32-feature halves
     assert sana.sana_linattn_plan_info(sana.SANA_DT_F16, 1, 8, 256, 64, 0)["mfma"] == 1
-    assert sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 8, 256, 16, 0)["mfma"] == 0
+    assert sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 8, 256, 16, 0)["mfma"] == 1   # two heads per 32 features
+    assert sana.sana_linattn_plan_info(sana.SANA_DT_F32, 1, 8, 256, 16, 0)["mfma"] == 0
     w16, w32, w64 = (sana.sana_linattn_workspace_bytes(1, 8, 4096, d, 0) for d in (16, 32, 64))
     assert w16 < w32 < w64
     for d in (8, 48, 128):

@@ -321,15 +321,21 @@ HEAD_DIMS = [
     workloads.Workload("d64_B2_N33_H1_bf16", 2, 33, 1, 64, workloads.DT_BF16, seed=128),
     workloads.Workload("d64_B1_N4097_H3_L1_bf16", 1, 4097, 3, 64, workloads.DT_BF16, seed=129, block_len=1),
     workloads.Workload("d64_B1_N16384_H35_bf16", 1, 16384, 35, 64, workloads.DT_BF16, seed=130),
+    workloads.Workload("d16_B3_N1000_H7_L100_bf16", 3, 1000, 7, 16, workloads.DT_BF16, seed=131, block_len=100),
+    workloads.Workload("d16_B2_N33_H1_f16", 2, 33, 1, 16, workloads.DT_F16, seed=132),
+    workloads.Workload("d16_B1_N4097_H5_L1_bf16", 1, 4097, 5, 16, workloads.DT_BF16, seed=133, block_len=1),
+    workloads.Workload("d16_B2_N1000_H3_f32", 2, 1000, 3, 16, workloads.DT_F32, seed=134),
+    workloads.Workload("d16_B1_N16384_H140_bf16", 1, 16384, 140, 16, workloads.DT_BF16, seed=135),
 ]
 
 
 @pytest.mark.parametrize("w", HEAD_DIMS, ids=lambda w: w.name)
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["f32out", "bf16out"])
 def test_other_head_dims(w, out_dtype):
-    """Head dims 16 and 64 against the oracle (D = 64 with 16-bit inputs on the
-    matrix cores, with the 16384 x 35 heads case the headline's byte count;
-    the others on the vector unit)."""
+    """Head dims 16 and 64 against the oracle (16-bit inputs on the matrix
+    cores, fp32 inputs on the vector unit); 16384 tokens x 35 heads of 64 and
+    x 140 heads of 16 move the headline's bytes; odd and single heads of 16
+    leave a 32-feature group half empty."""
     (q, k, v), want = inputs_and_oracle(w)
     got = run_hip(q, k, v, block_len=w.block_len, eps=w.eps, out_dtype=out_dtype)
     compare(got, want, v, out_dtype == torch.bfloat16, w.name)

@@ -29,8 +29,11 @@
 // fp16 inputs take the same matrix-core kernels (products of fp16 values are
 // exact in fp32 as well); in the apply kernel each ReLU(q) element is split
 // exactly into two bf16 terms, so the state side stays the bf16 split.  fp32
-// inputs take the vector kernels (k_*_valu), which also serve as a second
-// implementation for cross-checks.
+// inputs (head dim 32) split K, V and q into three bf16 terms each
+// (k_state_partial_mfma_f32 and the fp32 branch of k_apply_mfma).  Head dims
+// 16 and 64 with 16-bit inputs run the same kernels on 32-feature groups of
+// the token row; the vector kernels (k_*_valu) take fp32 inputs of those dims
+// and serve as a second implementation for cross-checks.
 #include "linattn_device.h"
 
 #include <type_traits>

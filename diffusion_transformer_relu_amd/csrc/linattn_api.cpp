@@ -38,10 +38,9 @@ int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 long round_up(long a, long m) { return (a + m - 1) / m * m; }
 
 // Decomposition of one call.  Sizes were range-checked by the caller.
-// f32_mfma: fp32 inputs may use the matrix-core forward kernels (the forward-
-// mode derivative has vector kernels only for them).
+// allow_mfma = false gives the vector path's plan (for workspace queries).
 int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block_len, Plan* pl,
-              bool f32_mfma = true) {
+              bool allow_mfma = true) {
     if (B < 0 || H < 0 || N < 0 || D < 1 || block_len < 0) return SANA_ERR_INVALID_ARG;
     if ((in_dtype != SANA_DT_F32 && in_dtype != SANA_DT_BF16 && in_dtype != SANA_DT_F16) ||
         (out_dtype != SANA_DT_F32 && out_dtype != SANA_DT_BF16 && out_dtype != SANA_DT_F16))
@@ -64,7 +63,7 @@ int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block
     // inputs (the kernels see a token row as 32-feature groups: a head of 64
     // is two of them, a group holds two heads of 16); units are pairs of groups
     const bool mfma_dim = D == sana::kD || in_dtype != SANA_DT_F32;
-    pl->mfma = (mfma_dim && !env_is("SANA_LINATTN_PATH", "valu") && (in_dtype != SANA_DT_F32 || f32_mfma)) ? 1 : 0;
+    pl->mfma = (mfma_dim && allow_mfma && !env_is("SANA_LINATTN_PATH", "valu")) ? 1 : 0;
     pl->mfma16 = pl->mfma && in_dtype != SANA_DT_F32;
     pl->HP = pl->mfma ? ceil_div(ceil_div((long)H * D, sana::kD), 2) : H;
     const long units = (long)B * pl->HP * pl->NB;   // independent (b, head unit, block) triples
@@ -214,9 +213,9 @@ int forward(const void* q, const void* k, const void* v, void* out, int in_dtype
 constexpr int kBwdTile = 256;   // tokens per query/key work-group (one per thread)
 
 int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, int N, int D, int block_len,
-                  sana::BwdPlan* bp) {
+                  sana::BwdPlan* bp, bool allow_mfma = true) {
     std::memset(bp, 0, sizeof *bp);
-    const int st = make_plan(in_dtype, SANA_DT_F32, B, H, N, D, block_len, &bp->fw);
+    const int st = make_plan(in_dtype, SANA_DT_F32, B, H, N, D, block_len, &bp->fw, allow_mfma);
     if (st != SANA_OK) return st;
     if (D != sana::kD) return SANA_ERR_UNSUPPORTED;   // the backward is built for D = 32
     for (int c : {dout_dtype, grad_dtype})
@@ -324,8 +323,9 @@ int backward(const void* q, const void* k, const void* v, const void* dout, void
 
 // Forward-mode derivative: the forward's plan with the workspace doubled (a
 // state and a tangent state per head).
-int make_jvp_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block_len, Plan* pl) {
-    const int st = make_plan(in_dtype, out_dtype, B, H, N, D, block_len, pl, false);
+int make_jvp_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block_len, Plan* pl,
+                  bool allow_mfma = true) {
+    const int st = make_plan(in_dtype, out_dtype, B, H, N, D, block_len, pl, allow_mfma);
     if (st != SANA_OK) return st;
     if (D != sana::kD) return SANA_ERR_UNSUPPORTED;   // the forward-mode derivative is built for D = 32
     if (B == 0 || H == 0 || N == 0) return SANA_OK;
@@ -413,12 +413,13 @@ int sana_linattn_workspace_bytes(int B, int H, int N, int D, int block_len, size
 int sana_linattn_bwd_workspace_bytes(int B, int H, int N, int D, int block_len, size_t* bytes) {
     if (!bytes) return SANA_ERR_INVALID_ARG;
     size_t most = 0;
-    for (int dt : {SANA_DT_BF16, SANA_DT_F32}) {
-        sana::BwdPlan bp;
-        const int st = make_bwd_plan(dt, SANA_DT_F32, SANA_DT_F32, B, H, N, D, block_len, &bp);
-        if (st != SANA_OK) return st;
-        most = std::max(most, bp.bytes);
-    }
+    for (int dt : {SANA_DT_BF16, SANA_DT_F32})
+        for (bool mf : {true, false}) {   // the vector path's plan too (SANA_LINATTN_PATH=valu)
+            sana::BwdPlan bp;
+            const int st = make_bwd_plan(dt, SANA_DT_F32, SANA_DT_F32, B, H, N, D, block_len, &bp, mf);
+            if (st != SANA_OK) return st;
+            most = std::max(most, bp.bytes);
+        }
     *bytes = most;
     return SANA_OK;
 }
@@ -434,12 +435,13 @@ int sana_linattn_bwd(const void* q, const void* k, const void* v, const void* do
 int sana_linattn_jvp_workspace_bytes(int B, int H, int N, int D, int block_len, size_t* bytes) {
     if (!bytes) return SANA_ERR_INVALID_ARG;
     size_t most = 0;
-    for (int dt : {SANA_DT_BF16, SANA_DT_F32}) {
-        Plan pl;
-        const int st = make_jvp_plan(dt, SANA_DT_F32, B, H, N, D, block_len, &pl);
-        if (st != SANA_OK) return st;
-        most = std::max(most, pl.bytes);
-    }
+    for (int dt : {SANA_DT_BF16, SANA_DT_F32})
+        for (bool mf : {true, false}) {   // the vector path's plan too (SANA_LINATTN_PATH=valu)
+            Plan pl;
+            const int st = make_jvp_plan(dt, SANA_DT_F32, B, H, N, D, block_len, &pl, mf);
+            if (st != SANA_OK) return st;
+            most = std::max(most, pl.bytes);
+        }
     *bytes = most;
     return SANA_OK;
 }

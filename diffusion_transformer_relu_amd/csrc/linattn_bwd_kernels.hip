@@ -403,56 +403,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
     }
 }
 
-// fp32 inputs: features 8g..8g+7 and 16+8g..16+8g+7 of an fp32 row (the B
-// operand layout), 4 x 16 bytes.
-struct F32Operand {
-    f32x4 x[4];
-    __device__ __forceinline__ void load(const float* row, int g) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-            x[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 16 * (p >> 1) + 8 * g + 4 * (p & 1)));
-    }
-    // the 8 values of half ks (features 16 ks + 8 g ..), optionally ReLU'd
-    __device__ __forceinline__ void half(int ks, bool relu, float out[8]) const {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float t = x[2 * ks + (e >> 2)][e & 3];
-            out[e] = relu ? fmaxf(t, 0.f) : t;
-        }
-    }
-    // bit j set when feature j of the token is > 0 (the partner lane, i + 32,
-    // holds the other 16 features)
-    __device__ __forceinline__ uint32_t positive(int g) const {
-        uint32_t m = 0;
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) m |= (uint32_t)(x[p][e] > 0.f) << (16 * (p >> 1) + 8 * g + 4 * (p & 1) + e);
-        return m | (uint32_t)__shfl_xor((int)m, 32);
-    }
-};
-
-// acc += A B over 32 features with A given as three split terms (index 0 the
-// largest) and B as an fp32 operand split here into three truncation terms:
-// the products of terms i + j <= 2, smallest first; the others lie below
-// 2^-24 of the product and are dropped.
-__device__ __forceinline__ f32x16 mma_split3(const u32x4 A[2][3], const F32Operand& b, bool relu, f32x16 acc) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        float x[8];
-        b.half(ks, relu, x);
-        u32x4 t[3];
-        split3_trunc_f32x8(x, t);
-        acc = mfma_bf16(A[ks][0], t[2], acc);
-        acc = mfma_bf16(A[ks][1], t[1], acc);
-        acc = mfma_bf16(A[ks][2], t[0], acc);
-        acc = mfma_bf16(A[ks][0], t[1], acc);
-        acc = mfma_bf16(A[ks][1], t[0], acc);
-        acc = mfma_bf16(A[ks][0], t[0], acc);
-    }
-    return acc;
-}
-
 // The key pass for fp32 k and v: the work-group, waves and sub-tiles of the
 // 16-bit kernel, but each wave reads its own 32 keys straight from global
 // memory in the operand layout (the next sub-tile's loads issued before this

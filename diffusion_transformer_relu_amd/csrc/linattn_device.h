@@ -246,6 +246,76 @@ __device__ __forceinline__ void store_tile(float* ot, const f32x16& acc, int lan
     __builtin_amdgcn_wave_barrier();
 }
 
+// fp32 inputs: features 8g..8g+7 and 16+8g..16+8g+7 of an fp32 row (the B
+// operand layout), 4 x 16 bytes.
+struct F32Operand {
+    f32x4 x[4];
+    __device__ __forceinline__ void load(const float* row, int g) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            x[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 16 * (p >> 1) + 8 * g + 4 * (p & 1)));
+    }
+    // the 8 values of half ks (features 16 ks + 8 g ..), optionally ReLU'd
+    __device__ __forceinline__ void half(int ks, bool relu, float out[8]) const {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float t = x[2 * ks + (e >> 2)][e & 3];
+            out[e] = relu ? fmaxf(t, 0.f) : t;
+        }
+    }
+    // bit j set when feature j of the token is > 0 (the partner lane, i + 32,
+    // holds the other 16 features)
+    __device__ __forceinline__ uint32_t positive(int g) const {
+        uint32_t m = 0;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m |= (uint32_t)(x[p][e] > 0.f) << (16 * (p >> 1) + 8 * g + 4 * (p & 1) + e);
+        return m | (uint32_t)__shfl_xor((int)m, 32);
+    }
+};
+
+// The three truncation terms of half ks of an fp32 operand, optionally
+// ReLU'd, or (mask given) kept only where the mask operand is > 0.
+__device__ __forceinline__ void split_half(const F32Operand& b, int ks, bool relu, u32x4 t[3]) {
+    float x[8];
+    b.half(ks, relu, x);
+    split3_trunc_f32x8(x, t);
+}
+__device__ __forceinline__ void split_half_where(const F32Operand& b, const F32Operand& mask, int ks, u32x4 t[3]) {
+    float x[8], m[8];
+    b.half(ks, false, x);
+    mask.half(ks, false, m);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = m[e] > 0.f ? x[e] : 0.f;
+    split3_trunc_f32x8(x, t);
+}
+
+// acc += A B for one K-step of 16 features, A and B both as three bf16 terms
+// (index 0 the largest): the products of terms i + j <= 2, smallest first;
+// the others lie below 2^-24 of the product and are dropped.
+__device__ __forceinline__ f32x16 mma_terms(const u32x4 A[3], const u32x4 t[3], f32x16 acc) {
+    acc = mfma_bf16(A[0], t[2], acc);
+    acc = mfma_bf16(A[1], t[1], acc);
+    acc = mfma_bf16(A[2], t[0], acc);
+    acc = mfma_bf16(A[0], t[1], acc);
+    acc = mfma_bf16(A[1], t[0], acc);
+    acc = mfma_bf16(A[0], t[0], acc);
+    return acc;
+}
+
+// acc += A B over 32 features with A given as three split terms (index 0 the
+// largest) and B as an fp32 operand split here into three truncation terms.
+__device__ __forceinline__ f32x16 mma_split3(const u32x4 A[2][3], const F32Operand& b, bool relu, f32x16 acc) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        u32x4 t[3];
+        split_half(b, ks, relu, t);
+        acc = mma_terms(A[ks], t, acc);
+    }
+    return acc;
+}
+
 // ------------------------------------------------------------------ transposing LDS gathers
 // Operand of v_mfma_f32_32x32x16 with tokens as the reduction dimension, from
 // a token-major LDS tile of 16-bit elements (`pitch` per row): lane (g, m)

@@ -64,6 +64,21 @@ def test_jvp_full_size(w, out_t):
     check_tangent(got_t, want_t, out_t, w.name)
 
 
+F32_IN = [workloads.with_shape(workloads.HEADLINE, in_dtype=workloads.DT_F32, name="sana1600m_4096px_f32in"),
+          workloads.with_shape(workloads.BLOCK_CAUSAL, in_dtype=workloads.DT_F32, name="blockcausal_16x1024_f32in")]
+
+
+@pytest.mark.parametrize("w", F32_IN, ids=lambda w: w.name)
+@pytest.mark.parametrize("out_t", [torch.float32, torch.bfloat16], ids=["f32out", "bf16out"])
+def test_jvp_full_size_fp32_inputs(w, out_t):
+    """fp32 inputs and tangents: the matrix-core kernels on three-term bf16
+    splits of a, v, a_t, v_t, f and f_t."""
+    x, (want, want_t) = case(w)
+    got, got_t = run(x, w, out_t)
+    compare(got, want, x[2], out_t == torch.bfloat16, w.name)
+    check_tangent(got_t, want_t, out_t, w.name)
+
+
 EDGE = [(2, 33, 3, 0, 1), (1, 257, 2, 64, 1), (3, 1000, 5, 100, 2), (1, 300, 2, 1, 0), (1, 4097, 1, 0, 2),
         (1, 1, 1, 0, 1)]
 

@@ -410,7 +410,24 @@ def main() -> int:
             "pct_hbm_peak": round(100 * b32 / ms / 1e6 / HBM_PEAK_GBPS, 2),
             "note": "sana_linattn_bwd, fp32 q/k/v/dout/gradients (the headline inputs widened); "
                     "algorithmic bytes = 7 tensors"}
-        del sets32, grads32, ws_b32
+        del grads32, ws_b32
+
+        # fp32 forward-mode derivative: fp32 q, k, v and tangents -> fp32 out and out_t
+        outs_j32 = [torch.empty((B, N, H, D), dtype=torch.float32, device=dev) for _ in range(2)]
+        ws_j32 = torch.empty(sana.sana_linattn_jvp_workspace_bytes(B, H, N, D, 0), dtype=torch.uint8, device=dev)
+
+        def jvp32(i):
+            q, k, v = sets32[i % NSETS]
+            qt, kt, vt = sets32[(i + 1) % NSETS]
+            sana.sana_linattn_jvp(q, k, v, qt, kt, vt, *outs_j32, ws_j32, eps=w.eps, stream=stream)
+        ms = timed(jvp32, args.steps)
+        j32 = w.token_heads * D * 4 * 8
+        extra["jvp_f32"] = {
+            "ms_per_step": round(ms, 5), "GBps": round(j32 / ms / 1e6, 1),
+            "pct_hbm_peak": round(100 * j32 / ms / 1e6 / HBM_PEAK_GBPS, 2),
+            "note": "sana_linattn_jvp, fp32 inputs, tangents and outputs (the headline inputs widened); "
+                    "algorithmic bytes = 6 inputs + 2 outputs"}
+        del sets32, outs_j32, ws_j32
 
         # other head dims at the same byte count: the headline buffers viewed as
         # 35 heads of 64 and as 140 heads of 16

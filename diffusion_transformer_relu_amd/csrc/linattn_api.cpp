@@ -59,11 +59,10 @@ int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block
 
     pl->L = (block_len == 0 || block_len >= N) ? N : block_len;
     pl->NB = ceil_div(N, pl->L);
-    // matrix cores: D = 32 for every input type, D = 16 and 64 for 16-bit
-    // inputs (the kernels see a token row as 32-feature groups: a head of 64
-    // is two of them, a group holds two heads of 16); units are pairs of groups
-    const bool mfma_dim = D == sana::kD || in_dtype != SANA_DT_F32;
-    pl->mfma = (mfma_dim && allow_mfma && !env_is("SANA_LINATTN_PATH", "valu")) ? 1 : 0;
+    // matrix cores for every head dim and input type (the kernels see a token
+    // row as 32-feature groups: a head of 64 is two of them, a group holds two
+    // heads of 16); units are pairs of groups
+    pl->mfma = (allow_mfma && !env_is("SANA_LINATTN_PATH", "valu")) ? 1 : 0;
     pl->mfma16 = pl->mfma && in_dtype != SANA_DT_F32;
     pl->HP = pl->mfma ? ceil_div(ceil_div((long)H * D, sana::kD), 2) : H;
     const long units = (long)B * pl->HP * pl->NB;   // independent (b, head unit, block) triples
@@ -92,8 +91,8 @@ int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block
             tile = (int)round_up(tile, 64);
         } else {
             // fp16 and fp32 q run the apply kernel at 4 waves per SIMD instead
-            // of 5, head dim 64 at 3
-            const long slots = D == 2 * sana::kD ? sana::kCUs * 3
+            // of 5, head dim 64 at 3 (2 for fp32 q)
+            const long slots = D == 2 * sana::kD ? sana::kCUs * (in_dtype == SANA_DT_F32 ? 2 : 3)
                                : in_dtype != SANA_DT_BF16 ? sana::kApplyGroups * 4 / 5 : sana::kApplyGroups;
             const long per_block = std::max<long>(1, slots / units);
             tile = (int)round_up(ceil_div(pl->L, per_block), 64);

@@ -31,9 +31,8 @@
 // exactly into two bf16 terms, so the state side stays the bf16 split.  fp32
 // inputs (head dim 32) split K, V and q into three bf16 terms each
 // (k_state_partial_mfma_f32 and the fp32 branch of k_apply_mfma).  Head dims
-// 16 and 64 with 16-bit inputs run the same kernels on 32-feature groups of
-// the token row; the vector kernels (k_*_valu) take fp32 inputs of those dims
-// and serve as a second implementation for cross-checks.
+// 16 and 64 run the same kernels on 32-feature groups of the token row.  The
+// vector kernels (k_*_valu) are a second implementation for cross-checks.
 #include "linattn_device.h"
 
 #include <type_traits>
@@ -50,6 +49,26 @@ constexpr int kHeadStride = kStateTile * 64 + 64;   // bytes
 constexpr int kTensorStride = 2 * kHeadStride;
 
 static_assert(2 * kTensorStride >= 2 * 2 * 16 * 64 * (int)sizeof(float), "reduction area exceeds the LDS tile");
+
+// Head dim 16: the diagonal 16 x 16 blocks of group grp's 32 x 32 sums (this
+// wave's accumulators plus the other token half's, staged in red as
+// [head][V|O][16][64]) are the states of heads 2 grp and 2 grp + 1, written
+// when those heads exist.  Rows 0..15 (r < 8) are the first head's, 16..31
+// the second's; the lanes of columns of the same half hold that head's state.
+__device__ __forceinline__ void write_diag16(float* part, const float* red, const f32x16& accV, const f32x16& accO,
+                                             int b, int HR, int P, int p, int grp, int hh, int lane) {
+    constexpr int W16 = kD / 2 + 1;
+    const int g = lane >> 5, j = lane & 31;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int half = r >> 3, head = 2 * grp + half;
+        if ((j >> 4) != half || head >= HR) continue;
+        const int row = 8 * ((r >> 2) & 1) + 4 * g + (r & 3);
+        float* dst = part + (((size_t)b * HR + head) * P + p) * (kD / 2 * W16);
+        dst[row * W16 + (j & 15)] = accV[r] + red[((hh * 2 + 0) * 16 + r) * 64 + lane];
+        if ((j & 15) == 0) dst[row * W16 + kD / 2] = accO[r] + red[((hh * 2 + 1) * 16 + r) * 64 + lane];
+    }
+}
 
 // grid.x = (b * HP + hp) * P + p; one work-group = one chunk of one head pair.
 // Wave w reduces head (w & 1) over token half (w >> 1) of each 64-token tile.
@@ -180,20 +199,7 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
     }
     __syncthreads();
     if constexpr (HD == kD / 2) {
-        if (th == 0 && hh < nh) {
-            // rows 0..15 (r < 8) are the group's first head, 16..31 its second;
-            // the lanes of columns of the same half hold that head's state
-            constexpr int W16 = kD / 2 + 1;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int half = r >> 3, head = 2 * (h0 + hh) + half;
-                if ((j >> 4) != half || head >= HR) continue;
-                const int row = 8 * ((r >> 2) & 1) + 4 * g + (r & 3);
-                float* dst = part + (((size_t)b * HR + head) * P + p) * (kD / 2 * W16);
-                dst[row * W16 + (j & 15)] = accV[r] + red[((hh * 2 + 0) * 16 + r) * 64 + lane];
-                if ((j & 15) == 0) dst[row * W16 + kD / 2] = accO[r] + red[((hh * 2 + 1) * 16 + r) * 64 + lane];
-            }
-        }
+        if (th == 0 && hh < nh) write_diag16(part, red, accV, accO, b, HR, P, p, h0 + hh, hh, lane);
         return;
     }
     if (th == 0 && hh < nh) {
@@ -219,12 +225,16 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
 //   S_v += a_i^T v_j over the term pairs i + j <= 4 (1-based; the dropped
 //          products are below 2^-24 of the exact one)
 //   S_1 += (a_1 + a_2 + a_3)^T 1 (exact)
-// Wave w: head w & 1, token half w >> 1 of each tile.
+// Wave w: head w & 1, token half w >> 1 of each tile.  Head dims 16 and 64
+// work on 32-feature groups as the 16-bit kernel does (HD = 64: wave w owns
+// state block (K group w & 1, V group w >> 1) over all tokens; HD = 16: the
+// diagonal blocks of each group are kept).
 constexpr int kF32Tile = 64 * kD;   // 16-bit elements of one term tile [token][feature] of one head
 
+template <int HD>
 __global__ __launch_bounds__(kThreads) void k_state_partial_mfma_f32(
     const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ part,
-    int N, int H, int HP, int L, int cpb, int P, int chunk, Strides sk, Strides sv) {
+    int N, int H, int HP, int HR, int L, int cpb, int P, int chunk, Strides sk, Strides sv) {
     __shared__ __attribute__((aligned(16))) uint16_t lds[2][3][2][kF32Tile];   // [tensor][term][head] = 48 KB
 
     const int p = blockIdx.x % P;
@@ -247,8 +257,8 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma_f32(
             const int pc = tid + kThreads * i;
             const int part_ = pc & 3, hd = (pc >> 2) & 1, tok = pc >> 3;
             const int n = t0 + tok;
-            if (n < cr.c1 && hd < nh) {
-                const long long col = (long long)(h0 + hd) * kD + part_ * 8;
+            const int col = (h0 + hd) * kD + part_ * 8;
+            if (n < cr.c1 && col < HR * HD) {
                 const f32x4* ks = reinterpret_cast<const f32x4*>(k + (b * sk.b + n * sk.n + col));
                 const f32x4* vs = reinterpret_cast<const f32x4*>(v + (b * sv.b + n * sv.n + col));
                 rk[i][0] = __builtin_nontemporal_load(ks);
@@ -292,14 +302,15 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma_f32(
         __syncthreads();
         if (t0 + 64 < cr.c1) load_tile(t0 + 64);   // in flight during the MFMAs
 
+        constexpr bool D64 = HD == 2 * kD;
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            const int tb = 32 * th + 16 * st;   // first token of this K-step in the tile
+        for (int st = 0; st < (D64 ? 4 : 2); ++st) {
+            const int tb = D64 ? 16 * st : 32 * th + 16 * st;   // first token of this K-step in the tile
             u32x4 ta[3], tv[3];
 #pragma unroll
             for (int t = 0; t < 3; ++t) {
                 ta[t] = gather_tokens_t16(lds[0][t][hh], kD, tb, 0, lane);   // lane (g, j): tokens tb + 8g + e, feature j
-                tv[t] = gather_tokens_t16(lds[1][t][hh], kD, tb, 0, lane);   // lane (g, c): tokens tb + 8g + e, channel c
+                tv[t] = gather_tokens_t16(lds[1][t][D64 ? th : hh], kD, tb, 0, lane);   // lane (g, c): tokens tb + 8g + e, channel c
             }
             // smallest products first
             accV = mfma_bf16(ta[2], tv[0], accV);
@@ -308,12 +319,26 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma_f32(
             accV = mfma_bf16(ta[1], tv[0], accV);
             accV = mfma_bf16(ta[0], tv[1], accV);
             accV = mfma_bf16(ta[0], tv[0], accV);
-            accO = mfma_bf16(ta[2], ones, accO);
-            accO = mfma_bf16(ta[1], ones, accO);
-            accO = mfma_bf16(ta[0], ones, accO);
+            if (!D64 || th == 0) {
+                accO = mfma_bf16(ta[2], ones, accO);
+                accO = mfma_bf16(ta[1], ones, accO);
+                accO = mfma_bf16(ta[0], ones, accO);
+            }
         }
     }
 
+    if constexpr (HD == 2 * kD) {
+        // each wave owns its block over the whole chunk
+        constexpr int W64 = 2 * kD + 1;
+        float* dst = part + (((size_t)b * HP + hp) * P + p) * (2 * kD * W64);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = kD * hh + 8 * (r >> 2) + 4 * g + (r & 3);
+            dst[row * W64 + kD * th + j] = accV[r];
+            if (th == 0 && j == 0) dst[row * W64 + 2 * kD] = accO[r];
+        }
+        return;
+    }
     // Combine the two token halves of each head in a fixed order, then write.
     __syncthreads();
     float* red = reinterpret_cast<float*>(&lds[0][0][0][0]);   // [head][V|O][16][64] floats = 16 KiB
@@ -325,6 +350,10 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma_f32(
         }
     }
     __syncthreads();
+    if constexpr (HD == kD / 2) {
+        if (th == 0 && hh < nh) write_diag16(part, red, accV, accO, b, HR, P, p, h0 + hh, hh, lane);
+        return;
+    }
     if (th == 0 && hh < nh) {
         float* dst = part + (((size_t)b * H + h0 + hh) * P + p) * kStateFloats;
 #pragma unroll
@@ -490,16 +519,15 @@ constexpr int kOutPitch = 36;   // floats per LDS output row: 32 + 4 keeps rows 
 //    product gives both heads' numerators, and each head takes its own
 //    normaliser (K-step 0 is the first head's features, 1 the second's).
 template <typename InT, typename OutT, int HD>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 2 * kD ? 3 : std::is_same<InT, uint16_t>::value ? 5 : 4, 8))) void k_apply_mfma(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 2 * kD ? (std::is_same<InT, float>::value ? 2 : 3) : std::is_same<InT, uint16_t>::value ? 5 : 4, 8))) void k_apply_mfma(
     const InT* __restrict__ q, const float* __restrict__ state, OutT* __restrict__ out,
     int N, int H, int HP, int HR, int L, int NB, int tile, int tpb, float eps, Strides sq, Strides so) {
     constexpr bool F16 = std::is_same<InT, _Float16>::value;
     constexpr bool F32 = std::is_same<InT, float>::value;
     constexpr bool D64 = HD == 2 * kD, D16 = HD == kD / 2;
-    static_assert(HD == kD || !F32, "head dims 16 and 64 take 16-bit q");
     constexpr int KS = D64 ? 4 : 2;   // K-steps of 16 features
     constexpr int SW = HD + 1;        // state row
-    constexpr int QW = F32 ? 4 : KS;  // 16-byte pieces of a lane's q features (16 ks + 8 g .. + 7)
+    constexpr int QW = F32 ? 2 * KS : KS;   // 16-byte pieces of a lane's q features (16 ks + 8 g .. + 7)
     __shared__ __attribute__((aligned(16))) float otile[4][32 * kOutPitch];   // fp32 out only
 
     const int per_unit = NB * tpb;
@@ -568,11 +596,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 
     };
     const bool second = !D16 || 2 * hs + 1 < HR;   // head dim 16: group hs has a second head
     auto load_row = [&](const u32x4* src, QRow& r) {
-        if constexpr (F32) {   // features 8g..8g+7 = src[0..1], 16+8g..16+8g+7 = src[4..5]
-            r.x[0] = src[0];
-            r.x[1] = src[1];
-            r.x[2] = src[4];
-            r.x[3] = src[5];
+        if constexpr (F32) {   // features 16 ks + 8g..8g+7 = src[4 ks .. 4 ks + 1]
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bool on = !D16 || ks == 0 || second;   // head dim 16: the second head only if it exists
+                r.x[2 * ks] = on ? src[4 * ks] : (u32x4){0u, 0u, 0u, 0u};
+                r.x[2 * ks + 1] = on ? src[4 * ks + 1] : (u32x4){0u, 0u, 0u, 0u};
+            }
         } else if constexpr (D16) {   // the second head's features only if it exists
             r.x[0] = src[0];
             r.x[1] = second ? src[2] : (u32x4){0u, 0u, 0u, 0u};
@@ -601,9 +631,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 
         float dp = 0.f, dp1 = 0.f;   // dp1: head dim 16, the group's second head
         if constexpr (F32) {
             // f = ReLU(q) in fp32 (features 16 ks + 8 g + e at f[8 ks + e])
-            float f[16];
+            float f[8 * KS];
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+            for (int c = 0; c < QW; ++c)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     // through a scalar: bit_cast of a vector element expression
@@ -612,9 +642,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 
                     f[4 * c + e] = fmaxf(__builtin_bit_cast(float, bits), 0.f);
                 }
 #pragma unroll
-            for (int e = 0; e < 16; ++e) dp = fmaf(f[e], sden[e], dp);
+            for (int e = 0; e < 8 * KS; ++e) {
+                float& t = (D16 && e >= 8) ? dp1 : dp;
+                t = fmaf(f[e], sden[e], t);
+            }
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
+            for (int ks = 0; ks < KS; ++ks) {
                 u32x4 fb[3];
                 split3_trunc_f32x8(f + 8 * ks, fb);
                 // term pairs (S, q) with i + j <= 4, smallest first
@@ -811,9 +844,12 @@ hipError_t launch_state(const Plan& pl, const void* k, const void* v, float* par
     if (pl.mfma) {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.P);
         if (pl.in_dtype == 0)
-            hipLaunchKernelGGL(k_state_partial_mfma_f32, dim3(grid), dim3(kThreads), 0, stream,
-                               static_cast<const float*>(k), static_cast<const float*>(v), part, pl.N, pl.H, pl.HP,
-                               pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
+            by_head_dim(pl.D, [&](auto dd) {
+                constexpr int DD = decltype(dd)::value;
+                hipLaunchKernelGGL(k_state_partial_mfma_f32<DD>, dim3(grid), dim3(kThreads), 0, stream,
+                                   static_cast<const float*>(k), static_cast<const float*>(v), part, pl.N,
+                                   groups32(pl), pl.HP, pl.H, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
+            });
         else
             by_head_dim(pl.D, [&](auto dd) {
                 constexpr int DD = decltype(dd)::value;
@@ -853,19 +889,12 @@ hipError_t launch_apply(const Plan& pl, const void* q, const float* state, void*
             by_dtype(pl.out_dtype, [&](auto o) {
                 using IT = typename decltype(in)::type;
                 using OT = typename decltype(o)::type;
-                if constexpr (sizeof(IT) == 2) {
-                    by_head_dim(pl.D, [&](auto dd) {
-                        constexpr int DD = decltype(dd)::value;
-                        hipLaunchKernelGGL((k_apply_mfma<IT, OT, DD>), dim3(grid), dim3(kThreads), 0, stream,
-                                           static_cast<const IT*>(q), state, static_cast<OT*>(out), pl.N,
-                                           groups32(pl), pl.HP, pl.H, pl.L, pl.NB, pl.tile, pl.tpb, eps, pl.sq,
-                                           pl.so);
-                    });
-                } else {
-                    hipLaunchKernelGGL((k_apply_mfma<IT, OT, kD>), dim3(grid), dim3(kThreads), 0, stream,
-                                       static_cast<const IT*>(q), state, static_cast<OT*>(out), pl.N, pl.H, pl.HP,
-                                       pl.H, pl.L, pl.NB, pl.tile, pl.tpb, eps, pl.sq, pl.so);
-                }
+                by_head_dim(pl.D, [&](auto dd) {
+                    constexpr int DD = decltype(dd)::value;
+                    hipLaunchKernelGGL((k_apply_mfma<IT, OT, DD>), dim3(grid), dim3(kThreads), 0, stream,
+                                       static_cast<const IT*>(q), state, static_cast<OT*>(out), pl.N, groups32(pl),
+                                       pl.HP, pl.H, pl.L, pl.NB, pl.tile, pl.tpb, eps, pl.sq, pl.so);
+                });
             });
         });
     } else {

@@ -37,9 +37,8 @@
  *            fp16 out cannot overflow).  D is 32 (the Sana head dim, on the matrix
  *            cores; fp32 inputs as three-term bf16 splits with the products
  *            below 2^-24 dropped) or, for the forward entry points, 16 or
- *            64 (matrix cores for 16-bit inputs, which see a token row as
- *            32-feature groups; vector unit for fp32); the backward and the
- *            forward-mode derivative take D = 32.
+ *            64 (the same kernels on 32-feature groups of the token row);
+ *            the backward and the forward-mode derivative take D = 32.
  * Memory     Every pointer is device memory on the current HIP device, owned
  *            by the caller.  The library allocates nothing, keeps nothing
  *            after return, and never synchronises: work is enqueued on

@@ -42,7 +42,7 @@ def test_other_head_dims():
     assert sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 8, 256, 64, 0)["mfma"] == 1   # pairs of 32-feature halves
     assert sana.sana_linattn_plan_info(sana.SANA_DT_F16, 1, 8, 256, 64, 0)["mfma"] == 1
     assert sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 8, 256, 16, 0)["mfma"] == 1   # two heads per 32 features
-    assert sana.sana_linattn_plan_info(sana.SANA_DT_F32, 1, 8, 256, 16, 0)["mfma"] == 0
+    assert sana.sana_linattn_plan_info(sana.SANA_DT_F32, 1, 8, 256, 16, 0)["mfma"] == 1
     w16, w32, w64 = (sana.sana_linattn_workspace_bytes(1, 8, 4096, d, 0) for d in (16, 32, 64))
     assert w16 < w32 < w64
     for d in (8, 48, 128):
@@ -63,7 +63,7 @@ def test_workspace_and_plan_queries():
     assert info["mfma"] == 1 and info["chunk_tokens"] % 64 == 0 and info["apply_tokens"] % 64 == 0
     assert info["num_chunks"] * info["chunk_tokens"] >= 16384
     assert sana.sana_linattn_plan_info(sana.SANA_DT_F32, 1, 2, 256, 32, 0)["mfma"] == 1   # fp32 in: split terms
-    assert sana.sana_linattn_plan_info(sana.SANA_DT_F32, 1, 2, 256, 64, 0)["mfma"] == 0
+    assert sana.sana_linattn_plan_info(sana.SANA_DT_F32, 1, 2, 256, 64, 0)["mfma"] == 1
     f16 = sana.sana_linattn_plan_info(sana.SANA_DT_F16, 1, 70, 16384, 32, 0)
     assert f16["mfma"] == 1 and f16["apply_tokens"] >= info["apply_tokens"]   # fp16 apply: 4 work-groups per CU
     bc = sana.sana_linattn_plan_info(sana.SANA_DT_BF16, 1, 70, 16384, 32, 1000)

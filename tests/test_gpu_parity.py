@@ -326,19 +326,31 @@ HEAD_DIMS = [
     workloads.Workload("d16_B1_N4097_H5_L1_bf16", 1, 4097, 5, 16, workloads.DT_BF16, seed=133, block_len=1),
     workloads.Workload("d16_B2_N1000_H3_f32", 2, 1000, 3, 16, workloads.DT_F32, seed=134),
     workloads.Workload("d16_B1_N16384_H140_bf16", 1, 16384, 140, 16, workloads.DT_BF16, seed=135),
+    workloads.Workload("d16_B1_N777_H7_L256_f32", 1, 777, 7, 16, workloads.DT_F32, seed=136, block_len=256),
+    workloads.Workload("d64_B1_N16384_H35_f32", 1, 16384, 35, 64, workloads.DT_F32, seed=137),
+    workloads.Workload("d16_B1_N16384_H140_f32", 1, 16384, 140, 16, workloads.DT_F32, seed=138),
 ]
 
 
 @pytest.mark.parametrize("w", HEAD_DIMS, ids=lambda w: w.name)
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["f32out", "bf16out"])
 def test_other_head_dims(w, out_dtype):
-    """Head dims 16 and 64 against the oracle (16-bit inputs on the matrix
-    cores, fp32 inputs on the vector unit); 16384 tokens x 35 heads of 64 and
-    x 140 heads of 16 move the headline's bytes; odd and single heads of 16
+    """Head dims 16 and 64 against the oracle (matrix cores; fp32 inputs as
+    three-term splits); 16384 tokens x 35 heads of 64 and x 140 heads of 16
+    are the headline's token-head-feature count; odd and single heads of 16
     leave a 32-feature group half empty."""
     (q, k, v), want = inputs_and_oracle(w)
     got = run_hip(q, k, v, block_len=w.block_len, eps=w.eps, out_dtype=out_dtype)
     compare(got, want, v, out_dtype == torch.bfloat16, w.name)
+
+
+@pytest.mark.parametrize("w", [w for w in HEAD_DIMS if w.N < 16384], ids=lambda w: w.name)
+def test_other_head_dims_vector_path(monkeypatch, w):
+    """The vector-unit kernels (SANA_LINATTN_PATH=valu) for the same cases."""
+    monkeypatch.setenv("SANA_LINATTN_PATH", "valu")
+    (q, k, v), want = inputs_and_oracle(w)
+    got = run_hip(q, k, v, block_len=w.block_len, eps=w.eps, out_dtype=torch.float32)
+    compare(got, want, v, False, w.name + "/valu")
 
 
 def test_other_head_dims_streaming_and_strided():

@@ -369,6 +369,42 @@ def main() -> int:
             "note": "same-shape buffers as the non-causal run, block_len 1024"}
         del outs2, ws_bc
 
+        # streaming block-causal: the same sequence in 4 calls of 4096 tokens,
+        # the state carried between them (block_len 1024)
+        C = N // 4
+        ws_st = torch.empty(sana.sana_linattn_workspace_bytes(B, H, C, D, L), dtype=torch.uint8, device=dev)
+        carried = torch.empty((B, H, D, D + 1), dtype=torch.float32, device=dev)
+        chunks = [[[t[:, c * C:(c + 1) * C].contiguous() for t in st] for c in range(4)] for st in sets]
+        couts = [torch.empty((B, C, H, D), dtype=out_t, device=dev) for _ in range(4)]
+
+        def stream4(i):
+            for c in range(4):
+                q, k, v = chunks[i % NSETS][c]
+                sana.sana_linattn_blockcausal_stream_fwd(q, k, v, couts[c], ws_st, L,
+                                                         state_in=carried if c else None, state_out=carried,
+                                                         eps=w.eps, stream=stream)
+        ms = timed(stream4, args.steps)
+        extra["stream_4x4096_bc1024_" + args.out_dtype + "out"] = {
+            "ms_per_step": round(ms, 5), "GBps": round(alg_bytes / ms / 1e6, 1),
+            "pct_hbm_peak": round(100 * alg_bytes / ms / 1e6 / HBM_PEAK_GBPS, 2),
+            "note": "the headline sequence as 4 chained calls of 4096 tokens with the state carried "
+                    "(block_len 1024); ms per whole sequence"}
+        del chunks, couts, ws_st, carried
+
+        # q, k, v as strided views of one fused [B, N, 3, H, D] projection output
+        fused = [torch.stack(st, dim=2) for st in sets]
+
+        def strided(i):
+            f = fused[i % NSETS]
+            sana.sana_linattn_fwd_strided(f[:, :, 0], f[:, :, 1], f[:, :, 2], outs[i % NSETS], ws, eps=w.eps,
+                                          stream=stream)
+        ms = timed(strided, args.steps)
+        extra["fused_qkv_strided_" + args.out_dtype + "out"] = {
+            "ms_per_step": round(ms, 5), "GBps": round(alg_bytes / ms / 1e6, 1),
+            "pct_hbm_peak": round(100 * alg_bytes / ms / 1e6 / HBM_PEAK_GBPS, 2),
+            "note": "q, k, v read in place from one [B, N, 3, H, D] buffer (token stride 3 H D)"}
+        del fused
+
         # fp16 inputs (the same values, converted on the device), fp32 out
         sets16 = [[t.to(torch.float16) for t in st] for st in sets]
 

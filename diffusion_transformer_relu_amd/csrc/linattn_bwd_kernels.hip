@@ -279,30 +279,6 @@ __device__ __forceinline__ uint32_t positive_rows(const uint8_t* row, int g) {
     return m;
 }
 
-// The same mask from a row already loaded in the accumulator layout
-// (x[rr] = features 8 rr + 4 g .. + 3).
-__device__ __forceinline__ uint32_t positive_rows(const u32x2 x[4]) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const short hv = (short)((e & 1) ? (x[rr][e >> 1] >> 16) : (x[rr][e >> 1] & 0xffffu));
-            m |= (uint32_t)(hv > 0) << (4 * rr + e);
-        }
-    return m;
-}
-
-// The same mask from an fp32 row in the accumulator layout.
-__device__ __forceinline__ uint32_t positive_rows(const f32x4 x[4]) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) m |= (uint32_t)(x[rr][e] > 0.f) << (4 * rr + e);
-    return m;
-}
-
 // B operand of token `tok` of a staged tile: lane (g, i) gets features 8g..8g+7
 // and 16+8g..16+8g+7 of tensor ts, head hh.
 __device__ __forceinline__ void tile_operand(const uint8_t* lds, int ts, int hh, int tok, int g, u32x4& x0,
@@ -604,10 +580,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     auto body = [&](int tt, const Tile& x) {
         asm volatile("" ::: "memory");   // keep the LDS operands in LDS (see the key kernel)
         const int n = min(32, t1 - tt);
-        const uint32_t mask = positive_rows(x.qa.x);
         // f at this lane's accumulator rows (decoded where used, to keep few
-        // registers live); z = P[:, D] at the same rows
-        auto fa = [&](int rr, int e) { return fmaxf(x.qa.at(rr, e), 0.f); };
+        // registers live; f > 0 is the mask q > 0); z = P[:, D] at the same rows
+        auto fa = [&](int rr, int e) { return relu_f32(x.qa.at(rr, e)); };
         auto zrow = [&](int rr) { return *reinterpret_cast<const f32x4*>(&pzs[hh][8 * rr + 4 * g]); };
         float dp = 0.f;
 #pragma unroll
@@ -695,7 +670,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
         auto gather = [&](int tok, float& fv, float& uv, float& wv_) {
             if constexpr (kStage) {
                 const uint16_t fb = *reinterpret_cast<const uint16_t*>(qrows + tok * kTileRow + 2 * i);
-                fv = fmaxf(std::is_same<QT, _Float16>::value ? f16_to_f32(fb) : bf16_to_f32(fb), 0.f);
+                const uint16_t fr = relu_16(fb);
+                fv = std::is_same<QT, _Float16>::value ? f16_to_f32(fr) : bf16_to_f32(fr);
             } else {
                 fv = ft[tok * kPitch + i];
             }
@@ -729,7 +705,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int rg = 4 * rr + e;
-                acc[rg] = ((mask >> rg) & 1u) ? fmaf(z[e], w, acc[rg] * rs) : 0.f;
+                acc[rg] = fa(rr, e) > 0.f ? fmaf(z[e], w, acc[rg] * rs) : 0.f;
             }
         }
         __builtin_amdgcn_wave_barrier();

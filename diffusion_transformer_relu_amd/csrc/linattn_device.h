@@ -24,6 +24,15 @@ __device__ __forceinline__ uint32_t relu_bf16x2(uint32_t x) {
     return __builtin_bit_cast(uint32_t, s);
 }
 
+// ReLU of an fp32 value on its bits: as an int32 a float orders like its
+// sign, so max(bits, 0) keeps positives and maps negatives (and -0) to +0 in
+// one integer max (fmaxf also canonicalises its input: two instructions).
+__device__ __forceinline__ float relu_f32(float x) {
+    return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+// The same on one bf16 or fp16 value's bits (int16 order).
+__device__ __forceinline__ uint16_t relu_16(uint16_t h) { return (uint16_t)max((int)(short)h, 0); }
+
 __device__ __forceinline__ u32x4 relu_bf16x8(u32x4 x) {
     return (u32x4){relu_bf16x2(x[0]), relu_bf16x2(x[1]), relu_bf16x2(x[2]), relu_bf16x2(x[3])};
 }
@@ -260,7 +269,7 @@ struct F32Operand {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float t = x[2 * ks + (e >> 2)][e & 3];
-            out[e] = relu ? fmaxf(t, 0.f) : t;
+            out[e] = relu ? relu_f32(t) : t;
         }
     }
     // bit j set when feature j of the token is > 0 (the partner lane, i + 32,

@@ -297,7 +297,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float kk = r[0][e >> 2][e & 3];
-                x[0][e] = fmaxf(kk, 0.f);
+                x[0][e] = relu_f32(kk);
                 x[1][e] = r[1][e >> 2][e & 3];
                 x[2][e] = kk > 0.f ? r[2][e >> 2][e & 3] : 0.f;
                 x[3][e] = r[3][e >> 2][e & 3];

@@ -284,8 +284,8 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma_f32(
             float a[8], w[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                a[e] = fmaxf(rk[i][0][e], 0.f);
-                a[4 + e] = fmaxf(rk[i][1][e], 0.f);
+                a[e] = relu_f32(rk[i][0][e]);
+                a[4 + e] = relu_f32(rk[i][1][e]);
                 w[e] = rv[i][0][e];
                 w[4 + e] = rv[i][1][e];
             }
@@ -639,7 +639,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 
                     // through a scalar: bit_cast of a vector element expression
                     // reads the vector's first element with this compiler
                     const uint32_t bits = qr.x[c][e];
-                    f[4 * c + e] = fmaxf(__builtin_bit_cast(float, bits), 0.f);
+                    f[4 * c + e] = relu_f32(__builtin_bit_cast(float, bits));
                 }
 #pragma unroll
             for (int e = 0; e < 8 * KS; ++e) {

@@ -326,13 +326,15 @@ int make_jvp_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int b
                   bool allow_mfma = true) {
     const int st = make_plan(in_dtype, out_dtype, B, H, N, D, block_len, pl, allow_mfma);
     if (st != SANA_OK) return st;
-    if (D != sana::kD) return SANA_ERR_UNSUPPORTED;   // the forward-mode derivative is built for D = 32
+    // head dims 16 and 64 on the matrix cores only (the vector kernels are built for 32)
+    if (D != sana::kD && !pl->mfma && B > 0 && H > 0 && N > 0) return SANA_ERR_UNSUPPORTED;
     if (B == 0 || H == 0 || N == 0) return SANA_OK;
     const size_t bh2 = (size_t)B * H * 2;
     if ((long long)bh2 > INT_MAX) return SANA_ERR_UNSUPPORTED;
+    const size_t sf = (size_t)D * (D + 1);
     pl->off_part = 0;
-    pl->off_state = round_up((long)(bh2 * pl->P * sana::kStateFloats * sizeof(float)), 256);
-    pl->bytes = pl->off_state + round_up((long)(bh2 * pl->NB * sana::kStateFloats * sizeof(float)), 256);
+    pl->off_state = round_up((long)(bh2 * pl->P * sf * sizeof(float)), 256);
+    pl->bytes = pl->off_state + round_up((long)(bh2 * pl->NB * sf * sizeof(float)), 256);
     return SANA_OK;
 }
 
@@ -438,6 +440,7 @@ int sana_linattn_jvp_workspace_bytes(int B, int H, int N, int D, int block_len, 
         for (bool mf : {true, false}) {   // the vector path's plan too (SANA_LINATTN_PATH=valu)
             Plan pl;
             const int st = make_jvp_plan(dt, SANA_DT_F32, B, H, N, D, block_len, &pl, mf);
+            if (st == SANA_ERR_UNSUPPORTED && !mf && D != sana::kD) continue;   // no vector path for that dim
             if (st != SANA_OK) return st;
             most = std::max(most, pl.bytes);
         }

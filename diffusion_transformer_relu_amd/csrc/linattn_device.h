@@ -184,6 +184,98 @@ __device__ __forceinline__ void state_operands(const float* S, int lane, bool tr
     }
 }
 
+// K-steps of 16 features in a 32-column block's product for head dim HD
+// (the kernels see a token row as 32-feature groups: a head of 64 is two, a
+// group holds two heads of 16).
+template <int HD> struct KSteps { static constexpr int value = HD == 2 * kD ? 4 : 2; };
+
+// A operands of out^T = S^T f^T for one 32-column block of head-dim HD states,
+// as three bf16 terms (each the round-to-nearest bf16 of what the previous
+// ones left, remainders exact), and the normaliser entries at this lane's
+// features: lane (g, i) gets S[16 ks + 8 g + e][c(i)] in sa[ks][sp] (element
+// e) and S[16 ks + 8 g + e][HD] in z[8 ks + e].  head(r) points at head r's
+// HD x (HD + 1) state.
+//   HD = 32: head grp, c(i) = i.
+//   HD = 64: head grp, c(i) = 32 half + i (four K-steps).
+//   HD = 16: heads 2 grp (K-step 0) and 2 grp + 1 (K-step 1; zero when
+//            there is none, grp's row then being a lone head) as one
+//            block-diagonal matrix: K-step ks is nonzero in columns 16 ks ..
+//            16 ks + 15 only.
+template <int HD, typename HeadState>
+__device__ __forceinline__ void apply_operands(HeadState head, int grp, int half, int HR, int lane,
+                                               u32x4 (&sa)[KSteps<HD>::value][3],
+                                               float (&z)[8 * KSteps<HD>::value]) {
+    constexpr int KS = KSteps<HD>::value, SW = HD + 1;
+    const int g = lane >> 5, i = lane & 31;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const float* S;
+        bool on = true, zon = true;
+        int row0, col;
+        if constexpr (HD == kD / 2) {
+            const int hr = 2 * grp + ks;
+            zon = hr < HR;
+            on = zon && (i >> 4) == ks;
+            S = head(min(hr, HR - 1));
+            row0 = 0;
+            col = i & 15;
+        } else {
+            S = head(grp);
+            row0 = 16 * ks;
+            col = (HD == 2 * kD ? kD * half : 0) + i;
+        }
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t w[3] = {0u, 0u, 0u};
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int row = row0 + 8 * g + 2 * d + hf;
+                float r = on ? S[row * SW + col] : 0.f;
+                z[8 * ks + 2 * d + hf] = zon ? S[row * SW + HD] : 0.f;
+#pragma unroll
+                for (int sp = 0; sp < 3; ++sp) {   // S = hi + mid + lo, each remainder exact
+                    const uint16_t t = f32_to_bf16(r);
+                    r -= bf16_to_f32(t);
+                    w[sp] |= (uint32_t)t << (16 * hf);
+                }
+            }
+#pragma unroll
+            for (int sp = 0; sp < 3; ++sp) sa[ks][sp][d] = w[sp];
+        }
+    }
+}
+
+// acc += A B over KS K-steps, B a 16-bit operand per K-step (bf16 exact;
+// fp16 split exactly into two bf16 terms), A three split terms; small terms
+// first.  For KS = 2 this is mma_split below.
+template <bool F16, int KS>
+__device__ __forceinline__ f32x16 mma_split_ks(const u32x4 (&A)[KS][3], const u32x4 (&b)[KS], f32x16 acc) {
+    if constexpr (F16) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 hi, lo;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                uint32_t h, l;
+                float f0, f1;
+                split_f16x2(b[ks][d], h, l, f0, f1);
+                hi[d] = h;
+                lo[d] = l;
+            }
+#pragma unroll
+            for (int sp = 2; sp >= 0; --sp) acc = mfma_bf16(A[ks][sp], lo, acc);
+#pragma unroll
+            for (int sp = 2; sp >= 0; --sp) acc = mfma_bf16(A[ks][sp], hi, acc);
+        }
+    } else {
+#pragma unroll
+        for (int sp = 2; sp >= 0; --sp)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16(A[ks][sp], b[ks], acc);
+    }
+    return acc;
+}
+
 // acc += sum over the 32 features of A (three split terms) times the B operand
 // b0 (features 8g..8g+7 of this lane's token) and b1 (features 16+8g..): bf16
 // bits, or fp16 bits split exactly into two bf16 terms.  Small terms first.
@@ -237,9 +329,11 @@ __device__ __forceinline__ uint32_t nonzero_mask(u32x4 x0, u32x4 x1, int g) {
 // stores whole rows: dst(t) is the output row of token tt + t.  Rows t >= n
 // were computed from the clamped input row n - 1, so they hold exactly row
 // n - 1's values: they are stored there again (the same values), which keeps
-// every store unconditional.
+// the row stores unconditional.  Only the first ncols columns of each row are
+// stored (16 for a 32-feature group that is a lone head of dim 16).
 template <typename OutT, typename RowPtr>
-__device__ __forceinline__ void store_tile(float* ot, const f32x16& acc, int lane, int n, RowPtr dst) {
+__device__ __forceinline__ void store_tile(float* ot, const f32x16& acc, int lane, int n, RowPtr dst,
+                                           int ncols = 32) {
     const int g = lane >> 5, i = lane & 31;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
@@ -250,19 +344,22 @@ __device__ __forceinline__ void store_tile(float* ot, const f32x16& acc, int lan
     for (int s4 = 0; s4 < 4; ++s4) {
         const int r = 8 * s4 + (lane >> 3), cc = (lane & 7) * 4;
         const f32x4 x = *reinterpret_cast<const f32x4*>(ot + r * kPitch + cc);
-        store4(dst(min(r, n - 1)) + cc, x);
+        if (cc < ncols) store4(dst(min(r, n - 1)) + cc, x);
     }
     __builtin_amdgcn_wave_barrier();
 }
 
 // fp32 inputs: features 8g..8g+7 and 16+8g..16+8g+7 of an fp32 row (the B
-// operand layout), 4 x 16 bytes.
+// operand layout), 4 x 16 bytes.  upper = false leaves features 16.. as zero
+// without reading them (a 32-feature group that is a lone head of dim 16).
 struct F32Operand {
     f32x4 x[4];
-    __device__ __forceinline__ void load(const float* row, int g) {
+    __device__ __forceinline__ void load(const float* row, int g, bool upper = true) {
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-            x[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 16 * (p >> 1) + 8 * g + 4 * (p & 1)));
+            x[p] = (p < 2 || upper)
+                       ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 16 * (p >> 1) + 8 * g + 4 * (p & 1)))
+                       : (f32x4){0.f, 0.f, 0.f, 0.f};
     }
     // the 8 values of half ks (features 16 ks + 8 g ..), optionally ReLU'd
     __device__ __forceinline__ void half(int ks, bool relu, float out[8]) const {

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sana {
 
 constexpr int kD = 32;                    // head dim of the matrix-core kernels (every Sana model: 32)
@@ -38,19 +40,33 @@ struct Plan {
     int B, H, N;
     int L;        // block length in tokens (N for the non-causal operator)
     int NB;       // number of blocks
-    int HP;       // head units per batch: head pairs (matrix path) or heads (vector path)
+    int HP;       // units per batch: pairs of 32-feature groups (matrix path) or heads (vector path)
     int chunk;    // tokens per state chunk (multiple of 64)
     int cpb;      // chunks per block
     int P;        // chunks per (b, h) = NB * cpb
     int tile;     // tokens per apply work-group
     int tpb;      // apply work-groups per block
-    int mfma;     // 1: matrix-core forward kernels (D = 32; bf16, fp16 or fp32 inputs), 0: vector kernels
-    int mfma16;   // 1: mfma with 16-bit inputs (the backward and JVP matrix-core kernels need them)
-    int D;        // head dim: 32, or 16 / 64 (vector kernels only)
+    int mfma;     // 1: matrix-core kernels, 0: vector kernels
+    int mfma16;   // 1: mfma with 16-bit inputs
+    int D;        // head dim: 16, 32 or 64
     int in_dtype, out_dtype;
     size_t off_part, off_state, bytes;
     Strides sq, sk, sv, so;   // element strides of q, k, v, out
 };
+
+// 32-feature groups of a token row: the "heads" of the matrix-core kernels (a
+// head of dim 64 is two groups, a group holds two heads of dim 16).
+inline int groups32(const Plan& pl) { return (pl.H * pl.D + kD - 1) / kD; }
+
+// Calls f with std::integral_constant<int, D> for a head dim D of 16, 32 or 64.
+template <typename F> void by_head_dim(int D, F&& f) {
+    if (D == 16)
+        f(std::integral_constant<int, 16>{});
+    else if (D == 64)
+        f(std::integral_constant<int, 64>{});
+    else
+        f(std::integral_constant<int, 32>{});
+}
 
 // Each launcher enqueues one kernel on `stream` and returns hipGetLastError().
 hipError_t launch_state(const Plan& pl, const void* k, const void* v, float* part, hipStream_t stream);

@@ -27,6 +27,72 @@ __device__ __forceinline__ u32x4 keep_where_nonzero(u32x4 a, u32x4 t) {
                    keep_where_nonzero(a[3], t[3])};
 }
 
+// Writes a chunk's state and tangent-state partials, part[((b * HR + head) * 2
+// + s) * P + p] (s = 0 the state, 1 the tangent state), from each wave's four
+// accumulators acc = {S_v, S_z, St_v, St_z} (row 8 (r / 4) + 4 g + r % 4 of
+// column j in register r of lane (g, j)).  Must be reached by the whole
+// work-group.
+//  - HD = 32 and 16: wave (hh, th) holds token half th of group h0 + hh's
+//    sums; the halves are added in a fixed order through red (LDS, [head][4]
+//    [16][64] floats).  HD = 16 keeps each group's diagonal 16 x 16 blocks, the
+//    states of heads 2 (h0 + hh) and 2 (h0 + hh) + 1.
+//  - HD = 64: wave (hh, th) holds the whole sums of block (K group hh, V group
+//    th) of head h0 / 2 and writes them itself (V group 0 also the z column).
+template <int HD>
+__device__ __forceinline__ void jvp_write_partials(float* part, float* red, const f32x16 (&acc)[4], int b, int HR,
+                                                   int h0, int nh, int P, int p, int hh, int th, int lane) {
+    constexpr int SW = HD + 1, SF = HD * SW;
+    const int g = lane >> 5, j = lane & 31;
+    if constexpr (HD == 2 * kD) {
+        const size_t bh = (size_t)b * HR + h0 / 2;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            float* dst = part + ((bh * 2 + s) * P + p) * SF;
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) {
+                const int row = kD * hh + 8 * (rg >> 2) + 4 * g + (rg & 3);
+                dst[row * SW + kD * th + j] = acc[2 * s][rg];
+                if (th == 0 && j == 0) dst[row * SW + HD] = acc[2 * s + 1][rg];
+            }
+        }
+        return;
+    }
+    __syncthreads();   // the tiles in red's space have been consumed
+    if (th == 1) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) red[((hh * 4 + q4) * 16 + rg) * 64 + lane] = acc[q4][rg];
+    }
+    __syncthreads();
+    if (th != 0 || hh >= nh) return;
+    auto sum = [&](int q4, int rg) { return acc[q4][rg] + red[((hh * 4 + q4) * 16 + rg) * 64 + lane]; };
+#pragma unroll
+    for (int rg = 0; rg < 16; ++rg) {
+        int head, row, col;
+        if constexpr (HD == kD / 2) {
+            // rows 0..15 (rg < 8) are the group's first head, 16..31 its second;
+            // the lanes of columns of the same half hold that head's state
+            const int half = rg >> 3;
+            head = 2 * (h0 + hh) + half;
+            if ((j >> 4) != half || head >= HR) continue;
+            row = 8 * ((rg >> 2) & 1) + 4 * g + (rg & 3);
+            col = j & 15;
+        } else {
+            head = h0 + hh;
+            row = 8 * (rg >> 2) + 4 * g + (rg & 3);
+            col = j;
+        }
+        const size_t bh = (size_t)b * HR + head;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            float* dst = part + ((bh * 2 + s) * P + p) * SF;
+            dst[row * SW + col] = sum(2 * s, rg);
+            if (col == 0) dst[row * SW + HD] = sum(2 * s + 1, rg);
+        }
+    }
+}
+
 // ------------------------------------------------------------------ state and tangent state, MFMA
 // As the forward's state kernel, with four tensors in the LDS tile:
 // [a | v | at | vt][head 0|1][token][32 x 16 bit].
@@ -35,13 +101,17 @@ constexpr int kJTensor = 2 * kJHead;
 constexpr int kJPieces = kStateTile / 32;
 static_assert(4 * kJTensor >= 2 * 4 * 16 * 64 * (int)sizeof(float), "reduction area exceeds the LDS tile");
 
-// grid.x = (b * HP + hp) * P + p.  Partials: part[((b * H + h) * 2 + s) * P + p],
-// s = 0 the state, s = 1 the tangent state.
-template <bool F16>
+// grid.x = (b * HP + hp) * P + p.  Partials as jvp_write_partials.  Head dims
+// 16 and 64 as in the forward's state kernel: H counts the 32-feature groups
+// of a token row, HP their pairs, HR the real heads (rows of HR * HD elements;
+// pieces past the row read as zero); HD = 64: wave w accumulates block (K
+// group w & 1, V group w >> 1) over all tokens of each tile.
+template <bool F16, int HD>
 __global__ __launch_bounds__(kThreads) void k_jvp_state_mfma(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const uint16_t* __restrict__ kt,
-    const uint16_t* __restrict__ vt, float* __restrict__ part, int N, int H, int HP, int L, int cpb, int P,
+    const uint16_t* __restrict__ vt, float* __restrict__ part, int N, int H, int HP, int HR, int L, int cpb, int P,
     int chunk) {
+    constexpr bool D64 = HD == 2 * kD;
     __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kJTensor];
 
     const int p = blockIdx.x % P;
@@ -52,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void k_jvp_state_mfma(
     const ChunkRange cr = chunk_range(p, cpb, chunk, L, N);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hh = wave & 1, th = wave >> 1;
-    const long long hstride = (long long)H * kD;
+    const long long hstride = (long long)HR * HD;
     const uint16_t* src[4] = {k, v, kt, vt};
 
     u32x4 r[4][kJPieces];
@@ -62,8 +132,10 @@ __global__ __launch_bounds__(kThreads) void k_jvp_state_mfma(
             const int pc = tid + kThreads * i;
             const int part_ = pc & 3, hd = (pc >> 2) & 1, tok = pc >> 3;
             const int n = t0 + tok;
-            const bool ok = n < cr.c1 && hd < nh;
-            const long long off = ((long long)b * N + (ok ? n : cr.c0)) * hstride + (h0 + (ok ? hd : 0)) * kD + part_ * 8;
+            const int col = (h0 + hd) * kD + part_ * 8;
+            const bool ok = n < cr.c1 && col < HR * HD;
+            // a piece outside the range reads the range's first row, column 0 (in bounds)
+            const long long off = ((long long)b * N + (ok ? n : cr.c0)) * hstride + (ok ? col : 0);
 #pragma unroll
             for (int ts = 0; ts < 4; ++ts) {
                 const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src[ts] + off));
@@ -72,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void k_jvp_state_mfma(
         }
     };
 
-    f32x16 accV = {}, accO = {}, accVt = {}, accOt = {};
+    f32x16 acc[4] = {};   // S_v, S_z, St_v, St_z
     constexpr uint32_t kOne2 = F16 ? 0x3c003c00u : 0x3f803f80u;
     const u32x4 ones = {kOne2, kOne2, kOne2, kOne2};
     const int g = lane >> 5, j = lane & 31;
@@ -94,13 +166,15 @@ __global__ __launch_bounds__(kThreads) void k_jvp_state_mfma(
         __syncthreads();
         if (t0 + kStateTile < cr.c1) load_tile(t0 + kStateTile);
 
+        // K group hh (a, at); V group hh, or th for HD = 64 (v, vt)
         const uint16_t* T[4];
 #pragma unroll
-        for (int ts = 0; ts < 4; ++ts) T[ts] = reinterpret_cast<const uint16_t*>(lds + ts * kJTensor + hh * kJHead);
+        for (int ts = 0; ts < 4; ++ts)
+            T[ts] = reinterpret_cast<const uint16_t*>(lds + ts * kJTensor + ((D64 && (ts & 1)) ? th : hh) * kJHead);
 #pragma unroll
-        for (int st = 0; st < kStateTile / 32; ++st) {
+        for (int st = 0; st < (D64 ? kStateTile / 16 : kStateTile / 32); ++st) {
             // element e of lane (g, j) is token tb + 2e + g (row j of a, at; column j of v, vt)
-            const int tb = (kStateTile / 2) * th + 16 * st;
+            const int tb = D64 ? 16 * st : (kStateTile / 2) * th + 16 * st;
             u32x4 op[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -109,49 +183,56 @@ __global__ __launch_bounds__(kThreads) void k_jvp_state_mfma(
 #pragma unroll
                 for (int ts = 0; ts < 4; ++ts) op[ts][t] = (uint32_t)T[ts][r0] | ((uint32_t)T[ts][r1] << 16);
             }
-            accV = mfma16<F16>(op[0], op[1], accV);
-            accO = mfma16<F16>(op[0], ones, accO);
-            accVt = mfma16<F16>(op[2], op[1], accVt);
-            accVt = mfma16<F16>(op[0], op[3], accVt);
-            accOt = mfma16<F16>(op[2], ones, accOt);
+            acc[0] = mfma16<F16>(op[0], op[1], acc[0]);
+            if (!D64 || th == 0) acc[1] = mfma16<F16>(op[0], ones, acc[1]);
+            acc[2] = mfma16<F16>(op[2], op[1], acc[2]);
+            acc[2] = mfma16<F16>(op[0], op[3], acc[2]);
+            if (!D64 || th == 0) acc[3] = mfma16<F16>(op[2], ones, acc[3]);
         }
     }
+    jvp_write_partials<HD>(part, reinterpret_cast<float*>(lds), acc, b, HR, h0, nh, P, p, hh, th, lane);
+}
 
-    __syncthreads();
-    float* red = reinterpret_cast<float*>(lds);   // [head][4][16][64]
-    const f32x16* accs[4] = {&accV, &accO, &accVt, &accOt};
-    if (th == 1) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-            for (int rg = 0; rg < 16; ++rg) red[((hh * 4 + q4) * 16 + rg) * 64 + lane] = (*accs[q4])[rg];
+// out = num r and out_t = (num_t - out den_t) r, r = 1 / (den + eps), from
+// this lane's partial normaliser dot products (its half of the features; the
+// partner lane i + 32 holds the other).  Head dim 16 (D16): rows 0..15 (r < 8)
+// are the group's first head (dp, dpt), 16..31 its second (dp1, dpt1).
+template <bool D16>
+__device__ __forceinline__ void finish_tangent(f32x16& acc, f32x16& acct, float dp, float dpt, float dp1, float dpt1,
+                                               float eps) {
+    const float den = dp + __shfl_xor(dp, 32);
+    const float dent = dpt + __shfl_xor(dpt, 32);
+    const float rinv = 1.0f / (den + eps);
+    float rinv1 = rinv, dent1 = dent;
+    if constexpr (D16) {
+        const float den1 = dp1 + __shfl_xor(dp1, 32);
+        dent1 = dpt1 + __shfl_xor(dpt1, 32);
+        rinv1 = 1.0f / (den1 + eps);
     }
-    __syncthreads();
-    if (th == 0 && hh < nh) {
-        const size_t bh = (size_t)b * H + h0 + hh;
-        float* dS = part + ((bh * 2 + 0) * P + p) * kStateFloats;
-        float* dT = part + ((bh * 2 + 1) * P + p) * kStateFloats;
 #pragma unroll
-        for (int rg = 0; rg < 16; ++rg) {
-            const int row = 8 * (rg >> 2) + 4 * g + (rg & 3);
-            dS[row * kW + j] = accV[rg] + red[((hh * 4 + 0) * 16 + rg) * 64 + lane];
-            dT[row * kW + j] = accVt[rg] + red[((hh * 4 + 2) * 16 + rg) * 64 + lane];
-            if (j == 0) {
-                dS[row * kW + kD] = accO[rg] + red[((hh * 4 + 1) * 16 + rg) * 64 + lane];
-                dT[row * kW + kD] = accOt[rg] + red[((hh * 4 + 3) * 16 + rg) * 64 + lane];
-            }
-        }
+    for (int rg = 0; rg < 16; ++rg) {
+        const float r = (D16 && rg >= 8) ? rinv1 : rinv;
+        const float dt = (D16 && rg >= 8) ? dent1 : dent;
+        const float o = acc[rg] * r;
+        acc[rg] = o;
+        acct[rg] = (acct[rg] - o * dt) * r;
     }
 }
 
 // ------------------------------------------------------------------ output and tangent, MFMA
-// grid.x = (b * HP + hp) * (NB * tpb) + beta * tpb + tile; wave w: head
-// 2*hp + (w & 1), every other 32-token sub-tile (w >> 1).
-template <bool F16, typename OutT>
+// grid.x = (b * HP + hp) * (NB * tpb) + beta * tpb + tile; wave w: 32-feature
+// group 2*hp + (w & 1) of the token row, every other 32-token sub-tile
+// (w >> 1).  H counts the groups, HR the real heads.  Head dim 32: the group
+// is head 2 hp + (w & 1); 64: output half w & 1 of head hp, reducing over all
+// 64 features of q; 16: heads 2 h and 2 h + 1 of group h against their
+// block-diagonal states, each with its own normalisers (see apply_operands).
+template <bool F16, typename OutT, int HD>
 __global__ __launch_bounds__(kThreads) void k_jvp_apply_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ qt, const float* __restrict__ state,
-    OutT* __restrict__ out, OutT* __restrict__ outt, int N, int H, int HP, int L, int NB, int tile, int tpb,
+    OutT* __restrict__ out, OutT* __restrict__ outt, int N, int H, int HP, int HR, int L, int NB, int tile, int tpb,
     float eps) {
+    constexpr int KS = KSteps<HD>::value, SF = HD * (HD + 1);
+    constexpr bool D64 = HD == 2 * kD, D16 = HD == kD / 2;
     __shared__ __attribute__((aligned(16))) float otile[4][32 * kPitch];
 
     const int per_unit = NB * tpb;
@@ -167,74 +248,86 @@ __global__ __launch_bounds__(kThreads) void k_jvp_apply_mfma(
     if (t0 >= t1) return;
     const int g = lane >> 5, i = lane & 31;
 
-    const size_t bh = (size_t)b * H + h;
-    const float* S = state + ((bh * 2 + 0) * NB + beta) * kStateFloats;
-    const float* St = state + ((bh * 2 + 1) * NB + beta) * kStateFloats;
-    u32x4 sa[2][3], sat[2][3];
-    state_operands(S, lane, true, sa);
-    state_operands(St, lane, true, sat);
-    float sz[16], szt[16];   // S[:, D] and St[:, D] at this lane's features 16 ks + 8 g + e
+    const size_t bhr = (size_t)b * HR;
+    auto head_S = [&](int hr) { return state + (((bhr + hr) * 2 + 0) * NB + beta) * SF; };
+    auto head_St = [&](int hr) { return state + (((bhr + hr) * 2 + 1) * NB + beta) * SF; };
+    u32x4 sa[KS][3], sat[KS][3];
+    // S[:, D] and St[:, D] at this lane's features 16 ks + 8 g + e, kept in
+    // the wave's LDS (the same for all lanes of a half): registers go to the
+    // operands
+    __shared__ __attribute__((aligned(16))) float zlds[4][2][2][8 * KS];   // [wave][S | St][g]
+    {
+        float sz[8 * KS], szt[8 * KS];
+        apply_operands<HD>(head_S, D64 ? hp : h, wave & 1, HR, lane, sa, sz);
+        apply_operands<HD>(head_St, D64 ? hp : h, wave & 1, HR, lane, sat, szt);
+        if (i == 0) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            sz[8 * ks + e] = S[(16 * ks + 8 * g + e) * kW + kD];
-            szt[8 * ks + e] = St[(16 * ks + 8 * g + e) * kW + kD];
+            for (int e = 0; e < 8 * KS; ++e) {
+                zlds[wave][0][g][e] = sz[e];
+                zlds[wave][1][g][e] = szt[e];
+            }
         }
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+    }
+    const float* sz = zlds[wave][0][g];
+    const float* szt = zlds[wave][1][g];
 
-    const long long hstride = (long long)H * kD;
+    const long long hstride = (long long)HR * HD;
+    const int qcol = (D64 ? 2 * hp : h) * kD + 8 * g;   // this lane's first q feature in the row
+    const bool second = !D16 || 2 * h + 1 < HR;       // head dim 16: the group has a second head
+    const int ncols = second ? 32 : 16;
     float* ot = otile[wave];
     for (int tt = t0 + 32 * (wave >> 1); tt < t1; tt += 64) {
         const int row = min(tt + i, t1 - 1);   // clamped rows repeat the last row (see store_tile)
-        const u32x4* srcq = reinterpret_cast<const u32x4*>(q + ((long long)b * N + row) * hstride + h * kD + 8 * g);
-        const u32x4* srct = reinterpret_cast<const u32x4*>(qt + ((long long)b * N + row) * hstride + h * kD + 8 * g);
-        const u32x4 f0 = relu_bf16x8(srcq[0]), f1 = relu_bf16x8(srcq[2]);
-        const u32x4 ft0 = keep_where_nonzero(f0, srct[0]), ft1 = keep_where_nonzero(f1, srct[2]);
+        const u32x4* srcq = reinterpret_cast<const u32x4*>(q + ((long long)b * N + row) * hstride + qcol);
+        const u32x4* srct = reinterpret_cast<const u32x4*>(qt + ((long long)b * N + row) * hstride + qcol);
+        u32x4 f[KS], ft[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bool on = ks == 0 || second;   // features 16 ks + 8 g .. + 7 = src[2 ks]
+            f[ks] = relu_bf16x8(on ? srcq[2 * ks] : (u32x4){0u, 0u, 0u, 0u});
+            ft[ks] = keep_where_nonzero(f[ks], on ? srct[2 * ks] : (u32x4){0u, 0u, 0u, 0u});
+        }
         const int n = min(32, t1 - tt);
 
         f32x16 acc = {}, acct = {};
-        acc = mma_split<F16>(sa, f0, f1, acc);
-        acct = mma_split<F16>(sat, f0, f1, acct);
-        acct = mma_split<F16>(sa, ft0, ft1, acct);
-        float dp = 0.f, dpt = 0.f;
+        acc = mma_split_ks<F16, KS>(sa, f, acc);
+        acct = mma_split_ks<F16, KS>(sat, f, acct);
+        acct = mma_split_ks<F16, KS>(sa, ft, acct);
+        float dp = 0.f, dpt = 0.f, dp1 = 0.f, dpt1 = 0.f;   // dp1, dpt1: head dim 16, the second head
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const u32x4 fx = ks ? f1 : f0, fy = ks ? ft1 : ft0;
+        for (int ks = 0; ks < KS; ++ks) {
+            float& a = (D16 && ks == 1) ? dp1 : dp;
+            float& at = (D16 && ks == 1) ? dpt1 : dpt;
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 float x0, x1, y0, y1;
                 if constexpr (F16) {
-                    x0 = f16_to_f32((uint16_t)(fx[d] & 0xffffu));
-                    x1 = f16_to_f32((uint16_t)(fx[d] >> 16));
-                    y0 = f16_to_f32((uint16_t)(fy[d] & 0xffffu));
-                    y1 = f16_to_f32((uint16_t)(fy[d] >> 16));
+                    x0 = f16_to_f32((uint16_t)(f[ks][d] & 0xffffu));
+                    x1 = f16_to_f32((uint16_t)(f[ks][d] >> 16));
+                    y0 = f16_to_f32((uint16_t)(ft[ks][d] & 0xffffu));
+                    y1 = f16_to_f32((uint16_t)(ft[ks][d] >> 16));
                 } else {
-                    x0 = lo_bf16(fx[d]);
-                    x1 = hi_bf16(fx[d]);
-                    y0 = lo_bf16(fy[d]);
-                    y1 = hi_bf16(fy[d]);
+                    x0 = lo_bf16(f[ks][d]);
+                    x1 = hi_bf16(f[ks][d]);
+                    y0 = lo_bf16(ft[ks][d]);
+                    y1 = hi_bf16(ft[ks][d]);
                 }
                 const int e = 8 * ks + 2 * d;
-                dp = fmaf(x0, sz[e], dp);
-                dp = fmaf(x1, sz[e + 1], dp);
-                dpt = fmaf(x0, szt[e], dpt);
-                dpt = fmaf(x1, szt[e + 1], dpt);
-                dpt = fmaf(y0, sz[e], dpt);
-                dpt = fmaf(y1, sz[e + 1], dpt);
+                a = fmaf(x0, sz[e], a);
+                a = fmaf(x1, sz[e + 1], a);
+                at = fmaf(x0, szt[e], at);
+                at = fmaf(x1, szt[e + 1], at);
+                at = fmaf(y0, sz[e], at);
+                at = fmaf(y1, sz[e + 1], at);
             }
         }
-        const float den = dp + __shfl_xor(dp, 32);
-        const float dent = dpt + __shfl_xor(dpt, 32);
-        const float rinv = 1.0f / (den + eps);
-#pragma unroll
-        for (int rg = 0; rg < 16; ++rg) {
-            const float o = acc[rg] * rinv;
-            acc[rg] = o;
-            acct[rg] = (acct[rg] - o * dent) * rinv;
-        }
-        store_tile<OutT>(ot, acc, lane, n, [&](int t) { return out + ((long long)b * N + tt + t) * hstride + h * kD; });
+        finish_tangent<D16>(acc, acct, dp, dpt, dp1, dpt1, eps);
+        store_tile<OutT>(ot, acc, lane, n, [&](int t) { return out + ((long long)b * N + tt + t) * hstride + h * kD; },
+                         ncols);
         store_tile<OutT>(ot, acct, lane, n,
-                         [&](int t) { return outt + ((long long)b * N + tt + t) * hstride + h * kD; });
+                         [&](int t) { return outt + ((long long)b * N + tt + t) * hstride + h * kD; }, ncols);
     }
 }
 
@@ -251,9 +344,12 @@ __global__ __launch_bounds__(kThreads) void k_jvp_apply_mfma(
 constexpr int kJF32Tok = 32;
 constexpr int kJF32Tile = kJF32Tok * kD;   // 16-bit elements of one term tile of one head
 
+template <int HD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_jvp_state_mfma_f32(
     const float* __restrict__ k, const float* __restrict__ v, const float* __restrict__ kt,
-    const float* __restrict__ vt, float* __restrict__ part, int N, int H, int HP, int L, int cpb, int P, int chunk) {
+    const float* __restrict__ vt, float* __restrict__ part, int N, int H, int HP, int HR, int L, int cpb, int P,
+    int chunk) {
+    constexpr bool D64 = HD == 2 * kD;
     __shared__ __attribute__((aligned(16))) uint16_t lds[4][3][2][kJF32Tile];   // [a | v | at | vt][term][head]
     static_assert(sizeof(lds) >= 2 * 4 * 16 * 64 * sizeof(float), "reduction area exceeds the LDS tile");
 
@@ -265,8 +361,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
     const ChunkRange cr = chunk_range(p, cpb, chunk, L, N);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hh = wave & 1, th = wave >> 1;
-    const int g = lane >> 5, j = lane & 31;
-    const long long hstride = (long long)H * kD;
+    const long long hstride = (long long)HR * HD;
     const float* src[4] = {k, v, kt, vt};
 
     // this thread's piece of a tile: part (tid & 3) = features 8 part .. + 7,
@@ -275,8 +370,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
     f32x4 r[4][2];
     auto load_tile = [&](int t0) {
         const int n = t0 + tok;
-        const bool ok = n < cr.c1 && hd < nh;
-        const long long off = ((long long)b * N + (ok ? n : cr.c0)) * hstride + (h0 + (ok ? hd : 0)) * kD + part_ * 8;
+        const int col = (h0 + hd) * kD + part_ * 8;
+        const bool ok = n < cr.c1 && col < HR * HD;
+        // a piece outside the range reads the range's first row, column 0 (in bounds)
+        const long long off = ((long long)b * N + (ok ? n : cr.c0)) * hstride + (ok ? col : 0);
 #pragma unroll
         for (int ts = 0; ts < 4; ++ts) {
             const f32x4* s = reinterpret_cast<const f32x4*>(src[ts] + off);
@@ -286,7 +383,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
         }
     };
 
-    f32x16 accV = {}, accO = {}, accVt = {}, accOt = {};
+    f32x16 acc[4] = {};   // S_v, S_z, St_v, St_z
     const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0 pairs
 
     if (cr.c0 < cr.c1) load_tile(cr.c0);
@@ -314,75 +411,62 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
         __syncthreads();
         if (t0 + kJF32Tok < cr.c1) load_tile(t0 + kJF32Tok);   // in flight during the MFMAs
 
-        // lane (g, j): tokens 16 th + 8 g + e of feature (a, at) / channel (v, vt) j
-        u32x4 ta[3], tv[3], tat[3], tvt[3];
+        // lane (g, j): tokens tb + 8 g + e of feature (a, at) / channel (v, vt)
+        // j: wave (hh, th) takes token half th of group hh; for HD = 64 all
+        // 32 tokens of K group hh against V group th
+        const int vg = D64 ? th : hh;
 #pragma unroll
-        for (int sp = 0; sp < 3; ++sp) {
-            ta[sp] = gather_tokens_t16(lds[0][sp][hh], kD, 16 * th, 0, lane);
-            tv[sp] = gather_tokens_t16(lds[1][sp][hh], kD, 16 * th, 0, lane);
-            tat[sp] = gather_tokens_t16(lds[2][sp][hh], kD, 16 * th, 0, lane);
-            tvt[sp] = gather_tokens_t16(lds[3][sp][hh], kD, 16 * th, 0, lane);
-        }
-        // smallest products first
-        accV = mma_terms(ta, tv, accV);
-        accVt = mfma_bf16(tat[2], tv[0], accVt);
-        accVt = mfma_bf16(tat[1], tv[1], accVt);
-        accVt = mfma_bf16(tat[0], tv[2], accVt);
-        accVt = mfma_bf16(ta[2], tvt[0], accVt);
-        accVt = mfma_bf16(ta[1], tvt[1], accVt);
-        accVt = mfma_bf16(ta[0], tvt[2], accVt);
-        accVt = mfma_bf16(tat[1], tv[0], accVt);
-        accVt = mfma_bf16(tat[0], tv[1], accVt);
-        accVt = mfma_bf16(ta[1], tvt[0], accVt);
-        accVt = mfma_bf16(ta[0], tvt[1], accVt);
-        accVt = mfma_bf16(tat[0], tv[0], accVt);
-        accVt = mfma_bf16(ta[0], tvt[0], accVt);
+        for (int st = 0; st < (D64 ? 2 : 1); ++st) {
+            const int tb = D64 ? 16 * st : 16 * th;
+            u32x4 ta[3], tv[3], tat[3], tvt[3];
 #pragma unroll
-        for (int sp = 2; sp >= 0; --sp) {
-            accO = mfma_bf16(ta[sp], ones, accO);
-            accOt = mfma_bf16(tat[sp], ones, accOt);
-        }
-    }
-
-    // the two token halves of each head in a fixed order, as the 16-bit kernel
-    __syncthreads();
-    float* red = reinterpret_cast<float*>(&lds[0][0][0][0]);   // [head][4][16][64]
-    const f32x16* accs[4] = {&accV, &accO, &accVt, &accOt};
-    if (th == 1) {
+            for (int sp = 0; sp < 3; ++sp) {
+                ta[sp] = gather_tokens_t16(lds[0][sp][hh], kD, tb, 0, lane);
+                tv[sp] = gather_tokens_t16(lds[1][sp][vg], kD, tb, 0, lane);
+                tat[sp] = gather_tokens_t16(lds[2][sp][hh], kD, tb, 0, lane);
+                tvt[sp] = gather_tokens_t16(lds[3][sp][vg], kD, tb, 0, lane);
+            }
+            // smallest products first
+            acc[0] = mma_terms(ta, tv, acc[0]);
+            acc[2] = mfma_bf16(tat[2], tv[0], acc[2]);
+            acc[2] = mfma_bf16(tat[1], tv[1], acc[2]);
+            acc[2] = mfma_bf16(tat[0], tv[2], acc[2]);
+            acc[2] = mfma_bf16(ta[2], tvt[0], acc[2]);
+            acc[2] = mfma_bf16(ta[1], tvt[1], acc[2]);
+            acc[2] = mfma_bf16(ta[0], tvt[2], acc[2]);
+            acc[2] = mfma_bf16(tat[1], tv[0], acc[2]);
+            acc[2] = mfma_bf16(tat[0], tv[1], acc[2]);
+            acc[2] = mfma_bf16(ta[1], tvt[0], acc[2]);
+            acc[2] = mfma_bf16(ta[0], tvt[1], acc[2]);
+            acc[2] = mfma_bf16(tat[0], tv[0], acc[2]);
+            acc[2] = mfma_bf16(ta[0], tvt[0], acc[2]);
+            if (!D64 || th == 0) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-            for (int rg = 0; rg < 16; ++rg) red[((hh * 4 + q4) * 16 + rg) * 64 + lane] = (*accs[q4])[rg];
-    }
-    __syncthreads();
-    if (th == 0 && hh < nh) {
-        const size_t bh = (size_t)b * H + h0 + hh;
-        float* dS = part + ((bh * 2 + 0) * P + p) * kStateFloats;
-        float* dT = part + ((bh * 2 + 1) * P + p) * kStateFloats;
-#pragma unroll
-        for (int rg = 0; rg < 16; ++rg) {
-            const int row = 8 * (rg >> 2) + 4 * g + (rg & 3);
-            dS[row * kW + j] = accV[rg] + red[((hh * 4 + 0) * 16 + rg) * 64 + lane];
-            dT[row * kW + j] = accVt[rg] + red[((hh * 4 + 2) * 16 + rg) * 64 + lane];
-            if (j == 0) {
-                dS[row * kW + kD] = accO[rg] + red[((hh * 4 + 1) * 16 + rg) * 64 + lane];
-                dT[row * kW + kD] = accOt[rg] + red[((hh * 4 + 3) * 16 + rg) * 64 + lane];
+                for (int sp = 2; sp >= 0; --sp) {
+                    acc[1] = mfma_bf16(ta[sp], ones, acc[1]);
+                    acc[3] = mfma_bf16(tat[sp], ones, acc[3]);
+                }
             }
         }
     }
+    jvp_write_partials<HD>(part, reinterpret_cast<float*>(&lds[0][0][0][0]), acc, b, HR, h0, nh, P, p, hh, th,
+                           lane);
 }
 
-// Output and tangent for fp32 q and qt: the 16-bit kernel's waves and
+// Output and tangent for fp32 q and qt: the 16-bit kernel's waves, groups and
 // sub-tiles, q and qt read per wave in the operand layout (the next
 // sub-tile's loads in flight during this one's work), f = ReLU(q) and
 // ft = [q > 0] qt split into three bf16 terms each:
 //   num = S_v^T f (6 term products per K-step), numt = St_v^T f + S_v^T ft (12);
 // the normalisers are fp32 dot products of the unsplit values.
-template <typename OutT>
+template <typename OutT, int HD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_jvp_apply_mfma_f32(
     const float* __restrict__ q, const float* __restrict__ qt, const float* __restrict__ state,
-    OutT* __restrict__ out, OutT* __restrict__ outt, int N, int H, int HP, int L, int NB, int tile, int tpb,
+    OutT* __restrict__ out, OutT* __restrict__ outt, int N, int H, int HP, int HR, int L, int NB, int tile, int tpb,
     float eps) {
+    constexpr int KS = KSteps<HD>::value, SF = HD * (HD + 1);
+    constexpr bool D64 = HD == 2 * kD, D16 = HD == kD / 2;
+    constexpr int G = KS / 2;   // 32-feature groups of q a wave reads
     __shared__ __attribute__((aligned(16))) float otile[4][32 * kPitch];
 
     const int per_unit = NB * tpb;
@@ -398,48 +482,69 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     if (t0 >= t1 || t0 + 32 * (wave >> 1) >= t1) return;
     const int g = lane >> 5, i = lane & 31;
 
-    const size_t bh = (size_t)b * H + h;
-    const float* S = state + ((bh * 2 + 0) * NB + beta) * kStateFloats;
-    const float* St = state + ((bh * 2 + 1) * NB + beta) * kStateFloats;
-    u32x4 sa[2][3], sat[2][3];
-    state_operands(S, lane, true, sa);
-    state_operands(St, lane, true, sat);
-    float sz[16], szt[16];   // S[:, D] and St[:, D] at this lane's features 16 ks + 8 g + e
+    const size_t bhr = (size_t)b * HR;
+    auto head_S = [&](int hr) { return state + (((bhr + hr) * 2 + 0) * NB + beta) * SF; };
+    auto head_St = [&](int hr) { return state + (((bhr + hr) * 2 + 1) * NB + beta) * SF; };
+    u32x4 sa[KS][3], sat[KS][3];
+    // S[:, D] and St[:, D] at this lane's features 16 ks + 8 g + e, kept in
+    // the wave's LDS (the same for all lanes of a half): registers go to the
+    // operands
+    __shared__ __attribute__((aligned(16))) float zlds[4][2][2][8 * KS];   // [wave][S | St][g]
+    {
+        float sz[8 * KS], szt[8 * KS];
+        apply_operands<HD>(head_S, D64 ? hp : h, wave & 1, HR, lane, sa, sz);
+        apply_operands<HD>(head_St, D64 ? hp : h, wave & 1, HR, lane, sat, szt);
+        if (i == 0) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            sz[8 * ks + e] = S[(16 * ks + 8 * g + e) * kW + kD];
-            szt[8 * ks + e] = St[(16 * ks + 8 * g + e) * kW + kD];
+            for (int e = 0; e < 8 * KS; ++e) {
+                zlds[wave][0][g][e] = sz[e];
+                zlds[wave][1][g][e] = szt[e];
+            }
         }
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+    }
+    const float* sz = zlds[wave][0][g];
+    const float* szt = zlds[wave][1][g];
 
-    const long long hstride = (long long)H * kD;
-    auto row_of = [&](const float* x, int tt) { return x + ((long long)b * N + min(tt + i, t1 - 1)) * hstride + h * kD; };
+    const long long hstride = (long long)HR * HD;
+    const int qcol = (D64 ? 2 * hp : h) * kD;     // first q feature of the wave's groups in the row
+    const bool second = !D16 || 2 * h + 1 < HR;   // head dim 16: the group has a second head
+    const int ncols = second ? 32 : 16;
+    auto row_of = [&](const float* x, int tt) { return x + ((long long)b * N + min(tt + i, t1 - 1)) * hstride + qcol; };
+    auto load = [&](F32Operand (&o)[G], const float* x, int tt) {
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) o[gi].load(row_of(x, tt) + kD * gi, g, second);
+    };
     float* ot = otile[wave];
-    F32Operand qc, tc;
-    qc.load(row_of(q, t0 + 32 * (wave >> 1)), g);
-    tc.load(row_of(qt, t0 + 32 * (wave >> 1)), g);
+    F32Operand qc[G], tc[G];
+    load(qc, q, t0 + 32 * (wave >> 1));
+    load(tc, qt, t0 + 32 * (wave >> 1));
     for (int tt = t0 + 32 * (wave >> 1); tt < t1; tt += 64) {
         const int n = min(32, t1 - tt);   // clamped rows repeat the last row (see store_tile)
-        F32Operand qn, tn;
+        // the next sub-tile's rows in flight during this one's work (head dim
+        // 64 reads them after it: two groups of q and qt would not fit)
+        F32Operand qn[G], tn[G];
         const bool more = tt + 64 < t1;
-        if (more) {
-            qn.load(row_of(q, tt + 64), g);
-            tn.load(row_of(qt, tt + 64), g);
+        if (more && G == 1) {
+            load(qn, q, tt + 64);
+            load(tn, qt, tt + 64);
         }
         f32x16 acc = {}, acct = {};
-        float dp = 0.f, dpt = 0.f;
+        float dp = 0.f, dpt = 0.f, dp1 = 0.f, dpt1 = 0.f;   // dp1, dpt1: head dim 16, the second head
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
+            float& a = (D16 && ks == 1) ? dp1 : dp;
+            float& at = (D16 && ks == 1) ? dpt1 : dpt;
             float f[8], ft[8];
-            qc.half(ks, true, f);
-            tc.half(ks, false, ft);
+            qc[ks >> 1].half(ks & 1, true, f);
+            tc[ks >> 1].half(ks & 1, false, ft);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 ft[e] = f[e] > 0.f ? ft[e] : 0.f;
-                dp = fmaf(f[e], sz[8 * ks + e], dp);
-                dpt = fmaf(f[e], szt[8 * ks + e], dpt);
-                dpt = fmaf(ft[e], sz[8 * ks + e], dpt);
+                a = fmaf(f[e], sz[8 * ks + e], a);
+                at = fmaf(f[e], szt[8 * ks + e], at);
+                at = fmaf(ft[e], sz[8 * ks + e], at);
             }
             u32x4 tf[3], tft[3];
             split3_trunc_f32x8(f, tf);
@@ -448,21 +553,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
             acct = mma_terms(sat[ks], tf, acct);
             acct = mma_terms(sa[ks], tft, acct);
         }
-        const float den = dp + __shfl_xor(dp, 32);
-        const float dent = dpt + __shfl_xor(dpt, 32);
-        const float rinv = 1.0f / (den + eps);
-#pragma unroll
-        for (int rg = 0; rg < 16; ++rg) {
-            const float o = acc[rg] * rinv;
-            acc[rg] = o;
-            acct[rg] = (acct[rg] - o * dent) * rinv;
-        }
-        store_tile<OutT>(ot, acc, lane, n, [&](int t) { return out + ((long long)b * N + tt + t) * hstride + h * kD; });
+        finish_tangent<D16>(acc, acct, dp, dpt, dp1, dpt1, eps);
+        store_tile<OutT>(ot, acc, lane, n, [&](int t) { return out + ((long long)b * N + tt + t) * hstride + h * kD; },
+                         ncols);
         store_tile<OutT>(ot, acct, lane, n,
-                         [&](int t) { return outt + ((long long)b * N + tt + t) * hstride + h * kD; });
-        if (more) {
-            qc = qn;
-            tc = tn;
+                         [&](int t) { return outt + ((long long)b * N + tt + t) * hstride + h * kD; }, ncols);
+        if (more && G == 1) {
+            qc[0] = qn[0];
+            tc[0] = tn[0];
+        } else if (more) {
+            load(qc, q, tt + 64);
+            load(tc, qt, tt + 64);
         }
     }
 }
@@ -593,21 +694,22 @@ template <typename F> void by_dtype(int code, F&& f) {
 
 hipError_t launch_jvp_state(const Plan& pl, const void* k, const void* v, const void* kt, const void* vt, float* part,
                             hipStream_t stream) {
-    if (pl.mfma && pl.in_dtype == 0) {
-        const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.P);
-        hipLaunchKernelGGL(k_jvp_state_mfma_f32, dim3(grid), dim3(kThreads), 0, stream, static_cast<const float*>(k),
-                           static_cast<const float*>(v), static_cast<const float*>(kt), static_cast<const float*>(vt),
-                           part, pl.N, pl.H, pl.HP, pl.L, pl.cpb, pl.P, pl.chunk);
-    } else if (pl.mfma16) {
+    if (pl.mfma) {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.P);
         const uint16_t *k16 = static_cast<const uint16_t*>(k), *v16 = static_cast<const uint16_t*>(v),
                        *kt16 = static_cast<const uint16_t*>(kt), *vt16 = static_cast<const uint16_t*>(vt);
-        if (pl.in_dtype == 2)
-            hipLaunchKernelGGL(k_jvp_state_mfma<true>, dim3(grid), dim3(kThreads), 0, stream, k16, v16, kt16, vt16,
-                               part, pl.N, pl.H, pl.HP, pl.L, pl.cpb, pl.P, pl.chunk);
-        else
-            hipLaunchKernelGGL(k_jvp_state_mfma<false>, dim3(grid), dim3(kThreads), 0, stream, k16, v16, kt16, vt16,
-                               part, pl.N, pl.H, pl.HP, pl.L, pl.cpb, pl.P, pl.chunk);
+        by_head_dim(pl.D, [&](auto dd) {
+            constexpr int DD = decltype(dd)::value;
+            if (pl.in_dtype == 0)
+                hipLaunchKernelGGL(k_jvp_state_mfma_f32<DD>, dim3(grid), dim3(kThreads), 0, stream,
+                                   static_cast<const float*>(k), static_cast<const float*>(v),
+                                   static_cast<const float*>(kt), static_cast<const float*>(vt), part, pl.N,
+                                   groups32(pl), pl.HP, pl.H, pl.L, pl.cpb, pl.P, pl.chunk);
+            else
+                hipLaunchKernelGGL((pl.in_dtype == 2 ? k_jvp_state_mfma<true, DD> : k_jvp_state_mfma<false, DD>),
+                                   dim3(grid), dim3(kThreads), 0, stream, k16, v16, kt16, vt16, part, pl.N,
+                                   groups32(pl), pl.HP, pl.H, pl.L, pl.cpb, pl.P, pl.chunk);
+        });
     } else {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.H * pl.P);
         by_dtype(pl.in_dtype, [&](auto it) {
@@ -622,28 +724,24 @@ hipError_t launch_jvp_state(const Plan& pl, const void* k, const void* v, const 
 
 hipError_t launch_jvp_apply(const Plan& pl, const void* q, const void* qt, const float* state, void* out, void* outt,
                             float eps, hipStream_t stream) {
-    if (pl.mfma && pl.in_dtype == 0) {
-        const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.NB * pl.tpb);
-        by_dtype(pl.out_dtype, [&](auto o) {
-            using OT = typename decltype(o)::type;
-            hipLaunchKernelGGL((k_jvp_apply_mfma_f32<OT>), dim3(grid), dim3(kThreads), 0, stream,
-                               static_cast<const float*>(q), static_cast<const float*>(qt), state,
-                               static_cast<OT*>(out), static_cast<OT*>(outt), pl.N, pl.H, pl.HP, pl.L, pl.NB, pl.tile,
-                               pl.tpb, eps);
-        });
-    } else if (pl.mfma16) {
+    if (pl.mfma) {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.NB * pl.tpb);
         const uint16_t *q16 = static_cast<const uint16_t*>(q), *qt16 = static_cast<const uint16_t*>(qt);
         by_dtype(pl.out_dtype, [&](auto o) {
-            using OT = typename decltype(o)::type;
-            if (pl.in_dtype == 2)
-                hipLaunchKernelGGL((k_jvp_apply_mfma<true, OT>), dim3(grid), dim3(kThreads), 0, stream, q16, qt16, state,
-                                   static_cast<OT*>(out), static_cast<OT*>(outt), pl.N, pl.H, pl.HP, pl.L, pl.NB,
-                                   pl.tile, pl.tpb, eps);
-            else
-                hipLaunchKernelGGL((k_jvp_apply_mfma<false, OT>), dim3(grid), dim3(kThreads), 0, stream, q16, qt16,
-                                   state, static_cast<OT*>(out), static_cast<OT*>(outt), pl.N, pl.H, pl.HP, pl.L,
-                                   pl.NB, pl.tile, pl.tpb, eps);
+            by_head_dim(pl.D, [&](auto dd) {
+                using OT = typename decltype(o)::type;
+                constexpr int DD = decltype(dd)::value;
+                if (pl.in_dtype == 0)
+                    hipLaunchKernelGGL((k_jvp_apply_mfma_f32<OT, DD>), dim3(grid), dim3(kThreads), 0, stream,
+                                       static_cast<const float*>(q), static_cast<const float*>(qt), state,
+                                       static_cast<OT*>(out), static_cast<OT*>(outt), pl.N, groups32(pl), pl.HP,
+                                       pl.H, pl.L, pl.NB, pl.tile, pl.tpb, eps);
+                else
+                    hipLaunchKernelGGL((pl.in_dtype == 2 ? k_jvp_apply_mfma<true, OT, DD> : k_jvp_apply_mfma<false, OT, DD>),
+                                       dim3(grid), dim3(kThreads), 0, stream, q16, qt16, state, static_cast<OT*>(out),
+                                       static_cast<OT*>(outt), pl.N, groups32(pl), pl.HP, pl.H, pl.L, pl.NB, pl.tile,
+                                       pl.tpb, eps);
+            });
         });
     } else {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.H * pl.NB * pl.tpb);

@@ -547,45 +547,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 
 
     const int g = lane >> 5, i = lane & 31;
     // A operand: lane (g, c = i), element e of (ks, split) = split term of
-    // S[16 ks + 8 g + e][c]; sden: this lane's 16 normaliser entries.
-    const float* S = D64 ? state + (((size_t)b * HP + hp) * NB + beta) * (2 * kD * SW) + kD * hh
-                         : state + (((size_t)b * H + hs) * NB + beta) * kStateFloats;
-    const float* Sz = D64 ? S - kD * hh + 2 * kD : S + kD;   // the normaliser column
+    // S[16 ks + 8 g + e][c]; sden: this lane's 8 KS normaliser entries.
+    const int SF = HD * SW;
+    auto head_state = [&](int hr) { return state + (((size_t)b * HR + hr) * NB + beta) * SF; };
     u32x4 sa[KS][3];
     float sden[8 * KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        // head dim 16: K-step ks is head 2 hs + ks (zero if there is none),
-        // present in the columns of the same half only
-        const int hr = 2 * hs + ks;
-        const bool on = !D16 || (hr < HR && (i >> 4) == ks);
-        const bool zon = !D16 || hr < HR;
-        const float* S16 = state + (((size_t)b * HR + min(hr, HR - 1)) * NB + beta) * (16 * 17);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            uint32_t w[3] = {0u, 0u, 0u};
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int row = 16 * ks + 8 * g + 2 * d + half;
-                float r;
-                if constexpr (D16) {
-                    r = on ? S16[(row - 16 * ks) * 17 + (i & 15)] : 0.f;
-                    sden[8 * ks + 2 * d + half] = zon ? S16[(row - 16 * ks) * 17 + 16] : 0.f;
-                } else {
-                    r = S[row * SW + i];
-                    sden[8 * ks + 2 * d + half] = Sz[row * SW];
-                }
-#pragma unroll
-                for (int sp = 0; sp < 3; ++sp) {   // S = hi + mid + lo, each remainder exact
-                    const uint16_t t = f32_to_bf16(r);
-                    r -= bf16_to_f32(t);
-                    w[sp] |= (uint32_t)t << (16 * half);
-                }
-            }
-#pragma unroll
-            for (int sp = 0; sp < 3; ++sp) sa[ks][sp][d] = w[sp];
-        }
-    }
+    apply_operands<HD>(head_state, D64 ? hp : hs, hh, HR, lane, sa, sden);
 
     // fp32 out: rows past the range read as zero and are not stored.  16-bit
     // out: they are clamped to the range's last row, so every load is
@@ -825,17 +792,6 @@ template <typename F> void by_dtype(int code, F&& f) {
 }
 
 // Calls f(std::integral_constant<int, D>) for the supported head dims.
-// 32-feature groups of a token row (the "heads" of the matrix-core kernels)
-int groups32(const Plan& pl) { return (pl.H * pl.D + kD - 1) / kD; }
-
-template <typename F> void by_head_dim(int D, F&& f) {
-    if (D == 16)
-        f(std::integral_constant<int, 16>{});
-    else if (D == 64)
-        f(std::integral_constant<int, 64>{});
-    else
-        f(std::integral_constant<int, 32>{});
-}
 }  // namespace
 
 hipError_t launch_state(const Plan& pl, const void* k, const void* v, float* part, hipStream_t stream) {

@@ -48,8 +48,11 @@ def test_other_head_dims():
     for d in (8, 48, 128):
         assert sana.lib.sana_linattn_workspace_bytes(1, 8, 4096, d, 0, ctypes.byref(ctypes.c_size_t())) == \
             sana.SANA_ERR_UNSUPPORTED
-    for f in (sana.lib.sana_linattn_bwd_workspace_bytes, sana.lib.sana_linattn_jvp_workspace_bytes):
-        assert f(1, 8, 4096, 64, 0, ctypes.byref(ctypes.c_size_t())) == sana.SANA_ERR_UNSUPPORTED
+    assert sana.lib.sana_linattn_bwd_workspace_bytes(1, 8, 4096, 64, 0, ctypes.byref(ctypes.c_size_t())) == \
+        sana.SANA_ERR_UNSUPPORTED
+    for d in (16, 64):   # the forward-mode derivative takes every head dim: one state and one tangent state
+        jw = sana.sana_linattn_jvp_workspace_bytes(1, 8, 4096, d, 0)
+        assert jw >= 2 * 8 * d * (d + 1) * 4
 
 
 def test_workspace_and_plan_queries():
@@ -264,7 +267,7 @@ def jvp(q=A, k=A + 64 * MB, v=A + 128 * MB, qt=A + 192 * MB, kt=A + 256 * MB, vt
     (dict(kt=None), sana.SANA_ERR_INVALID_ARG),
     (dict(outt=None), sana.SANA_ERR_INVALID_ARG),
     (dict(in_dt=3), sana.SANA_ERR_INVALID_ARG),
-    (dict(D=16), sana.SANA_ERR_UNSUPPORTED),
+    (dict(D=48), sana.SANA_ERR_UNSUPPORTED),
     (dict(eps=-1.0), sana.SANA_ERR_INVALID_ARG),
     (dict(vt=A + 320 * MB + 4), sana.SANA_ERR_ALIGNMENT),
     (dict(outt=A + 384 * MB), sana.SANA_ERR_ALIAS),     # out_t == out

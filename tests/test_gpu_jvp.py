@@ -96,6 +96,23 @@ def test_jvp_edge_shapes(monkeypatch, path, B, N, H, L, dt):
         check_tangent(got_t, want_t, out_t, f"{w.name}/{path}")
 
 
+HEAD_DIMS = [(2, 1000, 5, 100, 1, 64), (1, 777, 7, 0, 2, 16), (2, 33, 1, 0, 0, 16), (1, 4097, 3, 1, 0, 64),
+             (1, 16384, 35, 0, 1, 64), (1, 16384, 140, 0, 1, 16), (1, 16384, 35, 0, 0, 64)]
+
+
+@pytest.mark.parametrize("B,N,H,L,dt,D", HEAD_DIMS, ids=[f"B{b}N{n}H{h}L{l}dt{t}D{d}" for b, n, h, l, t, d in HEAD_DIMS])
+def test_jvp_other_head_dims(B, N, H, L, dt, D):
+    """Head dims 16 and 64 (32-feature groups on the matrix cores): ragged N,
+    odd and single heads (a group that is a lone head of 16), block lengths 1
+    and 100, the headline's token-head-feature count, fp32/bf16/fp16 inputs."""
+    w = workloads.Workload(f"jvp_B{B}N{N}H{H}L{L}dt{dt}D{D}", B, N, H, D, dt, seed=140 + N % 17 + D, block_len=L)
+    x, (want, want_t) = case(w)
+    for out_t in ((torch.float32, torch.bfloat16) if N < 16384 else (torch.float32,)):
+        got, got_t = run(x, w, out_t)
+        compare(got, want, x[2], out_t == torch.bfloat16, w.name)
+        check_tangent(got_t, want_t, out_t, w.name)
+
+
 def test_jvp_primal_is_the_forward_and_repeatable():
     """The primal output equals sana_linattn_fwd's bit for bit, and two calls agree bit for bit."""
     import diffusion_transformer_relu_amd as sana

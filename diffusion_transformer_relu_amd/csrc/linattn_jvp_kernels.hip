@@ -10,7 +10,9 @@
 //   num = S_v^T f,  den = S_z . f,  numt = St_v^T f + S_v^T ft,
 //   dent = St_z . f + S_z . ft
 //   out = num r,  outt = (numt - out dent) r,  r = 1 / (den + eps)
-// Everything accumulates in fp32; products of 16-bit inputs are exact.
+// Everything accumulates in fp32; products of 16-bit inputs are exact.  Head
+// dims 16 and 64 run the matrix-core kernels on 32-feature groups of the token
+// row, as the forward's kernels do.
 #include "linattn_device.h"
 
 namespace sana {
@@ -341,6 +343,8 @@ __global__ __launch_bounds__(kThreads) void k_jvp_apply_mfma(
 // transposing LDS reads and accumulates, over the term pairs i + j <= 2
 // (0-based; the dropped products are below 2^-24 of the exact one):
 //   S_v += a v,   St_v += at v + a vt,   S_z += a 1,   St_z += at 1 (exact)
+// Head dims 16 and 64 as in the 16-bit kernel ("heads" are 32-feature groups;
+// HD = 64: wave w takes all 32 tokens of K group w & 1 against V group w >> 1).
 constexpr int kJF32Tok = 32;
 constexpr int kJF32Tile = kJF32Tok * kD;   // 16-bit elements of one term tile of one head
 

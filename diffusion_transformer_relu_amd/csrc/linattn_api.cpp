@@ -216,15 +216,17 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
     std::memset(bp, 0, sizeof *bp);
     const int st = make_plan(in_dtype, SANA_DT_F32, B, H, N, D, block_len, &bp->fw, allow_mfma);
     if (st != SANA_OK) return st;
-    if (D != sana::kD) return SANA_ERR_UNSUPPORTED;   // the backward is built for D = 32
     for (int c : {dout_dtype, grad_dtype})
         if (c != SANA_DT_F32 && c != SANA_DT_BF16 && c != SANA_DT_F16) return SANA_ERR_INVALID_ARG;
     bp->dout_dtype = dout_dtype;
     bp->grad_dtype = grad_dtype;
     if (B == 0 || H == 0 || N == 0) return SANA_OK;
     const Plan& pl = bp->fw;
-    bp->key_mfma = bp->query_mfma = pl.mfma;
-    if (pl.mfma) {
+    // the matrix-core query and key kernels are built for D = 32; other head
+    // dims take the vector kernels (the forward's state is rebuilt on the
+    // matrix cores either way)
+    bp->key_mfma = bp->query_mfma = pl.mfma && D == sana::kD;
+    if (bp->query_mfma) {
         // Tiles (multiples of 64 tokens inside one block) for the (batch, head
         // pair, block) units: the key and query kernels' registers and LDS
         // fit 3 work-groups per CU (2 for fp32 inputs).  The tile count per block
@@ -252,7 +254,8 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
         bp->tk = tile_for(per_cu);
         bp->tq = tile_for(per_cu);
     } else {
-        bp->tk = bp->tq = kBwdTile;
+        bp->tk = kBwdTile;
+        bp->tq = D == 2 * sana::kD ? kBwdTile / 4 : kBwdTile;   // the vector query kernel's tokens per work-group
     }
     bp->tpbq = ceil_div(pl.L, bp->tq);
     bp->tpbk = ceil_div(pl.L, bp->tk);
@@ -261,9 +264,9 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
     const size_t bh = (size_t)B * H;
     size_t off = pl.bytes;
     bp->off_gpart = off;
-    off += round_up((long)(bh * bp->Pq * sana::kStateFloats * sizeof(float)), 256);
+    off += round_up((long)(bh * bp->Pq * (size_t)D * (D + 1) * sizeof(float)), 256);
     bp->off_ghat = off;
-    off += round_up((long)(bh * pl.NB * sana::kStateFloats * sizeof(float)), 256);
+    off += round_up((long)(bh * pl.NB * (size_t)D * (D + 1) * sizeof(float)), 256);
     bp->bytes = off;
     return SANA_OK;
 }

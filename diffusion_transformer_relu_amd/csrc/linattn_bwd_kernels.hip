@@ -28,176 +28,184 @@ __device__ __forceinline__ void st(float* p, long long i, float x) { store_out(p
 __device__ __forceinline__ void st(uint16_t* p, long long i, float x) { store_out(p, i, x); }
 __device__ __forceinline__ void st(_Float16* p, long long i, float x) { store_out(p, i, x); }
 
-constexpr int kTok = 256;   // tokens per work-group of the vector kernels (one per thread)
+// Tokens per work-group of the vector query kernel (one per thread; 64 for
+// head dim 64, whose per-token LDS rows are twice as long) and of the vector
+// key kernel.
+template <int DD> struct VTok { static constexpr int value = DD == 2 * kD ? 64 : 256; };
+constexpr int kTok = 256;
 
 // ------------------------------------------------------------------ query pass, vector unit
 // grid.x = ((b * H + h) * NB + beta) * tpb + tile; thread t = token
-// blk0 + tile * 256 + t of block beta.  Writes dq and the tile's partial
+// blk0 + tile * TOK + t of block beta.  Writes dq and the tile's partial
 // gradient state gpart[(b * H + h) * (NB * tpb) + beta * tpb + tile].
-template <typename InT, typename GT, typename OutT>
+// Head dim DD (16, 32 or 64): states are DD x (DD + 1).
+template <typename InT, typename GT, typename OutT, int DD>
 __global__ __launch_bounds__(kThreads) void k_bwd_query_valu(
     const InT* __restrict__ q, const GT* __restrict__ dout, const float* __restrict__ state,
     OutT* __restrict__ dq, float* __restrict__ gpart, int N, int H, int L, int NB, int tpb, float eps) {
-    __shared__ float sP[kStateFloats];
-    __shared__ float sf[kTok][kD + 1];    // f of each token (padded row)
-    __shared__ float suw[kTok][kW];       // [u | w] of each token
+    constexpr int WW = DD + 1, SF = DD * WW, TOK = VTok<DD>::value;
+    __shared__ float sP[SF];
+    __shared__ float sf[TOK][DD + 1];    // f of each token (padded row)
+    __shared__ float suw[TOK][WW];       // [u | w] of each token
 
     const int tile = blockIdx.x % tpb;
     const size_t bhb = blockIdx.x / tpb;          // (b * H + h) * NB + beta
     const int beta = (int)(bhb % NB);
     const size_t bh = bhb / NB;
     const int h = (int)(bh % H), b = (int)(bh / H);
-    for (int e = threadIdx.x; e < kStateFloats; e += kThreads) sP[e] = state[bhb * kStateFloats + e];
+    for (int e = threadIdx.x; e < SF; e += kThreads) sP[e] = state[bhb * SF + e];
     __syncthreads();
 
     const int blk0 = beta * L, blk1 = min(blk0 + L, N);
     const int t = threadIdx.x;
-    const int row = blk0 + tile * kTok + t;
-    if (row < blk1) {
-        const long long base = (((long long)b * N + row) * H + h) * kD;
-        float f[kD], u[kD];
+    const int row = blk0 + tile * TOK + t;
+    if (t < TOK && row < blk1) {
+        const long long base = (((long long)b * N + row) * H + h) * DD;
+        float f[DD], u[DD];
 #pragma unroll
-        for (int j = 0; j < kD; ++j) {
+        for (int j = 0; j < DD; ++j) {
             const float x = ld(q, base + j);
             f[j] = x > 0.f ? x : 0.f;
             sf[t][j] = f[j];
         }
         float den = 0.f;
 #pragma unroll
-        for (int j = 0; j < kD; ++j) den += f[j] * sP[j * kW + kD];
+        for (int j = 0; j < DD; ++j) den += f[j] * sP[j * WW + DD];
         const float r = 1.0f / (den + eps);
         float go = 0.f;   // dout . num
-        for (int c = 0; c < kD; ++c) {
+        for (int c = 0; c < DD; ++c) {
             float num = 0.f;
 #pragma unroll
-            for (int j = 0; j < kD; ++j) num += f[j] * sP[j * kW + c];
+            for (int j = 0; j < DD; ++j) num += f[j] * sP[j * WW + c];
             const float g = ld(dout, base + c);
             go += g * num;
             u[c] = g * r;
             suw[t][c] = u[c];
         }
         const float w = -(r * r) * go;
-        suw[t][kD] = w;
-        for (int j = 0; j < kD; ++j) {
-            float s = sP[j * kW + kD] * w;
+        suw[t][DD] = w;
+        for (int j = 0; j < DD; ++j) {
+            float s = sP[j * WW + DD] * w;
 #pragma unroll
-            for (int c = 0; c < kD; ++c) s += sP[j * kW + c] * u[c];
+            for (int c = 0; c < DD; ++c) s += sP[j * WW + c] * u[c];
             st(dq, base + j, ld(q, base + j) > 0.f ? s : 0.f);
         }
-    } else {
-        for (int j = 0; j < kD; ++j) sf[t][j] = 0.f;
-        for (int c = 0; c < kW; ++c) suw[t][c] = 0.f;
+    } else if (t < TOK) {
+        for (int j = 0; j < DD; ++j) sf[t][j] = 0.f;
+        for (int c = 0; c < WW; ++c) suw[t][c] = 0.f;
     }
     __syncthreads();
     // partial gradient state of this tile: thread t owns entries t, t + 256, ...
-    float* dst = gpart + (bhb * tpb + tile) * kStateFloats;   // (bh * NB + beta) * tpb + tile
-    for (int e = t; e < kStateFloats; e += kThreads) {
-        const int j = e / kW, c = e - j * kW;
+    float* dst = gpart + (bhb * tpb + tile) * SF;   // (bh * NB + beta) * tpb + tile
+    for (int e = t; e < SF; e += kThreads) {
+        const int j = e / WW, c = e - j * WW;
         float s = 0.f;
-        for (int tok = 0; tok < kTok; ++tok) s += sf[tok][j] * suw[tok][c];
+        for (int tok = 0; tok < TOK; ++tok) s += sf[tok][j] * suw[tok][c];
         dst[e] = s;
     }
 }
 
 // ------------------------------------------------------------------ suffix merge
-// grid.x = (b * H + h) * kGroups + m; thread t owns entry e = m * 256 + t.
+// grid.x = (b * H + h) * groups + m, groups = ceil(SF / 256); thread t owns
+// entry e = m * 256 + t of the SF-float states.
 // For beta = NB-1 down to 0: the block's tile partials are summed (in groups
 // of 8 added as a fixed pairwise tree, the groups in order) and added to the
 // running suffix sum, which is written as Ghat of block beta.  The loads of up
 // to 16 partials are issued together (the kernel is a few load round trips
 // long).
-constexpr int kGroups = (kStateFloats + kThreads - 1) / kThreads;
 
 __device__ __forceinline__ float tree8(const float* x) {
     return ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
 }
 
 __global__ __launch_bounds__(kThreads) void k_bwd_merge_suffix(const float* __restrict__ gpart,
-                                                                float* __restrict__ ghat, int NB, int tpb) {
-    const size_t bh = blockIdx.x / kGroups;
-    const int e = (blockIdx.x % kGroups) * kThreads + threadIdx.x;
-    if (e >= kStateFloats) return;
-    const float* src = gpart + bh * NB * tpb * kStateFloats + e;
-    float* dst = ghat + bh * NB * kStateFloats + e;
+                                                                float* __restrict__ ghat, int NB, int tpb, int SF) {
+    const int groups = (SF + kThreads - 1) / kThreads;
+    const size_t bh = blockIdx.x / groups;
+    const int e = (blockIdx.x % groups) * kThreads + threadIdx.x;
+    if (e >= SF) return;
+    const float* src = gpart + bh * NB * tpb * SF + e;
+    float* dst = ghat + bh * NB * SF + e;
     float acc = 0.f;
     if (tpb == 1) {
         // one partial per block: 16 blocks' loads at once, last block first
         for (int b1 = NB; b1 > 0; b1 -= 16) {
             float x[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = (b1 - 1 - i >= 0) ? src[(size_t)(b1 - 1 - i) * kStateFloats] : 0.f;
+            for (int i = 0; i < 16; ++i) x[i] = (b1 - 1 - i >= 0) ? src[(size_t)(b1 - 1 - i) * SF] : 0.f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 if (b1 - 1 - i >= 0) {
                     acc += 0.f + x[i];   // the block sum of one partial, as the general path forms it
-                    dst[(size_t)(b1 - 1 - i) * kStateFloats] = acc;
+                    dst[(size_t)(b1 - 1 - i) * SF] = acc;
                 }
             }
         }
     } else if (tpb <= 16) {
         for (int beta = NB - 1; beta >= 0; --beta) {
-            const float* blk = src + (size_t)beta * tpb * kStateFloats;
+            const float* blk = src + (size_t)beta * tpb * SF;
             float x[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = (i < tpb) ? blk[(size_t)i * kStateFloats] : 0.f;
+            for (int i = 0; i < 16; ++i) x[i] = (i < tpb) ? blk[(size_t)i * SF] : 0.f;
             float bs = 0.f;
             bs += tree8(x);
             if (tpb > 8) bs += tree8(x + 8);
             acc += bs;
-            dst[(size_t)beta * kStateFloats] = acc;
+            dst[(size_t)beta * SF] = acc;
         }
     } else {
         for (int beta = NB - 1; beta >= 0; --beta) {
-            const float* blk = src + (size_t)beta * tpb * kStateFloats;
+            const float* blk = src + (size_t)beta * tpb * SF;
             float bs = 0.f;
             for (int s0 = 0; s0 < tpb; s0 += 8) {
                 float x[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) x[i] = (s0 + i < tpb) ? blk[(size_t)(s0 + i) * kStateFloats] : 0.f;
+                for (int i = 0; i < 8; ++i) x[i] = (s0 + i < tpb) ? blk[(size_t)(s0 + i) * SF] : 0.f;
                 bs += tree8(x);
             }
             acc += bs;
-            dst[(size_t)beta * kStateFloats] = acc;
+            dst[(size_t)beta * SF] = acc;
         }
     }
 }
 
 // ------------------------------------------------------------------ key pass, vector unit
 // grid.x = ((b * H + h) * NB + beta) * tpb + tile; thread t = key token
-// blk0 + tile * 256 + t of block beta.
-template <typename InT, typename OutT>
+// blk0 + tile * 256 + t of block beta.  Head dim DD (16, 32 or 64).
+template <typename InT, typename OutT, int DD>
 __global__ __launch_bounds__(kThreads) void k_bwd_key_valu(
     const InT* __restrict__ k, const InT* __restrict__ v, const float* __restrict__ ghat,
     OutT* __restrict__ dk, OutT* __restrict__ dv, int N, int H, int L, int NB, int tpb) {
-    __shared__ float sG[kStateFloats];
+    constexpr int WW = DD + 1, SF = DD * WW;
+    __shared__ float sG[SF];
     const int tile = blockIdx.x % tpb;
     const size_t bhb = blockIdx.x / tpb;
     const int beta = (int)(bhb % NB);
     const size_t bh = bhb / NB;
     const int h = (int)(bh % H), b = (int)(bh / H);
-    for (int e = threadIdx.x; e < kStateFloats; e += kThreads) sG[e] = ghat[bhb * kStateFloats + e];
+    for (int e = threadIdx.x; e < SF; e += kThreads) sG[e] = ghat[bhb * SF + e];
     __syncthreads();
     const int blk0 = beta * L, blk1 = min(blk0 + L, N);
     const int row = blk0 + tile * kTok + threadIdx.x;
     if (row >= blk1) return;
-    const long long base = (((long long)b * N + row) * H + h) * kD;
-    float a[kD], x[kD];
+    const long long base = (((long long)b * N + row) * H + h) * DD;
+    float a[DD], x[DD];
 #pragma unroll
-    for (int j = 0; j < kD; ++j) {
+    for (int j = 0; j < DD; ++j) {
         const float kk = ld(k, base + j);
         a[j] = kk > 0.f ? kk : 0.f;
         x[j] = ld(v, base + j);
     }
-    for (int j = 0; j < kD; ++j) {
-        float s = sG[j * kW + kD];
+    for (int j = 0; j < DD; ++j) {
+        float s = sG[j * WW + DD];
 #pragma unroll
-        for (int c = 0; c < kD; ++c) s += sG[j * kW + c] * x[c];
+        for (int c = 0; c < DD; ++c) s += sG[j * WW + c] * x[c];
         st(dk, base + j, a[j] > 0.f ? s : 0.f);
     }
-    for (int c = 0; c < kD; ++c) {
+    for (int c = 0; c < DD; ++c) {
         float s = 0.f;
 #pragma unroll
-        for (int j = 0; j < kD; ++j) s += a[j] * sG[j * kW + c];
+        for (int j = 0; j < DD; ++j) s += a[j] * sG[j * WW + c];
         st(dv, base + c, s);
     }
 }
@@ -823,12 +831,15 @@ hipError_t launch_bwd_query(const BwdPlan& bp, const void* q, const void* dout, 
     by_dtype(pl.in_dtype, [&](auto it) {
         by_dtype(bp.dout_dtype, [&](auto gt) {
             by_dtype(bp.grad_dtype, [&](auto ot) {
-                using IT = typename decltype(it)::type;
-                using GT = typename decltype(gt)::type;
-                using OT = typename decltype(ot)::type;
-                hipLaunchKernelGGL((k_bwd_query_valu<IT, GT, OT>), dim3(grid), dim3(kThreads), 0, stream,
-                                   static_cast<const IT*>(q), static_cast<const GT*>(dout), state,
-                                   static_cast<OT*>(dq), gpart, pl.N, pl.H, pl.L, pl.NB, bp.tpbq, eps);
+                by_head_dim(pl.D, [&](auto dd) {
+                    using IT = typename decltype(it)::type;
+                    using GT = typename decltype(gt)::type;
+                    using OT = typename decltype(ot)::type;
+                    constexpr int DD = decltype(dd)::value;
+                    hipLaunchKernelGGL((k_bwd_query_valu<IT, GT, OT, DD>), dim3(grid), dim3(kThreads), 0, stream,
+                                       static_cast<const IT*>(q), static_cast<const GT*>(dout), state,
+                                       static_cast<OT*>(dq), gpart, pl.N, pl.H, pl.L, pl.NB, bp.tpbq, eps);
+                });
             });
         });
     });
@@ -837,8 +848,9 @@ hipError_t launch_bwd_query(const BwdPlan& bp, const void* q, const void* dout, 
 
 hipError_t launch_bwd_merge(const BwdPlan& bp, const float* gpart, float* ghat, hipStream_t stream) {
     const Plan& pl = bp.fw;
-    const unsigned grid = (unsigned)((size_t)pl.B * pl.H * kGroups);
-    hipLaunchKernelGGL(k_bwd_merge_suffix, dim3(grid), dim3(kThreads), 0, stream, gpart, ghat, pl.NB, bp.tpbq);
+    const int SF = pl.D * (pl.D + 1);
+    const unsigned grid = (unsigned)((size_t)pl.B * pl.H * ((SF + kThreads - 1) / kThreads));
+    hipLaunchKernelGGL(k_bwd_merge_suffix, dim3(grid), dim3(kThreads), 0, stream, gpart, ghat, pl.NB, bp.tpbq, SF);
     return hipGetLastError();
 }
 
@@ -870,11 +882,14 @@ hipError_t launch_bwd_key(const BwdPlan& bp, const void* k, const void* v, const
     const unsigned grid = (unsigned)((size_t)pl.B * pl.H * pl.NB * bp.tpbk);
     by_dtype(pl.in_dtype, [&](auto it) {
         by_dtype(bp.grad_dtype, [&](auto ot) {
-            using IT = typename decltype(it)::type;
-            using OT = typename decltype(ot)::type;
-            hipLaunchKernelGGL((k_bwd_key_valu<IT, OT>), dim3(grid), dim3(kThreads), 0, stream,
-                               static_cast<const IT*>(k), static_cast<const IT*>(v), ghat, static_cast<OT*>(dk),
-                               static_cast<OT*>(dv), pl.N, pl.H, pl.L, pl.NB, bp.tpbk);
+            by_head_dim(pl.D, [&](auto dd) {
+                using IT = typename decltype(it)::type;
+                using OT = typename decltype(ot)::type;
+                constexpr int DD = decltype(dd)::value;
+                hipLaunchKernelGGL((k_bwd_key_valu<IT, OT, DD>), dim3(grid), dim3(kThreads), 0, stream,
+                                   static_cast<const IT*>(k), static_cast<const IT*>(v), ghat, static_cast<OT*>(dk),
+                                   static_cast<OT*>(dv), pl.N, pl.H, pl.L, pl.NB, bp.tpbk);
+            });
         });
     });
     return hipGetLastError();

@@ -38,8 +38,9 @@
  *            cores; fp32 inputs as three-term bf16 splits with the products
  *            below 2^-24 dropped) or, for the forward entry points, 16 or
  *            64 (the same kernels on 32-feature groups of the token row);
- *            the forward-mode derivative takes all three, the backward
- *            D = 32.
+ *            the backward and the forward-mode derivative take all three
+ *            (the backward's query and key passes run on the vector unit
+ *            for 16 and 64).
  * Memory     Every pointer is device memory on the current HIP device, owned
  *            by the caller.  The library allocates nothing, keeps nothing
  *            after return, and never synchronises: work is enqueued on
@@ -91,7 +92,7 @@ typedef enum {
     SANA_OK = 0,
     SANA_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad dtype code,
                                   eps non-finite or < 0, block_len < 1, unknown stage bit */
-    SANA_ERR_UNSUPPORTED = 2,  /* D not 16, 32 or 64 (32 for the backward), or sizes
+    SANA_ERR_UNSUPPORTED = 2,  /* D not 16, 32 or 64, or sizes
                                   beyond what the launch grid covers */
     SANA_ERR_ALIGNMENT = 3,    /* q, k, v, out not 16-byte aligned, workspace not 256-byte aligned */
     SANA_ERR_ALIAS = 4,        /* out or workspace overlaps an input, or each other */

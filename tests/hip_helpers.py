@@ -40,6 +40,14 @@ def f16_round(x64: np.ndarray) -> np.ndarray:
     return x64.astype(np.float32).astype(np.float16).astype(np.float64)
 
 
+# Absolute error allowance of the fp32 pipeline for a 16-bit gradient or
+# tangent, relative to its scale (max |exact|): the recursive fp32 sum of n
+# products errs by at most about n u sum|terms| (u = 2^-24), the longest sum
+# has 64 terms (head dim 64), and the terms of a derivative are of the order
+# of its scale.  It matters only where the terms cancel (an exact dq of ~0).
+FP32_PIPELINE_FRAC = 64 * 2.0 ** -24
+
+
 def compare(got: np.ndarray, want: np.ndarray, v: np.ndarray, out_bf16, label: str = ""):
     """Returns (max_abs, rel_l2) and asserts the parity bar.  out_bf16: False
     (fp32 out), True (bf16 out) or "f16" (fp16 out)."""

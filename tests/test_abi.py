@@ -48,11 +48,13 @@ def test_other_head_dims():
     for d in (8, 48, 128):
         assert sana.lib.sana_linattn_workspace_bytes(1, 8, 4096, d, 0, ctypes.byref(ctypes.c_size_t())) == \
             sana.SANA_ERR_UNSUPPORTED
-    assert sana.lib.sana_linattn_bwd_workspace_bytes(1, 8, 4096, 64, 0, ctypes.byref(ctypes.c_size_t())) == \
-        sana.SANA_ERR_UNSUPPORTED
-    for d in (16, 64):   # the forward-mode derivative takes every head dim: one state and one tangent state
+    for d in (16, 64):   # the backward and the forward-mode derivative take every head dim
         jw = sana.sana_linattn_jvp_workspace_bytes(1, 8, 4096, d, 0)
-        assert jw >= 2 * 8 * d * (d + 1) * 4
+        assert jw >= 2 * 8 * d * (d + 1) * 4   # one state and one tangent state per head
+        bw = sana.sana_linattn_bwd_workspace_bytes(1, 8, 4096, d, 0)
+        assert bw >= 2 * 8 * d * (d + 1) * 4   # the forward's state and one gradient state per head
+    for f in (sana.lib.sana_linattn_bwd_workspace_bytes, sana.lib.sana_linattn_jvp_workspace_bytes):
+        assert f(1, 8, 4096, 48, 0, ctypes.byref(ctypes.c_size_t())) == sana.SANA_ERR_UNSUPPORTED
 
 
 def test_workspace_and_plan_queries():
@@ -120,7 +122,7 @@ def fwd(q=A, k=A + 64 * MB, v=A + 128 * MB, out=A + 192 * MB, in_dt=1, out_dt=0,
     (dict(out_dt=-1), sana.SANA_ERR_INVALID_ARG),
     (dict(out_dt=3), sana.SANA_ERR_INVALID_ARG),
     (dict(D=48), sana.SANA_ERR_UNSUPPORTED),
-    (dict(D=16, ws_bytes=1024), sana.SANA_ERR_WORKSPACE),   # head dims 16 and 64 run on the vector unit
+    (dict(D=16, ws_bytes=1024), sana.SANA_ERR_WORKSPACE),   # head dims 16 and 64: their own workspace sizes
     (dict(D=64, ws_bytes=1024), sana.SANA_ERR_WORKSPACE),
     (dict(B=-1), sana.SANA_ERR_INVALID_ARG),
     (dict(eps=float("nan")), sana.SANA_ERR_INVALID_ARG),
@@ -229,7 +231,7 @@ def bwd(q=A, k=A + 64 * MB, v=A + 128 * MB, g=A + 192 * MB, dq=A + 256 * MB, dk=
     (dict(g_dt=3), sana.SANA_ERR_INVALID_ARG),
     (dict(gr_dt=-1), sana.SANA_ERR_INVALID_ARG),
     (dict(in_dt=5), sana.SANA_ERR_INVALID_ARG),
-    (dict(D=64), sana.SANA_ERR_UNSUPPORTED),
+    (dict(D=48), sana.SANA_ERR_UNSUPPORTED),
     (dict(eps=float("nan")), sana.SANA_ERR_INVALID_ARG),
     (dict(dk=A + 320 * MB + 8), sana.SANA_ERR_ALIGNMENT),
     (dict(g=A + 192 * MB + 2), sana.SANA_ERR_ALIGNMENT),

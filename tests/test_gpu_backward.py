@@ -8,15 +8,15 @@ import torch
 
 import oracle
 import workloads
-from hip_helpers import bf16_round, f16_round, to_device
+from hip_helpers import FP32_PIPELINE_FRAC, bf16_round, f16_round, to_device
 
 pytestmark = pytest.mark.gpu
 
 # Bar: the forward's (rel-L2 <= 1e-4) with max-abs taken relative to each
 # gradient's own scale, max-abs <= 2e-3 * max|exact gradient|.  A 16-bit
 # gradient is compared with the rounded exact gradient instead, and each
-# element must lie within one ulp of the exact value plus 1e-6 of the scale
-# (the fp32 pipeline's own error), as for a 16-bit forward output.
+# element must lie within one ulp of the exact value plus the fp32 pipeline's
+# own error (FP32_PIPELINE_FRAC of the scale).
 REL_L2 = 1e-4
 MAX_ABS_FRAC = 2e-3
 
@@ -49,7 +49,7 @@ def check(got, want, grad_t, label):
         else:
             e = np.floor(np.log2(np.maximum(np.abs(b), 1e-300)))
             ulp = np.exp2(e - 7) if grad_t == torch.bfloat16 else np.exp2(np.maximum(e, -14) - 10)
-            bad = np.abs(a - b) > ulp + 1e-6 * scale
+            bad = np.abs(a - b) > ulp + FP32_PIPELINE_FRAC * scale
             assert not np.any(bad), f"{label}/{name}: {int(bad.sum())} values beyond one ulp"
 
 
@@ -95,6 +95,22 @@ def test_backward_edge_shapes(B, N, H, L, dt):
     (q, k, v, g), want = case(w, dt)
     check(run(q, k, v, g, L, w.eps, DT[dt]), want, DT[dt], w.name)
     check(run(q, k, v, g, L, w.eps, torch.float32), want, torch.float32, w.name + "/f32grad")
+
+
+HEAD_DIMS = [(2, 1000, 5, 100, 1, 64), (1, 777, 7, 0, 2, 16), (2, 33, 1, 0, 0, 16), (1, 300, 3, 1, 0, 64),
+             (1, 16384, 35, 0, 1, 64), (1, 16384, 140, 0, 1, 16)]
+
+
+@pytest.mark.parametrize("B,N,H,L,dt,D", HEAD_DIMS, ids=[f"B{b}N{n}H{h}L{l}dt{t}D{d}" for b, n, h, l, t, d in HEAD_DIMS])
+def test_backward_other_head_dims(B, N, H, L, dt, D):
+    """Head dims 16 and 64 (vector-unit query and key passes after the
+    forward's matrix-core state): ragged N, odd and single heads, block
+    lengths 1 and 100, the headline's token-head-feature count."""
+    w = workloads.Workload(f"bwd_B{B}N{N}H{H}L{L}dt{dt}D{D}", B, N, H, D, dt, seed=150 + N % 19 + D, block_len=L)
+    (q, k, v, g), want = case(w, dt)
+    check(run(q, k, v, g, L, w.eps, DT[dt]), want, DT[dt], w.name)
+    if N < 16384:
+        check(run(q, k, v, g, L, w.eps, torch.float32), want, torch.float32, w.name + "/f32grad")
 
 
 def test_backward_single_token_is_identity_in_v():

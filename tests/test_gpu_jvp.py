@@ -8,13 +8,14 @@ import torch
 
 import oracle
 import workloads
-from hip_helpers import bf16_round, compare, f16_round, to_device
+from hip_helpers import FP32_PIPELINE_FRAC, bf16_round, compare, f16_round, to_device
 
 pytestmark = pytest.mark.gpu
 
 # Tangent bar: rel-L2 <= 1e-4 and max-abs <= 2e-3 * max|exact tangent| (fp32
 # out); a 16-bit tangent against the rounded exact one, within one ulp plus
-# 1e-6 of the scale.  The primal output has the forward's bar.
+# the fp32 pipeline's error (FP32_PIPELINE_FRAC of the scale).  The primal
+# output has the forward's bar.
 REL_L2 = 1e-4
 MAX_ABS_FRAC = 2e-3
 
@@ -42,7 +43,7 @@ def check_tangent(got, want, out_t, label):
     else:
         e = np.floor(np.log2(np.maximum(np.abs(want), 1e-300)))
         ulp = np.exp2(e - 7) if out_t == torch.bfloat16 else np.exp2(np.maximum(e, -14) - 10)
-        assert not np.any(np.abs(got - want) > ulp + 1e-6 * scale), f"{label}: tangent beyond one ulp"
+        assert not np.any(np.abs(got - want) > ulp + FP32_PIPELINE_FRAC * scale), f"{label}: tangent beyond one ulp"
 
 
 def run(x, w, out_t):

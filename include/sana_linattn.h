@@ -36,11 +36,10 @@
  *            rounded to nearest-even (outputs lie within the range of V, so an
  *            fp16 out cannot overflow).  D is 32 (the Sana head dim, on the matrix
  *            cores; fp32 inputs as three-term bf16 splits with the products
- *            below 2^-24 dropped) or, for the forward entry points, 16 or
- *            64 (the same kernels on 32-feature groups of the token row);
- *            the backward and the forward-mode derivative take all three
- *            (the backward's query and key passes run on the vector unit
- *            for 16 and 64).
+ *            below 2^-24 dropped), 16 or 64 (the same kernels on 32-feature
+ *            groups of the token row) for every entry point; the
+ *            backward's query and key passes run on the vector unit for 16
+ *            and 64.
  * Memory     Every pointer is device memory on the current HIP device, owned
  *            by the caller.  The library allocates nothing, keeps nothing
  *            after return, and never synchronises: work is enqueued on

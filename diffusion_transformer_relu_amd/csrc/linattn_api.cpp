@@ -222,14 +222,18 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
     bp->grad_dtype = grad_dtype;
     if (B == 0 || H == 0 || N == 0) return SANA_OK;
     const Plan& pl = bp->fw;
-    // the matrix-core query and key kernels are built for D = 32; other head
-    // dims take the vector kernels (the forward's state is rebuilt on the
-    // matrix cores either way)
-    bp->key_mfma = bp->query_mfma = pl.mfma && D == sana::kD;
-    if (bp->query_mfma) {
+    // the matrix-core query kernel is built for D = 32, the key kernel for
+    // every head dim with 16-bit inputs and for D = 32 with fp32; the rest takes
+    // the vector kernels (the forward's state is rebuilt on the matrix cores
+    // either way)
+    bp->query_mfma = pl.mfma && D == sana::kD;
+    bp->key_mfma = pl.mfma && (D == sana::kD || in_dtype != SANA_DT_F32);
+    bp->tk = bp->tq = kBwdTile;
+    if (bp->query_mfma || bp->key_mfma) {
         // Tiles (multiples of 64 tokens inside one block) for the (batch, head
         // pair, block) units: the key and query kernels' registers and LDS
-        // fit 3 work-groups per CU (2 for fp32 inputs).  The tile count per block
+        // fit 3 work-groups per CU (2 for fp32 inputs and for the head-dim-64
+        // key kernel).  The tile count per block
         // minimises rounds of work-groups x (tile + 64), the 64 tokens
         // standing for a work-group's prologue and epilogue: one round when
         // the units allow it, else short tiles that fill the last round.
@@ -251,12 +255,10 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
             return (int)best;
         };
         const int per_cu = pl.mfma16 ? 3 : 2;
-        bp->tk = tile_for(per_cu);
-        bp->tq = tile_for(per_cu);
-    } else {
-        bp->tk = kBwdTile;
-        bp->tq = D == 2 * sana::kD ? kBwdTile / 4 : kBwdTile;   // the vector query kernel's tokens per work-group
+        if (bp->key_mfma) bp->tk = tile_for(D == 2 * sana::kD ? 2 : per_cu);
+        if (bp->query_mfma) bp->tq = tile_for(per_cu);
     }
+    if (!bp->query_mfma && D == 2 * sana::kD) bp->tq = kBwdTile / 4;   // the vector query kernel's tokens per work-group
     bp->tpbq = ceil_div(pl.L, bp->tq);
     bp->tpbk = ceil_div(pl.L, bp->tk);
     bp->Pq = pl.NB * bp->tpbq;

@@ -232,12 +232,12 @@ constexpr int kTileTensor = 2 * kTileHead;            // bytes per tensor
 
 struct TileLoader {
     const uint16_t* x[2];   // the two tensors (the second may be null: one tensor only)
-    long long hstride;      // elements per token row (H * D)
-    int b, N, h0, nh, t1;
+    long long hstride;      // elements per token row
+    int b, N, h0, row_elems, t1;   // row_elems: elements of a row that exist (pieces past them read as zero)
     u32x4 r[2][2];          // [tensor][piece]: this thread's 2 pieces of 16 bytes
 
     // piece p (0..511) of a tile: part (p & 3), head ((p >> 2) & 1), token p >> 3.
-    // A missing head reads as zero.  Tokens past t1 read as the row t1 - 1:
+    // A missing head (or the missing half of a 32-feature group) reads as zero.  Tokens past t1 read as the row t1 - 1:
     // their per-token results equal that row's (store_tile relies on it), and
     // code that sums over tokens must skip them.
     __device__ __forceinline__ void load(int t0) {
@@ -246,8 +246,9 @@ struct TileLoader {
             const int pc = threadIdx.x + kThreads * pi;
             const int part = pc & 3, hd = (pc >> 2) & 1, tok = pc >> 3;
             const int n = min(t0 + tok, t1 - 1);
-            const bool ok = hd < nh;
-            const long long off = ((long long)b * N + n) * hstride + (h0 + (ok ? hd : 0)) * kD + part * 8;
+            const int col = (h0 + hd) * kD + part * 8;
+            const bool ok = col < row_elems;
+            const long long off = ((long long)b * N + n) * hstride + (ok ? col : 0);
 #pragma unroll
             for (int ts = 0; ts < 2; ++ts) {
                 if (ts == 1 && !x[1]) break;
@@ -297,6 +298,46 @@ __device__ __forceinline__ void tile_operand(const uint8_t* lds, int ts, int hh,
 }
 
 // ------------------------------------------------------------------ key pass, matrix cores
+// Split-term operands (three bf16 terms, round to nearest) of one 32-row block
+// of a head-dim HD gradient state for the key pass, K-steps of 16: lane (g, i)
+// gets A[i][16 ks + 8 g + e] in out[ks][sp] (element e), with
+//   natural:    A[i][kk] = Ghat[row(i)][kk]    (dk^T = Ghat_v v^T)
+//   transposed: A[i][kk] = Ghat[kk][col(i)]    (dv^T = Ghat_v^T a^T)
+// head(r) points at head r's HD x (HD + 1) state.  HD = 32: head grp, row(i) =
+// col(i) = i.  HD = 64: head grp, row(i) = col(i) = 32 half + i, kk over all
+// 64 features (four K-steps).  HD = 16: block-diagonal over heads 2 grp
+// (K-step 0) and 2 grp + 1 (K-step 1, zero when there is none), nonzero in
+// rows 16 ks .. 16 ks + 15 of K-step ks only.
+template <int HD, typename HeadState>
+__device__ __forceinline__ void key_operands(HeadState head, int grp, int half, int HR, int lane, bool transposed,
+                                             u32x4 (&out)[KSteps<HD>::value][3]) {
+    constexpr int KS = KSteps<HD>::value, SW = HD + 1;
+    const int g = lane >> 5, i = lane & 31;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        float x[8];
+        if constexpr (HD == kD / 2) {
+            const int hr = 2 * grp + ks;
+            const bool on = hr < HR && (i >> 4) == ks;
+            const float* G = head(min(hr, HR - 1));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int kk = 8 * g + e, r = i & 15;
+                x[e] = on ? (transposed ? G[kk * SW + r] : G[r * SW + kk]) : 0.f;
+            }
+        } else {
+            const float* G = head(grp);
+            const int ri = (HD == 2 * kD ? kD * half : 0) + i;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int kk = 16 * ks + 8 * g + e;
+                x[e] = transposed ? G[kk * SW + ri] : G[ri * SW + kk];
+            }
+        }
+        split3_f32x8(x, out[ks]);
+    }
+}
+
 // grid.x = (b * HP + hp) * (NB * tpb) + beta * tpb + tile.  The work-group
 // stages 64-key tiles of k and v (both heads) through LDS; wave w then handles
 // head 2*hp + (w & 1) and keys 32 (w >> 1) .. + 31 of the tile.  With
@@ -304,10 +345,17 @@ __device__ __forceinline__ void tile_operand(const uint8_t* lds, int ts, int hh,
 //   dv^T = Ghat_v^T a^T          (A = Ghat transposed, B = a)
 //   da^T = Ghat_v v^T + Ghat_z   (A = Ghat natural,    B = v)
 //   dk   = da masked by k > 0
-template <bool F16, typename OutT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_bwd_key_mfma(
+// Head dims 16 and 64 take the forward's 32-feature groups ("heads" here: H of
+// them, HP pairs; HR real heads): HD = 64, wave w computes the rows of group
+// w & 1 of its head against all 64 features (four K-steps, the B operand from
+// both groups' staged rows); HD = 16, the group's two heads as one
+// block-diagonal state (key_operands).
+template <bool F16, typename OutT, int HD>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 2 * kD ? 2 : 3, 8))) void k_bwd_key_mfma(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ ghat,
-    OutT* __restrict__ dk, OutT* __restrict__ dv, int N, int H, int HP, int L, int NB, int tile, int tpb) {
+    OutT* __restrict__ dk, OutT* __restrict__ dv, int N, int H, int HP, int HR, int L, int NB, int tile, int tpb) {
+    constexpr int KS = KSteps<HD>::value, SW = HD + 1, SF = HD * SW;
+    constexpr bool D64 = HD == 2 * kD, D16 = HD == kD / 2;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kTileTensor];
     __shared__ __attribute__((aligned(16))) float otile[4][32 * kPitch];                // fp32 out
     __shared__ __attribute__((aligned(16))) uint16_t ctile[2][2][32 * kPairRow];        // 16-bit out: [half][dv, dk]
@@ -322,21 +370,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
     const int blk0 = beta * L, blk1 = min(blk0 + L, N);
     const int t0 = blk0 + tib * tile, t1 = min(t0 + tile, blk1);
     const int g = lane >> 5, i = lane & 31;
-    const int nh = min(2, H - 2 * hp);
     if (t0 >= t1) return;   // uniform over the work-group
 
-    // this wave's head: Ghat as split-term operands in both layouts, Ghat[:, D]
-    const int hs = min(h, H - 1);   // a missing second head computes on the first (never stored)
-    const float* G = ghat + (((size_t)b * H + hs) * NB + beta) * kStateFloats;
-    u32x4 gt[2][3], gn[2][3];
-    state_operands(G, lane, true, gt);
-    state_operands(G, lane, false, gn);
-    float gz[16];
+    // this wave's group: Ghat as split-term operands in both layouts, Ghat[:, D]
+    const int hs = min(h, H - 1);   // a missing second group computes on the first (never stored)
+    auto head_G = [&](int hr) { return ghat + (((size_t)b * HR + hr) * NB + beta) * SF; };
+    const int grp = D64 ? hp : hs;
+    u32x4 gt[KS][3], gn[KS][3];
+    key_operands<HD>(head_G, grp, hh, HR, lane, true, gt);
+    key_operands<HD>(head_G, grp, hh, HR, lane, false, gn);
+    float gz[16];   // Ghat[row][HD] at this lane's accumulator rows 8 (r / 4) + 4 g + r % 4
 #pragma unroll
-    for (int r = 0; r < 16; ++r) gz[r] = G[(8 * (r >> 2) + 4 * g + (r & 3)) * kW + kD];
+    for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * g + (r & 3);
+        if constexpr (D16) {
+            const int hr = 2 * hs + (row >> 4);
+            gz[r] = hr < HR ? head_G(hr)[(row & 15) * SW + HD] : 0.f;
+        } else {
+            gz[r] = head_G(grp)[((D64 ? kD * hh : 0) + row) * SW + HD];
+        }
+    }
 
-    const long long hstride = (long long)H * kD;
-    TileLoader ld = {{k, v}, hstride, b, N, 2 * hp, nh, t1, {}};
+    const long long hstride = (long long)HR * HD;
+    const int ncols = min(32, HR * HD - h * kD);                 // fp32 out: columns of this group that exist
+    const int nchunk = min(8, (HR * HD - 2 * hp * kD) / 8);      // 16-bit out: 16-byte chunks of the line
+    TileLoader ld = {{k, v}, hstride, b, N, 2 * hp, HR * HD, t1, {}};
     float* ot = otile[wave];
     ld.load(t0);
     for (int tt0 = t0; tt0 < t1; tt0 += kTileTok) {
@@ -353,21 +411,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
         // (16-bit out: every wave computes, so that the work-group barrier
         // below is reached by all; rows past the range hold the clamped last
         // row and a missing head computes on zeros, never stored)
-        u32x4 k0, k1, v0, v1;
-        tile_operand(lds, 0, hh, 32 * th + i, g, k0, k1);
-        tile_operand(lds, 1, hh, 32 * th + i, g, v0, v1);
-        const u32x4 a0 = relu_bf16x8(k0), a1 = relu_bf16x8(k1);
+        // B operands: features 16 ks + 8 g .. of the key (HD = 64: K-steps 0, 1
+        // from group 0's staged row, 2, 3 from group 1's)
+        u32x4 a[KS], vb[KS];
+#pragma unroll
+        for (int gi = 0; gi < KS / 2; ++gi) {
+            const int gr = D64 ? gi : hh;
+            tile_operand(lds, 0, gr, 32 * th + i, g, a[2 * gi], a[2 * gi + 1]);
+            tile_operand(lds, 1, gr, 32 * th + i, g, vb[2 * gi], vb[2 * gi + 1]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) a[ks] = relu_bf16x8(a[ks]);
         const uint32_t mask = positive_rows(lds + hh * kTileHead + (32 * th + i) * kTileRow, g);
 
         f32x16 accv = {};
-        accv = mma_split<F16>(gt, a0, a1, accv);
+        accv = mma_split_ks<F16, KS>(gt, a, accv);
         f32x16 acck = {};
-        acck = mma_split<F16>(gn, v0, v1, acck);
+        acck = mma_split_ks<F16, KS>(gn, vb, acck);
 #pragma unroll
         for (int r = 0; r < 16; ++r) acck[r] = ((mask >> r) & 1u) ? acck[r] + gz[r] : 0.f;
         if constexpr (sizeof(OutT) == 4) {
-            store_tile<OutT>(ot, accv, lane, n, [&](int t) { return dv + ((long long)b * N + tt + t) * hstride + h * kD; });
-            store_tile<OutT>(ot, acck, lane, n, [&](int t) { return dk + ((long long)b * N + tt + t) * hstride + h * kD; });
+            store_tile<OutT>(ot, accv, lane, n, [&](int t) { return dv + ((long long)b * N + tt + t) * hstride + h * kD; },
+                             ncols);
+            store_tile<OutT>(ot, acck, lane, n, [&](int t) { return dk + ((long long)b * N + tt + t) * hstride + h * kD; },
+                             ncols);
         } else {
             // both heads of a key share a 128-byte line of dk and of dv
             put_pair_tile<OutT>(ctile[th][0], accv, lane, hh);
@@ -380,8 +447,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
                     return reinterpret_cast<uint16_t*>(base + ((long long)b * N + min(tt + r, t1 - 1)) * hstride + 2 * hp * kD);
                 };
             };
-            store_pair_rows<OutT>(ctile[th][0], lane, 16 * hh, 4 * nh, row(dv));
-            store_pair_rows<OutT>(ctile[th][1], lane, 16 * hh, 4 * nh, row(dk));
+            store_pair_rows<OutT>(ctile[th][0], lane, 16 * hh, nchunk, row(dv));
+            store_pair_rows<OutT>(ctile[th][1], lane, 16 * hh, nchunk, row(dk));
             // the next tile's first barrier keeps the pair tiles until these reads are done
         }
     }
@@ -746,7 +813,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
         }
     } else if (t0 < t1) {   // uniform over the work-group
         const uint16_t* dsrc = kDoutOperand ? reinterpret_cast<const uint16_t*>(dout) : nullptr;
-        TileLoader ld = {{reinterpret_cast<const uint16_t*>(q), dsrc}, hstride, b, N, 2 * hp, min(2, H - 2 * hp), t1, {}};
+        TileLoader ld = {{reinterpret_cast<const uint16_t*>(q), dsrc}, hstride, b, N, 2 * hp, H * kD, t1, {}};
         ld.load(t0);
         for (int tt0 = t0; tt0 < t1; tt0 += kTileTok) {
             __syncthreads();   // the previous tile has been consumed
@@ -868,14 +935,14 @@ hipError_t launch_bwd_key(const BwdPlan& bp, const void* k, const void* v, const
                                    static_cast<const float*>(k), static_cast<const float*>(v), ghat,
                                    static_cast<OT*>(dk), static_cast<OT*>(dv), pl.N, pl.H, pl.HP, pl.L, pl.NB, bp.tk,
                                    bp.tpbk);
-            else if (pl.in_dtype == 2)
-                hipLaunchKernelGGL((k_bwd_key_mfma<true, OT>), dim3(grid), dim3(kThreads), 0, stream, k16, v16, ghat,
-                                   static_cast<OT*>(dk), static_cast<OT*>(dv), pl.N, pl.H, pl.HP, pl.L, pl.NB,
-                                   bp.tk, bp.tpbk);
             else
-                hipLaunchKernelGGL((k_bwd_key_mfma<false, OT>), dim3(grid), dim3(kThreads), 0, stream, k16, v16,
-                                   ghat, static_cast<OT*>(dk), static_cast<OT*>(dv), pl.N, pl.H, pl.HP, pl.L, pl.NB,
-                                   bp.tk, bp.tpbk);
+                by_head_dim(pl.D, [&](auto dd) {
+                    constexpr int DD = decltype(dd)::value;
+                    hipLaunchKernelGGL((pl.in_dtype == 2 ? k_bwd_key_mfma<true, OT, DD> : k_bwd_key_mfma<false, OT, DD>),
+                                       dim3(grid), dim3(kThreads), 0, stream, k16, v16, ghat, static_cast<OT*>(dk),
+                                       static_cast<OT*>(dv), pl.N, groups32(pl), pl.HP, pl.H, pl.L, pl.NB, bp.tk,
+                                       bp.tpbk);
+                });
         });
         return hipGetLastError();
     }

@@ -545,9 +545,12 @@ template <typename GT> struct GradRow;
 template <> struct GradRow<float> {
     f32x4 x[4];
     __device__ __forceinline__ void load_lds(const uint8_t*, int) {}   // fp32 rows are not staged
-    __device__ __forceinline__ void load(const float* row, int g) {
+    // rows rr >= nrr (features 16.. of a group that is a lone head of dim 16) read as zero
+    __device__ __forceinline__ void load(const float* row, int g, int nrr = 4) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) x[rr] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 8 * rr + 4 * g));
+        for (int rr = 0; rr < 4; ++rr)
+            x[rr] = rr < nrr ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 8 * rr + 4 * g))
+                             : (f32x4){0.f, 0.f, 0.f, 0.f};
     }
     __device__ __forceinline__ float at(int rr, int e) const { return x[rr][e]; }
 };
@@ -558,9 +561,11 @@ template <> struct GradRow<uint16_t> {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) x[rr] = *reinterpret_cast<const u32x2*>(row + 16 * rr + 8 * g);
     }
-    __device__ __forceinline__ void load(const uint16_t* row, int g) {
+    __device__ __forceinline__ void load(const uint16_t* row, int g, int nrr = 4) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) x[rr] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(row + 8 * rr + 4 * g));
+        for (int rr = 0; rr < 4; ++rr)
+            x[rr] = rr < nrr ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(row + 8 * rr + 4 * g))
+                             : (u32x2){0u, 0u};
     }
     __device__ __forceinline__ float at(int rr, int e) const {
         const uint32_t w = x[rr][e >> 1];
@@ -573,9 +578,11 @@ template <> struct GradRow<_Float16> {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) x[rr] = *reinterpret_cast<const u32x2*>(row + 16 * rr + 8 * g);
     }
-    __device__ __forceinline__ void load(const _Float16* row, int g) {
+    __device__ __forceinline__ void load(const _Float16* row, int g, int nrr = 4) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) x[rr] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(row + 8 * rr + 4 * g));
+        for (int rr = 0; rr < 4; ++rr)
+            x[rr] = rr < nrr ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(row + 8 * rr + 4 * g))
+                             : (u32x2){0u, 0u};
     }
     __device__ __forceinline__ float at(int rr, int e) const {
         const uint32_t w = x[rr][e >> 1];
@@ -599,11 +606,20 @@ template <> struct GradRow<_Float16> {
 // i, features 8 rr + 4 g + e), the layout of the MFMA result.
 // The two waves of a head then add their G in a fixed order and write the
 // tile's partial gradient state.
-template <typename QT, typename GT, typename OutT>
+//
+// Head dim 16 (HD = 16, 16-bit q): a 32-feature group holds two heads (H
+// counts the groups, HR the heads).  P is the group's block-diagonal state
+// (key_operands), so m = P_v dout keeps the heads apart; every per-token
+// scalar (r, w) exists per head (rows 0..15 the first, 16..31 the second),
+// and of the group's G only the diagonal 16 x 16 blocks are written.
+template <typename QT, typename GT, typename OutT, int HD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(QT) == 2 ? 3 : 2, 8))) void k_bwd_query_mfma(
     const QT* __restrict__ q, const GT* __restrict__ dout, const float* __restrict__ state,
-    OutT* __restrict__ dq, float* __restrict__ gpart, int N, int H, int HP, int L, int NB, int tile, int tpb,
+    OutT* __restrict__ dq, float* __restrict__ gpart, int N, int H, int HP, int HR, int L, int NB, int tile, int tpb,
     float eps) {
+    constexpr bool D16 = HD == kD / 2;
+    static_assert(HD == kD || (D16 && sizeof(QT) == 2), "head dim 16 takes 16-bit q");
+    constexpr int SW = HD + 1, SF = HD * SW;
     // 16-bit q (and 16-bit dout) are staged through LDS by the work-group;
     // fp32 q is read by each wave straight from global memory, its f = ReLU(q)
     // kept in an fp32 LDS tile per wave (in the staging area) for the G sums
@@ -611,7 +627,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     __shared__ OperandLds opnd;                                     // P natural split terms, both heads
     __shared__ __attribute__((aligned(16))) float pzs[2][32];       // P[:, D] of each head
     __shared__ __attribute__((aligned(16))) float ut[4][32 * kPitch];   // u tile, then the dq tile
-    __shared__ __attribute__((aligned(16))) float wv[4][32];        // w of each token
+    __shared__ __attribute__((aligned(16))) float wv[4][2][32];     // w of each token (head dim 16: of each head)
     __shared__ __attribute__((aligned(16))) uint8_t lds_in[2 * kTileTensor];   // staged q (and 16-bit dout)
     static_assert(sizeof(lds_in) >= 4 * 32 * kPitch * sizeof(float), "f tiles exceed the staging area");
 
@@ -626,22 +642,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     const int t0 = blk0 + tib * tile, t1 = min(t0 + tile, blk1);
     const int g = lane >> 5, i = lane & 31;
 
+    auto head_P = [&](int hr) { return state + (((size_t)b * HR + hr) * NB + beta) * SF; };
     if (wave < 2 && h < H) {
-        const float* Pst = state + (((size_t)b * H + h) * NB + beta) * kStateFloats;
         u32x4 t[2][3];
-        state_operands(Pst, lane, false, t);
+        key_operands<HD>(head_P, h, 0, HR, lane, false, t);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int sp = 0; sp < 3; ++sp) opnd.v[hh][ks][sp][lane] = t[ks][sp];
-        if (lane < 32) pzs[hh][lane] = Pst[lane * kW + kD];
+        if (lane < 32) {
+            if constexpr (D16) {
+                const int hr = 2 * h + (lane >> 4);
+                pzs[hh][lane] = hr < HR ? head_P(hr)[(lane & 15) * SW + HD] : 0.f;
+            } else {
+                pzs[hh][lane] = head_P(h)[lane * SW + HD];
+            }
+        }
     }
     __syncthreads();
 
-    const long long hstride = (long long)H * kD;
+    const long long hstride = (long long)HR * HD;
+    const int ncols = min(32, HR * HD - h * kD);   // columns of this group that exist (16: a lone head of dim 16)
     const bool active = h < H && t0 < t1;
     float* ot = ut[wave];
-    float* wl = wv[wave];
+    float* wl = wv[wave][0];
     f32x16 accG = {};
     float gz_acc = 0.f;   // lane (g, j): sum over this lane's tokens of f_j w
 
@@ -659,22 +683,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
         // registers live; f > 0 is the mask q > 0); z = P[:, D] at the same rows
         auto fa = [&](int rr, int e) { return relu_f32(x.qa.at(rr, e)); };
         auto zrow = [&](int rr) { return *reinterpret_cast<const f32x4*>(&pzs[hh][8 * rr + 4 * g]); };
-        float dp = 0.f;
+        float dp[2] = {0.f, 0.f};   // head dim 16: per head (rows rr < 2, rr >= 2)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const f32x4 z = zrow(rr);
+            float& d = dp[D16 && rr >= 2];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dp = fmaf(fa(rr, e), z[e], dp);
+            for (int e = 0; e < 4; ++e) d = fmaf(fa(rr, e), z[e], d);
         }
-        const float den = dp + __shfl_xor(dp, 32);
-        const float r = 1.0f / (den + eps);
+        float rh[2];
+#pragma unroll
+        for (int s2 = 0; s2 < (D16 ? 2 : 1); ++s2) rh[s2] = 1.0f / (dp[s2] + __shfl_xor(dp[s2], 32) + eps);
+        if constexpr (!D16) rh[1] = rh[0];
+        auto rrow = [&](int rr) { return rh[D16 && rr >= 2]; };   // r of the head of rows 8 rr ..
 
         // u to the LDS tile (token-major); for fp32 q also f
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             f32x4 u4;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) u4[e] = x.gr.at(rr, e) * r;
+            for (int e = 0; e < 4; ++e) u4[e] = x.gr.at(rr, e) * rrow(rr);
             *reinterpret_cast<f32x4*>(ot + i * kPitch + 8 * rr + 4 * g) = u4;
             if constexpr (!kStage) {
                 f32x4 f4;
@@ -685,7 +713,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
         }
 
         f32x16 acc = {};
-        float rs;   // per-token factor of the MFMA result: acc * rs = r P_v dout
+        float rs[2];   // per-token (per-head) factor of the MFMA result: acc * rs = r P_v dout
         {
             u32x4 A[2][3];
 #pragma unroll
@@ -694,7 +722,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
                 for (int sp = 0; sp < 3; ++sp) A[ks][sp] = opnd.v[hh][ks][sp][lane];
             if constexpr (kDoutOperand) {
                 acc = mma_split<std::is_same<GT, _Float16>::value>(A, x.g0, x.g1, acc);
-                rs = r;
+                rs[0] = rh[0];
+                rs[1] = rh[1];
             } else {
                 // u read back in the operand layout (channels 16 ks + 8 g ..)
                 // and split into three bf16 terms
@@ -723,18 +752,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
                     acc = mfma_bf16(A[ks][1], ub[ks][0], acc);
                     acc = mfma_bf16(A[ks][0], ub[ks][0], acc);
                 }
-                rs = 1.f;
+                rs[0] = rs[1] = 1.f;
             }
         }
-        // w = -r (dout . out) = -r (f . acc rs)
-        float go = 0.f;
+        // w = -r (dout . out) = -r (f . acc rs), per head for head dim 16
+        float go[2] = {0.f, 0.f};
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) go = fmaf(fa(rr, e), acc[4 * rr + e], go);
-        go += __shfl_xor(go, 32);
-        const float w = -r * (go * rs);
-        if (g == 0) wl[i] = i < n ? w : 0.f;   // 0 past the range: the G_z sum skips those tokens
+            for (int e = 0; e < 4; ++e) go[D16 && rr >= 2] = fmaf(fa(rr, e), acc[4 * rr + e], go[D16 && rr >= 2]);
+        float wh[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const float gs = go[s2] + __shfl_xor(go[s2], 32);
+            wh[s2] = -rh[s2] * (gs * rs[s2]);
+        }
+        if constexpr (!D16) wh[1] = wh[0];
+        if (g == 0) {   // 0 past the range: the G_z sum skips those tokens
+            wl[i] = i < n ? wh[0] : 0.f;
+            if constexpr (D16) wl[32 + i] = i < n ? wh[1] : 0.f;
+        }
         __builtin_amdgcn_wave_barrier();
         asm volatile("" ::: "memory");   // phase boundary: keeps each phase's LDS reads in its phase
 
@@ -751,7 +788,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
                 fv = ft[tok * kPitch + i];
             }
             uv = ot[tok * kPitch + i];
-            wv_ = wl[tok];
+            wv_ = wl[(D16 && i >= 16 ? 32 : 0) + tok];   // w of the head of feature i
         };
         if (n == 32) {   // a whole sub-tile (every one but a range's last)
 #pragma unroll
@@ -780,12 +817,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int rg = 4 * rr + e;
-                acc[rg] = fa(rr, e) > 0.f ? fmaf(z[e], w, acc[rg] * rs) : 0.f;
+                const int s2 = D16 && rr >= 2;
+                acc[rg] = fa(rr, e) > 0.f ? fmaf(z[e], wh[s2], acc[rg] * rs[s2]) : 0.f;
             }
         }
         __builtin_amdgcn_wave_barrier();
         asm volatile("" ::: "memory");   // every read of the u tile precedes the dq tile's writes
-        store_tile<OutT>(ot, acc, lane, n, [&](int t) { return dq + ((long long)b * N + tt + t) * hstride + h * kD; });
+        store_tile<OutT>(ot, acc, lane, n, [&](int t) { return dq + ((long long)b * N + tt + t) * hstride + h * kD; },
+                         ncols);
     };
 
     if constexpr (!kStage) {
@@ -813,7 +852,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
         }
     } else if (t0 < t1) {   // uniform over the work-group
         const uint16_t* dsrc = kDoutOperand ? reinterpret_cast<const uint16_t*>(dout) : nullptr;
-        TileLoader ld = {{reinterpret_cast<const uint16_t*>(q), dsrc}, hstride, b, N, 2 * hp, H * kD, t1, {}};
+        TileLoader ld = {{reinterpret_cast<const uint16_t*>(q), dsrc}, hstride, b, N, 2 * hp, HR * HD, t1, {}};
         ld.load(t0);
         for (int tt0 = t0; tt0 < t1; tt0 += kTileTok) {
             __syncthreads();   // the previous tile has been consumed
@@ -830,7 +869,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
                 x.gr.load_lds(lds_in + kTileTensor + hh * kTileHead + (32 * (wave >> 1) + i) * kTileRow, g);
             } else {
                 const int row = min(tt + i, t1 - 1);
-                x.gr.load(dout + ((long long)b * N + row) * hstride + h * kD, g);
+                x.gr.load(dout + ((long long)b * N + row) * hstride + h * kD, g, ncols / 8);
             }
             body(tt, x);
         }
@@ -850,13 +889,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     }
     __syncthreads();
     if (wave < 2 && h < H) {
-        float* dst = gpart + ((((size_t)b * H + h) * NB + beta) * tpb + tib) * kStateFloats;
+        auto part_of = [&](int hr) { return gpart + ((((size_t)b * HR + hr) * NB + beta) * tpb + tib) * SF; };
+        if constexpr (D16) {
+            // the diagonal 16 x 16 blocks: rows 0..15 (rg < 8) and the lanes of
+            // columns 0..15 are the first head's, the rest the second's
 #pragma unroll
-        for (int rg = 0; rg < 16; ++rg) {
-            const int j = 8 * (rg >> 2) + 4 * g + (rg & 3);
-            dst[j * kW + i] = accG[rg] + red[(hh * 16 + rg) * 64 + lane];
+            for (int rg = 0; rg < 16; ++rg) {
+                const int j = 8 * (rg >> 2) + 4 * g + (rg & 3), hr = 2 * h + (rg >> 3);
+                if ((i >> 4) == (rg >> 3) && hr < HR)
+                    part_of(hr)[(j & 15) * SW + (i & 15)] = accG[rg] + red[(hh * 16 + rg) * 64 + lane];
+            }
+            if (lane < 32 && 2 * h + (lane >> 4) < HR)
+                part_of(2 * h + (lane >> 4))[(lane & 15) * SW + HD] = gz + red[2 * 16 * 64 + hh * 32 + lane];
+        } else {
+            float* dst = part_of(h);
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) {
+                const int j = 8 * (rg >> 2) + 4 * g + (rg & 3);
+                dst[j * SW + i] = accG[rg] + red[(hh * 16 + rg) * 64 + lane];
+            }
+            if (lane < 32) dst[lane * SW + HD] = gz + red[2 * 16 * 64 + hh * 32 + lane];
         }
-        if (lane < 32) dst[lane * kW + kD] = gz + red[2 * 16 * 64 + hh * 32 + lane];
     }
 }
 
@@ -885,10 +938,19 @@ hipError_t launch_bwd_query(const BwdPlan& bp, const void* q, const void* dout, 
                 using OT = typename decltype(ot)::type;
                 by_dtype(pl.in_dtype, [&](auto it) {
                     using QT = typename decltype(it)::type;
-                    hipLaunchKernelGGL((k_bwd_query_mfma<QT, GT, OT>), dim3(grid), dim3(kThreads), 0, stream,
+                    if constexpr (sizeof(QT) == 2) {
+                        if (pl.D == kD / 2) {
+                            hipLaunchKernelGGL((k_bwd_query_mfma<QT, GT, OT, kD / 2>), dim3(grid), dim3(kThreads), 0,
+                                               stream, static_cast<const QT*>(q), static_cast<const GT*>(dout), state,
+                                               static_cast<OT*>(dq), gpart, pl.N, groups32(pl), pl.HP, pl.H, pl.L,
+                                               pl.NB, bp.tq, bp.tpbq, eps);
+                            return;
+                        }
+                    }
+                    hipLaunchKernelGGL((k_bwd_query_mfma<QT, GT, OT, kD>), dim3(grid), dim3(kThreads), 0, stream,
                                        static_cast<const QT*>(q), static_cast<const GT*>(dout), state,
-                                       static_cast<OT*>(dq), gpart, pl.N, pl.H, pl.HP, pl.L, pl.NB, bp.tq, bp.tpbq,
-                                       eps);
+                                       static_cast<OT*>(dq), gpart, pl.N, pl.H, pl.HP, pl.H, pl.L, pl.NB, bp.tq,
+                                       bp.tpbq, eps);
                 });
             });
         });

@@ -222,11 +222,14 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
     bp->grad_dtype = grad_dtype;
     if (B == 0 || H == 0 || N == 0) return SANA_OK;
     const Plan& pl = bp->fw;
-    // the matrix-core query kernel is built for D = 32 and for D = 16 with
-    // 16-bit inputs, the key kernel for every head dim with 16-bit inputs and
-    // for D = 32 with fp32; the rest takes the vector kernels (the forward's
-    // state is rebuilt on the matrix cores either way)
-    bp->query_mfma = pl.mfma && (D == sana::kD || (D == sana::kD / 2 && in_dtype != SANA_DT_F32));
+    // the matrix-core query kernel is built for D = 32, for D = 16 with 16-bit
+    // inputs and for D = 64 with 16-bit inputs and dout; the key kernel for
+    // every head dim with 16-bit inputs and for D = 32 with fp32; the rest
+    // takes the vector kernels (the forward's state is rebuilt on the matrix
+    // cores either way)
+    const bool in16 = in_dtype != SANA_DT_F32;
+    bp->query_mfma = pl.mfma && (D == sana::kD || (D == sana::kD / 2 && in16) ||
+                                 (D == 2 * sana::kD && in16 && dout_dtype != SANA_DT_F32));
     bp->key_mfma = pl.mfma && (D == sana::kD || in_dtype != SANA_DT_F32);
     bp->tk = bp->tq = kBwdTile;
     if (bp->query_mfma || bp->key_mfma) {
@@ -256,7 +259,7 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
         };
         const int per_cu = pl.mfma16 ? 3 : 2;
         if (bp->key_mfma) bp->tk = tile_for(D == 2 * sana::kD ? 2 : per_cu);
-        if (bp->query_mfma) bp->tq = tile_for(per_cu);
+        if (bp->query_mfma) bp->tq = tile_for(D == 2 * sana::kD ? 2 : per_cu);
     }
     if (!bp->query_mfma && D == 2 * sana::kD) bp->tq = kBwdTile / 4;   // the vector query kernel's tokens per work-group
     bp->tpbq = ceil_div(pl.L, bp->tq);

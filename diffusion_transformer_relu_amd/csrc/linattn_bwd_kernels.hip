@@ -13,7 +13,9 @@
 //                 there is one block)
 //   dk_n = [k_n > 0] (Ghat [v_n | 1]),   dv_n = Ghat[:, :D]^T a_n
 // The derivative of ReLU at 0 is taken as 0.  Everything accumulates in fp32;
-// reductions run in fixed orders, so results are bitwise repeatable.
+// reductions run in fixed orders, so results are bitwise repeatable.  Head dims
+// 16 and 64 use the forward kernels' view of a token row as 32-feature groups
+// (a group holds two heads of 16; a head of 64 is two groups).
 #include "linattn_device.h"
 
 #include <type_traits>

@@ -309,21 +309,6 @@ __device__ __forceinline__ f32x16 mma_split(const u32x4 A[2][3], u32x4 b0, u32x4
     return acc;
 }
 
-// Bit j set when feature j of this lane's token is non-zero in the packed
-// operand words x0 (features 8g + ..) and x1 (16 + 8g + ..); the partner lane
-// (i + 32) contributes the other 16 features.
-__device__ __forceinline__ uint32_t nonzero_mask(u32x4 x0, u32x4 x1, int g) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        m |= (uint32_t)((x0[d] & 0xffffu) != 0) << (8 * g + 2 * d);
-        m |= (uint32_t)((x0[d] >> 16) != 0) << (8 * g + 2 * d + 1);
-        m |= (uint32_t)((x1[d] & 0xffffu) != 0) << (16 + 8 * g + 2 * d);
-        m |= (uint32_t)((x1[d] >> 16) != 0) << (16 + 8 * g + 2 * d + 1);
-    }
-    return m | (uint32_t)__shfl_xor((int)m, 32);
-}
-
 // Writes a wave's 32 x 32 accumulator tile (row 8*(r/4) + 4g + r%4 of column
 // i in register r of lane (g, i)) token-major through the wave's LDS tile, then
 // stores whole rows: dst(t) is the output row of token tt + t.  Rows t >= n
@@ -381,19 +366,10 @@ struct F32Operand {
     }
 };
 
-// The three truncation terms of half ks of an fp32 operand, optionally
-// ReLU'd, or (mask given) kept only where the mask operand is > 0.
+// The three truncation terms of half ks of an fp32 operand, optionally ReLU'd.
 __device__ __forceinline__ void split_half(const F32Operand& b, int ks, bool relu, u32x4 t[3]) {
     float x[8];
     b.half(ks, relu, x);
-    split3_trunc_f32x8(x, t);
-}
-__device__ __forceinline__ void split_half_where(const F32Operand& b, const F32Operand& mask, int ks, u32x4 t[3]) {
-    float x[8], m[8];
-    b.half(ks, false, x);
-    mask.half(ks, false, m);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = m[e] > 0.f ? x[e] : 0.f;
     split3_trunc_f32x8(x, t);
 }
 

@@ -480,7 +480,21 @@ def main() -> int:
                 "ms_per_step": round(ms, 5), "GBps": round(alg_bytes / ms / 1e6, 1),
                 "pct_hbm_peak": round(100 * alg_bytes / ms / 1e6 / HBM_PEAK_GBPS, 2),
                 "note": f"head dim {Dx}: the headline buffers viewed as B=1, N=16384, H={Hx}, D={Dx}, bf16 in"}
-            del setsx, outsx, wsx
+
+            # and its backward: bf16 q, k, v, dout (another input set) -> bf16 gradients
+            gx = [torch.empty((B, N, Hx, Dx), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+            wsb = torch.empty(sana.sana_linattn_bwd_workspace_bytes(B, Hx, N, Dx, 0), dtype=torch.uint8, device=dev)
+
+            def hdx_bwd(i):
+                q, k, v = setsx[i % NSETS]
+                sana.sana_linattn_bwd(q, k, v, setsx[(i + 1) % NSETS][0], *gx, wsb, eps=w.eps, stream=stream)
+            ms = timed(hdx_bwd, args.steps)
+            bxb = w.token_heads * D * 2 * 7
+            extra[f"backward_d{Dx}_h{Hx}_bf16"] = {
+                "ms_per_step": round(ms, 5), "GBps": round(bxb / ms / 1e6, 1),
+                "pct_hbm_peak": round(100 * bxb / ms / 1e6 / HBM_PEAK_GBPS, 2),
+                "note": f"sana_linattn_bwd at head dim {Dx} (H={Hx}), bf16; algorithmic bytes = 7 tensors"}
+            del setsx, outsx, wsx, gx, wsb
 
         # backward (dq, dk, dv) of the same forward: bf16 q, k, v, dout -> bf16 gradients
         grads = [[torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev) for _ in range(3)]

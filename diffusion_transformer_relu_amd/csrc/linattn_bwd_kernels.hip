@@ -460,10 +460,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 
 // 16-bit kernel, but each wave reads its own 32 keys straight from global
 // memory in the operand layout (the next sub-tile's loads issued before this
 // one's work), and k, a = ReLU(k) and v enter the MFMAs as three bf16 terms.
-template <typename OutT>
+// Head dim 16 as in the 16-bit kernel (groups of two heads, block-diagonal
+// Ghat; a lone head's other half is neither read nor stored).
+template <typename OutT, int HD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_bwd_key_mfma_f32(
     const float* __restrict__ k, const float* __restrict__ v, const float* __restrict__ ghat,
-    OutT* __restrict__ dk, OutT* __restrict__ dv, int N, int H, int HP, int L, int NB, int tile, int tpb) {
+    OutT* __restrict__ dk, OutT* __restrict__ dv, int N, int H, int HP, int HR, int L, int NB, int tile, int tpb) {
+    static_assert(HD == kD || HD == kD / 2, "head dims 32 and 16");
+    constexpr bool D16 = HD == kD / 2;
+    constexpr int SW = HD + 1, SF = HD * SW;
     __shared__ __attribute__((aligned(16))) float otile[4][32 * kPitch];                // fp32 out
     __shared__ __attribute__((aligned(16))) uint16_t ctile[2][2][32 * kPairRow];        // 16-bit out: [half][dv, dk]
 
@@ -477,32 +482,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     const int blk0 = beta * L, blk1 = min(blk0 + L, N);
     const int t0 = blk0 + tib * tile, t1 = min(t0 + tile, blk1);
     const int g = lane >> 5, i = lane & 31;
-    const int nh = min(2, H - 2 * hp);
     if (t0 >= t1) return;   // uniform over the work-group
 
-    const int hs = min(h, H - 1);   // a missing second head computes on the first (never stored)
-    const float* G = ghat + (((size_t)b * H + hs) * NB + beta) * kStateFloats;
+    const int hs = min(h, H - 1);   // a missing second group computes on the first (never stored)
+    auto head_G = [&](int hr) { return ghat + (((size_t)b * HR + hr) * NB + beta) * SF; };
     u32x4 gt[2][3], gn[2][3];
-    state_operands(G, lane, true, gt);
-    state_operands(G, lane, false, gn);
-    float gz[16];
+    key_operands<HD>(head_G, hs, 0, HR, lane, true, gt);
+    key_operands<HD>(head_G, hs, 0, HR, lane, false, gn);
+    float gz[16];   // Ghat[row][HD] at this lane's accumulator rows
 #pragma unroll
-    for (int r = 0; r < 16; ++r) gz[r] = G[(8 * (r >> 2) + 4 * g + (r & 3)) * kW + kD];
+    for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * g + (r & 3);
+        if constexpr (D16) {
+            const int hr = 2 * hs + (row >> 4);
+            gz[r] = hr < HR ? head_G(hr)[(row & 15) * SW + HD] : 0.f;
+        } else {
+            gz[r] = head_G(hs)[row * SW + HD];
+        }
+    }
 
-    const long long hstride = (long long)H * kD;
+    const long long hstride = (long long)HR * HD;
+    const bool upper = HR * HD - hs * kD > kD / 2;                 // the group's second half exists
+    const int ncols = min(32, HR * HD - h * kD);                   // fp32 out: columns of this group that exist
+    const int nchunk = min(8, (HR * HD - 2 * hp * kD) / 8);        // 16-bit out: 16-byte chunks of the line
     auto row_of = [&](const float* x, int tt) { return x + ((long long)b * N + min(tt + i, t1 - 1)) * hstride + hs * kD; };
     float* ot = otile[wave];
     F32Operand kc, vc;
-    kc.load(row_of(k, t0 + 32 * th), g);
-    vc.load(row_of(v, t0 + 32 * th), g);
+    kc.load(row_of(k, t0 + 32 * th), g, upper);
+    vc.load(row_of(v, t0 + 32 * th), g, upper);
     for (int tt0 = t0; tt0 < t1; tt0 += kTileTok) {
         const int tt = tt0 + 32 * th;   // first key of this wave's half
         const int n = min(32, t1 - tt);
         F32Operand kn, vn;
         const bool more = tt0 + kTileTok < t1;
         if (more) {   // in flight during this sub-tile's work
-            kn.load(row_of(k, tt + kTileTok), g);
-            vn.load(row_of(v, tt + kTileTok), g);
+            kn.load(row_of(k, tt + kTileTok), g, upper);
+            vn.load(row_of(v, tt + kTileTok), g, upper);
         }
         // (rows past the range hold the clamped last row: with 16-bit outputs
         // every wave computes, so that the work-group barrier below is reached
@@ -517,8 +532,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
             for (int r = 0; r < 16; ++r)
                 acck[r] = ((mask >> (8 * (r >> 2) + 4 * g + (r & 3))) & 1u) ? acck[r] + gz[r] : 0.f;
             if constexpr (sizeof(OutT) == 4) {
-                store_tile<OutT>(ot, accv, lane, n, [&](int t) { return dv + ((long long)b * N + tt + t) * hstride + h * kD; });
-                store_tile<OutT>(ot, acck, lane, n, [&](int t) { return dk + ((long long)b * N + tt + t) * hstride + h * kD; });
+                store_tile<OutT>(ot, accv, lane, n,
+                                 [&](int t) { return dv + ((long long)b * N + tt + t) * hstride + h * kD; }, ncols);
+                store_tile<OutT>(ot, acck, lane, n,
+                                 [&](int t) { return dk + ((long long)b * N + tt + t) * hstride + h * kD; }, ncols);
             } else {
                 __syncthreads();   // the previous sub-tile's pair tiles have been stored
                 put_pair_tile<OutT>(ctile[th][0], accv, lane, hh);
@@ -529,8 +546,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
                         return reinterpret_cast<uint16_t*>(base + ((long long)b * N + min(tt + r, t1 - 1)) * hstride + 2 * hp * kD);
                     };
                 };
-                store_pair_rows<OutT>(ctile[th][0], lane, 16 * hh, 4 * nh, row(dv));
-                store_pair_rows<OutT>(ctile[th][1], lane, 16 * hh, 4 * nh, row(dk));
+                store_pair_rows<OutT>(ctile[th][0], lane, 16 * hh, nchunk, row(dv));
+                store_pair_rows<OutT>(ctile[th][1], lane, 16 * hh, nchunk, row(dk));
             }
         }
         if (more) {
@@ -620,7 +637,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     OutT* __restrict__ dq, float* __restrict__ gpart, int N, int H, int HP, int HR, int L, int NB, int tile, int tpb,
     float eps) {
     constexpr bool D16 = HD == kD / 2;
-    static_assert(HD == kD || (D16 && sizeof(QT) == 2), "head dim 16 takes 16-bit q");
+    static_assert(HD == kD || D16, "head dims 32 and 16");
     constexpr int SW = HD + 1, SF = HD * SW;
     // 16-bit q (and 16-bit dout) are staged through LDS by the work-group;
     // fp32 q is read by each wave straight from global memory, its f = ReLU(q)
@@ -832,14 +849,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     if constexpr (!kStage) {
         // fp32 q: each wave reads its sub-tiles' rows itself, the next
         // sub-tile's loads in flight during this one's work
+        // (a group that is a lone head of dim 16 reads only its first 16 features)
         auto load = [&](int tt, Tile& x) {
             const long long row = ((long long)b * N + min(tt + i, t1 - 1)) * hstride + h * kD;
-            x.qa.load(reinterpret_cast<const float*>(q) + row, g);
+            x.qa.load(reinterpret_cast<const float*>(q) + row, g, ncols / 8);
             if constexpr (kDoutOperand) {
                 x.g0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dout + row + 8 * g));
-                x.g1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dout + row + 16 + 8 * g));
+                x.g1 = ncols > 16 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dout + row + 16 + 8 * g))
+                                  : (u32x4){0u, 0u, 0u, 0u};
             }
-            x.gr.load(dout + row, g);
+            x.gr.load(dout + row, g, ncols / 8);
         };
         if (active && t0 + 32 * (wave >> 1) < t1) {
             Tile cur;
@@ -1143,7 +1162,7 @@ hipError_t launch_bwd_query(const BwdPlan& bp, const void* q, const void* dout, 
                             return;
                         }
                     }
-                    if constexpr (sizeof(QT) == 2) {
+                    {
                         if (pl.D == kD / 2) {
                             hipLaunchKernelGGL((k_bwd_query_mfma<QT, GT, OT, kD / 2>), dim3(grid), dim3(kThreads), 0,
                                                stream, static_cast<const QT*>(q), static_cast<const GT*>(dout), state,
@@ -1198,10 +1217,10 @@ hipError_t launch_bwd_key(const BwdPlan& bp, const void* k, const void* v, const
         by_dtype(bp.grad_dtype, [&](auto ot) {
             using OT = typename decltype(ot)::type;
             if (pl.in_dtype == 0)
-                hipLaunchKernelGGL((k_bwd_key_mfma_f32<OT>), dim3(grid), dim3(kThreads), 0, stream,
-                                   static_cast<const float*>(k), static_cast<const float*>(v), ghat,
-                                   static_cast<OT*>(dk), static_cast<OT*>(dv), pl.N, pl.H, pl.HP, pl.L, pl.NB, bp.tk,
-                                   bp.tpbk);
+                hipLaunchKernelGGL((pl.D == kD / 2 ? k_bwd_key_mfma_f32<OT, kD / 2> : k_bwd_key_mfma_f32<OT, kD>),
+                                   dim3(grid), dim3(kThreads), 0, stream, static_cast<const float*>(k),
+                                   static_cast<const float*>(v), ghat, static_cast<OT*>(dk), static_cast<OT*>(dv),
+                                   pl.N, groups32(pl), pl.HP, pl.H, pl.L, pl.NB, bp.tk, bp.tpbk);
             else
                 by_head_dim(pl.D, [&](auto dd) {
                     constexpr int DD = decltype(dd)::value;

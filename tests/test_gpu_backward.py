@@ -98,14 +98,14 @@ def test_backward_edge_shapes(B, N, H, L, dt):
 
 
 HEAD_DIMS = [(2, 1000, 5, 100, 1, 64), (1, 777, 7, 0, 2, 16), (2, 33, 1, 0, 0, 16), (1, 300, 3, 1, 0, 64),
-             (1, 513, 3, 64, 2, 64), (1, 16384, 35, 0, 1, 64), (1, 16384, 140, 0, 1, 16)]
+             (1, 513, 3, 64, 2, 64), (1, 777, 5, 100, 0, 16), (1, 16384, 35, 0, 1, 64), (1, 16384, 140, 0, 1, 16)]
 
 
 @pytest.mark.parametrize("B,N,H,L,dt,D", HEAD_DIMS, ids=[f"B{b}N{n}H{h}L{l}dt{t}D{d}" for b, n, h, l, t, d in HEAD_DIMS])
 def test_backward_other_head_dims(B, N, H, L, dt, D):
-    """Head dims 16 and 64 (matrix-core passes for 16-bit inputs, vector-unit
-    ones for fp32): ragged N, odd and single heads, block lengths 1, 64 and
-    100, the headline's token-head-feature count."""
+    """Head dims 16 and 64 (matrix-core passes; vector-unit ones for fp32
+    inputs of dim 64): ragged N, odd and single heads, block lengths 1, 64
+    and 100, the headline's token-head-feature count."""
     w = workloads.Workload(f"bwd_B{B}N{N}H{H}L{L}dt{dt}D{D}", B, N, H, D, dt, seed=150 + N % 19 + D, block_len=L)
     (q, k, v, g), want = case(w, dt)
     check(run(q, k, v, g, L, w.eps, DT[dt]), want, DT[dt], w.name)

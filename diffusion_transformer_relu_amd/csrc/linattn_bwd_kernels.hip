@@ -300,46 +300,6 @@ __device__ __forceinline__ void tile_operand(const uint8_t* lds, int ts, int hh,
 }
 
 // ------------------------------------------------------------------ key pass, matrix cores
-// Split-term operands (three bf16 terms, round to nearest) of one 32-row block
-// of a head-dim HD gradient state for the key pass, K-steps of 16: lane (g, i)
-// gets A[i][16 ks + 8 g + e] in out[ks][sp] (element e), with
-//   natural:    A[i][kk] = Ghat[row(i)][kk]    (dk^T = Ghat_v v^T)
-//   transposed: A[i][kk] = Ghat[kk][col(i)]    (dv^T = Ghat_v^T a^T)
-// head(r) points at head r's HD x (HD + 1) state.  HD = 32: head grp, row(i) =
-// col(i) = i.  HD = 64: head grp, row(i) = col(i) = 32 half + i, kk over all
-// 64 features (four K-steps).  HD = 16: block-diagonal over heads 2 grp
-// (K-step 0) and 2 grp + 1 (K-step 1, zero when there is none), nonzero in
-// rows 16 ks .. 16 ks + 15 of K-step ks only.
-template <int HD, typename HeadState>
-__device__ __forceinline__ void key_operands(HeadState head, int grp, int half, int HR, int lane, bool transposed,
-                                             u32x4 (&out)[KSteps<HD>::value][3]) {
-    constexpr int KS = KSteps<HD>::value, SW = HD + 1;
-    const int g = lane >> 5, i = lane & 31;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        float x[8];
-        if constexpr (HD == kD / 2) {
-            const int hr = 2 * grp + ks;
-            const bool on = hr < HR && (i >> 4) == ks;
-            const float* G = head(min(hr, HR - 1));
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int kk = 8 * g + e, r = i & 15;
-                x[e] = on ? (transposed ? G[kk * SW + r] : G[r * SW + kk]) : 0.f;
-            }
-        } else {
-            const float* G = head(grp);
-            const int ri = (HD == 2 * kD ? kD * half : 0) + i;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int kk = 16 * ks + 8 * g + e;
-                x[e] = transposed ? G[kk * SW + ri] : G[ri * SW + kk];
-            }
-        }
-        split3_f32x8(x, out[ks]);
-    }
-}
-
 // grid.x = (b * HP + hp) * (NB * tpb) + beta * tpb + tile.  The work-group
 // stages 64-key tiles of k and v (both heads) through LDS; wave w then handles
 // head 2*hp + (w & 1) and keys 32 (w >> 1) .. + 31 of the tile.  With
@@ -351,7 +311,7 @@ __device__ __forceinline__ void key_operands(HeadState head, int grp, int half, 
 // them, HP pairs; HR real heads): HD = 64, wave w computes the rows of group
 // w & 1 of its head against all 64 features (four K-steps, the B operand from
 // both groups' staged rows); HD = 16, the group's two heads as one
-// block-diagonal state (key_operands).
+// block-diagonal state (state_operands).
 template <bool F16, typename OutT, int HD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 2 * kD ? 2 : 3, 8))) void k_bwd_key_mfma(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ ghat,
@@ -379,8 +339,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 
     auto head_G = [&](int hr) { return ghat + (((size_t)b * HR + hr) * NB + beta) * SF; };
     const int grp = D64 ? hp : hs;
     u32x4 gt[KS][3], gn[KS][3];
-    key_operands<HD>(head_G, grp, hh, HR, lane, true, gt);
-    key_operands<HD>(head_G, grp, hh, HR, lane, false, gn);
+    state_operands<HD>(head_G, grp, hh, HR, lane, true, gt);
+    state_operands<HD>(head_G, grp, hh, HR, lane, false, gn);
     float gz[16];   // Ghat[row][HD] at this lane's accumulator rows 8 (r / 4) + 4 g + r % 4
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -487,8 +447,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     const int hs = min(h, H - 1);   // a missing second group computes on the first (never stored)
     auto head_G = [&](int hr) { return ghat + (((size_t)b * HR + hr) * NB + beta) * SF; };
     u32x4 gt[2][3], gn[2][3];
-    key_operands<HD>(head_G, hs, 0, HR, lane, true, gt);
-    key_operands<HD>(head_G, hs, 0, HR, lane, false, gn);
+    state_operands<HD>(head_G, hs, 0, HR, lane, true, gt);
+    state_operands<HD>(head_G, hs, 0, HR, lane, false, gn);
     float gz[16];   // Ghat[row][HD] at this lane's accumulator rows
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -628,7 +588,7 @@ template <> struct GradRow<_Float16> {
 //
 // Head dim 16 (HD = 16, 16-bit q): a 32-feature group holds two heads (H
 // counts the groups, HR the heads).  P is the group's block-diagonal state
-// (key_operands), so m = P_v dout keeps the heads apart; every per-token
+// (state_operands), so m = P_v dout keeps the heads apart; every per-token
 // scalar (r, w) exists per head (rows 0..15 the first, 16..31 the second),
 // and of the group's G only the diagonal 16 x 16 blocks are written.
 template <typename QT, typename GT, typename OutT, int HD>
@@ -664,7 +624,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     auto head_P = [&](int hr) { return state + (((size_t)b * HR + hr) * NB + beta) * SF; };
     if (wave < 2 && h < H) {
         u32x4 t[2][3];
-        key_operands<HD>(head_P, h, 0, HR, lane, false, t);
+        state_operands<HD>(head_P, h, 0, HR, lane, false, t);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -740,7 +700,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
 #pragma unroll
                 for (int sp = 0; sp < 3; ++sp) A[ks][sp] = opnd.v[hh][ks][sp][lane];
             if constexpr (kDoutOperand) {
-                acc = mma_split<std::is_same<GT, _Float16>::value>(A, x.g0, x.g1, acc);
+                const u32x4 gb[2] = {x.g0, x.g1};
+                acc = mma_split_ks<std::is_same<GT, _Float16>::value, 2>(A, gb, acc);
                 rs[0] = rh[0];
                 rs[1] = rh[1];
             } else {
@@ -984,7 +945,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     const float* P = state + (((size_t)b * HR + hq) * NB + beta) * SF;
     if (wave < 2) {
         u32x4 t[KS][3];
-        key_operands<HD>([&](int) { return P; }, hq, a, HR, lane, false, t);
+        state_operands<HD>([&](int) { return P; }, hq, a, HR, lane, false, t);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll

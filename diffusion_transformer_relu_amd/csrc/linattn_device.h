@@ -166,88 +166,80 @@ __device__ __forceinline__ ChunkRange chunk_range(int p, int cpb, int chunk, int
 // ------------------------------------------------------------------ matrix-core helpers
 constexpr int kPitch = 36;   // floats per LDS tile row: 32 + 4 keeps rows 16-byte aligned, no bank conflicts
 
-// MFMA operands of a D x (D+1) fp32 state S (row-major, kW floats per row),
-// each as three bf16 split terms, for lane (g, i) of a wave:
-//   transposed: A[row i][k = 16 ks + 8 g + e] = S[16 ks + 8 g + e][i]
-//   natural:    A[row i][k = 16 ks + 8 g + e] = S[i][16 ks + 8 g + e]
-__device__ __forceinline__ void state_operands(const float* S, int lane, bool transposed, u32x4 out[2][3]) {
-    const int g = lane >> 5, i = lane & 31;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int kk = 16 * ks + 8 * g + e;
-            x[e] = transposed ? S[kk * kW + i] : S[i * kW + kk];
-        }
-        split3_f32x8(x, out[ks]);
-    }
-}
-
 // K-steps of 16 features in a 32-column block's product for head dim HD
 // (the kernels see a token row as 32-feature groups: a head of 64 is two, a
 // group holds two heads of 16).
 template <int HD> struct KSteps { static constexpr int value = HD == 2 * kD ? 4 : 2; };
 
-// A operands of out^T = S^T f^T for one 32-column block of head-dim HD states,
-// as three bf16 terms (each the round-to-nearest bf16 of what the previous
-// ones left, remainders exact), and the normaliser entries at this lane's
-// features: lane (g, i) gets S[16 ks + 8 g + e][c(i)] in sa[ks][sp] (element
-// e) and S[16 ks + 8 g + e][HD] in z[8 ks + e].  head(r) points at head r's
-// HD x (HD + 1) state.
-//   HD = 32: head grp, c(i) = i.
-//   HD = 64: head grp, c(i) = 32 half + i (four K-steps).
-//   HD = 16: heads 2 grp (K-step 0) and 2 grp + 1 (K-step 1; zero when
-//            there is none, grp's row then being a lone head) as one
-//            block-diagonal matrix: K-step ks is nonzero in columns 16 ks ..
-//            16 ks + 15 only.
+// Split-term operands (three bf16 terms, each the round-to-nearest bf16 of
+// what the previous ones left, remainders exact) of one 32-row block of a
+// head-dim HD state S for the matrix cores, K-steps of 16: lane (g, i) gets
+// A[i][16 ks + 8 g + e] in out[ks][sp] (element e), with
+//   natural:    A[i][kk] = S[row(i)][kk]
+//   transposed: A[i][kk] = S[kk][row(i)]
+// head(r) points at head r's HD x (HD + 1) state.
+//   HD = 32: head grp, row(i) = i.
+//   HD = 64: head grp, row(i) = 32 half + i, kk over all 64 features (four
+//            K-steps).
+//   HD = 16: heads 2 grp (K-step 0) and 2 grp + 1 (K-step 1; zero when there
+//            is none, grp's row then being a lone head) as one block-diagonal
+//            matrix: K-step ks is nonzero in rows 16 ks .. 16 ks + 15 only.
+template <int HD, typename HeadState>
+__device__ __forceinline__ void state_operands(HeadState head, int grp, int half, int HR, int lane, bool transposed,
+                                               u32x4 (&out)[KSteps<HD>::value][3]) {
+    constexpr int KS = KSteps<HD>::value, SW = HD + 1;
+    const int g = lane >> 5, i = lane & 31;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        float x[8];
+        if constexpr (HD == kD / 2) {
+            const int hr = 2 * grp + ks;
+            const bool on = hr < HR && (i >> 4) == ks;
+            const float* S = head(min(hr, HR - 1));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int kk = 8 * g + e, r = i & 15;
+                x[e] = on ? (transposed ? S[kk * SW + r] : S[r * SW + kk]) : 0.f;
+            }
+        } else {
+            const float* S = head(grp);
+            const int ri = (HD == 2 * kD ? kD * half : 0) + i;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int kk = 16 * ks + 8 * g + e;
+                x[e] = transposed ? S[kk * SW + ri] : S[ri * SW + kk];
+            }
+        }
+        split3_f32x8(x, out[ks]);
+    }
+}
+
+// The apply kernels' operands of out^T = S^T f^T (state_operands, transposed)
+// and the normaliser entries at this lane's features: z[8 ks + e] =
+// S[16 ks + 8 g + e][HD] (HD = 16: of head 2 grp + ks, zero when there is none).
 template <int HD, typename HeadState>
 __device__ __forceinline__ void apply_operands(HeadState head, int grp, int half, int HR, int lane,
                                                u32x4 (&sa)[KSteps<HD>::value][3],
                                                float (&z)[8 * KSteps<HD>::value]) {
     constexpr int KS = KSteps<HD>::value, SW = HD + 1;
-    const int g = lane >> 5, i = lane & 31;
+    const int g = lane >> 5;
+    state_operands<HD>(head, grp, half, HR, lane, true, sa);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const float* S;
-        bool on = true, zon = true;
-        int row0, col;
-        if constexpr (HD == kD / 2) {
-            const int hr = 2 * grp + ks;
-            zon = hr < HR;
-            on = zon && (i >> 4) == ks;
-            S = head(min(hr, HR - 1));
-            row0 = 0;
-            col = i & 15;
-        } else {
-            S = head(grp);
-            row0 = 16 * ks;
-            col = (HD == 2 * kD ? kD * half : 0) + i;
-        }
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            uint32_t w[3] = {0u, 0u, 0u};
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int row = row0 + 8 * g + 2 * d + hf;
-                float r = on ? S[row * SW + col] : 0.f;
-                z[8 * ks + 2 * d + hf] = zon ? S[row * SW + HD] : 0.f;
-#pragma unroll
-                for (int sp = 0; sp < 3; ++sp) {   // S = hi + mid + lo, each remainder exact
-                    const uint16_t t = f32_to_bf16(r);
-                    r -= bf16_to_f32(t);
-                    w[sp] |= (uint32_t)t << (16 * hf);
-                }
+        for (int e = 0; e < 8; ++e) {
+            if constexpr (HD == kD / 2) {
+                const int hr = 2 * grp + ks;
+                z[8 * ks + e] = hr < HR ? head(hr)[(8 * g + e) * SW + HD] : 0.f;
+            } else {
+                z[8 * ks + e] = head(grp)[(16 * ks + 8 * g + e) * SW + HD];
             }
-#pragma unroll
-            for (int sp = 0; sp < 3; ++sp) sa[ks][sp][d] = w[sp];
         }
-    }
 }
 
 // acc += A B over KS K-steps, B a 16-bit operand per K-step (bf16 exact;
 // fp16 split exactly into two bf16 terms), A three split terms; small terms
-// first.  For KS = 2 this is mma_split below.
+// first.
 template <bool F16, int KS>
 __device__ __forceinline__ f32x16 mma_split_ks(const u32x4 (&A)[KS][3], const u32x4 (&b)[KS], f32x16 acc) {
     if constexpr (F16) {
@@ -272,39 +264,6 @@ __device__ __forceinline__ f32x16 mma_split_ks(const u32x4 (&A)[KS][3], const u3
         for (int sp = 2; sp >= 0; --sp)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16(A[ks][sp], b[ks], acc);
-    }
-    return acc;
-}
-
-// acc += sum over the 32 features of A (three split terms) times the B operand
-// b0 (features 8g..8g+7 of this lane's token) and b1 (features 16+8g..): bf16
-// bits, or fp16 bits split exactly into two bf16 terms.  Small terms first.
-template <bool F16>
-__device__ __forceinline__ f32x16 mma_split(const u32x4 A[2][3], u32x4 b0, u32x4 b1, f32x16 acc) {
-    if constexpr (F16) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const u32x4 x = ks ? b1 : b0;
-            u32x4 hi, lo;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                uint32_t h, l;
-                float f0, f1;
-                split_f16x2(x[d], h, l, f0, f1);
-                hi[d] = h;
-                lo[d] = l;
-            }
-#pragma unroll
-            for (int sp = 2; sp >= 0; --sp) acc = mfma_bf16(A[ks][sp], lo, acc);
-#pragma unroll
-            for (int sp = 2; sp >= 0; --sp) acc = mfma_bf16(A[ks][sp], hi, acc);
-        }
-    } else {
-#pragma unroll
-        for (int sp = 2; sp >= 0; --sp) {
-            acc = mfma_bf16(A[0][sp], b0, acc);
-            acc = mfma_bf16(A[1][sp], b1, acc);
-        }
     }
     return acc;
 }

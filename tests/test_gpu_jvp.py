@@ -114,10 +114,13 @@ def test_jvp_other_head_dims(B, N, H, L, dt, D):
         check_tangent(got_t, want_t, out_t, w.name)
 
 
-def test_jvp_primal_is_the_forward_and_repeatable():
-    """The primal output equals sana_linattn_fwd's bit for bit, and two calls agree bit for bit."""
+@pytest.mark.parametrize("D,H", [(32, 6), (16, 7)], ids=["D32", "D16"])
+def test_jvp_primal_is_the_forward_and_repeatable(D, H):
+    """The primal output equals sana_linattn_fwd's bit for bit (16-bit inputs:
+    the state kernels sum the tokens in the same order), and two calls agree
+    bit for bit."""
     import diffusion_transformer_relu_amd as sana
-    w = workloads.Workload("jvp_prim", 2, 2048, 6, 32, workloads.DT_BF16, seed=110, block_len=512)
+    w = workloads.Workload("jvp_prim", 2, 2048, H, D, workloads.DT_BF16, seed=110, block_len=512)
     x = [to_device(a) for a in workloads.make_inputs(w) + workloads.make_tangents(w)]
     o1, t1 = sana.linattn_jvp(*x, block_len=512)
     o2, t2 = sana.linattn_jvp(*x, block_len=512)

@@ -517,6 +517,91 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     }
 }
 
+// The key pass for fp32 k and v at head dim 64: the 16-bit dim-64 kernel's
+// work-groups and waves (wave w: the rows of group w & 1 of the head, keys
+// 32 (w >> 1) .. of each 64-key step), each wave reading both groups' k and v
+// rows straight from global memory in the operand layout (no loads ahead: the
+// four K-steps' operands of both layouts take the registers), k, a = ReLU(k)
+// and v split into three bf16 terms.
+template <typename OutT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_bwd_key_mfma_f32_64(
+    const float* __restrict__ k, const float* __restrict__ v, const float* __restrict__ ghat,
+    OutT* __restrict__ dk, OutT* __restrict__ dv, int N, int HR, int L, int NB, int tile, int tpb) {
+    constexpr int HD = 2 * kD, KS = KSteps<HD>::value, SW = HD + 1, SF = HD * SW;
+    __shared__ __attribute__((aligned(16))) float otile[4][32 * kPitch];                // fp32 out
+    __shared__ __attribute__((aligned(16))) uint16_t ctile[2][2][32 * kPairRow];        // 16-bit out: [half][dv, dk]
+
+    const int per_unit = NB * tpb;
+    const int tau = blockIdx.x % per_unit;
+    const int bh = blockIdx.x / per_unit;
+    const int hq = bh % HR, b = bh / HR;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int a = wave & 1, th = wave >> 1;
+    const int beta = tau / tpb, tib = tau - beta * tpb;
+    const int blk0 = beta * L, blk1 = min(blk0 + L, N);
+    const int t0 = blk0 + tib * tile, t1 = min(t0 + tile, blk1);
+    const int g = lane >> 5, i = lane & 31;
+    if (t0 >= t1) return;   // uniform over the work-group
+
+    const float* G = ghat + (((size_t)b * HR + hq) * NB + beta) * SF;
+    auto head_G = [&](int) { return G; };
+    u32x4 gt[KS][3], gn[KS][3];
+    state_operands<HD>(head_G, hq, a, HR, lane, true, gt);
+    state_operands<HD>(head_G, hq, a, HR, lane, false, gn);
+    float gz[16];   // Ghat[32 a + row][64] at this lane's accumulator rows
+#pragma unroll
+    for (int r = 0; r < 16; ++r) gz[r] = G[(kD * a + 8 * (r >> 2) + 4 * g + (r & 3)) * SW + HD];
+
+    const long long hstride = (long long)HR * HD;
+    auto row_of = [&](const float* x, int tt) { return x + ((long long)b * N + min(tt + i, t1 - 1)) * hstride + hq * HD; };
+    float* ot = otile[wave];
+    for (int tt0 = t0; tt0 < t1; tt0 += kTileTok) {
+        const int tt = tt0 + 32 * th;   // first key of this wave's half
+        const int n = min(32, t1 - tt);
+        // (rows past the range hold the clamped last row: with 16-bit outputs
+        // every wave computes, so that the work-group barriers are reached by all)
+        if (sizeof(OutT) == 2 || n > 0) {
+            F32Operand kx[2], vx[2];   // features 0..31 and 32..63 of the key
+#pragma unroll
+            for (int gi = 0; gi < 2; ++gi) {
+                kx[gi].load(row_of(k, tt) + kD * gi, g);
+                vx[gi].load(row_of(v, tt) + kD * gi, g);
+            }
+            const uint32_t m0 = kx[0].positive(g), m1 = kx[1].positive(g);
+            const uint32_t mask = a ? m1 : m0;   // bit j: feature 32 a + j of the key > 0
+            f32x16 accv = {}, acck = {};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4 t[3];
+                split_half(kx[ks >> 1], ks & 1, true, t);
+                accv = mma_terms(gt[ks], t, accv);
+                split_half(vx[ks >> 1], ks & 1, false, t);
+                acck = mma_terms(gn[ks], t, acck);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acck[r] = ((mask >> (8 * (r >> 2) + 4 * g + (r & 3))) & 1u) ? acck[r] + gz[r] : 0.f;
+            const int col = (2 * hq + a) * kD;
+            if constexpr (sizeof(OutT) == 4) {
+                store_tile<OutT>(ot, accv, lane, n, [&](int t) { return dv + ((long long)b * N + tt + t) * hstride + col; });
+                store_tile<OutT>(ot, acck, lane, n, [&](int t) { return dk + ((long long)b * N + tt + t) * hstride + col; });
+            } else {
+                __syncthreads();   // the previous step's pair tiles have been stored
+                put_pair_tile<OutT>(ctile[th][0], accv, lane, a);
+                put_pair_tile<OutT>(ctile[th][1], acck, lane, a);
+                __syncthreads();
+                auto row = [&](OutT* base) {
+                    return [=](int r) {
+                        return reinterpret_cast<uint16_t*>(base + ((long long)b * N + min(tt + r, t1 - 1)) * hstride + hq * HD);
+                    };
+                };
+                store_pair_rows<OutT>(ctile[th][0], lane, 16 * a, 8, row(dv));
+                store_pair_rows<OutT>(ctile[th][1], lane, 16 * a, 8, row(dk));
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ query pass, matrix cores
 // Upstream gradient of one token in the accumulator layout: lane (g, i) gets
 // features 8 rr + 4 g .. + 3 (rr = 0..3) of its token.
@@ -1177,7 +1262,12 @@ hipError_t launch_bwd_key(const BwdPlan& bp, const void* k, const void* v, const
         const uint16_t* v16 = static_cast<const uint16_t*>(v);
         by_dtype(bp.grad_dtype, [&](auto ot) {
             using OT = typename decltype(ot)::type;
-            if (pl.in_dtype == 0)
+            if (pl.in_dtype == 0 && pl.D == 2 * kD)
+                hipLaunchKernelGGL((k_bwd_key_mfma_f32_64<OT>), dim3(grid), dim3(kThreads), 0, stream,
+                                   static_cast<const float*>(k), static_cast<const float*>(v), ghat,
+                                   static_cast<OT*>(dk), static_cast<OT*>(dv), pl.N, pl.H, pl.L, pl.NB, bp.tk,
+                                   bp.tpbk);
+            else if (pl.in_dtype == 0)
                 hipLaunchKernelGGL((pl.D == kD / 2 ? k_bwd_key_mfma_f32<OT, kD / 2> : k_bwd_key_mfma_f32<OT, kD>),
                                    dim3(grid), dim3(kThreads), 0, stream, static_cast<const float*>(k),
                                    static_cast<const float*>(v), ghat, static_cast<OT*>(dk), static_cast<OT*>(dv),

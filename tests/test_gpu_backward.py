@@ -110,7 +110,8 @@ def test_backward_other_head_dims(B, N, H, L, dt, D):
     (q, k, v, g), want = case(w, dt)
     check(run(q, k, v, g, L, w.eps, DT[dt]), want, DT[dt], w.name)
     if N < 16384:
-        check(run(q, k, v, g, L, w.eps, torch.float32), want, torch.float32, w.name + "/f32grad")
+        other = torch.bfloat16 if dt == workloads.DT_F32 else torch.float32
+        check(run(q, k, v, g, L, w.eps, other), want, other, w.name + "/" + str(other))
 
 
 def test_backward_single_token_is_identity_in_v():

@@ -222,12 +222,9 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
     bp->grad_dtype = grad_dtype;
     if (B == 0 || H == 0 || N == 0) return SANA_OK;
     const Plan& pl = bp->fw;
-    // the matrix-core key kernels are built for every head dim and input
-    // type, the query kernels for D = 32 and 16 with every input type and for
-    // D = 64 with 16-bit q and dout; the rest takes the vector query kernel
-    // (the forward's state is rebuilt on the matrix cores either way)
-    const bool in16 = in_dtype != SANA_DT_F32;
-    bp->query_mfma = pl.mfma && (D != 2 * sana::kD || (in16 && dout_dtype != SANA_DT_F32));
+    // the matrix-core query and key kernels take every head dim and input
+    // type (the vector kernels only with SANA_LINATTN_PATH=valu)
+    bp->query_mfma = pl.mfma;
     bp->key_mfma = pl.mfma;
     bp->tk = bp->tq = kBwdTile;
     if (bp->query_mfma || bp->key_mfma) {

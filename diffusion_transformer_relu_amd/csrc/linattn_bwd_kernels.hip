@@ -983,37 +983,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
 static_assert(sizeof(OperandLds) >= (2 * 16 * 64 + 2 * 32) * sizeof(float), "G reduction area exceeds the operand space");
 
 // ------------------------------------------------------------------ query pass, matrix cores, head dim 64
-// 16-bit q and dout.  grid.x = (b * HR + hq) * (NB * tpb) + beta * tpb + tile:
-// one head hq (its two 32-feature groups staged as the pair of the dim-32
-// kernel); wave w works on group a = w & 1 (features 32 a .. 32 a + 31) and
-// every other 32-query sub-tile (w >> 1), next to the wave of the other group
-// on the same queries.  Per sub-tile, as the dim-32 kernel with the 64 x 65
-// state P:
+// grid.x = (b * HR + hq) * (NB * tpb) + beta * tpb + tile: one head hq (its two
+// 32-feature groups as the pair of the dim-32 kernel); wave w works on group
+// a = w & 1 (features 32 a .. 32 a + 31) and every other 32-query sub-tile
+// (w >> 1), next to the wave of the other group on the same queries.  Per
+// sub-tile, as the dim-32 kernel with the 64 x 65 state P:
 //   den = f . z over both groups (each wave reads both groups' q), r
-//   m_a = P[32 a .., :64] dout (four K-steps, dout of both groups as B)
 //   u_a = dout_a r to the wave's LDS tile
+//   m_a = P[32 a .., :64] dout (four K-steps; a 16-bit dout of both groups is
+//   the B operand as it is, an fp32 one goes in as both waves' u split into
+//   three bf16 terms)
 //   dout . num = f_0 . m_0 + f_1 . m_1: the two waves exchange their halves
 //   through LDS (a work-group barrier), w = -r^2 (dout . num)
 //   dq_a = [q_a > 0] (r m_a + w z_a)
 //   G[32 a .., 32 b ..] += f_a^T u_b for b = 0, 1 (u_b from the wave of
 //   group b), G_z[32 a ..] += f_a^T w
-// A second barrier keeps each u tile until the other wave has read it.  Every
+// A last barrier keeps each u tile until the other wave has read it.  Every
 // wave takes every step (a sub-tile past the range computes on the clamped
-// last row and stores nothing), so the barriers are reached by all.
+// last row and stores nothing), so the barriers are reached by all.  16-bit q
+// (and 16-bit dout) are staged through LDS by the work-group; fp32 q is read
+// by each wave, its f kept in an fp32 LDS tile (in the staging area).
 template <typename QT, typename GT, typename OutT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_bwd_query_mfma64(
     const QT* __restrict__ q, const GT* __restrict__ dout, const float* __restrict__ state, OutT* __restrict__ dq,
     float* __restrict__ gpart, int N, int HR, int L, int NB, int tile, int tpb, float eps) {
     constexpr int HD = 2 * kD, KS = KSteps<HD>::value, SW = HD + 1, SF = HD * SW;
-    constexpr bool GF16 = std::is_same<GT, _Float16>::value;
-    static_assert(sizeof(QT) == 2 && sizeof(GT) == 2, "16-bit q and dout");
+    constexpr bool kStageQ = sizeof(QT) == 2, kDout16 = sizeof(GT) == 2;
+    constexpr bool GF16 = std::is_same<GT, _Float16>::value, QF16 = std::is_same<QT, _Float16>::value;
     __shared__ u32x4 opnd[2][KS][3][64];                              // P natural split terms, rows of group a
     __shared__ __attribute__((aligned(16))) float pzs[2][32];          // P[:, 64] at the rows of each group
     __shared__ __attribute__((aligned(16))) float ut[4][32 * kPitch];  // u tile, then the dq tile
     __shared__ __attribute__((aligned(16))) float wv[4][32];           // w of each token
     __shared__ __attribute__((aligned(16))) float gop[4][32];          // f_a . m_a of each token
-    __shared__ __attribute__((aligned(16))) uint8_t lds_in[2 * kTileTensor];   // staged q and dout
+    __shared__ __attribute__((aligned(16))) uint8_t lds_in[2 * kTileTensor];   // staged q (and 16-bit dout) / f tiles
     static_assert(sizeof(opnd) >= (2 * 2 * 16 * 64 + 2 * 32) * sizeof(float), "G reduction area exceeds the operand space");
+    static_assert(sizeof(lds_in) >= 4 * 32 * kPitch * sizeof(float), "f tiles exceed the staging area");
 
     const int per_unit = NB * tpb;
     const int tau = blockIdx.x % per_unit;
@@ -1041,32 +1045,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 
     const long long hstride = (long long)HR * HD;
     float* ot = ut[wave];
+    float* ft = reinterpret_cast<float*>(lds_in) + wave * 32 * kPitch;   // fp32 q: f tile of this wave
     f32x16 accG[2] = {};   // G[32 a .., 32 b ..] for b = 0, 1
     float gz_acc = 0.f;    // lane (g, j): sum over this lane's tokens of f_j w (feature 32 a + j)
-    constexpr bool QF16 = std::is_same<QT, _Float16>::value;
     auto decode = [&](uint16_t x) { return QF16 ? f16_to_f32(x) : bf16_to_f32(x); };
+    auto zrow = [&](int gi, int rr) { return *reinterpret_cast<const f32x4*>(&pzs[gi][8 * rr + 4 * g]); };
 
-    TileLoader ld = {{reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(dout)}, hstride, b, N,
-                     2 * hq, HR * HD, t1, {}};
-    ld.load(t0);
+    const uint16_t* dstage = kDout16 ? reinterpret_cast<const uint16_t*>(dout) : nullptr;
+    TileLoader ld = {{reinterpret_cast<const uint16_t*>(q), dstage}, hstride, b, N, 2 * hq, HR * HD, t1, {}};
+    if constexpr (kStageQ) ld.load(t0);
     for (int tt0 = t0; tt0 < t1; tt0 += kTileTok) {
-        __syncthreads();   // the previous tile has been consumed
-        ld.store(lds_in);
-        __syncthreads();
-        if (tt0 + kTileTok < t1) ld.load(tt0 + kTileTok);   // in flight during this tile's work
+        if constexpr (kStageQ) {
+            __syncthreads();   // the previous tile has been consumed
+            ld.store(lds_in);
+            __syncthreads();
+            if (tt0 + kTileTok < t1) ld.load(tt0 + kTileTok);   // in flight during this tile's work
+        }
         const int tt = tt0 + 32 * sub;
         const int n = min(32, t1 - tt);   // <= 0: a step past the range (computes, stores nothing)
         const int tok = 32 * sub + i;     // this lane's token in the tile
+        const long long grow = ((long long)b * N + min(tt + i, t1 - 1)) * hstride + hq * HD;   // its global row
 
         // q of both groups for the normaliser (the same order in both waves of
         // the pair), and of this wave's group (a separate read: an index by the
         // wave's group would put the rows in memory)
-        auto zrow = [&](int gi, int rr) { return *reinterpret_cast<const f32x4*>(&pzs[gi][8 * rr + 4 * g]); };
+        auto load_q = [&](GradRow<QT>& r, int gi) {
+            if constexpr (kStageQ)
+                r.load_lds(lds_in + gi * kTileHead + tok * kTileRow, g);
+            else
+                r.load(q + grow + kD * gi, g);
+        };
         float den = 0.f;
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {
             GradRow<QT> qg;
-            qg.load_lds(lds_in + gi * kTileHead + tok * kTileRow, g);
+            load_q(qg, gi);
             float dp = 0.f;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
@@ -1077,33 +1090,72 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
             den += dp + __shfl_xor(dp, 32);
         }
         GradRow<QT> qo;
-        qo.load_lds(lds_in + a * kTileHead + tok * kTileRow, g);
+        load_q(qo, a);
         auto fa = [&](int rr, int e) { return relu_f32(qo.at(rr, e)); };
         const float r = 1.0f / (den + eps);
 
-        // u of this group's channels to the LDS tile (token-major)
+        // u of this group's channels to the LDS tile (token-major); for fp32 q also f
         GradRow<GT> gr;
-        gr.load_lds(lds_in + kTileTensor + a * kTileHead + tok * kTileRow, g);
+        if constexpr (kStageQ && kDout16)
+            gr.load_lds(lds_in + kTileTensor + a * kTileHead + tok * kTileRow, g);
+        else
+            gr.load(dout + grow + kD * a, g);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             f32x4 u4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) u4[e] = gr.at(rr, e) * r;
             *reinterpret_cast<f32x4*>(ot + i * kPitch + 8 * rr + 4 * g) = u4;
+            if constexpr (!kStageQ) {
+                f32x4 f4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) f4[e] = fa(rr, e);
+                *reinterpret_cast<f32x4*>(ft + i * kPitch + 8 * rr + 4 * g) = f4;
+            }
         }
 
-        // m_a^T = P[32 a .., :64] dout^T: dout of both groups as the B operand
+        // m_a^T = P[32 a .., :64] dout^T (acc rs = r m_a)
         f32x16 acc = {};
+        float rs;
         {
-            u32x4 db[KS];
-            tile_operand(lds_in, 1, 0, tok, g, db[0], db[1]);
-            tile_operand(lds_in, 1, 1, tok, g, db[2], db[3]);
             u32x4 A[KS][3];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int sp = 0; sp < 3; ++sp) A[ks][sp] = opnd[a][ks][sp][lane];
-            acc = mma_split_ks<GF16, KS>(A, db, acc);
+            if constexpr (kDout16) {
+                u32x4 db[KS];   // dout of both groups, features 16 ks + 8 g ..
+                if constexpr (kStageQ) {
+                    tile_operand(lds_in, 1, 0, tok, g, db[0], db[1]);
+                    tile_operand(lds_in, 1, 1, tok, g, db[2], db[3]);
+                } else {
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        db[ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dout + grow + 16 * ks + 8 * g));
+                }
+                acc = mma_split_ks<GF16, KS>(A, db, acc);
+                rs = r;
+            } else {
+                // both waves' u (channels 16 ks + 8 g .. of group ks / 2), split
+                // into three bf16 terms; products below 2^-24 dropped
+                __syncthreads();   // both u tiles written
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const float* uw = ut[2 * sub + (ks >> 1)] + i * kPitch + 16 * (ks & 1) + 8 * g;
+                    float uu[8];
+                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(uw);
+                    const f32x4 b4 = *reinterpret_cast<const f32x4*>(uw + 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        uu[e] = a4[e];
+                        uu[4 + e] = b4[e];
+                    }
+                    u32x4 ub[3];
+                    split3_trunc_f32x8(uu, ub);
+                    acc = mma_terms(A[ks], ub, acc);
+                }
+                rs = 1.f;
+            }
         }
         float go = 0.f;
 #pragma unroll
@@ -1114,13 +1166,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
         if (g == 0) gop[wave][i] = go;
         __syncthreads();   // both groups' halves of dout . num, both u tiles written
         const float gsum = gop[2 * sub][i] + gop[2 * sub + 1][i];
-        const float w = -r * (gsum * r);
+        const float w = -r * (gsum * rs);
         if (g == 0) wv[wave][i] = i < n ? w : 0.f;   // 0 past the range: the G_z sum skips those tokens
         __builtin_amdgcn_wave_barrier();
         asm volatile("" ::: "memory");
 
         // G[32 a .., 32 b ..] += f_a^T u_b on fp32 MFMA (32 x 32 x 2, token pairs)
         const uint8_t* qrows = lds_in + a * kTileHead + 32 * sub * kTileRow;
+        auto fgather = [&](int tk) {
+            if constexpr (kStageQ)
+                return decode(relu_16(*reinterpret_cast<const uint16_t*>(qrows + tk * kTileRow + 2 * i)));
+            else
+                return ft[tk * kPitch + i];
+        };
 #pragma unroll
         for (int bg = 0; bg < 2; ++bg) {
             const float* ub = ut[2 * sub + bg];
@@ -1128,8 +1186,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
             for (int m = 0; m < 16; ++m) {
                 const int tk = 2 * m + g;
                 const bool ok = tk < n;
-                const float fv = decode(relu_16(*reinterpret_cast<const uint16_t*>(qrows + tk * kTileRow + 2 * i)));
-                const float f_ = ok ? fv : 0.f;
+                const float f_ = ok ? fgather(tk) : 0.f;
                 accG[bg] = __builtin_amdgcn_mfma_f32_32x32x2f32(f_, ok ? ub[tk * kPitch + i] : 0.f, accG[bg], 0, 0, 0);
                 if (bg == 0) gz_acc = fmaf(f_, ok ? wv[wave][tk] : 0.f, gz_acc);
             }
@@ -1141,7 +1198,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int rg = 4 * rr + e;
-                acc[rg] = fa(rr, e) > 0.f ? fmaf(z[e], w, acc[rg] * r) : 0.f;
+                acc[rg] = fa(rr, e) > 0.f ? fmaf(z[e], w, acc[rg] * rs) : 0.f;
             }
         }
         __syncthreads();   // the other wave has read this wave's u tile
@@ -1175,7 +1232,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     }
 }
 
-
 template <typename T> struct Tag { using type = T; };
 template <typename F> void by_dtype(int code, F&& f) {
     if (code == 1)
@@ -1199,14 +1255,11 @@ hipError_t launch_bwd_query(const BwdPlan& bp, const void* q, const void* dout, 
                 using OT = typename decltype(ot)::type;
                 by_dtype(pl.in_dtype, [&](auto it) {
                     using QT = typename decltype(it)::type;
-                    if constexpr (sizeof(QT) == 2 && sizeof(GT) == 2) {
-                        if (pl.D == 2 * kD) {
-                            hipLaunchKernelGGL((k_bwd_query_mfma64<QT, GT, OT>), dim3(grid), dim3(kThreads), 0, stream,
-                                               static_cast<const QT*>(q), static_cast<const GT*>(dout), state,
-                                               static_cast<OT*>(dq), gpart, pl.N, pl.H, pl.L, pl.NB, bp.tq, bp.tpbq,
-                                               eps);
-                            return;
-                        }
+                    if (pl.D == 2 * kD) {
+                        hipLaunchKernelGGL((k_bwd_query_mfma64<QT, GT, OT>), dim3(grid), dim3(kThreads), 0, stream,
+                                           static_cast<const QT*>(q), static_cast<const GT*>(dout), state,
+                                           static_cast<OT*>(dq), gpart, pl.N, pl.H, pl.L, pl.NB, bp.tq, bp.tpbq, eps);
+                        return;
                     }
                     {
                         if (pl.D == kD / 2) {

@@ -103,15 +103,32 @@ HEAD_DIMS = [(2, 1000, 5, 100, 1, 64), (1, 777, 7, 0, 2, 16), (2, 33, 1, 0, 0, 1
 
 @pytest.mark.parametrize("B,N,H,L,dt,D", HEAD_DIMS, ids=[f"B{b}N{n}H{h}L{l}dt{t}D{d}" for b, n, h, l, t, d in HEAD_DIMS])
 def test_backward_other_head_dims(B, N, H, L, dt, D):
-    """Head dims 16 and 64 (matrix-core passes; vector-unit ones for fp32
-    inputs of dim 64): ragged N, odd and single heads, block lengths 1, 64
-    and 100, the headline's token-head-feature count."""
+    """Head dims 16 and 64 (matrix-core passes): ragged N, odd and single
+    heads, block lengths 1, 64 and 100, the headline's token-head-feature
+    count."""
     w = workloads.Workload(f"bwd_B{B}N{N}H{H}L{L}dt{dt}D{D}", B, N, H, D, dt, seed=150 + N % 19 + D, block_len=L)
     (q, k, v, g), want = case(w, dt)
     check(run(q, k, v, g, L, w.eps, DT[dt]), want, DT[dt], w.name)
     if N < 16384:
         other = torch.bfloat16 if dt == workloads.DT_F32 else torch.float32
         check(run(q, k, v, g, L, w.eps, other), want, other, w.name + "/" + str(other))
+
+
+D64_MIXED = [(1, 1000, 3, 100, workloads.DT_F32, workloads.DT_BF16), (2, 333, 2, 0, workloads.DT_F32, workloads.DT_F16),
+             (1, 1000, 3, 100, workloads.DT_BF16, workloads.DT_F32), (1, 513, 1, 64, workloads.DT_F16, workloads.DT_F32),
+             (1, 16384, 35, 0, workloads.DT_F32, workloads.DT_F32)]
+
+
+@pytest.mark.parametrize("B,N,H,L,dt,gdt", D64_MIXED, ids=[f"B{b}N{n}H{h}L{l}in{t}dout{g}" for b, n, h, l, t, g in D64_MIXED])
+def test_backward_head_dim_64_mixed_types(B, N, H, L, dt, gdt):
+    """Head dim 64 with fp32 q and a 16-bit upstream gradient (q read by each
+    wave), 16-bit q and an fp32 gradient (the gradient goes in as the split u
+    of both groups), and fp32 throughout at the headline's feature count."""
+    w = workloads.Workload(f"bwd64_B{B}N{N}H{H}L{L}in{dt}dout{gdt}", B, N, H, 64, dt, seed=170 + N % 23, block_len=L)
+    (q, k, v, g), want = case(w, gdt)
+    check(run(q, k, v, g, L, w.eps, torch.float32), want, torch.float32, w.name)
+    if N < 16384:
+        check(run(q, k, v, g, L, w.eps, torch.bfloat16), want, torch.bfloat16, w.name + "/bf16grad")
 
 
 def test_backward_single_token_is_identity_in_v():

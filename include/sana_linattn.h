@@ -37,9 +37,7 @@
  *            fp16 out cannot overflow).  D is 32 (the Sana head dim, on the matrix
  *            cores; fp32 inputs as three-term bf16 splits with the products
  *            below 2^-24 dropped), 16 or 64 (the same kernels on 32-feature
- *            groups of the token row) for every entry point; the
- *            backward's query pass of 64 with fp32 q or dout runs on the
- *            vector unit.
+ *            groups of the token row) for every entry point.
  * Memory     Every pointer is device memory on the current HIP device, owned
  *            by the caller.  The library allocates nothing, keeps nothing
  *            after return, and never synchronises: work is enqueued on

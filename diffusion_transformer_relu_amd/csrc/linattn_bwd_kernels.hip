@@ -231,6 +231,7 @@ constexpr int kTileRow = 80;                       // bytes per token row: 64 + 
                                                    // 8 consecutive rows in distinct banks
 constexpr int kTileHead = kTileTok * kTileRow + 64;   // bytes per head
 constexpr int kTileTensor = 2 * kTileHead;            // bytes per tensor
+constexpr int kUPitch = 40;   // 16-bit elements per row of a u term tile: 80 bytes, as the staged rows (8-byte aligned transposing reads)
 
 struct TileLoader {
     const uint16_t* x[2];   // the two tensors (the second may be null: one tensor only)
@@ -997,7 +998,10 @@ static_assert(sizeof(OperandLds) >= (2 * 16 * 64 + 2 * 32) * sizeof(float), "G r
 //   through LDS (a work-group barrier), w = -r^2 (dout . num)
 //   dq_a = [q_a > 0] (r m_a + w z_a)
 //   G[32 a .., 32 b ..] += f_a^T u_b for b = 0, 1 (u_b from the wave of
-//   group b), G_z[32 a ..] += f_a^T w
+//   group b), G_z[32 a ..] += f_a^T w; with bf16 q on the bf16 matrix
+//   instructions (tokens as the reduction dimension, both operands gathered
+//   transposed from LDS: f exact, u as the three bf16 terms of its truncation
+//   split, which sum to u exactly), with fp32 or fp16 q on the fp32 ones
 // A last barrier keeps each u tile until the other wave has read it.  Every
 // wave takes every step (a sub-tile past the range computes on the clamped
 // last row and stores nothing), so the barriers are reached by all.  16-bit q
@@ -1012,12 +1016,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     constexpr bool GF16 = std::is_same<GT, _Float16>::value, QF16 = std::is_same<QT, _Float16>::value;
     __shared__ u32x4 opnd[2][KS][3][64];                              // P natural split terms, rows of group a
     __shared__ __attribute__((aligned(16))) float pzs[2][32];          // P[:, 64] at the rows of each group
-    __shared__ __attribute__((aligned(16))) float ut[4][32 * kPitch];  // u tile, then the dq tile
+    __shared__ __attribute__((aligned(16))) uint16_t ush[4][3][32 * kUPitch];   // u as three bf16 terms, then the dq tile
     __shared__ __attribute__((aligned(16))) float wv[4][32];           // w of each token
     __shared__ __attribute__((aligned(16))) float gop[4][32];          // f_a . m_a of each token
     __shared__ __attribute__((aligned(16))) uint8_t lds_in[2 * kTileTensor];   // staged q (and 16-bit dout) / f tiles
     static_assert(sizeof(opnd) >= (2 * 2 * 16 * 64 + 2 * 32) * sizeof(float), "G reduction area exceeds the operand space");
     static_assert(sizeof(lds_in) >= 4 * 32 * kPitch * sizeof(float), "f tiles exceed the staging area");
+    static_assert(sizeof(ush[0]) >= 32 * kPitch * sizeof(float), "dq tile exceeds the u area");
 
     const int per_unit = NB * tpb;
     const int tau = blockIdx.x % per_unit;
@@ -1044,11 +1049,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     __syncthreads();
 
     const long long hstride = (long long)HR * HD;
-    float* ot = ut[wave];
+    float* ot = reinterpret_cast<float*>(&ush[wave][0][0]);   // dq tile (after the u terms are read)
     float* ft = reinterpret_cast<float*>(lds_in) + wave * 32 * kPitch;   // fp32 q: f tile of this wave
     f32x16 accG[2] = {};   // G[32 a .., 32 b ..] for b = 0, 1
     float gz_acc = 0.f;    // lane (g, j): sum over this lane's tokens of f_j w (feature 32 a + j)
-    auto decode = [&](uint16_t x) { return QF16 ? f16_to_f32(x) : bf16_to_f32(x); };
     auto zrow = [&](int gi, int rr) { return *reinterpret_cast<const f32x4*>(&pzs[gi][8 * rr + 4 * g]); };
 
     const uint16_t* dstage = kDout16 ? reinterpret_cast<const uint16_t*>(dout) : nullptr;
@@ -1061,6 +1065,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
             __syncthreads();
             if (tt0 + kTileTok < t1) ld.load(tt0 + kTileTok);   // in flight during this tile's work
         }
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");   // the last step's dq tile is read before the u terms overwrite it
         const int tt = tt0 + 32 * sub;
         const int n = min(32, t1 - tt);   // <= 0: a step past the range (computes, stores nothing)
         const int tok = 32 * sub + i;     // this lane's token in the tile
@@ -1094,7 +1100,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
         auto fa = [&](int rr, int e) { return relu_f32(qo.at(rr, e)); };
         const float r = 1.0f / (den + eps);
 
-        // u of this group's channels to the LDS tile (token-major); for fp32 q also f
+        // u of this group's channels to the LDS tiles as three bf16 truncation
+        // terms (token-major); for fp32 q also f.  Tokens past the range keep
+        // the clamped row's values (store_tile relies on it): the G products
+        // mask them through f.
         GradRow<GT> gr;
         if constexpr (kStageQ && kDout16)
             gr.load_lds(lds_in + kTileTensor + a * kTileHead + tok * kTileRow, g);
@@ -1105,7 +1114,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
             f32x4 u4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) u4[e] = gr.at(rr, e) * r;
-            *reinterpret_cast<f32x4*>(ot + i * kPitch + 8 * rr + 4 * g) = u4;
+            const float x8[8] = {u4[0], u4[1], u4[2], u4[3], 0.f, 0.f, 0.f, 0.f};
+            u32x4 ts[3];
+            split3_trunc_f32x8(x8, ts);
+#pragma unroll
+            for (int sp = 0; sp < 3; ++sp)
+                *reinterpret_cast<u32x2*>(&ush[wave][sp][i * kUPitch + 8 * rr + 4 * g]) = (u32x2){ts[sp][0], ts[sp][1]};
             if constexpr (!kStageQ) {
                 f32x4 f4;
 #pragma unroll
@@ -1136,22 +1150,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
                 acc = mma_split_ks<GF16, KS>(A, db, acc);
                 rs = r;
             } else {
-                // both waves' u (channels 16 ks + 8 g .. of group ks / 2), split
-                // into three bf16 terms; products below 2^-24 dropped
+                // both waves' u terms (channels 16 ks + 8 g .. of group ks / 2);
+                // products below 2^-24 dropped
                 __syncthreads();   // both u tiles written
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const float* uw = ut[2 * sub + (ks >> 1)] + i * kPitch + 16 * (ks & 1) + 8 * g;
-                    float uu[8];
-                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(uw);
-                    const f32x4 b4 = *reinterpret_cast<const f32x4*>(uw + 4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        uu[e] = a4[e];
-                        uu[4 + e] = b4[e];
-                    }
                     u32x4 ub[3];
-                    split3_trunc_f32x8(uu, ub);
+#pragma unroll
+                    for (int sp = 0; sp < 3; ++sp)
+                        ub[sp] = *reinterpret_cast<const u32x4*>(
+                            &ush[2 * sub + (ks >> 1)][sp][i * kUPitch + 16 * (ks & 1) + 8 * g]);
                     acc = mma_terms(A[ks], ub, acc);
                 }
                 rs = 1.f;
@@ -1171,24 +1179,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
         __builtin_amdgcn_wave_barrier();
         asm volatile("" ::: "memory");
 
-        // G[32 a .., 32 b ..] += f_a^T u_b on fp32 MFMA (32 x 32 x 2, token pairs)
-        const uint8_t* qrows = lds_in + a * kTileHead + 32 * sub * kTileRow;
-        auto fgather = [&](int tk) {
-            if constexpr (kStageQ)
-                return decode(relu_16(*reinterpret_cast<const uint16_t*>(qrows + tk * kTileRow + 2 * i)));
-            else
-                return ft[tk * kPitch + i];
-        };
+        // G[32 a .., 32 b ..] += f_a^T u_b; G_z from the same f (lane (g, j):
+        // feature j of its tokens)
+        if constexpr (kStageQ && !QF16) {
+            const uint16_t* qg = reinterpret_cast<const uint16_t*>(lds_in + a * kTileHead);
 #pragma unroll
-        for (int bg = 0; bg < 2; ++bg) {
-            const float* ub = ut[2 * sub + bg];
+            for (int ks = 0; ks < 2; ++ks) {
+                // f of tokens 32 sub + 16 ks + 8 g + e, feature i
+                u32x4 fa4 = gather_tokens_t16(qg, kTileRow / 2, 32 * sub + 16 * ks, 0, lane);
+                const f32x4 w0 = *reinterpret_cast<const f32x4*>(&wv[wave][16 * ks + 8 * g]);
+                const f32x4 w1 = *reinterpret_cast<const f32x4*>(&wv[wave][16 * ks + 8 * g + 4]);
 #pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                const int tk = 2 * m + g;
-                const bool ok = tk < n;
-                const float f_ = ok ? fgather(tk) : 0.f;
-                accG[bg] = __builtin_amdgcn_mfma_f32_32x32x2f32(f_, ok ? ub[tk * kPitch + i] : 0.f, accG[bg], 0, 0, 0);
-                if (bg == 0) gz_acc = fmaf(f_, ok ? wv[wave][tk] : 0.f, gz_acc);
+                for (int d = 0; d < 4; ++d) {
+                    const int tb = 16 * ks + 8 * g + 2 * d;   // the tokens of the two halves: tb, tb + 1
+                    const uint32_t keep = (tb < n ? 0xffffu : 0u) | (tb + 1 < n ? 0xffff0000u : 0u);
+                    const uint32_t x = fa4[d] & ~(((fa4[d] & 0x80008000u) >> 15) * 0xffffu) & keep;   // ReLU, range
+                    const float wl = d < 2 ? w0[2 * d] : w1[2 * d - 4], wh = d < 2 ? w0[2 * d + 1] : w1[2 * d - 3];
+                    fa4[d] = x;
+                    gz_acc = fmaf(hi_bf16(x), wh, fmaf(lo_bf16(x), wl, gz_acc));
+                }
+#pragma unroll
+                for (int bg = 0; bg < 2; ++bg)
+#pragma unroll
+                    for (int sp = 2; sp >= 0; --sp) {
+                        const u32x4 ub = gather_tokens_t16(ush[2 * sub + bg][sp], kUPitch, 16 * ks, 0, lane);
+                        accG[bg] = mfma_bf16(fa4, ub, accG[bg]);
+                    }
+            }
+        } else {
+            // fp32 (or fp16) f on fp32 MFMA (32 x 32 x 2, token pairs); u is the sum of its terms
+#pragma unroll
+            for (int bg = 0; bg < 2; ++bg) {
+#pragma unroll
+                for (int m = 0; m < 16; ++m) {
+                    const int tk = 2 * m + g;
+                    const bool ok = tk < n;
+                    float f_;
+                    if constexpr (kStageQ)
+                        f_ = ok ? f16_to_f32(relu_16(*reinterpret_cast<const uint16_t*>(
+                                      lds_in + a * kTileHead + (32 * sub + tk) * kTileRow + 2 * i)))
+                                : 0.f;
+                    else
+                        f_ = ok ? ft[tk * kPitch + i] : 0.f;
+                    const int o = tk * kUPitch + i;
+                    const uint16_t* ub = &ush[2 * sub + bg][0][0];
+                    const float uv = (bf16_to_f32(ub[o]) + bf16_to_f32(ub[32 * kUPitch + o])) +
+                                     bf16_to_f32(ub[2 * 32 * kUPitch + o]);
+                    accG[bg] = __builtin_amdgcn_mfma_f32_32x32x2f32(f_, uv, accG[bg], 0, 0, 0);
+                    if (bg == 0) gz_acc = fmaf(f_, ok ? wv[wave][tk] : 0.f, gz_acc);
+                }
             }
         }
 

@@ -34,11 +34,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    os.makedirs(LIBDIR, exist_ok=True)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *SOURCES, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -48,6 +44,26 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if msgs and verbose:
         print("\n".join(msgs))
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compiles every source to an object file in parallel (each kernel file
+    holds its own launchers, so no device code crosses files), then links."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    os.makedirs(LIBDIR, exist_ok=True)
+    objdir = os.path.join(LIBDIR, "obj")
+    os.makedirs(objdir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in SOURCES]
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        jobs = [ex.submit(_run, [hipcc(), *compile_flags, *extra_flags, *inc, "-c", s, "-o", o], verbose)
+                for s, o in zip(SOURCES, objs)]
+        for j in jobs:
+            j.result()
+    tmp = LIB + ".tmp"
+    _run([hipcc(), *HIPCC_FLAGS, *extra_flags, *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

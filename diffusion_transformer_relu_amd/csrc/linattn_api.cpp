@@ -90,11 +90,12 @@ int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block
         if (tile) {
             tile = (int)round_up(tile, 64);
         } else {
-            // fp16 and fp32 q run the apply kernel at 4 waves per SIMD instead
-            // of 5, head dim 64 at 3 (2 for fp32 q)
-            const long slots = D == 2 * sana::kD ? sana::kCUs * (in_dtype == SANA_DT_F32 ? 2 : 3)
-                               : in_dtype != SANA_DT_BF16 ? sana::kApplyGroups * 4 / 5 : sana::kApplyGroups;
-            const long per_block = std::max<long>(1, slots / units);
+            // head dim 64 runs the apply kernel at 3 waves per SIMD (2 for fp32
+            // q), so at most that many work-groups fit on a CU; the block count
+            // per unit is rounded to nearest, so that many short units (the
+            // block-causal shapes) still get about the target
+            const long slots = D == 2 * sana::kD ? sana::kCUs * (in_dtype == SANA_DT_F32 ? 2 : 3) : sana::kApplyGroups;
+            const long per_block = std::max<long>(1, (slots + units / 2) / units);
             tile = (int)round_up(ceil_div(pl->L, per_block), 64);
         }
         pl->tile = (int)std::min<long>(tile, round_up(pl->L, 64));

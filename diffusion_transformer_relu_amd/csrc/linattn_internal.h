@@ -20,13 +20,15 @@ constexpr int kValuApplyTokens = 256;     // tokens per work-group, vector apply
 constexpr int kMergeThreads = 256;        // state entries per merge work-group
 
 // Work-group counts per launch, tuned on MI355X (256 CUs).  The state kernel
-// streams K/V fastest with about 2 work-groups per CU (measured: 560 groups of
-// 1024-token chunks beat 1120 groups of 512 tokens and 280 of 2048 at the
-// 4096px shape); the apply kernel wants one full round at 5 work-groups per CU
-// (its occupancy at 5 waves per SIMD).
+// streams K/V fastest with at most 2 work-groups on any CU: at the 4096px shape
+// 490 groups of 1216-token chunks take 25.5 us, 560 groups of 1024 (some CUs
+// holding 3) 26.7 us, 525 of 1152 27.7 us, 1120 of 512 28.9 us.  The apply
+// kernel likewise prefers at most 4 per CU (1015 groups of 576 tokens:
+// 35.3 us with fp32 out and 25.8 with bf16 out, against 35.7 and 26.7 for 1120
+// groups of 512).
 constexpr int kCUs = 256;
-constexpr int kStateGroups = 576;
-constexpr int kApplyGroups = kCUs * 5;
+constexpr int kStateGroups = kCUs * 2;
+constexpr int kApplyGroups = kCUs * 4;
 constexpr int kMinChunk = 256;            // keeps the partial states a few % of the K/V bytes
 
 // Element strides of a [B][N][H][D] tensor view: consecutive heads are D

@@ -443,12 +443,17 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(
     const float* src = part + bh * P * SF + e;
     float* dst = state + bh * NB * SF + e;
     float acc = state_in ? state_in[bh * SF + e] : 0.f;
+    // Loads take clamped (always valid) indices and are unconditional, so a
+    // thread's loads are all in flight before the first sum; entries past the
+    // end are then replaced by zeros, or not stored.
     if (cpb == 1) {
         // one partial per block (the block-causal case): 16 blocks' loads at once
         for (int b0 = 0; b0 < NB; b0 += 16) {
             float x[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = (b0 + i < NB) ? src[(size_t)(b0 + i) * SF] : 0.f;
+            for (int i = 0; i < 16; ++i) x[i] = src[(size_t)min(b0 + i, NB - 1) * SF];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(x[i]));   // all 16 in flight first
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 if (b0 + i < NB) {
@@ -457,27 +462,24 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(
                 }
             }
         }
-    } else if (cpb <= 16) {
-        for (int beta = 0; beta < NB; ++beta) {
-            const float* blk = src + (size_t)beta * cpb * SF;
-            float x[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = (i < cpb) ? blk[(size_t)i * SF] : 0.f;
-            float bs = 0.f;
-            bs += tree8(x);
-            if (cpb > 8) bs += tree8(x + 8);
-            acc += bs;
-            dst[(size_t)beta * SF] = acc;
-        }
     } else {
+        // each block: its chunk partials in groups of 8 added as a fixed
+        // pairwise tree, the groups in order
         for (int beta = 0; beta < NB; ++beta) {
             const float* blk = src + (size_t)beta * cpb * SF;
             float bs = 0.f;
-            for (int s0 = 0; s0 < cpb; s0 += 8) {
-                float x[8];
+            for (int s0 = 0; s0 < cpb; s0 += 16) {
+                float x[16];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) x[i] = (s0 + i < cpb) ? blk[(size_t)(s0 + i) * SF] : 0.f;
+                for (int i = 0; i < 16; ++i) x[i] = blk[(size_t)min(s0 + i, cpb - 1) * SF];
+                // (keeps the compiler from deferring the second group's loads
+                // until the first group is summed)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(x[i]));
+#pragma unroll
+                for (int i = 0; i < 16; ++i) x[i] = s0 + i < cpb ? x[i] : 0.f;
                 bs += tree8(x);
+                if (s0 + 8 < cpb) bs += tree8(x + 8);
             }
             acc += bs;
             dst[(size_t)beta * SF] = acc;

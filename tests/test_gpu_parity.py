@@ -58,6 +58,8 @@ EDGE = [
     (2, 257, 5, 0, workloads.DT_BF16),
     (3, 1000, 7, 0, workloads.DT_BF16),
     (1, 4097, 2, 0, workloads.DT_BF16),
+    (1, 16384, 2, 0, workloads.DT_BF16),     # one head pair: 64 work-group ranges per block (>32 merge slots)
+    (2, 5000, 3, 1100, workloads.DT_BF16),   # ranges crossing head-pair, batch and block boundaries
     (2, 1000, 3, 100, workloads.DT_BF16),
     (1, 999, 4, 1, workloads.DT_BF16),
     (1, 1024, 2, 1024, workloads.DT_BF16),

@@ -25,6 +25,8 @@ SANA_ERR_ALIGNMENT = 3
 SANA_ERR_ALIAS = 4
 SANA_ERR_WORKSPACE = 5
 SANA_ERR_HIP = 6
+SANA_ERR_SCRATCH = 7
+SANA_LINATTN_SCRATCH_BYTES = 16 << 20
 SANA_STAGE_STATE = 1
 SANA_STAGE_MERGE = 2
 SANA_STAGE_APPLY = 4
@@ -53,6 +55,7 @@ _SIGNATURES = {
     "sana_linattn_jvp_workspace_bytes": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]),
     "sana_linattn_jvp": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P,
                               ctypes.c_size_t, _P]),
+    "sana_linattn_fwd_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]),
     "sana_linattn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P,
                               ctypes.c_size_t, _P]),
 }
@@ -152,6 +155,15 @@ def sana_linattn_fwd(q, k, v, out, workspace, *, eps: float = 1e-15, stream=None
                                 dtype_code(out), B, H, N, D, eps, workspace.data_ptr(),
                                 workspace.numel() * workspace.element_size(), _stream_handle(stream)),
            "sana_linattn_fwd")
+
+
+def sana_linattn_fwd_noalloc(q, k, v, out, *, eps: float = 1e-15, stream=None):
+    """Non-causal forward into `out` with the library's static device scratch
+    (no workspace argument, nothing allocated)."""
+    B, N, H, D = _shape(q, k, v, out)
+    _check(lib.sana_linattn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dtype_code(q),
+                                        dtype_code(out), B, H, N, D, eps, _stream_handle(stream)),
+           "sana_linattn_fwd_noalloc")
 
 
 def sana_linattn_blockcausal_fwd(q, k, v, out, workspace, block_len: int, *, eps: float = 1e-15,

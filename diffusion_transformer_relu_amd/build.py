@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libsana_linattn.so")
 SOURCES = [os.path.join(CSRC, "linattn_kernels.hip"), os.path.join(CSRC, "linattn_bwd_kernels.hip"),
-           os.path.join(CSRC, "linattn_jvp_kernels.hip"), os.path.join(CSRC, "linattn_api.cpp")]
+           os.path.join(CSRC, "linattn_jvp_kernels.hip"), os.path.join(CSRC, "linattn_noalloc.hip"),
+           os.path.join(CSRC, "linattn_api.cpp")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

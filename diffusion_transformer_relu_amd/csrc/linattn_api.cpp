@@ -384,6 +384,24 @@ int jvp(const void* q, const void* k, const void* v, const void* qt, const void*
 
 }  // namespace
 
+namespace sana {
+
+int forward_call(const void* q, const void* k, const void* v, void* out, int in_dtype, int out_dtype, int B, int H,
+                 int N, int D, int block_len, float eps, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return forward(q, k, v, out, in_dtype, out_dtype, B, H, N, D, block_len, eps, workspace, workspace_bytes, stream,
+                   SANA_STAGE_ALL);
+}
+
+int forward_workspace(int in_dtype, int out_dtype, int B, int H, int N, int D, int block_len, size_t* bytes) {
+    Plan pl;
+    const int st = make_plan(in_dtype, out_dtype, B, H, N, D, block_len, &pl);
+    if (st != SANA_OK) return st;
+    *bytes = pl.bytes;
+    return SANA_OK;
+}
+
+}  // namespace sana
+
 extern "C" {
 
 int sana_linattn_abi_version(void) { return SANA_LINATTN_ABI_VERSION; }
@@ -392,11 +410,13 @@ const char* sana_linattn_status_string(int status) {
     switch (status) {
         case SANA_OK: return "success";
         case SANA_ERR_INVALID_ARG: return "invalid argument";
-        case SANA_ERR_UNSUPPORTED: return "unsupported size or head dim (forward: D = 16, 32 or 64; backward and JVP: D = 32)";
+        case SANA_ERR_UNSUPPORTED: return "unsupported size or head dim (D must be 16, 32 or 64)";
         case SANA_ERR_ALIGNMENT: return "misaligned pointer (tensors need 16 bytes, workspace 256)";
         case SANA_ERR_ALIAS: return "output or workspace overlaps another buffer";
         case SANA_ERR_WORKSPACE: return "workspace too small";
         case SANA_ERR_HIP: return "HIP runtime error while enqueueing";
+        case SANA_ERR_SCRATCH:
+            return "problem needs more scratch than the no-allocation entry point holds (SANA_LINATTN_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

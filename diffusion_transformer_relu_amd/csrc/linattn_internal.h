@@ -70,6 +70,15 @@ template <typename F> void by_head_dim(int D, F&& f) {
         f(std::integral_constant<int, 32>{});
 }
 
+// The forward behind every forward entry point (linattn_api.cpp): argument
+// checks, then the state, merge and apply kernels on `stream` with the given
+// workspace; returns a sana_status_t code.
+int forward_call(const void* q, const void* k, const void* v, void* out, int in_dtype, int out_dtype, int B, int H,
+                 int N, int D, int block_len, float eps, void* workspace, size_t workspace_bytes, hipStream_t stream);
+// Workspace bytes that forward_call needs for these arguments (0 for an empty
+// problem); a sana_status_t code for invalid sizes, dtypes or head dims.
+int forward_workspace(int in_dtype, int out_dtype, int B, int H, int N, int D, int block_len, size_t* bytes);
+
 // Each launcher enqueues one kernel on `stream` and returns hipGetLastError().
 hipError_t launch_state(const Plan& pl, const void* k, const void* v, float* part, hipStream_t stream);
 hipError_t launch_merge(const Plan& pl, const float* part, float* state, const float* state_in,

@@ -94,8 +94,14 @@ typedef enum {
     SANA_ERR_ALIGNMENT = 3,    /* q, k, v, out not 16-byte aligned, workspace not 256-byte aligned */
     SANA_ERR_ALIAS = 4,        /* out or workspace overlaps an input, or each other */
     SANA_ERR_WORKSPACE = 5,    /* workspace_bytes smaller than required */
-    SANA_ERR_HIP = 6           /* a HIP runtime error while enqueueing */
+    SANA_ERR_HIP = 6,          /* a HIP runtime error while enqueueing */
+    SANA_ERR_SCRATCH = 7       /* sana_linattn_fwd_noalloc: the problem needs more than
+                                  SANA_LINATTN_SCRATCH_BYTES of scratch */
 } sana_status_t;
+
+/* Size of the library's static device scratch array used by
+ * sana_linattn_fwd_noalloc (one copy per GPU, held until the process ends). */
+#define SANA_LINATTN_SCRATCH_BYTES (16u << 20)
 
 /* Stage bits for sana_linattn_fwd_stages(). */
 #define SANA_STAGE_STATE 1  /* per-chunk partial states from k, v */
@@ -119,7 +125,7 @@ SANA_API const char* sana_linattn_status_string(int status);
  * (SANA_LINATTN_CHUNK, SANA_LINATTN_APPLY_TILE, SANA_LINATTN_PATH), so query it
  * in the same environment as the call.
  * Errors: INVALID_ARG (bytes NULL, negative sizes, block_len < 0),
- * UNSUPPORTED (D != 32, sizes too large).
+ * UNSUPPORTED (D not 16, 32 or 64, sizes too large).
  */
 SANA_API int sana_linattn_workspace_bytes(int B, int H, int N, int D, int block_len, size_t* bytes);
 
@@ -279,6 +285,26 @@ SANA_API int sana_linattn_jvp(const void* q, const void* k, const void* v, const
                               const void* v_t, void* out, void* out_t, int in_dtype, int out_dtype, int B, int H,
                               int N, int D, int block_len, float eps, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the forward
+ * of sana_linattn_fwd with the same arguments and results, minus the
+ * workspace.  Scratch space is a static device array of the library,
+ * SANA_LINATTN_SCRATCH_BYTES per GPU (its address is looked up once per device
+ * with hipGetSymbolAddress, on the first call on that device); the call
+ * allocates nothing (no hipMalloc, no allocating library routine).
+ *   Returns SANA_ERR_SCRATCH, before anything is enqueued, when the problem
+ *   needs more scratch than that (sana_linattn_workspace_bytes tells how much it
+ *   needs); other errors as for sana_linattn_fwd.
+ *   Every call on one GPU uses that GPU's one array: calls that may overlap on
+ *   one GPU (different streams or host threads without ordering) race and must
+ *   not be made; calls ordered on one stream are fine.  The array keeps the
+ *   last call's contents; nothing in it needs to start at zero.
+ */
+SANA_API int sana_linattn_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
+                                      int in_dtype, int out_dtype, int B, int H, int N, int D, float eps,
+                                      hipStream_t stream);
 
 #ifdef __cplusplus
 }

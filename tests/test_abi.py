@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(sana.lib, n), n           # resolves in the shared library
         assert n in sana._SIGNATURES, n          # and the binding declares its signature
@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported_and_bound():
 
 def test_version_and_status_strings():
     assert sana.sana_linattn_abi_version() == 1
-    for s in range(7):
+    for s in range(8):
         assert sana.sana_linattn_status_string(s) not in ("", "unknown status")
     assert sana.sana_linattn_status_string(99) == "unknown status"
     assert sana.sana_linattn_status_string(-1) == "unknown status"
@@ -288,3 +288,24 @@ def test_jvp_workspace_query():
     assert jw >= 2 * 70 * (16 + 1) * 4224 and jw % 256 == 0
     assert jw > sana.sana_linattn_workspace_bytes(1, 70, 16384, 32, 0)
     assert sana.lib.sana_linattn_jvp_workspace_bytes(1, 1, 1, 32, 0, None) == sana.SANA_ERR_INVALID_ARG
+
+
+def test_noalloc_entry_point_rejects_problems_beyond_its_scratch():
+    """The no-allocation forward checks its sizes before any HIP call: a problem
+    whose workspace exceeds the static scratch is refused with SCRATCH, bad
+    arguments with the usual codes, an empty problem succeeds (fake, never
+    dereferenced pointers)."""
+    fake = ctypes.c_void_p(1 << 20)
+    f = sana.lib.sana_linattn_fwd_noalloc
+    B, H, N, D = 64, 70, 1024, 32
+    assert sana.sana_linattn_workspace_bytes(B, H, N, D, 0) > sana.SANA_LINATTN_SCRATCH_BYTES
+    assert f(fake, fake, fake, fake, sana.SANA_DT_BF16, sana.SANA_DT_F32, B, H, N, D, 1e-15, None) == \
+        sana.SANA_ERR_SCRATCH
+    assert "scratch" in sana.sana_linattn_status_string(sana.SANA_ERR_SCRATCH)
+    assert f(fake, fake, fake, fake, sana.SANA_DT_BF16, sana.SANA_DT_F32, 1, 70, 16384, 48, 1e-15, None) == \
+        sana.SANA_ERR_UNSUPPORTED
+    assert f(fake, fake, fake, fake, 9, sana.SANA_DT_F32, 1, 70, 16384, 32, 1e-15, None) == sana.SANA_ERR_INVALID_ARG
+    assert f(None, None, None, None, sana.SANA_DT_BF16, sana.SANA_DT_F32, 1, 0, 16384, 32, 1e-15, None) == \
+        sana.SANA_OK
+    # the headline shape fits
+    assert sana.sana_linattn_workspace_bytes(1, 70, 16384, 32, 0) <= sana.SANA_LINATTN_SCRATCH_BYTES

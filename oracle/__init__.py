@@ -38,6 +38,12 @@ def _load():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_linattn_fwd_qknorm.restype = ctypes.c_int
+        lib.oracle_linattn_fwd_qknorm.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_linattn_bwd.restype = ctypes.c_int
         lib.oracle_linattn_bwd.argtypes = [
@@ -84,13 +90,17 @@ def num_blocks(N: int, block_len: int | None) -> int:
 
 
 def linattn_fwd(q, k, v, *, block_len: int | None = None, eps: float = 1e-15,
-                nthreads: int = 0, return_states: bool = False, state_in=None):
+                nthreads: int = 0, return_states: bool = False, state_in=None,
+                gamma_q=None, gamma_k=None, norm_eps: float = 0.0):
     """fp64 LiteLA forward on host arrays of shape [B, N, H, D].
 
     q, k, v: float32, float16, or uint16 holding bfloat16 bits (all three the same).
     block_len: None/0 for non-causal, else the frame-block length in tokens.
     state_in: optional float64 [B, H, D, D+1], the state before the first token
     (a carried state from an earlier call over the preceding tokens).
+    gamma_q, gamma_k: optional [H, D] per-channel scales of the qk_norm prologue
+    (each head's q or k row RMS-normalised over its D features, with norm_eps
+    under the root, then scaled, before phi); None leaves that side as it is.
     Returns out as float64 [B, N, H, D]; with return_states also the inclusive
     per-block states, float64 [B, H, NB, D, D+1] (the last one is the final state).
     """
@@ -111,9 +121,15 @@ def linattn_fwd(q, k, v, *, block_len: int | None = None, eps: float = 1e-15,
         state_in = np.ascontiguousarray(state_in, dtype=np.float64)
         if state_in.shape != (B, H, D, D + 1):
             raise ValueError(f"state_in must be [B, H, D, D+1] = {(B, H, D, D + 1)}")
-    rc = _load().oracle_linattn_fwd(
+    gq = gk = None
+    if gamma_q is not None:
+        gq = np.ascontiguousarray(gamma_q, dtype=np.float64).reshape(H, D)
+    if gamma_k is not None:
+        gk = np.ascontiguousarray(gamma_k, dtype=np.float64).reshape(H, D)
+    rc = _load().oracle_linattn_fwd_qknorm(
         q.ctypes.data, k.ctypes.data, v.ctypes.data, code, B, H, N, D,
-        int(block_len or 0), float(eps), out.ctypes.data,
+        int(block_len or 0), float(eps), gq.ctypes.data if gq is not None else None,
+        gk.ctypes.data if gk is not None else None, float(norm_eps), out.ctypes.data,
         states.ctypes.data if states is not None else None,
         state_in.ctypes.data if state_in is not None else None, int(nthreads))
     if rc != 0:

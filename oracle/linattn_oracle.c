@@ -37,6 +37,15 @@
  * starting from the previous call's final state, gives the same outputs as one
  * call over the whole sequence.
  *
+ * qk_norm (optional; the Sana page, section "What LiteLA actually computes",
+ * says every Sana-1.5 and Sprint configuration turns on `qk_norm` to keep the
+ * ReLU-linear logits from growing out of fp16 range, without giving a formula):
+ * read here as an RMS normalisation of each head's D features of q and of k,
+ * with a per-channel scale and a small constant under the root, before phi:
+ *     xhat[j] = gamma[h][j] * x[j] / sqrt((sum_j' x[j']^2) / D + norm_eps)
+ * separately for q (gamma_q) and k (gamma_k); a NULL gamma leaves that side as
+ * it is.  The rest of the operator is unchanged.
+ *
  * Arithmetic: every input element is decoded exactly to double (bf16 bits are
  * the upper half of an IEEE float32; fp16 is IEEE binary16), and all sums run
  * sequentially in token order in double precision.  No blocking or reordering
@@ -92,6 +101,21 @@ int oracle_decode(const void* src, int dtype, size_t n, double* out) {
 
 static double relu(double x) { return x > 0.0 ? x : 0.0; }
 
+/* Decodes row `row` (D elements) into x and, when gamma (the [H][D] scales of
+ * head h) is given, RMS-normalises it: x[j] = gamma[h][j] * x[j] / rms, with
+ * rms = sqrt(mean of x^2 over the row + norm_eps).  Then applies phi. */
+static void load_phi_row(const void* src, int dtype, size_t row, int D, const double* gamma, int h,
+                         double norm_eps, double* x) {
+    for (int j = 0; j < D; ++j) x[j] = load_elem(src, dtype, row + j);
+    if (gamma) {
+        double ss = 0.0;
+        for (int j = 0; j < D; ++j) ss += x[j] * x[j];
+        const double rms = sqrt(ss / D + norm_eps);
+        for (int j = 0; j < D; ++j) x[j] = gamma[(size_t)h * D + j] * x[j] / rms;
+    }
+    for (int j = 0; j < D; ++j) x[j] = relu(x[j]);
+}
+
 int oracle_abi_version(void) { return 1; }
 
 /*
@@ -103,10 +127,27 @@ int oracle_abi_version(void) { return 1; }
  * nthreads <= 0 leaves the OpenMP default.
  * Returns 0 on success, -1 on bad arguments.
  */
+int oracle_linattn_fwd_qknorm(const void* q, const void* k, const void* v, int in_dtype,
+                              int B, int H, int N, int D, int block_len, double eps,
+                              const double* gamma_q, const double* gamma_k, double norm_eps,
+                              double* out, double* states, const double* state_in, int nthreads);
+
 int oracle_linattn_fwd(const void* q, const void* k, const void* v, int in_dtype,
                        int B, int H, int N, int D, int block_len, double eps,
                        double* out, double* states, const double* state_in, int nthreads) {
-    if (B < 0 || H < 0 || N < 0 || D < 1) return -1;
+    return oracle_linattn_fwd_qknorm(q, k, v, in_dtype, B, H, N, D, block_len, eps, NULL, NULL, 0.0, out,
+                                     states, state_in, nthreads);
+}
+
+/*
+ * The same with the optional qk_norm prologue (see the file header):
+ * gamma_q, gamma_k: [H][D] doubles or NULL; norm_eps >= 0.
+ */
+int oracle_linattn_fwd_qknorm(const void* q, const void* k, const void* v, int in_dtype,
+                              int B, int H, int N, int D, int block_len, double eps,
+                              const double* gamma_q, const double* gamma_k, double norm_eps,
+                              double* out, double* states, const double* state_in, int nthreads) {
+    if (B < 0 || H < 0 || N < 0 || D < 1 || !(norm_eps >= 0.0)) return -1;
     if (in_dtype != ORACLE_F32 && in_dtype != ORACLE_BF16 && in_dtype != ORACLE_F16) return -1;
     if (B == 0 || H == 0 || N == 0) return 0;
     if (!q || !k || !v || !out) return -1;
@@ -143,7 +184,7 @@ int oracle_linattn_fwd(const void* q, const void* k, const void* v, int in_dtype
                     /* add this block's keys and values into the state */
                     for (int n = n0; n < n1; ++n) {
                         const size_t row = (((size_t)b * N + n) * H + h) * (size_t)D;
-                        for (int j = 0; j < D; ++j) a[j] = relu(load_elem(k, in_dtype, row + j));
+                        load_phi_row(k, in_dtype, row, D, gamma_k, h, norm_eps, a);
                         for (int j = 0; j < D; ++j) {
                             for (int c = 0; c < D; ++c)
                                 S[j * W + c] += a[j] * load_elem(v, in_dtype, row + c);
@@ -157,7 +198,7 @@ int oracle_linattn_fwd(const void* q, const void* k, const void* v, int in_dtype
                     /* apply the state to this block's queries */
                     for (int i = n0; i < n1; ++i) {
                         const size_t row = (((size_t)b * N + i) * H + h) * (size_t)D;
-                        for (int j = 0; j < D; ++j) f[j] = relu(load_elem(q, in_dtype, row + j));
+                        load_phi_row(q, in_dtype, row, D, gamma_q, h, norm_eps, f);
                         double den = 0.0;
                         for (int j = 0; j < D; ++j) den += f[j] * S[j * W + D];
                         for (int c = 0; c < D; ++c) {

@@ -188,7 +188,7 @@ def extra_names(out_dtype: str) -> list:
     names = [("bf16" if out_dtype == "f32" else "f32") + "_out",
              "blockcausal_16x1024_f32out", "blockcausal_16x1024_bf16out",
              "stream_4x4096_bc1024_" + o, "fused_qkv_strided_" + o, "f16_in_" + o, "f32_in_" + o,
-             "d64_h35_" + o, "d16_h140_" + o,
+             "d64_h35_" + o, "d16_h140_" + o, "qknorm_" + o, "qknorm_blockcausal_16x1024_" + o,
              "backward_bf16", "backward_f32", "backward_d64_h35_bf16", "backward_d16_h140_bf16",
              "jvp_bf16_f32out", "jvp_f32"]
     for tag in ("sana600m_1024px", "sana1600m_1024px", "sana1600m_2048px"):
@@ -423,6 +423,20 @@ def main() -> int:
             return fn, alg_bytes, f"head dim {Dx}: the headline buffers viewed as B=1, N=16384, H={Hx}, D={Dx}"
         return build
 
+    def case_qknorm(L):
+        def build():
+            gq, gk = (torch.from_numpy(g).to(dev) for g in workloads.make_gammas(w, 3))
+            ws_q = torch.empty(sana.sana_linattn_workspace_bytes(B, H, N, D, L), dtype=torch.uint8, device=dev)
+
+            def fn(i):
+                q, k, v = sets[i % NSETS]
+                sana.sana_linattn_fwd_qknorm(q, k, v, outs[i % NSETS], ws_q, gq, gk, norm_eps=1e-6, block_len=L,
+                                             eps=w.eps, stream=torch.cuda.current_stream())
+            return fn, alg_bytes + 2 * H * D * 4, (
+                "the headline buffers with the qk_norm prologue on q and k (per-channel scales, a third "
+                "negative)" + (f", block_len {L}" if L else "") + "; algorithmic bytes add the two [H, D] scales")
+        return build
+
     def case_config(wx, cold):
         """One of the smaller Sana configurations, fp32 out.  Cold: enough input and
         output sets rotate that the working set (> 512 MB) cannot stay in the
@@ -454,6 +468,8 @@ def main() -> int:
         "f32_in_" + args.out_dtype + "out": case_in(torch.float32),
         "d64_h35_" + args.out_dtype + "out": case_headdim(H // 2, 2 * D),
         "d16_h140_" + args.out_dtype + "out": case_headdim(2 * H, D // 2),
+        "qknorm_" + args.out_dtype + "out": case_qknorm(0),
+        "qknorm_blockcausal_16x1024_" + args.out_dtype + "out": case_qknorm(workloads.BLOCK_CAUSAL.block_len),
         "backward_bf16": case_bwd(torch.bfloat16),
         "backward_f32": case_bwd(torch.float32),
         "backward_d64_h35_bf16": case_bwd(torch.bfloat16, H // 2, 2 * D),

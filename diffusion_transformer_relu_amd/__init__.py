@@ -49,6 +49,8 @@ _SIGNATURES = {
                                                  _P, _P, _P, ctypes.c_size_t, _P]),
     "sana_linattn_fwd_strided": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
                                       ctypes.POINTER(ctypes.c_int64), _P, ctypes.c_size_t, _P]),
+    "sana_linattn_fwd_qknorm": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P,
+                                     ctypes.c_float, ctypes.POINTER(ctypes.c_int64), _P, ctypes.c_size_t, _P]),
     "sana_linattn_fwd_stages": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P,
                                      ctypes.c_size_t, _P, _I]),
     "sana_linattn_bwd_workspace_bytes": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]),
@@ -147,6 +149,17 @@ def _stream_handle(stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _torch_stream(stream):
+    """The torch stream object for `stream` (None = the current stream, an int
+    = a raw hipStream_t)."""
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream)
+    return stream
+
+
 def sana_linattn_fwd(q, k, v, out, workspace, *, eps: float = 1e-15, stream=None):
     """Non-causal forward into `out` (torch tensors on the GPU; `workspace` a
     uint8 GPU tensor of at least sana_linattn_workspace_bytes bytes)."""
@@ -219,6 +232,27 @@ def sana_linattn_fwd_strided(q, k, v, out, workspace, *, block_len: int = 0, eps
            "sana_linattn_fwd_strided")
 
 
+def sana_linattn_fwd_qknorm(q, k, v, out, workspace, gamma_q=None, gamma_k=None, *, norm_eps: float = 1e-6,
+                            block_len: int = 0, eps: float = 1e-15, stream=None):
+    """Forward with the qk_norm prologue on [B, N, H, D] views (free batch and
+    token strides): gamma_q / gamma_k are contiguous float32 [H, D] GPU tensors,
+    or None for no normalisation of that side."""
+    B, N, H, D = _view_shape(q, k, v, out)
+    for name, t in (("gamma_q", gamma_q), ("gamma_k", gamma_k)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous() or t.dtype != _torch().float32
+                              or tuple(t.shape) != (H, D)):
+            raise ValueError(f"{name} must be a contiguous float32 [H, D] GPU tensor")
+    st = (ctypes.c_int64 * 8)(q.stride(0), q.stride(1), k.stride(0), k.stride(1), v.stride(0), v.stride(1),
+                              out.stride(0), out.stride(1))
+    _check(lib.sana_linattn_fwd_qknorm(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dtype_code(q),
+                                       dtype_code(out), B, H, N, D, block_len, eps,
+                                       gamma_q.data_ptr() if gamma_q is not None else None,
+                                       gamma_k.data_ptr() if gamma_k is not None else None, norm_eps, st,
+                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                       _stream_handle(stream)),
+           "sana_linattn_fwd_qknorm")
+
+
 def sana_linattn_fwd_stages(q, k, v, out, workspace, stages: int, *, block_len: int = 0,
                             eps: float = 1e-15, stream=None):
     """Runs the selected kernels (SANA_STAGE_* bits) of the forward."""
@@ -231,20 +265,27 @@ def sana_linattn_fwd_stages(q, k, v, out, workspace, stages: int, *, block_len: 
 
 
 def linattn_fwd(q, k, v, *, eps: float = 1e-15, out_dtype=None, block_len: int | None = None,
-                stream=None):
+                gamma_q=None, gamma_k=None, norm_eps: float = 1e-6, stream=None):
     """Allocates `out` (float32 unless out_dtype is given) and the workspace with
-    torch, then runs the non-causal (block_len None) or block-causal forward."""
+    torch, then runs the non-causal (block_len None) or block-causal forward,
+    with the qk_norm prologue when gamma_q or gamma_k is given.  Both buffers
+    are allocated on the stream the kernels run on."""
     torch = _torch()
-    out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
-    B, N, H, D = q.shape
-    ws = torch.empty(max(sana_linattn_workspace_bytes(B, H, N, D, block_len or 0), 1),
-                     dtype=torch.uint8, device=q.device)
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        sana_linattn_fwd_strided(q, k, v, out, ws, block_len=block_len or 0, eps=eps, stream=stream)
-    elif block_len is None:
-        sana_linattn_fwd(q, k, v, out, ws, eps=eps, stream=stream)
-    else:
-        sana_linattn_blockcausal_fwd(q, k, v, out, ws, block_len, eps=eps, stream=stream)
+    s = _torch_stream(stream)
+    with torch.cuda.stream(s):
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+        B, N, H, D = q.shape
+        ws = torch.empty(max(sana_linattn_workspace_bytes(B, H, N, D, block_len or 0), 1),
+                         dtype=torch.uint8, device=q.device)
+        if gamma_q is not None or gamma_k is not None:
+            sana_linattn_fwd_qknorm(q, k, v, out, ws, gamma_q, gamma_k, norm_eps=norm_eps,
+                                    block_len=block_len or 0, eps=eps, stream=s)
+        elif not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+            sana_linattn_fwd_strided(q, k, v, out, ws, block_len=block_len or 0, eps=eps, stream=s)
+        elif block_len is None:
+            sana_linattn_fwd(q, k, v, out, ws, eps=eps, stream=s)
+        else:
+            sana_linattn_blockcausal_fwd(q, k, v, out, ws, block_len, eps=eps, stream=s)
     return out
 
 
@@ -276,12 +317,14 @@ def linattn_bwd(q, k, v, dout, *, eps: float = 1e-15, grad_dtype=None, block_len
     """Allocates dq, dk, dv (q's dtype unless grad_dtype is given) and the
     workspace with torch, runs the backward and returns (dq, dk, dv)."""
     torch = _torch()
-    gt = grad_dtype or q.dtype
-    dq, dk, dv = (torch.empty(q.shape, dtype=gt, device=q.device) for _ in range(3))
-    B, N, H, D = q.shape
-    ws = torch.empty(max(sana_linattn_bwd_workspace_bytes(B, H, N, D, block_len or 0), 1), dtype=torch.uint8,
-                     device=q.device)
-    sana_linattn_bwd(q, k, v, dout, dq, dk, dv, ws, block_len=block_len or 0, eps=eps, stream=stream)
+    s = _torch_stream(stream)
+    with torch.cuda.stream(s):   # allocated on the stream the kernels run on
+        gt = grad_dtype or q.dtype
+        dq, dk, dv = (torch.empty(q.shape, dtype=gt, device=q.device) for _ in range(3))
+        B, N, H, D = q.shape
+        ws = torch.empty(max(sana_linattn_bwd_workspace_bytes(B, H, N, D, block_len or 0), 1),
+                         dtype=torch.uint8, device=q.device)
+        sana_linattn_bwd(q, k, v, dout, dq, dk, dv, ws, block_len=block_len or 0, eps=eps, stream=s)
     return dq, dk, dv
 
 
@@ -313,11 +356,13 @@ def linattn_jvp(q, k, v, q_t, k_t, v_t, *, eps: float = 1e-15, out_dtype=None, b
     """Allocates out, out_t (float32 unless out_dtype is given) and the
     workspace with torch and returns (out, out_t)."""
     torch = _torch()
-    ot = out_dtype or torch.float32
-    out = torch.empty(q.shape, dtype=ot, device=q.device)
-    out_t = torch.empty(q.shape, dtype=ot, device=q.device)
-    B, N, H, D = q.shape
-    ws = torch.empty(max(sana_linattn_jvp_workspace_bytes(B, H, N, D, block_len or 0), 1), dtype=torch.uint8,
-                     device=q.device)
-    sana_linattn_jvp(q, k, v, q_t, k_t, v_t, out, out_t, ws, block_len=block_len or 0, eps=eps, stream=stream)
+    s = _torch_stream(stream)
+    with torch.cuda.stream(s):   # allocated on the stream the kernels run on
+        ot = out_dtype or torch.float32
+        out = torch.empty(q.shape, dtype=ot, device=q.device)
+        out_t = torch.empty(q.shape, dtype=ot, device=q.device)
+        B, N, H, D = q.shape
+        ws = torch.empty(max(sana_linattn_jvp_workspace_bytes(B, H, N, D, block_len or 0), 1),
+                         dtype=torch.uint8, device=q.device)
+        sana_linattn_jvp(q, k, v, q_t, k_t, v_t, out, out_t, ws, block_len=block_len or 0, eps=eps, stream=s)
     return out, out_t

@@ -39,8 +39,10 @@ long round_up(long a, long m) { return (a + m - 1) / m * m; }
 
 // Decomposition of one call.  Sizes were range-checked by the caller.
 // allow_mfma = false gives the vector path's plan (for workspace queries).
+// split_state: the keys take the split-term state kernel whatever their type
+// (qk_norm), which holds 3 work-groups per CU like the fp32 one.
 int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block_len, Plan* pl,
-              bool allow_mfma = true) {
+              bool allow_mfma = true, bool split_state = false) {
     if (B < 0 || H < 0 || N < 0 || D < 1 || block_len < 0) return SANA_ERR_INVALID_ARG;
     if ((in_dtype != SANA_DT_F32 && in_dtype != SANA_DT_BF16 && in_dtype != SANA_DT_F16) ||
         (out_dtype != SANA_DT_F32 && out_dtype != SANA_DT_BF16 && out_dtype != SANA_DT_F16))
@@ -76,7 +78,7 @@ int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block
     } else {
         // fp32 inputs on the matrix cores: their state kernel holds 3 work-
         // groups per CU and streams best with one full round of them
-        const long slots = (pl->mfma && in_dtype == SANA_DT_F32) ? sana::kCUs * 3 : sana::kStateGroups;
+        const long slots = (pl->mfma && (in_dtype == SANA_DT_F32 || split_state)) ? sana::kCUs * 3 : sana::kStateGroups;
         const long per_block = std::max<long>(1, slots / units);
         chunk = (int)std::max<long>(round_up(ceil_div(pl->L, per_block), 64), sana::kMinChunk);
     }
@@ -147,11 +149,16 @@ int forward(const void* q, const void* k, const void* v, void* out, int in_dtype
             int B, int H, int N, int D, int block_len, float eps, void* workspace,
             size_t workspace_bytes, hipStream_t stream, int stages,
             const float* state_in = nullptr, float* state_out = nullptr,
-            const int64_t* strides = nullptr) {
+            const int64_t* strides = nullptr, const float* gamma_q = nullptr, const float* gamma_k = nullptr,
+            float norm_eps = 0.f) {
     Plan pl;
-    const int st = make_plan(in_dtype, out_dtype, B, H, N, D, block_len, &pl);
+    const int st = make_plan(in_dtype, out_dtype, B, H, N, D, block_len, &pl, true, gamma_k != nullptr);
     if (st != SANA_OK) return st;
     if (!std::isfinite(eps) || eps < 0.f) return SANA_ERR_INVALID_ARG;
+    if ((gamma_q || gamma_k) && !(std::isfinite(norm_eps) && norm_eps > 0.f)) return SANA_ERR_INVALID_ARG;
+    pl.gq = gamma_q;
+    pl.gk = gamma_k;
+    pl.norm_eps = norm_eps;
     if (stages <= 0 || (stages & ~SANA_STAGE_ALL)) return SANA_ERR_INVALID_ARG;
     const size_t es_in = in_dtype == SANA_DT_F32 ? 4 : 2;
     const size_t es_out = out_dtype == SANA_DT_F32 ? 4 : 2;
@@ -193,6 +200,14 @@ int forward(const void* q, const void* k, const void* v, void* out, int in_dtype
                           overlaps(state_out, sb, workspace, pl.bytes) ||
                           (state_in && state_in != state_out && overlaps(state_out, sb, state_in, sb))))
             return SANA_ERR_ALIAS;
+    }
+    if (gamma_q || gamma_k) {
+        const size_t gb = (size_t)H * D * sizeof(float);
+        for (const float* gp : {gamma_q, gamma_k}) {
+            if (!gp) continue;
+            if (!aligned(gp, 4)) return SANA_ERR_ALIGNMENT;
+            if (overlaps(gp, gb, out, out_bytes) || overlaps(gp, gb, workspace, pl.bytes)) return SANA_ERR_ALIAS;
+        }
     }
     if (workspace_bytes < pl.bytes) return SANA_ERR_WORKSPACE;
 
@@ -523,6 +538,15 @@ int sana_linattn_fwd_strided(const void* q, const void* k, const void* v, void* 
     if (!strides || block_len < 0) return SANA_ERR_INVALID_ARG;
     return forward(q, k, v, out, in_dtype, out_dtype, B, H, N, D, block_len, eps, workspace,
                    workspace_bytes, stream, SANA_STAGE_ALL, nullptr, nullptr, strides);
+}
+
+int sana_linattn_fwd_qknorm(const void* q, const void* k, const void* v, void* out, int in_dtype, int out_dtype,
+                            int B, int H, int N, int D, int block_len, float eps, const float* gamma_q,
+                            const float* gamma_k, float norm_eps, const int64_t* strides, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    if (block_len < 0) return SANA_ERR_INVALID_ARG;
+    return forward(q, k, v, out, in_dtype, out_dtype, B, H, N, D, block_len, eps, workspace, workspace_bytes,
+                   stream, SANA_STAGE_ALL, nullptr, nullptr, strides, gamma_q, gamma_k, norm_eps);
 }
 
 int sana_linattn_fwd_stages(const void* q, const void* k, const void* v, void* out, int in_dtype,

@@ -186,7 +186,7 @@ template <int HD> struct KSteps { static constexpr int value = HD == 2 * kD ? 4 
 //            matrix: K-step ks is nonzero in rows 16 ks .. 16 ks + 15 only.
 template <int HD, typename HeadState>
 __device__ __forceinline__ void state_operands(HeadState head, int grp, int half, int HR, int lane, bool transposed,
-                                               u32x4 (&out)[KSteps<HD>::value][3]) {
+                                               u32x4 (&out)[KSteps<HD>::value][3], const float* kkscale = nullptr) {
     constexpr int KS = KSteps<HD>::value, SW = HD + 1;
     const int g = lane >> 5, i = lane & 31;
 #pragma unroll
@@ -200,6 +200,7 @@ __device__ __forceinline__ void state_operands(HeadState head, int grp, int half
             for (int e = 0; e < 8; ++e) {
                 const int kk = 8 * g + e, r = i & 15;
                 x[e] = on ? (transposed ? S[kk * SW + r] : S[r * SW + kk]) : 0.f;
+                if (kkscale) x[e] *= fabsf(kkscale[min(hr, HR - 1) * HD + kk]);
             }
         } else {
             const float* S = head(grp);
@@ -208,6 +209,7 @@ __device__ __forceinline__ void state_operands(HeadState head, int grp, int half
             for (int e = 0; e < 8; ++e) {
                 const int kk = 16 * ks + 8 * g + e;
                 x[e] = transposed ? S[kk * SW + ri] : S[ri * SW + kk];
+                if (kkscale) x[e] *= fabsf(kkscale[grp * HD + kk]);
             }
         }
         split3_f32x8(x, out[ks]);
@@ -217,13 +219,16 @@ __device__ __forceinline__ void state_operands(HeadState head, int grp, int half
 // The apply kernels' operands of out^T = S^T f^T (state_operands, transposed)
 // and the normaliser entries at this lane's features: z[8 ks + e] =
 // S[16 ks + 8 g + e][HD] (HD = 16: of head 2 grp + ks, zero when there is none).
+// With qscale (qk_norm: the per-channel scales of q, [HR][HD]) every entry of
+// feature kk is multiplied by |qscale[head][kk]|, which moves the magnitude of
+// the scale from the query onto the state.
 template <int HD, typename HeadState>
 __device__ __forceinline__ void apply_operands(HeadState head, int grp, int half, int HR, int lane,
                                                u32x4 (&sa)[KSteps<HD>::value][3],
-                                               float (&z)[8 * KSteps<HD>::value]) {
+                                               float (&z)[8 * KSteps<HD>::value], const float* qscale = nullptr) {
     constexpr int KS = KSteps<HD>::value, SW = HD + 1;
     const int g = lane >> 5;
-    state_operands<HD>(head, grp, half, HR, lane, true, sa);
+    state_operands<HD>(head, grp, half, HR, lane, true, sa, qscale);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -231,8 +236,10 @@ __device__ __forceinline__ void apply_operands(HeadState head, int grp, int half
             if constexpr (HD == kD / 2) {
                 const int hr = 2 * grp + ks;
                 z[8 * ks + e] = hr < HR ? head(hr)[(8 * g + e) * SW + HD] : 0.f;
+                if (qscale && hr < HR) z[8 * ks + e] *= fabsf(qscale[hr * HD + 8 * g + e]);
             } else {
                 z[8 * ks + e] = head(grp)[(16 * ks + 8 * g + e) * SW + HD];
+                if (qscale) z[8 * ks + e] *= fabsf(qscale[grp * HD + 16 * ks + 8 * g + e]);
             }
         }
 }

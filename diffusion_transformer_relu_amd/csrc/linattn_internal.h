@@ -52,6 +52,11 @@ struct Plan {
     int mfma16;   // 1: mfma with 16-bit inputs
     int D;        // head dim: 16, 32 or 64
     int in_dtype, out_dtype;
+    // qk_norm prologue: per-channel scales [H][D] of q and k (device fp32, or
+    // nullptr for none) and the constant under the root
+    const float* gq;
+    const float* gk;
+    float norm_eps;
     size_t off_part, off_state, bytes;
     Strides sq, sk, sv, so;   // element strides of q, k, v, out
 };

@@ -231,10 +231,67 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma(
 // diagonal blocks of each group are kept).
 constexpr int kF32Tile = 64 * kD;   // 16-bit elements of one term tile [token][feature] of one head
 
-template <int HD>
+// The same kernel serves the qk_norm prologue (QK) for every input type: a key
+// row of head h becomes r_n ReLU(sign(gamma_k) k_n), r_n = 1 / sqrt(mean(k_n^2) +
+// norm_eps) over the head's HD features, formed in fp32 and split into three
+// terms like an fp32 input (the merge multiplies row j of the state by
+// |gamma_k[h][j]|, which completes phi(gamma_k k_n r_n)).  16-bit values are
+// exact as bf16 terms (a bf16 value is one term, an fp16 value two), so only
+// the products with nonzero terms of V are formed.
+template <typename InT> struct Piece;   // 8 consecutive features of one token row
+template <> struct Piece<float> {
+    f32x4 x[2];
+    __device__ __forceinline__ void load(const float* p) {
+        x[0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+        x[1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1);
+    }
+    __device__ __forceinline__ void zero() { x[0] = x[1] = (f32x4){0.f, 0.f, 0.f, 0.f}; }
+    __device__ __forceinline__ void get(float f[8]) const {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[e] = x[0][e];
+            f[4 + e] = x[1][e];
+        }
+    }
+};
+template <> struct Piece<uint16_t> {
+    u32x4 x;
+    __device__ __forceinline__ void load(const uint16_t* p) {
+        x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    }
+    __device__ __forceinline__ void zero() { x = (u32x4){0u, 0u, 0u, 0u}; }
+    __device__ __forceinline__ void get(float f[8]) const {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t w = x[d];
+            f[2 * d] = lo_bf16(w);
+            f[2 * d + 1] = hi_bf16(w);
+        }
+    }
+};
+template <> struct Piece<_Float16> {
+    u32x4 x;
+    __device__ __forceinline__ void load(const _Float16* p) {
+        x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    }
+    __device__ __forceinline__ void zero() { x = (u32x4){0u, 0u, 0u, 0u}; }
+    __device__ __forceinline__ void get(float f[8]) const {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t w = x[d];
+            f[2 * d] = f16_to_f32((uint16_t)(w & 0xffffu));
+            f[2 * d + 1] = f16_to_f32((uint16_t)(w >> 16));
+        }
+    }
+};
+
+template <int HD, typename InT = float, bool QK = false>
 __global__ __launch_bounds__(kThreads) void k_state_partial_mfma_f32(
-    const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ part,
-    int N, int H, int HP, int HR, int L, int cpb, int P, int chunk, Strides sk, Strides sv) {
+    const InT* __restrict__ k, const InT* __restrict__ v, float* __restrict__ part,
+    int N, int H, int HP, int HR, int L, int cpb, int P, int chunk, Strides sk, Strides sv,
+    const float* __restrict__ gk, float norm_eps) {
+    // terms of a V value: bf16 1, fp16 2 (8 + 3 significant bits), fp32 3
+    constexpr int VT = std::is_same<InT, uint16_t>::value ? 1 : std::is_same<InT, _Float16>::value ? 2 : 3;
     __shared__ __attribute__((aligned(16))) uint16_t lds[2][3][2][kF32Tile];   // [tensor][term][head] = 48 KB
 
     const int p = blockIdx.x % P;
@@ -249,27 +306,43 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma_f32(
     const int g = lane >> 5, j = lane & 31;
 
     // piece pc = tid + 256 i: part (pc & 3) = features 8 part .. + 7, head
-    // (pc >> 2) & 1, token pc >> 3
-    f32x4 rk[2][2], rv[2][2];
+    // (pc >> 2) & 1, token pc >> 3; a thread's part and group are the same for
+    // both of its pieces
+    const int part0 = tid & 3, grp0 = (tid >> 2) & 1;
+    Piece<InT> rk[2], rv[2];
     auto load_tile = [&](int t0) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int pc = tid + kThreads * i;
-            const int part_ = pc & 3, hd = (pc >> 2) & 1, tok = pc >> 3;
+            const int tok = (tid >> 3) + 32 * i;
             const int n = t0 + tok;
-            const int col = (h0 + hd) * kD + part_ * 8;
+            const int col = (h0 + grp0) * kD + part0 * 8;
             if (n < cr.c1 && col < HR * HD) {
-                const f32x4* ks = reinterpret_cast<const f32x4*>(k + (b * sk.b + n * sk.n + col));
-                const f32x4* vs = reinterpret_cast<const f32x4*>(v + (b * sv.b + n * sv.n + col));
-                rk[i][0] = __builtin_nontemporal_load(ks);
-                rk[i][1] = __builtin_nontemporal_load(ks + 1);
-                rv[i][0] = __builtin_nontemporal_load(vs);
-                rv[i][1] = __builtin_nontemporal_load(vs + 1);
+                rk[i].load(k + (b * sk.b + n * sk.n + col));
+                rv[i].load(v + (b * sv.b + n * sv.n + col));
             } else {
-                rk[i][0] = rk[i][1] = rv[i][0] = rv[i][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                rk[i].zero();
+                rv[i].zero();
             }
         }
     };
+    // qk_norm: the sign of gamma_k at this thread's 8 features, as sign bits
+    uint32_t kneg = 0;
+    if constexpr (QK) {
+        int head, f0;   // the head and first feature this thread's pieces belong to
+        if constexpr (HD == 2 * kD) {
+            head = hp;
+            f0 = kD * grp0 + 8 * part0;
+        } else if constexpr (HD == kD) {
+            head = h0 + grp0;
+            f0 = 8 * part0;
+        } else {
+            head = 2 * (h0 + grp0) + (part0 >> 1);
+            f0 = 8 * (part0 & 1);
+        }
+        if (head < HR)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kneg |= (uint32_t)(gk[head * HD + f0 + e] < 0.f) << e;
+    }
 
     f32x16 accV = {}, accO = {};
     const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0 pairs
@@ -279,24 +352,37 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma_f32(
         __syncthreads();   // the previous tile has been consumed
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int pc = tid + kThreads * i;
-            const int part_ = pc & 3, hd = (pc >> 2) & 1, tok = pc >> 3;
+            const int tok = (tid >> 3) + 32 * i;
             float a[8], w[8];
+            rk[i].get(a);
+            rv[i].get(w);
+            if constexpr (QK) {
+                // r_n over the head's features: 4 threads hold a 32-feature
+                // group row, 8 (both groups) a head of 64, 2 a head of 16
+                float ss = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                a[e] = relu_f32(rk[i][0][e]);
-                a[4 + e] = relu_f32(rk[i][1][e]);
-                w[e] = rv[i][0][e];
-                w[4 + e] = rv[i][1][e];
+                for (int e = 0; e < 8; ++e) ss = fmaf(a[e], a[e], ss);
+                ss += __shfl_xor(ss, 1);
+                if constexpr (HD >= kD) ss += __shfl_xor(ss, 2);
+                if constexpr (HD == 2 * kD) ss += __shfl_xor(ss, 4);
+                const float r = 1.0f / sqrtf(ss * (1.0f / HD) + norm_eps);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t bits = __builtin_bit_cast(uint32_t, a[e]) ^ (((kneg >> e) & 1u) << 31);
+                    a[e] = r * relu_f32(__builtin_bit_cast(float, bits));
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a[e] = relu_f32(a[e]);
             }
             u32x4 ta[3], tv[3];
             split3_trunc_f32x8(a, ta);
             split3_trunc_f32x8(w, tv);
-            const int o = tok * kD + part_ * 8;
+            const int o = tok * kD + part0 * 8;
 #pragma unroll
             for (int t = 0; t < 3; ++t) {
-                *reinterpret_cast<u32x4*>(&lds[0][t][hd][o]) = ta[t];
-                *reinterpret_cast<u32x4*>(&lds[1][t][hd][o]) = tv[t];
+                *reinterpret_cast<u32x4*>(&lds[0][t][grp0][o]) = ta[t];
+                if (t < VT) *reinterpret_cast<u32x4*>(&lds[1][t][grp0][o]) = tv[t];
             }
         }
         __syncthreads();
@@ -310,14 +396,14 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma_f32(
 #pragma unroll
             for (int t = 0; t < 3; ++t) {
                 ta[t] = gather_tokens_t16(lds[0][t][hh], kD, tb, 0, lane);   // lane (g, j): tokens tb + 8g + e, feature j
-                tv[t] = gather_tokens_t16(lds[1][t][D64 ? th : hh], kD, tb, 0, lane);   // lane (g, c): tokens tb + 8g + e, channel c
+                if (t < VT) tv[t] = gather_tokens_t16(lds[1][t][D64 ? th : hh], kD, tb, 0, lane);   // lane (g, c): tokens tb + 8g + e, channel c
             }
-            // smallest products first
+            // term pairs with i + j <= 2, smallest products first
             accV = mfma_bf16(ta[2], tv[0], accV);
-            accV = mfma_bf16(ta[1], tv[1], accV);
-            accV = mfma_bf16(ta[0], tv[2], accV);
+            if constexpr (VT > 1) accV = mfma_bf16(ta[1], tv[1], accV);
+            if constexpr (VT > 2) accV = mfma_bf16(ta[0], tv[2], accV);
             accV = mfma_bf16(ta[1], tv[0], accV);
-            accV = mfma_bf16(ta[0], tv[1], accV);
+            if constexpr (VT > 1) accV = mfma_bf16(ta[0], tv[1], accV);
             accV = mfma_bf16(ta[0], tv[0], accV);
             if (!D64 || th == 0) {
                 accO = mfma_bf16(ta[2], ones, accO);
@@ -369,13 +455,17 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma_f32(
 // ------------------------------------------------------------------ state, vector path
 // grid.x = (b * H + h) * P + p.  Thread t owns state entries t, t+256, ...
 // Head dim DD (16, 32 or 64): a state is DD x (DD + 1).
+// With gk (qk_norm) each key row is RMS-normalised over its DD features,
+// scaled by gamma_k and passed through ReLU here, straight from the definition.
 template <typename InT, int DD>
 __global__ __launch_bounds__(kThreads) void k_state_partial_valu(
     const InT* __restrict__ k, const InT* __restrict__ v, float* __restrict__ part,
-    int N, int H, int L, int cpb, int P, int chunk, Strides stk, Strides stv) {
+    int N, int H, int L, int cpb, int P, int chunk, Strides stk, Strides stv, const float* __restrict__ gk,
+    float norm_eps) {
     constexpr int WW = DD + 1, SF = DD * WW, M = (SF + kThreads - 1) / kThreads;
     __shared__ float sa[kValuTile][DD + 1];   // ReLU(k) tile
     __shared__ float sv[kValuTile][WW];       // [v | 1] tile
+    __shared__ float rr[kValuTile];           // qk_norm: 1 / rms of each key row
 
     const int p = blockIdx.x % P;
     const int bh = blockIdx.x / P;
@@ -395,11 +485,25 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_valu(
                 kk = load_in(k, b * stk.b + n * stk.n + col);
                 vv = load_in(v, b * stv.b + n * stv.n + col);
             }
-            sa[tok][jj] = kk > 0.f ? kk : 0.f;
+            sa[tok][jj] = gk ? kk : (kk > 0.f ? kk : 0.f);
             sv[tok][jj] = vv;
         }
         if (tid < kValuTile) sv[tid][DD] = 1.f;
         __syncthreads();
+        if (gk) {
+            if (tid < kValuTile) {
+                float ss = 0.f;
+                for (int jj = 0; jj < DD; ++jj) ss += sa[tid][jj] * sa[tid][jj];
+                rr[tid] = 1.0f / sqrtf(ss / DD + norm_eps);
+            }
+            __syncthreads();
+            for (int e = tid; e < kValuTile * DD; e += kThreads) {
+                const int tok = e / DD, jj = e % DD;
+                const float x = gk[h * DD + jj] * sa[tok][jj] * rr[tok];
+                sa[tok][jj] = x > 0.f ? x : 0.f;
+            }
+            __syncthreads();
+        }
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             const int o = tid + kThreads * m;
@@ -435,11 +539,14 @@ __device__ __forceinline__ float tree8(const float* x) {
 
 __global__ __launch_bounds__(kMergeThreads) void k_merge(
     const float* __restrict__ part, float* __restrict__ state, const float* state_in, float* state_out,
-    int NB, int cpb, int P, int SF) {
+    int NB, int cpb, int P, int SF, const float* __restrict__ gk, int H, int D) {
     const int groups = (SF + kMergeThreads - 1) / kMergeThreads;
     const size_t bh = blockIdx.x / groups;
     const int e = (blockIdx.x % groups) * kMergeThreads + threadIdx.x;
     if (e >= SF) return;
+    // qk_norm: the partials hold sum_n r_n ReLU(sign(gamma_k) k_n) [v_n | 1];
+    // row j of the state is that times |gamma_k[h][j]|
+    const float gscale = gk ? fabsf(gk[(bh % H) * D + e / (D + 1)]) : 1.f;
     const float* src = part + bh * P * SF + e;
     float* dst = state + bh * NB * SF + e;
     float acc = state_in ? state_in[bh * SF + e] : 0.f;
@@ -457,7 +564,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 if (b0 + i < NB) {
-                    acc += 0.f + x[i];   // the block sum of one partial, as the general path forms it
+                    acc += gscale * (0.f + x[i]);   // the block sum of one partial, as the general path forms it
                     dst[(size_t)(b0 + i) * SF] = acc;
                 }
             }
@@ -481,7 +588,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(
                 bs += tree8(x);
                 if (s0 + 8 < cpb) bs += tree8(x + 8);
             }
-            acc += bs;
+            acc += gscale * bs;
             dst[(size_t)beta * SF] = acc;
         }
     }
@@ -520,10 +627,17 @@ constexpr int kOutPitch = 36;   // floats per LDS output row: 32 + 4 keeps rows 
 //    32 x 32 matrix of their two states (zero off the diagonal blocks), so the
 //    product gives both heads' numerators, and each head takes its own
 //    normaliser (K-step 0 is the first head's features, 1 the second's).
-template <typename InT, typename OutT, int HD>
+//
+// qk_norm (QK): phi(gamma_q q_i rho_i), rho_i = 1 / rms of the head's row of
+// q_i, equals rho_i |gamma_q| ReLU(sign(gamma_q) q_i); |gamma_q| goes onto the
+// rows of S when its operands are built, the sign flip is exact on the bits,
+// and rho_i cancels between numerator and normaliser except against eps, so
+// the normaliser becomes den + eps * rms_i (rms_i from the same registers).
+template <typename InT, typename OutT, int HD, bool QK = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 2 * kD ? (std::is_same<InT, float>::value ? 2 : 3) : std::is_same<InT, uint16_t>::value ? 5 : 4, 8))) void k_apply_mfma(
     const InT* __restrict__ q, const float* __restrict__ state, OutT* __restrict__ out,
-    int N, int H, int HP, int HR, int L, int NB, int tile, int tpb, float eps, Strides sq, Strides so) {
+    int N, int H, int HP, int HR, int L, int NB, int tile, int tpb, float eps, Strides sq, Strides so,
+    const float* __restrict__ gq, float norm_eps) {
     constexpr bool F16 = std::is_same<InT, _Float16>::value;
     constexpr bool F32 = std::is_same<InT, float>::value;
     constexpr bool D64 = HD == 2 * kD, D16 = HD == kD / 2;
@@ -554,7 +668,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 
     auto head_state = [&](int hr) { return state + (((size_t)b * HR + hr) * NB + beta) * SF; };
     u32x4 sa[KS][3];
     float sden[8 * KS];
-    apply_operands<HD>(head_state, D64 ? hp : hs, hh, HR, lane, sa, sden);
+    apply_operands<HD>(head_state, D64 ? hp : hs, hh, HR, lane, sa, sden, QK ? gq : nullptr);
+    // qk_norm: sign bits of gamma_q at this lane's features 16 ks + 8 g + e
+    // (head dim 16: K-step ks is head 2 hs + ks, features 8 g + e)
+    uint32_t qneg[KS] = {};
+    if constexpr (QK) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int hr = D64 ? hp : D16 ? 2 * hs + ks : hs;
+            const int f0 = D16 ? 8 * g : 16 * ks + 8 * g;
+            if (hr < HR)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qneg[ks] |= (uint32_t)(gq[hr * HD + f0 + e] < 0.f) << e;
+        }
+    }
+    // the same as 16-bit sign bits of a packed operand
+    auto neg16 = [&](int ks) {
+        u32x4 m;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) m[d] = (((qneg[ks] >> (2 * d)) & 1u) << 15) | (((qneg[ks] >> (2 * d + 1)) & 1u) << 31);
+        return m;
+    };
 
     // fp32 out: rows past the range read as zero and are not stored.  16-bit
     // out: they are clamped to the range's last row, so every load is
@@ -598,6 +732,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 
     auto compute = [&](const QRow& qr) -> f32x16 {
         f32x16 acc = {};
         float dp = 0.f, dp1 = 0.f;   // dp1: head dim 16, the group's second head
+        float ss = 0.f, ss1 = 0.f;   // qk_norm: sums of squares of the row (ss1: second head of dim 16)
         if constexpr (F32) {
             // f = ReLU(q) in fp32 (features 16 ks + 8 g + e at f[8 ks + e])
             float f[8 * KS];
@@ -607,7 +742,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 
                 for (int e = 0; e < 4; ++e) {
                     // through a scalar: bit_cast of a vector element expression
                     // reads the vector's first element with this compiler
-                    const uint32_t bits = qr.x[c][e];
+                    uint32_t bits = qr.x[c][e];
+                    if constexpr (QK) {
+                        const float x = __builtin_bit_cast(float, bits);
+                        float& t = (D16 && c >= 2) ? ss1 : ss;
+                        t = fmaf(x, x, t);
+                        bits ^= ((qneg[c >> 1] >> (4 * (c & 1) + e)) & 1u) << 31;
+                    }
                     f[4 * c + e] = relu_f32(__builtin_bit_cast(float, bits));
                 }
 #pragma unroll
@@ -632,7 +773,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 
             // normaliser takes the fp32 values as they are split
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 x = relu_bf16x8(qr.x[ks]);   // the sign test is the same for fp16
+                if constexpr (QK) {
+                    float& t = (D16 && ks == 1) ? ss1 : ss;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const uint32_t w = qr.x[ks][d];
+                        const float x0 = f16_to_f32((uint16_t)(w & 0xffffu)), x1 = f16_to_f32((uint16_t)(w >> 16));
+                        t = fmaf(x0, x0, t);
+                        t = fmaf(x1, x1, t);
+                    }
+                }
+                const u32x4 x = relu_bf16x8(QK ? (qr.x[ks] ^ neg16(ks)) : qr.x[ks]);   // the sign test is the same for fp16
                 u32x4 hi, lo;
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
@@ -653,7 +804,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 
         } else {
             u32x4 a[KS];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) a[ks] = relu_bf16x8(qr.x[ks]);
+            for (int ks = 0; ks < KS; ++ks) {
+                if constexpr (QK) {
+                    float& t = (D16 && ks == 1) ? ss1 : ss;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const uint32_t w = qr.x[ks][d];
+                        t = fmaf(lo_bf16(w), lo_bf16(w), t);
+                        t = fmaf(hi_bf16(w), hi_bf16(w), t);
+                    }
+                }
+                a[ks] = relu_bf16x8(QK ? (qr.x[ks] ^ neg16(ks)) : qr.x[ks]);
+            }
 #pragma unroll
             for (int sp = 2; sp >= 0; --sp)   // small split terms first
 #pragma unroll
@@ -668,11 +830,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 
                 }
         }
         const float den = dp + __shfl_xor(dp, 32);   // same sum on lanes i and i + 32
-        const float rinv = 1.0f / (den + eps);
+        // qk_norm: eps meets the normaliser divided by rho_i, i.e. eps * rms_i
+        float epsq = eps, epsq1 = eps;
+        if constexpr (QK) {
+            epsq = eps * sqrtf((ss + __shfl_xor(ss, 32)) * (1.0f / HD) + norm_eps);
+            if constexpr (D16) epsq1 = eps * sqrtf((ss1 + __shfl_xor(ss1, 32)) * (1.0f / HD) + norm_eps);
+        }
+        const float rinv = 1.0f / (den + epsq);
         if constexpr (D16) {
             // rows 0..15 (r < 8) are the first head's outputs, 16..31 the second's
             const float den1 = dp1 + __shfl_xor(dp1, 32);
-            const float rinv1 = 1.0f / (den1 + eps);
+            const float rinv1 = 1.0f / (den1 + epsq1);
 #pragma unroll
             for (int rg = 0; rg < 16; ++rg) acc[rg] *= rg < 8 ? rinv : rinv1;
         } else {
@@ -744,7 +912,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 
 template <typename InT, typename OutT, int DD>
 __global__ __launch_bounds__(kThreads) void k_apply_valu(
     const InT* __restrict__ q, const float* __restrict__ state, OutT* __restrict__ out,
-    int N, int H, int L, int NB, int tpb, float eps, Strides sq, Strides so) {
+    int N, int H, int L, int NB, int tpb, float eps, Strides sq, Strides so, const float* __restrict__ gq,
+    float norm_eps) {
     constexpr int WW = DD + 1, SF = DD * WW;
     __shared__ float s[SF];
     const int tile = blockIdx.x % tpb;
@@ -762,10 +931,17 @@ __global__ __launch_bounds__(kThreads) void k_apply_valu(
     const long long obase = b * so.b + row * so.n + (long long)h * DD;
     float f[DD];
 #pragma unroll
-    for (int jj = 0; jj < DD; ++jj) {
-        const float x = load_in(q, qbase + jj);
-        f[jj] = x > 0.f ? x : 0.f;
+    for (int jj = 0; jj < DD; ++jj) f[jj] = load_in(q, qbase + jj);
+    if (gq) {   // qk_norm, from the definition
+        float ss = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < DD; ++jj) ss += f[jj] * f[jj];
+        const float r = 1.0f / sqrtf(ss / DD + norm_eps);
+#pragma unroll
+        for (int jj = 0; jj < DD; ++jj) f[jj] = gq[h * DD + jj] * f[jj] * r;
     }
+#pragma unroll
+    for (int jj = 0; jj < DD; ++jj) f[jj] = f[jj] > 0.f ? f[jj] : 0.f;
     float den = 0.f;
 #pragma unroll
     for (int jj = 0; jj < DD; ++jj) den += f[jj] * s[jj * WW + DD];
@@ -801,12 +977,23 @@ hipError_t launch_state(const Plan& pl, const void* k, const void* v, float* par
     const uint16_t* v16 = static_cast<const uint16_t*>(v);
     if (pl.mfma) {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.P);
-        if (pl.in_dtype == 0)
+        if (pl.gk)   // qk_norm on the keys: every input type takes the split-term kernel
+            by_dtype(pl.in_dtype, [&](auto in) {
+                using IT = typename decltype(in)::type;
+                by_head_dim(pl.D, [&](auto dd) {
+                    constexpr int DD = decltype(dd)::value;
+                    hipLaunchKernelGGL((k_state_partial_mfma_f32<DD, IT, true>), dim3(grid), dim3(kThreads), 0, stream,
+                                       static_cast<const IT*>(k), static_cast<const IT*>(v), part, pl.N, groups32(pl),
+                                       pl.HP, pl.H, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv, pl.gk, pl.norm_eps);
+                });
+            });
+        else if (pl.in_dtype == 0)
             by_head_dim(pl.D, [&](auto dd) {
                 constexpr int DD = decltype(dd)::value;
                 hipLaunchKernelGGL(k_state_partial_mfma_f32<DD>, dim3(grid), dim3(kThreads), 0, stream,
                                    static_cast<const float*>(k), static_cast<const float*>(v), part, pl.N,
-                                   groups32(pl), pl.HP, pl.H, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
+                                   groups32(pl), pl.HP, pl.H, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv,
+                                   (const float*)nullptr, 0.f);
             });
         else
             by_head_dim(pl.D, [&](auto dd) {
@@ -823,7 +1010,7 @@ hipError_t launch_state(const Plan& pl, const void* k, const void* v, float* par
                 constexpr int DD = decltype(dd)::value;
                 hipLaunchKernelGGL((k_state_partial_valu<IT, DD>), dim3(grid), dim3(kThreads), 0, stream,
                                    static_cast<const IT*>(k), static_cast<const IT*>(v), part,
-                                   pl.N, pl.H, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv);
+                                   pl.N, pl.H, pl.L, pl.cpb, pl.P, pl.chunk, pl.sk, pl.sv, pl.gk, pl.norm_eps);
             });
         });
     }
@@ -835,7 +1022,7 @@ hipError_t launch_merge(const Plan& pl, const float* part, float* state, const f
     const int SF = pl.D * (pl.D + 1);
     const unsigned grid = (unsigned)((size_t)pl.B * pl.H * ((SF + kMergeThreads - 1) / kMergeThreads));
     hipLaunchKernelGGL(k_merge, dim3(grid), dim3(kMergeThreads), 0, stream, part, state, state_in, state_out,
-                       pl.NB, pl.cpb, pl.P, SF);
+                       pl.NB, pl.cpb, pl.P, SF, pl.mfma ? pl.gk : nullptr, pl.H, pl.D);
     return hipGetLastError();
 }
 
@@ -849,9 +1036,11 @@ hipError_t launch_apply(const Plan& pl, const void* q, const float* state, void*
                 using OT = typename decltype(o)::type;
                 by_head_dim(pl.D, [&](auto dd) {
                     constexpr int DD = decltype(dd)::value;
-                    hipLaunchKernelGGL((k_apply_mfma<IT, OT, DD>), dim3(grid), dim3(kThreads), 0, stream,
+                    auto kern = pl.gq ? k_apply_mfma<IT, OT, DD, true> : k_apply_mfma<IT, OT, DD, false>;
+                    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream,
                                        static_cast<const IT*>(q), state, static_cast<OT*>(out), pl.N, groups32(pl),
-                                       pl.HP, pl.H, pl.L, pl.NB, pl.tile, pl.tpb, eps, pl.sq, pl.so);
+                                       pl.HP, pl.H, pl.L, pl.NB, pl.tile, pl.tpb, eps, pl.sq, pl.so, pl.gq,
+                                       pl.norm_eps);
                 });
             });
         });
@@ -865,7 +1054,7 @@ hipError_t launch_apply(const Plan& pl, const void* q, const float* state, void*
                 constexpr int DD = decltype(dd)::value;
                 hipLaunchKernelGGL((k_apply_valu<IT, OT, DD>), dim3(grid), dim3(kThreads), 0, stream,
                                    static_cast<const IT*>(q), state, static_cast<OT*>(out), pl.N, pl.H, pl.L,
-                                   pl.NB, pl.tpb, eps, pl.sq, pl.so);
+                                   pl.NB, pl.tpb, eps, pl.sq, pl.so, pl.gq, pl.norm_eps);
               });
             });
         });

@@ -214,6 +214,35 @@ SANA_API int sana_linattn_fwd_strided(const void* q, const void* k, const void* 
                                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Forward with the qk_norm prologue.  The Sana page ("What LiteLA actually
+ * computes") has every Sana-1.5 and Sprint configuration normalise q and k
+ * before the feature map, to keep the linear logits inside fp16 range, and
+ * gives no formula; the reading taken here is the RMS normalisation of each
+ * head's D features with a per-channel scale:
+ *     xhat[b,n,h,j] = gamma[h][j] * x[b,n,h,j] / sqrt(mean_j'(x[b,n,h,j']^2) + norm_eps)
+ * for q (gamma_q) and for k (gamma_k), then the operator of sana_linattn_fwd
+ * on qhat and khat (v unchanged).
+ *   gamma_q, gamma_k  device fp32 [H][D], 4-byte aligned, or NULL for no
+ *              normalisation of that side; they may not overlap out or the
+ *              workspace (error ALIAS).
+ *   norm_eps   finite and > 0 when either gamma is given (error INVALID_ARG).
+ *   strides    NULL for contiguous [B][N][H][D] views, else as for
+ *              sana_linattn_fwd_strided.
+ *   block_len  0 = non-causal, >= 1 = block-causal.
+ * The workspace is sized by sana_linattn_workspace_bytes as for every other
+ * forward.  In the kernels the query's row scale cancels between numerator
+ * and normaliser except against eps, which becomes eps * rms of the row, and
+ * |gamma_q| is folded into the state rows; the keys are normalised in fp32
+ * and carried as three bf16 terms, like fp32 keys.  With both gammas NULL
+ * the result is bitwise that of sana_linattn_fwd_strided.
+ */
+SANA_API int sana_linattn_fwd_qknorm(const void* q, const void* k, const void* v, void* out,
+                                     int in_dtype, int out_dtype, int B, int H, int N, int D,
+                                     int block_len, float eps, const float* gamma_q, const float* gamma_k,
+                                     float norm_eps, const int64_t* strides, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
+/*
  * The same forward split into its three kernels, for per-kernel timing: a call
  * runs the stages whose bits are set in `stages`, in the order state, merge,
  * apply.  Calling it three times with SANA_STAGE_STATE, SANA_STAGE_MERGE and

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(sana.lib, n), n           # resolves in the shared library
         assert n in sana._SIGNATURES, n          # and the binding declares its signature
@@ -309,3 +309,35 @@ def test_noalloc_entry_point_rejects_problems_beyond_its_scratch():
         sana.SANA_OK
     # the headline shape fits
     assert sana.sana_linattn_workspace_bytes(1, 70, 16384, 32, 0) <= sana.SANA_LINATTN_SCRATCH_BYTES
+
+
+def test_qknorm_argument_errors():
+    """sana_linattn_fwd_qknorm checks norm_eps (finite, > 0 whenever a gamma is
+    given), the gammas' alignment and overlap, and the usual arguments, before
+    anything is enqueued (fake, never dereferenced pointers)."""
+    f = sana.lib.sana_linattn_fwd_qknorm
+    base = 1 << 30
+    q, k, v, out, ws = (ctypes.c_void_p(base + i * (1 << 26)) for i in range(5))
+    gq, gk = ctypes.c_void_p(base + 5 * (1 << 26)), ctypes.c_void_p(base + 6 * (1 << 26))
+    B, H, N, D = 1, 4, 1024, 32
+    wsb = sana.sana_linattn_workspace_bytes(B, H, N, D, 0)
+
+    def call(gamma_q=gq, gamma_k=gk, norm_eps=1e-6, o=out, block_len=0, eps=1e-15, dt=sana.SANA_DT_BF16, d=D,
+             nbytes=wsb):
+        return f(q, k, v, o, dt, sana.SANA_DT_F32, B, H, N, d, block_len, eps, gamma_q, gamma_k, norm_eps, None,
+                 ws, nbytes, None)
+
+    for bad in (0.0, -1e-6, float("nan"), float("inf")):
+        assert call(norm_eps=bad) == sana.SANA_ERR_INVALID_ARG
+        assert call(gamma_q=None, norm_eps=bad) == sana.SANA_ERR_INVALID_ARG
+    assert call(norm_eps=0.0, gamma_q=None, gamma_k=None, nbytes=0) == sana.SANA_ERR_WORKSPACE   # no gamma: eps unused
+    assert call(block_len=-1) == sana.SANA_ERR_INVALID_ARG
+    assert call(eps=float("nan")) == sana.SANA_ERR_INVALID_ARG
+    assert call(d=48) == sana.SANA_ERR_UNSUPPORTED
+    assert call(gamma_k=ctypes.c_void_p(base + 6 * (1 << 26) + 2)) == sana.SANA_ERR_ALIGNMENT
+    assert call(gamma_q=ctypes.c_void_p(out.value + 64)) == sana.SANA_ERR_ALIAS
+    assert call(gamma_k=ctypes.c_void_p(ws.value)) == sana.SANA_ERR_ALIAS
+    assert call(nbytes=wsb - 1) == sana.SANA_ERR_WORKSPACE
+    # an empty problem succeeds without touching any pointer
+    assert f(None, None, None, None, sana.SANA_DT_BF16, sana.SANA_DT_F32, 0, H, N, D, 0, 1e-15, None, None, 1e-6,
+             None, None, 0, None) == sana.SANA_OK

@@ -140,6 +140,38 @@ def test_non_default_stream_and_empty_problem():
     sana.sana_linattn_blockcausal_fwd(z, z, z, out, ws, 16)
 
 
+def test_allocating_wrappers_with_a_stream_that_is_not_current():
+    """linattn_fwd / linattn_bwd / linattn_jvp given `stream=` without making it
+    current: their output and workspace are allocated on that stream, so memory
+    that the current stream allocates and writes meanwhile (while the side
+    stream is still busy) never aliases them."""
+    import diffusion_transformer_relu_amd as sana
+    w = workloads.with_shape(workloads.S600M_1024, B=1, N=2048, H=8, name="side_stream")
+    (q, k, v), want = inputs_and_oracle(w)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())   # the inputs are ready on s
+    big = torch.randn((4096, 4096), device="cuda:0")
+    with torch.cuda.stream(s):
+        for _ in range(8):                      # keep s busy before the LiteLA kernels
+            big = big @ big
+            big /= big.abs().max()
+    out = sana.linattn_fwd(qd, kd, vd, eps=w.eps, stream=s)
+    dq, dk, dv = sana.linattn_bwd(qd, kd, vd, qd, eps=w.eps, stream=s)
+    o2, ot = sana.linattn_jvp(qd, kd, vd, qd, kd, vd, eps=w.eps, stream=s)
+    junk = [torch.full((1 << 22,), 3.0, device="cuda:0") for _ in range(8)]   # the current stream
+    s.synchronize()
+    torch.cuda.synchronize()
+    compare(out.cpu().double().numpy(), want, v, False, w.name)
+    assert torch.equal(o2.view(torch.int32), out.view(torch.int32))
+    ref = sana.linattn_bwd(qd, kd, vd, qd, eps=w.eps)
+    torch.cuda.synchronize()
+    for a, b in zip((dq, dk, dv), ref):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert all(torch.all(j == 3.0) for j in junk)
+    del big
+
+
 def test_device_argument_errors_leave_output_untouched():
     import diffusion_transformer_relu_amd as sana
     w = workloads.with_shape(workloads.S600M_1024, B=1, N=256, H=2, name="errs")

@@ -150,3 +150,19 @@ def make_tangents(w: Workload):
             x = x.astype(np.float16)
         out.append(x)
     return tuple(out)
+
+
+def make_gammas(w: Workload, negative_every: int = 0):
+    """Seeded per-channel scales (gamma_q, gamma_k) of the qk_norm prologue,
+    float32 [H, D]: ``default_rng([seed, t])`` with t = 7, 8, drawn as
+    1 + 0.25 * standard normal (learned RMS-norm scales start at 1).  With
+    negative_every = m > 0 every channel j with j % m == 0 is negated, so the
+    sign of a scale matters to phi."""
+    out = []
+    for t in (7, 8):
+        g = 1.0 + 0.25 * np.random.default_rng([w.seed, t]).standard_normal(size=(w.H, w.D), dtype=np.float32)
+        g = g.astype(np.float32)
+        if negative_every > 0:
+            g[:, ::negative_every] *= np.float32(-1.0)
+        out.append(g)
+    return tuple(out)

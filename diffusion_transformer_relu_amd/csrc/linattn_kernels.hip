@@ -616,7 +616,8 @@ constexpr int kOutPitch = 36;   // floats per LDS output row: 32 + 4 keeps rows 
 // truncation into three bf16 terms and the products of S's and q's terms with
 // i + j <= 4 (1-based) are summed (the dropped ones are below 2^-24 of the
 // exact product).  Occupancy target 5 waves per SIMD (4 for fp16 and fp32 q,
-// whose splits need more registers; 3 for head dim 64).
+// whose splits need more registers; 3 for head dim 64, 2 with fp32 q; one
+// less with qk_norm).
 //
 // Other head dims HD (16-bit q) use the 32-feature groups of a token row as
 // "heads" (H of them, HP pairs; HR real heads of rows HR * HD elements long):
@@ -633,8 +634,14 @@ constexpr int kOutPitch = 36;   // floats per LDS output row: 32 + 4 keeps rows 
 // rows of S when its operands are built, the sign flip is exact on the bits,
 // and rho_i cancels between numerator and normaliser except against eps, so
 // the normaliser becomes den + eps * rms_i (rms_i from the same registers).
+template <typename InT, int HD, bool QK>
+constexpr int apply_waves_per_simd() {
+    const int w = HD == 2 * kD ? (std::is_same<InT, float>::value ? 2 : 3) : std::is_same<InT, uint16_t>::value ? 5 : 4;
+    return QK && w > 2 ? w - 1 : w;   // qk_norm keeps sign masks and sums of squares live as well
+}
+
 template <typename InT, typename OutT, int HD, bool QK = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HD == 2 * kD ? (std::is_same<InT, float>::value ? 2 : 3) : std::is_same<InT, uint16_t>::value ? 5 : 4, 8))) void k_apply_mfma(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(apply_waves_per_simd<InT, HD, QK>(), 8))) void k_apply_mfma(
     const InT* __restrict__ q, const float* __restrict__ state, OutT* __restrict__ out,
     int N, int H, int HP, int HR, int L, int NB, int tile, int tpb, float eps, Strides sq, Strides so,
     const float* __restrict__ gq, float norm_eps) {

@@ -190,6 +190,7 @@ def extra_names(out_dtype: str) -> list:
              "stream_4x4096_bc1024_" + o, "fused_qkv_strided_" + o, "f16_in_" + o, "f32_in_" + o,
              "d64_h35_" + o, "d16_h140_" + o, "qknorm_" + o, "qknorm_blockcausal_16x1024_" + o,
              "backward_bf16", "backward_f32", "backward_d64_h35_bf16", "backward_d16_h140_bf16",
+             "backward_from_states_bf16", "train_step_bf16",
              "jvp_bf16_f32out", "jvp_f32"]
     for tag in ("sana600m_1024px", "sana1600m_1024px", "sana1600m_2048px"):
         names += [tag + "_cold", tag + "_warm"]
@@ -394,6 +395,36 @@ def main() -> int:
                 f"input set); algorithmic bytes = 7 tensors"
         return build
 
+    def case_saved(train):
+        """sana_linattn_bwd_from_states on the states a saving forward wrote
+        (train: the saving forward, bf16 out, and that backward, one step)."""
+        def build():
+            gx = [torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+            ob = [torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev) for _ in range(NSETS)]
+            st = [torch.empty(sana.sana_linattn_states_bytes(B, H, N, D, 0) // 4, dtype=torch.float32, device=dev)
+                  for _ in range(NSETS)]
+            wsb = torch.empty(max(sana.sana_linattn_bwd_workspace_bytes(B, H, N, D, 0), ws.numel()),
+                              dtype=torch.uint8, device=dev)
+            for i in range(NSETS):
+                sana.sana_linattn_fwd_save_states(*sets[i], ob[i], st[i], wsb, eps=w.eps,
+                                                  stream=torch.cuda.current_stream())
+
+            def fn(i):
+                q, k, v = sets[i % NSETS]
+                if train:
+                    sana.sana_linattn_fwd_save_states(q, k, v, ob[i % NSETS], st[i % NSETS], wsb, eps=w.eps,
+                                                      stream=torch.cuda.current_stream())
+                sana.sana_linattn_bwd_from_states(q, k, v, sets[(i + 1) % NSETS][0], st[i % NSETS], *gx, wsb,
+                                                  eps=w.eps, stream=torch.cuda.current_stream())
+            if train:
+                return fn, w.token_heads * D * 2 * 11, (
+                    "one training step of the layer: sana_linattn_fwd_save_states (bf16 out, the states kept) then "
+                    "sana_linattn_bwd_from_states, bf16 throughout; algorithmic bytes = 4 + 7 tensors")
+            return fn, w.token_heads * D * 2 * 7, (
+                "sana_linattn_bwd_from_states, bf16 q/k/v/dout/gradients, the states of an earlier saving forward; "
+                "algorithmic bytes = 7 tensors")
+        return build
+
     def case_jvp(dt):
         def build():
             sx = [[t.to(dt) for t in st] for st in sets]
@@ -474,6 +505,8 @@ def main() -> int:
         "backward_f32": case_bwd(torch.float32),
         "backward_d64_h35_bf16": case_bwd(torch.bfloat16, H // 2, 2 * D),
         "backward_d16_h140_bf16": case_bwd(torch.bfloat16, 2 * H, D // 2),
+        "backward_from_states_bf16": case_saved(False),
+        "train_step_bf16": case_saved(True),
         "jvp_bf16_f32out": case_jvp(torch.bfloat16),
         "jvp_f32": case_jvp(torch.float32),
     }

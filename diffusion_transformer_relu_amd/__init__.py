@@ -58,6 +58,11 @@ _SIGNATURES = {
     "sana_linattn_jvp": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P,
                               ctypes.c_size_t, _P]),
     "sana_linattn_fwd_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]),
+    "sana_linattn_states_bytes": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]),
+    "sana_linattn_fwd_save_states": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P,
+                                          ctypes.c_size_t, _P]),
+    "sana_linattn_bwd_from_states": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                          ctypes.c_float, _P, ctypes.c_size_t, _P]),
     "sana_linattn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P,
                               ctypes.c_size_t, _P]),
 }
@@ -310,6 +315,49 @@ def sana_linattn_bwd(q, k, v, dout, dq, dk, dv, workspace, *, block_len: int = 0
                                 B, H, N, D, block_len, eps, workspace.data_ptr(),
                                 workspace.numel() * workspace.element_size(), _stream_handle(stream)),
            "sana_linattn_bwd")
+
+
+def sana_linattn_states_bytes(B: int, H: int, N: int, D: int, block_len: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.sana_linattn_states_bytes(B, H, N, D, block_len, ctypes.byref(out)), "sana_linattn_states_bytes")
+    return out.value
+
+
+def sana_linattn_fwd_save_states(q, k, v, out, states, workspace, *, block_len: int = 0, eps: float = 1e-15,
+                                 stream=None):
+    """Forward into `out` that also writes the per-block prefix states into
+    `states` (float32 GPU tensor of at least sana_linattn_states_bytes bytes,
+    viewed as [B, H, NB, D, D+1])."""
+    B, N, H, D = _shape(q, k, v, out)
+    if not states.is_cuda or not states.is_contiguous() or states.dtype != _torch().float32 or \
+            states.numel() * 4 < sana_linattn_states_bytes(B, H, N, D, block_len):
+        raise ValueError("states must be a contiguous float32 GPU tensor of sana_linattn_states_bytes bytes")
+    _check(lib.sana_linattn_fwd_save_states(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dtype_code(q),
+                                            dtype_code(out), B, H, N, D, block_len, eps, states.data_ptr(),
+                                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                            _stream_handle(stream)),
+           "sana_linattn_fwd_save_states")
+
+
+def sana_linattn_bwd_from_states(q, k, v, dout, states, dq, dk, dv, workspace, *, block_len: int = 0,
+                                 eps: float = 1e-15, stream=None):
+    """Gradients dq, dk, dv (written in place) from the states a
+    sana_linattn_fwd_save_states call wrote for the same q, k, v."""
+    B, N, H, D = _shape(q, k, v, dout)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if tuple(t.shape) != (B, N, H, D) or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous GPU tensor of shape {(B, N, H, D)}")
+    if not (dq.dtype == dk.dtype == dv.dtype):
+        raise TypeError("dq, dk and dv must share one dtype")
+    if not states.is_cuda or not states.is_contiguous() or states.dtype != _torch().float32 or \
+            states.numel() * 4 < sana_linattn_states_bytes(B, H, N, D, block_len):
+        raise ValueError("states must be a contiguous float32 GPU tensor of sana_linattn_states_bytes bytes")
+    _check(lib.sana_linattn_bwd_from_states(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                                            states.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                            dtype_code(q), dtype_code(dout), dtype_code(dq), B, H, N, D, block_len,
+                                            eps, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                            _stream_handle(stream)),
+           "sana_linattn_bwd_from_states")
 
 
 def linattn_bwd(q, k, v, dout, *, eps: float = 1e-15, grad_dtype=None, block_len: int | None = None,

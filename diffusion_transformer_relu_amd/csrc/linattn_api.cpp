@@ -150,7 +150,7 @@ int forward(const void* q, const void* k, const void* v, void* out, int in_dtype
             size_t workspace_bytes, hipStream_t stream, int stages,
             const float* state_in = nullptr, float* state_out = nullptr,
             const int64_t* strides = nullptr, const float* gamma_q = nullptr, const float* gamma_k = nullptr,
-            float norm_eps = 0.f) {
+            float norm_eps = 0.f, float* states_out = nullptr) {
     Plan pl;
     const int st = make_plan(in_dtype, out_dtype, B, H, N, D, block_len, &pl, true, gamma_k != nullptr);
     if (st != SANA_OK) return st;
@@ -201,6 +201,14 @@ int forward(const void* q, const void* k, const void* v, void* out, int in_dtype
                           (state_in && state_in != state_out && overlaps(state_out, sb, state_in, sb))))
             return SANA_ERR_ALIAS;
     }
+    if (states_out) {   // the per-block prefix states, [B][H][NB][D][D+1] (no entry point passes a carried state too)
+        const size_t sb = (size_t)B * H * pl.NB * D * (D + 1) * sizeof(float);
+        if (!aligned(states_out, 4)) return SANA_ERR_ALIGNMENT;
+        if (overlaps(states_out, sb, q, q_bytes) || overlaps(states_out, sb, k, k_bytes) ||
+            overlaps(states_out, sb, v, v_bytes) || overlaps(states_out, sb, out, out_bytes) ||
+            overlaps(states_out, sb, workspace, pl.bytes))
+            return SANA_ERR_ALIAS;
+    }
     if (gamma_q || gamma_k) {
         const size_t gb = (size_t)H * D * sizeof(float);
         for (const float* gp : {gamma_q, gamma_k}) {
@@ -213,7 +221,7 @@ int forward(const void* q, const void* k, const void* v, void* out, int in_dtype
 
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     float* part = reinterpret_cast<float*>(ws + pl.off_part);
-    float* state = reinterpret_cast<float*>(ws + pl.off_state);
+    float* state = states_out ? states_out : reinterpret_cast<float*>(ws + pl.off_state);
     if ((stages & SANA_STAGE_STATE) && sana::launch_state(pl, k, v, part, stream) != hipSuccess)
         return SANA_ERR_HIP;
     if ((stages & SANA_STAGE_MERGE) && sana::launch_merge(pl, part, state, state_in, state_out, stream) != hipSuccess)
@@ -287,9 +295,11 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
     return SANA_OK;
 }
 
+// states_in: the forward's per-block prefix states ([B][H][NB][D][D+1]), or
+// nullptr to rebuild them from k and v.
 int backward(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
              int in_dtype, int dout_dtype, int grad_dtype, int B, int H, int N, int D, int block_len, float eps,
-             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+             void* workspace, size_t workspace_bytes, hipStream_t stream, const float* states_in = nullptr) {
     sana::BwdPlan bp;
     const int st = make_bwd_plan(in_dtype, dout_dtype, grad_dtype, B, H, N, D, block_len, &bp);
     if (st != SANA_OK) return st;
@@ -321,6 +331,13 @@ int backward(const void* q, const void* k, const void* v, const void* dout, void
     }
     for (int j = 0; j < 4; ++j)
         if (overlaps(workspace, bp.bytes, ins[j], in_b[j])) return SANA_ERR_ALIAS;
+    if (states_in) {
+        const size_t sb = (size_t)B * H * bp.fw.NB * D * (D + 1) * sizeof(float);
+        if (!aligned(states_in, 4)) return SANA_ERR_ALIGNMENT;
+        for (void* p : outs)
+            if (overlaps(p, gb, states_in, sb)) return SANA_ERR_ALIAS;
+        if (overlaps(workspace, bp.bytes, states_in, sb)) return SANA_ERR_ALIAS;
+    }
     if (workspace_bytes < bp.bytes) return SANA_ERR_WORKSPACE;
 
     Plan& pl = bp.fw;
@@ -330,9 +347,10 @@ int backward(const void* q, const void* k, const void* v, const void* dout, void
     float* state = reinterpret_cast<float*>(ws + pl.off_state);
     float* gpart = reinterpret_cast<float*>(ws + bp.off_gpart);
     float* ghat = reinterpret_cast<float*>(ws + bp.off_ghat);
-    if (sana::launch_state(pl, k, v, part, stream) != hipSuccess ||
-        sana::launch_merge(pl, part, state, nullptr, nullptr, stream) != hipSuccess ||
-        sana::launch_bwd_query(bp, q, dout, state, dq, gpart, eps, stream) != hipSuccess ||
+    if (!states_in && (sana::launch_state(pl, k, v, part, stream) != hipSuccess ||
+                       sana::launch_merge(pl, part, state, nullptr, nullptr, stream) != hipSuccess))
+        return SANA_ERR_HIP;
+    if (sana::launch_bwd_query(bp, q, dout, states_in ? states_in : state, dq, gpart, eps, stream) != hipSuccess ||
         sana::launch_bwd_merge(bp, gpart, ghat, stream) != hipSuccess ||
         sana::launch_bwd_key(bp, k, v, ghat, dk, dv, stream) != hipSuccess)
         return SANA_ERR_HIP;
@@ -470,6 +488,34 @@ int sana_linattn_bwd(const void* q, const void* k, const void* v, const void* do
     if (block_len < 0) return SANA_ERR_INVALID_ARG;
     return backward(q, k, v, dout, dq, dk, dv, in_dtype, dout_dtype, grad_dtype, B, H, N, D, block_len, eps,
                     workspace, workspace_bytes, stream);
+}
+
+int sana_linattn_states_bytes(int B, int H, int N, int D, int block_len, size_t* bytes) {
+    if (!bytes) return SANA_ERR_INVALID_ARG;
+    Plan pl;
+    const int st = make_plan(SANA_DT_BF16, SANA_DT_F32, B, H, N, D, block_len, &pl);
+    if (st != SANA_OK) return st;
+    *bytes = (B == 0 || H == 0 || N == 0) ? 0 : (size_t)B * H * pl.NB * D * (D + 1) * sizeof(float);
+    return SANA_OK;
+}
+
+int sana_linattn_fwd_save_states(const void* q, const void* k, const void* v, void* out, int in_dtype,
+                                 int out_dtype, int B, int H, int N, int D, int block_len, float eps, float* states,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (block_len < 0) return SANA_ERR_INVALID_ARG;
+    if (!states && B > 0 && H > 0 && N > 0) return SANA_ERR_INVALID_ARG;
+    return forward(q, k, v, out, in_dtype, out_dtype, B, H, N, D, block_len, eps, workspace, workspace_bytes,
+                   stream, SANA_STAGE_ALL, nullptr, nullptr, nullptr, nullptr, nullptr, 0.f, states);
+}
+
+int sana_linattn_bwd_from_states(const void* q, const void* k, const void* v, const void* dout, const float* states,
+                                 void* dq, void* dk, void* dv, int in_dtype, int dout_dtype, int grad_dtype, int B,
+                                 int H, int N, int D, int block_len, float eps, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    if (block_len < 0) return SANA_ERR_INVALID_ARG;
+    if (!states && B > 0 && H > 0 && N > 0) return SANA_ERR_INVALID_ARG;
+    return backward(q, k, v, dout, dq, dk, dv, in_dtype, dout_dtype, grad_dtype, B, H, N, D, block_len, eps,
+                    workspace, workspace_bytes, stream, states);
 }
 
 int sana_linattn_jvp_workspace_bytes(int B, int H, int N, int D, int block_len, size_t* bytes) {

@@ -290,6 +290,43 @@ SANA_API int sana_linattn_bwd(const void* q, const void* k, const void* v, const
                               hipStream_t stream);
 
 /*
+ * A training step runs the forward and then the backward over the same q, k,
+ * v; the backward above rebuilds the forward's states (one more pass over k
+ * and v).  These two entry points hand them over instead:
+ *
+ * sana_linattn_states_bytes: bytes of the per-block prefix states of a call,
+ *   B * H * NB * D * (D + 1) * 4 with NB = ceil(N / block_len) (1 when
+ *   block_len is 0 or >= N); 0 for an empty problem.
+ *
+ * sana_linattn_fwd_save_states: the forward of sana_linattn_fwd (block_len 0)
+ *   or sana_linattn_blockcausal_fwd (block_len >= 1), which also writes the
+ *   state each block's queries use, S_beta (the sum over the keys of blocks
+ *   0..beta, with the ones column), into `states`: device fp32
+ *   [B][H][NB][D][D+1], at least sana_linattn_states_bytes bytes, 4-byte
+ *   aligned, not overlapping q, k, v, out or the workspace (error ALIAS),
+ *   caller-owned.  The output is bitwise that of sana_linattn_fwd /
+ *   sana_linattn_blockcausal_fwd.
+ *
+ * sana_linattn_bwd_from_states: the backward of sana_linattn_bwd with the
+ *   states read from `states` (as written by sana_linattn_fwd_save_states for
+ *   the same q, k, v, in_dtype, block_len; not checked) instead of rebuilt;
+ *   `states` must not overlap dq, dk, dv or the workspace (error ALIAS).  The
+ *   gradients are bitwise those of sana_linattn_bwd on the same arguments.
+ *   The workspace is sized by sana_linattn_bwd_workspace_bytes.
+ */
+SANA_API int sana_linattn_states_bytes(int B, int H, int N, int D, int block_len, size_t* bytes);
+
+SANA_API int sana_linattn_fwd_save_states(const void* q, const void* k, const void* v, void* out, int in_dtype,
+                                          int out_dtype, int B, int H, int N, int D, int block_len, float eps,
+                                          float* states, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+
+SANA_API int sana_linattn_bwd_from_states(const void* q, const void* k, const void* v, const void* dout,
+                                          const float* states, void* dq, void* dk, void* dv, int in_dtype,
+                                          int dout_dtype, int grad_dtype, int B, int H, int N, int D, int block_len,
+                                          float eps, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Forward-mode derivative (Jacobian-vector product): the forward's output and
  * its directional derivative along tangents (q_t, k_t, v_t) of the inputs, as
  * forward-mode differentiation through attention needs (the consistency-model

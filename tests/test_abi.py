@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(sana.lib, n), n           # resolves in the shared library
         assert n in sana._SIGNATURES, n          # and the binding declares its signature
@@ -341,3 +341,42 @@ def test_qknorm_argument_errors():
     # an empty problem succeeds without touching any pointer
     assert f(None, None, None, None, sana.SANA_DT_BF16, sana.SANA_DT_F32, 0, H, N, D, 0, 1e-15, None, None, 1e-6,
              None, None, 0, None) == sana.SANA_OK
+
+
+def test_saved_states_size_and_argument_errors():
+    """sana_linattn_states_bytes is B H NB D (D+1) 4; the save / from-states
+    entry points reject a missing, misaligned or overlapping states buffer
+    before anything is enqueued (fake, never dereferenced pointers)."""
+    assert sana.sana_linattn_states_bytes(1, 70, 16384, 32, 0) == 70 * 32 * 33 * 4
+    assert sana.sana_linattn_states_bytes(1, 70, 16384, 32, 1024) == 16 * 70 * 32 * 33 * 4
+    assert sana.sana_linattn_states_bytes(2, 3, 1000, 64, 300) == 2 * 3 * 4 * 64 * 65 * 4
+    assert sana.sana_linattn_states_bytes(0, 3, 1000, 16, 0) == 0
+    assert sana.lib.sana_linattn_states_bytes(1, 3, 1000, 48, 0, ctypes.byref(ctypes.c_size_t())) == \
+        sana.SANA_ERR_UNSUPPORTED
+    base = 1 << 32
+    q, k, v, out, ws, st = (base + i * (1 << 26) for i in range(6))
+    B, H, N, D = 1, 4, 1024, 32
+    wsb = sana.sana_linattn_workspace_bytes(B, H, N, D, 256)
+    save = sana.lib.sana_linattn_fwd_save_states
+
+    def fwd(states=st, o=out, L=256):
+        return save(q, k, v, o, sana.SANA_DT_BF16, sana.SANA_DT_F32, B, H, N, D, L, 1e-15, states, ws, wsb, None)
+
+    assert fwd(states=None) == sana.SANA_ERR_INVALID_ARG
+    assert fwd(states=st + 2) == sana.SANA_ERR_ALIGNMENT
+    assert fwd(states=out + 64) == sana.SANA_ERR_ALIAS
+    assert fwd(states=ws) == sana.SANA_ERR_ALIAS
+    assert fwd(L=-1) == sana.SANA_ERR_INVALID_ARG
+    assert save(None, None, None, None, 1, 0, 0, H, N, D, 0, 1e-15, None, None, 0, None) == sana.SANA_OK
+    bw = sana.lib.sana_linattn_bwd_from_states
+    bwb = sana.sana_linattn_bwd_workspace_bytes(B, H, N, D, 256)
+    dq, dk, dv, dout = (base + (6 + i) * (1 << 26) for i in range(4))
+
+    def bwd(states=st, L=256, nbytes=bwb):
+        return bw(q, k, v, dout, states, dq, dk, dv, 1, 1, 1, B, H, N, D, L, 1e-15, ws, nbytes, None)
+
+    assert bwd(states=None) == sana.SANA_ERR_INVALID_ARG
+    assert bwd(states=st + 1) == sana.SANA_ERR_ALIGNMENT
+    assert bwd(states=dk + 128) == sana.SANA_ERR_ALIAS
+    assert bwd(states=ws + 256) == sana.SANA_ERR_ALIAS
+    assert bwd(nbytes=bwb - 1) == sana.SANA_ERR_WORKSPACE

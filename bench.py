@@ -102,8 +102,8 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out_dtype: str = "f32", ca
     sf, sw = calib(fetch), calib(write)
     # bf16 inputs, head dim 32: the state kernel's template arguments are
     # F16 = false and the head dim; the apply kernel's the input and output
-    # element types and the head dim
-    apply_tag = "k_apply_mfma<unsigned short, " + ("float" if out_dtype == "f32" else "unsigned short") + ", 32>"
+    # element types, the head dim and qk_norm off
+    apply_tag = "k_apply_mfma<unsigned short, " + ("float" if out_dtype == "f32" else "unsigned short") + ", 32, false>"
     kernels = {"k_state_partial_mfma": lambda n: "k_state_partial_mfma<false, 32>" in n,
                "k_merge": lambda n: "k_merge" in n,
                "k_apply_mfma": lambda n: apply_tag in n}
@@ -237,6 +237,27 @@ def graph_time_ms(torch, fn, n: int) -> float:
     return ms
 
 
+def summarize_counters(csv_path: str) -> int:
+    """Markdown table of a rocprofv3 --pmc run_counter_collection.csv: the
+    median per dispatch of every counter, per LiteLA kernel."""
+    import csv
+    import statistics
+    vals = {}
+    for row in csv.DictReader(open(csv_path)):
+        name = short_kernel_name(row["Kernel_Name"])
+        if not name.startswith("k_"):
+            continue
+        vals.setdefault(name, {}).setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    counters = sorted({c for d in vals.values() for c in d})
+    print("| kernel | dispatches | " + " | ".join(counters) + " |")
+    print("|---|---|" + "---|" * len(counters))
+    for name, d in vals.items():
+        n = max(len(v) for v in d.values())
+        cells = [f"{statistics.median(d[c]):.4g}" if c in d else "" for c in counters]
+        print(f"| `{name}` | {n} | " + " | ".join(cells) + " |")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,12 +281,17 @@ def main() -> int:
                          "WRITE_SIZE) of a profiled bench run into profiles/traffic.json")
     ap.add_argument("--traffic-case", default="headline",
                     help="with --traffic-from: the case the counter runs profiled (its key in traffic.json)")
+    ap.add_argument("--counters-from", metavar="COUNTER_CSV",
+                    help="no GPU run: print a rocprofv3 --pmc run_counter_collection.csv as a markdown table "
+                         "(median per dispatch of each counter, per LiteLA kernel)")
     ap.add_argument("--trace-from", metavar="STATS_CSV",
                     help="no GPU run: print a rocprofv3 --kernel-trace --stats run_kernel_stats.csv as a "
                          "markdown table")
     args = ap.parse_args()
     if args.trace_from:
         return summarize_trace(args.trace_from)
+    if args.counters_from:
+        return summarize_counters(args.counters_from)
     if args.traffic_from:
         return summarize_traffic(*args.traffic_from, out_dtype=args.out_dtype, case=args.traffic_case)
 

@@ -13,7 +13,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "lib", "libsana_linattn.so")
+# SANA_LINATTN_LIB selects another build of the same sources (the host
+# sanitizer build, lib_san/)
+LIB_PATH = os.environ.get("SANA_LINATTN_LIB") or os.path.join(_PKG, "lib", "libsana_linattn.so")
 
 SANA_DT_F32 = 0
 SANA_DT_BF16 = 1

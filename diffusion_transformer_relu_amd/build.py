@@ -47,27 +47,40 @@ def _run(cmd, verbose):
         print("\n".join(msgs))
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
+# Host-only AddressSanitizer + UndefinedBehaviorSanitizer for the sanitizer
+# build (each flag applies to the host pass only; device code is built as
+# usual).
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def build(verbose: bool = False, extra_flags=(), sanitize: bool = False) -> str:
     """Compiles every source to an object file in parallel (each kernel file
-    holds its own launchers, so no device code crosses files), then links."""
+    holds its own launchers, so no device code crosses files), then links.
+    sanitize: the host code (the C-ABI layer and the launchers) with
+    AddressSanitizer and UndefinedBehaviorSanitizer, into lib_san/ (load it
+    with SANA_LINATTN_LIB and the sanitizer runtime preloaded)."""
     from concurrent.futures import ThreadPoolExecutor
 
-    os.makedirs(LIBDIR, exist_ok=True)
-    objdir = os.path.join(LIBDIR, "obj")
+    libdir = LIBDIR + "_san" if sanitize else LIBDIR
+    lib = os.path.join(libdir, os.path.basename(LIB))
+    extra = [*extra_flags, *(SAN_FLAGS if sanitize else [])]
+    os.makedirs(libdir, exist_ok=True)
+    objdir = os.path.join(libdir, "obj")
     os.makedirs(objdir, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
     objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in SOURCES]
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        jobs = [ex.submit(_run, [hipcc(), *compile_flags, *extra_flags, *inc, "-c", s, "-o", o], verbose)
+        jobs = [ex.submit(_run, [hipcc(), *compile_flags, *extra, *inc, "-c", s, "-o", o], verbose)
                 for s, o in zip(SOURCES, objs)]
         for j in jobs:
             j.result()
-    tmp = LIB + ".tmp"
-    _run([hipcc(), *HIPCC_FLAGS, *extra_flags, *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = lib + ".tmp"
+    _run([hipcc(), *HIPCC_FLAGS, *extra, *objs, "-o", tmp], verbose)
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv))

@@ -18,7 +18,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liblinattn_oracle.so")
+# SANA_ORACLE_LIB selects another build of the same source (the sanitizer build)
+_LIB_PATH = os.environ.get("SANA_ORACLE_LIB") or os.path.join(_HERE, "liblinattn_oracle.so")
 _lib = None
 
 F32 = 0

@@ -15,16 +15,25 @@ SRC = os.path.join(HERE, "linattn_oracle.c")
 LIB = os.path.join(HERE, "liblinattn_oracle.so")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
+SAN_LIB = os.path.join(HERE, "liblinattn_oracle_san.so")
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """sanitize: an AddressSanitizer + UndefinedBehaviorSanitizer build into
+    liblinattn_oracle_san.so (load it with SANA_ORACLE_LIB and libasan
+    preloaded) for the host sanitizer pass over the oracle's tests."""
+    lib = SAN_LIB if sanitize else LIB
+    tmp = lib + ".tmp"
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"] \
+        if sanitize else []
     cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
-           "-Wall", "-Wextra", "-Werror", SRC, "-o", tmp]
+           "-Wall", "-Wextra", "-Werror", *san, SRC, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

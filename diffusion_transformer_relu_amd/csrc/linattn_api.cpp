@@ -76,9 +76,12 @@ int make_plan(int in_dtype, int out_dtype, int B, int H, int N, int D, int block
     if (chunk) {
         chunk = (int)round_up(chunk, 64);
     } else {
-        // fp32 inputs on the matrix cores: their state kernel holds 3 work-
-        // groups per CU and streams best with one full round of them
-        const long slots = (pl->mfma && (in_dtype == SANA_DT_F32 || split_state)) ? sana::kCUs * 3 : sana::kStateGroups;
+        // the split-term state kernel (fp32 keys, and qk_norm keys of any
+        // type) streams best with one full round of as many work-groups as
+        // fit a CU: 3 with fp32 V (48 KB of LDS each), 4 with 16-bit V (32
+        // or 40 KB)
+        const long slots = !(pl->mfma && (in_dtype == SANA_DT_F32 || split_state)) ? sana::kStateGroups
+                           : sana::kCUs * (in_dtype == SANA_DT_F32 ? 3 : 4);
         const long per_block = std::max<long>(1, slots / units);
         chunk = (int)std::max<long>(round_up(ceil_div(pl->L, per_block), 64), sana::kMinChunk);
     }
@@ -459,12 +462,14 @@ int sana_linattn_workspace_bytes(int B, int H, int N, int D, int block_len, size
     Plan pl;
     const int st = make_plan(SANA_DT_BF16, SANA_DT_F32, B, H, N, D, block_len, &pl);
     if (st != SANA_OK) return st;
-    // fp32 inputs (their own chunking) and the vector path (SANA_LINATTN_PATH=valu)
-    // may need more; report the largest.
-    Plan pf, pv;
+    // fp32 inputs and qk_norm keys (the split-term state kernel's own
+    // chunking) and the vector path (SANA_LINATTN_PATH=valu) may need more;
+    // report the largest.
+    Plan pf, pq, pv;
     make_plan(SANA_DT_F32, SANA_DT_F32, B, H, N, D, block_len, &pf);
+    make_plan(SANA_DT_BF16, SANA_DT_F32, B, H, N, D, block_len, &pq, true, true);
     make_plan(SANA_DT_F32, SANA_DT_F32, B, H, N, D, block_len, &pv, false);
-    *bytes = std::max(pl.bytes, std::max(pf.bytes, pv.bytes));
+    *bytes = std::max({pl.bytes, pf.bytes, pq.bytes, pv.bytes});
     return SANA_OK;
 }
 

@@ -292,7 +292,11 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma_f32(
     const float* __restrict__ gk, float norm_eps) {
     // terms of a V value: bf16 1, fp16 2 (8 + 3 significant bits), fp32 3
     constexpr int VT = std::is_same<InT, uint16_t>::value ? 1 : std::is_same<InT, _Float16>::value ? 2 : 3;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][3][2][kF32Tile];   // [tensor][term][head] = 48 KB
+    // term tiles [term][head]: K three terms, V as many as its type needs
+    // (24 + 8, 16 or 24 KB), so that 16-bit V leaves room for a fourth
+    // work-group per CU
+    __shared__ __attribute__((aligned(16))) uint16_t ldk[3][2][kF32Tile];
+    __shared__ __attribute__((aligned(16))) uint16_t ldv[VT][2][kF32Tile];
 
     const int p = blockIdx.x % P;
     const int bhp = blockIdx.x / P;
@@ -381,8 +385,8 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma_f32(
             const int o = tok * kD + part0 * 8;
 #pragma unroll
             for (int t = 0; t < 3; ++t) {
-                *reinterpret_cast<u32x4*>(&lds[0][t][grp0][o]) = ta[t];
-                if (t < VT) *reinterpret_cast<u32x4*>(&lds[1][t][grp0][o]) = tv[t];
+                *reinterpret_cast<u32x4*>(&ldk[t][grp0][o]) = ta[t];
+                if (t < VT) *reinterpret_cast<u32x4*>(&ldv[t][grp0][o]) = tv[t];
             }
         }
         __syncthreads();
@@ -395,8 +399,8 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma_f32(
             u32x4 ta[3], tv[3];
 #pragma unroll
             for (int t = 0; t < 3; ++t) {
-                ta[t] = gather_tokens_t16(lds[0][t][hh], kD, tb, 0, lane);   // lane (g, j): tokens tb + 8g + e, feature j
-                if (t < VT) tv[t] = gather_tokens_t16(lds[1][t][D64 ? th : hh], kD, tb, 0, lane);   // lane (g, c): tokens tb + 8g + e, channel c
+                ta[t] = gather_tokens_t16(ldk[t][hh], kD, tb, 0, lane);   // lane (g, j): tokens tb + 8g + e, feature j
+                if (t < VT) tv[t] = gather_tokens_t16(ldv[t][D64 ? th : hh], kD, tb, 0, lane);   // lane (g, c): tokens tb + 8g + e, channel c
             }
             // term pairs with i + j <= 2, smallest products first
             accV = mfma_bf16(ta[2], tv[0], accV);
@@ -427,7 +431,8 @@ __global__ __launch_bounds__(kThreads) void k_state_partial_mfma_f32(
     }
     // Combine the two token halves of each head in a fixed order, then write.
     __syncthreads();
-    float* red = reinterpret_cast<float*>(&lds[0][0][0][0]);   // [head][V|O][16][64] floats = 16 KiB
+    static_assert(sizeof(ldk) >= 2 * 2 * 16 * 64 * sizeof(float), "reduction area exceeds the K term tiles");
+    float* red = reinterpret_cast<float*>(&ldk[0][0][0]);   // [head][V|O][16][64] floats = 16 KiB
     if (th == 1) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {

@@ -1034,7 +1034,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     const int blk0 = beta * L, blk1 = min(blk0 + L, N);
     const int t0 = blk0 + tib * tile, t1 = min(t0 + tile, blk1);
     const int g = lane >> 5, i = lane & 31;
-    if (t0 >= t1) return;   // uniform over the work-group
+    if (t0 >= t1) {
+        // a tile past the end of a short last block: its partial gradient
+        // state is zero (the suffix merge adds every tile slot of a block)
+        float* dst = gpart + ((((size_t)b * HR + hq) * NB + beta) * tpb + tib) * SF;
+        for (int e = threadIdx.x; e < SF; e += kThreads) dst[e] = 0.f;
+        return;   // uniform over the work-group
+    }
 
     const float* P = state + (((size_t)b * HR + hq) * NB + beta) * SF;
     if (wave < 2) {

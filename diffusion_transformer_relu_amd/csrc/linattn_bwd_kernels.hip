@@ -1277,6 +1277,301 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     }
 }
 
+// ------------------------------------------------------------------ query pass, head dim 32, 16-bit q and dout
+// The direct query kernel reads each wave's 32 rows straight from global
+// memory in the MFMA operand layout (lane (g, i): token i, features 8 g .. + 7
+// and 16 + 8 g .. + 7, two 16-byte loads per tensor), with the next sub-tile's
+// loads in flight, as the forward's apply kernel does; nothing is staged in
+// LDS.  The state operand's rows are permuted so that a product lands on the
+// features the lane has loaded: output row r of a 32 x 32 MFMA tile (register
+// 4 rr + e of lane (g, .), r = 8 rr + 4 g + e) is made feature perm_row(r),
+// which swaps bits 2 and 3 of r, and register rg of lane (g, .) then holds
+// feature 16 (rg >> 3) + 8 g + (rg & 7): element rg & 7 of the lane's operand
+// half rg >> 3.  Masks and per-feature terms then use the lane's own
+// registers.
+__device__ __forceinline__ int perm_row(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+__device__ __forceinline__ int perm_feature(int g, int rg) { return 16 * (rg >> 3) + 8 * g + (rg & 7); }
+
+// Split-term operands (state_operands' three bf16 terms) of a head's 32 x 33
+// state S with permuted rows: lane (g, i) gets A[i][16 ks + 8 g + e] =
+// S[perm_row(i)][16 ks + 8 g + e].
+__device__ __forceinline__ void perm_operands(const float* S, int lane, u32x4 (&out)[2][3]) {
+    constexpr int SW = kD + 1;
+    const int g = lane >> 5, ri = perm_row(lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = S[ri * SW + 16 * ks + 8 * g + e];
+        split3_f32x8(x, out[ks]);
+    }
+}
+
+// Element rg & 7 of operand half rg >> 3 (a packed 16-bit operand) as fp32.
+template <bool F16>
+__device__ __forceinline__ float operand_elem(const u32x4 (&x)[2], int rg) {
+    const uint32_t w = x[rg >> 3][(rg & 7) >> 1];
+    if constexpr (F16)
+        return f16_to_f32((uint16_t)((rg & 1) ? (w >> 16) : (w & 0xffffu)));
+    else
+        return (rg & 1) ? hi_bf16(w) : lo_bf16(w);
+}
+
+// Two fp32 values rounded (nearest-even) to OutT and packed (one
+// v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+template <typename OutT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    if constexpr (std::is_same<OutT, _Float16>::value) {
+        // pin the fp32 values (see put_pair_tile)
+        asm volatile("" : "+v"(a));
+        asm volatile("" : "+v"(b));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+    } else {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+    }
+}
+
+// A permuted-layout tile (lane (g, i): token i, register rg = feature
+// perm_feature(g, rg)) rounded to OutT into head hh's half of a pair tile.
+template <typename OutT>
+__device__ __forceinline__ void put_pair_tile_perm(uint16_t* ct, const f32x16& acc, int lane, int hh) {
+    const int g = lane >> 5, i = lane & 31;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        u32x4 p;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) p[d] = pack2<OutT>(acc[8 * hf + 2 * d], acc[8 * hf + 2 * d + 1]);
+        *reinterpret_cast<u32x4*>(ct + i * kPairRow + hh * 32 + 16 * hf + 8 * g) = p;
+    }
+}
+
+// store_tile for a permuted-layout fp32 tile: through the wave's LDS tile,
+// then whole 128-byte rows; rows t >= n repeat row n - 1 (same values).
+template <typename RowPtr>
+__device__ __forceinline__ void store_tile_perm(float* ot, const f32x16& acc, int lane, int n, RowPtr dst) {
+    const int g = lane >> 5, i = lane & 31;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        *reinterpret_cast<f32x4*>(ot + i * kPitch + 16 * (p >> 1) + 8 * g + 4 * (p & 1)) =
+            (f32x4){acc[4 * p], acc[4 * p + 1], acc[4 * p + 2], acc[4 * p + 3]};
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+        const int r = 8 * s4 + (lane >> 3), cc = (lane & 7) * 4;
+        store4(dst(min(r, n - 1)) + cc, *reinterpret_cast<const f32x4*>(ot + r * kPitch + cc));
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// 16-bit rows of q and dout for the 32 tokens of a sub-tile (operand layout).
+struct Rows16 {
+    u32x4 x[2], y[2];
+};
+__device__ __forceinline__ void load_rows16(const uint16_t* x, const uint16_t* y, long long off, Rows16& r) {
+    const u32x4* px = reinterpret_cast<const u32x4*>(x + off);
+    const u32x4* py = reinterpret_cast<const u32x4*>(y + off);
+    r.x[0] = px[0];
+    r.x[1] = px[2];
+    r.y[0] = py[0];
+    r.y[1] = py[2];
+}
+
+// grid.x = (b * HP + hp) * (NB * tpb) + beta * tpb + tile; wave w handles head
+// 2 hp + (w & 1) and the 32-query sub-tiles 32 (w >> 1) + 64 s of the tile.
+// Per sub-tile, with f = ReLU(q), P the block's state (rows permuted), z =
+// P[:, D]:
+//   den = f . z (fp32, the lane's 16 features and its partner's), r = 1/(den + eps)
+//   m = P_v dout^T on MFMA (six products: P's split terms, the 16-bit dout
+//   exact; fp16 dout as two exact bf16 terms)
+//   w = -r (r (f . m)) (dout . num = f . m), dq = [q > 0] (r m + w z)
+// then the gradient state, tokens as the reduction dimension: f^T and dout^T
+// come out of MFMAs against identity operands (exact: one product 1 * x per
+// output), which leave lane (g, j) with feature j of the tokens 8 rr + 4 g + e
+// in register 4 rr + e; r and w of those tokens are read back from the wave's
+// LDS row (zero for tokens past the range), u = r dout^T, and
+//   G_v += f^T u, bf16 q: on the bf16 matrix instructions, 16 tokens per
+//                 K-step, f^T exact and u as the three terms of its
+//                 truncation split (which sum to u exactly): three MFMAs per
+//                 K-step instead of eight fp32 ones;
+//                 fp16 q: 16 fp32 MFMAs 32 x 32 x 2 (f is not a bf16 value)
+//   G_z += f^T w (vector FMAs).
+// 16-bit dq: the two waves of a sub-tile fill a pair tile and store whole
+// 128-byte lines (two work-group barriers per step; every wave takes the same
+// number of steps, a step past the range working on the clamped last row);
+// fp32 dq: each wave stores its own rows through its LDS tile.  At the end the
+// two waves of a head add their G in a fixed order and write the tile's
+// partial gradient state (zero for a tile with no tokens).
+template <bool QF16, bool GF16, typename OutT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(OutT) == 4 ? 2 : 3, 8))) void k_bwd_query_direct(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout, const float* __restrict__ state,
+    OutT* __restrict__ dq, float* __restrict__ gpart, int N, int H, int HP, int L, int NB, int tile, int tpb,
+    float eps) {
+    constexpr int SW = kD + 1, SF = kD * SW;
+    constexpr bool kPair = sizeof(OutT) == 2;
+    __shared__ __attribute__((aligned(16))) uint16_t ct[kPair ? 2 : 1][kPair ? 2 : 1][kPair ? 32 * kPairRow : 8];   // [step & 1][sub]
+    __shared__ __attribute__((aligned(16))) float otile[kPair ? 1 : 4][kPair ? 4 : 32 * kPitch];
+    __shared__ __attribute__((aligned(16))) float rw[4][2][32];   // r and w of each wave's tokens
+    __shared__ __attribute__((aligned(16))) float red[2][16 * 64 + 32];   // the second waves' G
+
+    const int per_unit = NB * tpb;
+    const int tau = blockIdx.x % per_unit;
+    const int bhp = blockIdx.x / per_unit;
+    const int hp = bhp % HP, b = bhp / HP;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int hh = wave & 1, sub = wave >> 1, h = 2 * hp + hh;
+    const int hs = min(h, H - 1);   // a missing second head computes on the first (never stored)
+    const int beta = tau / tpb, tib = tau - beta * tpb;
+    const int blk0 = beta * L, blk1 = min(blk0 + L, N);
+    const int t0 = blk0 + tib * tile, t1 = min(t0 + tile, blk1);
+    const int g = lane >> 5, i = lane & 31;
+
+    const float* P = state + (((size_t)b * H + hs) * NB + beta) * SF;
+    f32x16 accG = {};
+    float gzacc = 0.f;   // lane (g, j): sum over this lane's tokens of f_j w
+    if (t0 < t1) {       // uniform over the work-group
+        u32x4 pa[2][3];
+        perm_operands(P, lane, pa);
+        float zr[16];
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) zr[rg] = P[perm_feature(g, rg) * SW + kD];
+        // identity operands: element e of K-step ks is one where 16 ks + 8 g + e = i
+        u32x4 iq[2], ig[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int e0 = 16 * ks + 8 * g + 2 * d;
+                const uint32_t oq = QF16 ? 0x3c00u : 0x3f80u, og = GF16 ? 0x3c00u : 0x3f80u;
+                iq[ks][d] = (e0 == i ? oq : 0u) | (e0 + 1 == i ? oq << 16 : 0u);
+                ig[ks][d] = (e0 == i ? og : 0u) | (e0 + 1 == i ? og << 16 : 0u);
+            }
+
+        const long long hstride = (long long)H * kD;
+        auto row_off = [&](int tt) { return ((long long)b * N + min(tt + i, t1 - 1)) * hstride + hs * kD + 8 * g; };
+        const int steps = (t1 - t0 + 63) / 64;
+        int tt = t0 + 32 * sub;
+        Rows16 cur;   // x: q, y: dout
+        load_rows16(q, dout, row_off(tt), cur);
+        for (int st = 0; st < steps; ++st, tt += 64) {
+            Rows16 nxt;
+            load_rows16(q, dout, row_off(tt + 64), nxt);   // in flight during this sub-tile's work
+            const int n = min(32, t1 - tt);
+            const u32x4 fq[2] = {relu_bf16x8(cur.x[0]), relu_bf16x8(cur.x[1])};
+            float dp = 0.f;
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) dp = fmaf(operand_elem<QF16>(fq, rg), zr[rg], dp);
+            const float r = 1.0f / (dp + __shfl_xor(dp, 32) + eps);
+            f32x16 acc = {};
+            acc = mma_split_ks<GF16, 2>(pa, cur.y, acc);
+            float go = 0.f;
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) go = fmaf(operand_elem<QF16>(fq, rg), acc[rg], go);
+            const float w = -r * ((go + __shfl_xor(go, 32)) * r);
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg)
+                acc[rg] = operand_elem<QF16>(fq, rg) > 0.f ? fmaf(zr[rg], w, acc[rg] * r) : 0.f;
+            if (g == 0) {   // zero past the range: the G sums skip those tokens
+                rw[wave][0][i] = i < n ? r : 0.f;
+                rw[wave][1][i] = i < n ? w : 0.f;
+            }
+            // f^T and dout^T: lane (g, j) gets feature j of tokens 8 rr + 4 g + e
+            f32x16 fT = {}, gT = {};
+            fT = mfma16<QF16>(fq[0], iq[0], fT);
+            fT = mfma16<QF16>(fq[1], iq[1], fT);
+            gT = mfma16<GF16>(cur.y[0], ig[0], gT);
+            gT = mfma16<GF16>(cur.y[1], ig[1], gT);
+            if constexpr (kPair) {
+                put_pair_tile_perm<OutT>(ct[st & 1][sub], acc, lane, hh);
+            } else if (n > 0 && h < H) {
+                store_tile_perm(otile[wave], acc, lane, n, [&](int t) {
+                    return reinterpret_cast<float*>(dq + ((long long)b * N + tt + t) * hstride + h * kD);
+                });
+            }
+            __builtin_amdgcn_wave_barrier();
+            asm volatile("" ::: "memory");   // the r, w rows are written before they are read
+            if constexpr (!QF16) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    float uu[8];
+                    u32x4 fp;
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int rr = 2 * ks + h2;
+                        const f32x4 r4 = *reinterpret_cast<const f32x4*>(&rw[wave][0][8 * rr + 4 * g]);
+                        const f32x4 w4 = *reinterpret_cast<const f32x4*>(&rw[wave][1][8 * rr + 4 * g]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int s = 4 * rr + e;
+                            uu[4 * h2 + e] = gT[s] * r4[e];
+                            gzacc = fmaf(fT[s], w4[e], gzacc);
+                        }
+#pragma unroll
+                        for (int d = 0; d < 2; ++d) {
+                            // through scalars: bit_cast of a vector element
+                            // expression reads the vector's first element with
+                            // this compiler
+                            const float f0 = fT[4 * rr + 2 * d], f1 = fT[4 * rr + 2 * d + 1];
+                            fp[2 * h2 + d] = (__builtin_bit_cast(uint32_t, f0) >> 16) |
+                                             (__builtin_bit_cast(uint32_t, f1) & 0xffff0000u);
+                        }
+                    }
+                    u32x4 ut[3];
+                    split3_trunc_f32x8(uu, ut);
+                    accG = mfma_bf16(fp, ut[2], accG);
+                    accG = mfma_bf16(fp, ut[1], accG);
+                    accG = mfma_bf16(fp, ut[0], accG);
+                }
+            } else {
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const f32x4 r4 = *reinterpret_cast<const f32x4*>(&rw[wave][0][8 * rr + 4 * g]);
+                    const f32x4 w4 = *reinterpret_cast<const f32x4*>(&rw[wave][1][8 * rr + 4 * g]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int s = 4 * rr + e;
+                        accG = __builtin_amdgcn_mfma_f32_32x32x2f32(fT[s], gT[s] * r4[e], accG, 0, 0, 0);
+                        gzacc = fmaf(fT[s], w4[e], gzacc);
+                    }
+                }
+            }
+            if constexpr (kPair) {
+                // double-buffered pair tiles: this step's barrier also orders
+                // the previous step's reads of the other buffer before its
+                // next writes
+                __syncthreads();
+                const int nchunk = min(8, (H - 2 * hp) * kD / 8);
+                store_pair_rows<OutT>(ct[st & 1][sub], lane, 16 * hh, nchunk, [&](int rrow) {
+                    return reinterpret_cast<uint16_t*>(dq + ((long long)b * N + min(tt + rrow, t1 - 1)) * hstride + 2 * hp * kD);
+                });
+            }
+            __builtin_amdgcn_wave_barrier();
+            asm volatile("" ::: "memory");   // every read of the r, w rows precedes the next writes
+            cur = nxt;
+        }
+    }
+
+    // the two waves of a head add their G in a fixed order
+    const float gz = gzacc + __shfl_xor(gzacc, 32);
+    if (sub == 1) {
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) red[hh][rg * 64 + lane] = accG[rg];
+        if (lane < 32) red[hh][16 * 64 + lane] = gz;
+    }
+    __syncthreads();
+    if (sub == 0 && h < H) {
+        float* dst = gpart + ((((size_t)b * H + h) * NB + beta) * tpb + tib) * SF;
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) {
+            const int j = 8 * (rg >> 2) + 4 * g + (rg & 3);
+            dst[j * SW + i] = accG[rg] + red[hh][rg * 64 + lane];
+        }
+        if (lane < 32) dst[lane * SW + kD] = gz + red[hh][16 * 64 + lane];
+    }
+}
+
 template <typename T> struct Tag { using type = T; };
 template <typename F> void by_dtype(int code, F&& f) {
     if (code == 1)
@@ -1292,6 +1587,19 @@ template <typename F> void by_dtype(int code, F&& f) {
 hipError_t launch_bwd_query(const BwdPlan& bp, const void* q, const void* dout, const float* state, void* dq,
                             float* gpart, float eps, hipStream_t stream) {
     const Plan& pl = bp.fw;
+    if (bp.query_direct) {
+        const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.NB * bp.tpbq);
+        by_dtype(bp.grad_dtype, [&](auto ot) {
+            using OT = typename decltype(ot)::type;
+            const bool qf16 = pl.in_dtype == 2, gf16 = bp.dout_dtype == 2;
+            auto kern = qf16 ? (gf16 ? k_bwd_query_direct<true, true, OT> : k_bwd_query_direct<true, false, OT>)
+                             : (gf16 ? k_bwd_query_direct<false, true, OT> : k_bwd_query_direct<false, false, OT>);
+            hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, static_cast<const uint16_t*>(q),
+                               static_cast<const uint16_t*>(dout), state, static_cast<OT*>(dq), gpart, pl.N, pl.H,
+                               pl.HP, pl.L, pl.NB, bp.tq, bp.tpbq, eps);
+        });
+        return hipGetLastError();
+    }
     if (bp.query_mfma) {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.NB * bp.tpbq);
         by_dtype(bp.dout_dtype, [&](auto gt) {

@@ -107,6 +107,7 @@ struct BwdPlan {
     int tq, tpbq, Pq;    // query tile, query tiles per block, query tiles per (b, h)
     int tk, tpbk;        // key tile, key tiles per block
     int query_mfma, key_mfma;   // 1: matrix-core query / key kernels
+    int query_direct;           // 1: the head-dim-32 query kernel for 16-bit q and dout (per-wave row loads)
     size_t off_gpart, off_ghat, bytes;
 };
 

@@ -373,12 +373,12 @@ def main() -> int:
         ws_st = torch.empty(sana.sana_linattn_workspace_bytes(B, H, C, D, L), dtype=torch.uint8, device=dev)
         carried = torch.empty((B, H, D, D + 1), dtype=torch.float32, device=dev)
         chunks = [[[t[:, c * C:(c + 1) * C].contiguous() for t in st] for c in range(4)] for st in sets]
-        couts = [torch.empty((B, C, H, D), dtype=out_t, device=dev) for _ in range(4)]
+        couts = [[torch.empty((B, C, H, D), dtype=out_t, device=dev) for _ in range(4)] for _ in range(NSETS)]
 
         def fn(i):
             for c in range(4):
                 q, k, v = chunks[i % NSETS][c]
-                sana.sana_linattn_blockcausal_stream_fwd(q, k, v, couts[c], ws_st, L,
+                sana.sana_linattn_blockcausal_stream_fwd(q, k, v, couts[i % NSETS][c], ws_st, L,
                                                          state_in=carried if c else None, state_out=carried,
                                                          eps=w.eps, stream=torch.cuda.current_stream())
         return fn, alg_bytes, ("the headline sequence as 4 chained calls of 4096 tokens with the state carried "
@@ -405,27 +405,33 @@ def main() -> int:
                 f"the headline inputs converted to {str(dt).split('.')[-1]} on the device"
         return build
 
+    # The backward and JVP cases rotate NSETS sets of every buffer they touch:
+    # inputs, dout (or tangents) of their own, and the outputs, so no call
+    # reads or writes what the previous call touched (the 256 MB Infinity
+    # Cache would otherwise serve part of it).
     def case_bwd(dt, Hx=H, Dx=D):
         def build():
             sx = [[t.view(B, N, Hx, Dx).to(dt) for t in st] for st in sets]
-            gx = [torch.empty((B, N, Hx, Dx), dtype=dt, device=dev) for _ in range(3)]
+            dx = [st[0].clone() for st in sx]
+            gx = [[torch.empty((B, N, Hx, Dx), dtype=dt, device=dev) for _ in range(3)] for _ in range(NSETS)]
             wsb = torch.empty(sana.sana_linattn_bwd_workspace_bytes(B, Hx, N, Dx, 0), dtype=torch.uint8, device=dev)
 
             def fn(i):
                 q, k, v = sx[i % NSETS]
-                sana.sana_linattn_bwd(q, k, v, sx[(i + 1) % NSETS][0], *gx, wsb, eps=w.eps,
+                sana.sana_linattn_bwd(q, k, v, dx[i % NSETS], *gx[i % NSETS], wsb, eps=w.eps,
                                       stream=torch.cuda.current_stream())
             es = 4 if dt == torch.float32 else 2
             return fn, w.token_heads * D * es * 7, \
-                f"sana_linattn_bwd, H={Hx}, D={Dx}, {str(dt).split('.')[-1]} q/k/v/dout/gradients (dout another " \
-                f"input set); algorithmic bytes = 7 tensors"
+                f"sana_linattn_bwd, H={Hx}, D={Dx}, {str(dt).split('.')[-1]} q/k/v/dout/gradients; algorithmic " \
+                f"bytes = 7 tensors"
         return build
 
     def case_saved(train):
         """sana_linattn_bwd_from_states on the states a saving forward wrote
         (train: the saving forward, bf16 out, and that backward, one step)."""
         def build():
-            gx = [torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+            gx = [[torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev) for _ in range(3)] for _ in range(NSETS)]
+            dx = [st[0].clone() for st in sets]
             ob = [torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev) for _ in range(NSETS)]
             st = [torch.empty(sana.sana_linattn_states_bytes(B, H, N, D, 0) // 4, dtype=torch.float32, device=dev)
                   for _ in range(NSETS)]
@@ -440,7 +446,7 @@ def main() -> int:
                 if train:
                     sana.sana_linattn_fwd_save_states(q, k, v, ob[i % NSETS], st[i % NSETS], wsb, eps=w.eps,
                                                       stream=torch.cuda.current_stream())
-                sana.sana_linattn_bwd_from_states(q, k, v, sets[(i + 1) % NSETS][0], st[i % NSETS], *gx, wsb,
+                sana.sana_linattn_bwd_from_states(q, k, v, dx[i % NSETS], st[i % NSETS], *gx[i % NSETS], wsb,
                                                   eps=w.eps, stream=torch.cuda.current_stream())
             if train:
                 return fn, w.token_heads * D * 2 * 11, (
@@ -454,18 +460,19 @@ def main() -> int:
     def case_jvp(dt):
         def build():
             sx = [[t.to(dt) for t in st] for st in sets]
+            tx = [[t.clone() for t in st] for st in sx]
             ot = torch.float32
-            jo = [torch.empty((B, N, H, D), dtype=ot, device=dev) for _ in range(2)]
+            jo = [[torch.empty((B, N, H, D), dtype=ot, device=dev) for _ in range(2)] for _ in range(NSETS)]
             wsj = torch.empty(sana.sana_linattn_jvp_workspace_bytes(B, H, N, D, 0), dtype=torch.uint8, device=dev)
 
             def fn(i):
                 q, k, v = sx[i % NSETS]
-                qt, kt, vt = sx[(i + 1) % NSETS]
-                sana.sana_linattn_jvp(q, k, v, qt, kt, vt, *jo, wsj, eps=w.eps, stream=torch.cuda.current_stream())
+                qt, kt, vt = tx[i % NSETS]
+                sana.sana_linattn_jvp(q, k, v, qt, kt, vt, *jo[i % NSETS], wsj, eps=w.eps,
+                                      stream=torch.cuda.current_stream())
             es = 4 if dt == torch.float32 else 2
             return fn, w.token_heads * D * (6 * es + 2 * 4), \
-                "sana_linattn_jvp, fp32 out and out_t; tangents another input set; algorithmic bytes = 6 inputs + " \
-                "2 outputs"
+                "sana_linattn_jvp, fp32 out and out_t; algorithmic bytes = 6 inputs + 2 outputs"
         return build
 
     def case_headdim(Hx, Dx):

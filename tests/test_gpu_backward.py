@@ -131,6 +131,22 @@ def test_backward_head_dim_64_mixed_types(B, N, H, L, dt, gdt):
         check(run(q, k, v, g, L, w.eps, torch.bfloat16), want, torch.bfloat16, w.name + "/bf16grad")
 
 
+D32_MIXED16 = [(2, 1000, 5, 100, workloads.DT_BF16, workloads.DT_F16), (1, 777, 3, 0, workloads.DT_F16, workloads.DT_BF16),
+               (1, 2049, 1, 512, workloads.DT_BF16, workloads.DT_F16)]
+
+
+@pytest.mark.parametrize("B,N,H,L,dt,gdt", D32_MIXED16, ids=[f"B{b}N{n}H{h}L{l}in{t}dout{g}" for b, n, h, l, t, g in D32_MIXED16])
+def test_backward_head_dim_32_mixed_16bit_types(B, N, H, L, dt, gdt):
+    """Head dim 32 with 16-bit q and a 16-bit upstream gradient of the other
+    format (the per-wave query kernel's four q/dout format pairs; identity
+    operands of both formats), ragged tails, odd and single heads, fp32, bf16
+    and fp16 gradients."""
+    w = workloads.Workload(f"bwd32_B{B}N{N}H{H}L{L}in{dt}dout{gdt}", B, N, H, 32, dt, seed=190 + N % 29, block_len=L)
+    (q, k, v, g), want = case(w, gdt)
+    for grad_t in (torch.float32, torch.bfloat16, torch.float16):
+        check(run(q, k, v, g, L, w.eps, grad_t), want, grad_t, f"{w.name}/{grad_t}")
+
+
 def test_backward_single_token_is_identity_in_v():
     """N = 1: out = v * den / (den + eps) does not depend on q or k (their
     exact gradients vanish; what is left is rounding of cancelling terms), and

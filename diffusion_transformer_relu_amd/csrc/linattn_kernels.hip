@@ -574,6 +574,32 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(
                 }
             }
         }
+    } else if (cpb <= 8 && NB > 1) {
+        // each block: its chunk partials added as a fixed pairwise tree of 8
+        // (zeros past cpb); the loads of 4 blocks in flight at once (a
+        // streamed call has few blocks of few chunks each: 2 us less per
+        // call of 4096 tokens; with one block the general path is faster)
+        for (int b0 = 0; b0 < NB; b0 += 4) {
+            float x[4][8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    x[j][c] = src[((size_t)min(b0 + j, NB - 1) * cpb + min(c, cpb - 1)) * SF];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) asm volatile("" : "+v"(x[j][c]));   // all in flight first
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (b0 + j < NB) {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) x[j][c] = c < cpb ? x[j][c] : 0.f;
+                    acc += gscale * (0.f + tree8(x[j]));   // the block sum as the general path forms it
+                    dst[(size_t)(b0 + j) * SF] = acc;
+                }
+            }
+        }
     } else {
         // each block: its chunk partials in groups of 8 added as a fixed
         // pairwise tree, the groups in order

@@ -143,12 +143,41 @@ __global__ __launch_bounds__(kThreads) void k_bwd_merge_suffix(const float* __re
                 }
             }
         }
+    } else if (tpb <= 8) {
+        // 4 blocks' partials in flight at once, last block first (loads take
+        // clamped, always valid indices and are unconditional; entries past
+        // tpb then read as zero): the block-causal shape has 16 blocks of 4
+        for (int b1 = NB; b1 > 0; b1 -= 4) {
+            float x[4][8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    x[j][c] = src[((size_t)max(b1 - 1 - j, 0) * tpb + min(c, tpb - 1)) * SF];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) asm volatile("" : "+v"(x[j][c]));   // all in flight first
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (b1 - 1 - j >= 0) {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) x[j][c] = c < tpb ? x[j][c] : 0.f;
+                    acc += 0.f + tree8(x[j]);   // the block sum as the general path forms it
+                    dst[(size_t)(b1 - 1 - j) * SF] = acc;
+                }
+            }
+        }
     } else if (tpb <= 16) {
         for (int beta = NB - 1; beta >= 0; --beta) {
             const float* blk = src + (size_t)beta * tpb * SF;
             float x[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = (i < tpb) ? blk[(size_t)i * SF] : 0.f;
+            for (int i = 0; i < 16; ++i) x[i] = blk[(size_t)min(i, tpb - 1) * SF];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(x[i]));   // all in flight first
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[i] = i < tpb ? x[i] : 0.f;
             float bs = 0.f;
             bs += tree8(x);
             if (tpb > 8) bs += tree8(x + 8);

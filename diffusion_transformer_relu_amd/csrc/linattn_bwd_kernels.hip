@@ -1336,6 +1336,25 @@ __device__ __forceinline__ void perm_operands(const float* S, int lane, u32x4 (&
     }
 }
 
+// The same for head dim 16: the 32-feature group grp holds heads 2 grp and
+// 2 grp + 1 (the second may not exist: zero), whose states form one
+// block-diagonal 32 x 32 matrix; row i is feature perm_row(i) of head
+// 2 grp + (perm_row(i) >> 4), nonzero in that head's 16 columns only.
+template <typename HeadState>
+__device__ __forceinline__ void perm_operands16(HeadState head, int grp, int HR, int lane, u32x4 (&out)[2][3]) {
+    constexpr int SW = kD / 2 + 1;
+    const int g = lane >> 5, f = perm_row(lane & 31), hr = 2 * grp + (f >> 4);
+    const float* S = head(min(hr, HR - 1));
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        float x[8];
+        const bool on = hr < HR && ks == (f >> 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = on ? S[(f & 15) * SW + 8 * g + e] : 0.f;
+        split3_f32x8(x, out[ks]);
+    }
+}
+
 // Element rg & 7 of operand half rg >> 3 (a packed 16-bit operand) as fp32.
 template <bool F16>
 __device__ __forceinline__ float operand_elem(const u32x4 (&x)[2], int rg) {
@@ -1380,7 +1399,8 @@ __device__ __forceinline__ void put_pair_tile_perm(uint16_t* ct, const f32x16& a
 // store_tile for a permuted-layout fp32 tile: through the wave's LDS tile,
 // then whole 128-byte rows; rows t >= n repeat row n - 1 (same values).
 template <typename RowPtr>
-__device__ __forceinline__ void store_tile_perm(float* ot, const f32x16& acc, int lane, int n, RowPtr dst) {
+__device__ __forceinline__ void store_tile_perm(float* ot, const f32x16& acc, int lane, int n, RowPtr dst,
+                                                int ncols = 32) {
     const int g = lane >> 5, i = lane & 31;
 #pragma unroll
     for (int p = 0; p < 4; ++p)
@@ -1390,7 +1410,7 @@ __device__ __forceinline__ void store_tile_perm(float* ot, const f32x16& acc, in
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
         const int r = 8 * s4 + (lane >> 3), cc = (lane & 7) * 4;
-        store4(dst(min(r, n - 1)) + cc, *reinterpret_cast<const f32x4*>(ot + r * kPitch + cc));
+        if (cc < ncols) store4(dst(min(r, n - 1)) + cc, *reinterpret_cast<const f32x4*>(ot + r * kPitch + cc));
     }
     __builtin_amdgcn_wave_barrier();
 }
@@ -1433,16 +1453,19 @@ __device__ __forceinline__ void load_rows16(const uint16_t* x, const uint16_t* y
 // fp32 dq: each wave stores its own rows through its LDS tile.  At the end the
 // two waves of a head add their G in a fixed order and write the tile's
 // partial gradient state (zero for a tile with no tokens).
-template <bool QF16, bool GF16, typename OutT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(OutT) == 4 ? 2 : 3, 8))) void k_bwd_query_direct(
+template <bool QF16, bool GF16, typename OutT, int HD>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(OutT) == 4 || HD == kD / 2 ? 2 : 3, 8))) void k_bwd_query_direct(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout, const float* __restrict__ state,
-    OutT* __restrict__ dq, float* __restrict__ gpart, int N, int H, int HP, int L, int NB, int tile, int tpb,
-    float eps) {
-    constexpr int SW = kD + 1, SF = kD * SW;
+    OutT* __restrict__ dq, float* __restrict__ gpart, int N, int H, int HP, int HR, int L, int NB, int tile,
+    int tpb, float eps) {
+    constexpr bool D16 = HD == kD / 2;
+    static_assert(HD == kD || D16, "head dims 32 and 16");
+    constexpr int NS = D16 ? 2 : 1;   // heads per 32-feature group
+    constexpr int SW = HD + 1, SF = HD * SW;
     constexpr bool kPair = sizeof(OutT) == 2;
     __shared__ __attribute__((aligned(16))) uint16_t ct[kPair ? 2 : 1][kPair ? 2 : 1][kPair ? 32 * kPairRow : 8];   // [step & 1][sub]
     __shared__ __attribute__((aligned(16))) float otile[kPair ? 1 : 4][kPair ? 4 : 32 * kPitch];
-    __shared__ __attribute__((aligned(16))) float rw[4][2][32];   // r and w of each wave's tokens
+    __shared__ __attribute__((aligned(16))) float rw[4][NS][2][32];   // r and w of each wave's tokens (per head)
     __shared__ __attribute__((aligned(16))) float red[2][16 * 64 + 32];   // the second waves' G
 
     const int per_unit = NB * tpb;
@@ -1457,15 +1480,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     const int t0 = blk0 + tib * tile, t1 = min(t0 + tile, blk1);
     const int g = lane >> 5, i = lane & 31;
 
-    const float* P = state + (((size_t)b * H + hs) * NB + beta) * SF;
+    auto head_P = [&](int hr) { return state + (((size_t)b * HR + hr) * NB + beta) * SF; };
+    const bool second = !D16 || 2 * hs + 1 < HR;   // head dim 16: group hs has a second head
     f32x16 accG = {};
     float gzacc = 0.f;   // lane (g, j): sum over this lane's tokens of f_j w
     if (t0 < t1) {       // uniform over the work-group
         u32x4 pa[2][3];
-        perm_operands(P, lane, pa);
         float zr[16];
+        if constexpr (D16) {
+            perm_operands16(head_P, hs, HR, lane, pa);
 #pragma unroll
-        for (int rg = 0; rg < 16; ++rg) zr[rg] = P[perm_feature(g, rg) * SW + kD];
+            for (int rg = 0; rg < 16; ++rg) {
+                const int f = perm_feature(g, rg), hr = 2 * hs + (f >> 4);
+                zr[rg] = hr < HR ? head_P(hr)[(f & 15) * SW + HD] : 0.f;
+            }
+        } else {
+            const float* P = head_P(hs);
+            perm_operands(P, lane, pa);
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) zr[rg] = P[perm_feature(g, rg) * SW + HD];
+        }
         // identity operands: element e of K-step ks is one where 16 ks + 8 g + e = i
         u32x4 iq[2], ig[2];
 #pragma unroll
@@ -1478,33 +1512,59 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
                 ig[ks][d] = (e0 == i ? og : 0u) | (e0 + 1 == i ? og << 16 : 0u);
             }
 
-        const long long hstride = (long long)H * kD;
+        const long long hstride = (long long)HR * HD;
         auto row_off = [&](int tt) { return ((long long)b * N + min(tt + i, t1 - 1)) * hstride + hs * kD + 8 * g; };
+        // a lone head of dim 16 has no features 16.. (they are read as zero)
+        auto load = [&](int tt, Rows16& r) {
+            if (second) {
+                load_rows16(q, dout, row_off(tt), r);
+            } else {
+                const long long o = row_off(tt);
+                r.x[0] = *reinterpret_cast<const u32x4*>(q + o);
+                r.y[0] = *reinterpret_cast<const u32x4*>(dout + o);
+                r.x[1] = r.y[1] = (u32x4){0u, 0u, 0u, 0u};
+            }
+        };
         const int steps = (t1 - t0 + 63) / 64;
         int tt = t0 + 32 * sub;
         Rows16 cur;   // x: q, y: dout
-        load_rows16(q, dout, row_off(tt), cur);
+        load(tt, cur);
         for (int st = 0; st < steps; ++st, tt += 64) {
             Rows16 nxt;
-            load_rows16(q, dout, row_off(tt + 64), nxt);   // in flight during this sub-tile's work
+            load(tt + 64, nxt);   // in flight during this sub-tile's work
             const int n = min(32, t1 - tt);
             const u32x4 fq[2] = {relu_bf16x8(cur.x[0]), relu_bf16x8(cur.x[1])};
-            float dp = 0.f;
+            // per head of the group (head dim 16: registers rg >> 3 = head)
+            float dp[NS] = {};
 #pragma unroll
-            for (int rg = 0; rg < 16; ++rg) dp = fmaf(operand_elem<QF16>(fq, rg), zr[rg], dp);
-            const float r = 1.0f / (dp + __shfl_xor(dp, 32) + eps);
+            for (int rg = 0; rg < 16; ++rg) {
+                float& d = dp[D16 ? rg >> 3 : 0];
+                d = fmaf(operand_elem<QF16>(fq, rg), zr[rg], d);
+            }
+            float r[NS], w[NS];
+#pragma unroll
+            for (int s2 = 0; s2 < NS; ++s2) r[s2] = 1.0f / (dp[s2] + __shfl_xor(dp[s2], 32) + eps);
             f32x16 acc = {};
             acc = mma_split_ks<GF16, 2>(pa, cur.y, acc);
-            float go = 0.f;
+            float go[NS] = {};
 #pragma unroll
-            for (int rg = 0; rg < 16; ++rg) go = fmaf(operand_elem<QF16>(fq, rg), acc[rg], go);
-            const float w = -r * ((go + __shfl_xor(go, 32)) * r);
+            for (int rg = 0; rg < 16; ++rg) {
+                float& o = go[D16 ? rg >> 3 : 0];
+                o = fmaf(operand_elem<QF16>(fq, rg), acc[rg], o);
+            }
 #pragma unroll
-            for (int rg = 0; rg < 16; ++rg)
-                acc[rg] = operand_elem<QF16>(fq, rg) > 0.f ? fmaf(zr[rg], w, acc[rg] * r) : 0.f;
+            for (int s2 = 0; s2 < NS; ++s2) w[s2] = -r[s2] * ((go[s2] + __shfl_xor(go[s2], 32)) * r[s2]);
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) {
+                const int s2 = D16 ? rg >> 3 : 0;
+                acc[rg] = operand_elem<QF16>(fq, rg) > 0.f ? fmaf(zr[rg], w[s2], acc[rg] * r[s2]) : 0.f;
+            }
             if (g == 0) {   // zero past the range: the G sums skip those tokens
-                rw[wave][0][i] = i < n ? r : 0.f;
-                rw[wave][1][i] = i < n ? w : 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < NS; ++s2) {
+                    rw[wave][s2][0][i] = i < n ? r[s2] : 0.f;
+                    rw[wave][s2][1][i] = i < n ? w[s2] : 0.f;
+                }
             }
             // f^T and dout^T: lane (g, j) gets feature j of tokens 8 rr + 4 g + e
             f32x16 fT = {}, gT = {};
@@ -1517,7 +1577,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
             } else if (n > 0 && h < H) {
                 store_tile_perm(otile[wave], acc, lane, n, [&](int t) {
                     return reinterpret_cast<float*>(dq + ((long long)b * N + tt + t) * hstride + h * kD);
-                });
+                }, min(32, HR * HD - h * kD));
             }
             __builtin_amdgcn_wave_barrier();
             asm volatile("" ::: "memory");   // the r, w rows are written before they are read
@@ -1529,8 +1589,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2) {
                         const int rr = 2 * ks + h2;
-                        const f32x4 r4 = *reinterpret_cast<const f32x4*>(&rw[wave][0][8 * rr + 4 * g]);
-                        const f32x4 w4 = *reinterpret_cast<const f32x4*>(&rw[wave][1][8 * rr + 4 * g]);
+                        const f32x4 r4 = *reinterpret_cast<const f32x4*>(&rw[wave][D16 ? i >> 4 : 0][0][8 * rr + 4 * g]);
+                        const f32x4 w4 = *reinterpret_cast<const f32x4*>(&rw[wave][D16 ? i >> 4 : 0][1][8 * rr + 4 * g]);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int s = 4 * rr + e;
@@ -1556,8 +1616,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
             } else {
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
-                    const f32x4 r4 = *reinterpret_cast<const f32x4*>(&rw[wave][0][8 * rr + 4 * g]);
-                    const f32x4 w4 = *reinterpret_cast<const f32x4*>(&rw[wave][1][8 * rr + 4 * g]);
+                    const f32x4 r4 = *reinterpret_cast<const f32x4*>(&rw[wave][D16 ? i >> 4 : 0][0][8 * rr + 4 * g]);
+                    const f32x4 w4 = *reinterpret_cast<const f32x4*>(&rw[wave][D16 ? i >> 4 : 0][1][8 * rr + 4 * g]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int s = 4 * rr + e;
@@ -1571,7 +1631,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
                 // the previous step's reads of the other buffer before its
                 // next writes
                 __syncthreads();
-                const int nchunk = min(8, (H - 2 * hp) * kD / 8);
+                const int nchunk = min(8, (HR * HD - 2 * hp * kD) / 8);
                 store_pair_rows<OutT>(ct[st & 1][sub], lane, 16 * hh, nchunk, [&](int rrow) {
                     return reinterpret_cast<uint16_t*>(dq + ((long long)b * N + min(tt + rrow, t1 - 1)) * hstride + 2 * hp * kD);
                 });
@@ -1591,13 +1651,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     }
     __syncthreads();
     if (sub == 0 && h < H) {
-        float* dst = gpart + ((((size_t)b * H + h) * NB + beta) * tpb + tib) * SF;
+        auto part_of = [&](int hr) { return gpart + ((((size_t)b * HR + hr) * NB + beta) * tpb + tib) * SF; };
+        if constexpr (D16) {
+            // the diagonal 16 x 16 blocks: rows 0..15 and the lanes of columns
+            // 0..15 are the first head's, the rest the second's
 #pragma unroll
-        for (int rg = 0; rg < 16; ++rg) {
-            const int j = 8 * (rg >> 2) + 4 * g + (rg & 3);
-            dst[j * SW + i] = accG[rg] + red[hh][rg * 64 + lane];
+            for (int rg = 0; rg < 16; ++rg) {
+                const int j = 8 * (rg >> 2) + 4 * g + (rg & 3), hr = 2 * h + (j >> 4);
+                if ((i >> 4) == (j >> 4) && hr < HR)
+                    part_of(hr)[(j & 15) * SW + (i & 15)] = accG[rg] + red[hh][rg * 64 + lane];
+            }
+            if (lane < 32 && 2 * h + (lane >> 4) < HR)
+                part_of(2 * h + (lane >> 4))[(lane & 15) * SW + HD] = gz + red[hh][16 * 64 + lane];
+        } else {
+            float* dst = part_of(h);
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) {
+                const int j = 8 * (rg >> 2) + 4 * g + (rg & 3);
+                dst[j * SW + i] = accG[rg] + red[hh][rg * 64 + lane];
+            }
+            if (lane < 32) dst[lane * SW + HD] = gz + red[hh][16 * 64 + lane];
         }
-        if (lane < 32) dst[lane * SW + kD] = gz + red[hh][16 * 64 + lane];
     }
 }
 
@@ -1621,11 +1695,15 @@ hipError_t launch_bwd_query(const BwdPlan& bp, const void* q, const void* dout, 
         by_dtype(bp.grad_dtype, [&](auto ot) {
             using OT = typename decltype(ot)::type;
             const bool qf16 = pl.in_dtype == 2, gf16 = bp.dout_dtype == 2;
-            auto kern = qf16 ? (gf16 ? k_bwd_query_direct<true, true, OT> : k_bwd_query_direct<true, false, OT>)
-                             : (gf16 ? k_bwd_query_direct<false, true, OT> : k_bwd_query_direct<false, false, OT>);
+            auto pick = [&](auto dd) {
+                constexpr int DD = decltype(dd)::value;
+                return qf16 ? (gf16 ? k_bwd_query_direct<true, true, OT, DD> : k_bwd_query_direct<true, false, OT, DD>)
+                            : (gf16 ? k_bwd_query_direct<false, true, OT, DD> : k_bwd_query_direct<false, false, OT, DD>);
+            };
+            auto kern = pl.D == kD / 2 ? pick(std::integral_constant<int, kD / 2>{}) : pick(std::integral_constant<int, kD>{});
             hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, static_cast<const uint16_t*>(q),
-                               static_cast<const uint16_t*>(dout), state, static_cast<OT*>(dq), gpart, pl.N, pl.H,
-                               pl.HP, pl.L, pl.NB, bp.tq, bp.tpbq, eps);
+                               static_cast<const uint16_t*>(dout), state, static_cast<OT*>(dq), gpart, pl.N,
+                               groups32(pl), pl.HP, pl.H, pl.L, pl.NB, bp.tq, bp.tpbq, eps);
         });
         return hipGetLastError();
     }

@@ -131,17 +131,21 @@ def test_backward_head_dim_64_mixed_types(B, N, H, L, dt, gdt):
         check(run(q, k, v, g, L, w.eps, torch.bfloat16), want, torch.bfloat16, w.name + "/bf16grad")
 
 
-D32_MIXED16 = [(2, 1000, 5, 100, workloads.DT_BF16, workloads.DT_F16), (1, 777, 3, 0, workloads.DT_F16, workloads.DT_BF16),
-               (1, 2049, 1, 512, workloads.DT_BF16, workloads.DT_F16)]
+MIXED16 = [(2, 1000, 5, 100, workloads.DT_BF16, workloads.DT_F16, 32), (1, 777, 3, 0, workloads.DT_F16, workloads.DT_BF16, 32),
+           (1, 2049, 1, 512, workloads.DT_BF16, workloads.DT_F16, 32), (1, 777, 7, 100, workloads.DT_BF16, workloads.DT_F16, 16),
+           (2, 1000, 3, 0, workloads.DT_F16, workloads.DT_BF16, 16), (1, 513, 1, 64, workloads.DT_BF16, workloads.DT_BF16, 16)]
 
 
-@pytest.mark.parametrize("B,N,H,L,dt,gdt", D32_MIXED16, ids=[f"B{b}N{n}H{h}L{l}in{t}dout{g}" for b, n, h, l, t, g in D32_MIXED16])
-def test_backward_head_dim_32_mixed_16bit_types(B, N, H, L, dt, gdt):
-    """Head dim 32 with 16-bit q and a 16-bit upstream gradient of the other
-    format (the per-wave query kernel's four q/dout format pairs; identity
-    operands of both formats), ragged tails, odd and single heads, fp32, bf16
-    and fp16 gradients."""
-    w = workloads.Workload(f"bwd32_B{B}N{N}H{H}L{L}in{dt}dout{gdt}", B, N, H, 32, dt, seed=190 + N % 29, block_len=L)
+@pytest.mark.parametrize("B,N,H,L,dt,gdt,D", MIXED16,
+                         ids=[f"B{b}N{n}H{h}L{l}in{t}dout{g}D{d}" for b, n, h, l, t, g, d in MIXED16])
+def test_backward_mixed_16bit_types(B, N, H, L, dt, gdt, D):
+    """Head dims 32 and 16 with 16-bit q and a 16-bit upstream gradient of
+    either format (the per-wave query kernel's four q/dout format pairs;
+    identity operands of both formats), ragged tails, odd and single heads
+    (head dim 16: a group that is a lone head), fp32, bf16 and fp16
+    gradients."""
+    w = workloads.Workload(f"bwdmix_B{B}N{N}H{H}L{L}in{dt}dout{gdt}D{D}", B, N, H, D, dt, seed=190 + N % 29 + D,
+                           block_len=L)
     (q, k, v, g), want = case(w, gdt)
     for grad_t in (torch.float32, torch.bfloat16, torch.float16):
         check(run(q, k, v, g, L, w.eps, grad_t), want, grad_t, f"{w.name}/{grad_t}")

@@ -282,12 +282,12 @@ int make_bwd_plan(int in_dtype, int dout_dtype, int grad_dtype, int B, int H, in
         const int per_cu = pl.mfma16 ? 3 : 2;
         if (bp->key_mfma) bp->tk = tile_for(D == 2 * sana::kD ? 2 : per_cu);
         if (bp->query_mfma) bp->tq = tile_for(D == 2 * sana::kD ? 2 : per_cu);
-        // head dims 32 and 16 with 16-bit inputs: the query kernel that loads
-        // its rows per wave (16-bit dout); for it and the 16-bit key kernel
-        // tiles sized for 2 work-groups per CU: they run faster with fewer,
-        // longer work-groups (490 of 1216 tokens at 16384 x 70) than with
-        // every slot of the CUs filled
-        bp->query_direct = pl.mfma16 && D <= sana::kD && dout_dtype != SANA_DT_F32;
+        // 16-bit inputs and dout: the query kernels that load their rows per
+        // wave (every head dim); for them and the 16-bit key kernel at head
+        // dims 32 and 16 tiles sized for 2 work-groups per CU: they run faster
+        // with fewer, longer work-groups (490 of 1216 tokens at 16384 x 70)
+        // than with every slot of the CUs filled
+        bp->query_direct = pl.mfma16 && dout_dtype != SANA_DT_F32;
         if (pl.mfma16 && D <= sana::kD) bp->tk = tile_for(2);
         if (bp->query_direct) bp->tq = tile_for(2);
         if (const int t = env_positive("SANA_LINATTN_BWD_TILE"))

@@ -1675,6 +1675,229 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     }
 }
 
+// ------------------------------------------------------------------ query pass, head dim 64, 16-bit q and dout
+// The per-wave scheme of k_bwd_query_direct for a head of 64 features, seen
+// as two 32-feature groups.  grid.x = (b * HR + hq) * (NB * tpb) + beta * tpb
+// + tile; wave w works on group a = w & 1 of head hq and the 32-query
+// sub-tiles 32 (w >> 1) + 64 s, next to the wave of the other group on the
+// same queries.  Per sub-tile, with P the head's 64 x 65 state (rows 32 a ..
+// of group a, permuted as perm_row does):
+//   den_a = f_a . z_a, m_a = P[32 a .., :64] dout^T (four K-steps: dout of
+//   both groups is loaded by each wave), f_a . m_a;
+//   the two waves exchange den_a and f_a . m_a through LDS (a work-group
+//   barrier) and both form den = den_0 + den_1, dout . num = f_0 . m_0 +
+//   f_1 . m_1 in that order, r and w;
+//   dq_a = [q_a > 0] (r m_a + w z_a) into the head's pair tile (group a in
+//   its half of each 128-byte line);
+//   G[32 a .., 32 b ..] += f_a^T u_b for b = 0, 1 (f_a^T and dout_b^T from
+//   identity MFMAs, u_b = r dout_b^T split into three bf16 terms; bf16 q;
+//   fp32 products 32 x 32 x 2 for fp16 q), G_z[32 a ..] += f_a^T w.
+// Every wave takes every step (a step past the range works on the clamped
+// last row), so the barriers are reached by all.  At the end the two waves of
+// a group add their G in a fixed order and write rows 32 a .. of the tile's
+// partial gradient state (zero for a tile with no tokens).
+template <bool QF16, bool GF16, typename OutT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_bwd_query_direct64(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout, const float* __restrict__ state,
+    OutT* __restrict__ dq, float* __restrict__ gpart, int N, int HR, int L, int NB, int tile, int tpb, float eps) {
+    constexpr int HD = 2 * kD, SW = HD + 1, SF = HD * SW;
+    constexpr bool kPair = sizeof(OutT) == 2;
+    __shared__ __attribute__((aligned(16))) uint16_t ct[kPair ? 2 : 1][kPair ? 2 : 1][kPair ? 32 * kPairRow : 8];   // [step & 1][sub]
+    __shared__ __attribute__((aligned(16))) float otile[kPair ? 1 : 4][kPair ? 4 : 32 * kPitch];
+    __shared__ __attribute__((aligned(16))) float rw[4][2][32];        // r and w of each wave's tokens
+    __shared__ __attribute__((aligned(16))) float xch[2][2][2][32];    // [sub][group][den, f . m] partial sums
+    __shared__ __attribute__((aligned(16))) float red[2][2 * 16 * 64 + 32];   // the second waves' G
+
+    const int per_unit = NB * tpb;
+    const int tau = blockIdx.x % per_unit;
+    const int bh = blockIdx.x / per_unit;
+    const int hq = bh % HR, b = bh / HR;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int a = wave & 1, sub = wave >> 1;
+    const int beta = tau / tpb, tib = tau - beta * tpb;
+    const int blk0 = beta * L, blk1 = min(blk0 + L, N);
+    const int t0 = blk0 + tib * tile, t1 = min(t0 + tile, blk1);
+    const int g = lane >> 5, i = lane & 31;
+
+    const float* P = state + (((size_t)b * HR + hq) * NB + beta) * SF;
+    f32x16 accG[2] = {};
+    float gzacc = 0.f;   // lane (g, j): sum over this lane's tokens of f_(32 a + j) w
+    if (t0 < t1) {       // uniform over the work-group
+        // P rows 32 a + perm_row(i), all 64 columns (four K-steps)
+        u32x4 pa[4][3];
+        {
+            const int ri = kD * a + perm_row(i);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = P[ri * SW + 16 * ks + 8 * g + e];
+                split3_f32x8(x, pa[ks]);
+            }
+        }
+        float zr[16];
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) zr[rg] = P[(kD * a + perm_feature(g, rg)) * SW + HD];
+        // identity operands: element e of K-step ks is one where 16 ks + 8 g + e = i
+        u32x4 iq[2], ig[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int e0 = 16 * ks + 8 * g + 2 * d;
+                const uint32_t oq = QF16 ? 0x3c00u : 0x3f80u, og = GF16 ? 0x3c00u : 0x3f80u;
+                iq[ks][d] = (e0 == i ? oq : 0u) | (e0 + 1 == i ? oq << 16 : 0u);
+                ig[ks][d] = (e0 == i ? og : 0u) | (e0 + 1 == i ? og << 16 : 0u);
+            }
+
+        const long long hstride = (long long)HR * HD;
+        struct Rows {
+            u32x4 x[2], y[4];   // q of group a; dout of both groups
+        };
+        auto load = [&](int tt, Rows& r) {
+            const long long row = ((long long)b * N + min(tt + i, t1 - 1)) * hstride + hq * HD + 8 * g;
+            const u32x4* px = reinterpret_cast<const u32x4*>(q + row + kD * a);
+            const u32x4* py = reinterpret_cast<const u32x4*>(dout + row);
+            r.x[0] = px[0];
+            r.x[1] = px[2];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) r.y[ks] = py[2 * ks];
+        };
+        const int steps = (t1 - t0 + 63) / 64;
+        int tt = t0 + 32 * sub;
+        Rows cur;
+        load(tt, cur);
+        for (int st = 0; st < steps; ++st, tt += 64) {
+            Rows nxt;
+            load(tt + 64, nxt);   // in flight during this sub-tile's work
+            const int n = min(32, t1 - tt);
+            const u32x4 fq[2] = {relu_bf16x8(cur.x[0]), relu_bf16x8(cur.x[1])};
+            float dp = 0.f;
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) dp = fmaf(operand_elem<QF16>(fq, rg), zr[rg], dp);
+            f32x16 acc = {};
+            acc = mma_split_ks<GF16, 4>(pa, cur.y, acc);
+            float go = 0.f;
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) go = fmaf(operand_elem<QF16>(fq, rg), acc[rg], go);
+            dp += __shfl_xor(dp, 32);
+            go += __shfl_xor(go, 32);
+            if (g == 0) {
+                xch[sub][a][0][i] = dp;
+                xch[sub][a][1][i] = go;
+            }
+            __syncthreads();   // both groups' partial sums are in xch
+            const float r = 1.0f / (xch[sub][0][0][i] + xch[sub][1][0][i] + eps);
+            const float w = -r * ((xch[sub][0][1][i] + xch[sub][1][1][i]) * r);
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg)
+                acc[rg] = operand_elem<QF16>(fq, rg) > 0.f ? fmaf(zr[rg], w, acc[rg] * r) : 0.f;
+            if (g == 0) {   // zero past the range: the G sums skip those tokens
+                rw[wave][0][i] = i < n ? r : 0.f;
+                rw[wave][1][i] = i < n ? w : 0.f;
+            }
+            f32x16 fT = {};
+            fT = mfma16<QF16>(fq[0], iq[0], fT);
+            fT = mfma16<QF16>(fq[1], iq[1], fT);
+            if constexpr (kPair) {
+                put_pair_tile_perm<OutT>(ct[st & 1][sub], acc, lane, a);
+            } else if (n > 0) {
+                store_tile_perm(otile[wave], acc, lane, n, [&](int t) {
+                    return reinterpret_cast<float*>(dq + ((long long)b * N + tt + t) * hstride + hq * HD + kD * a);
+                });
+            }
+            __builtin_amdgcn_wave_barrier();
+            asm volatile("" ::: "memory");   // the r, w rows are written before they are read
+#pragma unroll
+            for (int bg = 0; bg < 2; ++bg) {
+                f32x16 gT = {};
+                gT = mfma16<GF16>(cur.y[2 * bg], ig[0], gT);
+                gT = mfma16<GF16>(cur.y[2 * bg + 1], ig[1], gT);
+                if constexpr (!QF16) {
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        float uu[8];
+                        u32x4 fp;
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; ++h2) {
+                            const int rr = 2 * ks + h2;
+                            const f32x4 r4 = *reinterpret_cast<const f32x4*>(&rw[wave][0][8 * rr + 4 * g]);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) uu[4 * h2 + e] = gT[4 * rr + e] * r4[e];
+#pragma unroll
+                            for (int d = 0; d < 2; ++d) {
+                                // through scalars: bit_cast of a vector element
+                                // expression reads the vector's first element
+                                // with this compiler
+                                const float f0 = fT[4 * rr + 2 * d], f1 = fT[4 * rr + 2 * d + 1];
+                                fp[2 * h2 + d] = (__builtin_bit_cast(uint32_t, f0) >> 16) |
+                                                 (__builtin_bit_cast(uint32_t, f1) & 0xffff0000u);
+                            }
+                        }
+                        u32x4 ut[3];
+                        split3_trunc_f32x8(uu, ut);
+                        accG[bg] = mfma_bf16(fp, ut[2], accG[bg]);
+                        accG[bg] = mfma_bf16(fp, ut[1], accG[bg]);
+                        accG[bg] = mfma_bf16(fp, ut[0], accG[bg]);
+                    }
+                } else {
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const f32x4 r4 = *reinterpret_cast<const f32x4*>(&rw[wave][0][8 * rr + 4 * g]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int s = 4 * rr + e;
+                            accG[bg] = __builtin_amdgcn_mfma_f32_32x32x2f32(fT[s], gT[s] * r4[e], accG[bg], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const f32x4 w4 = *reinterpret_cast<const f32x4*>(&rw[wave][1][8 * rr + 4 * g]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) gzacc = fmaf(fT[4 * rr + e], w4[e], gzacc);
+            }
+            if constexpr (kPair) {
+                // double-buffered pair tiles (the head's 128-byte rows): this
+                // step's barrier also orders the previous step's reads of the
+                // other buffer before its next writes
+                __syncthreads();
+                store_pair_rows<OutT>(ct[st & 1][sub], lane, 16 * a, 8, [&](int rrow) {
+                    return reinterpret_cast<uint16_t*>(dq + ((long long)b * N + min(tt + rrow, t1 - 1)) * hstride + hq * HD);
+                });
+            } else {
+                __syncthreads();   // every read of xch precedes the next step's writes
+            }
+            __builtin_amdgcn_wave_barrier();
+            asm volatile("" ::: "memory");   // every read of the r, w rows precedes the next writes
+            cur = nxt;
+        }
+    }
+
+    // the two waves of a group add their G in a fixed order
+    const float gz = gzacc + __shfl_xor(gzacc, 32);
+    if (sub == 1) {
+#pragma unroll
+        for (int bg = 0; bg < 2; ++bg)
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) red[a][(bg * 16 + rg) * 64 + lane] = accG[bg][rg];
+        if (lane < 32) red[a][2 * 16 * 64 + lane] = gz;
+    }
+    __syncthreads();
+    if (sub == 0) {
+        float* dst = gpart + ((((size_t)b * HR + hq) * NB + beta) * tpb + tib) * SF;
+#pragma unroll
+        for (int bg = 0; bg < 2; ++bg)
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) {
+                const int j = 8 * (rg >> 2) + 4 * g + (rg & 3);
+                dst[(kD * a + j) * SW + kD * bg + i] = accG[bg][rg] + red[a][(bg * 16 + rg) * 64 + lane];
+            }
+        if (lane < 32) dst[(kD * a + lane) * SW + HD] = gz + red[a][2 * 16 * 64 + lane];
+    }
+}
+
 template <typename T> struct Tag { using type = T; };
 template <typename F> void by_dtype(int code, F&& f) {
     if (code == 1)
@@ -1700,6 +1923,14 @@ hipError_t launch_bwd_query(const BwdPlan& bp, const void* q, const void* dout, 
                 return qf16 ? (gf16 ? k_bwd_query_direct<true, true, OT, DD> : k_bwd_query_direct<true, false, OT, DD>)
                             : (gf16 ? k_bwd_query_direct<false, true, OT, DD> : k_bwd_query_direct<false, false, OT, DD>);
             };
+            if (pl.D == 2 * kD) {
+                auto kern64 = qf16 ? (gf16 ? k_bwd_query_direct64<true, true, OT> : k_bwd_query_direct64<true, false, OT>)
+                                   : (gf16 ? k_bwd_query_direct64<false, true, OT> : k_bwd_query_direct64<false, false, OT>);
+                hipLaunchKernelGGL(kern64, dim3(grid), dim3(kThreads), 0, stream, static_cast<const uint16_t*>(q),
+                                   static_cast<const uint16_t*>(dout), state, static_cast<OT*>(dq), gpart, pl.N, pl.H,
+                                   pl.L, pl.NB, bp.tq, bp.tpbq, eps);
+                return;
+            }
             auto kern = pl.D == kD / 2 ? pick(std::integral_constant<int, kD / 2>{}) : pick(std::integral_constant<int, kD>{});
             hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, static_cast<const uint16_t*>(q),
                                static_cast<const uint16_t*>(dout), state, static_cast<OT*>(dq), gpart, pl.N,

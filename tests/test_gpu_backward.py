@@ -133,14 +133,15 @@ def test_backward_head_dim_64_mixed_types(B, N, H, L, dt, gdt):
 
 MIXED16 = [(2, 1000, 5, 100, workloads.DT_BF16, workloads.DT_F16, 32), (1, 777, 3, 0, workloads.DT_F16, workloads.DT_BF16, 32),
            (1, 2049, 1, 512, workloads.DT_BF16, workloads.DT_F16, 32), (1, 777, 7, 100, workloads.DT_BF16, workloads.DT_F16, 16),
-           (2, 1000, 3, 0, workloads.DT_F16, workloads.DT_BF16, 16), (1, 513, 1, 64, workloads.DT_BF16, workloads.DT_BF16, 16)]
+           (2, 1000, 3, 0, workloads.DT_F16, workloads.DT_BF16, 16), (1, 513, 1, 64, workloads.DT_BF16, workloads.DT_BF16, 16),
+           (1, 777, 3, 100, workloads.DT_BF16, workloads.DT_F16, 64), (2, 333, 2, 0, workloads.DT_F16, workloads.DT_BF16, 64)]
 
 
 @pytest.mark.parametrize("B,N,H,L,dt,gdt,D", MIXED16,
                          ids=[f"B{b}N{n}H{h}L{l}in{t}dout{g}D{d}" for b, n, h, l, t, g, d in MIXED16])
 def test_backward_mixed_16bit_types(B, N, H, L, dt, gdt, D):
-    """Head dims 32 and 16 with 16-bit q and a 16-bit upstream gradient of
-    either format (the per-wave query kernel's four q/dout format pairs;
+    """Head dims 32, 16 and 64 with 16-bit q and a 16-bit upstream gradient
+    of either format (the per-wave query kernels' four q/dout format pairs;
     identity operands of both formats), ragged tails, odd and single heads
     (head dim 16: a group that is a lone head), fp32, bf16 and fp16
     gradients."""

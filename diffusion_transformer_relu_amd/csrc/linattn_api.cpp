@@ -485,14 +485,18 @@ int sana_linattn_workspace_bytes(int B, int H, int N, int D, int block_len, size
 
 int sana_linattn_bwd_workspace_bytes(int B, int H, int N, int D, int block_len, size_t* bytes) {
     if (!bytes) return SANA_ERR_INVALID_ARG;
+    // the plan (its query tiles, and so the partial gradient states) depends
+    // on the input type (16-bit or fp32) and on whether dout is 16-bit: the
+    // most any of them needs
     size_t most = 0;
     for (int dt : {SANA_DT_BF16, SANA_DT_F32})
-        for (bool mf : {true, false}) {   // the vector path's plan too (SANA_LINATTN_PATH=valu)
-            sana::BwdPlan bp;
-            const int st = make_bwd_plan(dt, SANA_DT_F32, SANA_DT_F32, B, H, N, D, block_len, &bp, mf);
-            if (st != SANA_OK) return st;
-            most = std::max(most, bp.bytes);
-        }
+        for (int gt : {SANA_DT_BF16, SANA_DT_F32})
+            for (bool mf : {true, false}) {   // the vector path's plan too (SANA_LINATTN_PATH=valu)
+                sana::BwdPlan bp;
+                const int st = make_bwd_plan(dt, gt, SANA_DT_F32, B, H, N, D, block_len, &bp, mf);
+                if (st != SANA_OK) return st;
+                most = std::max(most, bp.bytes);
+            }
     *bytes = most;
     return SANA_OK;
 }

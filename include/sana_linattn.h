@@ -278,7 +278,10 @@ SANA_API int sana_linattn_fwd_stages(const void* q, const void* k, const void* v
  *               each other, an input or the workspace (error ALIAS).
  *   block_len   0 = non-causal, >= 1 = block-causal.
  *   workspace   >= sana_linattn_bwd_workspace_bytes(B, H, N, D, block_len)
- *               bytes, 256-byte aligned.
+ *               bytes, 256-byte aligned (the query covers every combination
+ *               of input, dout and gradient types; like the forward's, it
+ *               depends on the tuning environment variables, here also
+ *               SANA_LINATTN_BWD_TILE).
  * Other conventions as for sana_linattn_fwd (16-byte alignment of the tensors,
  * empty problems, error codes, asynchronous on `stream`, bitwise repeatable).
  */

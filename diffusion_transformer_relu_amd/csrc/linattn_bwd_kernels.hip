@@ -1940,35 +1940,39 @@ hipError_t launch_bwd_query(const BwdPlan& bp, const void* q, const void* dout, 
     }
     if (bp.query_mfma) {
         const unsigned grid = (unsigned)((size_t)pl.B * pl.HP * pl.NB * bp.tpbq);
+        bool routed = true;
         by_dtype(bp.dout_dtype, [&](auto gt) {
             by_dtype(bp.grad_dtype, [&](auto ot) {
                 using GT = typename decltype(gt)::type;
                 using OT = typename decltype(ot)::type;
                 by_dtype(pl.in_dtype, [&](auto it) {
                     using QT = typename decltype(it)::type;
-                    if (pl.D == 2 * kD) {
-                        hipLaunchKernelGGL((k_bwd_query_mfma64<QT, GT, OT>), dim3(grid), dim3(kThreads), 0, stream,
-                                           static_cast<const QT*>(q), static_cast<const GT*>(dout), state,
-                                           static_cast<OT*>(dq), gpart, pl.N, pl.H, pl.L, pl.NB, bp.tq, bp.tpbq, eps);
-                        return;
-                    }
-                    {
-                        if (pl.D == kD / 2) {
+                    // 16-bit q with a 16-bit dout takes the per-wave kernels
+                    // above: only combinations with an fp32 q or dout come here
+                    if constexpr (std::is_same<QT, float>::value || std::is_same<GT, float>::value) {
+                        if (pl.D == 2 * kD) {
+                            hipLaunchKernelGGL((k_bwd_query_mfma64<QT, GT, OT>), dim3(grid), dim3(kThreads), 0, stream,
+                                               static_cast<const QT*>(q), static_cast<const GT*>(dout), state,
+                                               static_cast<OT*>(dq), gpart, pl.N, pl.H, pl.L, pl.NB, bp.tq, bp.tpbq,
+                                               eps);
+                        } else if (pl.D == kD / 2) {
                             hipLaunchKernelGGL((k_bwd_query_mfma<QT, GT, OT, kD / 2>), dim3(grid), dim3(kThreads), 0,
                                                stream, static_cast<const QT*>(q), static_cast<const GT*>(dout), state,
                                                static_cast<OT*>(dq), gpart, pl.N, groups32(pl), pl.HP, pl.H, pl.L,
                                                pl.NB, bp.tq, bp.tpbq, eps);
-                            return;
+                        } else {
+                            hipLaunchKernelGGL((k_bwd_query_mfma<QT, GT, OT, kD>), dim3(grid), dim3(kThreads), 0, stream,
+                                               static_cast<const QT*>(q), static_cast<const GT*>(dout), state,
+                                               static_cast<OT*>(dq), gpart, pl.N, pl.H, pl.HP, pl.H, pl.L, pl.NB,
+                                               bp.tq, bp.tpbq, eps);
                         }
+                    } else {
+                        routed = false;   // the plan sends these to the per-wave kernels
                     }
-                    hipLaunchKernelGGL((k_bwd_query_mfma<QT, GT, OT, kD>), dim3(grid), dim3(kThreads), 0, stream,
-                                       static_cast<const QT*>(q), static_cast<const GT*>(dout), state,
-                                       static_cast<OT*>(dq), gpart, pl.N, pl.H, pl.HP, pl.H, pl.L, pl.NB, bp.tq,
-                                       bp.tpbq, eps);
                 });
             });
         });
-        return hipGetLastError();
+        return routed ? hipGetLastError() : hipErrorInvalidConfiguration;
     }
     const unsigned grid = (unsigned)((size_t)pl.B * pl.H * pl.NB * bp.tpbq);
     by_dtype(pl.in_dtype, [&](auto it) {

@@ -643,7 +643,7 @@ template <> struct GradRow<float> {
     __device__ __forceinline__ void load(const float* row, int g, int nrr = 4) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
-            x[rr] = rr < nrr ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 8 * rr + 4 * g))
+            x[rr] = rr < nrr ? *reinterpret_cast<const f32x4*>(row + 8 * rr + 4 * g)
                              : (f32x4){0.f, 0.f, 0.f, 0.f};
     }
     __device__ __forceinline__ float at(int rr, int e) const { return x[rr][e]; }
@@ -658,7 +658,7 @@ template <> struct GradRow<uint16_t> {
     __device__ __forceinline__ void load(const uint16_t* row, int g, int nrr = 4) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
-            x[rr] = rr < nrr ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(row + 8 * rr + 4 * g))
+            x[rr] = rr < nrr ? *reinterpret_cast<const u32x2*>(row + 8 * rr + 4 * g)
                              : (u32x2){0u, 0u};
     }
     __device__ __forceinline__ float at(int rr, int e) const {
@@ -675,7 +675,7 @@ template <> struct GradRow<_Float16> {
     __device__ __forceinline__ void load(const _Float16* row, int g, int nrr = 4) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
-            x[rr] = rr < nrr ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(row + 8 * rr + 4 * g))
+            x[rr] = rr < nrr ? *reinterpret_cast<const u32x2*>(row + 8 * rr + 4 * g)
                              : (u32x2){0u, 0u};
     }
     __device__ __forceinline__ float at(int rr, int e) const {
@@ -930,8 +930,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
             const long long row = ((long long)b * N + min(tt + i, t1 - 1)) * hstride + h * kD;
             x.qa.load(reinterpret_cast<const float*>(q) + row, g, ncols / 8);
             if constexpr (kDoutOperand) {
-                x.g0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dout + row + 8 * g));
-                x.g1 = ncols > 16 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dout + row + 16 + 8 * g))
+                x.g0 = *reinterpret_cast<const u32x4*>(dout + row + 8 * g);
+                x.g1 = ncols > 16 ? *reinterpret_cast<const u32x4*>(dout + row + 16 + 8 * g)
                                   : (u32x4){0u, 0u, 0u, 0u};
             }
             x.gr.load(dout + row, g, ncols / 8);
@@ -1180,7 +1180,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
                 } else {
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks)
-                        db[ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dout + grow + 16 * ks + 8 * g));
+                        db[ks] = *reinterpret_cast<const u32x4*>(dout + grow + 16 * ks + 8 * g);
                 }
                 acc = mma_split_ks<GF16, KS>(A, db, acc);
                 rs = r;

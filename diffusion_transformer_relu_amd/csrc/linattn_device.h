@@ -301,7 +301,10 @@ __device__ __forceinline__ void store_tile(float* ot, const f32x16& acc, int lan
 }
 
 // fp32 inputs: features 8g..8g+7 and 16+8g..16+8g+7 of an fp32 row (the B
-// operand layout), 4 x 16 bytes.  upper = false leaves features 16.. as zero
+// operand layout), 4 x 16 bytes.  Plain loads: each instruction reads a part
+// of each line it touches, and a non-temporal load of part of a line does not
+// keep the line for the loads of its other parts (such reads measured at
+// half the bandwidth of plain ones); whole-line reads are non-temporal.  upper = false leaves features 16.. as zero
 // without reading them (a 32-feature group that is a lone head of dim 16).
 struct F32Operand {
     f32x4 x[4];
@@ -309,7 +312,7 @@ struct F32Operand {
 #pragma unroll
         for (int p = 0; p < 4; ++p)
             x[p] = (p < 2 || upper)
-                       ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 16 * (p >> 1) + 8 * g + 4 * (p & 1)))
+                       ? *reinterpret_cast<const f32x4*>(row + 16 * (p >> 1) + 8 * g + 4 * (p & 1))
                        : (f32x4){0.f, 0.f, 0.f, 0.f};
     }
     // the 8 values of half ks (features 16 ks + 8 g ..), optionally ReLU'd

@@ -381,7 +381,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
 #pragma unroll
         for (int ts = 0; ts < 4; ++ts) {
             const f32x4* s = reinterpret_cast<const f32x4*>(src[ts] + off);
-            const f32x4 x0 = __builtin_nontemporal_load(s), x1 = __builtin_nontemporal_load(s + 1);
+            const f32x4 x0 = s[0], x1 = s[1];   // plain loads: each reads half of a line
             r[ts][0] = ok ? x0 : (f32x4){0.f, 0.f, 0.f, 0.f};
             r[ts][1] = ok ? x1 : (f32x4){0.f, 0.f, 0.f, 0.f};
         }

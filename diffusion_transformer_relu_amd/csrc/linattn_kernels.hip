@@ -242,8 +242,8 @@ template <typename InT> struct Piece;   // 8 consecutive features of one token r
 template <> struct Piece<float> {
     f32x4 x[2];
     __device__ __forceinline__ void load(const float* p) {
-        x[0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-        x[1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1);
+        x[0] = reinterpret_cast<const f32x4*>(p)[0];   // plain loads: each reads half of a line (see F32Operand)
+        x[1] = reinterpret_cast<const f32x4*>(p)[1];
     }
     __device__ __forceinline__ void zero() { x[0] = x[1] = (f32x4){0.f, 0.f, 0.f, 0.f}; }
     __device__ __forceinline__ void get(float f[8]) const {

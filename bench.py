@@ -191,7 +191,7 @@ def extra_names(out_dtype: str) -> list:
              "d64_h35_" + o, "d16_h140_" + o, "qknorm_" + o, "qknorm_blockcausal_16x1024_" + o,
              "backward_bf16", "backward_f32", "backward_d64_h35_bf16", "backward_d16_h140_bf16",
              "backward_from_states_bf16", "train_step_bf16",
-             "jvp_bf16_f32out", "jvp_f32"]
+             "jvp_bf16_f32out", "jvp_f32", "jvp_bf16"]
     for tag in ("sana600m_1024px", "sana1600m_1024px", "sana1600m_2048px"):
         names += [tag + "_cold", tag + "_warm"]
     return names
@@ -457,11 +457,10 @@ def main() -> int:
                 "algorithmic bytes = 7 tensors")
         return build
 
-    def case_jvp(dt):
+    def case_jvp(dt, ot=torch.float32):
         def build():
             sx = [[t.to(dt) for t in st] for st in sets]
             tx = [[t.clone() for t in st] for st in sx]
-            ot = torch.float32
             jo = [[torch.empty((B, N, H, D), dtype=ot, device=dev) for _ in range(2)] for _ in range(NSETS)]
             wsj = torch.empty(sana.sana_linattn_jvp_workspace_bytes(B, H, N, D, 0), dtype=torch.uint8, device=dev)
 
@@ -471,8 +470,9 @@ def main() -> int:
                 sana.sana_linattn_jvp(q, k, v, qt, kt, vt, *jo[i % NSETS], wsj, eps=w.eps,
                                       stream=torch.cuda.current_stream())
             es = 4 if dt == torch.float32 else 2
-            return fn, w.token_heads * D * (6 * es + 2 * 4), \
-                "sana_linattn_jvp, fp32 out and out_t; algorithmic bytes = 6 inputs + 2 outputs"
+            eo = 4 if ot == torch.float32 else 2
+            return fn, w.token_heads * D * (6 * es + 2 * eo), \
+                f"sana_linattn_jvp, {'fp32' if eo == 4 else 'bf16'} out and out_t; algorithmic bytes = 6 inputs + 2 outputs"
         return build
 
     def case_headdim(Hx, Dx):
@@ -542,6 +542,7 @@ def main() -> int:
         "train_step_bf16": case_saved(True),
         "jvp_bf16_f32out": case_jvp(torch.bfloat16),
         "jvp_f32": case_jvp(torch.float32),
+        "jvp_bf16": case_jvp(torch.bfloat16, torch.bfloat16),
     }
     for wx, tag in ((workloads.S600M_1024, "sana600m_1024px"), (workloads.S1600M_1024, "sana1600m_1024px"),
                     (workloads.S1600M_2048, "sana1600m_2048px")):

@@ -95,20 +95,23 @@ __device__ __forceinline__ void store_out(float* p, long long i, float x) { p[i]
 __device__ __forceinline__ void store_out(uint16_t* p, long long i, float x) { p[i] = f32_to_bf16(x); }
 __device__ __forceinline__ void store_out(_Float16* p, long long i, float x) { p[i] = (_Float16)x; }
 
-// Output stores are non-temporal: out is written once and never read here, and
-// streaming it past the caches raises the write bandwidth markedly on gfx950.
+// fp32 output stores are non-temporal: out is written once and never read
+// here, and streaming whole lines past the caches raises the write bandwidth
+// markedly on gfx950.  A 16-bit row piece here is half of each line an
+// instruction touches, and those stores are plain (non-temporal half-line
+// stores measured slower: the JVP with bf16 out 148.4 against 151.5 us).
 __device__ __forceinline__ void store4(float* p, f32x4 x) {
     __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
 }
 __device__ __forceinline__ void store4(uint16_t* p, f32x4 x) {
     const uint32_t lo = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
     const uint32_t hi = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
-    __builtin_nontemporal_store((u32x2){lo, hi}, reinterpret_cast<u32x2*>(p));
+    *reinterpret_cast<u32x2*>(p) = (u32x2){lo, hi};
 }
 __device__ __forceinline__ void store4(_Float16* p, f32x4 x) {
     const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)x[0]), h1 = __builtin_bit_cast(uint16_t, (_Float16)x[1]);
     const uint32_t h2 = __builtin_bit_cast(uint16_t, (_Float16)x[2]), h3 = __builtin_bit_cast(uint16_t, (_Float16)x[3]);
-    __builtin_nontemporal_store((u32x2){h0 | (h1 << 16), h2 | (h3 << 16)}, reinterpret_cast<u32x2*>(p));
+    *reinterpret_cast<u32x2*>(p) = (u32x2){h0 | (h1 << 16), h2 | (h3 << 16)};
 }
 
 // Three bf16 terms of an fp32 value, x = t0 + t1 + t2 to about 2^-24 relative:

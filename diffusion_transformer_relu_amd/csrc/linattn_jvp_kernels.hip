@@ -228,8 +228,16 @@ __device__ __forceinline__ void finish_tangent(f32x16& acc, f32x16& acct, float 
 // is head 2 hp + (w & 1); 64: output half w & 1 of head hp, reducing over all
 // 64 features of q; 16: heads 2 h and 2 h + 1 of group h against their
 // block-diagonal states, each with its own normalisers (see apply_operands).
+// Occupancy target of the 16-bit apply kernel: 3 waves per SIMD for bf16 q at
+// head dims 16 and 32 with 16-bit outputs (166-168 VGPRs, no spills; the JVP
+// with bf16 out 141-143 against 150 us, same box); with fp32 outputs that
+// was slower (153-155 against 151 us), and fp16 q (the split of f and f_t)
+// and head dim 64 would spill, so those are left to the compiler (2).
+template <bool F16, int HD, typename OutT>
+constexpr int jvp_apply_waves() { return !F16 && HD != 2 * kD && sizeof(OutT) == 2 ? 3 : 1; }
+
 template <bool F16, typename OutT, int HD>
-__global__ __launch_bounds__(kThreads) void k_jvp_apply_mfma(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(jvp_apply_waves<F16, HD, OutT>(), 8))) void k_jvp_apply_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ qt, const float* __restrict__ state,
     OutT* __restrict__ out, OutT* __restrict__ outt, int N, int H, int HP, int HR, int L, int NB, int tile, int tpb,
     float eps) {

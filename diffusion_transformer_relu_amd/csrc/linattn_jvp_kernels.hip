@@ -15,6 +15,8 @@
 // row, as the forward's kernels do.
 #include "linattn_device.h"
 
+#include <type_traits>
+
 namespace sana {
 namespace {
 
@@ -288,19 +290,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(jvp_ap
     const bool second = !D16 || 2 * h + 1 < HR;       // head dim 16: the group has a second head
     const int ncols = second ? 32 : 16;
     float* ot = otile[wave];
-    for (int tt = t0 + 32 * (wave >> 1); tt < t1; tt += 64) {
-        const int row = min(tt + i, t1 - 1);   // clamped rows repeat the last row (see store_tile)
-        const u32x4* srcq = reinterpret_cast<const u32x4*>(q + ((long long)b * N + row) * hstride + qcol);
-        const u32x4* srct = reinterpret_cast<const u32x4*>(qt + ((long long)b * N + row) * hstride + qcol);
-        u32x4 f[KS], ft[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bool on = ks == 0 || second;   // features 16 ks + 8 g .. + 7 = src[2 ks]
-            f[ks] = relu_bf16x8(on ? srcq[2 * ks] : (u32x4){0u, 0u, 0u, 0u});
-            ft[ks] = keep_where_nonzero(f[ks], on ? srct[2 * ks] : (u32x4){0u, 0u, 0u, 0u});
-        }
+    // One sub-tile's products, normalisers and stores from its prepared rows
+    // f = ReLU(q) and f_t (zero where q <= 0); NC: the group's columns stored.
+    auto body = [&](int tt, const u32x4 (&f)[KS], const u32x4 (&ft)[KS], auto ncols_c) {
+        const int NC = ncols_c;   // an int, or a constant that folds the stores' column test
         const int n = min(32, t1 - tt);
-
         f32x16 acc = {}, acct = {};
         acc = mma_split_ks<F16, KS>(sa, f, acc);
         acct = mma_split_ks<F16, KS>(sat, f, acct);
@@ -334,10 +328,111 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(jvp_ap
             }
         }
         finish_tangent<D16>(acc, acct, dp, dpt, dp1, dpt1, eps);
-        store_tile<OutT>(ot, acc, lane, n, [&](int t) { return out + ((long long)b * N + tt + t) * hstride + h * kD; },
-                         ncols);
+        store_tile<OutT>(ot, acc, lane, n,
+                         [&](int t) { return out + ((long long)b * N + tt + t) * hstride + h * kD; }, NC);
         store_tile<OutT>(ot, acct, lane, n,
-                         [&](int t) { return outt + ((long long)b * N + tt + t) * hstride + h * kD; }, ncols);
+                         [&](int t) { return outt + ((long long)b * N + tt + t) * hstride + h * kD; }, NC);
+    };
+    if constexpr (jvp_apply_waves<F16, HD, OutT>() != 3) {
+        // The next sub-tile's rows are requested before this one's products
+        // and prepared after its stores have been issued, so that the wait for
+        // them leaves the stores in flight.  Loads are unconditional: rows past
+        // the range are clamped to its last row (see store_tile), and a missing
+        // second head of a group of dim 16 reads the first head's piece, zeroed
+        // when prepared.  The stores are unconditional when the group's 32
+        // columns all exist (a loop of its own for a lone head of dim 16).
+        // (At 3 waves per SIMD the extra rows would spill: the loop below.)
+        struct Rows {
+            u32x4 x[KS], t[KS];
+        };
+        auto load = [&](int tt, Rows& r) {
+            const int row = min(tt + i, t1 - 1);
+            const u32x4* srcq = reinterpret_cast<const u32x4*>(q + ((long long)b * N + row) * hstride + qcol);
+            const u32x4* srct = reinterpret_cast<const u32x4*>(qt + ((long long)b * N + row) * hstride + qcol);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int c = ks == 0 || second ? 2 * ks : 0;   // features 16 ks + 8 g .. + 7 = src[2 ks]
+                r.x[ks] = srcq[c];
+                r.t[ks] = srct[c];
+            }
+        };
+        u32x4 f[KS], ft[KS];
+        auto prepare = [&](const Rows& r) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bool on = ks == 0 || second;
+                f[ks] = relu_bf16x8(on ? r.x[ks] : (u32x4){0u, 0u, 0u, 0u});
+                ft[ks] = keep_where_nonzero(f[ks], on ? r.t[ks] : (u32x4){0u, 0u, 0u, 0u});
+            }
+        };
+        auto run = [&](auto ncols_c) {
+            int tt = t0 + 32 * (wave >> 1);
+            if (tt >= t1) return;
+            Rows nx;
+            load(tt, nx);
+            prepare(nx);
+            for (; tt < t1; tt += 64) {
+                load(tt + 64, nx);
+                body(tt, f, ft, ncols_c);
+                prepare(nx);   // the next sub-tile's rows (past the end: the last row again, unused)
+            }
+        };
+        if (ncols == 32)
+            run(std::integral_constant<int, 32>{});
+        else
+            run(std::integral_constant<int, 16>{});
+    } else {
+        for (int tt = t0 + 32 * (wave >> 1); tt < t1; tt += 64) {
+            const int row = min(tt + i, t1 - 1);   // clamped rows repeat the last row (see store_tile)
+            const u32x4* srcq = reinterpret_cast<const u32x4*>(q + ((long long)b * N + row) * hstride + qcol);
+            const u32x4* srct = reinterpret_cast<const u32x4*>(qt + ((long long)b * N + row) * hstride + qcol);
+            u32x4 f[KS], ft[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bool on = ks == 0 || second;   // features 16 ks + 8 g .. + 7 = src[2 ks]
+                f[ks] = relu_bf16x8(on ? srcq[2 * ks] : (u32x4){0u, 0u, 0u, 0u});
+                ft[ks] = keep_where_nonzero(f[ks], on ? srct[2 * ks] : (u32x4){0u, 0u, 0u, 0u});
+            }
+            const int n = min(32, t1 - tt);
+
+            f32x16 acc = {}, acct = {};
+            acc = mma_split_ks<F16, KS>(sa, f, acc);
+            acct = mma_split_ks<F16, KS>(sat, f, acct);
+            acct = mma_split_ks<F16, KS>(sa, ft, acct);
+            float dp = 0.f, dpt = 0.f, dp1 = 0.f, dpt1 = 0.f;   // dp1, dpt1: head dim 16, the second head
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                float& a = (D16 && ks == 1) ? dp1 : dp;
+                float& at = (D16 && ks == 1) ? dpt1 : dpt;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    float x0, x1, y0, y1;
+                    if constexpr (F16) {
+                        x0 = f16_to_f32((uint16_t)(f[ks][d] & 0xffffu));
+                        x1 = f16_to_f32((uint16_t)(f[ks][d] >> 16));
+                        y0 = f16_to_f32((uint16_t)(ft[ks][d] & 0xffffu));
+                        y1 = f16_to_f32((uint16_t)(ft[ks][d] >> 16));
+                    } else {
+                        x0 = lo_bf16(f[ks][d]);
+                        x1 = hi_bf16(f[ks][d]);
+                        y0 = lo_bf16(ft[ks][d]);
+                        y1 = hi_bf16(ft[ks][d]);
+                    }
+                    const int e = 8 * ks + 2 * d;
+                    a = fmaf(x0, sz[e], a);
+                    a = fmaf(x1, sz[e + 1], a);
+                    at = fmaf(x0, szt[e], at);
+                    at = fmaf(x1, szt[e + 1], at);
+                    at = fmaf(y0, sz[e], at);
+                    at = fmaf(y1, sz[e + 1], at);
+                }
+            }
+            finish_tangent<D16>(acc, acct, dp, dpt, dp1, dpt1, eps);
+            store_tile<OutT>(ot, acc, lane, n, [&](int t) { return out + ((long long)b * N + tt + t) * hstride + h * kD; },
+                             ncols);
+            store_tile<OutT>(ot, acct, lane, n,
+                             [&](int t) { return outt + ((long long)b * N + tt + t) * hstride + h * kD; }, ncols);
+        }
     }
 }
 

@@ -187,7 +187,8 @@ def extra_names(out_dtype: str) -> list:
     o = out_dtype + "out"
     names = [("bf16" if out_dtype == "f32" else "f32") + "_out",
              "blockcausal_16x1024_f32out", "blockcausal_16x1024_bf16out",
-             "stream_4x4096_bc1024_" + o, "fused_qkv_strided_" + o, "f16_in_" + o, "f32_in_" + o,
+             "stream_4x4096_bc1024_" + o, "fused_qkv_strided_" + o, "fused_qkv_strided_2sets_" + o,
+             "rotation_6sets_" + o, "f16_in_" + o, "f32_in_" + o,
              "d64_h35_" + o, "d16_h140_" + o, "qknorm_" + o, "qknorm_blockcausal_16x1024_" + o,
              "backward_bf16", "backward_f32", "backward_d64_h35_bf16", "backward_d16_h140_bf16",
              "backward_from_states_bf16", "train_step_bf16",
@@ -384,6 +385,28 @@ def main() -> int:
         return fn, alg_bytes, ("the headline sequence as 4 chained calls of 4096 tokens with the state carried "
                                "(block_len 1024); time per whole sequence")
 
+    def case_rotation(nsets, fused):
+        """The headline forward over nsets rotating buffer sets (the default
+        measurement uses NSETS): the apply kernel slows down once the working
+        set of recently used buffers grows past about 1-2 GB."""
+        def build():
+            more = max(0, nsets - NSETS)
+            xs = (sets + [[t.clone() for t in base] for _ in range(more)])[:nsets]
+            xo = (outs + [torch.empty_like(outs[0]) for _ in range(more)])[:nsets]
+            fz = [torch.stack(st, dim=2) for st in xs] if fused else None
+
+            def fn(i):
+                if fused:
+                    f = fz[i % nsets]
+                    sana.sana_linattn_fwd_strided(f[:, :, 0], f[:, :, 1], f[:, :, 2], xo[i % nsets], ws, eps=w.eps,
+                                                  stream=torch.cuda.current_stream())
+                else:
+                    q, k, v = xs[i % nsets]
+                    sana.sana_linattn_fwd(q, k, v, xo[i % nsets], ws, eps=w.eps, stream=torch.cuda.current_stream())
+            layout = "q, k, v strided views of one [B, N, 3, H, D] buffer" if fused else "contiguous q, k, v"
+            return fn, alg_bytes, f"the headline forward, {layout}, over {nsets} rotating input/output sets"
+        return build
+
     def case_strided():
         fused = [torch.stack(st, dim=2) for st in sets]
 
@@ -528,6 +551,8 @@ def main() -> int:
         "blockcausal_16x1024_bf16out": case_blockcausal(torch.bfloat16),
         "stream_4x4096_bc1024_" + args.out_dtype + "out": case_stream4,
         "fused_qkv_strided_" + args.out_dtype + "out": case_strided,
+        "fused_qkv_strided_2sets_" + args.out_dtype + "out": case_rotation(2, True),
+        "rotation_6sets_" + args.out_dtype + "out": case_rotation(6, False),
         "f16_in_" + args.out_dtype + "out": case_in(torch.float16),
         "f32_in_" + args.out_dtype + "out": case_in(torch.float32),
         "d64_h35_" + args.out_dtype + "out": case_headdim(H // 2, 2 * D),
